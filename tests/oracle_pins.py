@@ -1,0 +1,298 @@
+"""Pins for the float64 oracle: each pin checks the oracle against something other
+than itself (exact rational brute force, closed forms, invariants the pages'
+statements imply).  Every pin takes the oracle implementation as an argument so
+that the mutation tests can run the same pins against deliberately broken
+copies of the oracle and show that each planted mistake is caught.
+"""
+
+import numpy as np
+
+from exact_ref import exact_attention, exact_state, token_causal_recurrence
+
+EPS = 1e-6
+
+
+def _dyadic(rng, shape, lo=-2.0, hi=2.0):
+    """Small dyadic values (multiples of 1/4): exact in bf16, fp32 and float64."""
+    return np.round(rng.uniform(lo, hi, size=shape) * 4.0) / 4.0
+
+
+def _close(a, b, rtol, what):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    scale = max(np.max(np.abs(b)), 1e-300)
+    err = np.max(np.abs(a - b)) / scale if a.size else 0.0
+    assert err <= rtol, f"{what}: max |diff|/max|ref| = {err:.3e} > {rtol:.1e}"
+
+
+# --------------------------------------------------------------------------
+# Exact brute force (quadratic definition, rational arithmetic)
+# --------------------------------------------------------------------------
+
+def pin_exact_noncausal(impl):
+    rng = np.random.default_rng(11)
+    for N, D in [(1, 1), (2, 2), (3, 4), (5, 4), (6, 2)]:
+        q, k, v = (_dyadic(rng, (N, D)) for _ in range(3))
+        want = exact_attention(q, k, v, EPS)
+        got = impl.linattn(q[None, None], k[None, None], v[None, None], EPS)[0, 0]
+        _close(got, want, 1e-12, f"linear vs exact quadratic N={N} D={D}")
+        got_bf = impl.brute_force(q[None, None], k[None, None], v[None, None], EPS)[0, 0]
+        _close(got_bf, want, 1e-12, f"numpy quadratic vs exact N={N} D={D}")
+
+
+def pin_exact_state(impl):
+    rng = np.random.default_rng(12)
+    k, v = _dyadic(rng, (7, 4)), _dyadic(rng, (7, 4))
+    S_want, z_want = exact_state(k, v)
+    S, z = impl.kv_state(k[None, None], v[None, None])
+    _close(S[0, 0], S_want, 0.0, "S = relu(K)^T V (row d = key feature, column e = value feature)")
+    _close(z[0, 0], z_want, 0.0, "z = sum relu(K_j)")
+
+
+def pin_exact_rope(impl):
+    rng = np.random.default_rng(13)
+    for N, D in [(2, 2), (4, 4), (5, 6)]:
+        q, k, v = (_dyadic(rng, (N, D)) for _ in range(3))
+        ang = rng.uniform(-3.0, 3.0, size=(N, D // 2))
+        want = exact_attention(q, k, v, EPS, np.cos(ang), np.sin(ang))
+        got = impl.linattn(q[None, None], k[None, None], v[None, None], EPS, angles=ang)[0, 0]
+        _close(got, want, 1e-12, f"RoPE linear vs exact quadratic N={N} D={D}")
+        got_bf = impl.brute_force(q[None, None], k[None, None], v[None, None], EPS, angles=ang)[0, 0]
+        _close(got_bf, want, 1e-12, f"RoPE numpy quadratic vs exact N={N} D={D}")
+
+
+def pin_exact_block(impl):
+    rng = np.random.default_rng(14)
+    for N, D, L in [(5, 2, 2), (6, 4, 3), (7, 4, 1), (4, 2, 4), (5, 2, 9)]:
+        q, k, v = (_dyadic(rng, (N, D)) for _ in range(3))
+        want = exact_attention(q, k, v, EPS, chunk=L)
+        got, _, _ = impl.block_causal(q[None, None], k[None, None], v[None, None], L, EPS)
+        _close(got[0, 0], want, 1e-12, f"chunked recurrence vs exact masked quadratic N={N} L={L}")
+        got_bf = impl.brute_force(q[None, None], k[None, None], v[None, None], EPS, chunk=L)[0, 0]
+        _close(got_bf, want, 1e-12, f"numpy masked quadratic vs exact N={N} L={L}")
+
+
+def pin_exact_block_rope(impl):
+    rng = np.random.default_rng(15)
+    N, D, L = 6, 4, 4
+    q, k, v = (_dyadic(rng, (N, D)) for _ in range(3))
+    ang = rng.uniform(-3.0, 3.0, size=(N, D // 2))
+    want = exact_attention(q, k, v, EPS, np.cos(ang), np.sin(ang), chunk=L)
+    got, _, _ = impl.block_causal(q[None, None], k[None, None], v[None, None], L, EPS, angles=ang)
+    _close(got[0, 0], want, 1e-12, "block-causal RoPE vs exact masked quadratic")
+
+
+def pin_token_causal(impl):
+    """Chunks of one token reduce to the inclusive token-causal recurrence."""
+    rng = np.random.default_rng(16)
+    q, k, v = (_dyadic(rng, (6, 4)) for _ in range(3))
+    want = token_causal_recurrence(q, k, v, EPS)
+    got, _, _ = impl.block_causal(q[None, None], k[None, None], v[None, None], 1, EPS)
+    _close(got[0, 0], want, 1e-12, "chunk length 1 vs token-causal recurrence")
+
+
+# --------------------------------------------------------------------------
+# Closed forms
+# --------------------------------------------------------------------------
+
+def pin_closed_forms(impl):
+    rng = np.random.default_rng(21)
+    D = 32
+    # N = 1: O = v * s / (s + eps), s = relu(q).relu(k)
+    q, k, v = (rng.standard_normal((1, 1, 1, D)) for _ in range(3))
+    s = np.sum(np.maximum(q, 0) * np.maximum(k, 0))
+    _close(impl.linattn(q, k, v, EPS), v * s / (s + EPS), 1e-14, "N=1 closed form")
+    # one-hot relu(Q_i) = e_a -> O_i = sum_j relu(K_ja) V_j / (sum_j relu(K_ja) + eps)
+    N = 40
+    k, v = rng.standard_normal((1, 1, N, D)), rng.standard_normal((1, 1, N, D))
+    for a in (0, 7, 31):
+        q = -np.ones((1, 1, 1, D))
+        q[..., a] = 1.0
+        w = np.maximum(k[0, 0, :, a], 0)
+        want = (w @ v[0, 0]) / (w.sum() + EPS)
+        _close(impl.apply_state(q, *impl.kv_state(k, v), EPS)[0, 0, 0], want, 1e-13,
+               f"one-hot query on feature {a}")
+    # all keys negative -> every output is exactly 0 (0 / eps)
+    q = rng.standard_normal((1, 2, 9, D))
+    k = -np.abs(rng.standard_normal((1, 2, 9, D))) - 0.1
+    v = rng.standard_normal((1, 2, 9, D))
+    o = impl.linattn(q, k, v, EPS)
+    assert np.all(o == 0.0), "all-negative keys must give exact zeros"
+    # all queries negative -> exact zeros
+    o = impl.linattn(-np.abs(q) - 0.1, rng.standard_normal(k.shape), v, EPS)
+    assert np.all(o == 0.0), "all-negative queries must give exact zeros"
+    # D = 1: scalars
+    q, k, v = (rng.standard_normal((1, 1, 12, 1)) for _ in range(3))
+    rk = np.maximum(k[0, 0, :, 0], 0)
+    rq = np.maximum(q[0, 0, :, 0], 0)
+    want = rq * np.dot(rk, v[0, 0, :, 0]) / (rq * rk.sum() + EPS)
+    _close(impl.linattn(q, k, v, EPS)[0, 0, :, 0], want, 1e-13, "D=1 scalar form")
+
+
+def pin_constant_v(impl):
+    """Constant V = c gives O_i = c s_i / (s_i + eps) (non-RoPE modes)."""
+    rng = np.random.default_rng(22)
+    q, k = rng.standard_normal((2, 3, 64, 32)), rng.standard_normal((2, 3, 64, 32))
+    c = rng.standard_normal(32)
+    v = np.broadcast_to(c, q.shape).copy()
+    s = np.maximum(q, 0) @ np.maximum(k, 0).sum(axis=-2)[..., None]
+    want = c * s / (s + EPS)
+    _close(impl.linattn(q, k, v, EPS), want, 1e-13, "constant V (non-causal)")
+    o, _, _ = impl.block_causal(q, k, v, 16, EPS)
+    assert np.max(np.abs(o - c)) <= 1e-4 * np.max(np.abs(c)), "constant V (block-causal)"
+
+
+# --------------------------------------------------------------------------
+# Invariants
+# --------------------------------------------------------------------------
+
+def pin_invariants(impl):
+    rng = np.random.default_rng(31)
+    q, k, v1, v2 = (rng.standard_normal((1, 2, 48, 32)) for _ in range(4))
+    # linearity in V
+    a, b = 0.75, -1.5
+    _close(impl.linattn(q, k, a * v1 + b * v2, EPS),
+           a * impl.linattn(q, k, v1, EPS) + b * impl.linattn(q, k, v2, EPS), 1e-12, "linearity in V")
+    # joint permutation of (K_j, V_j) leaves the non-causal output unchanged
+    perm = rng.permutation(48)
+    _close(impl.linattn(q, k[:, :, perm], v1[:, :, perm], EPS), impl.linattn(q, k, v1, EPS), 1e-12,
+           "key/value permutation")
+    # positive scaling of Q or of K cancels exactly when eps = 0
+    _close(impl.linattn(3.0 * q, k, v1, 0.0), impl.linattn(q, k, v1, 0.0), 1e-12, "Q scaling")
+    _close(impl.linattn(q, 0.25 * k, v1, 0.0), impl.linattn(q, k, v1, 0.0), 1e-12, "K scaling")
+    # the output is a convex combination of V rows per feature (weights >= 0)
+    o = impl.linattn(q, k, v1, EPS)
+    assert np.all(o <= v1.max(axis=-2, keepdims=True) + 1e-12)
+    assert np.all(o >= v1.min(axis=-2, keepdims=True) - 1e-12)
+
+
+# --------------------------------------------------------------------------
+# RoPE
+# --------------------------------------------------------------------------
+
+def pin_rope_angles(impl):
+    T, Hl, Wl = 3, 4, 5
+    ang = impl.rope3d_angles(T, Hl, Wl)
+    assert ang.shape == (T * Hl * Wl, 16)
+
+    def n(t, h, w):
+        return (t * Hl + h) * Wl + w
+
+    # pair 0 of every axis turns at one radian per step of its coordinate
+    assert ang[n(2, 0, 0), 0] == 2.0 and ang[n(0, 3, 0), 4] == 3.0 and ang[n(0, 0, 4), 10] == 4.0
+    # t axis: 8 dims, pair k frequency 10000**(-2k/8) = 0.1**k
+    _close(ang[n(1, 0, 0), 0:4], [1.0, 0.1, 0.01, 0.001], 1e-14, "t-axis frequencies")
+    # h and w axes: 12 dims, pair 3 frequency 10000**(-6/12) = 0.01
+    _close(ang[n(0, 1, 0), 7], 0.01, 1e-14, "h-axis pair 3")
+    _close(ang[n(0, 0, 1), 13], 0.01, 1e-14, "w-axis pair 3")
+    # each axis owns its pairs: t -> 0..3, h -> 4..9, w -> 10..15
+    base = ang[n(1, 2, 3)]
+    assert np.all(ang[n(2, 2, 3), 4:] == base[4:]) and np.any(ang[n(2, 2, 3), :4] != base[:4])
+    assert np.all(ang[n(1, 0, 3), [*range(4), *range(10, 16)]] == base[[*range(4), *range(10, 16)]])
+    assert np.all(ang[n(1, 2, 0), :10] == base[:10])
+    assert np.all(impl.rope3d_angles(1, 1, 1) == 0.0)
+
+
+def pin_rope_properties(impl):
+    rng = np.random.default_rng(41)
+    T, Hl, Wl = 3, 4, 5
+    N = T * Hl * Wl
+    q, k, v = (rng.standard_normal((1, 2, N, 32)) for _ in range(3))
+    # identity rotation (all angles 0) reduces to the plain form
+    _close(impl.linattn(q, k, v, EPS, angles=np.zeros((N, 16))), impl.linattn(q, k, v, EPS), 1e-13,
+           "identity RoPE")
+    # rotation preserves the norm of every pair
+    ang = impl.rope3d_angles(T, Hl, Wl)
+    x = rng.standard_normal((N, 32))
+    r = impl.rotate_pairs(x, ang)
+    _close(np.hypot(r[:, 0::2], r[:, 1::2]), np.hypot(x[:, 0::2], x[:, 1::2]), 1e-14, "pair norms")
+    # shifting every token's position by the same amount along one axis leaves
+    # the output unchanged (the numerator only sees relative rotations)
+    big = impl.rope3d_angles(T + 2, Hl + 3, Wl + 1)
+
+    def sub(dt, dh, dw):
+        idx = [((t + dt) * (Hl + 3) + (h + dh)) * (Wl + 1) + (w + dw)
+               for t in range(T) for h in range(Hl) for w in range(Wl)]
+        return big[idx]
+
+    ref = impl.linattn(q, k, v, EPS, angles=sub(0, 0, 0))
+    for shift in [(2, 0, 0), (0, 3, 0), (0, 0, 1), (1, 2, 1)]:
+        _close(impl.linattn(q, k, v, EPS, angles=sub(*shift)), ref, 1e-11, f"position shift {shift}")
+    # the denominator never sees the rotation: O_i * (relu(Q_i).z + eps) is the
+    # rotated numerator computed pair by pair from the quadratic definition
+    o = impl.linattn(q, k, v, EPS, angles=ang)
+    pq, pk = np.maximum(q, 0), np.maximum(k, 0)
+    den = pq @ pk.sum(axis=-2)[..., None] + EPS
+    R = np.zeros((N, 32, 32))
+    for p in range(16):
+        c, s = np.cos(ang[:, p]), np.sin(ang[:, p])
+        R[:, 2 * p, 2 * p], R[:, 2 * p, 2 * p + 1] = c, -s
+        R[:, 2 * p + 1, 2 * p], R[:, 2 * p + 1, 2 * p + 1] = s, c
+    rq = np.einsum("nij,bhnj->bhni", R, pq)
+    rk = np.einsum("nij,bhnj->bhni", R, pk)
+    _close(o * den, (rq @ np.swapaxes(rk, -1, -2)) @ v, 1e-11, "un-rotated denominator")
+
+
+# --------------------------------------------------------------------------
+# Block-causal properties
+# --------------------------------------------------------------------------
+
+def pin_block_properties(impl):
+    rng = np.random.default_rng(51)
+    N, L = 50, 12
+    q, k, v = (rng.standard_normal((2, 2, N, 32)) for _ in range(3))
+    o, S, z = impl.block_causal(q, k, v, L, EPS)
+    # one chunk covering everything is the non-causal form
+    o1, _, _ = impl.block_causal(q, k, v, N, EPS)
+    _close(o1, impl.linattn(q, k, v, EPS), 1e-12, "single chunk == non-causal")
+    # the last chunk's rows see everything: equal to the non-causal rows
+    last = slice((N - 1) // L * L, N)
+    _close(o[:, :, last], impl.linattn(q, k, v, EPS)[:, :, last], 1e-12, "last chunk == non-causal rows")
+    # the first chunk sees only itself
+    _close(o[:, :, :L], impl.linattn(q[:, :, :L], k[:, :, :L], v[:, :, :L], EPS), 1e-12,
+           "first chunk == its own non-causal attention")
+    # the final carried state is the full-sequence state
+    S_full, z_full = impl.kv_state(k, v)
+    _close(S, S_full, 1e-12, "final S")
+    _close(z, z_full, 1e-12, "final z")
+    # causality: changing chunk 2 onwards leaves chunks 0..1 bit-identical
+    q2, k2, v2 = q.copy(), k.copy(), v.copy()
+    for x in (q2, k2, v2):
+        x[:, :, 2 * L:] = rng.standard_normal(x[:, :, 2 * L:].shape)
+    o2, _, _ = impl.block_causal(q2, k2, v2, L, EPS)
+    assert np.array_equal(o2[:, :, :2 * L], o[:, :, :2 * L]), "earlier chunks saw a later chunk"
+    assert not np.array_equal(o2[:, :, 2 * L:3 * L], o[:, :, 2 * L:3 * L])
+    # save / restore of the carried state mid-sequence is bit-identical
+    S_c = np.zeros((2, 2, 32, 32))
+    z_c = np.zeros((2, 2, 32))
+    outs = []
+    for c, start in enumerate(range(0, N, L)):
+        sl = slice(start, min(N, start + L))
+        if c == 2:
+            S_c, z_c = np.array(S_c.tolist()), np.array(z_c.tolist())   # round trip through host lists
+        oc, S_c, z_c = impl.block_forward(q[:, :, sl], k[:, :, sl], v[:, :, sl], S_c, z_c, EPS)
+        outs.append(oc)
+    assert np.array_equal(np.concatenate(outs, axis=2), o), "save/restore changed the result"
+    # state_update applied in two pieces equals one call
+    Sa, za = impl.state_update(k[:, :, :20], v[:, :, :20], np.zeros_like(S), np.zeros_like(z))
+    Sa, za = impl.state_update(k[:, :, 20:], v[:, :, 20:], Sa, za, None, 20)
+    _close(Sa, S_full, 1e-12, "two-piece state_update S")
+    _close(za, z_full, 1e-12, "two-piece state_update z")
+
+
+def pin_block_rope_positions(impl):
+    """Block mode with RoPE indexes the angle table by global token position."""
+    rng = np.random.default_rng(52)
+    T, Hl, Wl = 2, 3, 4
+    N, L = T * Hl * Wl, 5
+    ang = impl.rope3d_angles(T, Hl, Wl)
+    q, k, v = (rng.standard_normal((1, 1, N, 32)) for _ in range(3))
+    o, _, _ = impl.block_causal(q, k, v, L, EPS, angles=ang)
+    _close(o, impl.brute_force(q, k, v, EPS, angles=ang, chunk=L), 1e-11, "block RoPE vs masked quadratic")
+
+
+ALL_PINS = [
+    pin_exact_noncausal, pin_exact_state, pin_exact_rope, pin_exact_block, pin_exact_block_rope,
+    pin_token_causal, pin_closed_forms, pin_constant_v, pin_invariants, pin_rope_angles,
+    pin_rope_properties, pin_block_properties, pin_block_rope_positions,
+]

@@ -1,0 +1,71 @@
+"""CPU tests of the float64 oracle against its pins, and mutation tests showing
+that each plausible mistake planted in a copy of the oracle fails a pin."""
+
+import inspect
+import types
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.linattn_oracle as oracle_src
+from oracle_pins import ALL_PINS
+
+
+@pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)
+def test_oracle_pin(pin):
+    pin(oracle)
+
+
+def _mutant(old, new, count=1):
+    src = inspect.getsource(oracle_src)
+    assert src.count(old) == count, f"mutation anchor {old!r} found {src.count(old)} times"
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src.replace(old, new), "oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+# Each mutant is one plausible mistake: (anchor text in the oracle, replacement).
+MUTANTS = {
+    "relu_also_on_v": ("    v = np.asarray(v, dtype=np.float64)\n    pos = _positions(angles, phik.shape[-2], pos_offset)",
+                       "    v = feature_map(v)\n    pos = _positions(angles, phik.shape[-2], pos_offset)"),
+    "no_relu": ("return np.maximum(np.asarray(x, dtype=np.float64), 0.0)",
+                "return np.asarray(x, dtype=np.float64)"),
+    "state_transposed": ("S = np.matmul(np.swapaxes(phik_num, -1, -2), v)",
+                         "S = np.swapaxes(np.matmul(np.swapaxes(phik_num, -1, -2), v), -1, -2)"),
+    "eps_in_numerator": ("return num / den", "return (num + eps) / den"),
+    "eps_dropped": ("den = np.matmul(phiq, z[..., :, None]) + eps", "den = np.matmul(phiq, z[..., :, None])"),
+    "rope_in_denominator": ("den = np.matmul(phiq, z[..., :, None]) + eps",
+                            "den = np.matmul(phiq_num, z[..., :, None]) + eps"),
+    "rope_key_sum": ("z = phik.sum(axis=-2)", "z = phik_num.sum(axis=-2)"),
+    "rope_before_relu": ("    phik = feature_map(k)\n    v = np.asarray(v, dtype=np.float64)\n    pos = _positions(angles, phik.shape[-2], pos_offset)\n    phik_num = phik if pos is None else rotate_pairs(phik, pos)",
+                         "    phik = feature_map(k)\n    v = np.asarray(v, dtype=np.float64)\n    pos = _positions(angles, phik.shape[-2], pos_offset)\n    phik_num = phik if pos is None else feature_map(rotate_pairs(k, pos))"),
+    "rotation_sign": ("out[..., 1::2] = x0 * s + x1 * c", "out[..., 1::2] = -x0 * s + x1 * c"),
+    "pairs_not_interleaved": ("x0 = x[..., 0::2]\n    x1 = x[..., 1::2]",
+                              "x0 = x[..., :x.shape[-1] // 2].repeat(1, axis=-1)[..., :x.shape[-1] // 2]\n    x1 = x[..., x.shape[-1] // 2:]"),
+    "rope_base": ("def rope3d_angles(T, Hl, Wl, D=32, split=(8, 12, 12), base=10000.0):",
+                  "def rope3d_angles(T, Hl, Wl, D=32, split=(8, 12, 12), base=1000.0):"),
+    "rope_axis_order": ("coords = [tt.reshape(-1), hh.reshape(-1), ww.reshape(-1)]",
+                        "coords = [ww.reshape(-1), hh.reshape(-1), tt.reshape(-1)]"),
+    "rope_freq_exponent": ("freq = base ** (-2.0 * k / width)", "freq = base ** (-1.0 * k / width)"),
+    "block_exclusive_mask": ("M = (idx[None, :] <= idx[:, None])", "M = (idx[None, :] < idx[:, None])"),
+    "block_state_not_carried": ("o, S, z = block_forward(q[..., sl, :], k[..., sl, :], v[..., sl, :], S, z,",
+                                "o, _S, _z = block_forward(q[..., sl, :], k[..., sl, :], v[..., sl, :], S, z,"),
+    "block_uses_previous_state_only": ("    o = apply_state(q, S_new, z_new, eps, angles, pos_offset)",
+                                       "    o = apply_state(q, np.asarray(S_in, dtype=np.float64), np.asarray(z_in, dtype=np.float64), eps, angles, pos_offset)"),
+    "block_positions_restart": ("eps, angles, start)", "eps, angles, 0)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name):
+    old, new = MUTANTS[name]
+    mod = _mutant(old, new)
+    failures = []
+    for pin in ALL_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(mod)
+        except (AssertionError, ValueError, IndexError, ZeroDivisionError, FloatingPointError) as exc:
+            failures.append(f"{pin.__name__}: {str(exc).splitlines()[0] if str(exc) else type(exc).__name__}")
+    assert failures, f"mutant {name} passed every pin"
