@@ -1,0 +1,163 @@
+/*
+ * sana_linattn.h -- C ABI of SANA's ReLU linear attention on MI355X (gfx950).
+ *
+ * The operation (phi = ReLU on queries and keys, D = head width):
+ *
+ *   per (batch b, head h):  S = sum_j phi(K_j)^T V_j   (D x D, row d = key feature,
+ *                                                        column e = value feature)
+ *                           z = sum_j phi(K_j)         (D)
+ *   per token i:            O_i = phi(Q_i) . S / (phi(Q_i) . z + eps)
+ *
+ * Sources (page title, section):
+ *   - "Sana: Efficient High-Resolution Image Synthesis with Linear Diffusion
+ *     Transformers" (research note), "Model architecture" item 2) Linear DiT:
+ *     ReLU linear attention whose shared sums sum ReLU(K_j)^T V_j and
+ *     sum ReLU(K_j) are computed once and reused by every query.
+ *   - "SANA-Video: Efficient Video Generation with Block Linear Diffusion
+ *     Transformer" (paper notes), section 2.1 (precomputed state, O(D^2) per
+ *     token), 2.2 (RoPE applied after the ReLU, left out of the denominator),
+ *     2.3 (constant-memory causal state: D x D state sum plus D x 1 key sum)
+ *     and 4 (block inference: denoising steps read the cache, a final pass on
+ *     the clean chunk commits it).
+ *   - SANA-Video news article (mjgaz.cn), "Design details": later blocks see
+ *     earlier ones, never the reverse; KV1 + KV2 -> KV1-2 ... -> KVsum, and
+ *     each block sums KVsum with its own KV.
+ *
+ * The pages print no normalisation formula (it is lost in the extraction); eps
+ * is added after the dot product, as written above.  There is no 1/sqrt(D)
+ * scale.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *   Layout     Q, K, V, O are contiguous [B][H][N][D] arrays, D innermost, in
+ *              device memory, each 16-byte aligned.  kv state is [B][H][D][D]
+ *              float (row = key feature, column = value feature), ksum state
+ *              is [B][H][D] float, both in device memory, 4-byte aligned.
+ *   Dtype      One dtype for Q, K, V and O (sana_dtype).  States, RoPE tables
+ *              and all accumulation are fp32.  bf16 results are rounded to
+ *              nearest-even once, at the store.
+ *   D          Only D = 32 (the head width of Sana-0.6B and Sana-1.6B) has
+ *              kernels; any other positive D returns SANA_ERR_UNSUPPORTED.
+ *   Ownership  The caller allocates and owns every buffer, the workspace
+ *              included.  The library never allocates, frees or synchronises;
+ *              it keeps no state between calls and is re-entrant.
+ *   Streams    Work is enqueued asynchronously on `hip_stream` (a
+ *              hipStream_t; NULL = the default stream) and the call returns
+ *              without waiting for it.
+ *   Workspace  `ws` is device scratch of at least
+ *              sana_linattn_workspace_bytes(...) bytes, 256-byte aligned, with
+ *              no initial contents required.  Calls that overlap in time must
+ *              use different workspaces.
+ *   Errors     Arguments are checked before anything is enqueued; on error
+ *              nothing is launched and a negative sana_status is returned:
+ *                SANA_ERR_INVALID      NULL pointer where work exists, B, H or
+ *                                      N negative, D <= 0, unknown dtype,
+ *                                      non-finite or negative eps, misaligned
+ *                                      pointer, O overlapping Q/K/V, RoPE rows
+ *                                      out of the table, size overflow
+ *                SANA_ERR_UNSUPPORTED  D != 32
+ *                SANA_ERR_WORKSPACE    ws NULL or ws_bytes too small
+ *                SANA_ERR_HIP          a launch reported a HIP error
+ *   Empty      B*H*N == 0 is a no-op returning SANA_OK (pointers unchecked).
+ *   RoPE       A NULL `rope` means no rotation.  Otherwise token n of every
+ *              head (global position pos_offset + n) rotates the interleaved
+ *              pairs (2p, 2p+1) of phi(Q_n) and phi(K_n) by the angle whose
+ *              cosine and sine are cos[pos][p] and sin[pos][p]:
+ *              (x0, x1) -> (x0 c - x1 s, x0 s + x1 c).  The rotation enters
+ *              the numerator only; z and the denominator stay un-rotated.
+ */
+#ifndef SANA_LINATTN_H
+#define SANA_LINATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SANA_OK = 0,
+    SANA_ERR_INVALID = -1,
+    SANA_ERR_UNSUPPORTED = -2,
+    SANA_ERR_WORKSPACE = -3,
+    SANA_ERR_HIP = -4
+} sana_status;
+
+typedef enum {
+    SANA_DT_F32 = 0,
+    SANA_DT_BF16 = 1
+} sana_dtype;
+
+/* RoPE tables: device pointers to [n_pos][D/2] fp32 arrays (16-byte aligned),
+ * pair p of position pos at [pos][p].  Rows pos_offset .. pos_offset+N-1 are
+ * read; they must lie inside the table. */
+typedef struct {
+    const float* cos;
+    const float* sin;
+    int64_t n_pos;
+    int64_t pos_offset;
+} sana_rope;
+
+/* Bytes of device workspace that the three compute entry points need for
+ * these sizes (0 when B*H*N == 0).  Pure host function, no HIP call.  Returns
+ * 0 as well for invalid sizes; the entry points then reject the sizes. */
+size_t sana_linattn_workspace_bytes(int B, int H, int64_t N, int D, int dtype, int has_rope);
+
+/* Non-causal forward ("Sana" research note, Model architecture item 2;
+ * "SANA-Video" paper notes 2.1, 2.2):
+ *   O_i = phi~(Q_i) . S / (phi(Q_i) . z + eps) with S, z summed over all N
+ *   tokens of the same (b, h).  phi~ is phi rotated by `rope` (positions
+ *   pos_offset .. pos_offset+N-1), or phi itself when rope is NULL.
+ * q, k, v: inputs [B][H][N][D]; o: output, same shape and dtype, must not
+ * overlap q, k or v. */
+int sana_linattn_forward(const void* q, const void* k, const void* v, void* o,
+                         int B, int H, int64_t N, int D, int dtype, float eps,
+                         const sana_rope* rope, void* ws, size_t ws_bytes, void* hip_stream);
+
+/* Commit N tokens into a carried state, without outputs ("SANA-Video" paper
+ * notes 2.3 and 4; news article "Design details", KV1 + KV2 -> KV1-2):
+ *   kv_state[b][h]   += sum_j phi~(K_j)^T V_j
+ *   ksum_state[b][h] += sum_j phi(K_j)
+ * k, v: inputs [B][H][N][D]; kv_state, ksum_state: read and updated in place.
+ * With rope, key j is rotated at position pos_offset + j; ksum never is. */
+int sana_linattn_state_update(const void* k, const void* v, float* kv_state, float* ksum_state,
+                              int B, int H, int64_t N, int D, int dtype,
+                              const sana_rope* rope, void* ws, size_t ws_bytes, void* hip_stream);
+
+/* One chunk of block-causal attention ("SANA-Video" paper notes 2.3 and 4;
+ * news article "Design details"): the chunk's queries see the state carried
+ * from earlier chunks plus every token of the chunk itself.
+ *   S_new = kv_in + sum_{j in chunk} phi~(K_j)^T V_j,   z_new = ksum_in + sum phi(K_j)
+ *   O_i   = phi~(Q_i) . S_new / (phi(Q_i) . z_new + eps)
+ * kv_in/ksum_in: state of earlier chunks, or both NULL for a zero state (first
+ * chunk).  kv_out/ksum_out: where S_new/z_new are committed, or both NULL to
+ * leave the carried state untouched (a denoising step that only reads the
+ * cache).  kv_out may equal kv_in and ksum_out may equal ksum_in (in-place
+ * commit); no other overlap between state buffers and q/k/v/o is allowed.
+ * With rope, the chunk's token n sits at global position pos_offset + n. */
+int sana_linattn_block_forward(const void* q, const void* k, const void* v, void* o,
+                               const float* kv_in, const float* ksum_in,
+                               float* kv_out, float* ksum_out,
+                               int B, int H, int64_t N, int D, int dtype, float eps,
+                               const sana_rope* rope, void* ws, size_t ws_bytes, void* hip_stream);
+
+/* Host-side builder of 3D RoPE tables ("SANA-Video" paper notes, section 3
+ * Stage 2, rotary position encoding extended to space-time).  Token
+ * n = (t*Hl + h)*Wl + w; the first dt dims (dt/2 pairs) turn with t, the next
+ * dh with h, the last dw with w; pair k of an axis of width d_a turns by
+ * coordinate * base^(-2k/d_a).  Angles are formed in double precision and
+ * their cosine and sine rounded to float.  cos_host, sin_host: host arrays of
+ * T*Hl*Wl*(D/2) floats, written row-major [n][p].  dt, dh, dw must be even,
+ * non-negative and sum to D. */
+int sana_linattn_rope3d_table(int T, int Hl, int Wl, int D, int dt, int dh, int dw, double base,
+                              float* cos_host, float* sin_host);
+
+/* Static string naming a status code. */
+const char* sana_linattn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SANA_LINATTN_H */

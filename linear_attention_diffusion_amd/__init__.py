@@ -1,0 +1,28 @@
+"""SANA ReLU linear attention on MI355X (gfx950): HIP kernels behind a C ABI.
+
+Entry points (same names as the C ABI in include/sana_linattn.h):
+  sana_linattn_forward, sana_linattn_state_update, sana_linattn_block_forward,
+  rope3d_table / rope3d_device (host builder of the 3D RoPE tables).
+"""
+
+from .binding import (  # noqa: F401
+    EXPORTED,
+    SANA_DT_BF16,
+    SANA_DT_F32,
+    SANA_ERR_HIP,
+    SANA_ERR_INVALID,
+    SANA_ERR_UNSUPPORTED,
+    SANA_ERR_WORKSPACE,
+    SANA_OK,
+    Rope,
+    SanaError,
+    lib,
+    make_workspace,
+    rope3d_device,
+    rope3d_table,
+    sana_linattn_block_forward,
+    sana_linattn_forward,
+    sana_linattn_state_update,
+    sana_linattn_status_string,
+    workspace_bytes,
+)

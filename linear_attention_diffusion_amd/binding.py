@@ -1,0 +1,232 @@
+"""ctypes binding of libsana_linattn.so.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI (include/sana_linattn.h).  torch supplies device
+memory and the stream handle.  There is no CPU fallback: if the library is
+missing, loading raises.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+
+from .build import LIB_PATH
+
+SANA_OK, SANA_ERR_INVALID, SANA_ERR_UNSUPPORTED, SANA_ERR_WORKSPACE, SANA_ERR_HIP = 0, -1, -2, -3, -4
+SANA_DT_F32, SANA_DT_BF16 = 0, 1
+
+EXPORTED = (
+    "sana_linattn_workspace_bytes",
+    "sana_linattn_forward",
+    "sana_linattn_state_update",
+    "sana_linattn_block_forward",
+    "sana_linattn_rope3d_table",
+    "sana_linattn_status_string",
+)
+
+
+class sana_rope(ctypes.Structure):
+    _fields_ = [("cos", ctypes.c_void_p), ("sin", ctypes.c_void_p),
+                ("n_pos", ctypes.c_int64), ("pos_offset", ctypes.c_int64)]
+
+
+_LIB = None
+
+
+def lib():
+    """Load the library once and declare the C prototypes."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built: run __graft_entry__.build() "
+                          "(or python -m linear_attention_diffusion_amd.build) first")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    rp = ctypes.POINTER(sana_rope)
+    L.sana_linattn_workspace_bytes.argtypes = [i32, i32, i64, i32, i32, i32]
+    L.sana_linattn_workspace_bytes.restype = sz
+    L.sana_linattn_forward.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32, i32, f32, rp, vp, sz, vp]
+    L.sana_linattn_forward.restype = i32
+    L.sana_linattn_state_update.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32, i32, rp, vp, sz, vp]
+    L.sana_linattn_state_update.restype = i32
+    L.sana_linattn_block_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, f32,
+                                             rp, vp, sz, vp]
+    L.sana_linattn_block_forward.restype = i32
+    L.sana_linattn_rope3d_table.argtypes = [i32, i32, i32, i32, i32, i32, i32, ctypes.c_double, vp, vp]
+    L.sana_linattn_rope3d_table.restype = i32
+    L.sana_linattn_status_string.argtypes = [i32]
+    L.sana_linattn_status_string.restype = ctypes.c_char_p
+    _LIB = L
+    return L
+
+
+class SanaError(RuntimeError):
+    def __init__(self, code):
+        self.code = code
+        super().__init__(lib().sana_linattn_status_string(code).decode())
+
+
+def _check(code):
+    if code != SANA_OK:
+        raise SanaError(code)
+
+
+def sana_linattn_status_string(code):
+    return lib().sana_linattn_status_string(code).decode()
+
+
+# --------------------------------------------------------------------------
+# torch marshalling
+# --------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return SANA_DT_BF16
+    if t.dtype == torch.float32:
+        return SANA_DT_F32
+    raise TypeError(f"unsupported dtype {t.dtype}: Q, K, V, O must be bfloat16 or float32")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _shape4(t, name):
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be [B, H, N, D], got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return tuple(t.shape)
+
+
+def _stream(stream, device):
+    if stream is not None:
+        return ctypes.c_void_p(stream if isinstance(stream, int) else stream.cuda_stream)
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+class Rope:
+    """Device RoPE tables [n_pos, D/2] (float32) and the position of token 0."""
+
+    def __init__(self, cos, sin, pos_offset=0):
+        torch = _torch()
+        if cos.shape != sin.shape or cos.dim() != 2:
+            raise ValueError("cos and sin must both be [n_pos, D/2]")
+        if cos.dtype != torch.float32 or sin.dtype != torch.float32:
+            raise TypeError("RoPE tables are float32")
+        if not (cos.is_cuda and sin.is_cuda and cos.is_contiguous() and sin.is_contiguous()):
+            raise ValueError("RoPE tables must be contiguous device tensors")
+        self.cos, self.sin, self.pos_offset = cos, sin, int(pos_offset)
+
+    def at(self, pos_offset):
+        return Rope(self.cos, self.sin, pos_offset)
+
+    def struct(self):
+        return sana_rope(self.cos.data_ptr(), self.sin.data_ptr(), self.cos.shape[0], self.pos_offset)
+
+
+def _rope_arg(rope):
+    return None if rope is None else ctypes.byref(rope.struct())
+
+
+def rope3d_table(T, Hl, Wl, D=32, split=(8, 12, 12), base=10000.0):
+    """Host 3D RoPE tables (numpy float32 cos, sin of shape [T*Hl*Wl, D/2])."""
+    n = T * Hl * Wl
+    cos = np.empty((n, D // 2), np.float32)
+    sin = np.empty((n, D // 2), np.float32)
+    _check(lib().sana_linattn_rope3d_table(T, Hl, Wl, D, split[0], split[1], split[2], float(base),
+                                           cos.ctypes.data_as(ctypes.c_void_p),
+                                           sin.ctypes.data_as(ctypes.c_void_p)))
+    return cos, sin
+
+
+def rope3d_device(T, Hl, Wl, device, D=32, split=(8, 12, 12), base=10000.0):
+    torch = _torch()
+    cos, sin = rope3d_table(T, Hl, Wl, D, split, base)
+    return Rope(torch.from_numpy(cos).to(device), torch.from_numpy(sin).to(device))
+
+
+def workspace_bytes(B, H, N, D=32, dtype=SANA_DT_BF16, has_rope=False):
+    return int(lib().sana_linattn_workspace_bytes(B, H, N, D, dtype, int(bool(has_rope))))
+
+
+def make_workspace(B, H, N, device, D=32, dtype=SANA_DT_BF16, has_rope=False):
+    torch = _torch()
+    n = workspace_bytes(B, H, N, D, dtype, has_rope)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def _workspace(ws, B, H, N, D, dt, has_rope, device):
+    if ws is None:
+        ws = make_workspace(B, H, N, device, D, dt, has_rope)
+    return ws, ws.numel() * ws.element_size()
+
+
+def sana_linattn_forward(q, k, v, o=None, eps=1e-6, rope=None, workspace=None, stream=None):
+    """Non-causal ReLU linear attention; returns O (allocated if not given)."""
+    torch = _torch()
+    B, H, N, D = _shape4(q, "q")
+    if _shape4(k, "k") != (B, H, N, D) or _shape4(v, "v") != (B, H, N, D):
+        raise ValueError("q, k, v must have the same shape")
+    if o is None:
+        o = torch.empty_like(q)
+    elif _shape4(o, "o") != (B, H, N, D) or o.dtype != q.dtype:
+        raise ValueError("o must match q in shape and dtype")
+    dt = _dtype_code(q)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    ws, nbytes = _workspace(workspace, B, H, N, D, dt, rope is not None, q.device)
+    _check(lib().sana_linattn_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, N, D, dt, float(eps),
+                                      _rope_arg(rope), _ptr(ws), nbytes, _stream(stream, q.device)))
+    return o
+
+
+def sana_linattn_state_update(k, v, kv_state, ksum_state, rope=None, workspace=None, stream=None):
+    """kv_state += sum phi~(K)^T V, ksum_state += sum phi(K), in place."""
+    torch = _torch()
+    B, H, N, D = _shape4(k, "k")
+    if _shape4(v, "v") != (B, H, N, D) or v.dtype != k.dtype:
+        raise ValueError("k and v must match")
+    if tuple(kv_state.shape) != (B, H, D, D) or tuple(ksum_state.shape) != (B, H, D):
+        raise ValueError("kv_state must be [B, H, D, D] and ksum_state [B, H, D]")
+    for t in (kv_state, ksum_state):
+        if t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("states must be contiguous float32 device tensors")
+    dt = _dtype_code(k)
+    ws, nbytes = _workspace(workspace, B, H, N, D, dt, rope is not None, k.device)
+    _check(lib().sana_linattn_state_update(_ptr(k), _ptr(v), _ptr(kv_state), _ptr(ksum_state), B, H, N, D, dt,
+                                           _rope_arg(rope), _ptr(ws), nbytes, _stream(stream, k.device)))
+
+
+def sana_linattn_block_forward(q, k, v, o=None, kv_in=None, ksum_in=None, kv_out=None, ksum_out=None,
+                               eps=1e-6, rope=None, workspace=None, stream=None):
+    """One block-causal chunk; returns O.  kv_in/ksum_in None = zero state;
+    kv_out/ksum_out None = do not commit."""
+    torch = _torch()
+    B, H, N, D = _shape4(q, "q")
+    if _shape4(k, "k") != (B, H, N, D) or _shape4(v, "v") != (B, H, N, D):
+        raise ValueError("q, k, v must have the same shape")
+    if o is None:
+        o = torch.empty_like(q)
+    elif _shape4(o, "o") != (B, H, N, D) or o.dtype != q.dtype:
+        raise ValueError("o must match q in shape and dtype")
+    for t, shape in ((kv_in, (B, H, D, D)), (ksum_in, (B, H, D)), (kv_out, (B, H, D, D)), (ksum_out, (B, H, D))):
+        if t is not None and (tuple(t.shape) != shape or t.dtype != torch.float32 or not t.is_contiguous()):
+            raise ValueError("states must be contiguous float32 [B, H, D, D] / [B, H, D]")
+    dt = _dtype_code(q)
+    ws, nbytes = _workspace(workspace, B, H, N, D, dt, rope is not None, q.device)
+    _check(lib().sana_linattn_block_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(kv_in), _ptr(ksum_in),
+                                            _ptr(kv_out), _ptr(ksum_out), B, H, N, D, dt, float(eps),
+                                            _rope_arg(rope), _ptr(ws), nbytes, _stream(stream, q.device)))
+    return o

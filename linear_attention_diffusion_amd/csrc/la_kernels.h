@@ -1,0 +1,669 @@
+// HIP kernels (gfx950 / CDNA4) of SANA's ReLU linear attention.
+//
+// The method (phi = ReLU):
+//   state pass   S = sum_j phi~(K_j)^T V_j, z = sum_j phi(K_j) per (batch, head)
+//   apply pass   O_i = phi~(Q_i).S / (phi(Q_i).z + eps)
+// "Sana: Efficient High-Resolution Image Synthesis with Linear Diffusion
+// Transformers" (research note), Model architecture item 2) Linear DiT: the
+// two shared sums are computed once and reused by every query.  "SANA-Video"
+// paper notes 2.2: RoPE (phi~) is applied after the ReLU and only in the
+// numerator; 2.3: the carried state is the running sum of S and z.
+//
+// Data layout: Q, K, V, O are [BH][N][32] with the 32 features contiguous
+// (64-byte rows in bf16).  Partial states are [BH][P][33][32] fp32: rows 0..31
+// hold S[d][e], row 32 holds z[d].  States are kv [BH][32][32] + ksum [BH][32].
+//
+// bf16 kernels put both 32-wide contractions on v_mfma_f32_16x16x32_bf16:
+//   A (16x32) lane l holds row (l % 16), k-slice group (l / 16), 8 values;
+//   B (32x16) lane l holds column (l % 16), k-slice group (l / 16), 8 values;
+//   D (16x16) lane l holds column (l % 16), rows 4*(l / 16) + i, i = 0..3.
+// The contraction pairs A slot (group, s) with B slot (group, s), so any
+// assignment of physical indices to (group, slot) works as long as A and B use
+// the same one; the kernels choose assignments that make every global load
+// and store a contiguous 16-byte (apply) or 4-byte (state) lane access.
+//
+// Precision: bf16 x bf16 products are exact in fp32 and MFMA accumulates in
+// fp32.  fp32 operands (the state in the apply pass, rotated features under
+// RoPE) are split into three bf16 parts, x = hi + mid + lo, which is exact for
+// any normal fp32 value (3 x 8 significant bits), and contracted with one MFMA
+// per product term kept: with one exact bf16 operand that is 3 terms; with two
+// split operands the 6 terms of weight >= 2^-16 (hh, hm, mh, hl, lh, mm).
+//
+// Reduction of the split-N partials: every state workgroup writes its partial
+// (or, when a head has a single split, the finished state); a separate
+// finalize kernel then sums each head's P partials in split order
+// (deterministic) plus the carried state.  The kernel boundary makes the
+// partials visible across all XCDs; an in-kernel hand-off would need an L2
+// write-back per publishing wave, which costs far more at this grid size.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace la {
+
+constexpr int kD = 32;               // head width (features per token)
+constexpr int kStateElems = 33 * 32; // S (32x32) + z (32) per partial / state
+constexpr int kThreads = 256;        // 4 wave64 per workgroup
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x2_t __attribute__((ext_vector_type(2)));
+
+// Where a state pass puts its result.
+struct StateArgs {
+  float* partials;                 // [BH][P][33][32] scratch (P > 1)
+  const float* kv_in;              // carried state [BH][32][32] or null (zero)
+  const float* ksum_in;            // [BH][32] or null
+  float* kv_out;                   // S_new destination [BH][32][32] (may equal kv_in)
+  float* ksum_out;                 // z_new destination [BH][32] (may equal ksum_in)
+  int P;                           // partials per head
+};
+
+// ---------------------------------------------------------------------------
+// bf16 helpers
+// ---------------------------------------------------------------------------
+
+// ReLU of two packed bf16: a bf16 with the sign bit set is a negative int16,
+// so a signed 16-bit max against 0 clears it (and maps -0 to +0).
+__device__ __forceinline__ unsigned relu_bf16x2(unsigned x) {
+  const s16x2_t zero = {0, 0};
+  return __builtin_bit_cast(unsigned, __builtin_elementwise_max(__builtin_bit_cast(s16x2_t, x), zero));
+}
+
+__device__ __forceinline__ float bf16lo_to_f32(unsigned x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float bf16hi_to_f32(unsigned x) { return __uint_as_float(x & 0xffff0000u); }
+
+// Two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
+  const bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(unsigned, v);
+}
+
+// x = hi + mid + lo with hi = bf16(x), mid = bf16(x - hi), lo = bf16(x - hi - mid);
+// each residual is exact in fp32.  Called for a pair (a, b), each part comes
+// back as one dword of two packed bf16.
+__device__ __forceinline__ void split3_bf16x2(float a, float b, unsigned& hi, unsigned& mid, unsigned& lo) {
+  hi = pack_bf16x2(a, b);
+  const float ra = a - bf16lo_to_f32(hi), rb = b - bf16hi_to_f32(hi);
+  mid = pack_bf16x2(ra, rb);
+  lo = pack_bf16x2(ra - bf16lo_to_f32(mid), rb - bf16hi_to_f32(mid));
+}
+
+__device__ __forceinline__ unsigned lo_halves(unsigned a, unsigned b) { return (a & 0xffffu) | (b << 16); }
+__device__ __forceinline__ unsigned hi_halves(unsigned a, unsigned b) { return (a >> 16) | (b & 0xffff0000u); }
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(unsigned a, unsigned b, unsigned c, unsigned d) {
+  const u32x4_t v = {a, b, c, d};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// even (low) halves of 8 dwords as 8 bf16, and odd (high) halves
+__device__ __forceinline__ bf16x8_t even8(const unsigned (&x)[8]) {
+  return as_bf16x8(lo_halves(x[0], x[1]), lo_halves(x[2], x[3]), lo_halves(x[4], x[5]), lo_halves(x[6], x[7]));
+}
+__device__ __forceinline__ bf16x8_t odd8(const unsigned (&x)[8]) {
+  return as_bf16x8(hi_halves(x[0], x[1]), hi_halves(x[2], x[3]), hi_halves(x[4], x[5]), hi_halves(x[6], x[7]));
+}
+
+__device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Writing a workgroup's partial state, and the finalize kernel
+// ---------------------------------------------------------------------------
+
+// S_in + x into the state destination, element idx of the 33 x 32 layout.
+__device__ __forceinline__ void store_state(const StateArgs& a, int64_t bh, int idx, float x) {
+  if (idx < 1024) {
+    if (a.kv_in) x = a.kv_in[bh * 1024 + idx] + x;
+    a.kv_out[bh * 1024 + idx] = x;
+  } else {
+    if (a.ksum_in) x = a.ksum_in[bh * 32 + (idx - 1024)] + x;
+    a.ksum_out[bh * 32 + (idx - 1024)] = x;
+  }
+}
+
+// `mine` (LDS, 33x32 floats) holds this workgroup's sum for head bh, split s.
+// With one split per head it is already the head's sum and goes straight to
+// the destination; otherwise it is stored as partial s.
+__device__ __forceinline__ void write_partial(const float* mine, int64_t bh, int s, const StateArgs& a) {
+  if (a.P == 1) {
+    for (int idx = threadIdx.x; idx < kStateElems; idx += kThreads) store_state(a, bh, idx, mine[idx]);
+  } else {
+    float* out = a.partials + ((int64_t)bh * a.P + s) * kStateElems;
+    for (int idx = threadIdx.x; idx < kStateElems; idx += kThreads) out[idx] = mine[idx];
+  }
+}
+
+// One thread per state element of every head: S_new = S_in + sum_s partial_s,
+// summed in split order.  A thread issues the loads of 16 partials at once
+// (the ones past P read as 0, which leaves the ordered sum unchanged) before
+// its first add.  kv_out may alias kv_in: each element is read and written by
+// the same thread.
+__global__ __launch_bounds__(kThreads) void state_finalize(StateArgs a, int64_t n_elems) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= n_elems) return;
+  const int64_t bh = i / kStateElems;
+  const int idx = (int)(i % kStateElems);
+  const float* src = a.partials + bh * a.P * kStateElems + idx;
+  float acc = 0.f;
+  for (int sp = 0; sp < a.P; sp += 16) {
+    float v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v[u] = (sp + u < a.P) ? src[(int64_t)(sp + u) * kStateElems] : 0.f;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) acc += v[u];
+  }
+  store_state(a, bh, idx, acc);
+}
+
+// ---------------------------------------------------------------------------
+// bf16 state pass: split-N partial S and z with MFMA
+// ---------------------------------------------------------------------------
+//
+// One workgroup reduces tokens [s*Ls, min(N, (s+1)*Ls)) of one (batch, head);
+// its four waves take 32-token tiles, two at a time.
+//
+// The contraction runs over tokens, but rows in memory are token-major.  Each
+// lane therefore loads whole-row pieces -- lane l (n = l % 16, g = l / 16)
+// reads the 16 bytes holding features 8g .. 8g+7 of token t0 + 16tb + n, so a
+// wave reads 16 rows (1 KB contiguous) per load -- and the rows are turned
+// around on the matrix core: with the tile as A (row = token, k = feature) and
+// a 0/1 selection matrix E_fh as B (E_fh[k][c] = [k == 16fh + c]), the MFMA
+// returns D[token][c] = X[token][16fh + c] in the D layout, i.e. lane (n, g)
+// holds feature 16fh + n of tokens t0 + 16tb + 4g + i, i = 0..3.  The values
+// are bf16 times 1.0, so the turn-around is exact.  Packed back to bf16,
+// those are exactly the operands of the token contraction:
+//   A_fh (rows = key features 16fh + n, k-slots = the lane group's 8 tokens)
+//   B_fh (columns = value features 16fh + n, same token slots)
+// and S[16fh + 4g + i][16fh' + n] accumulates in MFMA (fh, fh').  Two more
+// MFMAs against a B of ones give z.
+//
+// Under RoPE the rotation acts on pairs (2p, 2p+1) of a token, which a lane
+// holds together before the turn-around: the lane rotates its 4 pairs in fp32
+// with 16-byte cos/sin loads, splits the result into three bf16 parts, and
+// each part is turned around and contracted separately.  z always comes from
+// the un-rotated phi(K).
+
+// E_fh as the B operand of lane (n, g): slot s is 1.0 where 8g + s == 16fh + n
+__device__ __forceinline__ bf16x8_t select_operand(int g, int n, int fh) {
+  unsigned d[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int k = 8 * g + 2 * p;
+    d[p] = (k == 16 * fh + n ? 0x3f80u : 0u) | (k + 1 == 16 * fh + n ? 0x3f800000u : 0u);
+  }
+  return as_bf16x8(d[0], d[1], d[2], d[3]);
+}
+
+// Turned-around tile halves (tb = 0, 1) of feature half fh -> bf16 operand
+__device__ __forceinline__ bf16x8_t turned_operand(bf16x8_t x0, bf16x8_t x1, bf16x8_t sel) {
+  const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+  const f32x4_t t0 = mfma16(x0, sel, zero4);
+  const f32x4_t t1 = mfma16(x1, sel, zero4);
+  return as_bf16x8(pack_bf16x2(t0[0], t0[1]), pack_bf16x2(t0[2], t0[3]), pack_bf16x2(t1[0], t1[1]),
+                   pack_bf16x2(t1[2], t1[3]));
+}
+
+__device__ __forceinline__ u32x4_t relu_bf16x8(u32x4_t x) {
+  x[0] = relu_bf16x2(x[0]);
+  x[1] = relu_bf16x2(x[1]);
+  x[2] = relu_bf16x2(x[2]);
+  x[3] = relu_bf16x2(x[3]);
+  return x;
+}
+
+// acc[fh][fh']: S blocks (key half fh, value half fh'); accz[fh]: z of key half fh
+template <bool ROPE>
+__device__ __forceinline__ void state_tile(const u32x4_t (&kx)[2], const u32x4_t (&vx)[2], int64_t t0,
+                                           int64_t n_end, int g, int n, const float* cos_t, const float* sin_t,
+                                           int64_t pos0, const bf16x8_t (&sel)[2], f32x4_t (&acc)[2][2],
+                                           f32x4_t (&accz)[2]) {
+  const unsigned one2 = 0x3f803f80u;  // two bf16 1.0
+  const bf16x8_t ones = as_bf16x8(one2, one2, one2, one2);
+  bf16x8_t k_nat[2], v_nat[2];
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb) {
+    k_nat[tb] = __builtin_bit_cast(bf16x8_t, relu_bf16x8(kx[tb]));
+    v_nat[tb] = __builtin_bit_cast(bf16x8_t, vx[tb]);
+  }
+  bf16x8_t a[2], b[2];
+#pragma unroll
+  for (int fh = 0; fh < 2; ++fh) {
+    a[fh] = turned_operand(k_nat[0], k_nat[1], sel[fh]);
+    b[fh] = turned_operand(v_nat[0], v_nat[1], sel[fh]);
+  }
+#pragma unroll
+  for (int fh = 0; fh < 2; ++fh) accz[fh] = mfma16(a[fh], ones, accz[fh]);
+  if constexpr (!ROPE) {
+#pragma unroll
+    for (int fh = 0; fh < 2; ++fh) {
+      acc[fh][0] = mfma16(a[fh], b[0], acc[fh][0]);
+      acc[fh][1] = mfma16(a[fh], b[1], acc[fh][1]);
+    }
+  } else {
+    // rotate the lane's pairs 4g .. 4g+3 of token t0 + 16tb + n, split in three parts
+    unsigned part[3][2][4];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      const int64_t tok = t0 + 16 * tb + n;
+      f32x4_t c = {1.f, 1.f, 1.f, 1.f}, sn = {0.f, 0.f, 0.f, 0.f};
+      if (tok < n_end) {
+        c = *reinterpret_cast<const f32x4_t*>(cos_t + (pos0 + tok) * 16 + 4 * g);
+        sn = *reinterpret_cast<const f32x4_t*>(sin_t + (pos0 + tok) * 16 + 4 * g);
+      }
+      const u32x4_t kr = relu_bf16x8(kx[tb]);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const float x0 = bf16lo_to_f32(kr[p]);
+        const float x1 = bf16hi_to_f32(kr[p]);
+        split3_bf16x2(x0 * c[p] - x1 * sn[p], x0 * sn[p] + x1 * c[p], part[0][tb][p], part[1][tb][p],
+                      part[2][tb][p]);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+#pragma unroll
+      for (int fh = 0; fh < 2; ++fh) {
+        const unsigned(&p0)[4] = part[k][0];
+        const unsigned(&p1)[4] = part[k][1];
+        const bf16x8_t ar = turned_operand(as_bf16x8(p0[0], p0[1], p0[2], p0[3]),
+                                           as_bf16x8(p1[0], p1[1], p1[2], p1[3]), sel[fh]);
+        acc[fh][0] = mfma16(ar, b[0], acc[fh][0]);
+        acc[fh][1] = mfma16(ar, b[1], acc[fh][1]);
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void load_rows(const u32x4_t* X, int64_t t0, int64_t n_end, u32x4_t (&x)[2]) {
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb) {
+    const int64_t tok = t0 + 16 * tb;
+    x[tb] = u32x4_t{0u, 0u, 0u, 0u};
+    // streamed once: non-temporal
+    if (tok < n_end) x[tb] = __builtin_nontemporal_load(&X[tok * 4]);
+  }
+}
+
+template <bool ROPE>
+__global__ __launch_bounds__(kThreads) void state_bf16(const u32x4_t* __restrict__ K, const u32x4_t* __restrict__ V,
+                                                       int64_t N, int64_t Ls, const float* __restrict__ cos_t,
+                                                       const float* __restrict__ sin_t, int64_t pos0,
+                                                       StateArgs a) {
+  __shared__ float red[4][kStateElems];
+
+  const int64_t bh = blockIdx.x / a.P;
+  const int s = blockIdx.x % a.P;
+  const int64_t n_begin = (int64_t)s * Ls;
+  const int64_t n_end = (n_begin + Ls < N) ? n_begin + Ls : N;
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int n = lane & 15;
+  const int g = lane >> 4;
+
+  // lane's 16-byte piece of row (token): features 8g .. 8g+7, i.e. X[tok * 4]
+  // below is relative to token n of the tile
+  const u32x4_t* Kh = K + (bh * N + n) * 4 + g;
+  const u32x4_t* Vh = V + (bh * N + n) * 4 + g;
+  const int64_t n_end_lane = n_end - n;  // token t0 + n is live iff t0 < n_end_lane
+
+  const bf16x8_t sel[2] = {select_operand(g, n, 0), select_operand(g, n, 1)};
+  f32x4_t acc[2][2], accz[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    accz[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    acc[i][0] = accz[i];
+    acc[i][1] = accz[i];
+  }
+
+  // each wave takes 64-token chunks (two 32-token tiles); the next chunk's
+  // loads are issued before the current chunk is computed
+  int64_t t0 = n_begin + 64 * w;
+  u32x4_t nk[4], nv[4];
+  auto load_chunk = [&](int64_t c0) {
+    u32x4_t x[2];
+    load_rows(Kh, c0, n_end_lane, x);
+    nk[0] = x[0];
+    nk[1] = x[1];
+    load_rows(Vh, c0, n_end_lane, x);
+    nv[0] = x[0];
+    nv[1] = x[1];
+    load_rows(Kh, c0 + 32, n_end_lane, x);
+    nk[2] = x[0];
+    nk[3] = x[1];
+    load_rows(Vh, c0 + 32, n_end_lane, x);
+    nv[2] = x[0];
+    nv[3] = x[1];
+  };
+  if (t0 < n_end) load_chunk(t0);
+  for (; t0 < n_end; t0 += 256) {
+    const u32x4_t ka[2] = {nk[0], nk[1]}, va[2] = {nv[0], nv[1]};
+    const u32x4_t kb[2] = {nk[2], nk[3]}, vb[2] = {nv[2], nv[3]};
+    if (t0 + 256 < n_end) load_chunk(t0 + 256);
+    state_tile<ROPE>(ka, va, t0, n_end, g, n, cos_t, sin_t, pos0, sel, acc, accz);
+    if (t0 + 32 < n_end) state_tile<ROPE>(kb, vb, t0 + 32, n_end, g, n, cos_t, sin_t, pos0, sel, acc, accz);
+  }
+
+  // D lane (n, g): rows 4g + i -> key feature 16fh + 4g + i, column n -> value feature 16fh' + n
+  float* rw = red[w];
+#pragma unroll
+  for (int fh = 0; fh < 2; ++fh) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d = 16 * fh + 4 * g + i;
+      rw[d * 32 + n] = acc[fh][0][i];
+      rw[d * 32 + 16 + n] = acc[fh][1][i];
+      if (n == 0) rw[1024 + d] = accz[fh][i];
+    }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < kStateElems; idx += kThreads)
+    red[0][idx] = (red[0][idx] + red[1][idx]) + (red[2][idx] + red[3][idx]);
+  __syncthreads();
+  write_partial(red[0], bh, s, a);
+}
+
+// ---------------------------------------------------------------------------
+// fp32 state pass (VALU): each thread owns S[d][e0..e0+3] (and z[d])
+// ---------------------------------------------------------------------------
+template <bool ROPE>
+__global__ __launch_bounds__(kThreads) void state_f32(const float* __restrict__ K, const float* __restrict__ V,
+                                                      int64_t N, int64_t Ls, const float* __restrict__ cos_t,
+                                                      const float* __restrict__ sin_t, int64_t pos0,
+                                                      StateArgs a) {
+  __shared__ float sk[64][kD + 1];   // phi(K), un-rotated
+  __shared__ float skr[64][kD + 1];  // phi~(K), rotated (RoPE only)
+  __shared__ float sv[64][kD + 1];
+  __shared__ float mine[kStateElems];
+
+  const int64_t bh = blockIdx.x / a.P;
+  const int s = blockIdx.x % a.P;
+  const int64_t n_begin = (int64_t)s * Ls;
+  const int64_t n_end = (n_begin + Ls < N) ? n_begin + Ls : N;
+  const int t = threadIdx.x;
+  const int d = t >> 3;
+  const int e0 = (t & 7) * 4;
+  const float* Kh = K + bh * N * kD;
+  const float* Vh = V + bh * N * kD;
+
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  float zacc = 0.f;
+  for (int64_t t0 = n_begin; t0 < n_end; t0 += 64) {
+    // 64 tokens x 16 pairs = 1024 pairs, 4 per thread
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int pidx = t + kThreads * i;
+      const int tok = pidx >> 4;
+      const int p = pidx & 15;
+      const int64_t gt = t0 + tok;
+      float k0 = 0.f, k1 = 0.f, v0 = 0.f, v1 = 0.f;
+      if (gt < n_end) {
+        k0 = fmaxf(Kh[gt * kD + 2 * p], 0.f);
+        k1 = fmaxf(Kh[gt * kD + 2 * p + 1], 0.f);
+        v0 = Vh[gt * kD + 2 * p];
+        v1 = Vh[gt * kD + 2 * p + 1];
+      }
+      sk[tok][2 * p] = k0;
+      sk[tok][2 * p + 1] = k1;
+      sv[tok][2 * p] = v0;
+      sv[tok][2 * p + 1] = v1;
+      if constexpr (ROPE) {
+        float c = 1.f, sn = 0.f;
+        if (gt < n_end) {
+          c = cos_t[(pos0 + gt) * 16 + p];
+          sn = sin_t[(pos0 + gt) * 16 + p];
+        }
+        skr[tok][2 * p] = k0 * c - k1 * sn;
+        skr[tok][2 * p + 1] = k0 * sn + k1 * c;
+      }
+    }
+    __syncthreads();
+    for (int j = 0; j < 64; ++j) {
+      const float x = ROPE ? skr[j][d] : sk[j][d];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[c] = fmaf(x, sv[j][e0 + c], acc[c]);
+      zacc += sk[j][d];
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) mine[d * 32 + e0 + c] = acc[c];
+  if (e0 == 0) mine[1024 + d] = zacc;
+  __syncthreads();
+  write_partial(mine, bh, s, a);
+}
+
+// ---------------------------------------------------------------------------
+// bf16 apply pass: O = phi~(Q).S / (phi(Q).z + eps) with MFMA
+// ---------------------------------------------------------------------------
+//
+// Computed transposed, O^T (32 e x 16 tokens) = S^T (32 e x 32 d) . phi(Q)^T.
+// Lane l (m = l % 16, g = l / 16) loads the 16 bytes holding features
+// 8g .. 8g+7 of token t0 + m, so one load instruction of the wave reads 16
+// whole rows (1 KB contiguous).  Slot s of group g is feature d = 8g + s.
+// The 32 output features are two MFMAs of 16 rows; MFMA h row r maps to
+// e = 8(r / 4) + 4h + (r % 4), so lane l ends with e = 8g .. 8g+7 of its token
+// and stores them as one 16-byte write.  A third MFMA group whose rows all hold
+// z gives the denominator of the lane's token in every accumulator.
+//
+// Work split: the B*H*N tokens, flattened head-major, are cut into equal
+// contiguous ranges, one per workgroup; a range that crosses a head boundary
+// is processed head segment by head segment.  Each wave takes 64-token chunks
+// (four 16-token tiles, four loads in flight) of the current segment.
+
+struct ApplyOperands {
+  bf16x8_t s[2][3];  // S^T rows for output halves h = 0, 1; three bf16 parts
+  bf16x8_t z[3];     // z in every row; three bf16 parts
+};
+
+__device__ __forceinline__ void load_apply_operands(const float* S, const float* z, int g, int m,
+                                                    ApplyOperands& op) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int e = 8 * (m >> 2) + 4 * h + (m & 3);
+    unsigned part[3][4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+      split3_bf16x2(S[(8 * g + 2 * p) * 32 + e], S[(8 * g + 2 * p + 1) * 32 + e], part[0][p], part[1][p],
+                    part[2][p]);
+#pragma unroll
+    for (int k = 0; k < 3; ++k) op.s[h][k] = as_bf16x8(part[k][0], part[k][1], part[k][2], part[k][3]);
+  }
+  unsigned part[3][4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p)
+    split3_bf16x2(z[8 * g + 2 * p], z[8 * g + 2 * p + 1], part[0][p], part[1][p], part[2][p]);
+#pragma unroll
+  for (int k = 0; k < 3; ++k) op.z[k] = as_bf16x8(part[k][0], part[k][1], part[k][2], part[k][3]);
+}
+
+// One 16-token tile: q holds this lane's 8 raw features; returns the 8 outputs
+// packed as bf16 (RNE).
+template <bool ROPE>
+__device__ __forceinline__ u32x4_t apply_tile(u32x4_t q, const ApplyOperands& op, float eps, f32x4_t c,
+                                              f32x4_t sn) {
+  const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+  q[0] = relu_bf16x2(q[0]);
+  q[1] = relu_bf16x2(q[1]);
+  q[2] = relu_bf16x2(q[2]);
+  q[3] = relu_bf16x2(q[3]);
+  const bf16x8_t b = __builtin_bit_cast(bf16x8_t, q);
+
+  f32x4_t den = mfma16(op.z[0], b, zero4);
+  den = mfma16(op.z[1], b, den);
+  den = mfma16(op.z[2], b, den);
+  f32x4_t n0, n1;
+  if constexpr (!ROPE) {
+    n0 = mfma16(op.s[0][0], b, zero4);
+    n0 = mfma16(op.s[0][1], b, n0);
+    n0 = mfma16(op.s[0][2], b, n0);
+    n1 = mfma16(op.s[1][0], b, zero4);
+    n1 = mfma16(op.s[1][1], b, n1);
+    n1 = mfma16(op.s[1][2], b, n1);
+  } else {
+    unsigned rq[3][4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const float x0 = bf16lo_to_f32(q[p]);
+      const float x1 = bf16hi_to_f32(q[p]);
+      split3_bf16x2(x0 * c[p] - x1 * sn[p], x0 * sn[p] + x1 * c[p], rq[0][p], rq[1][p], rq[2][p]);
+    }
+    bf16x8_t b_r[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) b_r[k] = as_bf16x8(rq[k][0], rq[k][1], rq[k][2], rq[k][3]);
+    // the six product terms of weight >= 2^-16: hh, hm, mh, hl, lh, mm
+    n0 = mfma16(op.s[0][0], b_r[0], zero4);
+    n0 = mfma16(op.s[0][0], b_r[1], n0);
+    n0 = mfma16(op.s[0][1], b_r[0], n0);
+    n0 = mfma16(op.s[0][0], b_r[2], n0);
+    n0 = mfma16(op.s[0][2], b_r[0], n0);
+    n0 = mfma16(op.s[0][1], b_r[1], n0);
+    n1 = mfma16(op.s[1][0], b_r[0], zero4);
+    n1 = mfma16(op.s[1][0], b_r[1], n1);
+    n1 = mfma16(op.s[1][1], b_r[0], n1);
+    n1 = mfma16(op.s[1][0], b_r[2], n1);
+    n1 = mfma16(op.s[1][2], b_r[0], n1);
+    n1 = mfma16(op.s[1][1], b_r[1], n1);
+  }
+  const float rinv = 1.0f / (den[0] + eps);
+  u32x4_t o;
+  o[0] = pack_bf16x2(n0[0] * rinv, n0[1] * rinv);
+  o[1] = pack_bf16x2(n0[2] * rinv, n0[3] * rinv);
+  o[2] = pack_bf16x2(n1[0] * rinv, n1[1] * rinv);
+  o[3] = pack_bf16x2(n1[2] * rinv, n1[3] * rinv);
+  return o;
+}
+
+// The four 16-token tiles of a wave's 64-token chunk at t0 (this lane: token
+// t0 + 16u + m, features 8g .. 8g+7), with cos/sin of its pairs under RoPE.
+template <bool ROPE>
+struct ApplyChunk {
+  u32x4_t q[4];
+  f32x4_t c[4], sn[4];
+};
+
+template <bool ROPE>
+__device__ __forceinline__ void load_apply_chunk(const u32x4_t* Qh, int64_t t0, int64_t n_end, int m, int g,
+                                                 const float* cos_t, const float* sin_t, int64_t pos0,
+                                                 ApplyChunk<ROPE>& ch) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t tok = t0 + 16 * u + m;
+    ch.q[u] = u32x4_t{0u, 0u, 0u, 0u};
+    ch.c[u] = f32x4_t{1.f, 1.f, 1.f, 1.f};
+    ch.sn[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (tok < n_end) {
+      // streamed once: non-temporal, so it does not displace reused lines
+      ch.q[u] = __builtin_nontemporal_load(&Qh[tok * 4]);
+      if constexpr (ROPE) {
+        // pairs 4g .. 4g+3 of the token at position pos0 + tok
+        ch.c[u] = *reinterpret_cast<const f32x4_t*>(cos_t + (pos0 + tok) * 16 + 4 * g);
+        ch.sn[u] = *reinterpret_cast<const f32x4_t*>(sin_t + (pos0 + tok) * 16 + 4 * g);
+      }
+    }
+  }
+}
+
+template <bool ROPE>
+__global__ __launch_bounds__(kThreads) void apply_bf16(const u32x4_t* __restrict__ Q, u32x4_t* __restrict__ O,
+                                                       const float* __restrict__ kv,
+                                                       const float* __restrict__ ksum, int64_t N, int64_t total,
+                                                       int64_t La, float eps, const float* __restrict__ cos_t,
+                                                       const float* __restrict__ sin_t, int64_t pos0) {
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int m = lane & 15;
+  const int g = lane >> 4;
+  const int64_t f_begin = (int64_t)blockIdx.x * La;
+  const int64_t f_end = (f_begin + La < total) ? f_begin + La : total;
+
+  for (int64_t f = f_begin; f < f_end;) {
+    const int64_t bh = f / N;
+    const int64_t seg_end = (f_end < (bh + 1) * N) ? f_end : (bh + 1) * N;
+    const int64_t n_begin = f - bh * N;
+    const int64_t n_end = seg_end - bh * N;
+    f = seg_end;
+    const u32x4_t* Qh = Q + bh * N * 4 + g;  // 4 x 16 bytes per token row
+    u32x4_t* Oh = O + bh * N * 4 + g;
+
+    // the first chunk's loads go out before the state operands are fetched,
+    // and each chunk's loads before the previous chunk is computed
+    int64_t t0 = n_begin + 64 * w;
+    ApplyChunk<ROPE> next;
+    if (t0 < n_end) load_apply_chunk<ROPE>(Qh, t0, n_end, m, g, cos_t, sin_t, pos0, next);
+    ApplyOperands op;
+    load_apply_operands(kv + bh * 1024, ksum + bh * 32, g, m, op);
+
+    for (; t0 < n_end; t0 += 256) {
+      const ApplyChunk<ROPE> cur = next;
+      if (t0 + 256 < n_end) load_apply_chunk<ROPE>(Qh, t0 + 256, n_end, m, g, cos_t, sin_t, pos0, next);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t tok = t0 + 16 * u + m;
+        const u32x4_t o = apply_tile<ROPE>(cur.q[u], op, eps, cur.c[u], cur.sn[u]);
+        if (tok < n_end) __builtin_nontemporal_store(o, &Oh[tok * 4]);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 apply pass (VALU): thread = (token, 4 output features)
+// ---------------------------------------------------------------------------
+template <bool ROPE>
+__global__ __launch_bounds__(kThreads) void apply_f32(const float* __restrict__ Q, float* __restrict__ O,
+                                                      const float* __restrict__ kv,
+                                                      const float* __restrict__ ksum, int64_t N, int T,
+                                                      int64_t Lt, float eps, const float* __restrict__ cos_t,
+                                                      const float* __restrict__ sin_t, int64_t pos0) {
+  __shared__ float sS[kD][kD];
+  __shared__ float sz[kD];
+  const int64_t bh = blockIdx.x / T;
+  const int tile = blockIdx.x % T;
+  const int64_t n_begin = (int64_t)tile * Lt;
+  const int64_t n_end = (n_begin + Lt < N) ? n_begin + Lt : N;
+  const int t = threadIdx.x;
+  for (int idx = t; idx < 1024; idx += kThreads) sS[idx >> 5][idx & 31] = kv[bh * 1024 + idx];
+  if (t < kD) sz[t] = ksum[bh * 32 + t];
+  __syncthreads();
+  const int tl = t >> 3;
+  const int e0 = (t & 7) * 4;
+  for (int64_t tok = n_begin + tl; tok < n_end; tok += 32) {
+    const float* qrow = Q + (bh * N + tok) * kD;
+    float pq[kD], pr[kD];
+#pragma unroll
+    for (int d = 0; d < kD; ++d) pq[d] = fmaxf(qrow[d], 0.f);
+    float den = 0.f;
+#pragma unroll
+    for (int d = 0; d < kD; ++d) den = fmaf(pq[d], sz[d], den);
+    den += eps;
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+      if constexpr (ROPE) {
+        const float c = cos_t[(pos0 + tok) * 16 + p];
+        const float sn = sin_t[(pos0 + tok) * 16 + p];
+        pr[2 * p] = pq[2 * p] * c - pq[2 * p + 1] * sn;
+        pr[2 * p + 1] = pq[2 * p] * sn + pq[2 * p + 1] * c;
+      } else {
+        pr[2 * p] = pq[2 * p];
+        pr[2 * p + 1] = pq[2 * p + 1];
+      }
+    }
+    float num[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int d = 0; d < kD; ++d) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) num[c] = fmaf(pr[d], sS[d][e0 + c], num[c]);
+    }
+    float* orow = O + (bh * N + tok) * kD + e0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) orow[c] = num[c] / den;
+  }
+}
+
+}  // namespace la

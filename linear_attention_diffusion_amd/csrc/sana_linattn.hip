@@ -1,0 +1,335 @@
+// Host side of the C ABI declared in include/sana_linattn.h: argument checks,
+// launch geometry, workspace layout and the 3D RoPE table builder.
+//
+// A compute call enqueues up to three kernels on the caller's stream:
+//   1. state pass  (P workgroups per head, each a contiguous token range,
+//                   writing one partial state each; with P = 1 the workgroup
+//                   writes the head's state itself)
+//   2. finalize    (P > 1 only: one thread per state element sums the P
+//                   partials in order and adds the carried state)
+//   3. apply pass  (equal contiguous ranges of the flattened head x token
+//                   space, one per workgroup)
+// state_update runs 1-2 only.  Nothing is allocated, freed or synchronised.
+
+#include "sana_linattn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "la_kernels.h"
+
+namespace {
+
+// MI355X: 256 compute units.  Both passes size their grids to one resident
+// round of workgroups, at the count that measured fastest on the Sana-1.6B
+// 4096 px layer: state 2 per CU (8 waves, each with a 64-token chunk of K and V
+// in flight), apply 3 per CU (2 with RoPE, whose register use allows no more).
+constexpr int64_t kCUs = 256;
+constexpr int64_t kStateGroups = kCUs * 2;
+constexpr int64_t kStateGroupsRope = kCUs * 2;
+constexpr int64_t kApplyGroups = kCUs * 3;
+constexpr int64_t kApplyGroupsRope = kCUs * 2;
+constexpr int64_t kMaxSplits = 64;       // partial states per head
+constexpr int64_t kMinSplitTokens = 256;
+constexpr int64_t kMinApplyTokens = 256;
+constexpr int64_t kMinApplyTokensF32 = 256;
+constexpr int64_t kMaxApplyTokensF32 = 1024;
+// a launch may hold at most 2^32 - 1 work-items: 2^24 - 1 workgroups of 256
+constexpr int64_t kMaxGroups = ((int64_t)1 << 24) - 1;
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+struct Geometry {
+  int64_t BH = 0, N = 0;
+  int64_t P = 0, Ls = 0;   // state pass: splits per head, tokens per split
+  int64_t Ga = 0, La = 0;  // bf16 apply pass: workgroups, flattened tokens per workgroup
+  int64_t T = 0, Lt = 0;   // fp32 apply pass: tiles per head, tokens per tile
+  size_t partial_off = 0, state_off = 0, total_bytes = 0;
+};
+
+Geometry make_geometry(int64_t BH, int64_t N, bool rope) {
+  Geometry g;
+  g.BH = BH;
+  g.N = N;
+  if (BH <= 0 || N <= 0) return g;
+  const int64_t apply_groups = rope ? kApplyGroupsRope : kApplyGroups;
+  int64_t p = (rope ? kStateGroupsRope : kStateGroups) / BH;
+  const int64_t p_max = ceil_div(N, kMinSplitTokens);
+  if (p > p_max) p = p_max;
+  if (p > kMaxSplits) p = kMaxSplits;
+  if (p < 1) p = 1;
+  g.Ls = round_up(ceil_div(N, p), 32);
+  g.P = ceil_div(N, g.Ls);
+
+  const int64_t total = BH * N;
+  int64_t la = round_up(ceil_div(total, apply_groups), 64);
+  if (la < kMinApplyTokens) la = kMinApplyTokens;
+  if (ceil_div(total, la) > kMaxGroups) la = round_up(ceil_div(total, kMaxGroups), 64);
+  g.La = la;
+  g.Ga = ceil_div(total, la);
+
+  int64_t lt = round_up(ceil_div(N, ceil_div(apply_groups, BH)), 64);
+  if (lt < kMinApplyTokensF32) lt = kMinApplyTokensF32;
+  if (lt > kMaxApplyTokensF32) lt = kMaxApplyTokensF32;
+  const int64_t lt_floor = round_up(ceil_div(N, kMaxGroups / BH), 64);
+  if (lt < lt_floor) lt = lt_floor;
+  g.Lt = lt;
+  g.T = ceil_div(N, lt);
+
+  const size_t partial_bytes = g.P > 1 ? (size_t)(BH * g.P) * la::kStateElems * sizeof(float) : 0;
+  const size_t state_bytes = (size_t)BH * la::kStateElems * sizeof(float);
+  g.partial_off = 0;
+  g.state_off = (size_t)round_up((int64_t)partial_bytes, 256);
+  g.total_bytes = g.state_off + (size_t)round_up((int64_t)state_bytes, 256);
+  return g;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
+  if (!a || !b || an == 0 || bn == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + bn && b0 < a0 + an;
+}
+
+int elem_size(int dtype) { return dtype == SANA_DT_BF16 ? 2 : (dtype == SANA_DT_F32 ? 4 : 0); }
+
+// Checks shared by every compute call.  Returns SANA_OK and fills `elems`
+// (B*H*N*D) and `BH` when the sizes are valid.
+int check_sizes(int B, int H, int64_t N, int D, int dtype, int64_t* BH, int64_t* elems) {
+  if (B < 0 || H < 0 || N < 0 || D <= 0) return SANA_ERR_INVALID;
+  if (elem_size(dtype) == 0) return SANA_ERR_INVALID;
+  if (D != la::kD) return SANA_ERR_UNSUPPORTED;
+  const int64_t bh = (int64_t)B * (int64_t)H;
+  if (bh > 0 && N > (INT64_MAX / 64) / bh) return SANA_ERR_INVALID;
+  if (bh * kMaxSplits > kMaxGroups) return SANA_ERR_INVALID;  // state-pass grid bound
+  *BH = bh;
+  *elems = bh * N * D;
+  return SANA_OK;
+}
+
+int check_rope(const sana_rope* rope, int64_t N) {
+  if (!rope) return SANA_OK;
+  if (!rope->cos || !rope->sin) return SANA_ERR_INVALID;
+  if (!aligned(rope->cos, 16) || !aligned(rope->sin, 16)) return SANA_ERR_INVALID;
+  if (rope->pos_offset < 0 || rope->n_pos < 0) return SANA_ERR_INVALID;
+  if (rope->pos_offset > rope->n_pos || N > rope->n_pos - rope->pos_offset) return SANA_ERR_INVALID;
+  return SANA_OK;
+}
+
+int check_workspace(const Geometry& g, const void* ws, size_t ws_bytes) {
+  if (!ws || ws_bytes < g.total_bytes) return SANA_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return SANA_ERR_INVALID;
+  return SANA_OK;
+}
+
+int check_tensor(const void* p) { return (p && aligned(p, 16)) ? SANA_OK : SANA_ERR_INVALID; }
+
+float* ws_at(void* ws, size_t off) { return reinterpret_cast<float*>(static_cast<char*>(ws) + off); }
+
+la::StateArgs state_args(void* ws, const Geometry& g, const float* kv_in, const float* ksum_in, float* kv_out,
+                         float* ksum_out) {
+  la::StateArgs a;
+  a.partials = ws_at(ws, g.partial_off);
+  a.kv_in = kv_in;
+  a.ksum_in = ksum_in;
+  a.kv_out = kv_out;
+  a.ksum_out = ksum_out;
+  a.P = (int)g.P;
+  return a;
+}
+
+void launch_state(const void* k, const void* v, int dtype, const Geometry& g, const sana_rope* rope,
+                  const la::StateArgs& a, hipStream_t st) {
+  const float* ct = rope ? rope->cos : nullptr;
+  const float* sn = rope ? rope->sin : nullptr;
+  const int64_t pos0 = rope ? rope->pos_offset : 0;
+  const dim3 grid((unsigned)(g.BH * g.P)), block(la::kThreads);
+  if (dtype == SANA_DT_BF16) {
+    const la::u32x4_t* K = static_cast<const la::u32x4_t*>(k);
+    const la::u32x4_t* V = static_cast<const la::u32x4_t*>(v);
+    if (rope)
+      la::state_bf16<true><<<grid, block, 0, st>>>(K, V, g.N, g.Ls, ct, sn, pos0, a);
+    else
+      la::state_bf16<false><<<grid, block, 0, st>>>(K, V, g.N, g.Ls, ct, sn, pos0, a);
+  } else {
+    const float* K = static_cast<const float*>(k);
+    const float* V = static_cast<const float*>(v);
+    if (rope)
+      la::state_f32<true><<<grid, block, 0, st>>>(K, V, g.N, g.Ls, ct, sn, pos0, a);
+    else
+      la::state_f32<false><<<grid, block, 0, st>>>(K, V, g.N, g.Ls, ct, sn, pos0, a);
+  }
+  if (g.P > 1) {
+    const int64_t n_elems = g.BH * la::kStateElems;
+    la::state_finalize<<<dim3((unsigned)ceil_div(n_elems, la::kThreads)), dim3(la::kThreads), 0, st>>>(a, n_elems);
+  }
+}
+
+void launch_apply(const void* q, void* o, int dtype, float eps, const Geometry& g, const sana_rope* rope,
+                  const float* kv, const float* ksum, hipStream_t st) {
+  const float* ct = rope ? rope->cos : nullptr;
+  const float* sn = rope ? rope->sin : nullptr;
+  const int64_t pos0 = rope ? rope->pos_offset : 0;
+  if (dtype == SANA_DT_BF16) {
+    const dim3 grid((unsigned)g.Ga), block(la::kThreads);
+    const la::u32x4_t* Q = static_cast<const la::u32x4_t*>(q);
+    la::u32x4_t* O = static_cast<la::u32x4_t*>(o);
+    if (rope)
+      la::apply_bf16<true><<<grid, block, 0, st>>>(Q, O, kv, ksum, g.N, g.BH * g.N, g.La, eps, ct, sn, pos0);
+    else
+      la::apply_bf16<false><<<grid, block, 0, st>>>(Q, O, kv, ksum, g.N, g.BH * g.N, g.La, eps, ct, sn, pos0);
+  } else {
+    const dim3 grid((unsigned)(g.BH * g.T)), block(la::kThreads);
+    const float* Q = static_cast<const float*>(q);
+    float* O = static_cast<float*>(o);
+    if (rope)
+      la::apply_f32<true><<<grid, block, 0, st>>>(Q, O, kv, ksum, g.N, (int)g.T, g.Lt, eps, ct, sn, pos0);
+    else
+      la::apply_f32<false><<<grid, block, 0, st>>>(Q, O, kv, ksum, g.N, (int)g.T, g.Lt, eps, ct, sn, pos0);
+  }
+}
+
+int launch_status() { return hipGetLastError() == hipSuccess ? SANA_OK : SANA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+size_t sana_linattn_workspace_bytes(int B, int H, int64_t N, int D, int dtype, int has_rope) {
+  int64_t bh = 0, elems = 0;
+  if (check_sizes(B, H, N, D, dtype, &bh, &elems) != SANA_OK) return 0;
+  return make_geometry(bh, N, has_rope != 0).total_bytes;
+}
+
+int sana_linattn_forward(const void* q, const void* k, const void* v, void* o, int B, int H, int64_t N, int D,
+                         int dtype, float eps, const sana_rope* rope, void* ws, size_t ws_bytes,
+                         void* hip_stream) {
+  int64_t bh = 0, elems = 0;
+  int rc = check_sizes(B, H, N, D, dtype, &bh, &elems);
+  if (rc != SANA_OK) return rc;
+  if (!std::isfinite(eps) || eps < 0.f) return SANA_ERR_INVALID;
+  if (elems == 0) return SANA_OK;
+  if (check_tensor(q) || check_tensor(k) || check_tensor(v) || check_tensor(o)) return SANA_ERR_INVALID;
+  const size_t bytes = (size_t)elems * elem_size(dtype);
+  if (overlaps(o, bytes, q, bytes) || overlaps(o, bytes, k, bytes) || overlaps(o, bytes, v, bytes))
+    return SANA_ERR_INVALID;
+  if ((rc = check_rope(rope, N)) != SANA_OK) return rc;
+  const Geometry g = make_geometry(bh, N, rope != nullptr);
+  if ((rc = check_workspace(g, ws, ws_bytes)) != SANA_OK) return rc;
+
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  float* state = ws_at(ws, g.state_off);
+  launch_state(k, v, dtype, g, rope, state_args(ws, g, nullptr, nullptr, state, state + bh * 1024), st);
+  launch_apply(q, o, dtype, eps, g, rope, state, state + bh * 1024, st);
+  return launch_status();
+}
+
+int sana_linattn_state_update(const void* k, const void* v, float* kv_state, float* ksum_state, int B, int H,
+                              int64_t N, int D, int dtype, const sana_rope* rope, void* ws, size_t ws_bytes,
+                              void* hip_stream) {
+  int64_t bh = 0, elems = 0;
+  int rc = check_sizes(B, H, N, D, dtype, &bh, &elems);
+  if (rc != SANA_OK) return rc;
+  if (elems == 0) return SANA_OK;
+  if (check_tensor(k) || check_tensor(v)) return SANA_ERR_INVALID;
+  if (!kv_state || !ksum_state || !aligned(kv_state, 4) || !aligned(ksum_state, 4)) return SANA_ERR_INVALID;
+  const size_t bytes = (size_t)elems * elem_size(dtype);
+  const size_t kv_bytes = (size_t)bh * 1024 * sizeof(float), ks_bytes = (size_t)bh * 32 * sizeof(float);
+  if (overlaps(kv_state, kv_bytes, ksum_state, ks_bytes) || overlaps(kv_state, kv_bytes, k, bytes) ||
+      overlaps(kv_state, kv_bytes, v, bytes) || overlaps(ksum_state, ks_bytes, k, bytes) ||
+      overlaps(ksum_state, ks_bytes, v, bytes))
+    return SANA_ERR_INVALID;
+  if ((rc = check_rope(rope, N)) != SANA_OK) return rc;
+  const Geometry g = make_geometry(bh, N, rope != nullptr);
+  if ((rc = check_workspace(g, ws, ws_bytes)) != SANA_OK) return rc;
+
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  launch_state(k, v, dtype, g, rope, state_args(ws, g, kv_state, ksum_state, kv_state, ksum_state), st);
+  return launch_status();
+}
+
+int sana_linattn_block_forward(const void* q, const void* k, const void* v, void* o, const float* kv_in,
+                               const float* ksum_in, float* kv_out, float* ksum_out, int B, int H, int64_t N,
+                               int D, int dtype, float eps, const sana_rope* rope, void* ws, size_t ws_bytes,
+                               void* hip_stream) {
+  int64_t bh = 0, elems = 0;
+  int rc = check_sizes(B, H, N, D, dtype, &bh, &elems);
+  if (rc != SANA_OK) return rc;
+  if (!std::isfinite(eps) || eps < 0.f) return SANA_ERR_INVALID;
+  if (elems == 0) return SANA_OK;
+  if (check_tensor(q) || check_tensor(k) || check_tensor(v) || check_tensor(o)) return SANA_ERR_INVALID;
+  if ((kv_in == nullptr) != (ksum_in == nullptr)) return SANA_ERR_INVALID;
+  if ((kv_out == nullptr) != (ksum_out == nullptr)) return SANA_ERR_INVALID;
+  if ((kv_in && (!aligned(kv_in, 4) || !aligned(ksum_in, 4))) ||
+      (kv_out && (!aligned(kv_out, 4) || !aligned(ksum_out, 4))))
+    return SANA_ERR_INVALID;
+  const size_t bytes = (size_t)elems * elem_size(dtype);
+  if (overlaps(o, bytes, q, bytes) || overlaps(o, bytes, k, bytes) || overlaps(o, bytes, v, bytes))
+    return SANA_ERR_INVALID;
+  const size_t kv_bytes = (size_t)bh * 1024 * sizeof(float), ks_bytes = (size_t)bh * 32 * sizeof(float);
+  const void* tensors[4] = {q, k, v, o};
+  const void* states[4] = {kv_in, ksum_in, kv_out, ksum_out};
+  const size_t state_sizes[4] = {kv_bytes, ks_bytes, kv_bytes, ks_bytes};
+  for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 4; ++j)
+      if (overlaps(states[i], state_sizes[i], tensors[j], bytes)) return SANA_ERR_INVALID;
+  // among the states only exact in-place aliasing (kv_out == kv_in, ksum_out == ksum_in) is allowed
+  if (overlaps(kv_in, kv_bytes, ksum_in, ks_bytes) || overlaps(kv_out, kv_bytes, ksum_out, ks_bytes) ||
+      overlaps(kv_in, kv_bytes, ksum_out, ks_bytes) || overlaps(ksum_in, ks_bytes, kv_out, kv_bytes))
+    return SANA_ERR_INVALID;
+  if (kv_out && overlaps(kv_in, kv_bytes, kv_out, kv_bytes) && kv_in != kv_out) return SANA_ERR_INVALID;
+  if (ksum_out && overlaps(ksum_in, ks_bytes, ksum_out, ks_bytes) && ksum_in != ksum_out) return SANA_ERR_INVALID;
+  if ((rc = check_rope(rope, N)) != SANA_OK) return rc;
+  const Geometry g = make_geometry(bh, N, rope != nullptr);
+  if ((rc = check_workspace(g, ws, ws_bytes)) != SANA_OK) return rc;
+
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  float* kv_new = kv_out ? kv_out : ws_at(ws, g.state_off);
+  float* ksum_new = kv_out ? ksum_out : ws_at(ws, g.state_off) + bh * 1024;
+  launch_state(k, v, dtype, g, rope, state_args(ws, g, kv_in, ksum_in, kv_new, ksum_new), st);
+  launch_apply(q, o, dtype, eps, g, rope, kv_new, ksum_new, st);
+  return launch_status();
+}
+
+int sana_linattn_rope3d_table(int T, int Hl, int Wl, int D, int dt, int dh, int dw, double base, float* cos_host,
+                              float* sin_host) {
+  if (T < 0 || Hl < 0 || Wl < 0 || D <= 0 || dt < 0 || dh < 0 || dw < 0) return SANA_ERR_INVALID;
+  if ((dt | dh | dw) & 1 || dt + dh + dw != D || !(base > 0.0) || !std::isfinite(base)) return SANA_ERR_INVALID;
+  const int64_t n = (int64_t)T * Hl * Wl;
+  if (n == 0) return SANA_OK;
+  if (!cos_host || !sin_host) return SANA_ERR_INVALID;
+  const int pairs = D / 2;
+  const int widths[3] = {dt, dh, dw};
+  for (int t = 0; t < T; ++t)
+    for (int h = 0; h < Hl; ++h)
+      for (int w = 0; w < Wl; ++w) {
+        const int64_t row = ((int64_t)t * Hl + h) * Wl + w;
+        const double coord[3] = {(double)t, (double)h, (double)w};
+        int p = 0;
+        for (int a = 0; a < 3; ++a)
+          for (int kk = 0; kk < widths[a] / 2; ++kk, ++p) {
+            const double theta = coord[a] * std::pow(base, -2.0 * kk / widths[a]);
+            cos_host[row * pairs + p] = (float)std::cos(theta);
+            sin_host[row * pairs + p] = (float)std::sin(theta);
+          }
+      }
+  return SANA_OK;
+}
+
+const char* sana_linattn_status_string(int status) {
+  switch (status) {
+    case SANA_OK: return "SANA_OK";
+    case SANA_ERR_INVALID: return "SANA_ERR_INVALID: invalid argument";
+    case SANA_ERR_UNSUPPORTED: return "SANA_ERR_UNSUPPORTED: unsupported head width (only D = 32)";
+    case SANA_ERR_WORKSPACE: return "SANA_ERR_WORKSPACE: workspace missing or too small";
+    case SANA_ERR_HIP: return "SANA_ERR_HIP: a HIP launch failed";
+    default: return "unknown sana_status";
+  }
+}
+
+}  // extern "C"

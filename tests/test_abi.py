@@ -1,0 +1,178 @@
+"""CPU tests of the C ABI: the library loads and exports every declared entry
+point, argument errors come back as status codes before anything is launched,
+workspace sizing behaves, and the host RoPE table builder matches the oracle's
+float64 angles.  No compute call reaches a GPU here."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import linear_attention_diffusion_amd as la
+from linear_attention_diffusion_amd.binding import sana_rope
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sana_linattn.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(sana_linattn_\w+)\s*\(", text)))
+
+
+def test_header_declares_what_the_binding_exports():
+    assert _declared() == sorted(la.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    L = la.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", L._name], capture_output=True, text=True).stdout
+    for name in _declared():
+        assert re.search(rf"\bT {name}$", out, re.M), f"{name} not exported"
+
+
+def test_status_strings():
+    for code in (la.SANA_OK, la.SANA_ERR_INVALID, la.SANA_ERR_UNSUPPORTED, la.SANA_ERR_WORKSPACE, la.SANA_ERR_HIP):
+        assert la.sana_linattn_status_string(code).startswith("SANA_")
+    assert "unknown" in la.sana_linattn_status_string(42)
+
+
+def test_workspace_bytes():
+    wb = la.workspace_bytes
+    assert wb(1, 70, 0) == 0 and wb(0, 70, 100) == 0
+    assert wb(1, 70, 16384) > 0
+    assert wb(1, 70, 16384) % 256 == 0
+    # invalid sizes -> 0
+    assert wb(1, 70, 100, D=64) == 0 and wb(-1, 70, 100) == 0 and wb(1, 70, 100, dtype=7) == 0
+    # never smaller than the state it holds (33 x 32 floats per head), and
+    # bounded: at most 64 partials + 1 state + 1 counter per head
+    for B, H, N in [(1, 1, 1), (4, 36, 1024), (1, 70, 16384), (1, 70, 4680), (1, 70, 46800), (2, 3, 5)]:
+        for rope in (False, True):
+            n = wb(B, H, N, has_rope=rope)
+            assert B * H * 33 * 32 * 4 <= n <= B * H * (33 * 32 * 4 * 65 + 8) + 768, (B, H, N, n)
+    # the same for either dtype
+    assert wb(1, 70, 18480) == wb(1, 70, 18480, dtype=la.SANA_DT_F32)
+    assert wb(1, 70, 18480, has_rope=True) == wb(1, 70, 18480, dtype=la.SANA_DT_F32, has_rope=True)
+
+
+# Fake, 256-byte-aligned addresses.  Every call below carries an argument error,
+# so the library must return before touching them or the GPU.
+A = 0x10000000
+Bp = 0x20000000
+C = 0x30000000
+Dp = 0x40000000
+WS = 0x50000000
+
+
+def _fwd(q=A, k=Bp, v=C, o=Dp, B=1, H=2, N=64, D=32, dt=la.SANA_DT_BF16, eps=1e-6, rope=None,
+         ws=WS, nbytes=None):
+    if nbytes is None:
+        nbytes = la.workspace_bytes(max(B, 0), max(H, 0), max(N, 0))
+    return la.lib().sana_linattn_forward(q, k, v, o, B, H, N, D, dt, eps, rope, ws, nbytes, None)
+
+
+def test_forward_argument_errors():
+    E = la
+    assert _fwd(q=None) == E.SANA_ERR_INVALID
+    assert _fwd(o=None) == E.SANA_ERR_INVALID
+    assert _fwd(q=A + 8) == E.SANA_ERR_INVALID            # misaligned
+    assert _fwd(B=-1) == E.SANA_ERR_INVALID
+    assert _fwd(N=-5) == E.SANA_ERR_INVALID
+    assert _fwd(D=0) == E.SANA_ERR_INVALID
+    assert _fwd(D=64) == E.SANA_ERR_UNSUPPORTED
+    assert _fwd(D=16) == E.SANA_ERR_UNSUPPORTED
+    assert _fwd(dt=5) == E.SANA_ERR_INVALID
+    assert _fwd(eps=-1.0) == E.SANA_ERR_INVALID
+    assert _fwd(eps=float("nan")) == E.SANA_ERR_INVALID
+    assert _fwd(eps=float("inf")) == E.SANA_ERR_INVALID
+    assert _fwd(o=A) == E.SANA_ERR_INVALID                # o aliases q
+    assert _fwd(o=Bp + 64) == E.SANA_ERR_INVALID          # o overlaps k
+    assert _fwd(ws=None) == E.SANA_ERR_WORKSPACE
+    assert _fwd(nbytes=16) == E.SANA_ERR_WORKSPACE
+    assert _fwd(ws=WS + 16) == E.SANA_ERR_INVALID         # workspace not 256-byte aligned
+    # empty problems are no-ops, whatever the pointers
+    assert _fwd(q=None, k=None, v=None, o=None, N=0, ws=None) == E.SANA_OK
+    assert _fwd(q=None, k=None, v=None, o=None, B=0, ws=None) == E.SANA_OK
+    # RoPE tables must cover the positions read
+    r = sana_rope(0x60000000, 0x70000000, 63, 0)
+    assert _fwd(rope=ctypes.byref(r)) == E.SANA_ERR_INVALID
+    r = sana_rope(0x60000000, 0x70000000, 100, 40)
+    assert _fwd(rope=ctypes.byref(r)) == E.SANA_ERR_INVALID
+    r = sana_rope(0x60000000, 0x70000000, 100, -1)
+    assert _fwd(rope=ctypes.byref(r)) == E.SANA_ERR_INVALID
+    r = sana_rope(None, 0x70000000, 100, 0)
+    assert _fwd(rope=ctypes.byref(r)) == E.SANA_ERR_INVALID
+    r = sana_rope(0x60000004, 0x70000000, 100, 0)
+    assert _fwd(rope=ctypes.byref(r)) == E.SANA_ERR_INVALID
+
+
+def test_state_update_argument_errors():
+    L = la.lib()
+    n = la.workspace_bytes(1, 2, 64)
+
+    def su(k=A, v=Bp, kv=C, ks=Dp, N=64, D=32, ws=WS):
+        return L.sana_linattn_state_update(k, v, kv, ks, 1, 2, N, D, la.SANA_DT_BF16, None, ws, n, None)
+
+    assert su(kv=None) == la.SANA_ERR_INVALID
+    assert su(ks=None) == la.SANA_ERR_INVALID
+    assert su(kv=C + 2) == la.SANA_ERR_INVALID
+    assert su(ks=C + 4 * 1024) == la.SANA_ERR_INVALID     # ksum overlaps kv (2 heads x 4 KiB)
+    assert su(kv=A) == la.SANA_ERR_INVALID                # state overlaps k
+    assert su(D=48) == la.SANA_ERR_UNSUPPORTED
+    assert su(ws=None) == la.SANA_ERR_WORKSPACE
+    assert su(k=None, v=None, kv=None, ks=None, N=0, ws=None) == la.SANA_OK
+
+
+def test_block_forward_argument_errors():
+    L = la.lib()
+    n = la.workspace_bytes(1, 2, 64)
+    S_IN, Z_IN, S_OUT, Z_OUT = 0x80000000, 0x90000000, 0xA0000000, 0xB0000000
+
+    def bf(q=A, o=Dp, kv_in=S_IN, ks_in=Z_IN, kv_out=S_OUT, ks_out=Z_OUT):
+        return L.sana_linattn_block_forward(q, Bp, C, o, kv_in, ks_in, kv_out, ks_out, 1, 2, 64, 32,
+                                            la.SANA_DT_BF16, 1e-6, None, WS, n, None)
+
+    assert bf(kv_in=None) == la.SANA_ERR_INVALID          # kv_in without ksum_in
+    assert bf(ks_out=None) == la.SANA_ERR_INVALID         # kv_out without ksum_out
+    assert bf(kv_out=S_IN + 64) == la.SANA_ERR_INVALID    # partial overlap of in and out states
+    assert bf(ks_out=S_IN) == la.SANA_ERR_INVALID         # ksum_out inside kv_in
+    assert bf(kv_in=A) == la.SANA_ERR_INVALID             # state overlaps q
+    assert bf(o=C) == la.SANA_ERR_INVALID                 # o aliases v
+    assert bf(q=None) == la.SANA_ERR_INVALID
+
+
+def test_rope3d_table_matches_oracle_angles():
+    import oracle
+    T, Hl, Wl = 4, 6, 5
+    cos, sin = la.rope3d_table(T, Hl, Wl)
+    ang = oracle.rope3d_angles(T, Hl, Wl)
+    # float32 rounding of cos/sin only
+    np.testing.assert_allclose(cos, np.cos(ang), rtol=0, atol=6e-8)
+    np.testing.assert_allclose(sin, np.sin(ang), rtol=0, atol=6e-8)
+    # full 720p grid: same
+    cos, sin = la.rope3d_table(21, 22, 40)
+    ang = oracle.rope3d_angles(21, 22, 40)
+    assert np.max(np.abs(cos - np.cos(ang))) < 6e-8 and np.max(np.abs(sin - np.sin(ang))) < 6e-8
+
+
+def test_rope3d_table_errors():
+    L = la.lib()
+    buf = np.empty(64, np.float32)
+    p = buf.ctypes.data_as(ctypes.c_void_p)
+    assert L.sana_linattn_rope3d_table(1, 2, 2, 32, 8, 12, 10, 1e4, p, p) == la.SANA_ERR_INVALID  # sum != D
+    assert L.sana_linattn_rope3d_table(1, 2, 2, 32, 7, 13, 12, 1e4, p, p) == la.SANA_ERR_INVALID  # odd split
+    assert L.sana_linattn_rope3d_table(1, 2, 2, 32, 8, 12, 12, 0.0, p, p) == la.SANA_ERR_INVALID  # bad base
+    assert L.sana_linattn_rope3d_table(1, 2, 2, 32, 8, 12, 12, 1e4, None, p) == la.SANA_ERR_INVALID
+    assert L.sana_linattn_rope3d_table(0, 2, 2, 32, 8, 12, 12, 1e4, None, None) == la.SANA_OK
+
+
+def test_binding_refuses_host_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(1, 1, 4, 32, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        la.sana_linattn_forward(x, x, x)
