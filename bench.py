@@ -14,16 +14,19 @@ Inputs are resident in HBM before timing starts.  Several input/output sets
 (at least 1.5 GiB in total) are cycled so that no step finds its inputs in the
 256 MB Infinity Cache left there by the step before.
 
-Prints ONE JSON line.  `roofline` describes the dominant kernel; `cpu_baseline`
-times the float64 oracle on the host cores.
+Prints ONE JSON line.  `roofline` describes the dominant kernel, the apply
+pass (apply_bf16): after the main timed region it is launched on its own,
+through sana_linattn_apply on the state the forward computes, in the same
+launch configuration, and timed with HIP events on the launch stream.
+`cpu_baseline` times the float64 oracle on the host cores.
 """
 
 import argparse
+import ctypes
 import hashlib
 import json
 import math
 import os
-import statistics
 import sys
 import time
 
@@ -57,8 +60,10 @@ def algorithmic_bytes(w):
 
 
 def stored_traffic(name):
-    """HBM bytes per step from committed rocprofv3 counter runs, if they were
-    taken on the current kernel sources; else None."""
+    """HBM bytes per launch of the dominant kernel, from committed rocprofv3
+    counter runs (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter
+    reads for a copy kernel of known size), if they were taken on the current
+    kernel sources; else None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
     if not os.path.exists(path):
         return None
@@ -66,7 +71,7 @@ def stored_traffic(name):
         rec = json.load(f)
     if rec.get("kernel_source_hash") != kernel_source_hash():
         return None
-    return rec.get("hbm_bytes_per_step")
+    return rec.get("hbm_bytes_per_launch")
 
 
 def cpu_baseline(w, x, budget_s):
@@ -155,7 +160,6 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     x = generate(w, with_f64=False)
-    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
 
     def to_dev(raw):
         if w.dtype == "bf16":
@@ -175,54 +179,108 @@ def main():
 
     rope = la.rope3d_device(*w.grid, dev) if w.mode == "rope" else None
     if w.mode == "block":
-        L = w.chunk
+        Lc = w.chunk
         for s in sets:
             for n in ("q", "k", "v", "o"):
                 t = s[n]
-                s[n + "_chunks"] = [t[:, :, c:min(w.N, c + L)].contiguous() for c in range(0, w.N, L)]
+                s[n + "_chunks"] = [t[:, :, c:min(w.N, c + Lc)].contiguous() for c in range(0, w.N, Lc)]
             s["kv"] = torch.zeros(w.B, w.H, 32, 32, device=dev)
             s["z"] = torch.zeros(w.B, w.H, 32, device=dev)
-        ws = la.make_workspace(w.B, w.H, L, dev, dtype=la.SANA_DT_BF16 if w.dtype == "bf16" else la.SANA_DT_F32)
+        ws = la.make_workspace(w.B, w.H, Lc, dev, dtype=la.SANA_DT_BF16 if w.dtype == "bf16" else la.SANA_DT_F32)
     else:
         ws = la.make_workspace(w.B, w.H, w.N, dev, dtype=la.SANA_DT_BF16 if w.dtype == "bf16" else la.SANA_DT_F32,
                                has_rope=rope is not None)
 
-    def step(i):
-        s = sets[i % n_sets]
+    # Pre-marshalled C calls: the timed loop makes no torch calls and no
+    # argument checks in Python, so the host stays ahead of the GPU.
+    L = la.lib()
+    dt = la.SANA_DT_BF16 if w.dtype == "bf16" else la.SANA_DT_F32
+    ws_ptr, ws_n = ctypes.c_void_p(ws.data_ptr()), ws.numel()
+    st_ptr = ctypes.c_void_p(stream.cuda_stream)
+    rope_ref = None if rope is None else ctypes.byref(rope.struct())
+    P = ctypes.c_void_p
+    calls = []
+    for s in sets:
         if w.mode == "block":
-            kv, z = s["kv"], s["z"]
+            seq = []
             for c, (qc, kc, vc, oc) in enumerate(zip(s["q_chunks"], s["k_chunks"], s["v_chunks"], s["o_chunks"])):
                 # chunk 0 starts from the zero state (kv_in = NULL); every chunk commits in place
-                la.sana_linattn_block_forward(qc, kc, vc, oc, kv_in=None if c == 0 else kv,
-                                              ksum_in=None if c == 0 else z, kv_out=kv, ksum_out=z,
-                                              eps=w.eps, workspace=ws, stream=stream)
+                kv_in = None if c == 0 else P(s["kv"].data_ptr())
+                z_in = None if c == 0 else P(s["z"].data_ptr())
+                seq.append((P(qc.data_ptr()), P(kc.data_ptr()), P(vc.data_ptr()), P(oc.data_ptr()), kv_in, z_in,
+                            P(s["kv"].data_ptr()), P(s["z"].data_ptr()), w.B, w.H, qc.shape[2], w.D, dt, w.eps,
+                            None, ws_ptr, ws_n, st_ptr))
+            calls.append(("block", seq))
         else:
-            la.sana_linattn_forward(s["q"], s["k"], s["v"], s["o"], eps=w.eps, rope=rope, workspace=ws,
-                                    stream=stream)
+            calls.append(("fwd", (P(s["q"].data_ptr()), P(s["k"].data_ptr()), P(s["v"].data_ptr()),
+                                  P(s["o"].data_ptr()), w.B, w.H, w.N, w.D, dt, w.eps, rope_ref, ws_ptr, ws_n,
+                                  st_ptr)))
+
+    def step(i):
+        kind, args = calls[i % n_sets]
+        if kind == "block":
+            for a in args:
+                rc = L.sana_linattn_block_forward(*a)
+                if rc:
+                    raise la.SanaError(rc)
+        else:
+            rc = L.sana_linattn_forward(*args)
+            if rc:
+                raise la.SanaError(rc)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    # timed region: K steps, an event pair around each (events on the launch stream)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # timed region: exactly K steps between one pair of events on the launch
+    # stream (per-step events would add marker packets to the measured time)
+    e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
+    e_start.record(stream)
     for i in range(args.steps):
-        evs[i][0].record(stream)
         step(args.warmup + i)
-        evs[i][1].record(stream)
+    e_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
-    per_step_ms = [a.elapsed_time(b) for a, b in evs]
-    total_ms = evs[0][0].elapsed_time(evs[-1][1])
+    total_ms = e_start.elapsed_time(e_end)
 
     ms_per_step = total_ms / args.steps
     value = w.token_heads * args.steps / (total_ms / 1e3)
     alg_bytes = algorithmic_bytes(w)
     launches = w.n_chunks if w.mode == "block" else 1
-    launch_ms = statistics.mean(per_step_ms) / launches
-    achieved = (alg_bytes / launches) / (launch_ms / 1e3) / 1e9
+    call_ms = ms_per_step / launches
+
+    # roofline of the dominant kernel: the apply pass, launched alone on the
+    # state of its head (one chunk's worth of tokens in block mode)
+    n_apply = w.chunk if w.mode == "block" else w.N
+    kv_st = torch.empty(w.B, w.H, 32, 32, device=dev)
+    z_st = torch.empty(w.B, w.H, 32, device=dev)
+    apply_sets = []
+    for s in sets:
+        qa = s["q_chunks"][0] if w.mode == "block" else s["q"]
+        oa = s["o_chunks"][0] if w.mode == "block" else s["o"]
+        apply_sets.append((P(qa.data_ptr()), P(oa.data_ptr()), P(kv_st.data_ptr()), P(z_st.data_ptr()), w.B, w.H,
+                           n_apply, w.D, dt, w.eps, rope_ref, st_ptr))
+    kv_st.zero_()
+    z_st.zero_()
+    k_state = sets[0]["k_chunks"][0] if w.mode == "block" else sets[0]["k"]
+    v_state = sets[0]["v_chunks"][0] if w.mode == "block" else sets[0]["v"]
+    la.sana_linattn_state_update(k_state, v_state, kv_st, z_st, rope=rope, stream=stream)
+    for i in range(args.warmup):
+        L.sana_linattn_apply(*apply_sets[i % n_sets])
+    torch.cuda.synchronize()
+    a_start, a_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a_start.record(stream)
+    for i in range(args.steps):
+        rc = L.sana_linattn_apply(*apply_sets[i % n_sets])
+        if rc:
+            raise la.SanaError(rc)
+    a_end.record(stream)
+    torch.cuda.synchronize()
+    apply_ms = a_start.elapsed_time(a_end) / args.steps
+    apply_bytes = w.B * w.H * n_apply * 2 * w.D * (2 if w.dtype == "bf16" else 4) + w.B * w.H * (32 * 32 + 32) * 4
+    achieved = apply_bytes / (apply_ms / 1e3) / 1e9
     traffic = stored_traffic(w.name)
 
     rec = {
@@ -242,19 +300,24 @@ def main():
                    "chunk": w.chunk, "grid": w.grid, "eps": w.eps, "input_sets_cycled": n_sets},
         "roofline": {
             "bound": "hbm",
-            "kernel": "sana_linattn_forward call (state partials + finalize + apply)"
-                      if w.mode != "block" else "sana_linattn_block_forward call (per chunk)",
+            "kernel": "apply_bf16" if w.dtype == "bf16" else "apply_f32",
             "achieved": achieved,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
             "traffic": traffic,
-            "algorithmic_bytes_per_launch": alg_bytes / launches,
-            "avg_launch_ms": launch_ms,
+            "algorithmic_bytes_per_launch": apply_bytes,
+            "avg_launch_ms": apply_ms,
+            "tokens_per_launch": w.B * w.H * n_apply,
         },
-        "step_ms": {"median": statistics.median(per_step_ms),
-                    "p10": float(np.percentile(per_step_ms, 10)),
-                    "p90": float(np.percentile(per_step_ms, 90))},
+        "call": {
+            "entry_point": "sana_linattn_block_forward (per chunk)" if w.mode == "block" else "sana_linattn_forward",
+            "kernels": "state pass + finalize + apply pass",
+            "avg_ms": call_ms,
+            "algorithmic_bytes": alg_bytes / launches,
+            "achieved_gbps": (alg_bytes / launches) / (call_ms / 1e3) / 1e9,
+            "frac_of_peak": (alg_bytes / launches) / (call_ms / 1e3) / 1e9 / HBM_PEAK_GBPS,
+        },
         "hbm_gbps_step": alg_bytes / (ms_per_step / 1e3) / 1e9,
         "wall_s_timed_region": wall,
         "input_sha256": x.sha256()[:16],

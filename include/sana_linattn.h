@@ -142,6 +142,19 @@ int sana_linattn_block_forward(const void* q, const void* k, const void* v, void
                                int B, int H, int64_t N, int D, int dtype, float eps,
                                const sana_rope* rope, void* ws, size_t ws_bytes, void* hip_stream);
 
+/* Apply a given state to queries, without changing it ("SANA-Video" paper
+ * notes 2.1: the precomputed sum is reused by every token; 2.2: RoPE in the
+ * numerator only):
+ *   O_i = phi~(Q_i) . S / (phi(Q_i) . z + eps),  S = kv_state[b][h], z = ksum_state[b][h]
+ * This is the last step of every other call, on its own: queries read a state
+ * that is already complete (for example one committed by state_update).
+ * q: input [B][H][N][D]; o: output, same shape and dtype, must not overlap q
+ * or the states; kv_state [B][H][D][D] and ksum_state [B][H][D] are read only.
+ * No workspace is used. */
+int sana_linattn_apply(const void* q, void* o, const float* kv_state, const float* ksum_state,
+                       int B, int H, int64_t N, int D, int dtype, float eps,
+                       const sana_rope* rope, void* hip_stream);
+
 /* Host-side builder of 3D RoPE tables ("SANA-Video" paper notes, section 3
  * Stage 2, rotary position encoding extended to space-time).  Token
  * n = (t*Hl + h)*Wl + w; the first dt dims (dt/2 pairs) turn with t, the next

@@ -21,6 +21,7 @@ EXPORTED = (
     "sana_linattn_forward",
     "sana_linattn_state_update",
     "sana_linattn_block_forward",
+    "sana_linattn_apply",
     "sana_linattn_rope3d_table",
     "sana_linattn_status_string",
 )
@@ -54,6 +55,8 @@ def lib():
     L.sana_linattn_block_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, f32,
                                              rp, vp, sz, vp]
     L.sana_linattn_block_forward.restype = i32
+    L.sana_linattn_apply.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32, i32, f32, rp, vp]
+    L.sana_linattn_apply.restype = i32
     L.sana_linattn_rope3d_table.argtypes = [i32, i32, i32, i32, i32, i32, i32, ctypes.c_double, vp, vp]
     L.sana_linattn_rope3d_table.restype = i32
     L.sana_linattn_status_string.argtypes = [i32]
@@ -229,4 +232,22 @@ def sana_linattn_block_forward(q, k, v, o=None, kv_in=None, ksum_in=None, kv_out
     _check(lib().sana_linattn_block_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(kv_in), _ptr(ksum_in),
                                             _ptr(kv_out), _ptr(ksum_out), B, H, N, D, dt, float(eps),
                                             _rope_arg(rope), _ptr(ws), nbytes, _stream(stream, q.device)))
+    return o
+
+
+def sana_linattn_apply(q, kv_state, ksum_state, o=None, eps=1e-6, rope=None, stream=None):
+    """O = phi~(Q).S / (phi(Q).z + eps) for a given state (read only); returns O."""
+    torch = _torch()
+    B, H, N, D = _shape4(q, "q")
+    if o is None:
+        o = torch.empty_like(q)
+    elif _shape4(o, "o") != (B, H, N, D) or o.dtype != q.dtype:
+        raise ValueError("o must match q in shape and dtype")
+    if tuple(kv_state.shape) != (B, H, D, D) or tuple(ksum_state.shape) != (B, H, D):
+        raise ValueError("kv_state must be [B, H, D, D] and ksum_state [B, H, D]")
+    for t in (kv_state, ksum_state):
+        if t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("states must be contiguous float32 device tensors")
+    _check(lib().sana_linattn_apply(_ptr(q), _ptr(o), _ptr(kv_state), _ptr(ksum_state), B, H, N, D, _dtype_code(q),
+                                    float(eps), _rope_arg(rope), _stream(stream, q.device)))
     return o

@@ -296,6 +296,25 @@ int sana_linattn_block_forward(const void* q, const void* k, const void* v, void
   return launch_status();
 }
 
+int sana_linattn_apply(const void* q, void* o, const float* kv_state, const float* ksum_state, int B, int H,
+                       int64_t N, int D, int dtype, float eps, const sana_rope* rope, void* hip_stream) {
+  int64_t bh = 0, elems = 0;
+  int rc = check_sizes(B, H, N, D, dtype, &bh, &elems);
+  if (rc != SANA_OK) return rc;
+  if (!std::isfinite(eps) || eps < 0.f) return SANA_ERR_INVALID;
+  if (elems == 0) return SANA_OK;
+  if (check_tensor(q) || check_tensor(o)) return SANA_ERR_INVALID;
+  if (!kv_state || !ksum_state || !aligned(kv_state, 4) || !aligned(ksum_state, 4)) return SANA_ERR_INVALID;
+  const size_t bytes = (size_t)elems * elem_size(dtype);
+  const size_t kv_bytes = (size_t)bh * 1024 * sizeof(float), ks_bytes = (size_t)bh * 32 * sizeof(float);
+  if (overlaps(o, bytes, q, bytes) || overlaps(o, bytes, kv_state, kv_bytes) || overlaps(o, bytes, ksum_state, ks_bytes))
+    return SANA_ERR_INVALID;
+  if ((rc = check_rope(rope, N)) != SANA_OK) return rc;
+  const Geometry g = make_geometry(bh, N, rope != nullptr);
+  launch_apply(q, o, dtype, eps, g, rope, kv_state, ksum_state, static_cast<hipStream_t>(hip_stream));
+  return launch_status();
+}
+
 int sana_linattn_rope3d_table(int T, int Hl, int Wl, int D, int dt, int dh, int dw, double base, float* cos_host,
                               float* sin_host) {
   if (T < 0 || Hl < 0 || Wl < 0 || D <= 0 || dt < 0 || dh < 0 || dw < 0) return SANA_ERR_INVALID;

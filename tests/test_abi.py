@@ -176,3 +176,19 @@ def test_binding_refuses_host_tensors():
     x = torch.zeros(1, 1, 4, 32, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         la.sana_linattn_forward(x, x, x)
+
+
+def test_apply_argument_errors():
+    L = la.lib()
+
+    def ap(q=A, o=Dp, kv=C, ks=0x50000000, N=64, D=32, eps=1e-6):
+        return L.sana_linattn_apply(q, o, kv, ks, 1, 2, N, D, la.SANA_DT_BF16, eps, None, None)
+
+    assert ap(q=None) == la.SANA_ERR_INVALID
+    assert ap(kv=None) == la.SANA_ERR_INVALID
+    assert ap(ks=None) == la.SANA_ERR_INVALID
+    assert ap(o=A) == la.SANA_ERR_INVALID                 # o aliases q
+    assert ap(o=C) == la.SANA_ERR_INVALID                 # o overlaps the state
+    assert ap(eps=-1.0) == la.SANA_ERR_INVALID
+    assert ap(D=64) == la.SANA_ERR_UNSUPPORTED
+    assert ap(q=None, o=None, kv=None, ks=None, N=0) == la.SANA_OK

@@ -267,3 +267,25 @@ def test_state_update_with_rope_and_offset():
     S_ref, z_ref = oracle.kv_state(x.f64["k"], x.f64["v"], angles=oracle.rope3d_angles(*grid))
     assert rel_l2(to_np(kv), S_ref) <= 1e-5
     assert rel_l2(to_np(z), z_ref) <= 1e-6
+
+
+def test_apply_matches_forward_and_oracle():
+    """forward == state_update into a zero state followed by apply (same
+    kernels, same order of sums), and apply on its own matches the oracle's
+    apply_state for a given state."""
+    torch = torch_mod()
+    for rope_grid in (None, (3, 10, 20)):
+        N = 3000 if rope_grid is None else 3 * 10 * 20
+        w = reduced(WORKLOADS["sana16b_4096px"], H=5, N=N, seed=11)
+        x = generate(w)
+        q, k, v = inputs_on_device(x)
+        rope = None if rope_grid is None else la.rope3d_device(*rope_grid, device())
+        kv = torch.zeros(1, 5, 32, 32, device=device())
+        z = torch.zeros(1, 5, 32, device=device())
+        la.sana_linattn_state_update(k, v, kv, z, rope=rope)
+        o_apply = la.sana_linattn_apply(q, kv, z, eps=w.eps, rope=rope)
+        o_fwd = la.sana_linattn_forward(q, k, v, eps=w.eps, rope=rope)
+        assert torch.equal(o_apply, o_fwd)
+        angles = None if rope_grid is None else oracle.rope3d_angles(*rope_grid)
+        ref = oracle.apply_state(x.f64["q"], to_np(kv), to_np(z), w.eps, angles=angles)
+        check(to_np(o_apply), ref, "bf16", f"apply on a given state (rope={rope_grid})")
