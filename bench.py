@@ -136,6 +136,9 @@ def main():
     ap.add_argument("--workload", default="sana16b_4096px", choices=list(WORKLOADS))
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--block-mode", choices=["chunks", "sequence"], default="chunks",
+                    help="block-causal workload: one block_forward call per chunk (inference, the default) or "
+                         "one block_causal call over the whole sequence (all chunks known at once)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="time a plain 1 GiB device-to-device copy instead (HBM reference and counter scale)")
     args = ap.parse_args()
@@ -186,7 +189,12 @@ def main():
                 s[n + "_chunks"] = [t[:, :, c:min(w.N, c + Lc)].contiguous() for c in range(0, w.N, Lc)]
             s["kv"] = torch.zeros(w.B, w.H, 32, 32, device=dev)
             s["z"] = torch.zeros(w.B, w.H, 32, device=dev)
-        ws = la.make_workspace(w.B, w.H, Lc, dev, dtype=la.SANA_DT_BF16 if w.dtype == "bf16" else la.SANA_DT_F32)
+        dtc = la.SANA_DT_BF16 if w.dtype == "bf16" else la.SANA_DT_F32
+        if args.block_mode == "sequence":
+            nb = la.block_causal_workspace_bytes(w.B, w.H, w.N, Lc, dtype=dtc)
+            ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
+        else:
+            ws = la.make_workspace(w.B, w.H, Lc, dev, dtype=dtc)
     else:
         ws = la.make_workspace(w.B, w.H, w.N, dev, dtype=la.SANA_DT_BF16 if w.dtype == "bf16" else la.SANA_DT_F32,
                                has_rope=rope is not None)
@@ -201,7 +209,11 @@ def main():
     P = ctypes.c_void_p
     calls = []
     for s in sets:
-        if w.mode == "block":
+        if w.mode == "block" and args.block_mode == "sequence":
+            calls.append(("sequence", (P(s["q"].data_ptr()), P(s["k"].data_ptr()), P(s["v"].data_ptr()),
+                                       P(s["o"].data_ptr()), None, None, P(s["kv"].data_ptr()), P(s["z"].data_ptr()),
+                                       w.B, w.H, w.N, w.chunk, w.D, dt, w.eps, None, ws_ptr, ws_n, st_ptr)))
+        elif w.mode == "block":
             seq = []
             for c, (qc, kc, vc, oc) in enumerate(zip(s["q_chunks"], s["k_chunks"], s["v_chunks"], s["o_chunks"])):
                 # chunk 0 starts from the zero state (kv_in = NULL); every chunk commits in place
@@ -218,7 +230,11 @@ def main():
 
     def step(i):
         kind, args = calls[i % n_sets]
-        if kind == "block":
+        if kind == "sequence":
+            rc = L.sana_linattn_block_causal(*args)
+            if rc:
+                raise la.SanaError(rc)
+        elif kind == "block":
             for a in args:
                 rc = L.sana_linattn_block_forward(*a)
                 if rc:
@@ -248,7 +264,7 @@ def main():
     ms_per_step = total_ms / args.steps
     value = w.token_heads * args.steps / (total_ms / 1e3)
     alg_bytes = algorithmic_bytes(w)
-    launches = w.n_chunks if w.mode == "block" else 1
+    launches = w.n_chunks if (w.mode == "block" and args.block_mode == "chunks") else 1
     call_ms = ms_per_step / launches
 
     # roofline of the dominant kernel: the apply pass, launched alone on the
@@ -297,7 +313,8 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic: seeded i.i.d. N(0,1)x0.5 bf16 tensors at the workload's latent shape (no dataset, no weights)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "D": w.D, "mode": w.mode,
-                   "chunk": w.chunk, "grid": w.grid, "eps": w.eps, "input_sets_cycled": n_sets},
+                   "chunk": w.chunk, "grid": w.grid, "eps": w.eps, "input_sets_cycled": n_sets,
+                   "block_calls": args.block_mode if w.mode == "block" else None},
         "roofline": {
             "bound": "hbm",
             "kernel": "apply_bf16" if w.dtype == "bf16" else "apply_f32",
@@ -311,7 +328,9 @@ def main():
             "tokens_per_launch": w.B * w.H * n_apply,
         },
         "call": {
-            "entry_point": "sana_linattn_block_forward (per chunk)" if w.mode == "block" else "sana_linattn_forward",
+            "entry_point": ("sana_linattn_forward" if w.mode != "block" else
+                            "sana_linattn_block_causal (whole sequence)" if args.block_mode == "sequence" else
+                            "sana_linattn_block_forward (per chunk)"),
             "kernels": "state pass + finalize + apply pass",
             "avg_ms": call_ms,
             "algorithmic_bytes": alg_bytes / launches,

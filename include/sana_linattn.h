@@ -51,7 +51,7 @@
  *   Errors     Arguments are checked before anything is enqueued; on error
  *              nothing is launched and a negative sana_status is returned:
  *                SANA_ERR_INVALID      NULL pointer where work exists, B, H or
- *                                      N negative, D <= 0, unknown dtype,
+ *                                      N negative, chunk <= 0, D <= 0, unknown dtype,
  *                                      non-finite or negative eps, misaligned
  *                                      pointer, O overlapping Q/K/V, RoPE rows
  *                                      out of the table, size overflow
@@ -99,9 +99,9 @@ typedef struct {
     int64_t pos_offset;
 } sana_rope;
 
-/* Bytes of device workspace that the three compute entry points need for
- * these sizes (0 when B*H*N == 0).  Pure host function, no HIP call.  Returns
- * 0 as well for invalid sizes; the entry points then reject the sizes. */
+/* Bytes of device workspace that forward, state_update and block_forward need
+ * for these sizes (0 when B*H*N == 0).  Pure host function, no HIP call.
+ * Returns 0 as well for invalid sizes; the entry points then reject them. */
 size_t sana_linattn_workspace_bytes(int B, int H, int64_t N, int D, int dtype, int has_rope);
 
 /* Non-causal forward ("Sana" research note, Model architecture item 2;
@@ -141,6 +141,32 @@ int sana_linattn_block_forward(const void* q, const void* k, const void* v, void
                                float* kv_out, float* ksum_out,
                                int B, int H, int64_t N, int D, int dtype, float eps,
                                const sana_rope* rope, void* ws, size_t ws_bytes, void* hip_stream);
+
+/* A whole sequence in block-causal chunks, in one call ("SANA-Video" paper
+ * notes 2.3 and section 3's block-wise training; news article "Design
+ * details": later blocks see earlier ones, never the reverse, and each block
+ * sums KVsum with its own KV).  Token n of a head belongs to chunk
+ * c(n) = n / chunk (the last chunk may be shorter); with
+ *   S_c = kv_in + sum_{j : c(j) <= c} phi~(K_j)^T V_j,  z_c = ksum_in + sum phi(K_j)
+ *   O_n = phi~(Q_n) . S_{c(n)} / (phi(Q_n) . z_{c(n)} + eps)
+ * i.e. the same result as calling block_forward chunk after chunk with an
+ * in-place commit, for when every chunk's Q, K, V is available at once (block
+ * training, re-encoding a sequence).  kv_in/ksum_in: state before the first
+ * chunk, or both NULL for zero; kv_out/ksum_out: where the state after the
+ * last chunk is committed, or both NULL (may equal kv_in/ksum_in).  chunk must
+ * be positive; chunk >= N is one chunk (the same as block_forward).  With
+ * rope, token n sits at global position pos_offset + n.  Workspace:
+ * sana_linattn_block_causal_workspace_bytes. */
+int sana_linattn_block_causal(const void* q, const void* k, const void* v, void* o,
+                              const float* kv_in, const float* ksum_in,
+                              float* kv_out, float* ksum_out,
+                              int B, int H, int64_t N, int64_t chunk, int D, int dtype, float eps,
+                              const sana_rope* rope, void* ws, size_t ws_bytes, void* hip_stream);
+
+/* Workspace bytes for sana_linattn_block_causal with these sizes (0 when
+ * B*H*N == 0 or the sizes are invalid).  Pure host function. */
+size_t sana_linattn_block_causal_workspace_bytes(int B, int H, int64_t N, int64_t chunk, int D, int dtype,
+                                                 int has_rope);
 
 /* Apply a given state to queries, without changing it ("SANA-Video" paper
  * notes 2.1: the precomputed sum is reused by every token; 2.2: RoPE in the

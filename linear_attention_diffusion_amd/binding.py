@@ -21,6 +21,8 @@ EXPORTED = (
     "sana_linattn_forward",
     "sana_linattn_state_update",
     "sana_linattn_block_forward",
+    "sana_linattn_block_causal",
+    "sana_linattn_block_causal_workspace_bytes",
     "sana_linattn_apply",
     "sana_linattn_rope3d_table",
     "sana_linattn_status_string",
@@ -55,6 +57,11 @@ def lib():
     L.sana_linattn_block_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, f32,
                                              rp, vp, sz, vp]
     L.sana_linattn_block_forward.restype = i32
+    L.sana_linattn_block_causal.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i64, i64, i32, i32, f32,
+                                            rp, vp, sz, vp]
+    L.sana_linattn_block_causal.restype = i32
+    L.sana_linattn_block_causal_workspace_bytes.argtypes = [i32, i32, i64, i64, i32, i32, i32]
+    L.sana_linattn_block_causal_workspace_bytes.restype = sz
     L.sana_linattn_apply.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32, i32, f32, rp, vp]
     L.sana_linattn_apply.restype = i32
     L.sana_linattn_rope3d_table.argtypes = [i32, i32, i32, i32, i32, i32, i32, ctypes.c_double, vp, vp]
@@ -232,6 +239,36 @@ def sana_linattn_block_forward(q, k, v, o=None, kv_in=None, ksum_in=None, kv_out
     _check(lib().sana_linattn_block_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(kv_in), _ptr(ksum_in),
                                             _ptr(kv_out), _ptr(ksum_out), B, H, N, D, dt, float(eps),
                                             _rope_arg(rope), _ptr(ws), nbytes, _stream(stream, q.device)))
+    return o
+
+
+def block_causal_workspace_bytes(B, H, N, chunk, D=32, dtype=SANA_DT_BF16, has_rope=False):
+    return int(lib().sana_linattn_block_causal_workspace_bytes(B, H, N, chunk, D, dtype, int(bool(has_rope))))
+
+
+def sana_linattn_block_causal(q, k, v, chunk, o=None, kv_in=None, ksum_in=None, kv_out=None, ksum_out=None,
+                              eps=1e-6, rope=None, workspace=None, stream=None):
+    """A whole sequence in block-causal chunks of `chunk` tokens; returns O.
+    kv_in/ksum_in None = zero state; kv_out/ksum_out None = do not commit."""
+    torch = _torch()
+    B, H, N, D = _shape4(q, "q")
+    if _shape4(k, "k") != (B, H, N, D) or _shape4(v, "v") != (B, H, N, D):
+        raise ValueError("q, k, v must have the same shape")
+    if o is None:
+        o = torch.empty_like(q)
+    elif _shape4(o, "o") != (B, H, N, D) or o.dtype != q.dtype:
+        raise ValueError("o must match q in shape and dtype")
+    for t, shape in ((kv_in, (B, H, D, D)), (ksum_in, (B, H, D)), (kv_out, (B, H, D, D)), (ksum_out, (B, H, D))):
+        if t is not None and (tuple(t.shape) != shape or t.dtype != torch.float32 or not t.is_contiguous()):
+            raise ValueError("states must be contiguous float32 [B, H, D, D] / [B, H, D]")
+    dt = _dtype_code(q)
+    if workspace is None:
+        workspace = torch.empty(max(block_causal_workspace_bytes(B, H, N, chunk, D, dt, rope is not None), 256),
+                                dtype=torch.uint8, device=q.device)
+    _check(lib().sana_linattn_block_causal(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(kv_in), _ptr(ksum_in),
+                                           _ptr(kv_out), _ptr(ksum_out), B, H, N, int(chunk), D, dt, float(eps),
+                                           _rope_arg(rope), _ptr(workspace), workspace.numel(),
+                                           _stream(stream, q.device)))
     return o
 
 

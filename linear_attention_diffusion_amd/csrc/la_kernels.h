@@ -29,12 +29,18 @@
 // per product term kept: with one exact bf16 operand that is 3 terms; with two
 // split operands the 6 terms of weight >= 2^-16 (hh, hm, mh, hl, lh, mm).
 //
+// Sequence layout: each head's N tokens form C chunks of L tokens (the last may
+// be shorter); a call without chunks has C = 1, L = N.  Each chunk is reduced
+// by Pc workgroups ("splits").
+//
 // Reduction of the split-N partials: every state workgroup writes its partial
-// (or, when a head has a single split, the finished state); a separate
-// finalize kernel then sums each head's P partials in split order
-// (deterministic) plus the carried state.  The kernel boundary makes the
-// partials visible across all XCDs; an in-kernel hand-off would need an L2
-// write-back per publishing wave, which costs far more at this grid size.
+// (or, when a head has a single chunk and split, the finished state); a
+// separate finalize kernel then walks each head's C x Pc partials in order
+// (deterministic), adding them to the carried state, and stores the running
+// sum at the end of every chunk: chunk c's state is S_in plus everything up
+// to and including chunk c.  The kernel boundary makes the partials visible
+// across all XCDs; an in-kernel hand-off would need an L2 write-back per
+// publishing wave, which costs far more at this grid size.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -52,14 +58,28 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x2_t __attribute__((ext_vector_type(2)));
 
-// Where a state pass puts its result.
+// Geometry of the state pass and where its results go.
 struct StateArgs {
-  float* partials;                 // [BH][P][33][32] scratch (P > 1)
+  float* partials;                 // [BH][C][Pc][33][32] scratch (when C * Pc > 1)
+  float* states;                   // [BH][C][33][32]: state of every chunk, read by the apply pass
   const float* kv_in;              // carried state [BH][32][32] or null (zero)
   const float* ksum_in;            // [BH][32] or null
-  float* kv_out;                   // S_new destination [BH][32][32] (may equal kv_in)
-  float* ksum_out;                 // z_new destination [BH][32] (may equal ksum_in)
-  int P;                           // partials per head
+  float* kv_out;                   // commit of the last chunk's state [BH][32][32] or null; may equal kv_in
+  float* ksum_out;                 // [BH][32] or null; may equal ksum_in
+  int64_t N;                       // tokens per head
+  int64_t L;                       // tokens per chunk
+  int64_t Ls;                      // tokens per split
+  int C;                           // chunks per head
+  int Pc;                          // splits per chunk
+};
+
+// Where the apply pass finds the state of (head bh, chunk c): S at
+// s_base + (bh * C + c) * s_stride (32 x 32), z at z_base + (bh * C + c) * z_stride.
+struct StateView {
+  const float* s_base;
+  const float* z_base;
+  int64_t s_stride;
+  int64_t z_stride;
 };
 
 // ---------------------------------------------------------------------------
@@ -116,49 +136,78 @@ __device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
 // Writing a workgroup's partial state, and the finalize kernel
 // ---------------------------------------------------------------------------
 
-// S_in + x into the state destination, element idx of the 33 x 32 layout.
-__device__ __forceinline__ void store_state(const StateArgs& a, int64_t bh, int idx, float x) {
-  if (idx < 1024) {
-    if (a.kv_in) x = a.kv_in[bh * 1024 + idx] + x;
-    a.kv_out[bh * 1024 + idx] = x;
-  } else {
-    if (a.ksum_in) x = a.ksum_in[bh * 32 + (idx - 1024)] + x;
-    a.ksum_out[bh * 32 + (idx - 1024)] = x;
-  }
+// Element idx (33 x 32 layout) of the carried state, 0 when there is none.
+__device__ __forceinline__ float carried(const StateArgs& a, int64_t bh, int idx) {
+  if (idx < 1024) return a.kv_in ? a.kv_in[bh * 1024 + idx] : 0.f;
+  return a.ksum_in ? a.ksum_in[bh * 32 + (idx - 1024)] : 0.f;
 }
 
-// `mine` (LDS, 33x32 floats) holds this workgroup's sum for head bh, split s.
-// With one split per head it is already the head's sum and goes straight to
-// the destination; otherwise it is stored as partial s.
-__device__ __forceinline__ void write_partial(const float* mine, int64_t bh, int s, const StateArgs& a) {
-  if (a.P == 1) {
-    for (int idx = threadIdx.x; idx < kStateElems; idx += kThreads) store_state(a, bh, idx, mine[idx]);
+// Stores element idx of the last chunk's state as the committed state.
+__device__ __forceinline__ void commit(const StateArgs& a, int64_t bh, int idx, float x) {
+  if (idx < 1024)
+    a.kv_out[bh * 1024 + idx] = x;
+  else
+    a.ksum_out[bh * 32 + (idx - 1024)] = x;
+}
+
+// `mine` (LDS, 33x32 floats) holds this workgroup's sum for head bh, chunk c,
+// split s.  With a single chunk and split it is already the head's sum: it
+// goes, with the carried state added, straight to the state (and the
+// commit); otherwise it is stored as a partial.
+__device__ __forceinline__ void write_partial(const float* mine, int64_t bh, int c, int s, const StateArgs& a) {
+  if (a.C * a.Pc == 1) {
+    for (int idx = threadIdx.x; idx < kStateElems; idx += kThreads) {
+      const float x = carried(a, bh, idx) + mine[idx];
+      a.states[bh * kStateElems + idx] = x;
+      if (a.kv_out) commit(a, bh, idx, x);
+    }
   } else {
-    float* out = a.partials + ((int64_t)bh * a.P + s) * kStateElems;
+    float* out = a.partials + (((int64_t)bh * a.C + c) * a.Pc + s) * kStateElems;
     for (int idx = threadIdx.x; idx < kStateElems; idx += kThreads) out[idx] = mine[idx];
   }
 }
 
-// One thread per state element of every head: S_new = S_in + sum_s partial_s,
-// summed in split order.  A thread issues the loads of 16 partials at once
-// (the ones past P read as 0, which leaves the ordered sum unchanged) before
-// its first add.  kv_out may alias kv_in: each element is read and written by
-// the same thread.
+// One thread per state element of every head.  It walks the head's C x Pc
+// partials in order, 16 loads in flight at a time (loads past the end read 0,
+// which leaves the ordered sum unchanged), adding each to the carried state,
+// and stores the running sum at the end of every chunk; the last one is also
+// committed.  kv_out may alias kv_in: each element is read and written by the
+// same thread.
 __global__ __launch_bounds__(kThreads) void state_finalize(StateArgs a, int64_t n_elems) {
   const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (i >= n_elems) return;
   const int64_t bh = i / kStateElems;
   const int idx = (int)(i % kStateElems);
-  const float* src = a.partials + bh * a.P * kStateElems + idx;
-  float acc = 0.f;
-  for (int sp = 0; sp < a.P; sp += 16) {
+  const int total = a.C * a.Pc;
+  const float* src = a.partials + bh * total * kStateElems + idx;
+  float* dst = a.states + bh * a.C * kStateElems + idx;
+  float acc = carried(a, bh, idx);
+  for (int q0 = 0; q0 < total; q0 += 16) {
     float v[16];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) v[u] = (sp + u < a.P) ? src[(int64_t)(sp + u) * kStateElems] : 0.f;
+    for (int u = 0; u < 16; ++u) v[u] = (q0 + u < total) ? src[(int64_t)(q0 + u) * kStateElems] : 0.f;
 #pragma unroll
-    for (int u = 0; u < 16; ++u) acc += v[u];
+    for (int u = 0; u < 16; ++u) {
+      const int q = q0 + u;
+      acc += v[u];
+      if (q < total && (q + 1) % a.Pc == 0) dst[(int64_t)(q / a.Pc) * kStateElems] = acc;
+    }
   }
-  store_state(a, bh, idx, acc);
+  if (a.kv_out) commit(a, bh, idx, acc);
+}
+
+// Token range [n_begin, n_end) of state workgroup (bh, c, s) = blockIdx.x.
+__device__ __forceinline__ void state_item(const StateArgs& a, int64_t& bh, int& c, int& s, int64_t& n_begin,
+                                           int64_t& n_end) {
+  const int per_head = a.C * a.Pc;
+  bh = blockIdx.x / per_head;
+  const int r = blockIdx.x % per_head;
+  c = r / a.Pc;
+  s = r % a.Pc;
+  const int64_t c_begin = (int64_t)c * a.L;
+  const int64_t c_end = (c_begin + a.L < a.N) ? c_begin + a.L : a.N;
+  n_begin = c_begin + (int64_t)s * a.Ls;
+  n_end = (n_begin + a.Ls < c_end) ? n_begin + a.Ls : c_end;
 }
 
 // ---------------------------------------------------------------------------
@@ -292,15 +341,15 @@ __device__ __forceinline__ void load_rows(const u32x4_t* X, int64_t t0, int64_t 
 
 template <bool ROPE>
 __global__ __launch_bounds__(kThreads) void state_bf16(const u32x4_t* __restrict__ K, const u32x4_t* __restrict__ V,
-                                                       int64_t N, int64_t Ls, const float* __restrict__ cos_t,
+                                                       const float* __restrict__ cos_t,
                                                        const float* __restrict__ sin_t, int64_t pos0,
                                                        StateArgs a) {
   __shared__ float red[4][kStateElems];
 
-  const int64_t bh = blockIdx.x / a.P;
-  const int s = blockIdx.x % a.P;
-  const int64_t n_begin = (int64_t)s * Ls;
-  const int64_t n_end = (n_begin + Ls < N) ? n_begin + Ls : N;
+  int64_t bh, n_begin, n_end;
+  int c, s;
+  state_item(a, bh, c, s, n_begin, n_end);
+  const int64_t N = a.N;
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int n = lane & 15;
@@ -365,7 +414,7 @@ __global__ __launch_bounds__(kThreads) void state_bf16(const u32x4_t* __restrict
   for (int idx = threadIdx.x; idx < kStateElems; idx += kThreads)
     red[0][idx] = (red[0][idx] + red[1][idx]) + (red[2][idx] + red[3][idx]);
   __syncthreads();
-  write_partial(red[0], bh, s, a);
+  write_partial(red[0], bh, c, s, a);
 }
 
 // ---------------------------------------------------------------------------
@@ -373,7 +422,7 @@ __global__ __launch_bounds__(kThreads) void state_bf16(const u32x4_t* __restrict
 // ---------------------------------------------------------------------------
 template <bool ROPE>
 __global__ __launch_bounds__(kThreads) void state_f32(const float* __restrict__ K, const float* __restrict__ V,
-                                                      int64_t N, int64_t Ls, const float* __restrict__ cos_t,
+                                                      const float* __restrict__ cos_t,
                                                       const float* __restrict__ sin_t, int64_t pos0,
                                                       StateArgs a) {
   __shared__ float sk[64][kD + 1];   // phi(K), un-rotated
@@ -381,10 +430,10 @@ __global__ __launch_bounds__(kThreads) void state_f32(const float* __restrict__ 
   __shared__ float sv[64][kD + 1];
   __shared__ float mine[kStateElems];
 
-  const int64_t bh = blockIdx.x / a.P;
-  const int s = blockIdx.x % a.P;
-  const int64_t n_begin = (int64_t)s * Ls;
-  const int64_t n_end = (n_begin + Ls < N) ? n_begin + Ls : N;
+  int64_t bh, n_begin, n_end;
+  int c, s;
+  state_item(a, bh, c, s, n_begin, n_end);
+  const int64_t N = a.N;
   const int t = threadIdx.x;
   const int d = t >> 3;
   const int e0 = (t & 7) * 4;
@@ -435,7 +484,7 @@ __global__ __launch_bounds__(kThreads) void state_f32(const float* __restrict__ 
   for (int c = 0; c < 4; ++c) mine[d * 32 + e0 + c] = acc[c];
   if (e0 == 0) mine[1024 + d] = zacc;
   __syncthreads();
-  write_partial(mine, bh, s, a);
+  write_partial(mine, bh, c, s, a);
 }
 
 // ---------------------------------------------------------------------------
@@ -571,8 +620,7 @@ __device__ __forceinline__ void load_apply_chunk(const u32x4_t* Qh, int64_t t0, 
 
 template <bool ROPE>
 __global__ __launch_bounds__(kThreads) void apply_bf16(const u32x4_t* __restrict__ Q, u32x4_t* __restrict__ O,
-                                                       const float* __restrict__ kv,
-                                                       const float* __restrict__ ksum, int64_t N, int64_t total,
+                                                       StateView sv, int64_t N, int64_t L, int C, int64_t total,
                                                        int64_t La, float eps, const float* __restrict__ cos_t,
                                                        const float* __restrict__ sin_t, int64_t pos0) {
   const int lane = threadIdx.x & 63;
@@ -582,12 +630,14 @@ __global__ __launch_bounds__(kThreads) void apply_bf16(const u32x4_t* __restrict
   const int64_t f_begin = (int64_t)blockIdx.x * La;
   const int64_t f_end = (f_begin + La < total) ? f_begin + La : total;
 
+  // the range is processed in segments that stay inside one head and chunk
   for (int64_t f = f_begin; f < f_end;) {
     const int64_t bh = f / N;
-    const int64_t seg_end = (f_end < (bh + 1) * N) ? f_end : (bh + 1) * N;
     const int64_t n_begin = f - bh * N;
-    const int64_t n_end = seg_end - bh * N;
-    f = seg_end;
+    const int c = (int)(n_begin / L);
+    const int64_t c_end = ((int64_t)c + 1) * L < N ? ((int64_t)c + 1) * L : N;
+    const int64_t n_end = (f_end - bh * N < c_end) ? f_end - bh * N : c_end;
+    f = bh * N + n_end;
     const u32x4_t* Qh = Q + bh * N * 4 + g;  // 4 x 16 bytes per token row
     u32x4_t* Oh = O + bh * N * 4 + g;
 
@@ -597,7 +647,8 @@ __global__ __launch_bounds__(kThreads) void apply_bf16(const u32x4_t* __restrict
     ApplyChunk<ROPE> next;
     if (t0 < n_end) load_apply_chunk<ROPE>(Qh, t0, n_end, m, g, cos_t, sin_t, pos0, next);
     ApplyOperands op;
-    load_apply_operands(kv + bh * 1024, ksum + bh * 32, g, m, op);
+    const int64_t sc = bh * C + c;
+    load_apply_operands(sv.s_base + sc * sv.s_stride, sv.z_base + sc * sv.z_stride, g, m, op);
 
     for (; t0 < n_end; t0 += 256) {
       const ApplyChunk<ROPE> cur = next;
@@ -615,21 +666,25 @@ __global__ __launch_bounds__(kThreads) void apply_bf16(const u32x4_t* __restrict
 // ---------------------------------------------------------------------------
 // fp32 apply pass (VALU): thread = (token, 4 output features)
 // ---------------------------------------------------------------------------
+// Workgroup (bh, c, tile) applies tokens [c*L + tile*Lt, ...) of chunk c.
 template <bool ROPE>
 __global__ __launch_bounds__(kThreads) void apply_f32(const float* __restrict__ Q, float* __restrict__ O,
-                                                      const float* __restrict__ kv,
-                                                      const float* __restrict__ ksum, int64_t N, int T,
+                                                      StateView sv, int64_t N, int64_t L, int C, int T,
                                                       int64_t Lt, float eps, const float* __restrict__ cos_t,
                                                       const float* __restrict__ sin_t, int64_t pos0) {
   __shared__ float sS[kD][kD];
   __shared__ float sz[kD];
-  const int64_t bh = blockIdx.x / T;
-  const int tile = blockIdx.x % T;
-  const int64_t n_begin = (int64_t)tile * Lt;
-  const int64_t n_end = (n_begin + Lt < N) ? n_begin + Lt : N;
+  const int64_t bh = blockIdx.x / ((int64_t)C * T);
+  const int r = (int)(blockIdx.x % ((int64_t)C * T));
+  const int c = r / T;
+  const int tile = r % T;
+  const int64_t c_end = ((int64_t)c + 1) * L < N ? ((int64_t)c + 1) * L : N;
+  const int64_t n_begin = (int64_t)c * L + (int64_t)tile * Lt;
+  const int64_t n_end = (n_begin + Lt < c_end) ? n_begin + Lt : c_end;
   const int t = threadIdx.x;
-  for (int idx = t; idx < 1024; idx += kThreads) sS[idx >> 5][idx & 31] = kv[bh * 1024 + idx];
-  if (t < kD) sz[t] = ksum[bh * 32 + t];
+  const int64_t sc = bh * C + c;
+  for (int idx = t; idx < 1024; idx += kThreads) sS[idx >> 5][idx & 31] = sv.s_base[sc * sv.s_stride + idx];
+  if (t < kD) sz[t] = sv.z_base[sc * sv.z_stride + t];
   __syncthreads();
   const int tl = t >> 3;
   const int e0 = (t & 7) * 4;

@@ -1,15 +1,21 @@
 // Host side of the C ABI declared in include/sana_linattn.h: argument checks,
 // launch geometry, workspace layout and the 3D RoPE table builder.
 //
-// A compute call enqueues up to three kernels on the caller's stream:
-//   1. state pass  (P workgroups per head, each a contiguous token range,
-//                   writing one partial state each; with P = 1 the workgroup
-//                   writes the head's state itself)
-//   2. finalize    (P > 1 only: one thread per state element sums the P
-//                   partials in order and adds the carried state)
+// Every compute call works on heads of N tokens split into C chunks of L
+// tokens (C = 1 for all calls but block_causal) and enqueues up to three
+// kernels on the caller's stream:
+//   1. state pass  (Pc workgroups per chunk, each a contiguous token range,
+//                   writing one partial state; with one chunk and one split
+//                   the workgroup writes the head's state itself)
+//   2. finalize    (when there are several partials: one thread per state
+//                   element walks a head's partials in order from the carried
+//                   state, storing the running sum at every chunk end and
+//                   committing the last)
 //   3. apply pass  (equal contiguous ranges of the flattened head x token
-//                   space, one per workgroup)
-// state_update runs 1-2 only.  Nothing is allocated, freed or synchronised.
+//                   space, one per workgroup, each cut at head and chunk
+//                   boundaries)
+// state_update runs 1-2 only, apply runs 3 only.  Nothing is allocated, freed
+// or synchronised.
 
 #include "sana_linattn.h"
 
@@ -29,10 +35,9 @@ namespace {
 // in flight), apply 3 per CU (2 with RoPE, whose register use allows no more).
 constexpr int64_t kCUs = 256;
 constexpr int64_t kStateGroups = kCUs * 2;
-constexpr int64_t kStateGroupsRope = kCUs * 2;
 constexpr int64_t kApplyGroups = kCUs * 3;
 constexpr int64_t kApplyGroupsRope = kCUs * 2;
-constexpr int64_t kMaxSplits = 64;       // partial states per head
+constexpr int64_t kMaxSplits = 64;       // partial states per chunk
 constexpr int64_t kMinSplitTokens = 256;
 constexpr int64_t kMinApplyTokens = 256;
 constexpr int64_t kMinApplyTokensF32 = 256;
@@ -44,47 +49,54 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 
 struct Geometry {
-  int64_t BH = 0, N = 0;
-  int64_t P = 0, Ls = 0;   // state pass: splits per head, tokens per split
+  int64_t BH = 0, N = 0, L = 0, C = 0;
+  int64_t Pc = 0, Ls = 0;  // state pass: splits per chunk, tokens per split
   int64_t Ga = 0, La = 0;  // bf16 apply pass: workgroups, flattened tokens per workgroup
-  int64_t T = 0, Lt = 0;   // fp32 apply pass: tiles per head, tokens per tile
+  int64_t T = 0, Lt = 0;   // fp32 apply pass: tiles per chunk, tokens per tile
   size_t partial_off = 0, state_off = 0, total_bytes = 0;
 };
 
-Geometry make_geometry(int64_t BH, int64_t N, bool rope) {
+// Heads of N tokens in chunks of L (L >= N: one chunk).
+Geometry make_geometry(int64_t BH, int64_t N, int64_t L, bool rope) {
   Geometry g;
   g.BH = BH;
   g.N = N;
   if (BH <= 0 || N <= 0) return g;
-  const int64_t apply_groups = rope ? kApplyGroupsRope : kApplyGroups;
-  int64_t p = (rope ? kStateGroupsRope : kStateGroups) / BH;
-  const int64_t p_max = ceil_div(N, kMinSplitTokens);
+  g.L = L < N ? L : N;
+  g.C = ceil_div(N, g.L);
+  // splits per chunk: about kStateGroups workgroups in all, at least
+  // kMinSplitTokens tokens each
+  int64_t p = ceil_div(kStateGroups / BH, g.C);
+  const int64_t p_max = ceil_div(g.L, kMinSplitTokens);
   if (p > p_max) p = p_max;
   if (p > kMaxSplits) p = kMaxSplits;
   if (p < 1) p = 1;
-  g.Ls = round_up(ceil_div(N, p), 32);
-  g.P = ceil_div(N, g.Ls);
+  g.Ls = round_up(ceil_div(g.L, p), 32);
+  g.Pc = ceil_div(g.L, g.Ls);
 
   const int64_t total = BH * N;
-  int64_t la = round_up(ceil_div(total, apply_groups), 64);
+  int64_t la = round_up(ceil_div(total, rope ? kApplyGroupsRope : kApplyGroups), 64);
   if (la < kMinApplyTokens) la = kMinApplyTokens;
   if (ceil_div(total, la) > kMaxGroups) la = round_up(ceil_div(total, kMaxGroups), 64);
   g.La = la;
   g.Ga = ceil_div(total, la);
 
-  int64_t lt = round_up(ceil_div(N, ceil_div(apply_groups, BH)), 64);
+  int64_t lt = round_up(ceil_div(g.L, ceil_div(kApplyGroups, BH * g.C)), 64);
   if (lt < kMinApplyTokensF32) lt = kMinApplyTokensF32;
   if (lt > kMaxApplyTokensF32) lt = kMaxApplyTokensF32;
-  const int64_t lt_floor = round_up(ceil_div(N, kMaxGroups / BH), 64);
-  if (lt < lt_floor) lt = lt_floor;
+  const int64_t per = kMaxGroups / (BH * g.C);
+  if (per >= 1) {
+    const int64_t lt_floor = round_up(ceil_div(g.L, per), 64);
+    if (lt < lt_floor) lt = lt_floor;
+  }
   g.Lt = lt;
-  g.T = ceil_div(N, lt);
+  g.T = ceil_div(g.L, lt);
 
-  const size_t partial_bytes = g.P > 1 ? (size_t)(BH * g.P) * la::kStateElems * sizeof(float) : 0;
-  const size_t state_bytes = (size_t)BH * la::kStateElems * sizeof(float);
+  const int64_t state = (int64_t)la::kStateElems * (int64_t)sizeof(float);
+  const int64_t partials = g.C * g.Pc > 1 ? BH * g.C * g.Pc * state : 0;
   g.partial_off = 0;
-  g.state_off = (size_t)round_up((int64_t)partial_bytes, 256);
-  g.total_bytes = g.state_off + (size_t)round_up((int64_t)state_bytes, 256);
+  g.state_off = (size_t)round_up(partials, 256);
+  g.total_bytes = g.state_off + (size_t)round_up(BH * g.C * state, 256);
   return g;
 }
 
@@ -106,7 +118,7 @@ int check_sizes(int B, int H, int64_t N, int D, int dtype, int64_t* BH, int64_t*
   if (D != la::kD) return SANA_ERR_UNSUPPORTED;
   const int64_t bh = (int64_t)B * (int64_t)H;
   if (bh > 0 && N > (INT64_MAX / 64) / bh) return SANA_ERR_INVALID;
-  if (bh * kMaxSplits > kMaxGroups) return SANA_ERR_INVALID;  // state-pass grid bound
+  if (bh > kMaxGroups) return SANA_ERR_INVALID;
   *BH = bh;
   *elems = bh * N * D;
   return SANA_OK;
@@ -121,7 +133,11 @@ int check_rope(const sana_rope* rope, int64_t N) {
   return SANA_OK;
 }
 
+// Grid bounds of the state pass and the fp32 apply pass.
+bool grids_fit(const Geometry& g) { return g.BH * g.C * g.Pc <= kMaxGroups && g.BH * g.C * g.T <= kMaxGroups; }
+
 int check_workspace(const Geometry& g, const void* ws, size_t ws_bytes) {
+  if (!grids_fit(g)) return SANA_ERR_INVALID;
   if (!ws || ws_bytes < g.total_bytes) return SANA_ERR_WORKSPACE;
   if (!aligned(ws, 256)) return SANA_ERR_INVALID;
   return SANA_OK;
@@ -129,49 +145,80 @@ int check_workspace(const Geometry& g, const void* ws, size_t ws_bytes) {
 
 int check_tensor(const void* p) { return (p && aligned(p, 16)) ? SANA_OK : SANA_ERR_INVALID; }
 
-float* ws_at(void* ws, size_t off) { return reinterpret_cast<float*>(static_cast<char*>(ws) + off); }
+// q/k/v/o against one another and against the state buffers: o may not
+// overlap anything; among the states only exact in-place aliasing
+// (kv_out == kv_in, ksum_out == ksum_in) is allowed.
+int check_overlaps(const void* q, const void* k, const void* v, const void* o, size_t bytes, const float* kv_in,
+                   const float* ksum_in, const float* kv_out, const float* ksum_out, int64_t bh) {
+  if (overlaps(o, bytes, q, bytes) || overlaps(o, bytes, k, bytes) || overlaps(o, bytes, v, bytes))
+    return SANA_ERR_INVALID;
+  const size_t kv_bytes = (size_t)bh * 1024 * sizeof(float), ks_bytes = (size_t)bh * 32 * sizeof(float);
+  const void* tensors[4] = {q, k, v, o};
+  const void* states[4] = {kv_in, ksum_in, kv_out, ksum_out};
+  const size_t state_sizes[4] = {kv_bytes, ks_bytes, kv_bytes, ks_bytes};
+  for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 4; ++j)
+      if (overlaps(states[i], state_sizes[i], tensors[j], bytes)) return SANA_ERR_INVALID;
+  if (overlaps(kv_in, kv_bytes, ksum_in, ks_bytes) || overlaps(kv_out, kv_bytes, ksum_out, ks_bytes) ||
+      overlaps(kv_in, kv_bytes, ksum_out, ks_bytes) || overlaps(ksum_in, ks_bytes, kv_out, kv_bytes))
+    return SANA_ERR_INVALID;
+  if (kv_out && overlaps(kv_in, kv_bytes, kv_out, kv_bytes) && kv_in != kv_out) return SANA_ERR_INVALID;
+  if (ksum_out && overlaps(ksum_in, ks_bytes, ksum_out, ks_bytes) && ksum_in != ksum_out) return SANA_ERR_INVALID;
+  return SANA_OK;
+}
 
 la::StateArgs state_args(void* ws, const Geometry& g, const float* kv_in, const float* ksum_in, float* kv_out,
                          float* ksum_out) {
   la::StateArgs a;
-  a.partials = ws_at(ws, g.partial_off);
+  a.partials = reinterpret_cast<float*>(static_cast<char*>(ws) + g.partial_off);
+  a.states = reinterpret_cast<float*>(static_cast<char*>(ws) + g.state_off);
   a.kv_in = kv_in;
   a.ksum_in = ksum_in;
   a.kv_out = kv_out;
   a.ksum_out = ksum_out;
-  a.P = (int)g.P;
+  a.N = g.N;
+  a.L = g.L;
+  a.Ls = g.Ls;
+  a.C = (int)g.C;
+  a.Pc = (int)g.Pc;
   return a;
 }
 
+// The workspace's per-chunk states (33 x 32 layout), as the apply pass reads them.
+la::StateView ws_view(const la::StateArgs& a) {
+  return la::StateView{a.states, a.states + 1024, la::kStateElems, la::kStateElems};
+}
+
+// State pass, and the finalize when there are several partials per head.
 void launch_state(const void* k, const void* v, int dtype, const Geometry& g, const sana_rope* rope,
                   const la::StateArgs& a, hipStream_t st) {
   const float* ct = rope ? rope->cos : nullptr;
   const float* sn = rope ? rope->sin : nullptr;
   const int64_t pos0 = rope ? rope->pos_offset : 0;
-  const dim3 grid((unsigned)(g.BH * g.P)), block(la::kThreads);
+  const dim3 grid((unsigned)(g.BH * g.C * g.Pc)), block(la::kThreads);
   if (dtype == SANA_DT_BF16) {
     const la::u32x4_t* K = static_cast<const la::u32x4_t*>(k);
     const la::u32x4_t* V = static_cast<const la::u32x4_t*>(v);
     if (rope)
-      la::state_bf16<true><<<grid, block, 0, st>>>(K, V, g.N, g.Ls, ct, sn, pos0, a);
+      la::state_bf16<true><<<grid, block, 0, st>>>(K, V, ct, sn, pos0, a);
     else
-      la::state_bf16<false><<<grid, block, 0, st>>>(K, V, g.N, g.Ls, ct, sn, pos0, a);
+      la::state_bf16<false><<<grid, block, 0, st>>>(K, V, ct, sn, pos0, a);
   } else {
     const float* K = static_cast<const float*>(k);
     const float* V = static_cast<const float*>(v);
     if (rope)
-      la::state_f32<true><<<grid, block, 0, st>>>(K, V, g.N, g.Ls, ct, sn, pos0, a);
+      la::state_f32<true><<<grid, block, 0, st>>>(K, V, ct, sn, pos0, a);
     else
-      la::state_f32<false><<<grid, block, 0, st>>>(K, V, g.N, g.Ls, ct, sn, pos0, a);
+      la::state_f32<false><<<grid, block, 0, st>>>(K, V, ct, sn, pos0, a);
   }
-  if (g.P > 1) {
+  if (g.C * g.Pc > 1) {
     const int64_t n_elems = g.BH * la::kStateElems;
     la::state_finalize<<<dim3((unsigned)ceil_div(n_elems, la::kThreads)), dim3(la::kThreads), 0, st>>>(a, n_elems);
   }
 }
 
 void launch_apply(const void* q, void* o, int dtype, float eps, const Geometry& g, const sana_rope* rope,
-                  const float* kv, const float* ksum, hipStream_t st) {
+                  const la::StateView& sv, hipStream_t st) {
   const float* ct = rope ? rope->cos : nullptr;
   const float* sn = rope ? rope->sin : nullptr;
   const int64_t pos0 = rope ? rope->pos_offset : 0;
@@ -180,53 +227,92 @@ void launch_apply(const void* q, void* o, int dtype, float eps, const Geometry& 
     const la::u32x4_t* Q = static_cast<const la::u32x4_t*>(q);
     la::u32x4_t* O = static_cast<la::u32x4_t*>(o);
     if (rope)
-      la::apply_bf16<true><<<grid, block, 0, st>>>(Q, O, kv, ksum, g.N, g.BH * g.N, g.La, eps, ct, sn, pos0);
+      la::apply_bf16<true><<<grid, block, 0, st>>>(Q, O, sv, g.N, g.L, (int)g.C, g.BH * g.N, g.La, eps, ct, sn, pos0);
     else
-      la::apply_bf16<false><<<grid, block, 0, st>>>(Q, O, kv, ksum, g.N, g.BH * g.N, g.La, eps, ct, sn, pos0);
+      la::apply_bf16<false><<<grid, block, 0, st>>>(Q, O, sv, g.N, g.L, (int)g.C, g.BH * g.N, g.La, eps, ct, sn, pos0);
   } else {
-    const dim3 grid((unsigned)(g.BH * g.T)), block(la::kThreads);
+    const dim3 grid((unsigned)(g.BH * g.C * g.T)), block(la::kThreads);
     const float* Q = static_cast<const float*>(q);
     float* O = static_cast<float*>(o);
     if (rope)
-      la::apply_f32<true><<<grid, block, 0, st>>>(Q, O, kv, ksum, g.N, (int)g.T, g.Lt, eps, ct, sn, pos0);
+      la::apply_f32<true><<<grid, block, 0, st>>>(Q, O, sv, g.N, g.L, (int)g.C, (int)g.T, g.Lt, eps, ct, sn, pos0);
     else
-      la::apply_f32<false><<<grid, block, 0, st>>>(Q, O, kv, ksum, g.N, (int)g.T, g.Lt, eps, ct, sn, pos0);
+      la::apply_f32<false><<<grid, block, 0, st>>>(Q, O, sv, g.N, g.L, (int)g.C, (int)g.T, g.Lt, eps, ct, sn, pos0);
   }
 }
 
 int launch_status() { return hipGetLastError() == hipSuccess ? SANA_OK : SANA_ERR_HIP; }
+
+// Shared body of forward, block_forward and block_causal: chunks of L tokens
+// (L >= N for one chunk), carried state in, optional commit out.
+int attend(const void* q, const void* k, const void* v, void* o, const float* kv_in, const float* ksum_in,
+           float* kv_out, float* ksum_out, int B, int H, int64_t N, int64_t L, int D, int dtype, float eps,
+           const sana_rope* rope, void* ws, size_t ws_bytes, void* hip_stream) {
+  int64_t bh = 0, elems = 0;
+  int rc = check_sizes(B, H, N, D, dtype, &bh, &elems);
+  if (rc != SANA_OK) return rc;
+  if (!std::isfinite(eps) || eps < 0.f) return SANA_ERR_INVALID;
+  if (L <= 0) return SANA_ERR_INVALID;
+  if (elems == 0) return SANA_OK;
+  if (check_tensor(q) || check_tensor(k) || check_tensor(v) || check_tensor(o)) return SANA_ERR_INVALID;
+  if ((kv_in == nullptr) != (ksum_in == nullptr)) return SANA_ERR_INVALID;
+  if ((kv_out == nullptr) != (ksum_out == nullptr)) return SANA_ERR_INVALID;
+  if ((kv_in && (!aligned(kv_in, 4) || !aligned(ksum_in, 4))) ||
+      (kv_out && (!aligned(kv_out, 4) || !aligned(ksum_out, 4))))
+    return SANA_ERR_INVALID;
+  const size_t bytes = (size_t)elems * elem_size(dtype);
+  if ((rc = check_overlaps(q, k, v, o, bytes, kv_in, ksum_in, kv_out, ksum_out, bh)) != SANA_OK) return rc;
+  if ((rc = check_rope(rope, N)) != SANA_OK) return rc;
+  const Geometry g = make_geometry(bh, N, L, rope != nullptr);
+  if ((rc = check_workspace(g, ws, ws_bytes)) != SANA_OK) return rc;
+
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  const la::StateArgs a = state_args(ws, g, kv_in, ksum_in, kv_out, ksum_out);
+  launch_state(k, v, dtype, g, rope, a, st);
+  launch_apply(q, o, dtype, eps, g, rope, ws_view(a), st);
+  return launch_status();
+}
+
+size_t workspace(int B, int H, int64_t N, int64_t L, int D, int dtype, int has_rope) {
+  int64_t bh = 0, elems = 0;
+  if (L <= 0 || check_sizes(B, H, N, D, dtype, &bh, &elems) != SANA_OK) return 0;
+  return make_geometry(bh, N, L, has_rope != 0).total_bytes;
+}
 
 }  // namespace
 
 extern "C" {
 
 size_t sana_linattn_workspace_bytes(int B, int H, int64_t N, int D, int dtype, int has_rope) {
-  int64_t bh = 0, elems = 0;
-  if (check_sizes(B, H, N, D, dtype, &bh, &elems) != SANA_OK) return 0;
-  return make_geometry(bh, N, has_rope != 0).total_bytes;
+  return workspace(B, H, N, N > 0 ? N : 1, D, dtype, has_rope);
+}
+
+size_t sana_linattn_block_causal_workspace_bytes(int B, int H, int64_t N, int64_t chunk, int D, int dtype,
+                                                 int has_rope) {
+  return workspace(B, H, N, chunk, D, dtype, has_rope);
 }
 
 int sana_linattn_forward(const void* q, const void* k, const void* v, void* o, int B, int H, int64_t N, int D,
                          int dtype, float eps, const sana_rope* rope, void* ws, size_t ws_bytes,
                          void* hip_stream) {
-  int64_t bh = 0, elems = 0;
-  int rc = check_sizes(B, H, N, D, dtype, &bh, &elems);
-  if (rc != SANA_OK) return rc;
-  if (!std::isfinite(eps) || eps < 0.f) return SANA_ERR_INVALID;
-  if (elems == 0) return SANA_OK;
-  if (check_tensor(q) || check_tensor(k) || check_tensor(v) || check_tensor(o)) return SANA_ERR_INVALID;
-  const size_t bytes = (size_t)elems * elem_size(dtype);
-  if (overlaps(o, bytes, q, bytes) || overlaps(o, bytes, k, bytes) || overlaps(o, bytes, v, bytes))
-    return SANA_ERR_INVALID;
-  if ((rc = check_rope(rope, N)) != SANA_OK) return rc;
-  const Geometry g = make_geometry(bh, N, rope != nullptr);
-  if ((rc = check_workspace(g, ws, ws_bytes)) != SANA_OK) return rc;
+  return attend(q, k, v, o, nullptr, nullptr, nullptr, nullptr, B, H, N, N > 0 ? N : 1, D, dtype, eps, rope, ws,
+                ws_bytes, hip_stream);
+}
 
-  hipStream_t st = static_cast<hipStream_t>(hip_stream);
-  float* state = ws_at(ws, g.state_off);
-  launch_state(k, v, dtype, g, rope, state_args(ws, g, nullptr, nullptr, state, state + bh * 1024), st);
-  launch_apply(q, o, dtype, eps, g, rope, state, state + bh * 1024, st);
-  return launch_status();
+int sana_linattn_block_forward(const void* q, const void* k, const void* v, void* o, const float* kv_in,
+                               const float* ksum_in, float* kv_out, float* ksum_out, int B, int H, int64_t N,
+                               int D, int dtype, float eps, const sana_rope* rope, void* ws, size_t ws_bytes,
+                               void* hip_stream) {
+  return attend(q, k, v, o, kv_in, ksum_in, kv_out, ksum_out, B, H, N, N > 0 ? N : 1, D, dtype, eps, rope, ws,
+                ws_bytes, hip_stream);
+}
+
+int sana_linattn_block_causal(const void* q, const void* k, const void* v, void* o, const float* kv_in,
+                              const float* ksum_in, float* kv_out, float* ksum_out, int B, int H, int64_t N,
+                              int64_t chunk, int D, int dtype, float eps, const sana_rope* rope, void* ws,
+                              size_t ws_bytes, void* hip_stream) {
+  return attend(q, k, v, o, kv_in, ksum_in, kv_out, ksum_out, B, H, N, chunk, D, dtype, eps, rope, ws, ws_bytes,
+                hip_stream);
 }
 
 int sana_linattn_state_update(const void* k, const void* v, float* kv_state, float* ksum_state, int B, int H,
@@ -245,54 +331,11 @@ int sana_linattn_state_update(const void* k, const void* v, float* kv_state, flo
       overlaps(ksum_state, ks_bytes, v, bytes))
     return SANA_ERR_INVALID;
   if ((rc = check_rope(rope, N)) != SANA_OK) return rc;
-  const Geometry g = make_geometry(bh, N, rope != nullptr);
+  const Geometry g = make_geometry(bh, N, N, rope != nullptr);
   if ((rc = check_workspace(g, ws, ws_bytes)) != SANA_OK) return rc;
 
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   launch_state(k, v, dtype, g, rope, state_args(ws, g, kv_state, ksum_state, kv_state, ksum_state), st);
-  return launch_status();
-}
-
-int sana_linattn_block_forward(const void* q, const void* k, const void* v, void* o, const float* kv_in,
-                               const float* ksum_in, float* kv_out, float* ksum_out, int B, int H, int64_t N,
-                               int D, int dtype, float eps, const sana_rope* rope, void* ws, size_t ws_bytes,
-                               void* hip_stream) {
-  int64_t bh = 0, elems = 0;
-  int rc = check_sizes(B, H, N, D, dtype, &bh, &elems);
-  if (rc != SANA_OK) return rc;
-  if (!std::isfinite(eps) || eps < 0.f) return SANA_ERR_INVALID;
-  if (elems == 0) return SANA_OK;
-  if (check_tensor(q) || check_tensor(k) || check_tensor(v) || check_tensor(o)) return SANA_ERR_INVALID;
-  if ((kv_in == nullptr) != (ksum_in == nullptr)) return SANA_ERR_INVALID;
-  if ((kv_out == nullptr) != (ksum_out == nullptr)) return SANA_ERR_INVALID;
-  if ((kv_in && (!aligned(kv_in, 4) || !aligned(ksum_in, 4))) ||
-      (kv_out && (!aligned(kv_out, 4) || !aligned(ksum_out, 4))))
-    return SANA_ERR_INVALID;
-  const size_t bytes = (size_t)elems * elem_size(dtype);
-  if (overlaps(o, bytes, q, bytes) || overlaps(o, bytes, k, bytes) || overlaps(o, bytes, v, bytes))
-    return SANA_ERR_INVALID;
-  const size_t kv_bytes = (size_t)bh * 1024 * sizeof(float), ks_bytes = (size_t)bh * 32 * sizeof(float);
-  const void* tensors[4] = {q, k, v, o};
-  const void* states[4] = {kv_in, ksum_in, kv_out, ksum_out};
-  const size_t state_sizes[4] = {kv_bytes, ks_bytes, kv_bytes, ks_bytes};
-  for (int i = 0; i < 4; ++i)
-    for (int j = 0; j < 4; ++j)
-      if (overlaps(states[i], state_sizes[i], tensors[j], bytes)) return SANA_ERR_INVALID;
-  // among the states only exact in-place aliasing (kv_out == kv_in, ksum_out == ksum_in) is allowed
-  if (overlaps(kv_in, kv_bytes, ksum_in, ks_bytes) || overlaps(kv_out, kv_bytes, ksum_out, ks_bytes) ||
-      overlaps(kv_in, kv_bytes, ksum_out, ks_bytes) || overlaps(ksum_in, ks_bytes, kv_out, kv_bytes))
-    return SANA_ERR_INVALID;
-  if (kv_out && overlaps(kv_in, kv_bytes, kv_out, kv_bytes) && kv_in != kv_out) return SANA_ERR_INVALID;
-  if (ksum_out && overlaps(ksum_in, ks_bytes, ksum_out, ks_bytes) && ksum_in != ksum_out) return SANA_ERR_INVALID;
-  if ((rc = check_rope(rope, N)) != SANA_OK) return rc;
-  const Geometry g = make_geometry(bh, N, rope != nullptr);
-  if ((rc = check_workspace(g, ws, ws_bytes)) != SANA_OK) return rc;
-
-  hipStream_t st = static_cast<hipStream_t>(hip_stream);
-  float* kv_new = kv_out ? kv_out : ws_at(ws, g.state_off);
-  float* ksum_new = kv_out ? ksum_out : ws_at(ws, g.state_off) + bh * 1024;
-  launch_state(k, v, dtype, g, rope, state_args(ws, g, kv_in, ksum_in, kv_new, ksum_new), st);
-  launch_apply(q, o, dtype, eps, g, rope, kv_new, ksum_new, st);
   return launch_status();
 }
 
@@ -310,8 +353,10 @@ int sana_linattn_apply(const void* q, void* o, const float* kv_state, const floa
   if (overlaps(o, bytes, q, bytes) || overlaps(o, bytes, kv_state, kv_bytes) || overlaps(o, bytes, ksum_state, ks_bytes))
     return SANA_ERR_INVALID;
   if ((rc = check_rope(rope, N)) != SANA_OK) return rc;
-  const Geometry g = make_geometry(bh, N, rope != nullptr);
-  launch_apply(q, o, dtype, eps, g, rope, kv_state, ksum_state, static_cast<hipStream_t>(hip_stream));
+  const Geometry g = make_geometry(bh, N, N, rope != nullptr);
+  if (!grids_fit(g)) return SANA_ERR_INVALID;
+  launch_apply(q, o, dtype, eps, g, rope, la::StateView{kv_state, ksum_state, 1024, 32},
+               static_cast<hipStream_t>(hip_stream));
   return launch_status();
 }
 

@@ -192,3 +192,22 @@ def test_apply_argument_errors():
     assert ap(eps=-1.0) == la.SANA_ERR_INVALID
     assert ap(D=64) == la.SANA_ERR_UNSUPPORTED
     assert ap(q=None, o=None, kv=None, ks=None, N=0) == la.SANA_OK
+
+
+def test_block_causal_argument_errors_and_workspace():
+    L = la.lib()
+    n = la.block_causal_workspace_bytes(1, 2, 640, 64)
+    assert n >= la.workspace_bytes(1, 2, 640)          # per-chunk states on top of one state
+    assert la.block_causal_workspace_bytes(1, 2, 640, 640) == la.workspace_bytes(1, 2, 640)
+    assert la.block_causal_workspace_bytes(1, 2, 640, 0) == 0
+    assert la.block_causal_workspace_bytes(1, 2, 640, 7) > la.block_causal_workspace_bytes(1, 2, 640, 70)
+
+    def bc(chunk=64, ws=WS, nbytes=n, q=A):
+        return L.sana_linattn_block_causal(q, Bp, C, Dp, None, None, None, None, 1, 2, 640, chunk, 32,
+                                           la.SANA_DT_BF16, 1e-6, None, ws, nbytes, None)
+
+    assert bc(chunk=0) == la.SANA_ERR_INVALID
+    assert bc(chunk=-4) == la.SANA_ERR_INVALID
+    assert bc(ws=None) == la.SANA_ERR_WORKSPACE
+    assert bc(nbytes=la.workspace_bytes(1, 2, 640)) == la.SANA_ERR_WORKSPACE   # too small for 10 chunks
+    assert bc(q=None) == la.SANA_ERR_INVALID

@@ -289,3 +289,66 @@ def test_apply_matches_forward_and_oracle():
         angles = None if rope_grid is None else oracle.rope3d_angles(*rope_grid)
         ref = oracle.apply_state(x.f64["q"], to_np(kv), to_np(z), w.eps, angles=angles)
         check(to_np(o_apply), ref, "bf16", f"apply on a given state (rope={rope_grid})")
+
+
+# --------------------------------------------------------------------------
+# whole-sequence block-causal call
+# --------------------------------------------------------------------------
+
+def _run_sequence(x, chunk, rope=None, with_state=False, S0=None, z0=None):
+    torch = torch_mod()
+    w = x.workload
+    q, k, v = inputs_on_device(x)
+    kv = z = None
+    if with_state:
+        kv = torch.from_numpy(S0.astype(np.float32)).to(device())
+        z = torch.from_numpy(z0.astype(np.float32)).to(device())
+    o = la.sana_linattn_block_causal(q, k, v, chunk, kv_in=kv, ksum_in=z, kv_out=kv, ksum_out=z, eps=w.eps,
+                                     rope=rope)
+    return to_np(o), (None if kv is None else to_np(kv)), (None if z is None else to_np(z))
+
+
+def test_block_causal_sequence_full_size():
+    w = WORKLOADS["video480p_blockcausal"]
+    x = generate(w)
+    o, _, _ = _run_sequence(x, w.chunk)
+    ref, _, _ = oracle.block_causal(x.f64["q"], x.f64["k"], x.f64["v"], w.chunk, w.eps)
+    check(o, ref, "bf16", "block-causal sequence call, 10 x 4680")
+
+
+@pytest.mark.parametrize("N,chunk,dtype", [(100, 40, "bf16"), (997, 128, "bf16"), (5000, 4680, "bf16"),
+                                           (4680, 4680, "bf16"), (64, 1, "bf16"), (2000, 333, "f32"),
+                                           (20000, 1500, "bf16")])
+def test_block_causal_sequence_cases(N, chunk, dtype):
+    base = WORKLOADS["noncausal_f32_b1h1n256"] if dtype == "f32" else WORKLOADS["video480p_blockcausal"]
+    w = reduced(base, B=2, H=3, N=N, mode="block", chunk=chunk, seed=N + chunk)
+    x = generate(w)
+    rng = np.random.default_rng(5)
+    S0 = rng.standard_normal((2, 3, 32, 32))
+    z0 = np.abs(rng.standard_normal((2, 3, 32))) * 50
+    o, S, z = _run_sequence(x, chunk, with_state=True, S0=S0, z0=z0)
+    # the oracle from the same carried state
+    Sr, zr = S0.astype(np.float32).astype(np.float64), z0.astype(np.float32).astype(np.float64)
+    ref = np.empty(x.f64["q"].shape)
+    for s0 in range(0, N, chunk):
+        sl = slice(s0, min(N, s0 + chunk))
+        ref[:, :, sl], Sr, zr = oracle.block_forward(x.f64["q"][:, :, sl], x.f64["k"][:, :, sl],
+                                                     x.f64["v"][:, :, sl], Sr, zr, w.eps)
+    check(o, ref, dtype, f"block-causal sequence N={N} chunk={chunk} with carried state")
+    assert rel_l2(S, Sr) <= 1e-5 and rel_l2(z, zr) <= 1e-6
+
+
+def test_block_causal_sequence_rope_and_chunk_loop_agree():
+    grid = (6, 10, 12)
+    w = reduced(WORKLOADS["video480p_blockcausal"], H=3, N=6 * 10 * 12, chunk=2 * 10 * 12, grid=grid)
+    x = generate(w)
+    rope = rope_for(w)
+    o_seq, _, _ = _run_sequence(x, w.chunk, rope=rope)
+    o_loop, _, _ = run_block_chunks(x, w.chunk, rope=rope)
+    ref, _, _ = oracle.block_causal(x.f64["q"], x.f64["k"], x.f64["v"], w.chunk, w.eps,
+                                    angles=oracle.rope3d_angles(*grid))
+    check(o_seq, ref, "bf16", "block-causal sequence with RoPE")
+    assert rel_l2(o_seq, o_loop) <= 4e-3
+    # one chunk covering everything is the plain forward
+    o_one, _, _ = _run_sequence(x, 10 ** 6)
+    assert np.array_equal(o_one, run_forward(x))
