@@ -22,7 +22,7 @@ from .binding import (  # noqa: F401
     rope3d_device,
     rope3d_table,
     block_causal_workspace_bytes,
-    sana_linattn_block_causal, sana_linattn_apply,
+    sana_linattn_apply,
     sana_linattn_block_causal,
     sana_linattn_block_forward,
     sana_linattn_forward,

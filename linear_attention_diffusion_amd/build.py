@@ -21,9 +21,13 @@ ARCH = "gfx950"
 
 # -packed-fp32-ops keeps the compiler from forming packed fp32 VALU ops; the
 # host pass warns that it does not know the feature, which is harmless.
+# -amdgpu-mfma-vgpr-form has MFMA write its results to ordinary VGPRs: the
+# kernels convert most MFMA results with VALU right away, and results left in
+# AGPRs would each cost a v_accvgpr_read first.
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wall", "-Wno-unused-command-line-argument",
 ]
 
