@@ -103,8 +103,9 @@ __device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
 }
 
 // x = hi + mid + lo with hi = bf16(x), mid = bf16(x - hi), lo = bf16(x - hi - mid);
-// each residual is exact in fp32.  Called for a pair (a, b), each part comes
-// back as one dword of two packed bf16.
+// each residual is exact in fp32 (x - bf16(x) has at most 16 significant
+// bits).  Called for a pair (a, b), each part comes back as one dword of two
+// packed bf16.
 __device__ __forceinline__ void split3_bf16x2(float a, float b, unsigned& hi, unsigned& mid, unsigned& lo) {
   hi = pack_bf16x2(a, b);
   const float ra = a - bf16lo_to_f32(hi), rb = b - bf16hi_to_f32(hi);
@@ -130,6 +131,45 @@ __device__ __forceinline__ bf16x8_t odd8(const unsigned (&x)[8]) {
 
 __device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Buffer access
+// ---------------------------------------------------------------------------
+//
+// The bf16 kernels address memory through buffer resources built in SGPRs, one
+// per 64-token chunk, whose size is the number of bytes left before the end of
+// the token range: the hardware range check then reads rows past the end as 0
+// and drops stores past it, so the loops need no per-lane predicates and no
+// 64-bit address arithmetic (lane offsets are 32-bit, tile offsets immediate).
+// The range check covers the per-lane offset plus the immediate, which is all
+// the kernels use.
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) buffer
+constexpr int kNonTemporal = 2;         // cache policy of data streamed once
+
+// `bytes` from `base` are in range.  The callers touch at most a few KB past
+// `base`, so clamping a larger size to what the descriptor holds cuts nothing.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int64_t nr = bytes < 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nr, kRsrcWord3);
+}
+
+__device__ __forceinline__ u32x4_t load16_nt(rsrc_t r, int off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNonTemporal));
+}
+
+__device__ __forceinline__ f32x4_t load16(rsrc_t r, int off) {
+  return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+__device__ __forceinline__ float load4(rsrc_t r, int off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
+__device__ __forceinline__ void store16_nt(rsrc_t r, int off, u32x4_t x) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, x), r, off, 0, kNonTemporal);
 }
 
 // ---------------------------------------------------------------------------
@@ -232,11 +272,13 @@ __device__ __forceinline__ void state_item(const StateArgs& a, int64_t& bh, int&
 // and S[16fh + 4g + i][16fh' + n] accumulates in MFMA (fh, fh').  Two more
 // MFMAs against a B of ones give z.
 //
-// Under RoPE the rotation acts on pairs (2p, 2p+1) of a token, which a lane
-// holds together before the turn-around: the lane rotates its 4 pairs in fp32
-// with 16-byte cos/sin loads, splits the result into three bf16 parts, and
-// each part is turned around and contracted separately.  z always comes from
-// the un-rotated phi(K).
+// Under RoPE the rotation acts on pairs (2p, 2p+1) of a token.  It is applied
+// after the turn-around, where lane (n, g) holds feature f = 16fh + n of
+// tokens t0 + 16tb + 4g + i: a second selection MFMA hands the lane the pair
+// partner f ^ 1 with the rotation's sign, cos/sin of pair f / 2 are gathered
+// per token, and the rotated fp32 values are split into three bf16 parts that
+// are contracted against V one by one.  z always comes from the un-rotated
+// phi(K).
 
 // E_fh as the B operand of lane (n, g): slot s is 1.0 where 8g + s == 16fh + n
 __device__ __forceinline__ bf16x8_t select_operand(int g, int n, int fh) {
@@ -249,11 +291,30 @@ __device__ __forceinline__ bf16x8_t select_operand(int g, int n, int fh) {
   return as_bf16x8(d[0], d[1], d[2], d[3]);
 }
 
-// Turned-around tile halves (tb = 0, 1) of feature half fh -> bf16 operand
-__device__ __forceinline__ bf16x8_t turned_operand(bf16x8_t x0, bf16x8_t x1, bf16x8_t sel) {
+// The pair partner's selection: slot s is where 8g + s == (16fh + n) ^ 1, with
+// value -1.0 for even n and +1.0 for odd n, so the turn-around returns
+// -x[f + 1] (f even) or +x[f - 1] (f odd) and the rotated value is
+// x[f] cos + partner sin (pair p: (x0 c - x1 s, x0 s + x1 c)).
+__device__ __forceinline__ bf16x8_t partner_operand(int g, int n, int fh) {
+  const int f = (16 * fh + n) ^ 1;
+  const unsigned one = (n & 1) ? 0x3f80u : 0xbf80u;
+  unsigned d[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int k = 8 * g + 2 * p;
+    d[p] = (k == f ? one : 0u) | (k + 1 == f ? one << 16 : 0u);
+  }
+  return as_bf16x8(d[0], d[1], d[2], d[3]);
+}
+
+// Turn-around of one 16-token half (exact: bf16 values times 1.0)
+__device__ __forceinline__ f32x4_t turn(bf16x8_t x, bf16x8_t sel) {
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
-  const f32x4_t t0 = mfma16(x0, sel, zero4);
-  const f32x4_t t1 = mfma16(x1, sel, zero4);
+  return mfma16(x, sel, zero4);
+}
+
+// Turned-around halves tb = 0, 1 of one feature half -> bf16 operand
+__device__ __forceinline__ bf16x8_t pack_turned(f32x4_t t0, f32x4_t t1) {
   return as_bf16x8(pack_bf16x2(t0[0], t0[1]), pack_bf16x2(t0[2], t0[3]), pack_bf16x2(t1[0], t1[1]),
                    pack_bf16x2(t1[2], t1[3]));
 }
@@ -266,25 +327,53 @@ __device__ __forceinline__ u32x4_t relu_bf16x8(u32x4_t x) {
   return x;
 }
 
+// cos and sin that lane (n, g) needs for a 32-token tile at t0: element
+// [fh][tb][i] belongs to pair 8fh + n / 2 of token t0 + 16tb + 4g + i.  Rows at
+// or past n_end read 0 (their phi(K) is 0 as well).
+struct TileAngles {
+  f32x4_t c[2][2], s[2][2];
+};
+
+__device__ __forceinline__ void gather_angles(const float* cos_t, const float* sin_t, int64_t pos0, int64_t t0,
+                                              int64_t n_end, int g, int n, TileAngles& ang) {
+  const rsrc_t rc = make_rsrc(cos_t + (pos0 + t0) * 16, (n_end - t0) * 64);
+  const rsrc_t rs = make_rsrc(sin_t + (pos0 + t0) * 16, (n_end - t0) * 64);
+  const int lane = 4 * g * 64 + (n >> 1) * 4;
+#pragma unroll
+  for (int fh = 0; fh < 2; ++fh)
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ang.c[fh][tb][i] = load4(rc, lane + (16 * tb + i) * 64 + 32 * fh);
+        ang.s[fh][tb][i] = load4(rs, lane + (16 * tb + i) * 64 + 32 * fh);
+      }
+}
+
 // acc[fh][fh']: S blocks (key half fh, value half fh'); accz[fh]: z of key half fh
 template <bool ROPE>
 __device__ __forceinline__ void state_tile(const u32x4_t (&kx)[2], const u32x4_t (&vx)[2], int64_t t0,
                                            int64_t n_end, int g, int n, const float* cos_t, const float* sin_t,
-                                           int64_t pos0, const bf16x8_t (&sel)[2], f32x4_t (&acc)[2][2],
-                                           f32x4_t (&accz)[2]) {
+                                           int64_t pos0, const bf16x8_t (&sel)[2], const bf16x8_t (&selp)[2],
+                                           f32x4_t (&acc)[2][2], f32x4_t (&accz)[2]) {
   const unsigned one2 = 0x3f803f80u;  // two bf16 1.0
   const bf16x8_t ones = as_bf16x8(one2, one2, one2, one2);
+  TileAngles ang;
+  if constexpr (ROPE) gather_angles(cos_t, sin_t, pos0, t0, n_end, g, n, ang);
   bf16x8_t k_nat[2], v_nat[2];
 #pragma unroll
   for (int tb = 0; tb < 2; ++tb) {
     k_nat[tb] = __builtin_bit_cast(bf16x8_t, relu_bf16x8(kx[tb]));
     v_nat[tb] = __builtin_bit_cast(bf16x8_t, vx[tb]);
   }
+  f32x4_t kt[2][2];  // [fh][tb]: phi(K) turned around, exact fp32
   bf16x8_t a[2], b[2];
 #pragma unroll
   for (int fh = 0; fh < 2; ++fh) {
-    a[fh] = turned_operand(k_nat[0], k_nat[1], sel[fh]);
-    b[fh] = turned_operand(v_nat[0], v_nat[1], sel[fh]);
+    kt[fh][0] = turn(k_nat[0], sel[fh]);
+    kt[fh][1] = turn(k_nat[1], sel[fh]);
+    a[fh] = pack_turned(kt[fh][0], kt[fh][1]);
+    b[fh] = pack_turned(turn(v_nat[0], sel[fh]), turn(v_nat[1], sel[fh]));
   }
 #pragma unroll
   for (int fh = 0; fh < 2; ++fh) accz[fh] = mfma16(a[fh], ones, accz[fh]);
@@ -295,47 +384,28 @@ __device__ __forceinline__ void state_tile(const u32x4_t (&kx)[2], const u32x4_t
       acc[fh][1] = mfma16(a[fh], b[1], acc[fh][1]);
     }
   } else {
-    // rotate the lane's pairs 4g .. 4g+3 of token t0 + 16tb + n, split in three parts
-    unsigned part[3][2][4];
+    unsigned part[3][2][4];  // [bf16 part][fh][dword]: the slot order of a[fh]
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
-      const int64_t tok = t0 + 16 * tb + n;
-      f32x4_t c = {1.f, 1.f, 1.f, 1.f}, sn = {0.f, 0.f, 0.f, 0.f};
-      if (tok < n_end) {
-        c = *reinterpret_cast<const f32x4_t*>(cos_t + (pos0 + tok) * 16 + 4 * g);
-        sn = *reinterpret_cast<const f32x4_t*>(sin_t + (pos0 + tok) * 16 + 4 * g);
-      }
-      const u32x4_t kr = relu_bf16x8(kx[tb]);
+    for (int fh = 0; fh < 2; ++fh) {
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const float x0 = bf16lo_to_f32(kr[p]);
-        const float x1 = bf16hi_to_f32(kr[p]);
-        split3_bf16x2(x0 * c[p] - x1 * sn[p], x0 * sn[p] + x1 * c[p], part[0][tb][p], part[1][tb][p],
-                      part[2][tb][p]);
+      for (int tb = 0; tb < 2; ++tb) {
+        const f32x4_t xp = turn(k_nat[tb], selp[fh]);
+        f32x4_t y;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) y[i] = kt[fh][tb][i] * ang.c[fh][tb][i] + xp[i] * ang.s[fh][tb][i];
+        split3_bf16x2(y[0], y[1], part[0][fh][2 * tb], part[1][fh][2 * tb], part[2][fh][2 * tb]);
+        split3_bf16x2(y[2], y[3], part[0][fh][2 * tb + 1], part[1][fh][2 * tb + 1], part[2][fh][2 * tb + 1]);
       }
     }
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
 #pragma unroll
       for (int fh = 0; fh < 2; ++fh) {
-        const unsigned(&p0)[4] = part[k][0];
-        const unsigned(&p1)[4] = part[k][1];
-        const bf16x8_t ar = turned_operand(as_bf16x8(p0[0], p0[1], p0[2], p0[3]),
-                                           as_bf16x8(p1[0], p1[1], p1[2], p1[3]), sel[fh]);
+        const bf16x8_t ar = as_bf16x8(part[k][fh][0], part[k][fh][1], part[k][fh][2], part[k][fh][3]);
         acc[fh][0] = mfma16(ar, b[0], acc[fh][0]);
         acc[fh][1] = mfma16(ar, b[1], acc[fh][1]);
       }
     }
-  }
-}
-
-__device__ __forceinline__ void load_rows(const u32x4_t* X, int64_t t0, int64_t n_end, u32x4_t (&x)[2]) {
-#pragma unroll
-  for (int tb = 0; tb < 2; ++tb) {
-    const int64_t tok = t0 + 16 * tb;
-    x[tb] = u32x4_t{0u, 0u, 0u, 0u};
-    // streamed once: non-temporal
-    if (tok < n_end) x[tb] = __builtin_nontemporal_load(&X[tok * 4]);
   }
 }
 
@@ -351,17 +421,17 @@ __global__ __launch_bounds__(kThreads) void state_bf16(const u32x4_t* __restrict
   state_item(a, bh, c, s, n_begin, n_end);
   const int64_t N = a.N;
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;
   const int g = lane >> 4;
 
-  // lane's 16-byte piece of row (token): features 8g .. 8g+7, i.e. X[tok * 4]
-  // below is relative to token n of the tile
-  const u32x4_t* Kh = K + (bh * N + n) * 4 + g;
-  const u32x4_t* Vh = V + (bh * N + n) * 4 + g;
-  const int64_t n_end_lane = n_end - n;  // token t0 + n is live iff t0 < n_end_lane
+  // lane's 16-byte piece of a row: features 8g .. 8g+7 of token (tile row) n
+  const char* Kh = reinterpret_cast<const char*>(K + bh * N * 4);
+  const char* Vh = reinterpret_cast<const char*>(V + bh * N * 4);
+  const int lane_off = n * 64 + g * 16;
 
   const bf16x8_t sel[2] = {select_operand(g, n, 0), select_operand(g, n, 1)};
+  const bf16x8_t selp[2] = {partner_operand(g, n, 0), partner_operand(g, n, 1)};
   f32x4_t acc[2][2], accz[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -370,32 +440,26 @@ __global__ __launch_bounds__(kThreads) void state_bf16(const u32x4_t* __restrict
     acc[i][1] = accz[i];
   }
 
-  // each wave takes 64-token chunks (two 32-token tiles); the next chunk's
-  // loads are issued before the current chunk is computed
+  // each wave takes 64-token chunks (two 32-token tiles of two 16-row halves);
+  // the next chunk's loads are issued before the current chunk is computed
   int64_t t0 = n_begin + 64 * w;
   u32x4_t nk[4], nv[4];
   auto load_chunk = [&](int64_t c0) {
-    u32x4_t x[2];
-    load_rows(Kh, c0, n_end_lane, x);
-    nk[0] = x[0];
-    nk[1] = x[1];
-    load_rows(Vh, c0, n_end_lane, x);
-    nv[0] = x[0];
-    nv[1] = x[1];
-    load_rows(Kh, c0 + 32, n_end_lane, x);
-    nk[2] = x[0];
-    nk[3] = x[1];
-    load_rows(Vh, c0 + 32, n_end_lane, x);
-    nv[2] = x[0];
-    nv[3] = x[1];
+    const rsrc_t rk = make_rsrc(Kh + c0 * 64, (n_end - c0) * 64);
+    const rsrc_t rv = make_rsrc(Vh + c0 * 64, (n_end - c0) * 64);
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      nk[h] = load16_nt(rk, lane_off + h * 1024);
+      nv[h] = load16_nt(rv, lane_off + h * 1024);
+    }
   };
   if (t0 < n_end) load_chunk(t0);
   for (; t0 < n_end; t0 += 256) {
     const u32x4_t ka[2] = {nk[0], nk[1]}, va[2] = {nv[0], nv[1]};
     const u32x4_t kb[2] = {nk[2], nk[3]}, vb[2] = {nv[2], nv[3]};
     if (t0 + 256 < n_end) load_chunk(t0 + 256);
-    state_tile<ROPE>(ka, va, t0, n_end, g, n, cos_t, sin_t, pos0, sel, acc, accz);
-    if (t0 + 32 < n_end) state_tile<ROPE>(kb, vb, t0 + 32, n_end, g, n, cos_t, sin_t, pos0, sel, acc, accz);
+    state_tile<ROPE>(ka, va, t0, n_end, g, n, cos_t, sin_t, pos0, sel, selp, acc, accz);
+    if (t0 + 32 < n_end) state_tile<ROPE>(kb, vb, t0 + 32, n_end, g, n, cos_t, sin_t, pos0, sel, selp, acc, accz);
   }
 
   // D lane (n, g): rows 4g + i -> key feature 16fh + 4g + i, column n -> value feature 16fh' + n
@@ -596,24 +660,23 @@ struct ApplyChunk {
   f32x4_t c[4], sn[4];
 };
 
+// Rows at or past n_end read 0; their outputs are not stored.
 template <bool ROPE>
-__device__ __forceinline__ void load_apply_chunk(const u32x4_t* Qh, int64_t t0, int64_t n_end, int m, int g,
+__device__ __forceinline__ void load_apply_chunk(const char* Qh, int64_t t0, int64_t n_end, int lane_off,
                                                  const float* cos_t, const float* sin_t, int64_t pos0,
                                                  ApplyChunk<ROPE>& ch) {
+  const rsrc_t rq = make_rsrc(Qh + t0 * 64, (n_end - t0) * 64);
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int64_t tok = t0 + 16 * u + m;
-    ch.q[u] = u32x4_t{0u, 0u, 0u, 0u};
-    ch.c[u] = f32x4_t{1.f, 1.f, 1.f, 1.f};
-    ch.sn[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    if (tok < n_end) {
-      // streamed once: non-temporal, so it does not displace reused lines
-      ch.q[u] = __builtin_nontemporal_load(&Qh[tok * 4]);
-      if constexpr (ROPE) {
-        // pairs 4g .. 4g+3 of the token at position pos0 + tok
-        ch.c[u] = *reinterpret_cast<const f32x4_t*>(cos_t + (pos0 + tok) * 16 + 4 * g);
-        ch.sn[u] = *reinterpret_cast<const f32x4_t*>(sin_t + (pos0 + tok) * 16 + 4 * g);
-      }
+  for (int u = 0; u < 4; ++u) ch.q[u] = load16_nt(rq, lane_off + u * 1024);
+  if constexpr (ROPE) {
+    // pairs 4g .. 4g+3 of the token at position pos0 + t0 + 16u + m: the same
+    // lane offset in a 64-byte table row
+    const rsrc_t rc = make_rsrc(cos_t + (pos0 + t0) * 16, (n_end - t0) * 64);
+    const rsrc_t rs = make_rsrc(sin_t + (pos0 + t0) * 16, (n_end - t0) * 64);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      ch.c[u] = load16(rc, lane_off + u * 1024);
+      ch.sn[u] = load16(rs, lane_off + u * 1024);
     }
   }
 }
@@ -624,9 +687,10 @@ __global__ __launch_bounds__(kThreads) void apply_bf16(const u32x4_t* __restrict
                                                        int64_t La, float eps, const float* __restrict__ cos_t,
                                                        const float* __restrict__ sin_t, int64_t pos0) {
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int m = lane & 15;
   const int g = lane >> 4;
+  const int lane_off = m * 64 + g * 16;  // features 8g .. 8g+7 of tile row m
   const int64_t f_begin = (int64_t)blockIdx.x * La;
   const int64_t f_end = (f_begin + La < total) ? f_begin + La : total;
 
@@ -638,27 +702,25 @@ __global__ __launch_bounds__(kThreads) void apply_bf16(const u32x4_t* __restrict
     const int64_t c_end = ((int64_t)c + 1) * L < N ? ((int64_t)c + 1) * L : N;
     const int64_t n_end = (f_end - bh * N < c_end) ? f_end - bh * N : c_end;
     f = bh * N + n_end;
-    const u32x4_t* Qh = Q + bh * N * 4 + g;  // 4 x 16 bytes per token row
-    u32x4_t* Oh = O + bh * N * 4 + g;
+    const char* Qh = reinterpret_cast<const char*>(Q + bh * N * 4);  // 64-byte token rows
+    char* Oh = reinterpret_cast<char*>(O + bh * N * 4);
 
     // the first chunk's loads go out before the state operands are fetched,
     // and each chunk's loads before the previous chunk is computed
     int64_t t0 = n_begin + 64 * w;
     ApplyChunk<ROPE> next;
-    if (t0 < n_end) load_apply_chunk<ROPE>(Qh, t0, n_end, m, g, cos_t, sin_t, pos0, next);
+    if (t0 < n_end) load_apply_chunk<ROPE>(Qh, t0, n_end, lane_off, cos_t, sin_t, pos0, next);
     ApplyOperands op;
     const int64_t sc = bh * C + c;
     load_apply_operands(sv.s_base + sc * sv.s_stride, sv.z_base + sc * sv.z_stride, g, m, op);
 
     for (; t0 < n_end; t0 += 256) {
       const ApplyChunk<ROPE> cur = next;
-      if (t0 + 256 < n_end) load_apply_chunk<ROPE>(Qh, t0 + 256, n_end, m, g, cos_t, sin_t, pos0, next);
+      if (t0 + 256 < n_end) load_apply_chunk<ROPE>(Qh, t0 + 256, n_end, lane_off, cos_t, sin_t, pos0, next);
+      const rsrc_t ro = make_rsrc(Oh + t0 * 64, (n_end - t0) * 64);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int64_t tok = t0 + 16 * u + m;
-        const u32x4_t o = apply_tile<ROPE>(cur.q[u], op, eps, cur.c[u], cur.sn[u]);
-        if (tok < n_end) __builtin_nontemporal_store(o, &Oh[tok * 4]);
-      }
+      for (int u = 0; u < 4; ++u)
+        store16_nt(ro, lane_off + u * 1024, apply_tile<ROPE>(cur.q[u], op, eps, cur.c[u], cur.sn[u]));
     }
   }
 }
