@@ -328,38 +328,72 @@ __device__ __forceinline__ u32x4_t relu_bf16x8(u32x4_t x) {
 }
 
 // cos and sin that lane (n, g) needs for a 32-token tile at t0: element
-// [fh][tb][i] belongs to pair 8fh + n / 2 of token t0 + 16tb + 4g + i.  Rows at
-// or past n_end read 0 (their phi(K) is 0 as well).
+// [fh][tb][i] belongs to pair 8fh + n / 2 of token t0 + 16tb + 4g + i.  They
+// are loaded like K (16-byte row pieces: lane (n, g) gets pairs 4g .. 4g+3 of
+// token t0 + 16tb + n; rows at or past n_end read 0, as does their phi(K)) and
+// turned around through a wave-private LDS tile, [cos | sin][32 rows][kAngRow]
+// floats: with rows of 18 floats the 16 lanes of each group g read 8
+// consecutive banks of their own.
+constexpr int kAngRow = 18;
+constexpr int kAngTile = 2 * 32 * kAngRow;  // floats per wave
+
 struct TileAngles {
   f32x4_t c[2][2], s[2][2];
 };
 
-__device__ __forceinline__ void gather_angles(const float* cos_t, const float* sin_t, int64_t pos0, int64_t t0,
-                                              int64_t n_end, int g, int n, TileAngles& ang) {
+struct TileAnglesRows {
+  f32x4_t c[2], s[2];
+};
+
+__device__ __forceinline__ void load_angle_rows(const float* cos_t, const float* sin_t, int64_t pos0, int64_t t0,
+                                                int64_t n_end, int lane_off, TileAnglesRows& rows) {
   const rsrc_t rc = make_rsrc(cos_t + (pos0 + t0) * 16, (n_end - t0) * 64);
   const rsrc_t rs = make_rsrc(sin_t + (pos0 + t0) * 16, (n_end - t0) * 64);
-  const int lane = 4 * g * 64 + (n >> 1) * 4;
 #pragma unroll
-  for (int fh = 0; fh < 2; ++fh)
+  for (int tb = 0; tb < 2; ++tb) {
+    rows.c[tb] = load16(rc, lane_off + tb * 1024);
+    rows.s[tb] = load16(rs, lane_off + tb * 1024);
+  }
+}
+
+// Every lane of the wave writes and then reads the tile: the wavefront-scope
+// fences keep the compiler from moving LDS accesses across them (a wave's LDS
+// accesses are performed in order, so no wait is needed).
+__device__ __forceinline__ void turn_angles(const TileAnglesRows& rows, float* lds, int g, int n, TileAngles& ang) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
+  for (int tb = 0; tb < 2; ++tb) {
+    float* rc = lds + (16 * tb + n) * kAngRow + 4 * g;
+    float* rs = rc + 32 * kAngRow;
+    *reinterpret_cast<float2*>(rc) = float2{rows.c[tb][0], rows.c[tb][1]};
+    *reinterpret_cast<float2*>(rc + 2) = float2{rows.c[tb][2], rows.c[tb][3]};
+    *reinterpret_cast<float2*>(rs) = float2{rows.s[tb][0], rows.s[tb][1]};
+    *reinterpret_cast<float2*>(rs + 2) = float2{rows.s[tb][2], rows.s[tb][3]};
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        ang.c[fh][tb][i] = load4(rc, lane + (16 * tb + i) * 64 + 32 * fh);
-        ang.s[fh][tb][i] = load4(rs, lane + (16 * tb + i) * 64 + 32 * fh);
+  for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float* rc = lds + (16 * tb + 4 * g + i) * kAngRow + (n >> 1);
+#pragma unroll
+      for (int fh = 0; fh < 2; ++fh) {
+        ang.c[fh][tb][i] = rc[8 * fh];
+        ang.s[fh][tb][i] = rc[32 * kAngRow + 8 * fh];
       }
+    }
 }
 
 // acc[fh][fh']: S blocks (key half fh, value half fh'); accz[fh]: z of key half fh
 template <bool ROPE>
-__device__ __forceinline__ void state_tile(const u32x4_t (&kx)[2], const u32x4_t (&vx)[2], int64_t t0,
-                                           int64_t n_end, int g, int n, const float* cos_t, const float* sin_t,
-                                           int64_t pos0, const bf16x8_t (&sel)[2], const bf16x8_t (&selp)[2],
+__device__ __forceinline__ void state_tile(const u32x4_t (&kx)[2], const u32x4_t (&vx)[2],
+                                           const TileAnglesRows& rows, int g, int n, float* lds,
+                                           const bf16x8_t (&sel)[2], const bf16x8_t (&selp)[2],
                                            f32x4_t (&acc)[2][2], f32x4_t (&accz)[2]) {
   const unsigned one2 = 0x3f803f80u;  // two bf16 1.0
   const bf16x8_t ones = as_bf16x8(one2, one2, one2, one2);
-  TileAngles ang;
-  if constexpr (ROPE) gather_angles(cos_t, sin_t, pos0, t0, n_end, g, n, ang);
   bf16x8_t k_nat[2], v_nat[2];
 #pragma unroll
   for (int tb = 0; tb < 2; ++tb) {
@@ -384,6 +418,8 @@ __device__ __forceinline__ void state_tile(const u32x4_t (&kx)[2], const u32x4_t
       acc[fh][1] = mfma16(a[fh], b[1], acc[fh][1]);
     }
   } else {
+    TileAngles ang;
+    turn_angles(rows, lds, g, n, ang);
     unsigned part[3][2][4];  // [bf16 part][fh][dword]: the slot order of a[fh]
 #pragma unroll
     for (int fh = 0; fh < 2; ++fh) {
@@ -415,6 +451,7 @@ __global__ __launch_bounds__(kThreads) void state_bf16(const u32x4_t* __restrict
                                                        const float* __restrict__ sin_t, int64_t pos0,
                                                        StateArgs a) {
   __shared__ float red[4][kStateElems];
+  __shared__ float angles[ROPE ? 4 : 1][ROPE ? kAngTile : 1];
 
   int64_t bh, n_begin, n_end;
   int c, s;
@@ -444,6 +481,7 @@ __global__ __launch_bounds__(kThreads) void state_bf16(const u32x4_t* __restrict
   // the next chunk's loads are issued before the current chunk is computed
   int64_t t0 = n_begin + 64 * w;
   u32x4_t nk[4], nv[4];
+  TileAnglesRows na[2];  // cos/sin rows of the two tiles (RoPE only)
   auto load_chunk = [&](int64_t c0) {
     const rsrc_t rk = make_rsrc(Kh + c0 * 64, (n_end - c0) * 64);
     const rsrc_t rv = make_rsrc(Vh + c0 * 64, (n_end - c0) * 64);
@@ -452,14 +490,20 @@ __global__ __launch_bounds__(kThreads) void state_bf16(const u32x4_t* __restrict
       nk[h] = load16_nt(rk, lane_off + h * 1024);
       nv[h] = load16_nt(rv, lane_off + h * 1024);
     }
+    if constexpr (ROPE) {
+      load_angle_rows(cos_t, sin_t, pos0, c0, n_end, lane_off, na[0]);
+      load_angle_rows(cos_t, sin_t, pos0, c0 + 32, n_end, lane_off, na[1]);
+    }
   };
+  float* lds = angles[ROPE ? w : 0];
   if (t0 < n_end) load_chunk(t0);
   for (; t0 < n_end; t0 += 256) {
     const u32x4_t ka[2] = {nk[0], nk[1]}, va[2] = {nv[0], nv[1]};
     const u32x4_t kb[2] = {nk[2], nk[3]}, vb[2] = {nv[2], nv[3]};
+    const TileAnglesRows ra = na[0], rb = na[1];
     if (t0 + 256 < n_end) load_chunk(t0 + 256);
-    state_tile<ROPE>(ka, va, t0, n_end, g, n, cos_t, sin_t, pos0, sel, selp, acc, accz);
-    if (t0 + 32 < n_end) state_tile<ROPE>(kb, vb, t0 + 32, n_end, g, n, cos_t, sin_t, pos0, sel, selp, acc, accz);
+    state_tile<ROPE>(ka, va, ra, g, n, lds, sel, selp, acc, accz);
+    if (t0 + 32 < n_end) state_tile<ROPE>(kb, vb, rb, g, n, lds, sel, selp, acc, accz);
   }
 
   // D lane (n, g): rows 4g + i -> key feature 16fh + 4g + i, column n -> value feature 16fh' + n

@@ -32,11 +32,10 @@ namespace {
 // MI355X: 256 compute units.  Both passes size their grids to one resident
 // round of workgroups, at the count that measured fastest on the Sana-1.6B
 // 4096 px layer: state 2 per CU (8 waves, each with a 64-token chunk of K and V
-// in flight; 3 with RoPE, whose longer tiles need more waves to cover memory
-// latency), apply 3 per CU (2 with RoPE, whose register use allows no more).
+// in flight; the RoPE variant's register use allows no more), apply 3 per CU
+// (2 with RoPE, for the same reason).
 constexpr int64_t kCUs = 256;
 constexpr int64_t kStateGroups = kCUs * 2;
-constexpr int64_t kStateGroupsRope = kCUs * 3;
 constexpr int64_t kApplyGroups = kCUs * 3;
 constexpr int64_t kApplyGroupsRope = kCUs * 2;
 constexpr int64_t kMaxSplits = 64;       // partial states per chunk
@@ -66,9 +65,9 @@ Geometry make_geometry(int64_t BH, int64_t N, int64_t L, bool rope) {
   if (BH <= 0 || N <= 0) return g;
   g.L = L < N ? L : N;
   g.C = ceil_div(N, g.L);
-  // splits per chunk: about kStateGroups (kStateGroupsRope) workgroups in all, at least
+  // splits per chunk: about kStateGroups workgroups in all, at least
   // kMinSplitTokens tokens each
-  int64_t p = ceil_div((rope ? kStateGroupsRope : kStateGroups) / BH, g.C);
+  int64_t p = ceil_div(kStateGroups / BH, g.C);
   const int64_t p_max = ceil_div(g.L, kMinSplitTokens);
   if (p > p_max) p = p_max;
   if (p > kMaxSplits) p = kMaxSplits;
