@@ -15,4 +15,5 @@ from .linattn_oracle import (  # noqa: F401
     block_forward,
     block_causal,
     brute_force,
+    backward,
 )

@@ -42,6 +42,12 @@ reason in the design notes of this repository):
   * Block-causal visibility: a token sees every token of its own chunk and of
     all earlier chunks, never a later chunk ([Video news] "Design details";
     [Video note] 2.3).
+  * Backward: the pages say the linear attention's forward and backward passes
+    are fused kernels ([Sana note] "Infra") and that the block-causal model is
+    trained ([Video note] 3), but print no gradient formulas.  The gradients
+    here are those of L = sum_i dout_i . O_i, by the chain rule through the
+    forward above, with ReLU'(0) = 0 (the subgradient that keeps exact-zero
+    inputs out of the gradient).
 """
 
 import numpy as np
@@ -225,3 +231,83 @@ def brute_force(q, k, v, eps=1e-6, angles=None, chunk=None):
         A = A * M
         A_num = A_num * M
     return np.matmul(A_num, v) / (A.sum(axis=-1, keepdims=True) + eps)
+
+
+# --------------------------------------------------------------------------
+# Backward
+# --------------------------------------------------------------------------
+
+def backward(q, k, v, dout, eps=1e-6, angles=None, chunk=None, S_in=None, z_in=None, dS_out=None, dz_out=None):
+    """Gradients of L = sum_i dout_i . O_i (+ <dS_out, S_out> + dz_out . z_out)
+    for block-causal attention with chunks of `chunk` tokens (None: one chunk,
+    i.e. non-causal) started from the carried state (S_in, z_in), where
+    (S_out, z_out) is the state after the last chunk (what a commit stores).
+
+    The forward of [Video note] 2.1-2.3 per chunk c, with S_c = S_in + the
+    chunks up to and including c (and z_c likewise):
+      num_i = phi~(Q_i) S_c,  den_i = phi(Q_i).z_c + eps,  O_i = num_i / den_i.
+    Chain rule, query side (tokens i of chunk c):
+      dnum_i = dout_i / den_i,  dden_i = -(dout_i . num_i) / den_i^2
+      dphi(Q_i) = R_i^T (S_c dnum_i) + z_c dden_i,  dQ_i = [Q_i > 0] dphi(Q_i)
+      dS_c = sum_i phi~(Q_i) dnum_i^T,  dz_c = sum_i phi(Q_i) dden_i.
+    Key side: chunk c's keys enter every S_c' with c' >= c and S_out, so with
+      G_c = dS_out + sum_{c' >= c} dS_c'  (Gz_c likewise)
+      dphi(K_j) = R_j^T (G_c V_j) + Gz_c,  dK_j = [K_j > 0] dphi(K_j),
+      dV_j = G_c^T phi~(K_j).
+    The carried state enters every S_c and S_out: dS_in = G_0, dz_in = Gz_0.
+
+    Returns (dq, dk, dv, dS_in, dz_in).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    N, D = q.shape[-2], q.shape[-1]
+    lead = q.shape[:-2]
+    L = N if chunk is None else chunk
+    phiq = feature_map(q)
+    phik = feature_map(k)
+    pos = _positions(angles, N, 0)
+    phiq_num = phiq if pos is None else rotate_pairs(phiq, pos)
+    phik_num = phik if pos is None else rotate_pairs(phik, pos)
+    chunks = [slice(start, min(N, start + L)) for start in range(0, N, L)]
+
+    # forward states: S_c, z_c after each chunk
+    S = np.zeros(lead + (D, D)) if S_in is None else np.asarray(S_in, dtype=np.float64)
+    z = np.zeros(lead + (D,)) if z_in is None else np.asarray(z_in, dtype=np.float64)
+    states = []
+    for sl in chunks:
+        S = S + np.matmul(np.swapaxes(phik_num[..., sl, :], -1, -2), v[..., sl, :])
+        z = z + phik[..., sl, :].sum(axis=-2)
+        states.append((S, z))
+
+    # query side
+    dq = np.zeros(q.shape)
+    dS_chunk, dz_chunk = [], []
+    for sl, (S_c, z_c) in zip(chunks, states):
+        num = np.matmul(phiq_num[..., sl, :], S_c)
+        den = np.matmul(phiq[..., sl, :], z_c[..., :, None]) + eps
+        dnum = dout[..., sl, :] / den
+        dden = -(dout[..., sl, :] * num).sum(axis=-1, keepdims=True) / den ** 2
+        dphiq_num = np.matmul(dnum, np.swapaxes(S_c, -1, -2))
+        dphiq_rot = dphiq_num if pos is None else rotate_pairs(dphiq_num, -pos[sl])
+        dphiq = dphiq_rot + dden * z_c[..., None, :]
+        dq[..., sl, :] = dphiq * (q[..., sl, :] > 0)
+        dS_chunk.append(np.matmul(np.swapaxes(phiq_num[..., sl, :], -1, -2), dnum))
+        dz_chunk.append((phiq[..., sl, :] * dden).sum(axis=-2))
+
+    # key side: suffix sums of the query-side state gradients
+    G = np.zeros(lead + (D, D)) if dS_out is None else np.asarray(dS_out, dtype=np.float64)
+    Gz = np.zeros(lead + (D,)) if dz_out is None else np.asarray(dz_out, dtype=np.float64)
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
+    for c in range(len(chunks) - 1, -1, -1):
+        sl = chunks[c]
+        G = G + dS_chunk[c]
+        Gz = Gz + dz_chunk[c]
+        dphik_num = np.matmul(v[..., sl, :], np.swapaxes(G, -1, -2))
+        dphik_rot = dphik_num if pos is None else rotate_pairs(dphik_num, -pos[sl])
+        dphik = dphik_rot + Gz[..., None, :]
+        dk[..., sl, :] = dphik * (k[..., sl, :] > 0)
+        dv[..., sl, :] = np.matmul(phik_num[..., sl, :], G)
+    return dq, dk, dv, G, Gz

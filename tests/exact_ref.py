@@ -104,3 +104,78 @@ def token_causal_recurrence(q, k, v, eps):
         out.append([float(sum((pq[d] * S[d][e] for d in range(D)), Fraction(0)) / den)
                     for e in range(D)])
     return out
+
+
+def _transpose(R):
+    return [list(row) for row in zip(*R)]
+
+
+def exact_gradients(q, k, v, dout, eps, cos=None, sin=None, chunk=None):
+    """Gradients of L = sum_i dout_i . O_i, differentiating the quadratic
+    definition above directly (not its linear/state form), exactly.
+
+      O_i = Num_i / d_i,  Num_i = sum_j M_ij A'_ij V_j,  d_i = sum_j M_ij A_ij + eps
+      dL/dV_j   = sum_i M_ij A'_ij dout_i / d_i
+      dL/dA'_ij = M_ij (dout_i . V_j) / d_i
+      dL/dA_ij  = -M_ij (dout_i . Num_i) / d_i^2
+      A'_ij = (R_i p_i).(R_j r_j): gradient R_i^T R_j r_j in p_i, R_j^T R_i p_i in r_j
+      A_ij  = p_i . r_j,  p = relu(Q), r = relu(K);  dQ = [Q > 0] dL/dp, dK = [K > 0] dL/dr.
+
+    Returns (dq, dk, dv) as [N][D] floats.
+    """
+    Q, K, V, G = _frac_rows(q), _frac_rows(k), _frac_rows(v), _frac_rows(dout)
+    eps = Fraction(float(eps))
+    N, D = len(Q), len(Q[0])
+    pq = [[_relu(x) for x in row] for row in Q]
+    pk = [[_relu(x) for x in row] for row in K]
+    if cos is not None:
+        C, S = _frac_rows(cos), _frac_rows(sin)
+        R = [_rotation_matrix(C[i], S[i]) for i in range(N)]
+        rq = [_matvec(R[i], pq[i]) for i in range(N)]
+        rk = [_matvec(R[j], pk[j]) for j in range(N)]
+    else:
+        rq, rk = pq, pk
+
+    def seen(i, j):
+        return chunk is None or j // chunk <= i // chunk
+
+    num, den = [], []
+    for i in range(N):
+        n_i = [Fraction(0)] * D
+        d_i = eps
+        for j in range(N):
+            if not seen(i, j):
+                continue
+            a = sum((pq[i][d] * pk[j][d] for d in range(D)), Fraction(0))
+            a_num = sum((rq[i][d] * rk[j][d] for d in range(D)), Fraction(0))
+            d_i += a
+            for e in range(D):
+                n_i[e] += a_num * V[j][e]
+        num.append(n_i)
+        den.append(d_i)
+
+    dp = [[Fraction(0)] * D for _ in range(N)]
+    dr = [[Fraction(0)] * D for _ in range(N)]
+    dV = [[Fraction(0)] * D for _ in range(N)]
+    for i in range(N):
+        g_dot_num = sum((G[i][e] * num[i][e] for e in range(D)), Fraction(0))
+        for j in range(N):
+            if not seen(i, j):
+                continue
+            a_num = sum((rq[i][d] * rk[j][d] for d in range(D)), Fraction(0))
+            for e in range(D):
+                dV[j][e] += a_num * G[i][e] / den[i]
+            g_a_num = sum((G[i][e] * V[j][e] for e in range(D)), Fraction(0)) / den[i]
+            g_a = -g_dot_num / (den[i] * den[i])
+            if cos is not None:
+                to_p = _matvec(_transpose(R[i]), rk[j])   # R_i^T R_j r_j
+                to_r = _matvec(_transpose(R[j]), rq[i])   # R_j^T R_i p_i
+            else:
+                to_p, to_r = pk[j], pq[i]
+            for d in range(D):
+                dp[i][d] += g_a_num * to_p[d] + g_a * pk[j][d]
+                dr[j][d] += g_a_num * to_r[d] + g_a * pq[i][d]
+    dq = [[float(dp[i][d]) if Q[i][d] > 0 else 0.0 for d in range(D)] for i in range(N)]
+    dk = [[float(dr[j][d]) if K[j][d] > 0 else 0.0 for d in range(D)] for j in range(N)]
+    dv = [[float(x) for x in row] for row in dV]
+    return dq, dk, dv

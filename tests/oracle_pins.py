@@ -7,7 +7,7 @@ copies of the oracle and show that each planted mistake is caught.
 
 import numpy as np
 
-from exact_ref import exact_attention, exact_state, token_causal_recurrence
+from exact_ref import exact_attention, exact_gradients, exact_state, token_causal_recurrence
 
 EPS = 1e-6
 
@@ -291,8 +291,74 @@ def pin_block_rope_positions(impl):
     _close(o, impl.brute_force(q, k, v, EPS, angles=ang, chunk=L), 1e-11, "block RoPE vs masked quadratic")
 
 
+# --------------------------------------------------------------------------
+# Backward
+# --------------------------------------------------------------------------
+
+def pin_backward_exact(impl):
+    """The state-form gradients against the exact gradients of the quadratic
+    definition (differentiated directly, in rational arithmetic)."""
+    rng = np.random.default_rng(61)
+    for N, D, L, rope in [(3, 2, None, False), (5, 4, 2, False), (7, 4, 1, False), (4, 4, None, True),
+                          (6, 4, 3, True), (5, 6, 5, False)]:
+        q, k, v, do = (_dyadic(rng, (N, D)) for _ in range(4))
+        ang = rng.uniform(-3.0, 3.0, size=(N, D // 2)) if rope else None
+        cs = (np.cos(ang), np.sin(ang)) if rope else (None, None)
+        want = exact_gradients(q, k, v, do, EPS, *cs, chunk=L)
+        got = impl.backward(q[None, None], k[None, None], v[None, None], do[None, None], EPS, angles=ang, chunk=L)
+        for g, w, name in zip(got[:3], want, ("dq", "dk", "dv")):
+            _close(g[0, 0], w, 1e-8, f"{name} vs exact quadratic-form gradient N={N} D={D} chunk={L} rope={rope}")
+
+
+def _away_from_zero(rng, shape):
+    """Normal draws pushed at least 0.2 away from 0, so that a finite-difference
+    step never crosses the ReLU kink."""
+    x = rng.standard_normal(shape)
+    return x + 0.2 * np.sign(x)
+
+
+def pin_backward_finite_differences(impl):
+    """Central differences of the forward (chunk by chunk through block_forward,
+    from a carried state, plus <dS_out, S_out> + dz_out . z_out) against every
+    gradient the backward returns, including those of the carried state."""
+    rng = np.random.default_rng(62)
+    T, Hl, Wl = 2, 2, 3
+    N, D, L = T * Hl * Wl, 8, 5
+    ang = impl.rope3d_angles(T, Hl, Wl, D=D, split=(2, 2, 4))
+    x = {n: _away_from_zero(rng, (N, D)) for n in ("q", "k", "v", "do")}
+    S_in, z_in = rng.standard_normal((D, D)), np.abs(rng.standard_normal(D)) + 0.5
+    dS_out, dz_out = rng.standard_normal((D, D)), rng.standard_normal(D)
+
+    def loss(q, k, v, S, z):
+        total = 0.0
+        for start in range(0, N, L):
+            sl = slice(start, min(N, start + L))
+            o, S, z = impl.block_forward(q[sl][None, None], k[sl][None, None], v[sl][None, None], S[None, None],
+                                         z[None, None], EPS, ang, start)
+            o, S, z = o[0, 0], S[0, 0], z[0, 0]
+            total += float((x["do"][sl] * o).sum())
+        return total + float((dS_out * S).sum()) + float((dz_out * z).sum())
+
+    got = impl.backward(x["q"][None, None], x["k"][None, None], x["v"][None, None], x["do"][None, None], EPS,
+                        angles=ang, chunk=L, S_in=S_in[None, None], z_in=z_in[None, None],
+                        dS_out=dS_out[None, None], dz_out=dz_out[None, None])
+    grads = {"q": got[0][0, 0], "k": got[1][0, 0], "v": got[2][0, 0], "S": got[3][0, 0], "z": got[4][0, 0]}
+    args = {"q": x["q"], "k": x["k"], "v": x["v"], "S": S_in, "z": z_in}
+    h = 1e-5
+    for name, arr in args.items():
+        fd = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            plus = {n: a.copy() for n, a in args.items()}
+            minus = {n: a.copy() for n, a in args.items()}
+            plus[name][idx] += h
+            minus[name][idx] -= h
+            fd[idx] = (loss(**plus) - loss(**minus)) / (2 * h)
+        _close(grads[name], fd, 1e-6, f"d{name} vs central differences of the forward")
+
+
 ALL_PINS = [
     pin_exact_noncausal, pin_exact_state, pin_exact_rope, pin_exact_block, pin_exact_block_rope,
     pin_token_causal, pin_closed_forms, pin_constant_v, pin_invariants, pin_rope_angles,
     pin_rope_properties, pin_block_properties, pin_block_rope_positions,
+    pin_backward_exact, pin_backward_finite_differences,
 ]

@@ -54,6 +54,25 @@ MUTANTS = {
     "block_uses_previous_state_only": ("    o = apply_state(q, S_new, z_new, eps, angles, pos_offset)",
                                        "    o = apply_state(q, np.asarray(S_in, dtype=np.float64), np.asarray(z_in, dtype=np.float64), eps, angles, pos_offset)"),
     "block_positions_restart": ("eps, angles, start)", "eps, angles, 0)"),
+    "bwd_dden_sign": ("dden = -(dout[..., sl, :] * num)", "dden = (dout[..., sl, :] * num)"),
+    "bwd_dden_power": ("/ den ** 2", "/ den"),
+    "bwd_no_relu_mask_on_q": ("dq[..., sl, :] = dphiq * (q[..., sl, :] > 0)", "dq[..., sl, :] = dphiq"),
+    "bwd_relu_mask_inclusive": ("dk[..., sl, :] = dphik * (k[..., sl, :] > 0)",
+                                "dk[..., sl, :] = dphik * (k[..., sl, :] >= 0) + 0.0 * (k[..., sl, :] == 0)"),
+    "bwd_rotation_not_inverted": ("rotate_pairs(dphiq_num, -pos[sl])", "rotate_pairs(dphiq_num, pos[sl])"),
+    "bwd_key_rotation_not_inverted": ("rotate_pairs(dphik_num, -pos[sl])", "rotate_pairs(dphik_num, pos[sl])"),
+    "bwd_state_not_transposed": ("dphiq_num = np.matmul(dnum, np.swapaxes(S_c, -1, -2))",
+                                 "dphiq_num = np.matmul(dnum, S_c)"),
+    "bwd_prefix_not_suffix": ("for c in range(len(chunks) - 1, -1, -1):", "for c in range(len(chunks)):"),
+    "bwd_key_sum_gradient_dropped": ("dphik = dphik_rot + Gz[..., None, :]", "dphik = dphik_rot"),
+    "bwd_dv_unrotated_keys": ("dv[..., sl, :] = np.matmul(phik_num[..., sl, :], G)",
+                              "dv[..., sl, :] = np.matmul(phik[..., sl, :], G)"),
+    "bwd_dS_rotation_dropped": ("dS_chunk.append(np.matmul(np.swapaxes(phiq_num[..., sl, :], -1, -2), dnum))",
+                                "dS_chunk.append(np.matmul(np.swapaxes(phiq[..., sl, :], -1, -2), dnum))"),
+    "bwd_out_gradient_ignored": ("G = np.zeros(lead + (D, D)) if dS_out is None else np.asarray(dS_out, dtype=np.float64)",
+                                 "G = np.zeros(lead + (D, D))"),
+    "bwd_carried_state_ignored": ("S = np.zeros(lead + (D, D)) if S_in is None else np.asarray(S_in, dtype=np.float64)\n    z = np.zeros(lead + (D,)) if z_in is None else np.asarray(z_in, dtype=np.float64)\n    states = []",
+                                  "S = np.zeros(lead + (D, D))\n    z = np.zeros(lead + (D,)) if z_in is None else np.asarray(z_in, dtype=np.float64)\n    states = []"),
 }
 
 
