@@ -128,6 +128,97 @@ def copy_probe(steps, warmup, nbytes=2 ** 30):
                       "ms_per_copy": ms, "gbps_read_plus_write": 2 * nbytes / (ms / 1e3) / 1e9}), flush=True)
 
 
+def backward_bench(w, args, dev, stream):
+    """Time sana_linattn_backward: one call per step (dQ, dK, dV from dO; the
+    chunk states are recomputed from K, V), the block-causal workload as one
+    whole-sequence call.  Algorithmic bytes per token-head: Q, K, V, dO read by
+    the passes that need them (K, V twice: state recompute and key pass; Q, dO
+    once) and dQ, dK, dV written once: 9 tensors x 64 B in bf16."""
+    import numpy as np
+    import torch
+
+    import linear_attention_diffusion_amd as la
+
+    x = generate(w, with_f64=False, names=("q", "k", "v", "dout"))
+
+    def to_dev(raw):
+        if w.dtype == "bf16":
+            return torch.from_numpy(raw.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(raw).to(dev)
+
+    base = {n: to_dev(x.raw[n]) for n in ("q", "k", "v", "dout")}
+    set_bytes = 7 * base["q"].numel() * base["q"].element_size()
+    n_sets = max(2, min(16, math.ceil(1.5 * 2 ** 30 / set_bytes) + 1))
+    sets = []
+    for i in range(n_sets):
+        s = {n: (t if i == 0 else t.clone()) for n, t in base.items()}
+        for n in ("dq", "dk", "dv"):
+            s[n] = torch.empty_like(base["q"])
+        sets.append(s)
+    chunk = w.chunk if w.mode == "block" else w.N
+    rope = la.rope3d_device(*w.grid, dev) if w.mode == "rope" else None
+    dt = la.SANA_DT_BF16 if w.dtype == "bf16" else la.SANA_DT_F32
+    nb = la.backward_workspace_bytes(w.B, w.H, w.N, chunk, dtype=dt, has_rope=rope is not None)
+    ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
+    L = la.lib()
+    P = ctypes.c_void_p
+    rope_ref = None if rope is None else ctypes.byref(rope.struct())
+    st_ptr = ctypes.c_void_p(stream.cuda_stream)
+    calls = [(P(s["q"].data_ptr()), P(s["k"].data_ptr()), P(s["v"].data_ptr()), P(s["dout"].data_ptr()),
+              P(s["dq"].data_ptr()), P(s["dk"].data_ptr()), P(s["dv"].data_ptr()), None, None, None, None, None,
+              None, w.B, w.H, w.N, chunk, w.D, dt, w.eps, rope_ref, P(ws.data_ptr()), ws.numel(), st_ptr)
+             for s in sets]
+
+    def step(i):
+        rc = L.sana_linattn_backward(*calls[i % n_sets])
+        if rc:
+            raise la.SanaError(rc)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_start = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms = e0.elapsed_time(e1) / args.steps
+    elem = 2 if w.dtype == "bf16" else 4
+    alg_bytes = w.token_heads * 9 * w.D * elem
+    # fp32 multiply-adds per token-head of the backward: the forward state
+    # recompute (S, z: 32*32 + 32), the query pass (num, den, S dnum, dS, dz:
+    # 3*32*32 + 2*32) and the key pass (G V, G^T phi~(K): 2*32*32), 2 flop each
+    flops = w.token_heads * 2 * (6 * 32 * 32 + 3 * 32)
+    rec = {
+        "metric": "linear-attn backward tokens·heads/s (dQ, dK, dV)",
+        "value": w.token_heads * args.steps / (ms * args.steps / 1e3),
+        "unit": UNIT,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic: seeded i.i.d. N(0,1)x0.5 bf16 tensors at the workload's latent shape (dO drawn after Q, K, V)",
+        "config": {"workload": w.name, "pass": "backward", "B": w.B, "H": w.H, "N": w.N, "D": w.D,
+                   "mode": w.mode, "chunk": chunk, "grid": w.grid, "input_sets_cycled": n_sets},
+        "call": {"entry_point": "sana_linattn_backward",
+                 "kernels": "state pass + finalize + query pass + reverse finalize + key pass",
+                 "avg_ms": ms, "algorithmic_bytes": alg_bytes,
+                 "achieved_gbps": alg_bytes / (ms / 1e3) / 1e9,
+                 "frac_of_hbm_peak": alg_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS,
+                 "flops": flops, "achieved_tflops": flops / (ms / 1e3) / 1e12},
+        "wall_s_timed_region": wall,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -139,6 +230,9 @@ def main():
     ap.add_argument("--block-mode", choices=["chunks", "sequence"], default="chunks",
                     help="block-causal workload: one block_forward call per chunk (inference, the default) or "
                          "one block_causal call over the whole sequence (all chunks known at once)")
+    ap.add_argument("--pass", dest="which", choices=["forward", "backward"], default="forward",
+                    help="forward (the default; the headline metric) or backward: one sana_linattn_backward "
+                         "call per step (dQ, dK, dV; whole sequence in block-causal chunks for that workload)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="time a plain 1 GiB device-to-device copy instead (HBM reference and counter scale)")
     args = ap.parse_args()
@@ -161,6 +255,9 @@ def main():
     dev = torch.device("cuda:0")
     la.lib()
     stream = torch.cuda.current_stream(dev)
+    if args.which == "backward":
+        backward_bench(w, args, dev, stream)
+        return
 
     x = generate(w, with_f64=False)
 

@@ -168,6 +168,44 @@ int sana_linattn_block_causal(const void* q, const void* k, const void* v, void*
 size_t sana_linattn_block_causal_workspace_bytes(int B, int H, int64_t N, int64_t chunk, int D, int dtype,
                                                  int has_rope);
 
+/* Backward of sana_linattn_block_causal (and, with chunk >= N, of
+ * sana_linattn_forward).  The "Sana" research note (Infra) fuses the linear
+ * attention's forward and backward into kernels, and "SANA-Video" paper notes
+ * 3 train the block-causal model; the pages print no gradient formulas, so
+ * these are the chain rule through the forward above, for
+ *   L = sum_n dout_n . O_n + <dkv_out, S_last> + dksum_out . z_last
+ * with S_last/z_last the state after the last chunk (what a commit stores):
+ *   den_n = phi(Q_n).z_c + eps,  dnum_n = dout_n / den_n,
+ *   dden_n = -(dout_n . phi~(Q_n) S_c) / den_n^2           (c = c(n))
+ *   dq_n = [Q_n > 0] (R_n^T S_c dnum_n + z_c dden_n)
+ *   G_c  = dkv_out + sum_{c' >= c} sum_{n in c'} phi~(Q_n) dnum_n^T   (Gz_c with phi(Q_n) dden_n)
+ *   dk_n = [K_n > 0] (R_n^T G_c V_n + Gz_c),   dv_n = G_c^T phi~(K_n)
+ *   dkv_in = G_0, dksum_in = Gz_0
+ * (ReLU'(0) = 0; R_n: the RoPE rotation at position pos_offset + n, identity
+ * without rope).  The chunk states S_c are recomputed from k, v and kv_in.
+ * q, k, v, dout: inputs [B][H][N][D] of one dtype; dq, dk, dv: outputs of the
+ * same shape and dtype, overlapping nothing.  kv_in/ksum_in: state the forward
+ * started from, or both NULL (zero).  dkv_out/dksum_out: gradient reaching the
+ * committed final state, or both NULL (zero).  dkv_in/dksum_in: where the
+ * gradient of kv_in/ksum_in is stored, or both NULL; they may equal
+ * dkv_out/dksum_out (in place), no other overlap is allowed.  Chaining: the
+ * backward of a chunk-by-chunk block_forward loop is this call chunk by chunk
+ * in reverse order, each passing its dkv_in on as the previous chunk's
+ * dkv_out.  N = 0 writes nothing.  Workspace:
+ * sana_linattn_backward_workspace_bytes.  Errors as for block_causal. */
+int sana_linattn_backward(const void* q, const void* k, const void* v, const void* dout,
+                          void* dq, void* dk, void* dv,
+                          const float* kv_in, const float* ksum_in,
+                          const float* dkv_out, const float* dksum_out,
+                          float* dkv_in, float* dksum_in,
+                          int B, int H, int64_t N, int64_t chunk, int D, int dtype, float eps,
+                          const sana_rope* rope, void* ws, size_t ws_bytes, void* hip_stream);
+
+/* Workspace bytes for sana_linattn_backward with these sizes (0 when B*H*N == 0
+ * or the sizes are invalid).  Pure host function. */
+size_t sana_linattn_backward_workspace_bytes(int B, int H, int64_t N, int64_t chunk, int D, int dtype,
+                                             int has_rope);
+
 /* Apply a given state to queries, without changing it ("SANA-Video" paper
  * notes 2.1: the precomputed sum is reused by every token; 2.2: RoPE in the
  * numerator only):

@@ -2,7 +2,7 @@
 
 Entry points (same names as the C ABI in include/sana_linattn.h):
   sana_linattn_forward, sana_linattn_state_update, sana_linattn_block_forward,
-  sana_linattn_block_causal, sana_linattn_apply,
+  sana_linattn_block_causal, sana_linattn_apply, sana_linattn_backward,
   rope3d_table / rope3d_device (host builder of the 3D RoPE tables).
 """
 
@@ -21,8 +21,10 @@ from .binding import (  # noqa: F401
     make_workspace,
     rope3d_device,
     rope3d_table,
+    backward_workspace_bytes,
     block_causal_workspace_bytes,
     sana_linattn_apply,
+    sana_linattn_backward,
     sana_linattn_block_causal,
     sana_linattn_block_forward,
     sana_linattn_forward,

@@ -24,6 +24,8 @@ EXPORTED = (
     "sana_linattn_block_causal",
     "sana_linattn_block_causal_workspace_bytes",
     "sana_linattn_apply",
+    "sana_linattn_backward",
+    "sana_linattn_backward_workspace_bytes",
     "sana_linattn_rope3d_table",
     "sana_linattn_status_string",
 )
@@ -64,6 +66,11 @@ def lib():
     L.sana_linattn_block_causal_workspace_bytes.restype = sz
     L.sana_linattn_apply.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32, i32, f32, rp, vp]
     L.sana_linattn_apply.restype = i32
+    L.sana_linattn_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i64, i64,
+                                        i32, i32, f32, rp, vp, sz, vp]
+    L.sana_linattn_backward.restype = i32
+    L.sana_linattn_backward_workspace_bytes.argtypes = [i32, i32, i64, i64, i32, i32, i32]
+    L.sana_linattn_backward_workspace_bytes.restype = sz
     L.sana_linattn_rope3d_table.argtypes = [i32, i32, i32, i32, i32, i32, i32, ctypes.c_double, vp, vp]
     L.sana_linattn_rope3d_table.restype = i32
     L.sana_linattn_status_string.argtypes = [i32]
@@ -270,6 +277,47 @@ def sana_linattn_block_causal(q, k, v, chunk, o=None, kv_in=None, ksum_in=None, 
                                            _rope_arg(rope), _ptr(workspace), workspace.numel(),
                                            _stream(stream, q.device)))
     return o
+
+
+def backward_workspace_bytes(B, H, N, chunk, D=32, dtype=SANA_DT_BF16, has_rope=False):
+    return lib().sana_linattn_backward_workspace_bytes(B, H, N, int(chunk), D, dtype, int(bool(has_rope)))
+
+
+def sana_linattn_backward(q, k, v, dout, chunk=None, dq=None, dk=None, dv=None, kv_in=None, ksum_in=None,
+                          dkv_out=None, dksum_out=None, dkv_in=None, dksum_in=None, eps=1e-6, rope=None,
+                          workspace=None, stream=None):
+    """Gradients of sum(dout * O) (+ <dkv_out, S_last> + dksum_out . z_last) of
+    block-causal attention with chunks of `chunk` tokens (None: one chunk, the
+    non-causal forward).  Returns (dq, dk, dv); dkv_in/dksum_in, when given,
+    receive the gradient of the carried state kv_in/ksum_in."""
+    torch = _torch()
+    B, H, N, D = _shape4(q, "q")
+    for t, name in ((k, "k"), (v, "v"), (dout, "dout")):
+        if _shape4(t, name) != (B, H, N, D) or t.dtype != q.dtype:
+            raise ValueError("q, k, v, dout must have the same shape and dtype")
+    outs = []
+    for t, name in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        if t is None:
+            t = torch.empty_like(q)
+        elif _shape4(t, name) != (B, H, N, D) or t.dtype != q.dtype:
+            raise ValueError(f"{name} must match q in shape and dtype")
+        outs.append(t)
+    for t, shape in ((kv_in, (B, H, D, D)), (ksum_in, (B, H, D)), (dkv_out, (B, H, D, D)), (dksum_out, (B, H, D)),
+                     (dkv_in, (B, H, D, D)), (dksum_in, (B, H, D))):
+        if t is not None and (tuple(t.shape) != shape or t.dtype != torch.float32 or not t.is_contiguous()):
+            raise ValueError("states must be contiguous float32 [B, H, D, D] / [B, H, D]")
+    L = N if chunk is None else int(chunk)
+    L = max(L, 1)
+    dt = _dtype_code(q)
+    if workspace is None:
+        workspace = torch.empty(max(backward_workspace_bytes(B, H, N, L, D, dt, rope is not None), 256),
+                                dtype=torch.uint8, device=q.device)
+    _check(lib().sana_linattn_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(outs[0]), _ptr(outs[1]),
+                                       _ptr(outs[2]), _ptr(kv_in), _ptr(ksum_in), _ptr(dkv_out), _ptr(dksum_out),
+                                       _ptr(dkv_in), _ptr(dksum_in), B, H, N, L, D, dt, float(eps),
+                                       _rope_arg(rope), _ptr(workspace), workspace.numel(),
+                                       _stream(stream, q.device)))
+    return tuple(outs)
 
 
 def sana_linattn_apply(q, kv_state, ksum_state, o=None, eps=1e-6, rope=None, stream=None):

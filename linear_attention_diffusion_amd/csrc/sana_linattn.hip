@@ -14,8 +14,9 @@
 //   3. apply pass  (equal contiguous ranges of the flattened head x token
 //                   space, one per workgroup, each cut at head and chunk
 //                   boundaries)
-// state_update runs 1-2 only, apply runs 3 only.  Nothing is allocated, freed
-// or synchronised.
+// state_update runs 1-2 only, apply runs 3 only.  The backward runs 1-2 to
+// recompute the chunk states, then its query pass, a reverse finalize and its
+// key pass.  Nothing is allocated, freed or synchronised.
 
 #include "sana_linattn.h"
 
@@ -25,6 +26,7 @@
 #include <cstdint>
 #include <cstring>
 
+#include "la_backward.h"
 #include "la_kernels.h"
 
 namespace {
@@ -274,6 +276,106 @@ int attend(const void* q, const void* k, const void* v, void* o, const float* kv
   return launch_status();
 }
 
+// Backward: recompute the chunk states (state pass + finalize), then the query
+// pass (dQ, partial dS/dz), the reverse finalize (suffix sums G_c, gradient of
+// the carried state) and the key pass (dK, dV).  The workspace layout is the
+// forward's: the query pass reuses the partials, the reverse finalize
+// overwrites the chunk states with G_c once the query pass has read them.
+template <typename T>
+void launch_backward(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk, void* dv,
+                     float eps, const Geometry& g, const sana_rope* rope, const la::StateArgs& fwd,
+                     const la::StateArgs& bwd, hipStream_t st) {
+  const float* ct = rope ? rope->cos : nullptr;
+  const float* sn = rope ? rope->sin : nullptr;
+  const int64_t pos0 = rope ? rope->pos_offset : 0;
+  const T* Q = static_cast<const T*>(q);
+  const T* K = static_cast<const T*>(k);
+  const T* V = static_cast<const T*>(v);
+  const T* dO = static_cast<const T*>(dout);
+  T* dQ = static_cast<T*>(dq);
+  T* dK = static_cast<T*>(dk);
+  T* dV = static_cast<T*>(dv);
+  const la::StateView view = ws_view(fwd);
+  const dim3 block(la::kThreads);
+  const dim3 qgrid((unsigned)(g.BH * g.C * g.Pc));
+  if (rope)
+    la::bwd_query_vec<T, true><<<qgrid, block, 0, st>>>(Q, dO, dQ, view, eps, ct, sn, pos0, bwd);
+  else
+    la::bwd_query_vec<T, false><<<qgrid, block, 0, st>>>(Q, dO, dQ, view, eps, ct, sn, pos0, bwd);
+  if (g.C * g.Pc > 1) {
+    const int64_t n_elems = g.BH * la::kStateElems;
+    la::state_finalize_reverse<<<dim3((unsigned)ceil_div(n_elems, la::kThreads)), block, 0, st>>>(bwd, n_elems);
+  }
+  const dim3 kgrid((unsigned)(g.BH * g.C * g.T));
+  if (rope)
+    la::bwd_key_vec<T, true><<<kgrid, block, 0, st>>>(K, V, dK, dV, view, g.N, g.L, (int)g.C, (int)g.T, g.Lt, ct,
+                                                       sn, pos0);
+  else
+    la::bwd_key_vec<T, false><<<kgrid, block, 0, st>>>(K, V, dK, dV, view, g.N, g.L, (int)g.C, (int)g.T, g.Lt, ct,
+                                                        sn, pos0);
+}
+
+bool state_pair_ok(const float* s, const float* z) {
+  if ((s == nullptr) != (z == nullptr)) return false;
+  return !s || (aligned(s, 4) && aligned(z, 4));
+}
+
+int backward(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk, void* dv,
+             const float* kv_in, const float* ksum_in, const float* dkv_out, const float* dksum_out, float* dkv_in,
+             float* dksum_in, int B, int H, int64_t N, int64_t L, int D, int dtype, float eps,
+             const sana_rope* rope, void* ws, size_t ws_bytes, void* hip_stream) {
+  int64_t bh = 0, elems = 0;
+  int rc = check_sizes(B, H, N, D, dtype, &bh, &elems);
+  if (rc != SANA_OK) return rc;
+  if (!std::isfinite(eps) || eps < 0.f) return SANA_ERR_INVALID;
+  if (L <= 0) return SANA_ERR_INVALID;
+  if (!state_pair_ok(kv_in, ksum_in) || !state_pair_ok(dkv_out, dksum_out) || !state_pair_ok(dkv_in, dksum_in))
+    return SANA_ERR_INVALID;
+  if (elems == 0) return SANA_OK;
+  const void* inputs[4] = {q, k, v, dout};
+  void* outputs[3] = {dq, dk, dv};
+  for (const void* p : inputs)
+    if (check_tensor(p)) return SANA_ERR_INVALID;
+  for (void* p : outputs)
+    if (check_tensor(p)) return SANA_ERR_INVALID;
+  const size_t bytes = (size_t)elems * elem_size(dtype);
+  const size_t kv_bytes = (size_t)bh * 1024 * sizeof(float), ks_bytes = (size_t)bh * 32 * sizeof(float);
+  // outputs overlap nothing; state gradients overlap no tensor, and dkv_in may
+  // only alias dkv_out exactly (likewise the key sums)
+  const void* states[6] = {kv_in, ksum_in, dkv_out, dksum_out, dkv_in, dksum_in};
+  const size_t state_sizes[6] = {kv_bytes, ks_bytes, kv_bytes, ks_bytes, kv_bytes, ks_bytes};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 4; ++j)
+      if (overlaps(outputs[i], bytes, inputs[j], bytes)) return SANA_ERR_INVALID;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlaps(outputs[i], bytes, outputs[j], bytes)) return SANA_ERR_INVALID;
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(outputs[i], bytes, states[j], state_sizes[j])) return SANA_ERR_INVALID;
+  }
+  for (int i = 0; i < 6; ++i)
+    for (int j = 0; j < 4; ++j)
+      if (overlaps(states[i], state_sizes[i], inputs[j], bytes)) return SANA_ERR_INVALID;
+  for (int i = 0; i < 6; ++i)
+    for (int j = i + 1; j < 6; ++j) {
+      if (!overlaps(states[i], state_sizes[i], states[j], state_sizes[j])) continue;
+      const bool in_place = (i == 2 && j == 4 && states[i] == states[j]) || (i == 3 && j == 5 && states[i] == states[j]);
+      if (!in_place) return SANA_ERR_INVALID;
+    }
+  if ((rc = check_rope(rope, N)) != SANA_OK) return rc;
+  const Geometry g = make_geometry(bh, N, L, rope != nullptr);
+  if ((rc = check_workspace(g, ws, ws_bytes)) != SANA_OK) return rc;
+
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  const la::StateArgs fwd = state_args(ws, g, kv_in, ksum_in, nullptr, nullptr);
+  const la::StateArgs bwd = state_args(ws, g, dkv_out, dksum_out, dkv_in, dksum_in);
+  launch_state(k, v, dtype, g, rope, fwd, st);
+  if (dtype == SANA_DT_BF16)
+    launch_backward<__bf16>(q, k, v, dout, dq, dk, dv, eps, g, rope, fwd, bwd, st);
+  else
+    launch_backward<float>(q, k, v, dout, dq, dk, dv, eps, g, rope, fwd, bwd, st);
+  return launch_status();
+}
+
 size_t workspace(int B, int H, int64_t N, int64_t L, int D, int dtype, int has_rope) {
   int64_t bh = 0, elems = 0;
   if (L <= 0 || check_sizes(B, H, N, D, dtype, &bh, &elems) != SANA_OK) return 0;
@@ -314,6 +416,20 @@ int sana_linattn_block_causal(const void* q, const void* k, const void* v, void*
                               size_t ws_bytes, void* hip_stream) {
   return attend(q, k, v, o, kv_in, ksum_in, kv_out, ksum_out, B, H, N, chunk, D, dtype, eps, rope, ws, ws_bytes,
                 hip_stream);
+}
+
+size_t sana_linattn_backward_workspace_bytes(int B, int H, int64_t N, int64_t chunk, int D, int dtype,
+                                            int has_rope) {
+  return workspace(B, H, N, chunk, D, dtype, has_rope);
+}
+
+int sana_linattn_backward(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk,
+                          void* dv, const float* kv_in, const float* ksum_in, const float* dkv_out,
+                          const float* dksum_out, float* dkv_in, float* dksum_in, int B, int H, int64_t N,
+                          int64_t chunk, int D, int dtype, float eps, const sana_rope* rope, void* ws,
+                          size_t ws_bytes, void* hip_stream) {
+  return backward(q, k, v, dout, dq, dk, dv, kv_in, ksum_in, dkv_out, dksum_out, dkv_in, dksum_in, B, H, N, chunk,
+                  D, dtype, eps, rope, ws, ws_bytes, hip_stream);
 }
 
 int sana_linattn_state_update(const void* k, const void* v, float* kv_state, float* ksum_state, int B, int H,

@@ -211,3 +211,36 @@ def test_block_causal_argument_errors_and_workspace():
     assert bc(ws=None) == la.SANA_ERR_WORKSPACE
     assert bc(nbytes=la.workspace_bytes(1, 2, 640)) == la.SANA_ERR_WORKSPACE   # too small for 10 chunks
     assert bc(q=None) == la.SANA_ERR_INVALID
+
+
+def test_backward_argument_errors_and_workspace():
+    L = la.lib()
+    n = la.backward_workspace_bytes(1, 2, 640, 64)
+    assert n == la.block_causal_workspace_bytes(1, 2, 640, 64)
+    assert la.backward_workspace_bytes(1, 2, 640, 0) == 0
+    span = 1 * 2 * 640 * 32 * 2                       # bytes of one bf16 [1, 2, 640, 32] tensor
+    dQ, dK, dV = (0x60000000 + i * 0x01000000 for i in range(3))
+    S1, Z1, S2, Z2 = 0x68000000, 0x68100000, 0x68200000, 0x68300000
+
+    def bw(q=A, k=Bp, v=C, do=Dp, dq=dQ, dk=dK, dv=dV, kv_in=None, ks_in=None, dkv_out=None, dks_out=None,
+           dkv_in=None, dks_in=None, N=640, chunk=64, eps=1e-6, ws=WS, nbytes=n):
+        return L.sana_linattn_backward(q, k, v, do, dq, dk, dv, kv_in, ks_in, dkv_out, dks_out, dkv_in, dks_in,
+                                       1, 2, N, chunk, 32, la.SANA_DT_BF16, eps, None, ws, nbytes, None)
+
+    assert bw(chunk=0) == la.SANA_ERR_INVALID
+    assert bw(eps=-1.0) == la.SANA_ERR_INVALID
+    assert bw(do=None) == la.SANA_ERR_INVALID
+    assert bw(dv=None) == la.SANA_ERR_INVALID
+    assert bw(dq=dQ + 8) == la.SANA_ERR_INVALID             # misaligned
+    assert bw(dq=A) == la.SANA_ERR_INVALID                  # output aliases an input
+    assert bw(dk=dQ + 64) == la.SANA_ERR_INVALID            # outputs overlap
+    assert bw(kv_in=S1) == la.SANA_ERR_INVALID              # state without its key sum
+    assert bw(dkv_out=S1) == la.SANA_ERR_INVALID
+    assert bw(dkv_in=S1) == la.SANA_ERR_INVALID
+    assert bw(dkv_out=S1, dks_out=Z1, dkv_in=S1 + 64, dks_in=Z2) == la.SANA_ERR_INVALID   # partial overlap
+    assert bw(dkv_in=dV, dks_in=Z1) == la.SANA_ERR_INVALID  # state gradient overlaps an output
+    assert bw(kv_in=S1, ks_in=Z1, dkv_in=S1, dks_in=Z2) == la.SANA_ERR_INVALID   # only dkv_out may be shared
+    assert bw(ws=None) == la.SANA_ERR_WORKSPACE
+    assert bw(nbytes=la.workspace_bytes(1, 2, 640)) == la.SANA_ERR_WORKSPACE
+    assert bw(q=None, k=None, v=None, do=None, dq=None, dk=None, dv=None, N=0, ws=None) == la.SANA_OK
+    assert span < 0x01000000

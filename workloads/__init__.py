@@ -21,7 +21,7 @@ The pages give no activation statistics, so i.i.d. Gaussians stand in for the
 real activations (about half of each tensor is cut by the ReLU).
 
 Recipe: numpy.random.default_rng(seed) (PCG64); float32 standard_normal drawn
-in the order Q, K, V, each [B, H, N, D] in C order; bf16 workloads multiply by
+in the order Q, K, V (then dO for the backward), each [B, H, N, D] in C order; bf16 workloads multiply by
 0.5 (exact) and round to bf16 by round-to-nearest-even.  The block-causal
 workload is drawn whole ([B, H, chunks*chunk_len, D]) and split along N.
 """
@@ -112,11 +112,15 @@ class Inputs:
         return h.hexdigest()
 
 
-def generate(w: Workload, seed: Optional[int] = None, with_f64: bool = True) -> Inputs:
+def generate(w: Workload, seed: Optional[int] = None, with_f64: bool = True,
+             names=("q", "k", "v")) -> Inputs:
+    """Draw the named tensors in order from one stream.  The backward's output
+    gradient is drawn as a fourth tensor, "dout", after Q, K, V, which are
+    therefore the same as the forward's."""
     rng = np.random.default_rng(w.seed if seed is None else seed)
     shape = (w.B, w.H, w.N, w.D)
     raw, f64 = {}, {}
-    for name in ("q", "k", "v"):
+    for name in names:
         x = rng.standard_normal(shape, dtype=np.float32)
         if w.scale != 1.0:
             x *= np.float32(w.scale)
