@@ -19,8 +19,9 @@
 // finalize walks each head's partials from the last chunk to the first,
 // storing G_c at every chunk start; bwd_key computes dK and dV.
 //
-// These kernels keep the arithmetic in fp32 on the VALU, with Q/K/V/dO/dQ/dK/dV
-// as fp32 or bf16 (converted on load, RNE on store).
+// The *_vec kernels keep the arithmetic in fp32 on the VALU (fp32 I/O); the
+// bf16 kernels put the contractions on v_mfma_f32_16x16x32_bf16 with the same
+// exact three-part splits of fp32 operands as the forward.
 #pragma once
 
 #include "la_kernels.h"
@@ -283,6 +284,475 @@ __global__ __launch_bounds__(kThreads) void bwd_key_vec(const T* __restrict__ K,
       store4(dV + row, dv);
     }
   }
+}
+
+// ===========================================================================
+// bf16 kernels (MFMA)
+// ===========================================================================
+//
+// Natural layout as in the apply pass: lane l (m = l % 16, g = l / 16) holds
+// features 8g .. 8g+7 of token row m of a 16-token tile, and MFMA output half
+// h row r stands for feature 8(r / 4) + 4h + r % 4, so each lane ends with the
+// outputs of its own 8 features.
+
+// A operand whose rows are the rows r of a 32 x 32 fp32 matrix M (row of MFMA
+// half h = 8(m / 4) + 4h + m % 4) and whose k-slot s of group g is column
+// 8g + s: M[r][8g + s] in three bf16 parts.  Against B = X^T (k = column
+// index, one column per token) it gives (M x)[r] per token.
+__device__ __forceinline__ void load_row_operands(const float* M, int g, int m, bf16x8_t (&a)[2][3]) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = 8 * (m >> 2) + 4 * h + (m & 3);
+    unsigned part[3][4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+      split3_bf16x2(M[r * 32 + 8 * g + 2 * p], M[r * 32 + 8 * g + 2 * p + 1], part[0][p], part[1][p], part[2][p]);
+#pragma unroll
+    for (int k = 0; k < 3; ++k) a[h][k] = as_bf16x8(part[k][0], part[k][1], part[k][2], part[k][3]);
+  }
+}
+
+// A operand whose rows are the columns e of M (M^T, same row mapping) and
+// whose k-slot s of group g is row 8g + s: M[8g + s][e].  Gives (M^T x)[e].
+__device__ __forceinline__ void load_column_operands(const float* M, int g, int m, bf16x8_t (&a)[2][3]) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int e = 8 * (m >> 2) + 4 * h + (m & 3);
+    unsigned part[3][4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+      split3_bf16x2(M[(8 * g + 2 * p) * 32 + e], M[(8 * g + 2 * p + 1) * 32 + e], part[0][p], part[1][p],
+                    part[2][p]);
+#pragma unroll
+    for (int k = 0; k < 3; ++k) a[h][k] = as_bf16x8(part[k][0], part[k][1], part[k][2], part[k][3]);
+  }
+}
+
+// A vector v[32] broadcast to every row: k-slot s of group g holds v[8g + s].
+__device__ __forceinline__ void load_vector_operands(const float* v, int g, bf16x8_t (&a)[3]) {
+  unsigned part[3][4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) split3_bf16x2(v[8 * g + 2 * p], v[8 * g + 2 * p + 1], part[0][p], part[1][p], part[2][p]);
+#pragma unroll
+  for (int k = 0; k < 3; ++k) a[k] = as_bf16x8(part[k][0], part[k][1], part[k][2], part[k][3]);
+}
+
+// Split operand a (three parts) times an exact bf16 operand b, both halves
+__device__ __forceinline__ void mfma3(const bf16x8_t (&a)[2][3], bf16x8_t b, f32x4_t& o0, f32x4_t& o1) {
+  const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+  o0 = mfma16(a[0][0], b, zero4);
+  o0 = mfma16(a[0][1], b, o0);
+  o0 = mfma16(a[0][2], b, o0);
+  o1 = mfma16(a[1][0], b, zero4);
+  o1 = mfma16(a[1][1], b, o1);
+  o1 = mfma16(a[1][2], b, o1);
+}
+
+// Two split operands: the six product terms of weight >= 2^-16
+__device__ __forceinline__ void mfma6(const bf16x8_t (&a)[2][3], const bf16x8_t (&b)[3], f32x4_t& o0,
+                                      f32x4_t& o1) {
+  const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+  f32x4_t* o[2] = {&o0, &o1};
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    f32x4_t x = mfma16(a[h][0], b[0], zero4);
+    x = mfma16(a[h][0], b[1], x);
+    x = mfma16(a[h][1], b[0], x);
+    x = mfma16(a[h][0], b[2], x);
+    x = mfma16(a[h][2], b[0], x);
+    x = mfma16(a[h][1], b[1], x);
+    *o[h] = x;
+  }
+}
+
+__device__ __forceinline__ void unpack8(u32x4_t x, float (&f)[8]) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    f[2 * p] = bf16lo_to_f32(x[p]);
+    f[2 * p + 1] = bf16hi_to_f32(x[p]);
+  }
+}
+
+__device__ __forceinline__ u32x4_t pack8(const float (&f)[8]) {
+  return u32x4_t{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])};
+}
+
+// Rotate the lane's 4 pairs (x[2p], x[2p+1]) by +theta (INVERSE: -theta)
+template <bool INVERSE>
+__device__ __forceinline__ void rotate8(float (&x)[8], f32x4_t c, f32x4_t sn) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const float s = INVERSE ? -sn[p] : sn[p];
+    const float x0 = x[2 * p], x1 = x[2 * p + 1];
+    x[2 * p] = x0 * c[p] - x1 * s;
+    x[2 * p + 1] = x0 * s + x1 * c[p];
+  }
+}
+
+__device__ __forceinline__ void split8(const float (&y)[8], bf16x8_t (&b)[3]) {
+  unsigned part[3][4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) split3_bf16x2(y[2 * p], y[2 * p + 1], part[0][p], part[1][p], part[2][p]);
+#pragma unroll
+  for (int k = 0; k < 3; ++k) b[k] = as_bf16x8(part[k][0], part[k][1], part[k][2], part[k][3]);
+}
+
+// ---------------------------------------------------------------------------
+// Key pass (bf16): per 16-token tile, dV = G^T phi~(K) and
+// dK = [K > 0] (R^T (G V) + Gz); both outputs in the natural layout.
+// Work split as the apply pass: equal flat ranges cut at head and chunk
+// boundaries; each wave takes 64-token chunks (four tiles) with the next
+// chunk's loads in flight.
+// ---------------------------------------------------------------------------
+
+template <bool ROPE>
+struct KeyChunk {
+  u32x4_t k[4], v[4];
+  f32x4_t c[4], sn[4];
+};
+
+template <bool ROPE>
+__device__ __forceinline__ void load_key_chunk(const char* Kh, const char* Vh, int64_t t0, int64_t n_end,
+                                               int lane_off, const float* cos_t, const float* sin_t, int64_t pos0,
+                                               KeyChunk<ROPE>& ch) {
+  const rsrc_t rk = make_rsrc(Kh + t0 * 64, (n_end - t0) * 64);
+  const rsrc_t rv = make_rsrc(Vh + t0 * 64, (n_end - t0) * 64);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    ch.k[u] = load16_nt(rk, lane_off + u * 1024);
+    ch.v[u] = load16_nt(rv, lane_off + u * 1024);
+  }
+  if constexpr (ROPE) {
+    const rsrc_t rc = make_rsrc(cos_t + (pos0 + t0) * 16, (n_end - t0) * 64);
+    const rsrc_t rs = make_rsrc(sin_t + (pos0 + t0) * 16, (n_end - t0) * 64);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      ch.c[u] = load16(rc, lane_off + u * 1024);
+      ch.sn[u] = load16(rs, lane_off + u * 1024);
+    }
+  }
+}
+
+template <bool ROPE>
+__global__ __launch_bounds__(kThreads) void bwd_key_bf16(const u32x4_t* __restrict__ K, const u32x4_t* __restrict__ V,
+                                                         u32x4_t* __restrict__ dK, u32x4_t* __restrict__ dV,
+                                                         StateView grad, int64_t N, int64_t L, int C, int64_t total,
+                                                         int64_t La, const float* __restrict__ cos_t,
+                                                         const float* __restrict__ sin_t, int64_t pos0) {
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int m = lane & 15;
+  const int g = lane >> 4;
+  const int lane_off = m * 64 + g * 16;
+  const int64_t f_begin = (int64_t)blockIdx.x * La;
+  const int64_t f_end = (f_begin + La < total) ? f_begin + La : total;
+
+  for (int64_t f = f_begin; f < f_end;) {
+    const int64_t bh = f / N;
+    const int64_t n_begin = f - bh * N;
+    const int c = (int)(n_begin / L);
+    const int64_t c_end = ((int64_t)c + 1) * L < N ? ((int64_t)c + 1) * L : N;
+    const int64_t n_end = (f_end - bh * N < c_end) ? f_end - bh * N : c_end;
+    f = bh * N + n_end;
+    const char* Kh = reinterpret_cast<const char*>(K + bh * N * 4);
+    const char* Vh = reinterpret_cast<const char*>(V + bh * N * 4);
+    char* dKh = reinterpret_cast<char*>(dK + bh * N * 4);
+    char* dVh = reinterpret_cast<char*>(dV + bh * N * 4);
+
+    int64_t t0 = n_begin + 64 * w;
+    KeyChunk<ROPE> next;
+    if (t0 < n_end) load_key_chunk<ROPE>(Kh, Vh, t0, n_end, lane_off, cos_t, sin_t, pos0, next);
+    const int64_t sc = bh * C + c;
+    const float* G = grad.s_base + sc * grad.s_stride;
+    const float* Gz = grad.z_base + sc * grad.z_stride;
+    bf16x8_t gcol[2][3], grow[2][3];
+    load_column_operands(G, g, m, gcol);  // dV = G^T phi~(K)
+    load_row_operands(G, g, m, grow);     // G V
+    float gz[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) gz[j] = Gz[8 * g + j];
+
+    for (; t0 < n_end; t0 += 256) {
+      const KeyChunk<ROPE> cur = next;
+      if (t0 + 256 < n_end) load_key_chunk<ROPE>(Kh, Vh, t0 + 256, n_end, lane_off, cos_t, sin_t, pos0, next);
+      const rsrc_t rdk = make_rsrc(dKh + t0 * 64, (n_end - t0) * 64);
+      const rsrc_t rdv = make_rsrc(dVh + t0 * 64, (n_end - t0) * 64);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const u32x4_t kr = relu_bf16x8(cur.k[u]);
+        f32x4_t o0, o1;
+        float x[8];
+        if constexpr (!ROPE) {
+          mfma3(gcol, __builtin_bit_cast(bf16x8_t, kr), o0, o1);
+        } else {
+          float y[8];
+          unpack8(kr, y);
+          rotate8<false>(y, cur.c[u], cur.sn[u]);
+          bf16x8_t b[3];
+          split8(y, b);
+          mfma6(gcol, b, o0, o1);
+        }
+        x[0] = o0[0], x[1] = o0[1], x[2] = o0[2], x[3] = o0[3];
+        x[4] = o1[0], x[5] = o1[1], x[6] = o1[2], x[7] = o1[3];
+        store16_nt(rdv, lane_off + u * 1024, pack8(x));
+        mfma3(grow, __builtin_bit_cast(bf16x8_t, cur.v[u]), o0, o1);
+        x[0] = o0[0], x[1] = o0[1], x[2] = o0[2], x[3] = o0[3];
+        x[4] = o1[0], x[5] = o1[1], x[6] = o1[2], x[7] = o1[3];
+        if constexpr (ROPE) rotate8<true>(x, cur.c[u], cur.sn[u]);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          x[2 * p] = (kr[p] & 0xffffu) ? x[2 * p] + gz[2 * p] : 0.f;
+          x[2 * p + 1] = (kr[p] >> 16) ? x[2 * p + 1] + gz[2 * p + 1] : 0.f;
+        }
+        store16_nt(rdk, lane_off + u * 1024, pack8(x));
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Query pass (bf16): dQ and one partial (dS, dz) per workgroup
+// ---------------------------------------------------------------------------
+//
+// Workgroup = item (head, chunk, split) of the state-pass geometry; each wave
+// takes 32-token tiles (two 16-token halves, the next tile's loads in flight).
+// Per half, in the natural layout:
+//   den (A rows = z), num = S^T phi~(Q) (A = S columns), S dO (A = S rows;
+//   dO is exact in bf16, so S dnum = (S dO) / den), dnum = dO / den,
+//   dden = -(dO . num) / den^2 (the lane's 8 features, then the 4 lanes of the
+//   token), dQ, and dz += phi(Q) dden per feature.
+// dS = sum phi~(Q) dnum^T contracts over tokens: dnum (and, under RoPE, the
+// rotated phi~(Q)) go through a wave-private LDS tile into the turned-around
+// layout (lane (n, g): feature n of tokens 4g + i), phi(Q) without RoPE is
+// turned around exactly on the matrix core, and dS accumulates in the
+// state pass's layout.
+constexpr int kTileRow = 36;                  // padded fp32 row of a 32-feature token
+constexpr int kTileFloats = 32 * kTileRow;    // one 32-token tile
+
+template <bool ROPE>
+struct QueryTile {
+  u32x4_t q[2], dout[2];
+  f32x4_t c[2], sn[2];
+};
+
+template <bool ROPE>
+__device__ __forceinline__ void load_query_tile(const char* Qh, const char* Oh, int64_t t0, int64_t n_end,
+                                                int lane_off, const float* cos_t, const float* sin_t, int64_t pos0,
+                                                QueryTile<ROPE>& tl) {
+  const rsrc_t rq = make_rsrc(Qh + t0 * 64, (n_end - t0) * 64);
+  const rsrc_t ro = make_rsrc(Oh + t0 * 64, (n_end - t0) * 64);
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb) {
+    tl.q[tb] = load16_nt(rq, lane_off + tb * 1024);
+    tl.dout[tb] = load16_nt(ro, lane_off + tb * 1024);
+  }
+  if constexpr (ROPE) {
+    const rsrc_t rc = make_rsrc(cos_t + (pos0 + t0) * 16, (n_end - t0) * 64);
+    const rsrc_t rs = make_rsrc(sin_t + (pos0 + t0) * 16, (n_end - t0) * 64);
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      tl.c[tb] = load16(rc, lane_off + tb * 1024);
+      tl.sn[tb] = load16(rs, lane_off + tb * 1024);
+    }
+  }
+}
+
+template <bool ROPE>
+__global__ __launch_bounds__(kThreads) void bwd_query_bf16(const u32x4_t* __restrict__ Q,
+                                                           const u32x4_t* __restrict__ dO, u32x4_t* __restrict__ dQ,
+                                                           StateView fwd, float eps, const float* __restrict__ cos_t,
+                                                           const float* __restrict__ sin_t, int64_t pos0,
+                                                           StateArgs a) {
+  __shared__ float red[4][kStateElems];
+  __shared__ float tiles[4][ROPE ? 2 : 1][kTileFloats];
+
+  int64_t bh, n_begin, n_end;
+  int c, s;
+  state_item(a, bh, c, s, n_begin, n_end);
+  const int64_t N = a.N;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15;  // also the token row m of the natural layout
+  const int g = lane >> 4;
+  const int lane_off = n * 64 + g * 16;
+  const char* Qh = reinterpret_cast<const char*>(Q + bh * N * 4);
+  const char* Oh = reinterpret_cast<const char*>(dO + bh * N * 4);
+  char* dQh = reinterpret_cast<char*>(dQ + bh * N * 4);
+  float* dn_tile = tiles[w][0];
+  float* pq_tile = tiles[w][ROPE ? 1 : 0];
+
+  int64_t t0 = n_begin + 32 * w;
+  QueryTile<ROPE> next;
+  if (t0 < n_end) load_query_tile<ROPE>(Qh, Oh, t0, n_end, lane_off, cos_t, sin_t, pos0, next);
+
+  const int64_t sc = bh * a.C + c;
+  const float* S = fwd.s_base + sc * fwd.s_stride;
+  const float* Z = fwd.z_base + sc * fwd.z_stride;
+  bf16x8_t scol[2][3], srow[2][3], zrow[3];
+  load_column_operands(S, g, n, scol);  // num = S^T phi~(Q)
+  load_row_operands(S, g, n, srow);     // S dO
+  load_vector_operands(Z, g, zrow);     // den
+  float zf[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) zf[j] = Z[8 * g + j];
+  const bf16x8_t sel[2] = {select_operand(g, n, 0), select_operand(g, n, 1)};
+
+  f32x4_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) acc[i][0] = acc[i][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float dzacc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) dzacc[j] = 0.f;
+
+  for (; t0 < n_end; t0 += 128) {
+    const QueryTile<ROPE> cur = next;
+    if (t0 + 128 < n_end) load_query_tile<ROPE>(Qh, Oh, t0 + 128, n_end, lane_off, cos_t, sin_t, pos0, next);
+    const rsrc_t rdq = make_rsrc(dQh + t0 * 64, (n_end - t0) * 64);
+    bf16x8_t bq[2];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      const u32x4_t qr = relu_bf16x8(cur.q[tb]);
+      bq[tb] = __builtin_bit_cast(bf16x8_t, qr);
+      const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+      f32x4_t dacc = mfma16(zrow[0], bq[tb], zero4);
+      dacc = mfma16(zrow[1], bq[tb], dacc);
+      dacc = mfma16(zrow[2], bq[tb], dacc);
+      const float rden = 1.f / (dacc[0] + eps);
+      float pq[8], y[8];
+      unpack8(qr, pq);
+      f32x4_t n0, n1;
+      if constexpr (!ROPE) {
+        mfma3(scol, bq[tb], n0, n1);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) y[j] = pq[j];
+        rotate8<false>(y, cur.c[tb], cur.sn[tb]);
+        bf16x8_t br[3];
+        split8(y, br);
+        mfma6(scol, br, n0, n1);
+      }
+      f32x4_t s0, s1;
+      mfma3(srow, __builtin_bit_cast(bf16x8_t, cur.dout[tb]), s0, s1);
+      float gd[8], num[8], dr[8];
+      unpack8(cur.dout[tb], gd);
+      num[0] = n0[0], num[1] = n0[1], num[2] = n0[2], num[3] = n0[3];
+      num[4] = n1[0], num[5] = n1[1], num[6] = n1[2], num[7] = n1[3];
+      dr[0] = s0[0], dr[1] = s0[1], dr[2] = s0[2], dr[3] = s0[3];
+      dr[4] = s1[0], dr[5] = s1[1], dr[6] = s1[2], dr[7] = s1[3];
+      float dot = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dot += gd[j] * num[j];
+      dot += __shfl_xor(dot, 16);
+      dot += __shfl_xor(dot, 32);
+      const float dden = -dot * rden * rden;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dr[j] *= rden;
+      if constexpr (ROPE) rotate8<true>(dr, cur.c[tb], cur.sn[tb]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        dr[j] = pq[j] > 0.f ? dr[j] + zf[j] * dden : 0.f;
+        dzacc[j] += pq[j] * dden;
+      }
+      store16_nt(rdq, lane_off + tb * 1024, pack8(dr));
+      // dnum (and phi~(Q)) of token row 16tb + n, features 8g .. 8g+7
+      float* rowp = dn_tile + (16 * tb + n) * kTileRow + 8 * g;
+      *reinterpret_cast<f32x4_t*>(rowp) = f32x4_t{gd[0] * rden, gd[1] * rden, gd[2] * rden, gd[3] * rden};
+      *reinterpret_cast<f32x4_t*>(rowp + 4) = f32x4_t{gd[4] * rden, gd[5] * rden, gd[6] * rden, gd[7] * rden};
+      if constexpr (ROPE) {
+        float* rowq = pq_tile + (16 * tb + n) * kTileRow + 8 * g;
+        *reinterpret_cast<f32x4_t*>(rowq) = f32x4_t{y[0], y[1], y[2], y[3]};
+        *reinterpret_cast<f32x4_t*>(rowq + 4) = f32x4_t{y[4], y[5], y[6], y[7]};
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // turned-around operands: lane (n, g), k-slots (tb, i) = tokens 16tb + 4g + i
+    bf16x8_t bd[2][3];  // dnum, B operand for value half fh' (columns n)
+#pragma unroll
+    for (int fh = 0; fh < 2; ++fh) {
+      unsigned part[3][4];
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        const float* col = dn_tile + (16 * tb + 4 * g) * kTileRow + 16 * fh + n;
+        split3_bf16x2(col[0], col[kTileRow], part[0][2 * tb], part[1][2 * tb], part[2][2 * tb]);
+        split3_bf16x2(col[2 * kTileRow], col[3 * kTileRow], part[0][2 * tb + 1], part[1][2 * tb + 1],
+                      part[2][2 * tb + 1]);
+      }
+#pragma unroll
+      for (int k = 0; k < 3; ++k) bd[fh][k] = as_bf16x8(part[k][0], part[k][1], part[k][2], part[k][3]);
+    }
+    if constexpr (!ROPE) {
+#pragma unroll
+      for (int fh = 0; fh < 2; ++fh) {
+        const bf16x8_t aq = pack_turned(turn(bq[0], sel[fh]), turn(bq[1], sel[fh]));
+#pragma unroll
+        for (int fv = 0; fv < 2; ++fv) {
+          acc[fh][fv] = mfma16(aq, bd[fv][0], acc[fh][fv]);
+          acc[fh][fv] = mfma16(aq, bd[fv][1], acc[fh][fv]);
+          acc[fh][fv] = mfma16(aq, bd[fv][2], acc[fh][fv]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int fh = 0; fh < 2; ++fh) {
+        unsigned part[3][4];
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+          const float* col = pq_tile + (16 * tb + 4 * g) * kTileRow + 16 * fh + n;
+          split3_bf16x2(col[0], col[kTileRow], part[0][2 * tb], part[1][2 * tb], part[2][2 * tb]);
+          split3_bf16x2(col[2 * kTileRow], col[3 * kTileRow], part[0][2 * tb + 1], part[1][2 * tb + 1],
+                        part[2][2 * tb + 1]);
+        }
+        bf16x8_t aq[3];
+#pragma unroll
+        for (int k = 0; k < 3; ++k) aq[k] = as_bf16x8(part[k][0], part[k][1], part[k][2], part[k][3]);
+#pragma unroll
+        for (int fv = 0; fv < 2; ++fv) {
+          f32x4_t x = acc[fh][fv];
+          x = mfma16(aq[0], bd[fv][0], x);
+          x = mfma16(aq[0], bd[fv][1], x);
+          x = mfma16(aq[1], bd[fv][0], x);
+          x = mfma16(aq[0], bd[fv][2], x);
+          x = mfma16(aq[2], bd[fv][0], x);
+          x = mfma16(aq[1], bd[fv][1], x);
+          acc[fh][fv] = x;
+        }
+      }
+    }
+  }
+
+  // dz: sum the 16 lanes of each group (token rows), feature 8g + j
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float x = dzacc[j];
+    x += __shfl_xor(x, 1);
+    x += __shfl_xor(x, 2);
+    x += __shfl_xor(x, 4);
+    x += __shfl_xor(x, 8);
+    dzacc[j] = x;
+  }
+  // D lane (n, g): rows 4g + i -> key feature 16fh + 4g + i, column n -> value feature 16fh' + n
+  float* rw = red[w];
+#pragma unroll
+  for (int fh = 0; fh < 2; ++fh) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d = 16 * fh + 4 * g + i;
+      rw[d * 32 + n] = acc[fh][0][i];
+      rw[d * 32 + 16 + n] = acc[fh][1][i];
+    }
+  }
+  if (n == 0) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) rw[1024 + 8 * g + j] = dzacc[j];
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < kStateElems; idx += kThreads)
+    red[0][idx] = (red[0][idx] + red[1][idx]) + (red[2][idx] + red[3][idx]);
+  __syncthreads();
+  write_partial(red[0], bh, c, s, a);
 }
 
 }  // namespace la

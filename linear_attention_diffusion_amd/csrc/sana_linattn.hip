@@ -281,38 +281,61 @@ int attend(const void* q, const void* k, const void* v, void* o, const float* kv
 // the carried state) and the key pass (dK, dV).  The workspace layout is the
 // forward's: the query pass reuses the partials, the reverse finalize
 // overwrites the chunk states with G_c once the query pass has read them.
-template <typename T>
 void launch_backward(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk, void* dv,
-                     float eps, const Geometry& g, const sana_rope* rope, const la::StateArgs& fwd,
+                     int dtype, float eps, const Geometry& g, const sana_rope* rope, const la::StateArgs& fwd,
                      const la::StateArgs& bwd, hipStream_t st) {
   const float* ct = rope ? rope->cos : nullptr;
   const float* sn = rope ? rope->sin : nullptr;
   const int64_t pos0 = rope ? rope->pos_offset : 0;
-  const T* Q = static_cast<const T*>(q);
-  const T* K = static_cast<const T*>(k);
-  const T* V = static_cast<const T*>(v);
-  const T* dO = static_cast<const T*>(dout);
-  T* dQ = static_cast<T*>(dq);
-  T* dK = static_cast<T*>(dk);
-  T* dV = static_cast<T*>(dv);
   const la::StateView view = ws_view(fwd);
   const dim3 block(la::kThreads);
   const dim3 qgrid((unsigned)(g.BH * g.C * g.Pc));
-  if (rope)
-    la::bwd_query_vec<T, true><<<qgrid, block, 0, st>>>(Q, dO, dQ, view, eps, ct, sn, pos0, bwd);
-  else
-    la::bwd_query_vec<T, false><<<qgrid, block, 0, st>>>(Q, dO, dQ, view, eps, ct, sn, pos0, bwd);
+  if (dtype == SANA_DT_BF16) {
+    const auto* Q = static_cast<const la::u32x4_t*>(q);
+    const auto* dO = static_cast<const la::u32x4_t*>(dout);
+    auto* dQ = static_cast<la::u32x4_t*>(dq);
+    if (rope)
+      la::bwd_query_bf16<true><<<qgrid, block, 0, st>>>(Q, dO, dQ, view, eps, ct, sn, pos0, bwd);
+    else
+      la::bwd_query_bf16<false><<<qgrid, block, 0, st>>>(Q, dO, dQ, view, eps, ct, sn, pos0, bwd);
+  } else {
+    const auto* Q = static_cast<const float*>(q);
+    const auto* dO = static_cast<const float*>(dout);
+    auto* dQ = static_cast<float*>(dq);
+    if (rope)
+      la::bwd_query_vec<float, true><<<qgrid, block, 0, st>>>(Q, dO, dQ, view, eps, ct, sn, pos0, bwd);
+    else
+      la::bwd_query_vec<float, false><<<qgrid, block, 0, st>>>(Q, dO, dQ, view, eps, ct, sn, pos0, bwd);
+  }
   if (g.C * g.Pc > 1) {
     const int64_t n_elems = g.BH * la::kStateElems;
     la::state_finalize_reverse<<<dim3((unsigned)ceil_div(n_elems, la::kThreads)), block, 0, st>>>(bwd, n_elems);
   }
-  const dim3 kgrid((unsigned)(g.BH * g.C * g.T));
-  if (rope)
-    la::bwd_key_vec<T, true><<<kgrid, block, 0, st>>>(K, V, dK, dV, view, g.N, g.L, (int)g.C, (int)g.T, g.Lt, ct,
-                                                       sn, pos0);
-  else
-    la::bwd_key_vec<T, false><<<kgrid, block, 0, st>>>(K, V, dK, dV, view, g.N, g.L, (int)g.C, (int)g.T, g.Lt, ct,
+  if (dtype == SANA_DT_BF16) {
+    const dim3 kgrid((unsigned)g.Ga);
+    const auto* K = static_cast<const la::u32x4_t*>(k);
+    const auto* V = static_cast<const la::u32x4_t*>(v);
+    auto* dK = static_cast<la::u32x4_t*>(dk);
+    auto* dV = static_cast<la::u32x4_t*>(dv);
+    if (rope)
+      la::bwd_key_bf16<true><<<kgrid, block, 0, st>>>(K, V, dK, dV, view, g.N, g.L, (int)g.C, g.BH * g.N, g.La, ct,
                                                         sn, pos0);
+    else
+      la::bwd_key_bf16<false><<<kgrid, block, 0, st>>>(K, V, dK, dV, view, g.N, g.L, (int)g.C, g.BH * g.N, g.La,
+                                                         ct, sn, pos0);
+  } else {
+    const dim3 kgrid((unsigned)(g.BH * g.C * g.T));
+    const auto* K = static_cast<const float*>(k);
+    const auto* V = static_cast<const float*>(v);
+    auto* dK = static_cast<float*>(dk);
+    auto* dV = static_cast<float*>(dv);
+    if (rope)
+      la::bwd_key_vec<float, true><<<kgrid, block, 0, st>>>(K, V, dK, dV, view, g.N, g.L, (int)g.C, (int)g.T, g.Lt,
+                                                              ct, sn, pos0);
+    else
+      la::bwd_key_vec<float, false><<<kgrid, block, 0, st>>>(K, V, dK, dV, view, g.N, g.L, (int)g.C, (int)g.T,
+                                                               g.Lt, ct, sn, pos0);
+  }
 }
 
 bool state_pair_ok(const float* s, const float* z) {
@@ -369,10 +392,7 @@ int backward(const void* q, const void* k, const void* v, const void* dout, void
   const la::StateArgs fwd = state_args(ws, g, kv_in, ksum_in, nullptr, nullptr);
   const la::StateArgs bwd = state_args(ws, g, dkv_out, dksum_out, dkv_in, dksum_in);
   launch_state(k, v, dtype, g, rope, fwd, st);
-  if (dtype == SANA_DT_BF16)
-    launch_backward<__bf16>(q, k, v, dout, dq, dk, dv, eps, g, rope, fwd, bwd, st);
-  else
-    launch_backward<float>(q, k, v, dout, dq, dk, dv, eps, g, rope, fwd, bwd, st);
+  launch_backward(q, k, v, dout, dq, dk, dv, dtype, eps, g, rope, fwd, bwd, st);
   return launch_status();
 }
 
