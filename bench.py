@@ -60,7 +60,8 @@ def algorithmic_bytes(w):
 
 
 def stored_traffic(name):
-    """HBM bytes per launch of the dominant kernel, from committed rocprofv3
+    """HBM bytes per launch of the dominant kernel (of the forward, or of the
+    backward for names "backward_<workload>"), from committed rocprofv3
     counter runs (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter
     reads for a copy kernel of known size), if they were taken on the current
     kernel sources; else None."""
@@ -188,6 +189,29 @@ def backward_bench(w, args, dev, stream):
     ms = e0.elapsed_time(e1) / args.steps
     elem = 2 if w.dtype == "bf16" else 4
     alg_bytes = w.token_heads * 9 * w.D * elem
+
+    # roofline of the dominant kernel: the key pass (dK, dV from a state
+    # gradient), launched alone through sana_linattn_state_update_backward on
+    # the whole sequence, timed with one event pair on the launch stream
+    g = torch.Generator(device="cpu").manual_seed(5)
+    dkv = torch.randn(w.B, w.H, 32, 32, generator=g).to(dev)
+    dksum = torch.randn(w.B, w.H, 32, generator=g).to(dev)
+    key_calls = [(P(s["k"].data_ptr()), P(s["v"].data_ptr()), P(dkv.data_ptr()), P(dksum.data_ptr()),
+                  P(s["dk"].data_ptr()), P(s["dv"].data_ptr()), w.B, w.H, w.N, w.D, dt, rope_ref, st_ptr)
+                 for s in sets]
+    for i in range(args.warmup):
+        L.sana_linattn_state_update_backward(*key_calls[i % n_sets])
+    torch.cuda.synchronize()
+    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    k0.record(stream)
+    for i in range(args.steps):
+        rc = L.sana_linattn_state_update_backward(*key_calls[i % n_sets])
+        if rc:
+            raise la.SanaError(rc)
+    k1.record(stream)
+    torch.cuda.synchronize()
+    key_ms = k0.elapsed_time(k1) / args.steps
+    key_bytes = w.token_heads * 4 * w.D * elem + w.B * w.H * (32 * 32 + 32) * 4
     # fp32 multiply-adds per token-head of the backward: the forward state
     # recompute (S, z: 32*32 + 32), the query pass (num, den, S dnum, dS, dz:
     # 3*32*32 + 2*32) and the key pass (G V, G^T phi~(K): 2*32*32), 2 flop each
@@ -207,6 +231,18 @@ def backward_bench(w, args, dev, stream):
         "data": "synthetic: seeded i.i.d. N(0,1)x0.5 bf16 tensors at the workload's latent shape (dO drawn after Q, K, V)",
         "config": {"workload": w.name, "pass": "backward", "B": w.B, "H": w.H, "N": w.N, "D": w.D,
                    "mode": w.mode, "chunk": chunk, "grid": w.grid, "input_sets_cycled": n_sets},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "bwd_key_bf16" if w.dtype == "bf16" else "bwd_key_vec",
+            "achieved": key_bytes / (key_ms / 1e3) / 1e9,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": key_bytes / (key_ms / 1e3) / 1e9 / HBM_PEAK_GBPS,
+            "traffic": stored_traffic("backward_" + w.name),
+            "algorithmic_bytes_per_launch": key_bytes,
+            "avg_launch_ms": key_ms,
+            "tokens_per_launch": w.token_heads,
+        },
         "call": {"entry_point": "sana_linattn_backward",
                  "kernels": "state pass + finalize + query pass + reverse finalize + key pass",
                  "avg_ms": ms, "algorithmic_bytes": alg_bytes,

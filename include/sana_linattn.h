@@ -201,6 +201,21 @@ int sana_linattn_backward(const void* q, const void* k, const void* v, const voi
                           int B, int H, int64_t N, int64_t chunk, int D, int dtype, float eps,
                           const sana_rope* rope, void* ws, size_t ws_bytes, void* hip_stream);
 
+/* Backward of sana_linattn_state_update (the key side of every backward):
+ * given the gradient (dkv, dksum) reaching an updated state, the gradients of
+ * the keys and values that were added into it.  With
+ * L = <dkv, S> + dksum . z, S = sum_j phi~(K_j)^T V_j, z = sum_j phi(K_j)
+ * ("SANA-Video" paper notes 2.2-2.3):
+ *   dk_j = [K_j > 0] (R_j^T dkv V_j + dksum),   dv_j = dkv^T phi~(K_j)
+ * (R_j: the RoPE rotation at position pos_offset + j, identity without rope;
+ * the state's own gradient passes through unchanged and is not written).
+ * k, v: inputs [B][H][N][D]; dkv [B][H][D][D], dksum [B][H][D]: fp32, read
+ * only; dk, dv: outputs of k's shape and dtype, overlapping nothing.  No
+ * workspace.  N = 0 writes nothing. */
+int sana_linattn_state_update_backward(const void* k, const void* v, const float* dkv, const float* dksum,
+                                       void* dk, void* dv, int B, int H, int64_t N, int D, int dtype,
+                                       const sana_rope* rope, void* hip_stream);
+
 /* Workspace bytes for sana_linattn_backward with these sizes (0 when B*H*N == 0
  * or the sizes are invalid).  Pure host function. */
 size_t sana_linattn_backward_workspace_bytes(int B, int H, int64_t N, int64_t chunk, int D, int dtype,

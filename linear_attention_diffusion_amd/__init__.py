@@ -3,6 +3,7 @@
 Entry points (same names as the C ABI in include/sana_linattn.h):
   sana_linattn_forward, sana_linattn_state_update, sana_linattn_block_forward,
   sana_linattn_block_causal, sana_linattn_apply, sana_linattn_backward,
+  sana_linattn_state_update_backward,
   rope3d_table / rope3d_device (host builder of the 3D RoPE tables).
 """
 
@@ -29,6 +30,7 @@ from .binding import (  # noqa: F401
     sana_linattn_block_forward,
     sana_linattn_forward,
     sana_linattn_state_update,
+    sana_linattn_state_update_backward,
     sana_linattn_status_string,
     workspace_bytes,
 )

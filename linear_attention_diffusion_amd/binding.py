@@ -26,6 +26,7 @@ EXPORTED = (
     "sana_linattn_apply",
     "sana_linattn_backward",
     "sana_linattn_backward_workspace_bytes",
+    "sana_linattn_state_update_backward",
     "sana_linattn_rope3d_table",
     "sana_linattn_status_string",
 )
@@ -71,6 +72,8 @@ def lib():
     L.sana_linattn_backward.restype = i32
     L.sana_linattn_backward_workspace_bytes.argtypes = [i32, i32, i64, i64, i32, i32, i32]
     L.sana_linattn_backward_workspace_bytes.restype = sz
+    L.sana_linattn_state_update_backward.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, rp, vp]
+    L.sana_linattn_state_update_backward.restype = i32
     L.sana_linattn_rope3d_table.argtypes = [i32, i32, i32, i32, i32, i32, i32, ctypes.c_double, vp, vp]
     L.sana_linattn_rope3d_table.restype = i32
     L.sana_linattn_status_string.argtypes = [i32]
@@ -317,6 +320,29 @@ def sana_linattn_backward(q, k, v, dout, chunk=None, dq=None, dk=None, dv=None, 
                                        _ptr(dkv_in), _ptr(dksum_in), B, H, N, L, D, dt, float(eps),
                                        _rope_arg(rope), _ptr(workspace), workspace.numel(),
                                        _stream(stream, q.device)))
+    return tuple(outs)
+
+
+def sana_linattn_state_update_backward(k, v, dkv, dksum, dk=None, dv=None, rope=None, stream=None):
+    """dK, dV of L = <dkv, S> + dksum . z for the state S, z that k, v add;
+    returns (dk, dv)."""
+    torch = _torch()
+    B, H, N, D = _shape4(k, "k")
+    if _shape4(v, "v") != (B, H, N, D) or v.dtype != k.dtype:
+        raise ValueError("k and v must have the same shape and dtype")
+    outs = []
+    for t, name in ((dk, "dk"), (dv, "dv")):
+        if t is None:
+            t = torch.empty_like(k)
+        elif _shape4(t, name) != (B, H, N, D) or t.dtype != k.dtype:
+            raise ValueError(f"{name} must match k in shape and dtype")
+        outs.append(t)
+    for t, shape in ((dkv, (B, H, D, D)), (dksum, (B, H, D))):
+        if tuple(t.shape) != shape or t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("state gradients must be contiguous float32 [B, H, D, D] / [B, H, D]")
+    _check(lib().sana_linattn_state_update_backward(_ptr(k), _ptr(v), _ptr(dkv), _ptr(dksum), _ptr(outs[0]),
+                                                    _ptr(outs[1]), B, H, N, D, _dtype_code(k), _rope_arg(rope),
+                                                    _stream(stream, k.device)))
     return tuple(outs)
 
 

@@ -276,6 +276,40 @@ int attend(const void* q, const void* k, const void* v, void* o, const float* kv
   return launch_status();
 }
 
+// Key pass of the backward: dK, dV from the state gradient G_c of every chunk.
+void launch_key_pass(const void* k, const void* v, void* dk, void* dv, int dtype, const Geometry& g,
+                     const sana_rope* rope, const la::StateView& view, hipStream_t st) {
+  const float* ct = rope ? rope->cos : nullptr;
+  const float* sn = rope ? rope->sin : nullptr;
+  const int64_t pos0 = rope ? rope->pos_offset : 0;
+  const dim3 block(la::kThreads);
+  if (dtype == SANA_DT_BF16) {
+    const dim3 kgrid((unsigned)g.Ga);
+    const auto* K = static_cast<const la::u32x4_t*>(k);
+    const auto* V = static_cast<const la::u32x4_t*>(v);
+    auto* dK = static_cast<la::u32x4_t*>(dk);
+    auto* dV = static_cast<la::u32x4_t*>(dv);
+    if (rope)
+      la::bwd_key_bf16<true><<<kgrid, block, 0, st>>>(K, V, dK, dV, view, g.N, g.L, (int)g.C, g.BH * g.N, g.La, ct,
+                                                        sn, pos0);
+    else
+      la::bwd_key_bf16<false><<<kgrid, block, 0, st>>>(K, V, dK, dV, view, g.N, g.L, (int)g.C, g.BH * g.N, g.La,
+                                                         ct, sn, pos0);
+  } else {
+    const dim3 kgrid((unsigned)(g.BH * g.C * g.T));
+    const auto* K = static_cast<const float*>(k);
+    const auto* V = static_cast<const float*>(v);
+    auto* dK = static_cast<float*>(dk);
+    auto* dV = static_cast<float*>(dv);
+    if (rope)
+      la::bwd_key_vec<float, true><<<kgrid, block, 0, st>>>(K, V, dK, dV, view, g.N, g.L, (int)g.C, (int)g.T, g.Lt,
+                                                              ct, sn, pos0);
+    else
+      la::bwd_key_vec<float, false><<<kgrid, block, 0, st>>>(K, V, dK, dV, view, g.N, g.L, (int)g.C, (int)g.T,
+                                                               g.Lt, ct, sn, pos0);
+  }
+}
+
 // Backward: recompute the chunk states (state pass + finalize), then the query
 // pass (dQ, partial dS/dz), the reverse finalize (suffix sums G_c, gradient of
 // the carried state) and the key pass (dK, dV).  The workspace layout is the
@@ -311,31 +345,7 @@ void launch_backward(const void* q, const void* k, const void* v, const void* do
     const int64_t n_elems = g.BH * la::kStateElems;
     la::state_finalize_reverse<<<dim3((unsigned)ceil_div(n_elems, la::kThreads)), block, 0, st>>>(bwd, n_elems);
   }
-  if (dtype == SANA_DT_BF16) {
-    const dim3 kgrid((unsigned)g.Ga);
-    const auto* K = static_cast<const la::u32x4_t*>(k);
-    const auto* V = static_cast<const la::u32x4_t*>(v);
-    auto* dK = static_cast<la::u32x4_t*>(dk);
-    auto* dV = static_cast<la::u32x4_t*>(dv);
-    if (rope)
-      la::bwd_key_bf16<true><<<kgrid, block, 0, st>>>(K, V, dK, dV, view, g.N, g.L, (int)g.C, g.BH * g.N, g.La, ct,
-                                                        sn, pos0);
-    else
-      la::bwd_key_bf16<false><<<kgrid, block, 0, st>>>(K, V, dK, dV, view, g.N, g.L, (int)g.C, g.BH * g.N, g.La,
-                                                         ct, sn, pos0);
-  } else {
-    const dim3 kgrid((unsigned)(g.BH * g.C * g.T));
-    const auto* K = static_cast<const float*>(k);
-    const auto* V = static_cast<const float*>(v);
-    auto* dK = static_cast<float*>(dk);
-    auto* dV = static_cast<float*>(dv);
-    if (rope)
-      la::bwd_key_vec<float, true><<<kgrid, block, 0, st>>>(K, V, dK, dV, view, g.N, g.L, (int)g.C, (int)g.T, g.Lt,
-                                                              ct, sn, pos0);
-    else
-      la::bwd_key_vec<float, false><<<kgrid, block, 0, st>>>(K, V, dK, dV, view, g.N, g.L, (int)g.C, (int)g.T,
-                                                               g.Lt, ct, sn, pos0);
-  }
+  launch_key_pass(k, v, dk, dv, dtype, g, rope, view, st);
 }
 
 bool state_pair_ok(const float* s, const float* z) {
@@ -450,6 +460,30 @@ int sana_linattn_backward(const void* q, const void* k, const void* v, const voi
                           size_t ws_bytes, void* hip_stream) {
   return backward(q, k, v, dout, dq, dk, dv, kv_in, ksum_in, dkv_out, dksum_out, dkv_in, dksum_in, B, H, N, chunk,
                   D, dtype, eps, rope, ws, ws_bytes, hip_stream);
+}
+
+int sana_linattn_state_update_backward(const void* k, const void* v, const float* dkv, const float* dksum,
+                                       void* dk, void* dv, int B, int H, int64_t N, int D, int dtype,
+                                       const sana_rope* rope, void* hip_stream) {
+  int64_t bh = 0, elems = 0;
+  int rc = check_sizes(B, H, N, D, dtype, &bh, &elems);
+  if (rc != SANA_OK) return rc;
+  if (elems == 0) return SANA_OK;
+  if (check_tensor(k) || check_tensor(v) || check_tensor(dk) || check_tensor(dv)) return SANA_ERR_INVALID;
+  if (!dkv || !dksum || !aligned(dkv, 4) || !aligned(dksum, 4)) return SANA_ERR_INVALID;
+  const size_t bytes = (size_t)elems * elem_size(dtype);
+  const size_t kv_bytes = (size_t)bh * 1024 * sizeof(float), ks_bytes = (size_t)bh * 32 * sizeof(float);
+  const void* ins[4] = {k, v, dkv, dksum};
+  const size_t in_bytes[4] = {bytes, bytes, kv_bytes, ks_bytes};
+  for (int i = 0; i < 4; ++i)
+    if (overlaps(dk, bytes, ins[i], in_bytes[i]) || overlaps(dv, bytes, ins[i], in_bytes[i])) return SANA_ERR_INVALID;
+  if (overlaps(dk, bytes, dv, bytes)) return SANA_ERR_INVALID;
+  if ((rc = check_rope(rope, N)) != SANA_OK) return rc;
+  const Geometry g = make_geometry(bh, N, N, rope != nullptr);
+  if (!grids_fit(g)) return SANA_ERR_INVALID;
+  launch_key_pass(k, v, dk, dv, dtype, g, rope, la::StateView{dkv, dksum, 1024, 32},
+                  static_cast<hipStream_t>(hip_stream));
+  return launch_status();
 }
 
 int sana_linattn_state_update(const void* k, const void* v, float* kv_state, float* ksum_state, int B, int H,

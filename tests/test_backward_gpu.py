@@ -177,3 +177,25 @@ def test_backward_zero_rows_and_empty():
     empty = q[:, :, :0].contiguous()
     outs = la.sana_linattn_backward(empty, empty, empty, empty, eps=w.eps)
     assert all(t.numel() == 0 for t in outs)
+
+
+@pytest.mark.parametrize("rope", [False, True])
+def test_state_update_backward(rope):
+    """dK, dV of <dkv, S> + dksum . z alone (the key pass) against the oracle's
+    backward with a zero output gradient and that state gradient."""
+    torch = torch_mod()
+    w = WORKLOADS["video720p_rope3d"] if rope else reduced(WORKLOADS["sana16b_4096px"], H=12, N=5000)
+    print(f"case state_update_backward rope={rope}: H={w.H} N={w.N}", flush=True)
+    x = generate(w)
+    k, v = (to_dev(x.raw[n], w.dtype) for n in ("k", "v"))
+    rng = np.random.default_rng(77)
+    dS = rng.standard_normal((w.B, w.H, 32, 32)).astype(np.float32)
+    dz = rng.standard_normal((w.B, w.H, 32)).astype(np.float32)
+    dk, dv = la.sana_linattn_state_update_backward(k, v, torch.from_numpy(dS).to(device()),
+                                                   torch.from_numpy(dz).to(device()),
+                                                   rope=rope_for(w) if rope else None)
+    f = x.f64
+    ang = oracle.rope3d_angles(*w.grid) if rope else None
+    ref = oracle.backward(f["q"], f["k"], f["v"], np.zeros_like(f["q"]), w.eps, angles=ang, dS_out=dS, dz_out=dz)
+    check(to_np(dk), ref[1], w.dtype, "state_update_backward dk")
+    check(to_np(dv), ref[2], w.dtype, "state_update_backward dv")
