@@ -109,6 +109,27 @@ def cpu_baseline(w, x, budget_s):
                       f"(B={w.B}) of this workload, {el:.1f} s on the host"}
 
 
+def step_percentiles(step, steps, first, stream):
+    """p10/p50/p90 of single steps, each between its own pair of events, in a
+    separate loop after the timed region (per-step events add their own marker
+    packets, so the headline time comes from the single event pair)."""
+    import torch
+    times = []
+    for i in range(steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step(first + i)
+        b.record(stream)
+        times.append((a, b))
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in times)
+
+    def pct(p):
+        return ms[min(len(ms) - 1, int(round(p / 100.0 * (len(ms) - 1))))]
+
+    return {"p10": pct(10), "p50": pct(50), "p90": pct(90)}
+
+
 def copy_probe(steps, warmup, nbytes=2 ** 30):
     """A plain copy kernel of known size: reads and writes `nbytes` per launch."""
     import torch
@@ -187,6 +208,7 @@ def backward_bench(w, args, dev, stream):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     ms = e0.elapsed_time(e1) / args.steps
+    step_pct = step_percentiles(step, args.steps, args.warmup + args.steps, stream)
     elem = 2 if w.dtype == "bf16" else 4
     alg_bytes = w.token_heads * 9 * w.D * elem
 
@@ -249,6 +271,7 @@ def backward_bench(w, args, dev, stream):
                  "achieved_gbps": alg_bytes / (ms / 1e3) / 1e9,
                  "frac_of_hbm_peak": alg_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS,
                  "flops": flops, "achieved_tflops": flops / (ms / 1e3) / 1e12},
+        "step_ms_percentiles": step_pct,
         "wall_s_timed_region": wall,
         "kernel_source_hash": kernel_source_hash(),
     }
@@ -396,6 +419,7 @@ def main():
 
     ms_per_step = total_ms / args.steps
     value = w.token_heads * args.steps / (total_ms / 1e3)
+    step_pct = step_percentiles(step, args.steps, args.warmup, stream)
     alg_bytes = algorithmic_bytes(w)
     launches = w.n_chunks if (w.mode == "block" and args.block_mode == "chunks") else 1
     call_ms = ms_per_step / launches
@@ -471,6 +495,7 @@ def main():
             "frac_of_peak": (alg_bytes / launches) / (call_ms / 1e3) / 1e9 / HBM_PEAK_GBPS,
         },
         "hbm_gbps_step": alg_bytes / (ms_per_step / 1e3) / 1e9,
+        "step_ms_percentiles": step_pct,
         "wall_s_timed_region": wall,
         "input_sha256": x.sha256()[:16],
         "kernel_source_hash": kernel_source_hash(),

@@ -352,3 +352,17 @@ def test_block_causal_sequence_rope_and_chunk_loop_agree():
     # one chunk covering everything is the plain forward
     o_one, _, _ = _run_sequence(x, 10 ** 6)
     assert np.array_equal(o_one, run_forward(x))
+
+
+# --------------------------------------------------------------------------
+# geometry extremes: one very long head (the split cap: 64 partials per head),
+# and many short heads (one workgroup per head, no finalize)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("B,H,N", [(1, 1, 1 << 20), (64, 64, 64), (2, 3, 300001)])
+def test_geometry_extremes(B, H, N):
+    w = reduced(WORKLOADS["sana16b_4096px"], B=B, H=H, N=N)
+    print(f"case extremes: B={B} H={H} N={N}", flush=True)
+    x = generate(w)
+    o = run_forward(x)
+    check(o, oracle.linattn(x.f64["q"], x.f64["k"], x.f64["v"], w.eps), "bf16", f"extremes B{B}H{H}N{N}")
