@@ -292,6 +292,10 @@ def main():
     ap.add_argument("--pass", dest="which", choices=["forward", "backward"], default="forward",
                     help="forward (the default; the headline metric) or backward: one sana_linattn_backward "
                          "call per step (dQ, dK, dV; whole sequence in block-causal chunks for that workload)")
+    ap.add_argument("--layout", choices=["bhnd", "packed"], default="bhnd",
+                    help="forward: bhnd = contiguous [B, H, N, D] (the default); packed = Q, K, V read as strided "
+                         "views of one [B, N, 3, H, D] projection-style buffer and O written to [B, N, H, D] "
+                         "(sana_linattn_forward_strided; non-causal and RoPE workloads)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="time a plain 1 GiB device-to-device copy instead (HBM reference and counter scale)")
     args = ap.parse_args()
@@ -328,8 +332,20 @@ def main():
     q0, k0, v0 = (to_dev(x.raw[n]) for n in ("q", "k", "v"))
     set_bytes = 4 * q0.numel() * q0.element_size()
     n_sets = max(2, min(16, math.ceil(1.5 * 2 ** 30 / set_bytes) + 1))
+    packed = args.layout == "packed"
+    if packed and w.mode == "block":
+        raise SystemExit("--layout packed covers the non-causal and RoPE workloads")
     sets = []
     for i in range(n_sets):
+        if packed:
+            # one [B, N, 3, H, D] buffer holding Q, K, V; O as [B, N, H, D]
+            buf = torch.empty(w.B, w.N, 3, w.H, w.D, dtype=q0.dtype, device=dev)
+            for j, t in enumerate((q0, k0, v0)):
+                buf[:, :, j] = t.permute(0, 2, 1, 3)
+            q, k, v = (buf[:, :, j].permute(0, 2, 1, 3) for j in range(3))
+            o = torch.empty(w.B, w.N, w.H, w.D, dtype=q0.dtype, device=dev).permute(0, 2, 1, 3)
+            sets.append({"q": q, "k": k, "v": v, "o": o, "buf": buf})
+            continue
         if i == 0:
             q, k, v = q0, k0, v0
         else:
@@ -379,6 +395,13 @@ def main():
                             P(s["kv"].data_ptr()), P(s["z"].data_ptr()), w.B, w.H, qc.shape[2], w.D, dt, w.eps,
                             None, ws_ptr, ws_n, st_ptr))
             calls.append(("block", seq))
+        elif packed:
+            lin = la.sana_layout(*s["q"].stride()[:3])
+            lout = la.sana_layout(*s["o"].stride()[:3])
+            s["layouts"] = (lin, lout)
+            calls.append(("strided", (P(s["q"].data_ptr()), P(s["k"].data_ptr()), P(s["v"].data_ptr()),
+                                      P(s["o"].data_ptr()), ctypes.byref(lin), ctypes.byref(lout), w.B, w.H, w.N,
+                                      w.D, dt, w.eps, rope_ref, ws_ptr, ws_n, st_ptr)))
         else:
             calls.append(("fwd", (P(s["q"].data_ptr()), P(s["k"].data_ptr()), P(s["v"].data_ptr()),
                                   P(s["o"].data_ptr()), w.B, w.H, w.N, w.D, dt, w.eps, rope_ref, ws_ptr, ws_n,
@@ -388,6 +411,10 @@ def main():
         kind, args = calls[i % n_sets]
         if kind == "sequence":
             rc = L.sana_linattn_block_causal(*args)
+            if rc:
+                raise la.SanaError(rc)
+        elif kind == "strided":
+            rc = L.sana_linattn_forward_strided(*args)
             if rc:
                 raise la.SanaError(rc)
         elif kind == "block":
@@ -433,12 +460,14 @@ def main():
     for s in sets:
         qa = s["q_chunks"][0] if w.mode == "block" else s["q"]
         oa = s["o_chunks"][0] if w.mode == "block" else s["o"]
+        if packed:  # the apply-alone entry point takes contiguous tensors
+            qa, oa = q0, torch.empty_like(q0)
         apply_sets.append((P(qa.data_ptr()), P(oa.data_ptr()), P(kv_st.data_ptr()), P(z_st.data_ptr()), w.B, w.H,
                            n_apply, w.D, dt, w.eps, rope_ref, st_ptr))
     kv_st.zero_()
     z_st.zero_()
-    k_state = sets[0]["k_chunks"][0] if w.mode == "block" else sets[0]["k"]
-    v_state = sets[0]["v_chunks"][0] if w.mode == "block" else sets[0]["v"]
+    k_state = sets[0]["k_chunks"][0] if w.mode == "block" else (k0 if packed else sets[0]["k"])
+    v_state = sets[0]["v_chunks"][0] if w.mode == "block" else (v0 if packed else sets[0]["v"])
     la.sana_linattn_state_update(k_state, v_state, kv_st, z_st, rope=rope, stream=stream)
     for i in range(args.warmup):
         L.sana_linattn_apply(*apply_sets[i % n_sets])
@@ -471,7 +500,8 @@ def main():
         "data": "synthetic: seeded i.i.d. N(0,1)x0.5 bf16 tensors at the workload's latent shape (no dataset, no weights)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "D": w.D, "mode": w.mode,
                    "chunk": w.chunk, "grid": w.grid, "eps": w.eps, "input_sets_cycled": n_sets,
-                   "block_calls": args.block_mode if w.mode == "block" else None},
+                   "block_calls": args.block_mode if w.mode == "block" else None,
+                   "layout": args.layout},
         "roofline": {
             "bound": "hbm",
             "kernel": "apply_bf16" if w.dtype == "bf16" else "apply_f32",
@@ -485,7 +515,8 @@ def main():
             "tokens_per_launch": w.B * w.H * n_apply,
         },
         "call": {
-            "entry_point": ("sana_linattn_forward" if w.mode != "block" else
+            "entry_point": ("sana_linattn_forward_strided (packed [B,N,3,H,D] in, [B,N,H,D] out)" if packed else
+                            "sana_linattn_forward" if w.mode != "block" else
                             "sana_linattn_block_causal (whole sequence)" if args.block_mode == "sequence" else
                             "sana_linattn_block_forward (per chunk)"),
             "kernels": "state pass + finalize + apply pass",

@@ -30,7 +30,8 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *   Layout     Q, K, V, O are contiguous [B][H][N][D] arrays, D innermost, in
- *              device memory, each 16-byte aligned.  kv state is [B][H][D][D]
+ *              device memory, each 16-byte aligned (the *_strided entry
+ *              points take other layouts, see sana_layout).  kv state is [B][H][D][D]
  *              float (row = key feature, column = value feature), ksum state
  *              is [B][H][D] float, both in device memory, 4-byte aligned.
  *   Dtype      One dtype for Q, K, V and O (sana_dtype).  States, RoPE tables
@@ -99,6 +100,24 @@ typedef struct {
     int64_t pos_offset;
 } sana_rope;
 
+/* Element strides of a [B][H][N][D] tensor view, D contiguous: token n of head
+ * h in batch b starts at element b*batch + h*head + n*token.  Examples (D = 32):
+ *   contiguous [B][H][N][D]             {H*N*D, N*D, D}   (what NULL means)
+ *   [B][N][H][D]                        {N*H*D, D, H*D}
+ *   q (k, v) of a packed [B][N][3][H][D] projection output: {N*3*H*D, D, 3*H*D},
+ *   with k and v at element offsets H*D and 2*H*D from q.
+ * Requirements: strides >= 0, token >= D; batch, head and token strides times
+ * the element size multiples of 16 bytes; token row stride at most 16 MiB.
+ * Input views may alias one another (as in the packed example); an output view
+ * must map distinct (b, h, n, d) to distinct elements (nested strides), and an
+ * output's address span (first to last element) must not overlap any other
+ * tensor's span or the state buffers.  Violations return SANA_ERR_INVALID. */
+typedef struct {
+    int64_t batch;
+    int64_t head;
+    int64_t token;
+} sana_layout;
+
 /* Bytes of device workspace that forward, state_update and block_forward need
  * for these sizes (0 when B*H*N == 0).  Pure host function, no HIP call.
  * Returns 0 as well for invalid sizes; the entry points then reject them. */
@@ -125,6 +144,15 @@ int sana_linattn_state_update(const void* k, const void* v, float* kv_state, flo
                               int B, int H, int64_t N, int D, int dtype,
                               const sana_rope* rope, void* ws, size_t ws_bytes, void* hip_stream);
 
+/* sana_linattn_forward with Q, K, V read through the view `in` and O written
+ * through `out` (NULL: contiguous), e.g. straight from a [B][N][3][H][D] QKV
+ * projection output, with no relayout copy.  Everything else as for
+ * sana_linattn_forward; the workspace size does not depend on the layout. */
+int sana_linattn_forward_strided(const void* q, const void* k, const void* v, void* o,
+                                 const sana_layout* in, const sana_layout* out,
+                                 int B, int H, int64_t N, int D, int dtype, float eps,
+                                 const sana_rope* rope, void* ws, size_t ws_bytes, void* hip_stream);
+
 /* One chunk of block-causal attention ("SANA-Video" paper notes 2.3 and 4;
  * news article "Design details"): the chunk's queries see the state carried
  * from earlier chunks plus every token of the chunk itself.
@@ -141,6 +169,14 @@ int sana_linattn_block_forward(const void* q, const void* k, const void* v, void
                                float* kv_out, float* ksum_out,
                                int B, int H, int64_t N, int D, int dtype, float eps,
                                const sana_rope* rope, void* ws, size_t ws_bytes, void* hip_stream);
+
+/* sana_linattn_block_forward through layout views (see sana_linattn_forward_strided). */
+int sana_linattn_block_forward_strided(const void* q, const void* k, const void* v, void* o,
+                                       const sana_layout* in, const sana_layout* out,
+                                       const float* kv_in, const float* ksum_in,
+                                       float* kv_out, float* ksum_out,
+                                       int B, int H, int64_t N, int D, int dtype, float eps,
+                                       const sana_rope* rope, void* ws, size_t ws_bytes, void* hip_stream);
 
 /* A whole sequence in block-causal chunks, in one call ("SANA-Video" paper
  * notes 2.3 and section 3's block-wise training; news article "Design
@@ -162,6 +198,14 @@ int sana_linattn_block_causal(const void* q, const void* k, const void* v, void*
                               float* kv_out, float* ksum_out,
                               int B, int H, int64_t N, int64_t chunk, int D, int dtype, float eps,
                               const sana_rope* rope, void* ws, size_t ws_bytes, void* hip_stream);
+
+/* sana_linattn_block_causal through layout views (see sana_linattn_forward_strided). */
+int sana_linattn_block_causal_strided(const void* q, const void* k, const void* v, void* o,
+                                      const sana_layout* in, const sana_layout* out,
+                                      const float* kv_in, const float* ksum_in,
+                                      float* kv_out, float* ksum_out,
+                                      int B, int H, int64_t N, int64_t chunk, int D, int dtype, float eps,
+                                      const sana_rope* rope, void* ws, size_t ws_bytes, void* hip_stream);
 
 /* Workspace bytes for sana_linattn_block_causal with these sizes (0 when
  * B*H*N == 0 or the sizes are invalid).  Pure host function. */
@@ -200,6 +244,19 @@ int sana_linattn_backward(const void* q, const void* k, const void* v, const voi
                           float* dkv_in, float* dksum_in,
                           int B, int H, int64_t N, int64_t chunk, int D, int dtype, float eps,
                           const sana_rope* rope, void* ws, size_t ws_bytes, void* hip_stream);
+
+/* sana_linattn_backward with q, k, v, dout read through the view `in` and
+ * dq, dk, dv written through `out` (NULL: contiguous); see
+ * sana_linattn_forward_strided.  dq, dk, dv each need a view of their own
+ * (distinct buffers or disjoint spans). */
+int sana_linattn_backward_strided(const void* q, const void* k, const void* v, const void* dout,
+                                  void* dq, void* dk, void* dv,
+                                  const sana_layout* in, const sana_layout* out,
+                                  const float* kv_in, const float* ksum_in,
+                                  const float* dkv_out, const float* dksum_out,
+                                  float* dkv_in, float* dksum_in,
+                                  int B, int H, int64_t N, int64_t chunk, int D, int dtype, float eps,
+                                  const sana_rope* rope, void* ws, size_t ws_bytes, void* hip_stream);
 
 /* Backward of sana_linattn_state_update (the key side of every backward):
  * given the gradient (dkv, dksum) reaching an updated state, the gradients of

@@ -17,6 +17,7 @@ from .binding import (  # noqa: F401
     SANA_ERR_WORKSPACE,
     SANA_OK,
     Rope,
+    sana_layout,
     SanaError,
     lib,
     make_workspace,

@@ -19,17 +19,25 @@ SANA_DT_F32, SANA_DT_BF16 = 0, 1
 EXPORTED = (
     "sana_linattn_workspace_bytes",
     "sana_linattn_forward",
+    "sana_linattn_forward_strided",
     "sana_linattn_state_update",
     "sana_linattn_block_forward",
+    "sana_linattn_block_forward_strided",
     "sana_linattn_block_causal",
+    "sana_linattn_block_causal_strided",
     "sana_linattn_block_causal_workspace_bytes",
     "sana_linattn_apply",
     "sana_linattn_backward",
+    "sana_linattn_backward_strided",
     "sana_linattn_backward_workspace_bytes",
     "sana_linattn_state_update_backward",
     "sana_linattn_rope3d_table",
     "sana_linattn_status_string",
 )
+
+
+class sana_layout(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("head", ctypes.c_int64), ("token", ctypes.c_int64)]
 
 
 class sana_rope(ctypes.Structure):
@@ -72,6 +80,18 @@ def lib():
     L.sana_linattn_backward.restype = i32
     L.sana_linattn_backward_workspace_bytes.argtypes = [i32, i32, i64, i64, i32, i32, i32]
     L.sana_linattn_backward_workspace_bytes.restype = sz
+    lp = ctypes.POINTER(sana_layout)
+    L.sana_linattn_forward_strided.argtypes = [vp, vp, vp, vp, lp, lp, i32, i32, i64, i32, i32, f32, rp, vp, sz, vp]
+    L.sana_linattn_forward_strided.restype = i32
+    L.sana_linattn_block_forward_strided.argtypes = [vp, vp, vp, vp, lp, lp, vp, vp, vp, vp, i32, i32, i64, i32, i32,
+                                                     f32, rp, vp, sz, vp]
+    L.sana_linattn_block_forward_strided.restype = i32
+    L.sana_linattn_block_causal_strided.argtypes = [vp, vp, vp, vp, lp, lp, vp, vp, vp, vp, i32, i32, i64, i64, i32,
+                                                    i32, f32, rp, vp, sz, vp]
+    L.sana_linattn_block_causal_strided.restype = i32
+    L.sana_linattn_backward_strided.argtypes = [vp, vp, vp, vp, vp, vp, vp, lp, lp, vp, vp, vp, vp, vp, vp, i32, i32,
+                                                i64, i64, i32, i32, f32, rp, vp, sz, vp]
+    L.sana_linattn_backward_strided.restype = i32
     L.sana_linattn_state_update_backward.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, rp, vp]
     L.sana_linattn_state_update_backward.restype = i32
     L.sana_linattn_rope3d_table.argtypes = [i32, i32, i32, i32, i32, i32, i32, ctypes.c_double, vp, vp]
@@ -119,14 +139,35 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _shape4(t, name):
+def _shape4(t, name, strided=False):
+    """Shape of a [B, H, N, D] device tensor: contiguous, or with strided=True
+    any view whose last dimension is contiguous."""
     if t.dim() != 4:
         raise ValueError(f"{name} must be [B, H, N, D], got shape {tuple(t.shape)}")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
-    if not t.is_contiguous():
+    if strided:
+        if t.shape[3] > 1 and t.stride(3) != 1:
+            raise ValueError(f"{name} must have contiguous features (stride 1 in its last dimension)")
+    elif not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return tuple(t.shape)
+
+
+def _view(*ts):
+    """The common sana_layout of tensors that share one view, or None when they
+    are all contiguous."""
+    strides = {tuple(t.stride()[:3]) for t in ts}
+    if len(strides) != 1:
+        raise ValueError("tensors passed as one group (q, k, v[, dout] or the outputs) must share their strides")
+    if all(t.is_contiguous() for t in ts):
+        return None
+    b, h, n = strides.pop()
+    return sana_layout(b, h, n)
+
+
+def _lay(view):
+    return None if view is None else ctypes.byref(view)
 
 
 def _stream(stream, device):
@@ -194,21 +235,29 @@ def _workspace(ws, B, H, N, D, dt, has_rope, device):
 
 
 def sana_linattn_forward(q, k, v, o=None, eps=1e-6, rope=None, workspace=None, stream=None):
-    """Non-causal ReLU linear attention; returns O (allocated if not given)."""
+    """Non-causal ReLU linear attention; returns O (allocated contiguous if not
+    given).  q, k, v (one shared view) and o may be strided [B, H, N, D] views,
+    e.g. of a packed [B, N, 3, H, D] projection output."""
     torch = _torch()
-    B, H, N, D = _shape4(q, "q")
-    if _shape4(k, "k") != (B, H, N, D) or _shape4(v, "v") != (B, H, N, D):
+    B, H, N, D = _shape4(q, "q", strided=True)
+    if _shape4(k, "k", strided=True) != (B, H, N, D) or _shape4(v, "v", strided=True) != (B, H, N, D):
         raise ValueError("q, k, v must have the same shape")
     if o is None:
-        o = torch.empty_like(q)
-    elif _shape4(o, "o") != (B, H, N, D) or o.dtype != q.dtype:
+        o = torch.empty((B, H, N, D), dtype=q.dtype, device=q.device)
+    elif _shape4(o, "o", strided=True) != (B, H, N, D) or o.dtype != q.dtype:
         raise ValueError("o must match q in shape and dtype")
     dt = _dtype_code(q)
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k, v must share one dtype")
+    vin, vout = _view(q, k, v), _view(o)
     ws, nbytes = _workspace(workspace, B, H, N, D, dt, rope is not None, q.device)
-    _check(lib().sana_linattn_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, N, D, dt, float(eps),
-                                      _rope_arg(rope), _ptr(ws), nbytes, _stream(stream, q.device)))
+    if vin is None and vout is None:
+        _check(lib().sana_linattn_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, N, D, dt, float(eps),
+                                          _rope_arg(rope), _ptr(ws), nbytes, _stream(stream, q.device)))
+    else:
+        _check(lib().sana_linattn_forward_strided(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _lay(vin), _lay(vout), B, H, N,
+                                                  D, dt, float(eps), _rope_arg(rope), _ptr(ws), nbytes,
+                                                  _stream(stream, q.device)))
     return o
 
 
@@ -232,23 +281,30 @@ def sana_linattn_state_update(k, v, kv_state, ksum_state, rope=None, workspace=N
 def sana_linattn_block_forward(q, k, v, o=None, kv_in=None, ksum_in=None, kv_out=None, ksum_out=None,
                                eps=1e-6, rope=None, workspace=None, stream=None):
     """One block-causal chunk; returns O.  kv_in/ksum_in None = zero state;
-    kv_out/ksum_out None = do not commit."""
+    kv_out/ksum_out None = do not commit.  Strided views as for the forward."""
     torch = _torch()
-    B, H, N, D = _shape4(q, "q")
-    if _shape4(k, "k") != (B, H, N, D) or _shape4(v, "v") != (B, H, N, D):
+    B, H, N, D = _shape4(q, "q", strided=True)
+    if _shape4(k, "k", strided=True) != (B, H, N, D) or _shape4(v, "v", strided=True) != (B, H, N, D):
         raise ValueError("q, k, v must have the same shape")
     if o is None:
-        o = torch.empty_like(q)
-    elif _shape4(o, "o") != (B, H, N, D) or o.dtype != q.dtype:
+        o = torch.empty((B, H, N, D), dtype=q.dtype, device=q.device)
+    elif _shape4(o, "o", strided=True) != (B, H, N, D) or o.dtype != q.dtype:
         raise ValueError("o must match q in shape and dtype")
     for t, shape in ((kv_in, (B, H, D, D)), (ksum_in, (B, H, D)), (kv_out, (B, H, D, D)), (ksum_out, (B, H, D))):
         if t is not None and (tuple(t.shape) != shape or t.dtype != torch.float32 or not t.is_contiguous()):
             raise ValueError("states must be contiguous float32 [B, H, D, D] / [B, H, D]")
     dt = _dtype_code(q)
+    vin, vout = _view(q, k, v), _view(o)
     ws, nbytes = _workspace(workspace, B, H, N, D, dt, rope is not None, q.device)
-    _check(lib().sana_linattn_block_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(kv_in), _ptr(ksum_in),
-                                            _ptr(kv_out), _ptr(ksum_out), B, H, N, D, dt, float(eps),
-                                            _rope_arg(rope), _ptr(ws), nbytes, _stream(stream, q.device)))
+    if vin is None and vout is None:
+        _check(lib().sana_linattn_block_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(kv_in), _ptr(ksum_in),
+                                                _ptr(kv_out), _ptr(ksum_out), B, H, N, D, dt, float(eps),
+                                                _rope_arg(rope), _ptr(ws), nbytes, _stream(stream, q.device)))
+    else:
+        _check(lib().sana_linattn_block_forward_strided(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _lay(vin), _lay(vout),
+                                                        _ptr(kv_in), _ptr(ksum_in), _ptr(kv_out), _ptr(ksum_out),
+                                                        B, H, N, D, dt, float(eps), _rope_arg(rope), _ptr(ws),
+                                                        nbytes, _stream(stream, q.device)))
     return o
 
 
@@ -259,14 +315,15 @@ def block_causal_workspace_bytes(B, H, N, chunk, D=32, dtype=SANA_DT_BF16, has_r
 def sana_linattn_block_causal(q, k, v, chunk, o=None, kv_in=None, ksum_in=None, kv_out=None, ksum_out=None,
                               eps=1e-6, rope=None, workspace=None, stream=None):
     """A whole sequence in block-causal chunks of `chunk` tokens; returns O.
-    kv_in/ksum_in None = zero state; kv_out/ksum_out None = do not commit."""
+    kv_in/ksum_in None = zero state; kv_out/ksum_out None = do not commit.
+    Strided views as for the forward."""
     torch = _torch()
-    B, H, N, D = _shape4(q, "q")
-    if _shape4(k, "k") != (B, H, N, D) or _shape4(v, "v") != (B, H, N, D):
+    B, H, N, D = _shape4(q, "q", strided=True)
+    if _shape4(k, "k", strided=True) != (B, H, N, D) or _shape4(v, "v", strided=True) != (B, H, N, D):
         raise ValueError("q, k, v must have the same shape")
     if o is None:
-        o = torch.empty_like(q)
-    elif _shape4(o, "o") != (B, H, N, D) or o.dtype != q.dtype:
+        o = torch.empty((B, H, N, D), dtype=q.dtype, device=q.device)
+    elif _shape4(o, "o", strided=True) != (B, H, N, D) or o.dtype != q.dtype:
         raise ValueError("o must match q in shape and dtype")
     for t, shape in ((kv_in, (B, H, D, D)), (ksum_in, (B, H, D)), (kv_out, (B, H, D, D)), (ksum_out, (B, H, D))):
         if t is not None and (tuple(t.shape) != shape or t.dtype != torch.float32 or not t.is_contiguous()):
@@ -275,10 +332,17 @@ def sana_linattn_block_causal(q, k, v, chunk, o=None, kv_in=None, ksum_in=None, 
     if workspace is None:
         workspace = torch.empty(max(block_causal_workspace_bytes(B, H, N, chunk, D, dt, rope is not None), 256),
                                 dtype=torch.uint8, device=q.device)
-    _check(lib().sana_linattn_block_causal(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(kv_in), _ptr(ksum_in),
-                                           _ptr(kv_out), _ptr(ksum_out), B, H, N, int(chunk), D, dt, float(eps),
-                                           _rope_arg(rope), _ptr(workspace), workspace.numel(),
-                                           _stream(stream, q.device)))
+    vin, vout = _view(q, k, v), _view(o)
+    if vin is None and vout is None:
+        _check(lib().sana_linattn_block_causal(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(kv_in), _ptr(ksum_in),
+                                               _ptr(kv_out), _ptr(ksum_out), B, H, N, int(chunk), D, dt, float(eps),
+                                               _rope_arg(rope), _ptr(workspace), workspace.numel(),
+                                               _stream(stream, q.device)))
+    else:
+        _check(lib().sana_linattn_block_causal_strided(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _lay(vin), _lay(vout),
+                                                       _ptr(kv_in), _ptr(ksum_in), _ptr(kv_out), _ptr(ksum_out), B, H,
+                                                       N, int(chunk), D, dt, float(eps), _rope_arg(rope),
+                                                       _ptr(workspace), workspace.numel(), _stream(stream, q.device)))
     return o
 
 
@@ -294,15 +358,15 @@ def sana_linattn_backward(q, k, v, dout, chunk=None, dq=None, dk=None, dv=None, 
     non-causal forward).  Returns (dq, dk, dv); dkv_in/dksum_in, when given,
     receive the gradient of the carried state kv_in/ksum_in."""
     torch = _torch()
-    B, H, N, D = _shape4(q, "q")
+    B, H, N, D = _shape4(q, "q", strided=True)
     for t, name in ((k, "k"), (v, "v"), (dout, "dout")):
-        if _shape4(t, name) != (B, H, N, D) or t.dtype != q.dtype:
+        if _shape4(t, name, strided=True) != (B, H, N, D) or t.dtype != q.dtype:
             raise ValueError("q, k, v, dout must have the same shape and dtype")
     outs = []
     for t, name in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
         if t is None:
-            t = torch.empty_like(q)
-        elif _shape4(t, name) != (B, H, N, D) or t.dtype != q.dtype:
+            t = torch.empty((B, H, N, D), dtype=q.dtype, device=q.device)
+        elif _shape4(t, name, strided=True) != (B, H, N, D) or t.dtype != q.dtype:
             raise ValueError(f"{name} must match q in shape and dtype")
         outs.append(t)
     for t, shape in ((kv_in, (B, H, D, D)), (ksum_in, (B, H, D)), (dkv_out, (B, H, D, D)), (dksum_out, (B, H, D)),
@@ -315,11 +379,19 @@ def sana_linattn_backward(q, k, v, dout, chunk=None, dq=None, dk=None, dv=None, 
     if workspace is None:
         workspace = torch.empty(max(backward_workspace_bytes(B, H, N, L, D, dt, rope is not None), 256),
                                 dtype=torch.uint8, device=q.device)
-    _check(lib().sana_linattn_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(outs[0]), _ptr(outs[1]),
-                                       _ptr(outs[2]), _ptr(kv_in), _ptr(ksum_in), _ptr(dkv_out), _ptr(dksum_out),
-                                       _ptr(dkv_in), _ptr(dksum_in), B, H, N, L, D, dt, float(eps),
-                                       _rope_arg(rope), _ptr(workspace), workspace.numel(),
-                                       _stream(stream, q.device)))
+    vin, vout = _view(q, k, v, dout), _view(*outs)
+    if vin is None and vout is None:
+        _check(lib().sana_linattn_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(outs[0]), _ptr(outs[1]),
+                                           _ptr(outs[2]), _ptr(kv_in), _ptr(ksum_in), _ptr(dkv_out), _ptr(dksum_out),
+                                           _ptr(dkv_in), _ptr(dksum_in), B, H, N, L, D, dt, float(eps),
+                                           _rope_arg(rope), _ptr(workspace), workspace.numel(),
+                                           _stream(stream, q.device)))
+    else:
+        _check(lib().sana_linattn_backward_strided(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(outs[0]),
+                                                   _ptr(outs[1]), _ptr(outs[2]), _lay(vin), _lay(vout), _ptr(kv_in),
+                                                   _ptr(ksum_in), _ptr(dkv_out), _ptr(dksum_out), _ptr(dkv_in),
+                                                   _ptr(dksum_in), B, H, N, L, D, dt, float(eps), _rope_arg(rope),
+                                                   _ptr(workspace), workspace.numel(), _stream(stream, q.device)))
     return tuple(outs)
 
 

@@ -112,7 +112,8 @@ __global__ __launch_bounds__(kThreads) void state_finalize_reverse(StateArgs a, 
 // tile, and element row d = t / 8, columns f0 .. f0+3 of the partial dS.
 template <typename T, bool ROPE>
 __global__ __launch_bounds__(kThreads) void bwd_query_vec(const T* __restrict__ Q, const T* __restrict__ dO,
-                                                          T* __restrict__ dQ, StateView fwd, float eps,
+                                                          T* __restrict__ dQ, Layout lin, Layout lout,
+                                                          StateView fwd, float eps,
                                                           const float* __restrict__ cos_t,
                                                           const float* __restrict__ sin_t, int64_t pos0,
                                                           StateArgs a) {
@@ -127,7 +128,6 @@ __global__ __launch_bounds__(kThreads) void bwd_query_vec(const T* __restrict__ 
   int64_t bh, n_begin, n_end;
   int c, s;
   state_item(a, bh, c, s, n_begin, n_end);
-  const int64_t N = a.N;
   const int t = threadIdx.x;
   const int tl = t >> 3;
   const int f0 = (t & 7) * 4;
@@ -140,7 +140,7 @@ __global__ __launch_bounds__(kThreads) void bwd_query_vec(const T* __restrict__ 
   for (int64_t t0 = n_begin; t0 < n_end; t0 += 32) {
     const int64_t tok = t0 + tl;
     const bool live = tok < n_end;
-    const int64_t row = (bh * N + tok) * kD + f0;
+    const int64_t row = lin.base(bh) + tok * lin.token + f0;
     f32x4_t x = {0.f, 0.f, 0.f, 0.f}, g = x;
     if (live) {
       x = load4(Q + row);
@@ -193,7 +193,7 @@ __global__ __launch_bounds__(kThreads) void bwd_query_vec(const T* __restrict__ 
     f32x4_t dq;
 #pragma unroll
     for (int u = 0; u < 4; ++u) dq[u] = x[u] > 0.f ? dr[u] + sz[f0 + u] * dden : 0.f;
-    if (live) store4(dQ + row, dq);
+    if (live) store4(dQ + lout.base(bh) + tok * lout.token + f0, dq);
     // partial dS row d = tl, columns f0 .. f0+3; dz[d]
     for (int j = 0; j < 32; ++j) {
       const float qd = spr[j][tl];
@@ -218,7 +218,8 @@ __global__ __launch_bounds__(kThreads) void bwd_query_vec(const T* __restrict__ 
 // 32-token tiles, thread t: features f0 = 4 (t % 8) .. f0+3 of token t / 8.
 template <typename T, bool ROPE>
 __global__ __launch_bounds__(kThreads) void bwd_key_vec(const T* __restrict__ K, const T* __restrict__ V,
-                                                        T* __restrict__ dK, T* __restrict__ dV, StateView grad,
+                                                        T* __restrict__ dK, T* __restrict__ dV, Layout lin,
+                                                        Layout lout, StateView grad,
                                                         int64_t N, int64_t L, int C, int tiles, int64_t Lt,
                                                         const float* __restrict__ cos_t,
                                                         const float* __restrict__ sin_t, int64_t pos0) {
@@ -244,7 +245,8 @@ __global__ __launch_bounds__(kThreads) void bwd_key_vec(const T* __restrict__ K,
   for (int64_t t0 = n_begin; t0 < n_end; t0 += 32) {
     const int64_t tok = t0 + tl;
     const bool live = tok < n_end;
-    const int64_t row = (bh * N + tok) * kD + f0;
+    const int64_t row = lin.base(bh) + tok * lin.token + f0;
+    const int64_t orow = lout.base(bh) + tok * lout.token + f0;
     f32x4_t x = {0.f, 0.f, 0.f, 0.f}, vv = x;
     if (live) {
       x = load4(K + row);
@@ -280,8 +282,8 @@ __global__ __launch_bounds__(kThreads) void bwd_key_vec(const T* __restrict__ K,
 #pragma unroll
     for (int u = 0; u < 4; ++u) dk[u] = x[u] > 0.f ? dr[u] + sGz[f0 + u] : 0.f;
     if (live) {
-      store4(dK + row, dk);
-      store4(dV + row, dv);
+      store4(dK + orow, dk);
+      store4(dV + orow, dv);
     }
   }
 }
@@ -412,38 +414,42 @@ struct KeyChunk {
 };
 
 template <bool ROPE>
-__device__ __forceinline__ void load_key_chunk(const char* Kh, const char* Vh, int64_t t0, int64_t n_end,
-                                               int lane_off, const float* cos_t, const float* sin_t, int64_t pos0,
-                                               KeyChunk<ROPE>& ch) {
-  const rsrc_t rk = make_rsrc(Kh + t0 * 64, (n_end - t0) * 64);
-  const rsrc_t rv = make_rsrc(Vh + t0 * 64, (n_end - t0) * 64);
+__device__ __forceinline__ void load_key_chunk(const char* Kh, const char* Vh, int64_t row, int64_t t0,
+                                               int64_t n_end, int lane_off, int tab_off, const float* cos_t,
+                                               const float* sin_t, int64_t pos0, KeyChunk<ROPE>& ch) {
+  const rsrc_t rk = rows_rsrc(Kh, t0, n_end, row);
+  const rsrc_t rv = rows_rsrc(Vh, t0, n_end, row);
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    ch.k[u] = load16_nt(rk, lane_off + u * 1024);
-    ch.v[u] = load16_nt(rv, lane_off + u * 1024);
+    ch.k[u] = load16_nt(rk, lane_off + u * 16 * (int)row);
+    ch.v[u] = load16_nt(rv, lane_off + u * 16 * (int)row);
   }
   if constexpr (ROPE) {
     const rsrc_t rc = make_rsrc(cos_t + (pos0 + t0) * 16, (n_end - t0) * 64);
     const rsrc_t rs = make_rsrc(sin_t + (pos0 + t0) * 16, (n_end - t0) * 64);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      ch.c[u] = load16(rc, lane_off + u * 1024);
-      ch.sn[u] = load16(rs, lane_off + u * 1024);
+      ch.c[u] = load16(rc, tab_off + u * 1024);
+      ch.sn[u] = load16(rs, tab_off + u * 1024);
     }
   }
 }
 
-template <bool ROPE>
+template <bool ROPE, bool DENSE>
 __global__ __launch_bounds__(kThreads) void bwd_key_bf16(const u32x4_t* __restrict__ K, const u32x4_t* __restrict__ V,
                                                          u32x4_t* __restrict__ dK, u32x4_t* __restrict__ dV,
-                                                         StateView grad, int64_t N, int64_t L, int C, int64_t total,
-                                                         int64_t La, const float* __restrict__ cos_t,
+                                                         Layout lin, Layout lout, StateView grad, int64_t N,
+                                                         int64_t L, int C, int64_t total, int64_t La,
+                                                         const float* __restrict__ cos_t,
                                                          const float* __restrict__ sin_t, int64_t pos0) {
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int m = lane & 15;
   const int g = lane >> 4;
-  const int lane_off = m * 64 + g * 16;
+  const int64_t irow = DENSE ? 64 : lin.token * 2, orow = DENSE ? 64 : lout.token * 2;  // bytes between tokens
+  const int lane_off = m * (int)irow + g * 16;
+  const int out_off = m * (int)orow + g * 16;
+  const int tab_off = m * 64 + g * 16;
   const int64_t f_begin = (int64_t)blockIdx.x * La;
   const int64_t f_end = (f_begin + La < total) ? f_begin + La : total;
 
@@ -454,14 +460,14 @@ __global__ __launch_bounds__(kThreads) void bwd_key_bf16(const u32x4_t* __restri
     const int64_t c_end = ((int64_t)c + 1) * L < N ? ((int64_t)c + 1) * L : N;
     const int64_t n_end = (f_end - bh * N < c_end) ? f_end - bh * N : c_end;
     f = bh * N + n_end;
-    const char* Kh = reinterpret_cast<const char*>(K + bh * N * 4);
-    const char* Vh = reinterpret_cast<const char*>(V + bh * N * 4);
-    char* dKh = reinterpret_cast<char*>(dK + bh * N * 4);
-    char* dVh = reinterpret_cast<char*>(dV + bh * N * 4);
+    const char* Kh = reinterpret_cast<const char*>(K) + lin.base(bh) * 2;
+    const char* Vh = reinterpret_cast<const char*>(V) + lin.base(bh) * 2;
+    char* dKh = reinterpret_cast<char*>(dK) + lout.base(bh) * 2;
+    char* dVh = reinterpret_cast<char*>(dV) + lout.base(bh) * 2;
 
     int64_t t0 = n_begin + 64 * w;
     KeyChunk<ROPE> next;
-    if (t0 < n_end) load_key_chunk<ROPE>(Kh, Vh, t0, n_end, lane_off, cos_t, sin_t, pos0, next);
+    if (t0 < n_end) load_key_chunk<ROPE>(Kh, Vh, irow, t0, n_end, lane_off, tab_off, cos_t, sin_t, pos0, next);
     const int64_t sc = bh * C + c;
     const float* G = grad.s_base + sc * grad.s_stride;
     const float* Gz = grad.z_base + sc * grad.z_stride;
@@ -474,9 +480,10 @@ __global__ __launch_bounds__(kThreads) void bwd_key_bf16(const u32x4_t* __restri
 
     for (; t0 < n_end; t0 += 256) {
       const KeyChunk<ROPE> cur = next;
-      if (t0 + 256 < n_end) load_key_chunk<ROPE>(Kh, Vh, t0 + 256, n_end, lane_off, cos_t, sin_t, pos0, next);
-      const rsrc_t rdk = make_rsrc(dKh + t0 * 64, (n_end - t0) * 64);
-      const rsrc_t rdv = make_rsrc(dVh + t0 * 64, (n_end - t0) * 64);
+      if (t0 + 256 < n_end)
+        load_key_chunk<ROPE>(Kh, Vh, irow, t0 + 256, n_end, lane_off, tab_off, cos_t, sin_t, pos0, next);
+      const rsrc_t rdk = rows_rsrc(dKh, t0, n_end, orow);
+      const rsrc_t rdv = rows_rsrc(dVh, t0, n_end, orow);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const u32x4_t kr = relu_bf16x8(cur.k[u]);
@@ -494,7 +501,7 @@ __global__ __launch_bounds__(kThreads) void bwd_key_bf16(const u32x4_t* __restri
         }
         x[0] = o0[0], x[1] = o0[1], x[2] = o0[2], x[3] = o0[3];
         x[4] = o1[0], x[5] = o1[1], x[6] = o1[2], x[7] = o1[3];
-        store16_nt(rdv, lane_off + u * 1024, pack8(x));
+        store16_nt(rdv, out_off + u * 16 * (int)orow, pack8(x));
         mfma3(grow, __builtin_bit_cast(bf16x8_t, cur.v[u]), o0, o1);
         x[0] = o0[0], x[1] = o0[1], x[2] = o0[2], x[3] = o0[3];
         x[4] = o1[0], x[5] = o1[1], x[6] = o1[2], x[7] = o1[3];
@@ -504,7 +511,7 @@ __global__ __launch_bounds__(kThreads) void bwd_key_bf16(const u32x4_t* __restri
           x[2 * p] = (kr[p] & 0xffffu) ? x[2 * p] + gz[2 * p] : 0.f;
           x[2 * p + 1] = (kr[p] >> 16) ? x[2 * p + 1] + gz[2 * p + 1] : 0.f;
         }
-        store16_nt(rdk, lane_off + u * 1024, pack8(x));
+        store16_nt(rdk, out_off + u * 16 * (int)orow, pack8(x));
       }
     }
   }
@@ -536,31 +543,32 @@ struct QueryTile {
 };
 
 template <bool ROPE>
-__device__ __forceinline__ void load_query_tile(const char* Qh, const char* Oh, int64_t t0, int64_t n_end,
-                                                int lane_off, const float* cos_t, const float* sin_t, int64_t pos0,
-                                                QueryTile<ROPE>& tl) {
-  const rsrc_t rq = make_rsrc(Qh + t0 * 64, (n_end - t0) * 64);
-  const rsrc_t ro = make_rsrc(Oh + t0 * 64, (n_end - t0) * 64);
+__device__ __forceinline__ void load_query_tile(const char* Qh, const char* Oh, int64_t row, int64_t t0,
+                                                int64_t n_end, int lane_off, int tab_off, const float* cos_t,
+                                                const float* sin_t, int64_t pos0, QueryTile<ROPE>& tl) {
+  const rsrc_t rq = rows_rsrc(Qh, t0, n_end, row);
+  const rsrc_t ro = rows_rsrc(Oh, t0, n_end, row);
 #pragma unroll
   for (int tb = 0; tb < 2; ++tb) {
-    tl.q[tb] = load16_nt(rq, lane_off + tb * 1024);
-    tl.dout[tb] = load16_nt(ro, lane_off + tb * 1024);
+    tl.q[tb] = load16_nt(rq, lane_off + tb * 16 * (int)row);
+    tl.dout[tb] = load16_nt(ro, lane_off + tb * 16 * (int)row);
   }
   if constexpr (ROPE) {
     const rsrc_t rc = make_rsrc(cos_t + (pos0 + t0) * 16, (n_end - t0) * 64);
     const rsrc_t rs = make_rsrc(sin_t + (pos0 + t0) * 16, (n_end - t0) * 64);
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
-      tl.c[tb] = load16(rc, lane_off + tb * 1024);
-      tl.sn[tb] = load16(rs, lane_off + tb * 1024);
+      tl.c[tb] = load16(rc, tab_off + tb * 1024);
+      tl.sn[tb] = load16(rs, tab_off + tb * 1024);
     }
   }
 }
 
-template <bool ROPE>
+template <bool ROPE, bool DENSE>
 __global__ __launch_bounds__(kThreads) void bwd_query_bf16(const u32x4_t* __restrict__ Q,
                                                            const u32x4_t* __restrict__ dO, u32x4_t* __restrict__ dQ,
-                                                           StateView fwd, float eps, const float* __restrict__ cos_t,
+                                                           Layout lin, Layout lout, StateView fwd, float eps,
+                                                           const float* __restrict__ cos_t,
                                                            const float* __restrict__ sin_t, int64_t pos0,
                                                            StateArgs a) {
   __shared__ float red[4][kStateElems];
@@ -569,21 +577,23 @@ __global__ __launch_bounds__(kThreads) void bwd_query_bf16(const u32x4_t* __rest
   int64_t bh, n_begin, n_end;
   int c, s;
   state_item(a, bh, c, s, n_begin, n_end);
-  const int64_t N = a.N;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;  // also the token row m of the natural layout
   const int g = lane >> 4;
-  const int lane_off = n * 64 + g * 16;
-  const char* Qh = reinterpret_cast<const char*>(Q + bh * N * 4);
-  const char* Oh = reinterpret_cast<const char*>(dO + bh * N * 4);
-  char* dQh = reinterpret_cast<char*>(dQ + bh * N * 4);
+  const int64_t irow = DENSE ? 64 : lin.token * 2, orow = DENSE ? 64 : lout.token * 2;  // bytes between tokens
+  const int lane_off = n * (int)irow + g * 16;
+  const int out_off = n * (int)orow + g * 16;
+  const int tab_off = n * 64 + g * 16;
+  const char* Qh = reinterpret_cast<const char*>(Q) + lin.base(bh) * 2;
+  const char* Oh = reinterpret_cast<const char*>(dO) + lin.base(bh) * 2;
+  char* dQh = reinterpret_cast<char*>(dQ) + lout.base(bh) * 2;
   float* dn_tile = tiles[w][0];
   float* pq_tile = tiles[w][ROPE ? 1 : 0];
 
   int64_t t0 = n_begin + 32 * w;
   QueryTile<ROPE> next;
-  if (t0 < n_end) load_query_tile<ROPE>(Qh, Oh, t0, n_end, lane_off, cos_t, sin_t, pos0, next);
+  if (t0 < n_end) load_query_tile<ROPE>(Qh, Oh, irow, t0, n_end, lane_off, tab_off, cos_t, sin_t, pos0, next);
 
   const int64_t sc = bh * a.C + c;
   const float* S = fwd.s_base + sc * fwd.s_stride;
@@ -606,8 +616,9 @@ __global__ __launch_bounds__(kThreads) void bwd_query_bf16(const u32x4_t* __rest
 
   for (; t0 < n_end; t0 += 128) {
     const QueryTile<ROPE> cur = next;
-    if (t0 + 128 < n_end) load_query_tile<ROPE>(Qh, Oh, t0 + 128, n_end, lane_off, cos_t, sin_t, pos0, next);
-    const rsrc_t rdq = make_rsrc(dQh + t0 * 64, (n_end - t0) * 64);
+    if (t0 + 128 < n_end)
+      load_query_tile<ROPE>(Qh, Oh, irow, t0 + 128, n_end, lane_off, tab_off, cos_t, sin_t, pos0, next);
+    const rsrc_t rdq = rows_rsrc(dQh, t0, n_end, orow);
     bf16x8_t bq[2];
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -655,7 +666,7 @@ __global__ __launch_bounds__(kThreads) void bwd_query_bf16(const u32x4_t* __rest
         dr[j] = pq[j] > 0.f ? dr[j] + zf[j] * dden : 0.f;
         dzacc[j] += pq[j] * dden;
       }
-      store16_nt(rdq, lane_off + tb * 1024, pack8(dr));
+      store16_nt(rdq, out_off + tb * 16 * (int)orow, pack8(dr));
       // dnum (and phi~(Q)) of token row 16tb + n, features 8g .. 8g+7
       float* rowp = dn_tile + (16 * tb + n) * kTileRow + 8 * g;
       *reinterpret_cast<f32x4_t*>(rowp) = f32x4_t{gd[0] * rden, gd[1] * rden, gd[2] * rden, gd[3] * rden};

@@ -82,6 +82,26 @@ struct StateView {
   int64_t z_stride;
 };
 
+// Where the tokens of a [B][H][N][32] tensor live: token n of head
+// bh = b * H + h starts at element b * batch + h * head + n * token, and its
+// 32 features are contiguous.  Contiguous [B][H][N][D] is
+// {H*N*32, N*32, 32}; [B][N][H][D] is {N*H*32, 32, H*32}; the q, k or v part
+// of a packed [B][N][3][H][D] projection output is {N*3*H*32, 32, 3*H*32}.
+struct Layout {
+  int64_t batch;
+  int64_t head;
+  int64_t token;
+  int64_t H;
+
+  // B*H < 2^24, so the head index splits with a 32-bit division; when the
+  // batch stride continues the head stride (contiguous heads) none is needed.
+  __device__ __forceinline__ int64_t base(int64_t bh) const {
+    if (batch == H * head) return bh * head;
+    const uint32_t b = (uint32_t)bh / (uint32_t)H;
+    return (int64_t)b * batch + (int64_t)((uint32_t)bh - b * (uint32_t)H) * head;
+  }
+};
+
 // ---------------------------------------------------------------------------
 // bf16 helpers
 // ---------------------------------------------------------------------------
@@ -154,6 +174,12 @@ constexpr int kNonTemporal = 2;         // cache policy of data streamed once
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
   const int64_t nr = bytes < 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : bytes);
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nr, kRsrcWord3);
+}
+
+// Descriptor for rows t0 .. n_end-1 of a tensor whose rows are `row` bytes
+// apart (64 of them in use): rows at or past n_end fall outside.
+__device__ __forceinline__ rsrc_t rows_rsrc(const char* head_base, int64_t t0, int64_t n_end, int64_t row) {
+  return make_rsrc(head_base + t0 * row, (n_end - t0 - 1) * row + 64);
 }
 
 __device__ __forceinline__ u32x4_t load16_nt(rsrc_t r, int off) {
@@ -346,13 +372,13 @@ struct TileAnglesRows {
 };
 
 __device__ __forceinline__ void load_angle_rows(const float* cos_t, const float* sin_t, int64_t pos0, int64_t t0,
-                                                int64_t n_end, int lane_off, TileAnglesRows& rows) {
+                                                int64_t n_end, int tab_off, TileAnglesRows& rows) {
   const rsrc_t rc = make_rsrc(cos_t + (pos0 + t0) * 16, (n_end - t0) * 64);
   const rsrc_t rs = make_rsrc(sin_t + (pos0 + t0) * 16, (n_end - t0) * 64);
 #pragma unroll
   for (int tb = 0; tb < 2; ++tb) {
-    rows.c[tb] = load16(rc, lane_off + tb * 1024);
-    rows.s[tb] = load16(rs, lane_off + tb * 1024);
+    rows.c[tb] = load16(rc, tab_off + tb * 1024);
+    rows.s[tb] = load16(rs, tab_off + tb * 1024);
   }
 }
 
@@ -445,9 +471,11 @@ __device__ __forceinline__ void state_tile(const u32x4_t (&kx)[2], const u32x4_t
   }
 }
 
-template <bool ROPE>
+// DENSE: consecutive tokens are adjacent 64-byte rows (token stride = 32
+// elements), so every tile offset is an instruction immediate.
+template <bool ROPE, bool DENSE>
 __global__ __launch_bounds__(kThreads) void state_bf16(const u32x4_t* __restrict__ K, const u32x4_t* __restrict__ V,
-                                                       const float* __restrict__ cos_t,
+                                                       Layout lkv, const float* __restrict__ cos_t,
                                                        const float* __restrict__ sin_t, int64_t pos0,
                                                        StateArgs a) {
   __shared__ float red[4][kStateElems];
@@ -456,16 +484,17 @@ __global__ __launch_bounds__(kThreads) void state_bf16(const u32x4_t* __restrict
   int64_t bh, n_begin, n_end;
   int c, s;
   state_item(a, bh, c, s, n_begin, n_end);
-  const int64_t N = a.N;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;
   const int g = lane >> 4;
 
   // lane's 16-byte piece of a row: features 8g .. 8g+7 of token (tile row) n
-  const char* Kh = reinterpret_cast<const char*>(K + bh * N * 4);
-  const char* Vh = reinterpret_cast<const char*>(V + bh * N * 4);
-  const int lane_off = n * 64 + g * 16;
+  const int64_t row = DENSE ? 64 : lkv.token * 2;  // bytes between tokens
+  const char* Kh = reinterpret_cast<const char*>(K) + lkv.base(bh) * 2;
+  const char* Vh = reinterpret_cast<const char*>(V) + lkv.base(bh) * 2;
+  const int lane_off = n * (int)row + g * 16;
+  const int tab_off = n * 64 + g * 16;  // the same piece of a cos/sin table row
 
   const bf16x8_t sel[2] = {select_operand(g, n, 0), select_operand(g, n, 1)};
   const bf16x8_t selp[2] = {partner_operand(g, n, 0), partner_operand(g, n, 1)};
@@ -483,16 +512,16 @@ __global__ __launch_bounds__(kThreads) void state_bf16(const u32x4_t* __restrict
   u32x4_t nk[4], nv[4];
   TileAnglesRows na[2];  // cos/sin rows of the two tiles (RoPE only)
   auto load_chunk = [&](int64_t c0) {
-    const rsrc_t rk = make_rsrc(Kh + c0 * 64, (n_end - c0) * 64);
-    const rsrc_t rv = make_rsrc(Vh + c0 * 64, (n_end - c0) * 64);
+    const rsrc_t rk = rows_rsrc(Kh, c0, n_end, row);
+    const rsrc_t rv = rows_rsrc(Vh, c0, n_end, row);
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
-      nk[h] = load16_nt(rk, lane_off + h * 1024);
-      nv[h] = load16_nt(rv, lane_off + h * 1024);
+      nk[h] = load16_nt(rk, lane_off + h * 16 * (int)row);
+      nv[h] = load16_nt(rv, lane_off + h * 16 * (int)row);
     }
     if constexpr (ROPE) {
-      load_angle_rows(cos_t, sin_t, pos0, c0, n_end, lane_off, na[0]);
-      load_angle_rows(cos_t, sin_t, pos0, c0 + 32, n_end, lane_off, na[1]);
+      load_angle_rows(cos_t, sin_t, pos0, c0, n_end, tab_off, na[0]);
+      load_angle_rows(cos_t, sin_t, pos0, c0 + 32, n_end, tab_off, na[1]);
     }
   };
   float* lds = angles[ROPE ? w : 0];
@@ -530,7 +559,7 @@ __global__ __launch_bounds__(kThreads) void state_bf16(const u32x4_t* __restrict
 // ---------------------------------------------------------------------------
 template <bool ROPE>
 __global__ __launch_bounds__(kThreads) void state_f32(const float* __restrict__ K, const float* __restrict__ V,
-                                                      const float* __restrict__ cos_t,
+                                                      Layout lkv, const float* __restrict__ cos_t,
                                                       const float* __restrict__ sin_t, int64_t pos0,
                                                       StateArgs a) {
   __shared__ float sk[64][kD + 1];   // phi(K), un-rotated
@@ -541,12 +570,11 @@ __global__ __launch_bounds__(kThreads) void state_f32(const float* __restrict__ 
   int64_t bh, n_begin, n_end;
   int c, s;
   state_item(a, bh, c, s, n_begin, n_end);
-  const int64_t N = a.N;
   const int t = threadIdx.x;
   const int d = t >> 3;
   const int e0 = (t & 7) * 4;
-  const float* Kh = K + bh * N * kD;
-  const float* Vh = V + bh * N * kD;
+  const float* Kh = K + lkv.base(bh);
+  const float* Vh = V + lkv.base(bh);
 
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   float zacc = 0.f;
@@ -560,10 +588,10 @@ __global__ __launch_bounds__(kThreads) void state_f32(const float* __restrict__ 
       const int64_t gt = t0 + tok;
       float k0 = 0.f, k1 = 0.f, v0 = 0.f, v1 = 0.f;
       if (gt < n_end) {
-        k0 = fmaxf(Kh[gt * kD + 2 * p], 0.f);
-        k1 = fmaxf(Kh[gt * kD + 2 * p + 1], 0.f);
-        v0 = Vh[gt * kD + 2 * p];
-        v1 = Vh[gt * kD + 2 * p + 1];
+        k0 = fmaxf(Kh[gt * lkv.token + 2 * p], 0.f);
+        k1 = fmaxf(Kh[gt * lkv.token + 2 * p + 1], 0.f);
+        v0 = Vh[gt * lkv.token + 2 * p];
+        v1 = Vh[gt * lkv.token + 2 * p + 1];
       }
       sk[tok][2 * p] = k0;
       sk[tok][2 * p + 1] = k1;
@@ -706,12 +734,12 @@ struct ApplyChunk {
 
 // Rows at or past n_end read 0; their outputs are not stored.
 template <bool ROPE>
-__device__ __forceinline__ void load_apply_chunk(const char* Qh, int64_t t0, int64_t n_end, int lane_off,
-                                                 const float* cos_t, const float* sin_t, int64_t pos0,
-                                                 ApplyChunk<ROPE>& ch) {
-  const rsrc_t rq = make_rsrc(Qh + t0 * 64, (n_end - t0) * 64);
+__device__ __forceinline__ void load_apply_chunk(const char* Qh, int64_t row, int64_t t0, int64_t n_end,
+                                                 int lane_off, int tab_off, const float* cos_t,
+                                                 const float* sin_t, int64_t pos0, ApplyChunk<ROPE>& ch) {
+  const rsrc_t rq = rows_rsrc(Qh, t0, n_end, row);
 #pragma unroll
-  for (int u = 0; u < 4; ++u) ch.q[u] = load16_nt(rq, lane_off + u * 1024);
+  for (int u = 0; u < 4; ++u) ch.q[u] = load16_nt(rq, lane_off + u * 16 * (int)row);
   if constexpr (ROPE) {
     // pairs 4g .. 4g+3 of the token at position pos0 + t0 + 16u + m: the same
     // lane offset in a 64-byte table row
@@ -719,22 +747,26 @@ __device__ __forceinline__ void load_apply_chunk(const char* Qh, int64_t t0, int
     const rsrc_t rs = make_rsrc(sin_t + (pos0 + t0) * 16, (n_end - t0) * 64);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      ch.c[u] = load16(rc, lane_off + u * 1024);
-      ch.sn[u] = load16(rs, lane_off + u * 1024);
+      ch.c[u] = load16(rc, tab_off + u * 1024);
+      ch.sn[u] = load16(rs, tab_off + u * 1024);
     }
   }
 }
 
-template <bool ROPE>
+template <bool ROPE, bool DENSE>
 __global__ __launch_bounds__(kThreads) void apply_bf16(const u32x4_t* __restrict__ Q, u32x4_t* __restrict__ O,
-                                                       StateView sv, int64_t N, int64_t L, int C, int64_t total,
-                                                       int64_t La, float eps, const float* __restrict__ cos_t,
+                                                       Layout lq, Layout lo, StateView sv, int64_t N, int64_t L,
+                                                       int C, int64_t total, int64_t La, float eps,
+                                                       const float* __restrict__ cos_t,
                                                        const float* __restrict__ sin_t, int64_t pos0) {
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int m = lane & 15;
   const int g = lane >> 4;
-  const int lane_off = m * 64 + g * 16;  // features 8g .. 8g+7 of tile row m
+  const int64_t qrow = DENSE ? 64 : lq.token * 2, orow = DENSE ? 64 : lo.token * 2;  // bytes between tokens
+  const int q_off = m * (int)qrow + g * 16;                // features 8g .. 8g+7 of tile row m
+  const int o_off = m * (int)orow + g * 16;
+  const int tab_off = m * 64 + g * 16;
   const int64_t f_begin = (int64_t)blockIdx.x * La;
   const int64_t f_end = (f_begin + La < total) ? f_begin + La : total;
 
@@ -746,25 +778,26 @@ __global__ __launch_bounds__(kThreads) void apply_bf16(const u32x4_t* __restrict
     const int64_t c_end = ((int64_t)c + 1) * L < N ? ((int64_t)c + 1) * L : N;
     const int64_t n_end = (f_end - bh * N < c_end) ? f_end - bh * N : c_end;
     f = bh * N + n_end;
-    const char* Qh = reinterpret_cast<const char*>(Q + bh * N * 4);  // 64-byte token rows
-    char* Oh = reinterpret_cast<char*>(O + bh * N * 4);
+    const char* Qh = reinterpret_cast<const char*>(Q) + lq.base(bh) * 2;
+    char* Oh = reinterpret_cast<char*>(O) + lo.base(bh) * 2;
 
     // the first chunk's loads go out before the state operands are fetched,
     // and each chunk's loads before the previous chunk is computed
     int64_t t0 = n_begin + 64 * w;
     ApplyChunk<ROPE> next;
-    if (t0 < n_end) load_apply_chunk<ROPE>(Qh, t0, n_end, lane_off, cos_t, sin_t, pos0, next);
+    if (t0 < n_end) load_apply_chunk<ROPE>(Qh, qrow, t0, n_end, q_off, tab_off, cos_t, sin_t, pos0, next);
     ApplyOperands op;
     const int64_t sc = bh * C + c;
     load_apply_operands(sv.s_base + sc * sv.s_stride, sv.z_base + sc * sv.z_stride, g, m, op);
 
     for (; t0 < n_end; t0 += 256) {
       const ApplyChunk<ROPE> cur = next;
-      if (t0 + 256 < n_end) load_apply_chunk<ROPE>(Qh, t0 + 256, n_end, lane_off, cos_t, sin_t, pos0, next);
-      const rsrc_t ro = make_rsrc(Oh + t0 * 64, (n_end - t0) * 64);
+      if (t0 + 256 < n_end)
+        load_apply_chunk<ROPE>(Qh, qrow, t0 + 256, n_end, q_off, tab_off, cos_t, sin_t, pos0, next);
+      const rsrc_t ro = rows_rsrc(Oh, t0, n_end, orow);
 #pragma unroll
       for (int u = 0; u < 4; ++u)
-        store16_nt(ro, lane_off + u * 1024, apply_tile<ROPE>(cur.q[u], op, eps, cur.c[u], cur.sn[u]));
+        store16_nt(ro, o_off + u * 16 * (int)orow, apply_tile<ROPE>(cur.q[u], op, eps, cur.c[u], cur.sn[u]));
     }
   }
 }
@@ -775,7 +808,8 @@ __global__ __launch_bounds__(kThreads) void apply_bf16(const u32x4_t* __restrict
 // Workgroup (bh, c, tile) applies tokens [c*L + tile*Lt, ...) of chunk c.
 template <bool ROPE>
 __global__ __launch_bounds__(kThreads) void apply_f32(const float* __restrict__ Q, float* __restrict__ O,
-                                                      StateView sv, int64_t N, int64_t L, int C, int T,
+                                                      Layout lq, Layout lo, StateView sv, int64_t N, int64_t L,
+                                                      int C, int T,
                                                       int64_t Lt, float eps, const float* __restrict__ cos_t,
                                                       const float* __restrict__ sin_t, int64_t pos0) {
   __shared__ float sS[kD][kD];
@@ -795,7 +829,7 @@ __global__ __launch_bounds__(kThreads) void apply_f32(const float* __restrict__ 
   const int tl = t >> 3;
   const int e0 = (t & 7) * 4;
   for (int64_t tok = n_begin + tl; tok < n_end; tok += 32) {
-    const float* qrow = Q + (bh * N + tok) * kD;
+    const float* qrow = Q + lq.base(bh) + tok * lq.token;
     float pq[kD], pr[kD];
 #pragma unroll
     for (int d = 0; d < kD; ++d) pq[d] = fmaxf(qrow[d], 0.f);
@@ -821,7 +855,7 @@ __global__ __launch_bounds__(kThreads) void apply_f32(const float* __restrict__ 
 #pragma unroll
       for (int c = 0; c < 4; ++c) num[c] = fmaf(pr[d], sS[d][e0 + c], num[c]);
     }
-    float* orow = O + (bh * N + tok) * kD + e0;
+    float* orow = O + lo.base(bh) + tok * lo.token + e0;
 #pragma unroll
     for (int c = 0; c < 4; ++c) orow[c] = num[c] / den;
   }

@@ -148,20 +148,75 @@ int check_workspace(const Geometry& g, const void* ws, size_t ws_bytes) {
 
 int check_tensor(const void* p) { return (p && aligned(p, 16)) ? SANA_OK : SANA_ERR_INVALID; }
 
+// A tensor's element layout and the bytes from its first element to one past
+// its last.
+struct View {
+  la::Layout lay;
+  size_t span = 0;
+};
+
+// Strides (stride, extent) nested without overlap: sorted by stride, each
+// stride at least the span of everything inside it (a row is D elements).
+bool injective(int64_t D, const int64_t (&stride)[3], const int64_t (&extent)[3]) {
+  int order[3] = {0, 1, 2};
+  for (int i = 0; i < 3; ++i)
+    for (int j = i + 1; j < 3; ++j)
+      if (stride[order[j]] < stride[order[i]]) {
+        const int t = order[i];
+        order[i] = order[j];
+        order[j] = t;
+      }
+  int64_t inner = D;
+  for (int i = 0; i < 3; ++i) {
+    const int a = order[i];
+    if (extent[a] <= 1) continue;
+    if (stride[a] < inner) return false;
+    inner = stride[a] * (extent[a] - 1) + inner;
+  }
+  return true;
+}
+
+// The view of a [B][H][N][D] tensor through `l` (NULL: contiguous).  Rows
+// (token starts) must be 16-byte aligned and at least D elements apart; the
+// bf16 kernels address a 64-token window with 32-bit offsets, so a row stride
+// is limited to 16 MiB.  Outputs must not map two elements to one address.
+int make_view(const sana_layout* l, int B, int H, int64_t N, int D, int es, bool output, View* v) {
+  if (!l) {
+    v->lay = la::Layout{(int64_t)H * N * D, N * D, D, H};
+  } else {
+    if (l->batch < 0 || l->head < 0 || l->token < D) return SANA_ERR_INVALID;
+    if ((l->batch * es) % 16 || (l->head * es) % 16 || (l->token * es) % 16) return SANA_ERR_INVALID;
+    if (l->token * es > ((int64_t)1 << 24)) return SANA_ERR_INVALID;
+    if (l->batch > (INT64_MAX / 4) / (B > 0 ? B : 1) || l->head > (INT64_MAX / 4) / (H > 0 ? H : 1) ||
+        l->token > (INT64_MAX / 4) / (N > 0 ? N : 1))
+      return SANA_ERR_INVALID;
+    if (output) {
+      const int64_t stride[3] = {l->batch, l->head, l->token}, extent[3] = {B, H, N};
+      if (!injective(D, stride, extent)) return SANA_ERR_INVALID;
+    }
+    v->lay = la::Layout{l->batch, l->head, l->token, H};
+  }
+  if (B > 0 && H > 0 && N > 0)
+    v->span = (size_t)(((int64_t)(B - 1) * v->lay.batch + (int64_t)(H - 1) * v->lay.head +
+                        (N - 1) * v->lay.token + D) * es);
+  return SANA_OK;
+}
+
 // q/k/v/o against one another and against the state buffers: o may not
 // overlap anything; among the states only exact in-place aliasing
 // (kv_out == kv_in, ksum_out == ksum_in) is allowed.
-int check_overlaps(const void* q, const void* k, const void* v, const void* o, size_t bytes, const float* kv_in,
-                   const float* ksum_in, const float* kv_out, const float* ksum_out, int64_t bh) {
-  if (overlaps(o, bytes, q, bytes) || overlaps(o, bytes, k, bytes) || overlaps(o, bytes, v, bytes))
+int check_overlaps(const void* q, const void* k, const void* v, const void* o, size_t in_span, size_t out_span,
+                   const float* kv_in, const float* ksum_in, const float* kv_out, const float* ksum_out, int64_t bh) {
+  if (overlaps(o, out_span, q, in_span) || overlaps(o, out_span, k, in_span) || overlaps(o, out_span, v, in_span))
     return SANA_ERR_INVALID;
   const size_t kv_bytes = (size_t)bh * 1024 * sizeof(float), ks_bytes = (size_t)bh * 32 * sizeof(float);
   const void* tensors[4] = {q, k, v, o};
+  const size_t spans[4] = {in_span, in_span, in_span, out_span};
   const void* states[4] = {kv_in, ksum_in, kv_out, ksum_out};
   const size_t state_sizes[4] = {kv_bytes, ks_bytes, kv_bytes, ks_bytes};
   for (int i = 0; i < 4; ++i)
     for (int j = 0; j < 4; ++j)
-      if (overlaps(states[i], state_sizes[i], tensors[j], bytes)) return SANA_ERR_INVALID;
+      if (overlaps(states[i], state_sizes[i], tensors[j], spans[j])) return SANA_ERR_INVALID;
   if (overlaps(kv_in, kv_bytes, ksum_in, ks_bytes) || overlaps(kv_out, kv_bytes, ksum_out, ks_bytes) ||
       overlaps(kv_in, kv_bytes, ksum_out, ks_bytes) || overlaps(ksum_in, ks_bytes, kv_out, kv_bytes))
     return SANA_ERR_INVALID;
@@ -193,8 +248,8 @@ la::StateView ws_view(const la::StateArgs& a) {
 }
 
 // State pass, and the finalize when there are several partials per head.
-void launch_state(const void* k, const void* v, int dtype, const Geometry& g, const sana_rope* rope,
-                  const la::StateArgs& a, hipStream_t st) {
+void launch_state(const void* k, const void* v, const la::Layout& lkv, int dtype, const Geometry& g,
+                  const sana_rope* rope, const la::StateArgs& a, hipStream_t st) {
   const float* ct = rope ? rope->cos : nullptr;
   const float* sn = rope ? rope->sin : nullptr;
   const int64_t pos0 = rope ? rope->pos_offset : 0;
@@ -202,17 +257,22 @@ void launch_state(const void* k, const void* v, int dtype, const Geometry& g, co
   if (dtype == SANA_DT_BF16) {
     const la::u32x4_t* K = static_cast<const la::u32x4_t*>(k);
     const la::u32x4_t* V = static_cast<const la::u32x4_t*>(v);
-    if (rope)
-      la::state_bf16<true><<<grid, block, 0, st>>>(K, V, ct, sn, pos0, a);
+    const bool dense = lkv.token == la::kD;
+    if (rope && dense)
+      la::state_bf16<true, true><<<grid, block, 0, st>>>(K, V, lkv, ct, sn, pos0, a);
+    else if (rope)
+      la::state_bf16<true, false><<<grid, block, 0, st>>>(K, V, lkv, ct, sn, pos0, a);
+    else if (dense)
+      la::state_bf16<false, true><<<grid, block, 0, st>>>(K, V, lkv, ct, sn, pos0, a);
     else
-      la::state_bf16<false><<<grid, block, 0, st>>>(K, V, ct, sn, pos0, a);
+      la::state_bf16<false, false><<<grid, block, 0, st>>>(K, V, lkv, ct, sn, pos0, a);
   } else {
     const float* K = static_cast<const float*>(k);
     const float* V = static_cast<const float*>(v);
     if (rope)
-      la::state_f32<true><<<grid, block, 0, st>>>(K, V, ct, sn, pos0, a);
+      la::state_f32<true><<<grid, block, 0, st>>>(K, V, lkv, ct, sn, pos0, a);
     else
-      la::state_f32<false><<<grid, block, 0, st>>>(K, V, ct, sn, pos0, a);
+      la::state_f32<false><<<grid, block, 0, st>>>(K, V, lkv, ct, sn, pos0, a);
   }
   if (g.C * g.Pc > 1) {
     const int64_t n_elems = g.BH * la::kStateElems;
@@ -220,7 +280,8 @@ void launch_state(const void* k, const void* v, int dtype, const Geometry& g, co
   }
 }
 
-void launch_apply(const void* q, void* o, int dtype, float eps, const Geometry& g, const sana_rope* rope,
+void launch_apply(const void* q, void* o, const la::Layout& lq, const la::Layout& lo, int dtype, float eps,
+                  const Geometry& g, const sana_rope* rope,
                   const la::StateView& sv, hipStream_t st) {
   const float* ct = rope ? rope->cos : nullptr;
   const float* sn = rope ? rope->sin : nullptr;
@@ -229,18 +290,29 @@ void launch_apply(const void* q, void* o, int dtype, float eps, const Geometry& 
     const dim3 grid((unsigned)g.Ga), block(la::kThreads);
     const la::u32x4_t* Q = static_cast<const la::u32x4_t*>(q);
     la::u32x4_t* O = static_cast<la::u32x4_t*>(o);
-    if (rope)
-      la::apply_bf16<true><<<grid, block, 0, st>>>(Q, O, sv, g.N, g.L, (int)g.C, g.BH * g.N, g.La, eps, ct, sn, pos0);
+    const bool dense = lq.token == la::kD && lo.token == la::kD;
+#define LA_APPLY(R, DN)                                                                                       \
+  la::apply_bf16<R, DN><<<grid, block, 0, st>>>(Q, O, lq, lo, sv, g.N, g.L, (int)g.C, g.BH * g.N, g.La, eps, ct, sn, \
+                                                pos0)
+    if (rope && dense)
+      LA_APPLY(true, true);
+    else if (rope)
+      LA_APPLY(true, false);
+    else if (dense)
+      LA_APPLY(false, true);
     else
-      la::apply_bf16<false><<<grid, block, 0, st>>>(Q, O, sv, g.N, g.L, (int)g.C, g.BH * g.N, g.La, eps, ct, sn, pos0);
+      LA_APPLY(false, false);
+#undef LA_APPLY
   } else {
     const dim3 grid((unsigned)(g.BH * g.C * g.T)), block(la::kThreads);
     const float* Q = static_cast<const float*>(q);
     float* O = static_cast<float*>(o);
     if (rope)
-      la::apply_f32<true><<<grid, block, 0, st>>>(Q, O, sv, g.N, g.L, (int)g.C, (int)g.T, g.Lt, eps, ct, sn, pos0);
+      la::apply_f32<true><<<grid, block, 0, st>>>(Q, O, lq, lo, sv, g.N, g.L, (int)g.C, (int)g.T, g.Lt, eps, ct, sn,
+                                                 pos0);
     else
-      la::apply_f32<false><<<grid, block, 0, st>>>(Q, O, sv, g.N, g.L, (int)g.C, (int)g.T, g.Lt, eps, ct, sn, pos0);
+      la::apply_f32<false><<<grid, block, 0, st>>>(Q, O, lq, lo, sv, g.N, g.L, (int)g.C, (int)g.T, g.Lt, eps, ct, sn,
+                                                 pos0);
   }
 }
 
@@ -248,9 +320,10 @@ int launch_status() { return hipGetLastError() == hipSuccess ? SANA_OK : SANA_ER
 
 // Shared body of forward, block_forward and block_causal: chunks of L tokens
 // (L >= N for one chunk), carried state in, optional commit out.
-int attend(const void* q, const void* k, const void* v, void* o, const float* kv_in, const float* ksum_in,
-           float* kv_out, float* ksum_out, int B, int H, int64_t N, int64_t L, int D, int dtype, float eps,
-           const sana_rope* rope, void* ws, size_t ws_bytes, void* hip_stream) {
+int attend(const void* q, const void* k, const void* v, void* o, const sana_layout* in, const sana_layout* out,
+           const float* kv_in, const float* ksum_in, float* kv_out, float* ksum_out, int B, int H, int64_t N,
+           int64_t L, int D, int dtype, float eps, const sana_rope* rope, void* ws, size_t ws_bytes,
+           void* hip_stream) {
   int64_t bh = 0, elems = 0;
   int rc = check_sizes(B, H, N, D, dtype, &bh, &elems);
   if (rc != SANA_OK) return rc;
@@ -263,22 +336,26 @@ int attend(const void* q, const void* k, const void* v, void* o, const float* kv
   if ((kv_in && (!aligned(kv_in, 4) || !aligned(ksum_in, 4))) ||
       (kv_out && (!aligned(kv_out, 4) || !aligned(ksum_out, 4))))
     return SANA_ERR_INVALID;
-  const size_t bytes = (size_t)elems * elem_size(dtype);
-  if ((rc = check_overlaps(q, k, v, o, bytes, kv_in, ksum_in, kv_out, ksum_out, bh)) != SANA_OK) return rc;
+  View vin, vout;
+  if ((rc = make_view(in, B, H, N, D, elem_size(dtype), false, &vin)) != SANA_OK) return rc;
+  if ((rc = make_view(out, B, H, N, D, elem_size(dtype), true, &vout)) != SANA_OK) return rc;
+  if ((rc = check_overlaps(q, k, v, o, vin.span, vout.span, kv_in, ksum_in, kv_out, ksum_out, bh)) != SANA_OK)
+    return rc;
   if ((rc = check_rope(rope, N)) != SANA_OK) return rc;
   const Geometry g = make_geometry(bh, N, L, rope != nullptr);
   if ((rc = check_workspace(g, ws, ws_bytes)) != SANA_OK) return rc;
 
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   const la::StateArgs a = state_args(ws, g, kv_in, ksum_in, kv_out, ksum_out);
-  launch_state(k, v, dtype, g, rope, a, st);
-  launch_apply(q, o, dtype, eps, g, rope, ws_view(a), st);
+  launch_state(k, v, vin.lay, dtype, g, rope, a, st);
+  launch_apply(q, o, vin.lay, vout.lay, dtype, eps, g, rope, ws_view(a), st);
   return launch_status();
 }
 
 // Key pass of the backward: dK, dV from the state gradient G_c of every chunk.
-void launch_key_pass(const void* k, const void* v, void* dk, void* dv, int dtype, const Geometry& g,
-                     const sana_rope* rope, const la::StateView& view, hipStream_t st) {
+void launch_key_pass(const void* k, const void* v, void* dk, void* dv, const la::Layout& lin,
+                     const la::Layout& lout, int dtype, const Geometry& g, const sana_rope* rope,
+                     const la::StateView& view, hipStream_t st) {
   const float* ct = rope ? rope->cos : nullptr;
   const float* sn = rope ? rope->sin : nullptr;
   const int64_t pos0 = rope ? rope->pos_offset : 0;
@@ -289,12 +366,19 @@ void launch_key_pass(const void* k, const void* v, void* dk, void* dv, int dtype
     const auto* V = static_cast<const la::u32x4_t*>(v);
     auto* dK = static_cast<la::u32x4_t*>(dk);
     auto* dV = static_cast<la::u32x4_t*>(dv);
-    if (rope)
-      la::bwd_key_bf16<true><<<kgrid, block, 0, st>>>(K, V, dK, dV, view, g.N, g.L, (int)g.C, g.BH * g.N, g.La, ct,
-                                                        sn, pos0);
+    const bool dense = lin.token == la::kD && lout.token == la::kD;
+#define LA_KEY(R, DN)                                                                                        \
+  la::bwd_key_bf16<R, DN><<<kgrid, block, 0, st>>>(K, V, dK, dV, lin, lout, view, g.N, g.L, (int)g.C, g.BH * g.N, \
+                                                   g.La, ct, sn, pos0)
+    if (rope && dense)
+      LA_KEY(true, true);
+    else if (rope)
+      LA_KEY(true, false);
+    else if (dense)
+      LA_KEY(false, true);
     else
-      la::bwd_key_bf16<false><<<kgrid, block, 0, st>>>(K, V, dK, dV, view, g.N, g.L, (int)g.C, g.BH * g.N, g.La,
-                                                         ct, sn, pos0);
+      LA_KEY(false, false);
+#undef LA_KEY
   } else {
     const dim3 kgrid((unsigned)(g.BH * g.C * g.T));
     const auto* K = static_cast<const float*>(k);
@@ -302,10 +386,10 @@ void launch_key_pass(const void* k, const void* v, void* dk, void* dv, int dtype
     auto* dK = static_cast<float*>(dk);
     auto* dV = static_cast<float*>(dv);
     if (rope)
-      la::bwd_key_vec<float, true><<<kgrid, block, 0, st>>>(K, V, dK, dV, view, g.N, g.L, (int)g.C, (int)g.T, g.Lt,
+      la::bwd_key_vec<float, true><<<kgrid, block, 0, st>>>(K, V, dK, dV, lin, lout, view, g.N, g.L, (int)g.C, (int)g.T, g.Lt,
                                                               ct, sn, pos0);
     else
-      la::bwd_key_vec<float, false><<<kgrid, block, 0, st>>>(K, V, dK, dV, view, g.N, g.L, (int)g.C, (int)g.T,
+      la::bwd_key_vec<float, false><<<kgrid, block, 0, st>>>(K, V, dK, dV, lin, lout, view, g.N, g.L, (int)g.C, (int)g.T,
                                                                g.Lt, ct, sn, pos0);
   }
 }
@@ -316,7 +400,7 @@ void launch_key_pass(const void* k, const void* v, void* dk, void* dv, int dtype
 // forward's: the query pass reuses the partials, the reverse finalize
 // overwrites the chunk states with G_c once the query pass has read them.
 void launch_backward(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk, void* dv,
-                     int dtype, float eps, const Geometry& g, const sana_rope* rope, const la::StateArgs& fwd,
+                     const la::Layout& lin, const la::Layout& lout, int dtype, float eps, const Geometry& g, const sana_rope* rope, const la::StateArgs& fwd,
                      const la::StateArgs& bwd, hipStream_t st) {
   const float* ct = rope ? rope->cos : nullptr;
   const float* sn = rope ? rope->sin : nullptr;
@@ -328,24 +412,29 @@ void launch_backward(const void* q, const void* k, const void* v, const void* do
     const auto* Q = static_cast<const la::u32x4_t*>(q);
     const auto* dO = static_cast<const la::u32x4_t*>(dout);
     auto* dQ = static_cast<la::u32x4_t*>(dq);
-    if (rope)
-      la::bwd_query_bf16<true><<<qgrid, block, 0, st>>>(Q, dO, dQ, view, eps, ct, sn, pos0, bwd);
+    const bool dense = lin.token == la::kD && lout.token == la::kD;
+    if (rope && dense)
+      la::bwd_query_bf16<true, true><<<qgrid, block, 0, st>>>(Q, dO, dQ, lin, lout, view, eps, ct, sn, pos0, bwd);
+    else if (rope)
+      la::bwd_query_bf16<true, false><<<qgrid, block, 0, st>>>(Q, dO, dQ, lin, lout, view, eps, ct, sn, pos0, bwd);
+    else if (dense)
+      la::bwd_query_bf16<false, true><<<qgrid, block, 0, st>>>(Q, dO, dQ, lin, lout, view, eps, ct, sn, pos0, bwd);
     else
-      la::bwd_query_bf16<false><<<qgrid, block, 0, st>>>(Q, dO, dQ, view, eps, ct, sn, pos0, bwd);
+      la::bwd_query_bf16<false, false><<<qgrid, block, 0, st>>>(Q, dO, dQ, lin, lout, view, eps, ct, sn, pos0, bwd);
   } else {
     const auto* Q = static_cast<const float*>(q);
     const auto* dO = static_cast<const float*>(dout);
     auto* dQ = static_cast<float*>(dq);
     if (rope)
-      la::bwd_query_vec<float, true><<<qgrid, block, 0, st>>>(Q, dO, dQ, view, eps, ct, sn, pos0, bwd);
+      la::bwd_query_vec<float, true><<<qgrid, block, 0, st>>>(Q, dO, dQ, lin, lout, view, eps, ct, sn, pos0, bwd);
     else
-      la::bwd_query_vec<float, false><<<qgrid, block, 0, st>>>(Q, dO, dQ, view, eps, ct, sn, pos0, bwd);
+      la::bwd_query_vec<float, false><<<qgrid, block, 0, st>>>(Q, dO, dQ, lin, lout, view, eps, ct, sn, pos0, bwd);
   }
   if (g.C * g.Pc > 1) {
     const int64_t n_elems = g.BH * la::kStateElems;
     la::state_finalize_reverse<<<dim3((unsigned)ceil_div(n_elems, la::kThreads)), block, 0, st>>>(bwd, n_elems);
   }
-  launch_key_pass(k, v, dk, dv, dtype, g, rope, view, st);
+  launch_key_pass(k, v, dk, dv, lin, lout, dtype, g, rope, view, st);
 }
 
 bool state_pair_ok(const float* s, const float* z) {
@@ -354,7 +443,7 @@ bool state_pair_ok(const float* s, const float* z) {
 }
 
 int backward(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk, void* dv,
-             const float* kv_in, const float* ksum_in, const float* dkv_out, const float* dksum_out, float* dkv_in,
+             const sana_layout* in, const sana_layout* out, const float* kv_in, const float* ksum_in, const float* dkv_out, const float* dksum_out, float* dkv_in,
              float* dksum_in, int B, int H, int64_t N, int64_t L, int D, int dtype, float eps,
              const sana_rope* rope, void* ws, size_t ws_bytes, void* hip_stream) {
   int64_t bh = 0, elems = 0;
@@ -371,7 +460,10 @@ int backward(const void* q, const void* k, const void* v, const void* dout, void
     if (check_tensor(p)) return SANA_ERR_INVALID;
   for (void* p : outputs)
     if (check_tensor(p)) return SANA_ERR_INVALID;
-  const size_t bytes = (size_t)elems * elem_size(dtype);
+  View vin, vout;
+  if ((rc = make_view(in, B, H, N, D, elem_size(dtype), false, &vin)) != SANA_OK) return rc;
+  if ((rc = make_view(out, B, H, N, D, elem_size(dtype), true, &vout)) != SANA_OK) return rc;
+  const size_t ibytes = vin.span, obytes = vout.span;
   const size_t kv_bytes = (size_t)bh * 1024 * sizeof(float), ks_bytes = (size_t)bh * 32 * sizeof(float);
   // outputs overlap nothing; state gradients overlap no tensor, and dkv_in may
   // only alias dkv_out exactly (likewise the key sums)
@@ -379,15 +471,15 @@ int backward(const void* q, const void* k, const void* v, const void* dout, void
   const size_t state_sizes[6] = {kv_bytes, ks_bytes, kv_bytes, ks_bytes, kv_bytes, ks_bytes};
   for (int i = 0; i < 3; ++i) {
     for (int j = 0; j < 4; ++j)
-      if (overlaps(outputs[i], bytes, inputs[j], bytes)) return SANA_ERR_INVALID;
+      if (overlaps(outputs[i], obytes, inputs[j], ibytes)) return SANA_ERR_INVALID;
     for (int j = i + 1; j < 3; ++j)
-      if (overlaps(outputs[i], bytes, outputs[j], bytes)) return SANA_ERR_INVALID;
+      if (overlaps(outputs[i], obytes, outputs[j], obytes)) return SANA_ERR_INVALID;
     for (int j = 0; j < 6; ++j)
-      if (overlaps(outputs[i], bytes, states[j], state_sizes[j])) return SANA_ERR_INVALID;
+      if (overlaps(outputs[i], obytes, states[j], state_sizes[j])) return SANA_ERR_INVALID;
   }
   for (int i = 0; i < 6; ++i)
     for (int j = 0; j < 4; ++j)
-      if (overlaps(states[i], state_sizes[i], inputs[j], bytes)) return SANA_ERR_INVALID;
+      if (overlaps(states[i], state_sizes[i], inputs[j], ibytes)) return SANA_ERR_INVALID;
   for (int i = 0; i < 6; ++i)
     for (int j = i + 1; j < 6; ++j) {
       if (!overlaps(states[i], state_sizes[i], states[j], state_sizes[j])) continue;
@@ -401,8 +493,8 @@ int backward(const void* q, const void* k, const void* v, const void* dout, void
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   const la::StateArgs fwd = state_args(ws, g, kv_in, ksum_in, nullptr, nullptr);
   const la::StateArgs bwd = state_args(ws, g, dkv_out, dksum_out, dkv_in, dksum_in);
-  launch_state(k, v, dtype, g, rope, fwd, st);
-  launch_backward(q, k, v, dout, dq, dk, dv, dtype, eps, g, rope, fwd, bwd, st);
+  launch_state(k, v, vin.lay, dtype, g, rope, fwd, st);
+  launch_backward(q, k, v, dout, dq, dk, dv, vin.lay, vout.lay, dtype, eps, g, rope, fwd, bwd, st);
   return launch_status();
 }
 
@@ -428,24 +520,49 @@ size_t sana_linattn_block_causal_workspace_bytes(int B, int H, int64_t N, int64_
 int sana_linattn_forward(const void* q, const void* k, const void* v, void* o, int B, int H, int64_t N, int D,
                          int dtype, float eps, const sana_rope* rope, void* ws, size_t ws_bytes,
                          void* hip_stream) {
-  return attend(q, k, v, o, nullptr, nullptr, nullptr, nullptr, B, H, N, N > 0 ? N : 1, D, dtype, eps, rope, ws,
-                ws_bytes, hip_stream);
+  return attend(q, k, v, o, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, B, H, N, N > 0 ? N : 1, D, dtype,
+                eps, rope, ws, ws_bytes, hip_stream);
+}
+
+int sana_linattn_forward_strided(const void* q, const void* k, const void* v, void* o, const sana_layout* in,
+                                 const sana_layout* out, int B, int H, int64_t N, int D, int dtype, float eps,
+                                 const sana_rope* rope, void* ws, size_t ws_bytes, void* hip_stream) {
+  return attend(q, k, v, o, in, out, nullptr, nullptr, nullptr, nullptr, B, H, N, N > 0 ? N : 1, D, dtype, eps,
+                rope, ws, ws_bytes, hip_stream);
 }
 
 int sana_linattn_block_forward(const void* q, const void* k, const void* v, void* o, const float* kv_in,
                                const float* ksum_in, float* kv_out, float* ksum_out, int B, int H, int64_t N,
                                int D, int dtype, float eps, const sana_rope* rope, void* ws, size_t ws_bytes,
                                void* hip_stream) {
-  return attend(q, k, v, o, kv_in, ksum_in, kv_out, ksum_out, B, H, N, N > 0 ? N : 1, D, dtype, eps, rope, ws,
-                ws_bytes, hip_stream);
+  return attend(q, k, v, o, nullptr, nullptr, kv_in, ksum_in, kv_out, ksum_out, B, H, N, N > 0 ? N : 1, D, dtype,
+                eps, rope, ws, ws_bytes, hip_stream);
+}
+
+int sana_linattn_block_forward_strided(const void* q, const void* k, const void* v, void* o, const sana_layout* in,
+                                       const sana_layout* out, const float* kv_in, const float* ksum_in,
+                                       float* kv_out, float* ksum_out, int B, int H, int64_t N, int D, int dtype,
+                                       float eps, const sana_rope* rope, void* ws, size_t ws_bytes,
+                                       void* hip_stream) {
+  return attend(q, k, v, o, in, out, kv_in, ksum_in, kv_out, ksum_out, B, H, N, N > 0 ? N : 1, D, dtype, eps, rope,
+                ws, ws_bytes, hip_stream);
 }
 
 int sana_linattn_block_causal(const void* q, const void* k, const void* v, void* o, const float* kv_in,
                               const float* ksum_in, float* kv_out, float* ksum_out, int B, int H, int64_t N,
                               int64_t chunk, int D, int dtype, float eps, const sana_rope* rope, void* ws,
                               size_t ws_bytes, void* hip_stream) {
-  return attend(q, k, v, o, kv_in, ksum_in, kv_out, ksum_out, B, H, N, chunk, D, dtype, eps, rope, ws, ws_bytes,
-                hip_stream);
+  return attend(q, k, v, o, nullptr, nullptr, kv_in, ksum_in, kv_out, ksum_out, B, H, N, chunk, D, dtype, eps, rope,
+                ws, ws_bytes, hip_stream);
+}
+
+int sana_linattn_block_causal_strided(const void* q, const void* k, const void* v, void* o, const sana_layout* in,
+                                      const sana_layout* out, const float* kv_in, const float* ksum_in,
+                                      float* kv_out, float* ksum_out, int B, int H, int64_t N, int64_t chunk, int D,
+                                      int dtype, float eps, const sana_rope* rope, void* ws, size_t ws_bytes,
+                                      void* hip_stream) {
+  return attend(q, k, v, o, in, out, kv_in, ksum_in, kv_out, ksum_out, B, H, N, chunk, D, dtype, eps, rope, ws,
+                ws_bytes, hip_stream);
 }
 
 size_t sana_linattn_backward_workspace_bytes(int B, int H, int64_t N, int64_t chunk, int D, int dtype,
@@ -458,8 +575,17 @@ int sana_linattn_backward(const void* q, const void* k, const void* v, const voi
                           const float* dksum_out, float* dkv_in, float* dksum_in, int B, int H, int64_t N,
                           int64_t chunk, int D, int dtype, float eps, const sana_rope* rope, void* ws,
                           size_t ws_bytes, void* hip_stream) {
-  return backward(q, k, v, dout, dq, dk, dv, kv_in, ksum_in, dkv_out, dksum_out, dkv_in, dksum_in, B, H, N, chunk,
-                  D, dtype, eps, rope, ws, ws_bytes, hip_stream);
+  return backward(q, k, v, dout, dq, dk, dv, nullptr, nullptr, kv_in, ksum_in, dkv_out, dksum_out, dkv_in, dksum_in,
+                  B, H, N, chunk, D, dtype, eps, rope, ws, ws_bytes, hip_stream);
+}
+
+int sana_linattn_backward_strided(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk,
+                                  void* dv, const sana_layout* in, const sana_layout* out, const float* kv_in,
+                                  const float* ksum_in, const float* dkv_out, const float* dksum_out, float* dkv_in,
+                                  float* dksum_in, int B, int H, int64_t N, int64_t chunk, int D, int dtype,
+                                  float eps, const sana_rope* rope, void* ws, size_t ws_bytes, void* hip_stream) {
+  return backward(q, k, v, dout, dq, dk, dv, in, out, kv_in, ksum_in, dkv_out, dksum_out, dkv_in, dksum_in, B, H, N,
+                  chunk, D, dtype, eps, rope, ws, ws_bytes, hip_stream);
 }
 
 int sana_linattn_state_update_backward(const void* k, const void* v, const float* dkv, const float* dksum,
@@ -481,7 +607,8 @@ int sana_linattn_state_update_backward(const void* k, const void* v, const float
   if ((rc = check_rope(rope, N)) != SANA_OK) return rc;
   const Geometry g = make_geometry(bh, N, N, rope != nullptr);
   if (!grids_fit(g)) return SANA_ERR_INVALID;
-  launch_key_pass(k, v, dk, dv, dtype, g, rope, la::StateView{dkv, dksum, 1024, 32},
+  const la::Layout flat{(int64_t)H * N * D, N * D, D, H};
+  launch_key_pass(k, v, dk, dv, flat, flat, dtype, g, rope, la::StateView{dkv, dksum, 1024, 32},
                   static_cast<hipStream_t>(hip_stream));
   return launch_status();
 }
@@ -506,7 +633,8 @@ int sana_linattn_state_update(const void* k, const void* v, float* kv_state, flo
   if ((rc = check_workspace(g, ws, ws_bytes)) != SANA_OK) return rc;
 
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
-  launch_state(k, v, dtype, g, rope, state_args(ws, g, kv_state, ksum_state, kv_state, ksum_state), st);
+  const la::Layout flat{(int64_t)H * N * D, N * D, D, H};
+  launch_state(k, v, flat, dtype, g, rope, state_args(ws, g, kv_state, ksum_state, kv_state, ksum_state), st);
   return launch_status();
 }
 
@@ -526,7 +654,8 @@ int sana_linattn_apply(const void* q, void* o, const float* kv_state, const floa
   if ((rc = check_rope(rope, N)) != SANA_OK) return rc;
   const Geometry g = make_geometry(bh, N, N, rope != nullptr);
   if (!grids_fit(g)) return SANA_ERR_INVALID;
-  launch_apply(q, o, dtype, eps, g, rope, la::StateView{kv_state, ksum_state, 1024, 32},
+  const la::Layout flat{(int64_t)H * N * D, N * D, D, H};
+  launch_apply(q, o, flat, flat, dtype, eps, g, rope, la::StateView{kv_state, ksum_state, 1024, 32},
                static_cast<hipStream_t>(hip_stream));
   return launch_status();
 }

@@ -244,3 +244,30 @@ def test_backward_argument_errors_and_workspace():
     assert bw(nbytes=la.workspace_bytes(1, 2, 640)) == la.SANA_ERR_WORKSPACE
     assert bw(q=None, k=None, v=None, do=None, dq=None, dk=None, dv=None, N=0, ws=None) == la.SANA_OK
     assert span < 0x01000000
+
+
+def test_strided_layout_validation():
+    """Layout errors come back before anything is launched; a valid packed
+    layout passes the checks and is stopped by the undersized workspace."""
+    L = la.lib()
+    B, H, N, D = 1, 4, 256, 32
+    packed = la.sana_layout(N * 3 * H * D, D, 3 * H * D)      # q/k/v of a [B, N, 3, H, D] buffer
+    bnhd = la.sana_layout(N * H * D, D, H * D)                 # [B, N, H, D]
+    QKV = 0x10000000
+    q, k, v = QKV, QKV + H * D * 2, QKV + 2 * H * D * 2
+    O = 0x20000000
+    def fwd(lin, lout, o=O, nbytes=16):
+        return L.sana_linattn_forward_strided(q, k, v, o, ctypes.byref(lin) if lin else None,
+                                              ctypes.byref(lout) if lout else None, B, H, N, D, la.SANA_DT_BF16,
+                                              1e-6, None, WS, nbytes, None)
+
+    assert fwd(packed, bnhd) == la.SANA_ERR_WORKSPACE          # accepted, then stopped by the workspace
+    assert fwd(None, None, o=0x30000000) == la.SANA_ERR_WORKSPACE  # inputs may overlap one another
+    assert fwd(la.sana_layout(N * 3 * H * D, D, 16), bnhd) == la.SANA_ERR_INVALID      # token stride < D
+    assert fwd(la.sana_layout(N * 3 * H * D, D, 3 * H * D + 1), bnhd) == la.SANA_ERR_INVALID   # rows not 16-B aligned
+    assert fwd(la.sana_layout(N * 3 * H * D, 33, 3 * H * D), bnhd) == la.SANA_ERR_INVALID      # head stride unaligned
+    assert fwd(la.sana_layout(-1, D, 3 * H * D), bnhd) == la.SANA_ERR_INVALID          # negative stride
+    assert fwd(la.sana_layout(0, D, 1 << 24), bnhd) == la.SANA_ERR_INVALID             # 32 MiB row stride
+    assert fwd(packed, la.sana_layout(N * H * D, 0, H * D)) == la.SANA_ERR_INVALID      # heads of o alias
+    assert fwd(packed, la.sana_layout(N * H * D, D, D)) == la.SANA_ERR_INVALID          # tokens of o overlap heads
+    assert fwd(packed, bnhd, o=QKV + 64) == la.SANA_ERR_INVALID                         # o inside the inputs' span
