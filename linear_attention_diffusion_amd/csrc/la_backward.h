@@ -29,21 +29,12 @@
 namespace la {
 
 // ---------------------------------------------------------------------------
-// Element I/O: four consecutive features as fp32
+// fp32 element I/O: four consecutive features
 // ---------------------------------------------------------------------------
 
 __device__ __forceinline__ f32x4_t load4(const float* p) { return *reinterpret_cast<const f32x4_t*>(p); }
 
-__device__ __forceinline__ f32x4_t load4(const __bf16* p) {
-  const uint2 w = *reinterpret_cast<const uint2*>(p);
-  return f32x4_t{bf16lo_to_f32(w.x), bf16hi_to_f32(w.x), bf16lo_to_f32(w.y), bf16hi_to_f32(w.y)};
-}
-
 __device__ __forceinline__ void store4(float* p, f32x4_t x) { *reinterpret_cast<f32x4_t*>(p) = x; }
-
-__device__ __forceinline__ void store4(__bf16* p, f32x4_t x) {
-  *reinterpret_cast<uint2*>(p) = uint2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
-}
 
 // Sum over the 8 consecutive lanes that share a token
 __device__ __forceinline__ float sum8(float x) {
@@ -110,9 +101,9 @@ __global__ __launch_bounds__(kThreads) void state_finalize_reverse(StateArgs a, 
 // item; a.kv_out/ksum_out: where that case commits dS_in).  32-token tiles:
 // thread t handles features f0 = 4 (t % 8) .. f0+3 of token t / 8 of the
 // tile, and element row d = t / 8, columns f0 .. f0+3 of the partial dS.
-template <typename T, bool ROPE>
-__global__ __launch_bounds__(kThreads) void bwd_query_vec(const T* __restrict__ Q, const T* __restrict__ dO,
-                                                          T* __restrict__ dQ, Layout lin, Layout lout,
+template <bool ROPE>
+__global__ __launch_bounds__(kThreads) void bwd_query_vec(const float* __restrict__ Q, const float* __restrict__ dO,
+                                                          float* __restrict__ dQ, Layout lin, Layout lout,
                                                           StateView fwd, float eps,
                                                           const float* __restrict__ cos_t,
                                                           const float* __restrict__ sin_t, int64_t pos0,
@@ -216,9 +207,9 @@ __global__ __launch_bounds__(kThreads) void bwd_query_vec(const T* __restrict__ 
 //
 // Workgroup (head, chunk, tile) takes tokens [c*L + tile*Lt, ...) of chunk c;
 // 32-token tiles, thread t: features f0 = 4 (t % 8) .. f0+3 of token t / 8.
-template <typename T, bool ROPE>
-__global__ __launch_bounds__(kThreads) void bwd_key_vec(const T* __restrict__ K, const T* __restrict__ V,
-                                                        T* __restrict__ dK, T* __restrict__ dV, Layout lin,
+template <bool ROPE>
+__global__ __launch_bounds__(kThreads) void bwd_key_vec(const float* __restrict__ K, const float* __restrict__ V,
+                                                        float* __restrict__ dK, float* __restrict__ dV, Layout lin,
                                                         Layout lout, StateView grad,
                                                         int64_t N, int64_t L, int C, int tiles, int64_t Lt,
                                                         const float* __restrict__ cos_t,

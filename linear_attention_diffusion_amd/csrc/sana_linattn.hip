@@ -386,10 +386,10 @@ void launch_key_pass(const void* k, const void* v, void* dk, void* dv, const la:
     auto* dK = static_cast<float*>(dk);
     auto* dV = static_cast<float*>(dv);
     if (rope)
-      la::bwd_key_vec<float, true><<<kgrid, block, 0, st>>>(K, V, dK, dV, lin, lout, view, g.N, g.L, (int)g.C, (int)g.T, g.Lt,
+      la::bwd_key_vec<true><<<kgrid, block, 0, st>>>(K, V, dK, dV, lin, lout, view, g.N, g.L, (int)g.C, (int)g.T, g.Lt,
                                                               ct, sn, pos0);
     else
-      la::bwd_key_vec<float, false><<<kgrid, block, 0, st>>>(K, V, dK, dV, lin, lout, view, g.N, g.L, (int)g.C, (int)g.T,
+      la::bwd_key_vec<false><<<kgrid, block, 0, st>>>(K, V, dK, dV, lin, lout, view, g.N, g.L, (int)g.C, (int)g.T,
                                                                g.Lt, ct, sn, pos0);
   }
 }
@@ -426,9 +426,9 @@ void launch_backward(const void* q, const void* k, const void* v, const void* do
     const auto* dO = static_cast<const float*>(dout);
     auto* dQ = static_cast<float*>(dq);
     if (rope)
-      la::bwd_query_vec<float, true><<<qgrid, block, 0, st>>>(Q, dO, dQ, lin, lout, view, eps, ct, sn, pos0, bwd);
+      la::bwd_query_vec<true><<<qgrid, block, 0, st>>>(Q, dO, dQ, lin, lout, view, eps, ct, sn, pos0, bwd);
     else
-      la::bwd_query_vec<float, false><<<qgrid, block, 0, st>>>(Q, dO, dQ, lin, lout, view, eps, ct, sn, pos0, bwd);
+      la::bwd_query_vec<false><<<qgrid, block, 0, st>>>(Q, dO, dQ, lin, lout, view, eps, ct, sn, pos0, bwd);
   }
   if (g.C * g.Pc > 1) {
     const int64_t n_elems = g.BH * la::kStateElems;

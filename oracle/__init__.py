@@ -16,4 +16,5 @@ from .linattn_oracle import (  # noqa: F401
     block_causal,
     brute_force,
     backward,
+    temporal_conv3,
 )

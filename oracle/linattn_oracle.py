@@ -311,3 +311,36 @@ def backward(q, k, v, dout, eps=1e-6, angles=None, chunk=None, S_in=None, z_in=N
         dk[..., sl, :] = dphik * (k[..., sl, :] > 0)
         dv[..., sl, :] = np.matmul(phik_num[..., sl, :], G)
     return dq, dk, dv, G, Gz
+
+
+# --------------------------------------------------------------------------
+# Temporal convolution of the block-inference cache
+# --------------------------------------------------------------------------
+
+def temporal_conv3(x, w, bias=None, prev_frame=None):
+    """Shortcut-integrated temporal convolution over frames, block-causal:
+    y[b, f, s, c] = x[b, f, s, c] + w[c, 0] x[b, f-1, s, c] + w[c, 1] x[b, f, s, c]
+                    + w[c, 2] x[b, f+1, s, c] + bias[c]
+    with x[b, -1] = prev_frame[b] (zeros when None) and x[b, F] = 0.
+
+    [Video news] "Design details": the Spatial-Temporal Mix-FFN uses 3x1x1
+    temporal filters; [Video note] 3 Stage 2: the 1D temporal convolution enters
+    the Mix-FFN through a shortcut; [Video note] 4: the block-inference cache
+    keeps the conv's last frame.  Readings: depthwise (one filter per channel,
+    as the Mix-FFN's spatial conv is depth-wise); the previous chunk's last
+    frame is the only context across a chunk boundary, and a chunk sees no
+    later frame (zero padding at its end).
+
+    x: [B, F, S, C] (frames, spatial tokens, channels); w: [C, 3]; bias: [C];
+    prev_frame: [B, S, C].  Returns y [B, F, S, C] and the cache for the next
+    chunk, x[:, F-1].
+    """
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    B, F, S, C = x.shape
+    prev = np.zeros((B, S, C)) if prev_frame is None else np.asarray(prev_frame, dtype=np.float64)
+    padded = np.concatenate([prev[:, None], x, np.zeros((B, 1, S, C))], axis=1)
+    y = x + w[:, 0] * padded[:, :F] + w[:, 1] * padded[:, 1:F + 1] + w[:, 2] * padded[:, 2:F + 2]
+    if bias is not None:
+        y = y + np.asarray(bias, dtype=np.float64)
+    return y, x[:, F - 1].copy()

@@ -362,3 +362,53 @@ ALL_PINS = [
     pin_rope_properties, pin_block_properties, pin_block_rope_positions,
     pin_backward_exact, pin_backward_finite_differences,
 ]
+
+
+# --------------------------------------------------------------------------
+# Temporal convolution (block-inference conv cache)
+# --------------------------------------------------------------------------
+
+def pin_temporal_conv(impl):
+    """Against a loop over frames written from the formula, exact in
+    rationals for dyadic inputs; chunking with the cache equals one pass over
+    the whole sequence except at the chunk ends (no look-ahead across chunks);
+    identity and shift filters."""
+    from fractions import Fraction
+    rng = np.random.default_rng(71)
+    B, F, S, C = 2, 4, 3, 5
+    x = _dyadic(rng, (B, F, S, C))
+    w = _dyadic(rng, (C, 3))
+    b = _dyadic(rng, (C,))
+    prev = _dyadic(rng, (B, S, C))
+    y, cache = impl.temporal_conv3(x, w, b, prev)
+    for bb in range(B):
+        for f in range(F):
+            for s in range(S):
+                for c in range(C):
+                    left = prev[bb, s, c] if f == 0 else x[bb, f - 1, s, c]
+                    right = 0.0 if f == F - 1 else x[bb, f + 1, s, c]
+                    want = (Fraction(x[bb, f, s, c]) + Fraction(w[c, 0]) * Fraction(left)
+                            + Fraction(w[c, 1]) * Fraction(x[bb, f, s, c]) + Fraction(w[c, 2]) * Fraction(right)
+                            + Fraction(b[c]))
+                    assert y[bb, f, s, c] == float(want), (bb, f, s, c)
+    assert np.array_equal(cache, x[:, F - 1])
+    # the first chunk starts from zeros
+    y0, _ = impl.temporal_conv3(x, w, b, None)
+    y1, _ = impl.temporal_conv3(x, w, b, np.zeros((B, S, C)))
+    assert np.array_equal(y0, y1)
+    # chunks of 2 frames with the cache: frame 1 of each chunk misses only its right neighbour
+    ya, ca = impl.temporal_conv3(x[:, :2], w, b, prev)
+    yb, cb = impl.temporal_conv3(x[:, 2:], w, b, ca)
+    _close(ya[:, 0], y[:, 0], 0.0, "first frame")
+    _close(yb, y[:, 2:], 0.0, "second chunk through the cache")
+    _close(ya[:, 1] + w[:, 2] * x[:, 2], y[:, 1], 1e-15, "chunk end: no later frame")
+    assert np.array_equal(cb, cache)
+    # w = (0, 0, 0) and no bias: the shortcut alone; w = (1, -1, 0): y = x_prev
+    z, _ = impl.temporal_conv3(x, np.zeros((C, 3)), None, prev)
+    assert np.array_equal(z, x)
+    sh = np.tile(np.array([1.0, -1.0, 0.0]), (C, 1))
+    z, _ = impl.temporal_conv3(x, sh, None, prev)
+    assert np.array_equal(z[:, 0], prev) and np.array_equal(z[:, 1:], x[:, :-1])
+
+
+ALL_PINS.append(pin_temporal_conv)

@@ -71,6 +71,12 @@ MUTANTS = {
                                 "dS_chunk.append(np.matmul(np.swapaxes(phiq[..., sl, :], -1, -2), dnum))"),
     "bwd_out_gradient_ignored": ("G = np.zeros(lead + (D, D)) if dS_out is None else np.asarray(dS_out, dtype=np.float64)",
                                  "G = np.zeros(lead + (D, D))"),
+    "conv_taps_swapped": ("y = x + w[:, 0] * padded[:, :F] + w[:, 1] * padded[:, 1:F + 1] + w[:, 2] * padded[:, 2:F + 2]",
+                          "y = x + w[:, 2] * padded[:, :F] + w[:, 1] * padded[:, 1:F + 1] + w[:, 0] * padded[:, 2:F + 2]"),
+    "conv_no_shortcut": ("y = x + w[:, 0] * padded[:, :F]", "y = 0 * x + w[:, 0] * padded[:, :F]"),
+    "conv_cache_first_frame": ("return y, x[:, F - 1].copy()", "return y, x[:, 0].copy()"),
+    "conv_wraps_around": ("padded = np.concatenate([prev[:, None], x, np.zeros((B, 1, S, C))], axis=1)",
+                          "padded = np.concatenate([prev[:, None], x, x[:, :1]], axis=1)"),
     "bwd_carried_state_ignored": ("S = np.zeros(lead + (D, D)) if S_in is None else np.asarray(S_in, dtype=np.float64)\n    z = np.zeros(lead + (D,)) if z_in is None else np.asarray(z_in, dtype=np.float64)\n    states = []",
                                   "S = np.zeros(lead + (D, D))\n    z = np.zeros(lead + (D,)) if z_in is None else np.asarray(z_in, dtype=np.float64)\n    states = []"),
 }
