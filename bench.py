@@ -150,6 +150,63 @@ def copy_probe(steps, warmup, nbytes=2 ** 30):
                       "ms_per_copy": ms, "gbps_read_plus_write": 2 * nbytes / (ms / 1e3) / 1e9}), flush=True)
 
 
+def conv_bench(args, dev, stream):
+    """Time the temporal convolution of block inference with its cache
+    (sana_linattn_temporal_conv3, reading the previous chunk's last frame and
+    committing the new one in place) on one 480p chunk: 3 latent frames of
+    30 x 52 tokens, at the Mix-FFN's hidden width (2.5 x 2240 = 5600 channels
+    for Sana-1.6B), bf16.  Algorithmic bytes: x read and y written once, the
+    cache read and written once."""
+    import torch
+
+    import linear_attention_diffusion_amd as la
+
+    B, F, S, C = 1, 3, 30 * 52, 5600
+    g = torch.Generator(device="cpu").manual_seed(7)
+    x0 = (torch.randn(B, F, S, C, generator=g) * 0.5).to(torch.bfloat16).to(dev)
+    w = (torch.randn(C, 3, generator=g) * 0.3).to(dev)
+    b = (torch.randn(C, generator=g) * 0.1).to(dev)
+    set_bytes = 2 * x0.numel() * 2
+    n_sets = max(2, min(64, math.ceil(1.5 * 2 ** 30 / set_bytes) + 1))
+    sets = [(x0.clone(), torch.empty_like(x0), torch.zeros(B, S, C, dtype=torch.bfloat16, device=dev))
+            for _ in range(n_sets)]
+    L = la.lib()
+    P = ctypes.c_void_p
+    st_ptr = ctypes.c_void_p(stream.cuda_stream)
+    calls = [(P(x.data_ptr()), P(y.data_ptr()), P(w.data_ptr()), P(b.data_ptr()), P(c.data_ptr()), P(c.data_ptr()),
+              B, F, S, C, la.SANA_DT_BF16, st_ptr) for x, y, c in sets]
+
+    def step(i):
+        rc = L.sana_linattn_temporal_conv3(*calls[i % n_sets])
+        if rc:
+            raise la.SanaError(rc)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    alg = 2 * B * F * S * C * 2 + 2 * B * S * C * 2
+    achieved = alg / (ms / 1e3) / 1e9
+    print(json.dumps({
+        "metric": "temporal conv (block-inference conv cache) GB/s",
+        "value": achieved, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1)x0.5 bf16 activations, random filters",
+        "config": {"workload": "480p chunk at Mix-FFN width", "pass": "conv", "B": B, "frames": F, "spatial": S,
+                   "channels": C, "input_sets_cycled": n_sets},
+        "roofline": {"bound": "hbm", "kernel": "temporal_conv3", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "algorithmic_bytes_per_launch": alg, "avg_launch_ms": ms},
+        "kernel_source_hash": kernel_source_hash(),
+    }), flush=True)
+
+
 def backward_bench(w, args, dev, stream):
     """Time sana_linattn_backward: one call per step (dQ, dK, dV from dO; the
     chunk states are recomputed from K, V), the block-causal workload as one
@@ -289,7 +346,7 @@ def main():
     ap.add_argument("--block-mode", choices=["chunks", "sequence"], default="chunks",
                     help="block-causal workload: one block_forward call per chunk (inference, the default) or "
                          "one block_causal call over the whole sequence (all chunks known at once)")
-    ap.add_argument("--pass", dest="which", choices=["forward", "backward"], default="forward",
+    ap.add_argument("--pass", dest="which", choices=["forward", "backward", "conv"], default="forward",
                     help="forward (the default; the headline metric) or backward: one sana_linattn_backward "
                          "call per step (dQ, dK, dV; whole sequence in block-causal chunks for that workload)")
     ap.add_argument("--layout", choices=["bhnd", "packed"], default="bhnd",
@@ -320,6 +377,9 @@ def main():
     stream = torch.cuda.current_stream(dev)
     if args.which == "backward":
         backward_bench(w, args, dev, stream)
+        return
+    if args.which == "conv":
+        conv_bench(args, dev, stream)
         return
 
     x = generate(w, with_f64=False)

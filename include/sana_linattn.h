@@ -291,6 +291,25 @@ int sana_linattn_apply(const void* q, void* o, const float* kv_state, const floa
                        int B, int H, int64_t N, int D, int dtype, float eps,
                        const sana_rope* rope, void* hip_stream);
 
+/* The temporal convolution of block inference and its cache (the third part
+ * of the block-inference cache, "SANA-Video" paper notes section 4: the conv
+ * cache holds the temporal conv's last frame).  The Spatial-Temporal Mix-FFN
+ * uses 3x1x1 temporal filters (news article, "Design details") entering
+ * through a shortcut (paper notes, section 3 Stage 2); read as depthwise:
+ *   y[b][f][s][c] = x[b][f][s][c] + w[c][0] x[b][f-1][s][c] + w[c][1] x[b][f][s][c]
+ *                   + w[c][2] x[b][f+1][s][c] + bias[c]
+ * x[b][-1] = cache_in[b] (zeros when cache_in is NULL: the first chunk);
+ * x[b][F] = 0 (a chunk sees no later frame).  cache_out (may equal cache_in,
+ * or NULL) receives x[b][F-1], the cache for the next chunk (a commit).
+ * x, y: [B][F][S][C] device arrays of dtype (F frames of S spatial tokens, C
+ * channels, C a multiple of 8), 16-byte aligned; y overlaps nothing.  w:
+ * [C][3] fp32; bias: [C] fp32 or NULL (both 16-byte aligned); cache_in,
+ * cache_out: [B][S][C] of dtype.  F = 0 or B*S*C = 0 is a no-op.  fp32 arithmetic, bf16 rounded to
+ * nearest even at the store. */
+int sana_linattn_temporal_conv3(const void* x, void* y, const float* w, const float* bias,
+                                const void* cache_in, void* cache_out,
+                                int B, int F, int64_t S, int C, int dtype, void* hip_stream);
+
 /* Host-side builder of 3D RoPE tables ("SANA-Video" paper notes, section 3
  * Stage 2, rotary position encoding extended to space-time).  Token
  * n = (t*Hl + h)*Wl + w; the first dt dims (dt/2 pairs) turn with t, the next

@@ -32,6 +32,7 @@ from .binding import (  # noqa: F401
     sana_linattn_forward,
     sana_linattn_state_update,
     sana_linattn_state_update_backward,
+    sana_linattn_temporal_conv3,
     sana_linattn_status_string,
     workspace_bytes,
 )

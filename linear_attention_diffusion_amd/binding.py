@@ -31,6 +31,7 @@ EXPORTED = (
     "sana_linattn_backward_strided",
     "sana_linattn_backward_workspace_bytes",
     "sana_linattn_state_update_backward",
+    "sana_linattn_temporal_conv3",
     "sana_linattn_rope3d_table",
     "sana_linattn_status_string",
 )
@@ -94,6 +95,8 @@ def lib():
     L.sana_linattn_backward_strided.restype = i32
     L.sana_linattn_state_update_backward.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, rp, vp]
     L.sana_linattn_state_update_backward.restype = i32
+    L.sana_linattn_temporal_conv3.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, vp]
+    L.sana_linattn_temporal_conv3.restype = i32
     L.sana_linattn_rope3d_table.argtypes = [i32, i32, i32, i32, i32, i32, i32, ctypes.c_double, vp, vp]
     L.sana_linattn_rope3d_table.restype = i32
     L.sana_linattn_status_string.argtypes = [i32]
@@ -416,6 +419,31 @@ def sana_linattn_state_update_backward(k, v, dkv, dksum, dk=None, dv=None, rope=
                                                     _ptr(outs[1]), B, H, N, D, _dtype_code(k), _rope_arg(rope),
                                                     _stream(stream, k.device)))
     return tuple(outs)
+
+
+def sana_linattn_temporal_conv3(x, w, bias=None, cache_in=None, cache_out=None, y=None, stream=None):
+    """y = x + depthwise 3-tap temporal conv over frames (+ bias) of x [B, F, S, C],
+    the previous chunk's last frame taken from cache_in [B, S, C] (None: zeros)
+    and x's last frame stored to cache_out (may be cache_in; None: no commit).
+    Returns y."""
+    torch = _torch()
+    if x.dim() != 4 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [B, F, S, C] device tensor")
+    B, F, S, C = x.shape
+    if y is None:
+        y = torch.empty_like(x)
+    elif tuple(y.shape) != (B, F, S, C) or y.dtype != x.dtype or not y.is_contiguous():
+        raise ValueError("y must match x")
+    if tuple(w.shape) != (C, 3) or w.dtype != torch.float32 or not w.is_contiguous():
+        raise ValueError("w must be contiguous float32 [C, 3]")
+    if bias is not None and (tuple(bias.shape) != (C,) or bias.dtype != torch.float32):
+        raise ValueError("bias must be float32 [C]")
+    for t in (cache_in, cache_out):
+        if t is not None and (tuple(t.shape) != (B, S, C) or t.dtype != x.dtype or not t.is_contiguous()):
+            raise ValueError("caches must be contiguous [B, S, C] of x's dtype")
+    _check(lib().sana_linattn_temporal_conv3(_ptr(x), _ptr(y), _ptr(w), _ptr(bias), _ptr(cache_in), _ptr(cache_out),
+                                             B, F, S, C, _dtype_code(x), _stream(stream, x.device)))
+    return y
 
 
 def sana_linattn_apply(q, kv_state, ksum_state, o=None, eps=1e-6, rope=None, stream=None):

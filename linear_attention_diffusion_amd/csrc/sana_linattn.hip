@@ -27,6 +27,7 @@
 #include <cstring>
 
 #include "la_backward.h"
+#include "la_conv.h"
 #include "la_kernels.h"
 
 namespace {
@@ -657,6 +658,39 @@ int sana_linattn_apply(const void* q, void* o, const float* kv_state, const floa
   const la::Layout flat{(int64_t)H * N * D, N * D, D, H};
   launch_apply(q, o, flat, flat, dtype, eps, g, rope, la::StateView{kv_state, ksum_state, 1024, 32},
                static_cast<hipStream_t>(hip_stream));
+  return launch_status();
+}
+
+int sana_linattn_temporal_conv3(const void* x, void* y, const float* w, const float* bias, const void* cache_in,
+                                void* cache_out, int B, int F, int64_t S, int C, int dtype, void* hip_stream) {
+  const int es = elem_size(dtype);
+  if (B < 0 || F < 0 || S < 0 || C < 0 || es == 0) return SANA_ERR_INVALID;
+  if (C % 8) return SANA_ERR_INVALID;
+  if (S > 0 && C > 0 && (int64_t)B > (INT64_MAX / 64) / S / C) return SANA_ERR_INVALID;
+  const int64_t cols = (int64_t)B * S * (C / 8);
+  if (cols == 0 || F == 0) return SANA_OK;
+  if (S * (int64_t)C > (INT64_MAX / 64) / F) return SANA_ERR_INVALID;
+  if (check_tensor(x) || check_tensor(y)) return SANA_ERR_INVALID;
+  if (!w || !aligned(w, 16) || (bias && !aligned(bias, 16))) return SANA_ERR_INVALID;
+  if ((cache_in && !aligned(cache_in, 16)) || (cache_out && !aligned(cache_out, 16))) return SANA_ERR_INVALID;
+  const size_t bytes = (size_t)B * F * S * C * es, cbytes = (size_t)B * S * C * es;
+  if (overlaps(y, bytes, x, bytes) || overlaps(y, bytes, cache_in, cbytes) || overlaps(y, bytes, cache_out, cbytes) ||
+      overlaps(cache_out, cbytes, x, bytes))
+    return SANA_ERR_INVALID;
+  if (cache_out && overlaps(cache_out, cbytes, cache_in, cbytes) && cache_out != cache_in) return SANA_ERR_INVALID;
+  if (overlaps(y, bytes, w, (size_t)C * 3 * sizeof(float)) || overlaps(y, bytes, bias, (size_t)C * sizeof(float)))
+    return SANA_ERR_INVALID;
+  const int64_t blocks = ceil_div(cols, la::kThreads);
+  if (blocks > INT32_MAX) return SANA_ERR_INVALID;
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  if (dtype == SANA_DT_BF16)
+    la::temporal_conv3<__bf16><<<dim3((unsigned)blocks), dim3(la::kThreads), 0, st>>>(
+        static_cast<const __bf16*>(x), static_cast<__bf16*>(y), w, bias, static_cast<const __bf16*>(cache_in),
+        static_cast<__bf16*>(cache_out), F, S, C, cols);
+  else
+    la::temporal_conv3<float><<<dim3((unsigned)blocks), dim3(la::kThreads), 0, st>>>(
+        static_cast<const float*>(x), static_cast<float*>(y), w, bias, static_cast<const float*>(cache_in),
+        static_cast<float*>(cache_out), F, S, C, cols);
   return launch_status();
 }
 
