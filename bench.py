@@ -38,15 +38,17 @@ from workloads import WORKLOADS, generate  # noqa: E402
 METRIC = "linear-attn tokens·heads/s + achieved HBM GB/s (% peak), Sana-1.6B 4096px layer"
 UNIT = "tokens·heads/s"
 HBM_PEAK_GBPS = 8000.0
-KERNEL_SOURCES = ["linear_attention_diffusion_amd/csrc/la_kernels.h",
-                  "linear_attention_diffusion_amd/csrc/sana_linattn.hip"]
+KERNEL_DIR = "linear_attention_diffusion_amd/csrc"
 
 
 def kernel_source_hash():
+    """sha256[:16] over every kernel source (csrc/*.h and *.hip, by name)."""
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+    d = os.path.join(ROOT, KERNEL_DIR)
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".h", ".hip")):
+            with open(os.path.join(d, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
@@ -201,7 +203,7 @@ def conv_bench(args, dev, stream):
         "config": {"workload": "480p chunk at Mix-FFN width", "pass": "conv", "B": B, "frames": F, "spatial": S,
                    "channels": C, "input_sets_cycled": n_sets},
         "roofline": {"bound": "hbm", "kernel": "temporal_conv3", "achieved": achieved, "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": stored_traffic("conv_480p_chunk"),
                      "algorithmic_bytes_per_launch": alg, "avg_launch_ms": ms},
         "kernel_source_hash": kernel_source_hash(),
     }), flush=True)
