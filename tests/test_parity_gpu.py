@@ -291,6 +291,39 @@ def test_apply_matches_forward_and_oracle():
         check(to_np(o_apply), ref, "bf16", f"apply on a given state (rope={rope_grid})")
 
 
+@pytest.mark.parametrize("H,N,grid", [(1, 4096, None), (1, 8192, None), (70, 4680, None), (3, 700, (7, 10, 10)),
+                                       (2, 2000, (5, 20, 20))])
+def test_block_forward_matches_state_update_then_apply(H, N, grid):
+    """From the same non-zero carried state, block_forward's in-place commit
+    and outputs equal bit for bit those of state_update followed by apply
+    (the same sums in the same order), for 1 to 32 partial states per head; a
+    read-only call gives the same outputs."""
+    torch = torch_mod()
+    w = reduced(WORKLOADS["video720p_rope3d"] if grid else WORKLOADS["sana16b_4096px"], H=H, N=N, grid=grid,
+                seed=23)
+    print(f"case block_forward vs state_update + apply H={H} N={N} grid={grid}", flush=True)
+    x = generate(w)
+    q, k, v = inputs_on_device(x)
+    rope = rope_for(w) if grid else None
+    g = torch.Generator().manual_seed(5)
+    kv0 = (torch.rand(1, H, 32, 32, generator=g) * 10).to(device())
+    z0 = (torch.rand(1, H, 32, generator=g) * 10).to(device())
+    kv_a, z_a = kv0.clone(), z0.clone()
+    la.sana_linattn_state_update(k, v, kv_a, z_a, rope=rope)
+    o_a = la.sana_linattn_apply(q, kv_a, z_a, eps=w.eps, rope=rope)
+    o_ro = la.sana_linattn_block_forward(q, k, v, kv_in=kv0, ksum_in=z0, eps=w.eps, rope=rope)
+    kv_b, z_b = kv0.clone(), z0.clone()
+    o_b = la.sana_linattn_block_forward(q, k, v, kv_in=kv_b, ksum_in=z_b, kv_out=kv_b, ksum_out=z_b, eps=w.eps,
+                                        rope=rope)
+    torch.cuda.synchronize()
+    assert torch.equal(kv_b, kv_a) and torch.equal(z_b, z_a)
+    assert torch.equal(o_b, o_a) and torch.equal(o_ro, o_a)
+    ang = oracle.rope3d_angles(*grid) if grid else None
+    S_ref, z_ref = oracle.kv_state(x.f64["k"], x.f64["v"], angles=ang)
+    assert rel_l2(to_np(kv_b), S_ref + to_np(kv0).astype(np.float64)) <= 1e-5
+    assert rel_l2(to_np(z_b), z_ref + to_np(z0).astype(np.float64)) <= 1e-6
+
+
 # --------------------------------------------------------------------------
 # whole-sequence block-causal call
 # --------------------------------------------------------------------------
