@@ -186,6 +186,15 @@ __device__ __forceinline__ u32x4_t load16_nt(rsrc_t r, int off) {
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNonTemporal));
 }
 
+// Streamed rows are loaded non-temporal, unless another wave of the workgroup
+// reads the other half of the same 128-byte lines (two heads per workgroup):
+// then the line must stay in L2 until that wave's load arrives.
+template <int HEADS>
+__device__ __forceinline__ u32x4_t load16_stream(rsrc_t r, int off) {
+  return __builtin_bit_cast(u32x4_t,
+                            __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, HEADS == 1 ? kNonTemporal : 0));
+}
+
 __device__ __forceinline__ f32x4_t load16(rsrc_t r, int off) {
   return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
@@ -220,16 +229,17 @@ __device__ __forceinline__ void commit(const StateArgs& a, int64_t bh, int idx, 
 // split s.  With a single chunk and split it is already the head's sum: it
 // goes, with the carried state added, straight to the state (and the
 // commit); otherwise it is stored as a partial.
-__device__ __forceinline__ void write_partial(const float* mine, int64_t bh, int c, int s, const StateArgs& a) {
+__device__ __forceinline__ void write_partial(const float* mine, int64_t bh, int c, int s, const StateArgs& a,
+                                              int tid = threadIdx.x) {
   if (a.C * a.Pc == 1) {
-    for (int idx = threadIdx.x; idx < kStateElems; idx += kThreads) {
+    for (int idx = tid; idx < kStateElems; idx += kThreads) {
       const float x = carried(a, bh, idx) + mine[idx];
       a.states[bh * kStateElems + idx] = x;
       if (a.kv_out) commit(a, bh, idx, x);
     }
   } else {
     float* out = a.partials + (((int64_t)bh * a.C + c) * a.Pc + s) * kStateElems;
-    for (int idx = threadIdx.x; idx < kStateElems; idx += kThreads) out[idx] = mine[idx];
+    for (int idx = tid; idx < kStateElems; idx += kThreads) out[idx] = mine[idx];
   }
 }
 
@@ -262,12 +272,20 @@ __global__ __launch_bounds__(kThreads) void state_finalize(StateArgs a, int64_t 
   if (a.kv_out) commit(a, bh, idx, acc);
 }
 
-// Token range [n_begin, n_end) of state workgroup (bh, c, s) = blockIdx.x.
+// Token range [n_begin, n_end) of state workgroup (bh, c, s) = blockIdx.x,
+// numbered head-major, or (units > 0) head-minor over `units` heads or head
+// pairs, so that workgroups launched together read the same tokens.
 __device__ __forceinline__ void state_item(const StateArgs& a, int64_t& bh, int& c, int& s, int64_t& n_begin,
-                                           int64_t& n_end) {
+                                           int64_t& n_end, int64_t units = 0) {
   const int per_head = a.C * a.Pc;
-  bh = blockIdx.x / per_head;
-  const int r = blockIdx.x % per_head;
+  int r;
+  if (units > 0) {
+    bh = blockIdx.x % units;
+    r = (int)(blockIdx.x / units);
+  } else {
+    bh = blockIdx.x / per_head;
+    r = blockIdx.x % per_head;
+  }
   c = r / a.Pc;
   s = r % a.Pc;
   const int64_t c_begin = (int64_t)c * a.L;
@@ -281,7 +299,14 @@ __device__ __forceinline__ void state_item(const StateArgs& a, int64_t& bh, int&
 // ---------------------------------------------------------------------------
 //
 // One workgroup reduces tokens [s*Ls, min(N, (s+1)*Ls)) of one (batch, head);
-// its four waves take 32-token tiles, two at a time.
+// its four waves take 32-token tiles, two at a time.  With HEADS = 2 it has
+// eight waves and takes heads 2u and 2u + 1 of the same tokens, four waves
+// each, exactly as two one-head workgroups would: when adjacent heads share
+// each 128-byte line (a [B][N][H][D] or packed QKV layout), both halves of every
+// line are then read by one CU at the same time.  Such layouts interleave the
+// heads of a token, so those workgroups are numbered head-minor: the ones
+// launched together take every head of the same tokens, and a DRAM page
+// holding one token's heads is read by all of them at about the same time.
 //
 // The contraction runs over tokens, but rows in memory are token-major.  Each
 // lane therefore loads whole-row pieces -- lane l (n = l % 16, g = l / 16)
@@ -473,19 +498,24 @@ __device__ __forceinline__ void state_tile(const u32x4_t (&kx)[2], const u32x4_t
 
 // DENSE: consecutive tokens are adjacent 64-byte rows (token stride = 32
 // elements), so every tile offset is an instruction immediate.
-template <bool ROPE, bool DENSE>
-__global__ __launch_bounds__(kThreads) void state_bf16(const u32x4_t* __restrict__ K, const u32x4_t* __restrict__ V,
-                                                       Layout lkv, const float* __restrict__ cos_t,
-                                                       const float* __restrict__ sin_t, int64_t pos0,
-                                                       StateArgs a) {
-  __shared__ float red[4][kStateElems];
-  __shared__ float angles[ROPE ? 4 : 1][ROPE ? kAngTile : 1];
+template <bool ROPE, bool DENSE, int HEADS>
+__global__ __launch_bounds__(kThreads* HEADS) void state_bf16(const u32x4_t* __restrict__ K,
+                                                              const u32x4_t* __restrict__ V, Layout lkv,
+                                                              const float* __restrict__ cos_t,
+                                                              const float* __restrict__ sin_t, int64_t pos0,
+                                                              StateArgs a, int64_t BH) {
+  __shared__ float red[4 * HEADS][kStateElems];
+  __shared__ float angles[ROPE ? 4 * HEADS : 1][ROPE ? kAngTile : 1];
 
   int64_t bh, n_begin, n_end;
   int c, s;
-  state_item(a, bh, c, s, n_begin, n_end);
+  state_item(a, bh, c, s, n_begin, n_end, HEADS == 2 ? (BH + 1) / 2 : 0);
   const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wg = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int half = wg >> 2;  // which of the workgroup's heads
+  const int w = wg & 3;      // wave within that head's four
+  bh = bh * HEADS + half;
+  const bool active = bh < BH;
   const int n = lane & 15;
   const int g = lane >> 4;
 
@@ -516,15 +546,16 @@ __global__ __launch_bounds__(kThreads) void state_bf16(const u32x4_t* __restrict
     const rsrc_t rv = rows_rsrc(Vh, c0, n_end, row);
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
-      nk[h] = load16_nt(rk, lane_off + h * 16 * (int)row);
-      nv[h] = load16_nt(rv, lane_off + h * 16 * (int)row);
+      nk[h] = load16_stream<HEADS>(rk, lane_off + h * 16 * (int)row);
+      nv[h] = load16_stream<HEADS>(rv, lane_off + h * 16 * (int)row);
     }
     if constexpr (ROPE) {
       load_angle_rows(cos_t, sin_t, pos0, c0, n_end, tab_off, na[0]);
       load_angle_rows(cos_t, sin_t, pos0, c0 + 32, n_end, tab_off, na[1]);
     }
   };
-  float* lds = angles[ROPE ? w : 0];
+  float* lds = angles[ROPE ? wg : 0];
+  if (!active) t0 = n_end;
   if (t0 < n_end) load_chunk(t0);
   for (; t0 < n_end; t0 += 256) {
     const u32x4_t ka[2] = {nk[0], nk[1]}, va[2] = {nv[0], nv[1]};
@@ -536,7 +567,7 @@ __global__ __launch_bounds__(kThreads) void state_bf16(const u32x4_t* __restrict
   }
 
   // D lane (n, g): rows 4g + i -> key feature 16fh + 4g + i, column n -> value feature 16fh' + n
-  float* rw = red[w];
+  float* rw = red[wg];
 #pragma unroll
   for (int fh = 0; fh < 2; ++fh) {
 #pragma unroll
@@ -548,10 +579,12 @@ __global__ __launch_bounds__(kThreads) void state_bf16(const u32x4_t* __restrict
     }
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < kStateElems; idx += kThreads)
-    red[0][idx] = (red[0][idx] + red[1][idx]) + (red[2][idx] + red[3][idx]);
+  float* const r = red[4 * half];
+  const int tid = threadIdx.x & (kThreads - 1);
+  for (int idx = tid; idx < kStateElems; idx += kThreads)
+    r[idx] = (r[idx] + r[kStateElems + idx]) + (r[2 * kStateElems + idx] + r[3 * kStateElems + idx]);
   __syncthreads();
-  write_partial(red[0], bh, c, s, a);
+  if (active) write_partial(r, bh, c, s, a, tid);
 }
 
 // ---------------------------------------------------------------------------
@@ -639,7 +672,11 @@ __global__ __launch_bounds__(kThreads) void state_f32(const float* __restrict__ 
 // Work split: the B*H*N tokens, flattened head-major, are cut into equal
 // contiguous ranges, one per workgroup; a range that crosses a head boundary
 // is processed head segment by head segment.  Each wave takes 64-token chunks
-// (four 16-token tiles, four loads in flight) of the current segment.
+// (four 16-token tiles, four loads in flight) of the current segment.  With
+// HEADS = 2 the workgroup's eight waves take the same tokens of heads 2u and
+// 2u + 1, four waves each, and workgroups are numbered head-minor: blockIdx.x
+// = blk * units + u takes tokens [blk * La, (blk + 1) * La) of pair u (see the
+// state pass).
 
 struct ApplyOperands {
   bf16x8_t s[2][3];  // S^T rows for output halves h = 0, 1; three bf16 parts
@@ -733,13 +770,13 @@ struct ApplyChunk {
 };
 
 // Rows at or past n_end read 0; their outputs are not stored.
-template <bool ROPE>
+template <bool ROPE, int HEADS>
 __device__ __forceinline__ void load_apply_chunk(const char* Qh, int64_t row, int64_t t0, int64_t n_end,
                                                  int lane_off, int tab_off, const float* cos_t,
                                                  const float* sin_t, int64_t pos0, ApplyChunk<ROPE>& ch) {
   const rsrc_t rq = rows_rsrc(Qh, t0, n_end, row);
 #pragma unroll
-  for (int u = 0; u < 4; ++u) ch.q[u] = load16_nt(rq, lane_off + u * 16 * (int)row);
+  for (int u = 0; u < 4; ++u) ch.q[u] = load16_stream<HEADS>(rq, lane_off + u * 16 * (int)row);
   if constexpr (ROPE) {
     // pairs 4g .. 4g+3 of the token at position pos0 + t0 + 16u + m: the same
     // lane offset in a 64-byte table row
@@ -753,31 +790,44 @@ __device__ __forceinline__ void load_apply_chunk(const char* Qh, int64_t row, in
   }
 }
 
-template <bool ROPE, bool DENSE>
-__global__ __launch_bounds__(kThreads) void apply_bf16(const u32x4_t* __restrict__ Q, u32x4_t* __restrict__ O,
-                                                       Layout lq, Layout lo, StateView sv, int64_t N, int64_t L,
-                                                       int C, int64_t total, int64_t La, float eps,
-                                                       const float* __restrict__ cos_t,
-                                                       const float* __restrict__ sin_t, int64_t pos0) {
+template <bool ROPE, bool DENSE, int HEADS>
+__global__ __launch_bounds__(kThreads* HEADS) void apply_bf16(const u32x4_t* __restrict__ Q, u32x4_t* __restrict__ O,
+                                                              Layout lq, Layout lo, StateView sv, int64_t N,
+                                                              int64_t L, int C, int64_t total, int64_t La, float eps,
+                                                              const float* __restrict__ cos_t,
+                                                              const float* __restrict__ sin_t, int64_t pos0,
+                                                              int64_t BH) {
   const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wg = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int half = wg >> 2;
+  const int w = wg & 3;
   const int m = lane & 15;
   const int g = lane >> 4;
   const int64_t qrow = DENSE ? 64 : lq.token * 2, orow = DENSE ? 64 : lo.token * 2;  // bytes between tokens
   const int q_off = m * (int)qrow + g * 16;                // features 8g .. 8g+7 of tile row m
   const int o_off = m * (int)orow + g * 16;
   const int tab_off = m * 64 + g * 16;
-  const int64_t f_begin = (int64_t)blockIdx.x * La;
-  const int64_t f_end = (f_begin + La < total) ? f_begin + La : total;
+  int64_t f_begin, f_end;
+  if constexpr (HEADS == 2) {
+    const int64_t units = (BH + 1) / 2;
+    const int64_t u = blockIdx.x % units;
+    f_begin = u * N + (int64_t)(blockIdx.x / units) * La;
+    f_end = (f_begin + La < (u + 1) * N) ? f_begin + La : (u + 1) * N;
+  } else {
+    f_begin = (int64_t)blockIdx.x * La;
+    f_end = (f_begin + La < total) ? f_begin + La : total;
+  }
 
   // the range is processed in segments that stay inside one head and chunk
   for (int64_t f = f_begin; f < f_end;) {
-    const int64_t bh = f / N;
-    const int64_t n_begin = f - bh * N;
+    const int64_t unit = f / N;
+    const int64_t n_begin = f - unit * N;
     const int c = (int)(n_begin / L);
     const int64_t c_end = ((int64_t)c + 1) * L < N ? ((int64_t)c + 1) * L : N;
-    const int64_t n_end = (f_end - bh * N < c_end) ? f_end - bh * N : c_end;
-    f = bh * N + n_end;
+    const int64_t n_end = (f_end - unit * N < c_end) ? f_end - unit * N : c_end;
+    f = unit * N + n_end;
+    const int64_t bh = unit * HEADS + half;
+    if (bh >= BH) continue;
     const char* Qh = reinterpret_cast<const char*>(Q) + lq.base(bh) * 2;
     char* Oh = reinterpret_cast<char*>(O) + lo.base(bh) * 2;
 
@@ -785,7 +835,7 @@ __global__ __launch_bounds__(kThreads) void apply_bf16(const u32x4_t* __restrict
     // and each chunk's loads before the previous chunk is computed
     int64_t t0 = n_begin + 64 * w;
     ApplyChunk<ROPE> next;
-    if (t0 < n_end) load_apply_chunk<ROPE>(Qh, qrow, t0, n_end, q_off, tab_off, cos_t, sin_t, pos0, next);
+    if (t0 < n_end) load_apply_chunk<ROPE, HEADS>(Qh, qrow, t0, n_end, q_off, tab_off, cos_t, sin_t, pos0, next);
     ApplyOperands op;
     const int64_t sc = bh * C + c;
     load_apply_operands(sv.s_base + sc * sv.s_stride, sv.z_base + sc * sv.z_stride, g, m, op);
@@ -793,7 +843,7 @@ __global__ __launch_bounds__(kThreads) void apply_bf16(const u32x4_t* __restrict
     for (; t0 < n_end; t0 += 256) {
       const ApplyChunk<ROPE> cur = next;
       if (t0 + 256 < n_end)
-        load_apply_chunk<ROPE>(Qh, qrow, t0 + 256, n_end, q_off, tab_off, cos_t, sin_t, pos0, next);
+        load_apply_chunk<ROPE, HEADS>(Qh, qrow, t0 + 256, n_end, q_off, tab_off, cos_t, sin_t, pos0, next);
       const rsrc_t ro = rows_rsrc(Oh, t0, n_end, orow);
 #pragma unroll
       for (int u = 0; u < 4; ++u)

@@ -248,6 +248,11 @@ la::StateView ws_view(const la::StateArgs& a) {
   return la::StateView{a.states, a.states + 1024, la::kStateElems, la::kStateElems};
 }
 
+// Whether adjacent heads of one token are adjacent 64-byte rows, so that one
+// 128-byte line holds two heads: the bf16 passes then give each workgroup two
+// heads of the same tokens.
+bool paired_heads(const la::Layout& l) { return l.head == la::kD; }
+
 // State pass, and the finalize when there are several partials per head.
 void launch_state(const void* k, const void* v, const la::Layout& lkv, int dtype, const Geometry& g,
                   const sana_rope* rope, const la::StateArgs& a, hipStream_t st) {
@@ -259,14 +264,19 @@ void launch_state(const void* k, const void* v, const la::Layout& lkv, int dtype
     const la::u32x4_t* K = static_cast<const la::u32x4_t*>(k);
     const la::u32x4_t* V = static_cast<const la::u32x4_t*>(v);
     const bool dense = lkv.token == la::kD;
+    const dim3 pgrid((unsigned)(ceil_div(g.BH, 2) * g.C * g.Pc)), pblock(2 * la::kThreads);
     if (rope && dense)
-      la::state_bf16<true, true><<<grid, block, 0, st>>>(K, V, lkv, ct, sn, pos0, a);
+      la::state_bf16<true, true, 1><<<grid, block, 0, st>>>(K, V, lkv, ct, sn, pos0, a, g.BH);
+    else if (rope && paired_heads(lkv))
+      la::state_bf16<true, false, 2><<<pgrid, pblock, 0, st>>>(K, V, lkv, ct, sn, pos0, a, g.BH);
     else if (rope)
-      la::state_bf16<true, false><<<grid, block, 0, st>>>(K, V, lkv, ct, sn, pos0, a);
+      la::state_bf16<true, false, 1><<<grid, block, 0, st>>>(K, V, lkv, ct, sn, pos0, a, g.BH);
     else if (dense)
-      la::state_bf16<false, true><<<grid, block, 0, st>>>(K, V, lkv, ct, sn, pos0, a);
+      la::state_bf16<false, true, 1><<<grid, block, 0, st>>>(K, V, lkv, ct, sn, pos0, a, g.BH);
+    else if (paired_heads(lkv))
+      la::state_bf16<false, false, 2><<<pgrid, pblock, 0, st>>>(K, V, lkv, ct, sn, pos0, a, g.BH);
     else
-      la::state_bf16<false, false><<<grid, block, 0, st>>>(K, V, lkv, ct, sn, pos0, a);
+      la::state_bf16<false, false, 1><<<grid, block, 0, st>>>(K, V, lkv, ct, sn, pos0, a, g.BH);
   } else {
     const float* K = static_cast<const float*>(k);
     const float* V = static_cast<const float*>(v);
@@ -288,21 +298,29 @@ void launch_apply(const void* q, void* o, const la::Layout& lq, const la::Layout
   const float* sn = rope ? rope->sin : nullptr;
   const int64_t pos0 = rope ? rope->pos_offset : 0;
   if (dtype == SANA_DT_BF16) {
-    const dim3 grid((unsigned)g.Ga), block(la::kThreads);
     const la::u32x4_t* Q = static_cast<const la::u32x4_t*>(q);
     la::u32x4_t* O = static_cast<la::u32x4_t*>(o);
     const bool dense = lq.token == la::kD && lo.token == la::kD;
-#define LA_APPLY(R, DN)                                                                                       \
-  la::apply_bf16<R, DN><<<grid, block, 0, st>>>(Q, O, lq, lo, sv, g.N, g.L, (int)g.C, g.BH * g.N, g.La, eps, ct, sn, \
-                                                pos0)
+    const bool pair = !dense && (paired_heads(lq) || paired_heads(lo));
+    // ranges of g.La tokens over (head, token), or per head pair
+    const int64_t units = pair ? ceil_div(g.BH, 2) : g.BH;
+    const dim3 grid((unsigned)(pair ? units * ceil_div(g.N, g.La) : ceil_div(units * g.N, g.La))),
+        block(pair ? 2 * la::kThreads : la::kThreads);
+#define LA_APPLY(R, DN, HD)                                                                                     \
+  la::apply_bf16<R, DN, HD><<<grid, block, 0, st>>>(Q, O, lq, lo, sv, g.N, g.L, (int)g.C, units * g.N, g.La, eps, \
+                                                    ct, sn, pos0, g.BH)
     if (rope && dense)
-      LA_APPLY(true, true);
+      LA_APPLY(true, true, 1);
+    else if (rope && pair)
+      LA_APPLY(true, false, 2);
     else if (rope)
-      LA_APPLY(true, false);
+      LA_APPLY(true, false, 1);
     else if (dense)
-      LA_APPLY(false, true);
+      LA_APPLY(false, true, 1);
+    else if (pair)
+      LA_APPLY(false, false, 2);
     else
-      LA_APPLY(false, false);
+      LA_APPLY(false, false, 1);
 #undef LA_APPLY
   } else {
     const dim3 grid((unsigned)(g.BH * g.C * g.T)), block(la::kThreads);
