@@ -77,6 +77,13 @@ def stored_traffic(name):
     return rec.get("hbm_bytes_per_launch")
 
 
+def make_rope(la, w, dev, form):
+    """The workload's 3D RoPE on the device (None without RoPE)."""
+    if w.mode != "rope":
+        return None
+    return la.rope3d_axes_device(*w.grid, dev) if form == "axes" else la.rope3d_device(*w.grid, dev)
+
+
 def cpu_baseline(w, x, budget_s):
     """Time the float64 oracle on the host on the same workload's inputs."""
     import numpy as np
@@ -237,7 +244,7 @@ def backward_bench(w, args, dev, stream):
             s[n] = torch.empty_like(base["q"])
         sets.append(s)
     chunk = w.chunk if w.mode == "block" else w.N
-    rope = la.rope3d_device(*w.grid, dev) if w.mode == "rope" else None
+    rope = make_rope(la, w, dev, args.rope_form)
     dt = la.SANA_DT_BF16 if w.dtype == "bf16" else la.SANA_DT_F32
     nb = la.backward_workspace_bytes(w.B, w.H, w.N, chunk, dtype=dt, has_rope=rope is not None)
     ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
@@ -311,7 +318,8 @@ def backward_bench(w, args, dev, stream):
         "dtype": w.dtype,
         "data": "synthetic: seeded i.i.d. N(0,1)x0.5 bf16 tensors at the workload's latent shape (dO drawn after Q, K, V)",
         "config": {"workload": w.name, "pass": "backward", "B": w.B, "H": w.H, "N": w.N, "D": w.D,
-                   "mode": w.mode, "chunk": chunk, "grid": w.grid, "input_sets_cycled": n_sets},
+                   "mode": w.mode, "chunk": chunk, "grid": w.grid, "input_sets_cycled": n_sets,
+                   "rope_form": args.rope_form if w.mode == "rope" else None},
         "roofline": {
             "bound": "hbm",
             "kernel": "bwd_key_bf16" if w.dtype == "bf16" else "bwd_key_vec",
@@ -355,6 +363,9 @@ def main():
                     help="forward: bhnd = contiguous [B, H, N, D] (the default); packed = Q, K, V read as strided "
                          "views of one [B, N, 3, H, D] projection-style buffer and O written to [B, N, H, D] "
                          "(sana_linattn_forward_strided; non-causal and RoPE workloads)")
+    ap.add_argument("--rope-form", choices=["table", "axes"], default="axes",
+                    help="RoPE workload: axes = the 3D RoPE's per-axis tables, staged in LDS by each workgroup (the "
+                         "default); table = full [pos][16] cos/sin tables, streamed per head")
     ap.add_argument("--copy-probe", action="store_true",
                     help="time a plain 1 GiB device-to-device copy instead (HBM reference and counter scale)")
     args = ap.parse_args()
@@ -414,7 +425,7 @@ def main():
             q, k, v = q0.clone(), k0.clone(), v0.clone()
         sets.append({"q": q, "k": k, "v": v, "o": torch.empty_like(q)})
 
-    rope = la.rope3d_device(*w.grid, dev) if w.mode == "rope" else None
+    rope = make_rope(la, w, dev, args.rope_form)
     if w.mode == "block":
         Lc = w.chunk
         for s in sets:
@@ -563,7 +574,7 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "D": w.D, "mode": w.mode,
                    "chunk": w.chunk, "grid": w.grid, "eps": w.eps, "input_sets_cycled": n_sets,
                    "block_calls": args.block_mode if w.mode == "block" else None,
-                   "layout": args.layout},
+                   "layout": args.layout, "rope_form": args.rope_form if w.mode == "rope" else None},
         "roofline": {
             "bound": "hbm",
             "kernel": "apply_bf16" if w.dtype == "bf16" else "apply_f32",

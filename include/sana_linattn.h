@@ -90,14 +90,30 @@ typedef enum {
     SANA_DT_BF16 = 1
 } sana_dtype;
 
-/* RoPE tables: device pointers to [n_pos][D/2] fp32 arrays (16-byte aligned),
- * pair p of position pos at [pos][p].  Rows pos_offset .. pos_offset+N-1 are
- * read; they must lie inside the table. */
+/* RoPE angles ("SANA-Video" paper notes, section 2.2: applied after the ReLU,
+ * numerator only).  Pair p of a token rotates features (2p, 2p+1) by the angle
+ * whose cosine and sine the tables give for the token's position
+ * pos_offset + n; positions pos_offset .. pos_offset+N-1 must lie in
+ * [0, n_pos).  Two forms:
+ *   full tables (grid and pairs all 0): cos, sin are device arrays
+ *     [n_pos][D/2] fp32, 16-byte aligned, pair p of position pos at [pos][p];
+ *   per-axis tables of a 3D RoPE (grid = {T, Hl, Wl}, all > 0; section 3
+ *     Stage 2): position pos is the latent point pos = (t*Hl + h)*Wl + w,
+ *     n_pos = T*Hl*Wl; the first pairs[0] pairs turn with t, the next
+ *     pairs[1] with h, the last pairs[2] with w (even counts summing to D/2),
+ *     by angles that depend on that coordinate only.  cos, sin are device
+ *     arrays (4-byte aligned) holding [T][pairs[0]], then [Hl][pairs[1]],
+ *     then [Wl][pairs[2]] fp32 back to back, at most 1024 floats each;
+ *     Hl*Wl < 2^20.  Each workgroup copies them to LDS instead of streaming a
+ *     [n_pos][D/2] table per head; with equal angle values both forms give
+ *     identical results. */
 typedef struct {
     const float* cos;
     const float* sin;
     int64_t n_pos;
     int64_t pos_offset;
+    int32_t grid[3];
+    int32_t pairs[3];
 } sana_rope;
 
 /* Element strides of a [B][H][N][D] tensor view, D contiguous: token n of head
@@ -320,6 +336,15 @@ int sana_linattn_temporal_conv3(const void* x, void* y, const float* w, const fl
  * non-negative and sum to D. */
 int sana_linattn_rope3d_table(int T, int Hl, int Wl, int D, int dt, int dh, int dw, double base,
                               float* cos_host, float* sin_host);
+
+/* Host-side builder of the per-axis form of the same 3D RoPE (see sana_rope):
+ * cos_host, sin_host receive T*dt/2 + Hl*dh/2 + Wl*dw/2 floats, the t table
+ * [T][dt/2], then the h table [Hl][dh/2], then the w table [Wl][dw/2]; entry
+ * [x][k] of an axis of width d_a is the cosine (sine) of x * base^(-2k/d_a),
+ * the same float as in sana_linattn_rope3d_table.  Use with grid = {T, Hl, Wl}
+ * and pairs = {dt/2, dh/2, dw/2}. */
+int sana_linattn_rope3d_axes(int T, int Hl, int Wl, int D, int dt, int dh, int dw, double base,
+                             float* cos_host, float* sin_host);
 
 /* Static string naming a status code. */
 const char* sana_linattn_status_string(int status);

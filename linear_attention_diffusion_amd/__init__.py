@@ -4,7 +4,8 @@ Entry points (same names as the C ABI in include/sana_linattn.h):
   sana_linattn_forward, sana_linattn_state_update, sana_linattn_block_forward,
   sana_linattn_block_causal, sana_linattn_apply, sana_linattn_backward,
   sana_linattn_state_update_backward,
-  rope3d_table / rope3d_device (host builder of the 3D RoPE tables).
+  rope3d_table / rope3d_device (host builder of the 3D RoPE tables),
+  rope3d_axes / rope3d_axes_device (the same RoPE as per-axis tables).
 """
 
 from .binding import (  # noqa: F401
@@ -21,6 +22,8 @@ from .binding import (  # noqa: F401
     SanaError,
     lib,
     make_workspace,
+    rope3d_axes,
+    rope3d_axes_device,
     rope3d_device,
     rope3d_table,
     backward_workspace_bytes,

@@ -33,6 +33,7 @@ EXPORTED = (
     "sana_linattn_state_update_backward",
     "sana_linattn_temporal_conv3",
     "sana_linattn_rope3d_table",
+    "sana_linattn_rope3d_axes",
     "sana_linattn_status_string",
 )
 
@@ -43,7 +44,8 @@ class sana_layout(ctypes.Structure):
 
 class sana_rope(ctypes.Structure):
     _fields_ = [("cos", ctypes.c_void_p), ("sin", ctypes.c_void_p),
-                ("n_pos", ctypes.c_int64), ("pos_offset", ctypes.c_int64)]
+                ("n_pos", ctypes.c_int64), ("pos_offset", ctypes.c_int64),
+                ("grid", ctypes.c_int32 * 3), ("pairs", ctypes.c_int32 * 3)]
 
 
 _LIB = None
@@ -99,6 +101,8 @@ def lib():
     L.sana_linattn_temporal_conv3.restype = i32
     L.sana_linattn_rope3d_table.argtypes = [i32, i32, i32, i32, i32, i32, i32, ctypes.c_double, vp, vp]
     L.sana_linattn_rope3d_table.restype = i32
+    L.sana_linattn_rope3d_axes.argtypes = [i32, i32, i32, i32, i32, i32, i32, ctypes.c_double, vp, vp]
+    L.sana_linattn_rope3d_axes.restype = i32
     L.sana_linattn_status_string.argtypes = [i32]
     L.sana_linattn_status_string.restype = ctypes.c_char_p
     _LIB = L
@@ -181,23 +185,37 @@ def _stream(stream, device):
 
 
 class Rope:
-    """Device RoPE tables [n_pos, D/2] (float32) and the position of token 0."""
+    """Device RoPE tables and the position of token 0: full tables [n_pos, D/2]
+    (float32), or, with `grid` = (T, Hl, Wl) and `pairs` = (pt, ph, pw), the
+    per-axis tables of a 3D RoPE back to back (1-D float32)."""
 
-    def __init__(self, cos, sin, pos_offset=0):
+    def __init__(self, cos, sin, pos_offset=0, grid=None, pairs=None):
         torch = _torch()
-        if cos.shape != sin.shape or cos.dim() != 2:
-            raise ValueError("cos and sin must both be [n_pos, D/2]")
+        if cos.shape != sin.shape or cos.dim() != (1 if grid else 2):
+            raise ValueError("cos and sin must both be [n_pos, D/2] (or 1-D per-axis tables with a grid)")
         if cos.dtype != torch.float32 or sin.dtype != torch.float32:
             raise TypeError("RoPE tables are float32")
         if not (cos.is_cuda and sin.is_cuda and cos.is_contiguous() and sin.is_contiguous()):
             raise ValueError("RoPE tables must be contiguous device tensors")
+        if (grid is None) != (pairs is None):
+            raise ValueError("the per-axis form needs both grid and pairs")
         self.cos, self.sin, self.pos_offset = cos, sin, int(pos_offset)
+        self.grid = tuple(int(x) for x in grid) if grid else None
+        self.pairs = tuple(int(x) for x in pairs) if pairs else None
 
     def at(self, pos_offset):
-        return Rope(self.cos, self.sin, pos_offset)
+        return Rope(self.cos, self.sin, pos_offset, self.grid, self.pairs)
+
+    @property
+    def n_pos(self):
+        return self.grid[0] * self.grid[1] * self.grid[2] if self.grid else self.cos.shape[0]
 
     def struct(self):
-        return sana_rope(self.cos.data_ptr(), self.sin.data_ptr(), self.cos.shape[0], self.pos_offset)
+        r = sana_rope(self.cos.data_ptr(), self.sin.data_ptr(), self.n_pos, self.pos_offset)
+        if self.grid:
+            r.grid[:] = self.grid
+            r.pairs[:] = self.pairs
+        return r
 
 
 def _rope_arg(rope):
@@ -219,6 +237,26 @@ def rope3d_device(T, Hl, Wl, device, D=32, split=(8, 12, 12), base=10000.0):
     torch = _torch()
     cos, sin = rope3d_table(T, Hl, Wl, D, split, base)
     return Rope(torch.from_numpy(cos).to(device), torch.from_numpy(sin).to(device))
+
+
+def rope3d_axes(T, Hl, Wl, D=32, split=(8, 12, 12), base=10000.0):
+    """Host per-axis tables of the same 3D RoPE (numpy float32 cos, sin of
+    T*dt/2 + Hl*dh/2 + Wl*dw/2 floats: the t, h and w tables back to back)."""
+    n = T * split[0] // 2 + Hl * split[1] // 2 + Wl * split[2] // 2
+    cos = np.empty(n, np.float32)
+    sin = np.empty(n, np.float32)
+    _check(lib().sana_linattn_rope3d_axes(T, Hl, Wl, D, split[0], split[1], split[2], float(base),
+                                          cos.ctypes.data_as(ctypes.c_void_p),
+                                          sin.ctypes.data_as(ctypes.c_void_p)))
+    return cos, sin
+
+
+def rope3d_axes_device(T, Hl, Wl, device, D=32, split=(8, 12, 12), base=10000.0):
+    """The 3D RoPE in per-axis form (a few KB) on `device`."""
+    torch = _torch()
+    cos, sin = rope3d_axes(T, Hl, Wl, D, split, base)
+    return Rope(torch.from_numpy(cos).to(device), torch.from_numpy(sin).to(device), grid=(T, Hl, Wl),
+                pairs=(split[0] // 2, split[1] // 2, split[2] // 2))
 
 
 def workspace_bytes(B, H, N, D=32, dtype=SANA_DT_BF16, has_rope=False):

@@ -44,15 +44,16 @@ __device__ __forceinline__ float sum8(float x) {
   return x;
 }
 
-// Features f0 .. f0+3 (two pairs) of a token rotated by +theta (forward) or
-// -theta (the transpose, on the way back).
-template <bool INVERSE>
-__device__ __forceinline__ f32x4_t rotate4(f32x4_t x, const float* cos_row, const float* sin_row, int f0) {
+// Features f0 .. f0+3 (two pairs) of the token at position pos rotated by
+// +theta (forward) or -theta (the transpose, on the way back).
+template <bool INVERSE, int ROPE>
+__device__ __forceinline__ f32x4_t rotate4(f32x4_t x, const Rope& rp, const float* rtab, int64_t pos, int f0) {
   f32x4_t y;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const float c = cos_row[f0 / 2 + u];
-    const float s = INVERSE ? -sin_row[f0 / 2 + u] : sin_row[f0 / 2 + u];
+    float c, s;
+    rope_pair<ROPE>(rp, rtab, pos, f0 / 2 + u, c, s);
+    if (INVERSE) s = -s;
     y[2 * u] = x[2 * u] * c - x[2 * u + 1] * s;
     y[2 * u + 1] = x[2 * u] * s + x[2 * u + 1] * c;
   }
@@ -101,13 +102,11 @@ __global__ __launch_bounds__(kThreads) void state_finalize_reverse(StateArgs a, 
 // item; a.kv_out/ksum_out: where that case commits dS_in).  32-token tiles:
 // thread t handles features f0 = 4 (t % 8) .. f0+3 of token t / 8 of the
 // tile, and element row d = t / 8, columns f0 .. f0+3 of the partial dS.
-template <bool ROPE>
+template <int ROPE>
 __global__ __launch_bounds__(kThreads) void bwd_query_vec(const float* __restrict__ Q, const float* __restrict__ dO,
                                                           float* __restrict__ dQ, Layout lin, Layout lout,
-                                                          StateView fwd, float eps,
-                                                          const float* __restrict__ cos_t,
-                                                          const float* __restrict__ sin_t, int64_t pos0,
-                                                          StateArgs a) {
+                                                          StateView fwd, float eps, Rope rp, StateArgs a) {
+  __shared__ __attribute__((aligned(16))) float rtab[ROPE == kRopeAxes ? 2 * kMaxAxisTab : 1];
   __shared__ float sS[kD][kD + 1];
   __shared__ float sz[kD];
   __shared__ float sp[32][kD + 1];   // phi(Q)
@@ -125,6 +124,8 @@ __global__ __launch_bounds__(kThreads) void bwd_query_vec(const float* __restric
   const int64_t sc = bh * a.C + c;
   for (int idx = t; idx < kD * kD; idx += kThreads) sS[idx >> 5][idx & 31] = fwd.s_base[sc * fwd.s_stride + idx];
   if (t < kD) sz[t] = fwd.z_base[sc * fwd.z_stride + t];
+  rope_stage<ROPE>(rp, rtab, t, kThreads);
+  if constexpr (ROPE == kRopeAxes) __syncthreads();
 
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   float zacc = 0.f;
@@ -142,7 +143,7 @@ __global__ __launch_bounds__(kThreads) void bwd_query_vec(const float* __restric
     for (int u = 0; u < 4; ++u) p[u] = fmaxf(x[u], 0.f);
     pr = p;
     if constexpr (ROPE) {
-      if (live) pr = rotate4<false>(p, cos_t + (pos0 + tok) * 16, sin_t + (pos0 + tok) * 16, f0);
+      if (live) pr = rotate4<false, ROPE>(p, rp, rtab, rp.pos0 + tok, f0);
     }
     __syncthreads();  // previous tile's readers are done (and S, z are in place)
 #pragma unroll
@@ -179,7 +180,7 @@ __global__ __launch_bounds__(kThreads) void bwd_query_vec(const float* __restric
       for (int u = 0; u < 4; ++u) dr[u] += sS[f0 + u][e] * de;
     }
     if constexpr (ROPE) {
-      if (live) dr = rotate4<true>(dr, cos_t + (pos0 + tok) * 16, sin_t + (pos0 + tok) * 16, f0);
+      if (live) dr = rotate4<true, ROPE>(dr, rp, rtab, rp.pos0 + tok, f0);
     }
     f32x4_t dq;
 #pragma unroll
@@ -207,13 +208,13 @@ __global__ __launch_bounds__(kThreads) void bwd_query_vec(const float* __restric
 //
 // Workgroup (head, chunk, tile) takes tokens [c*L + tile*Lt, ...) of chunk c;
 // 32-token tiles, thread t: features f0 = 4 (t % 8) .. f0+3 of token t / 8.
-template <bool ROPE>
+template <int ROPE>
 __global__ __launch_bounds__(kThreads) void bwd_key_vec(const float* __restrict__ K, const float* __restrict__ V,
                                                         float* __restrict__ dK, float* __restrict__ dV, Layout lin,
                                                         Layout lout, StateView grad,
                                                         int64_t N, int64_t L, int C, int tiles, int64_t Lt,
-                                                        const float* __restrict__ cos_t,
-                                                        const float* __restrict__ sin_t, int64_t pos0) {
+                                                        Rope rp) {
+  __shared__ __attribute__((aligned(16))) float rtab[ROPE == kRopeAxes ? 2 * kMaxAxisTab : 1];
   __shared__ float sG[kD][kD + 1];
   __shared__ float sGz[kD];
   __shared__ float skr[32][kD + 1];  // phi~(K)
@@ -232,6 +233,8 @@ __global__ __launch_bounds__(kThreads) void bwd_key_vec(const float* __restrict_
   const int64_t sc = bh * C + c;
   for (int idx = t; idx < kD * kD; idx += kThreads) sG[idx >> 5][idx & 31] = grad.s_base[sc * grad.s_stride + idx];
   if (t < kD) sGz[t] = grad.z_base[sc * grad.z_stride + t];
+  rope_stage<ROPE>(rp, rtab, t, kThreads);
+  if constexpr (ROPE == kRopeAxes) __syncthreads();
 
   for (int64_t t0 = n_begin; t0 < n_end; t0 += 32) {
     const int64_t tok = t0 + tl;
@@ -247,7 +250,7 @@ __global__ __launch_bounds__(kThreads) void bwd_key_vec(const float* __restrict_
 #pragma unroll
     for (int u = 0; u < 4; ++u) p[u] = fmaxf(x[u], 0.f);
     if constexpr (ROPE) {
-      if (live) p = rotate4<false>(p, cos_t + (pos0 + tok) * 16, sin_t + (pos0 + tok) * 16, f0);
+      if (live) p = rotate4<false, ROPE>(p, rp, rtab, rp.pos0 + tok, f0);
     }
     __syncthreads();
 #pragma unroll
@@ -267,7 +270,7 @@ __global__ __launch_bounds__(kThreads) void bwd_key_vec(const float* __restrict_
       }
     }
     if constexpr (ROPE) {
-      if (live) dr = rotate4<true>(dr, cos_t + (pos0 + tok) * 16, sin_t + (pos0 + tok) * 16, f0);
+      if (live) dr = rotate4<true, ROPE>(dr, rp, rtab, rp.pos0 + tok, f0);
     }
     f32x4_t dk;
 #pragma unroll
@@ -398,16 +401,17 @@ __device__ __forceinline__ void split8(const float (&y)[8], bf16x8_t (&b)[3]) {
 // chunk's loads in flight.
 // ---------------------------------------------------------------------------
 
-template <bool ROPE>
+template <int ROPE>
 struct KeyChunk {
   u32x4_t k[4], v[4];
   f32x4_t c[4], sn[4];
 };
 
-template <bool ROPE>
+template <int ROPE>
 __device__ __forceinline__ void load_key_chunk(const char* Kh, const char* Vh, int64_t row, int64_t t0,
-                                               int64_t n_end, int lane_off, int tab_off, const float* cos_t,
-                                               const float* sin_t, int64_t pos0, KeyChunk<ROPE>& ch) {
+                                               int64_t n_end, int lane_off, int tab_off, int m, int g,
+                                               const Rope& rp, const float* rtab, const AxisLane& al,
+                                               KeyChunk<ROPE>& ch) {
   const rsrc_t rk = rows_rsrc(Kh, t0, n_end, row);
   const rsrc_t rv = rows_rsrc(Vh, t0, n_end, row);
 #pragma unroll
@@ -415,28 +419,31 @@ __device__ __forceinline__ void load_key_chunk(const char* Kh, const char* Vh, i
     ch.k[u] = load16_nt(rk, lane_off + u * 16 * (int)row);
     ch.v[u] = load16_nt(rv, lane_off + u * 16 * (int)row);
   }
-  if constexpr (ROPE) {
-    const rsrc_t rc = make_rsrc(cos_t + (pos0 + t0) * 16, (n_end - t0) * 64);
-    const rsrc_t rs = make_rsrc(sin_t + (pos0 + t0) * 16, (n_end - t0) * 64);
+  if constexpr (ROPE == kRopeTable) {
+    const rsrc_t rc = make_rsrc(rp.cos + (rp.pos0 + t0) * 16, (n_end - t0) * 64);
+    const rsrc_t rs = make_rsrc(rp.sin + (rp.pos0 + t0) * 16, (n_end - t0) * 64);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       ch.c[u] = load16(rc, tab_off + u * 1024);
       ch.sn[u] = load16(rs, tab_off + u * 1024);
     }
   }
+  // the axis form's angles come from LDS when the tile is computed
 }
 
-template <bool ROPE, bool DENSE>
+template <int ROPE, bool DENSE>
 __global__ __launch_bounds__(kThreads) void bwd_key_bf16(const u32x4_t* __restrict__ K, const u32x4_t* __restrict__ V,
                                                          u32x4_t* __restrict__ dK, u32x4_t* __restrict__ dV,
                                                          Layout lin, Layout lout, StateView grad, int64_t N,
-                                                         int64_t L, int C, int64_t total, int64_t La,
-                                                         const float* __restrict__ cos_t,
-                                                         const float* __restrict__ sin_t, int64_t pos0) {
+                                                         int64_t L, int C, int64_t total, int64_t La, Rope rp) {
+  __shared__ __attribute__((aligned(16))) float rtab[ROPE == kRopeAxes ? 2 * kMaxAxisTab : 1];
+  rope_stage<ROPE>(rp, rtab, threadIdx.x, kThreads);
+  if constexpr (ROPE == kRopeAxes) __syncthreads();
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int m = lane & 15;
   const int g = lane >> 4;
+  const AxisLane al = axis_lane(rp, g);  // axis form only
   const int64_t irow = DENSE ? 64 : lin.token * 2, orow = DENSE ? 64 : lout.token * 2;  // bytes between tokens
   const int lane_off = m * (int)irow + g * 16;
   const int out_off = m * (int)orow + g * 16;
@@ -458,7 +465,7 @@ __global__ __launch_bounds__(kThreads) void bwd_key_bf16(const u32x4_t* __restri
 
     int64_t t0 = n_begin + 64 * w;
     KeyChunk<ROPE> next;
-    if (t0 < n_end) load_key_chunk<ROPE>(Kh, Vh, irow, t0, n_end, lane_off, tab_off, cos_t, sin_t, pos0, next);
+    if (t0 < n_end) load_key_chunk<ROPE>(Kh, Vh, irow, t0, n_end, lane_off, tab_off, m, g, rp, rtab, al, next);
     const int64_t sc = bh * C + c;
     const float* G = grad.s_base + sc * grad.s_stride;
     const float* Gz = grad.z_base + sc * grad.z_stride;
@@ -472,7 +479,7 @@ __global__ __launch_bounds__(kThreads) void bwd_key_bf16(const u32x4_t* __restri
     for (; t0 < n_end; t0 += 256) {
       const KeyChunk<ROPE> cur = next;
       if (t0 + 256 < n_end)
-        load_key_chunk<ROPE>(Kh, Vh, irow, t0 + 256, n_end, lane_off, tab_off, cos_t, sin_t, pos0, next);
+        load_key_chunk<ROPE>(Kh, Vh, irow, t0 + 256, n_end, lane_off, tab_off, m, g, rp, rtab, al, next);
       const rsrc_t rdk = rows_rsrc(dKh, t0, n_end, orow);
       const rsrc_t rdv = rows_rsrc(dVh, t0, n_end, orow);
 #pragma unroll
@@ -480,12 +487,14 @@ __global__ __launch_bounds__(kThreads) void bwd_key_bf16(const u32x4_t* __restri
         const u32x4_t kr = relu_bf16x8(cur.k[u]);
         f32x4_t o0, o1;
         float x[8];
+        f32x4_t ang_c = cur.c[u], ang_s = cur.sn[u];
+        if constexpr (ROPE == kRopeAxes) rope_axis_row4(rp, rtab, al, rp.pos0 + t0 + 16 * u + m, ang_c, ang_s);
         if constexpr (!ROPE) {
           mfma3(gcol, __builtin_bit_cast(bf16x8_t, kr), o0, o1);
         } else {
           float y[8];
           unpack8(kr, y);
-          rotate8<false>(y, cur.c[u], cur.sn[u]);
+          rotate8<false>(y, ang_c, ang_s);
           bf16x8_t b[3];
           split8(y, b);
           mfma6(gcol, b, o0, o1);
@@ -496,7 +505,7 @@ __global__ __launch_bounds__(kThreads) void bwd_key_bf16(const u32x4_t* __restri
         mfma3(grow, __builtin_bit_cast(bf16x8_t, cur.v[u]), o0, o1);
         x[0] = o0[0], x[1] = o0[1], x[2] = o0[2], x[3] = o0[3];
         x[4] = o1[0], x[5] = o1[1], x[6] = o1[2], x[7] = o1[3];
-        if constexpr (ROPE) rotate8<true>(x, cur.c[u], cur.sn[u]);
+        if constexpr (ROPE) rotate8<true>(x, ang_c, ang_s);
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
           x[2 * p] = (kr[p] & 0xffffu) ? x[2 * p] + gz[2 * p] : 0.f;
@@ -527,16 +536,17 @@ __global__ __launch_bounds__(kThreads) void bwd_key_bf16(const u32x4_t* __restri
 constexpr int kTileRow = 36;                  // padded fp32 row of a 32-feature token
 constexpr int kTileFloats = 32 * kTileRow;    // one 32-token tile
 
-template <bool ROPE>
+template <int ROPE>
 struct QueryTile {
   u32x4_t q[2], dout[2];
   f32x4_t c[2], sn[2];
 };
 
-template <bool ROPE>
+template <int ROPE>
 __device__ __forceinline__ void load_query_tile(const char* Qh, const char* Oh, int64_t row, int64_t t0,
-                                                int64_t n_end, int lane_off, int tab_off, const float* cos_t,
-                                                const float* sin_t, int64_t pos0, QueryTile<ROPE>& tl) {
+                                                int64_t n_end, int lane_off, int tab_off, int m, int g,
+                                                const Rope& rp, const float* rtab, const AxisLane& al,
+                                                QueryTile<ROPE>& tl) {
   const rsrc_t rq = rows_rsrc(Qh, t0, n_end, row);
   const rsrc_t ro = rows_rsrc(Oh, t0, n_end, row);
 #pragma unroll
@@ -544,26 +554,28 @@ __device__ __forceinline__ void load_query_tile(const char* Qh, const char* Oh, 
     tl.q[tb] = load16_nt(rq, lane_off + tb * 16 * (int)row);
     tl.dout[tb] = load16_nt(ro, lane_off + tb * 16 * (int)row);
   }
-  if constexpr (ROPE) {
-    const rsrc_t rc = make_rsrc(cos_t + (pos0 + t0) * 16, (n_end - t0) * 64);
-    const rsrc_t rs = make_rsrc(sin_t + (pos0 + t0) * 16, (n_end - t0) * 64);
+  if constexpr (ROPE == kRopeTable) {
+    const rsrc_t rc = make_rsrc(rp.cos + (rp.pos0 + t0) * 16, (n_end - t0) * 64);
+    const rsrc_t rs = make_rsrc(rp.sin + (rp.pos0 + t0) * 16, (n_end - t0) * 64);
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
       tl.c[tb] = load16(rc, tab_off + tb * 1024);
       tl.sn[tb] = load16(rs, tab_off + tb * 1024);
     }
   }
+  // the axis form's angles come from LDS when the tile is computed
 }
 
-template <bool ROPE, bool DENSE>
+template <int ROPE, bool DENSE>
 __global__ __launch_bounds__(kThreads) void bwd_query_bf16(const u32x4_t* __restrict__ Q,
                                                            const u32x4_t* __restrict__ dO, u32x4_t* __restrict__ dQ,
                                                            Layout lin, Layout lout, StateView fwd, float eps,
-                                                           const float* __restrict__ cos_t,
-                                                           const float* __restrict__ sin_t, int64_t pos0,
-                                                           StateArgs a) {
+                                                           Rope rp, StateArgs a) {
   __shared__ float red[4][kStateElems];
   __shared__ float tiles[4][ROPE ? 2 : 1][kTileFloats];
+  __shared__ __attribute__((aligned(16))) float rtab[ROPE == kRopeAxes ? 2 * kMaxAxisTab : 1];
+  rope_stage<ROPE>(rp, rtab, threadIdx.x, kThreads);
+  if constexpr (ROPE == kRopeAxes) __syncthreads();
 
   int64_t bh, n_begin, n_end;
   int c, s;
@@ -572,6 +584,7 @@ __global__ __launch_bounds__(kThreads) void bwd_query_bf16(const u32x4_t* __rest
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;  // also the token row m of the natural layout
   const int g = lane >> 4;
+  const AxisLane al = axis_lane(rp, g);  // axis form only
   const int64_t irow = DENSE ? 64 : lin.token * 2, orow = DENSE ? 64 : lout.token * 2;  // bytes between tokens
   const int lane_off = n * (int)irow + g * 16;
   const int out_off = n * (int)orow + g * 16;
@@ -584,7 +597,7 @@ __global__ __launch_bounds__(kThreads) void bwd_query_bf16(const u32x4_t* __rest
 
   int64_t t0 = n_begin + 32 * w;
   QueryTile<ROPE> next;
-  if (t0 < n_end) load_query_tile<ROPE>(Qh, Oh, irow, t0, n_end, lane_off, tab_off, cos_t, sin_t, pos0, next);
+  if (t0 < n_end) load_query_tile<ROPE>(Qh, Oh, irow, t0, n_end, lane_off, tab_off, n, g, rp, rtab, al, next);
 
   const int64_t sc = bh * a.C + c;
   const float* S = fwd.s_base + sc * fwd.s_stride;
@@ -608,7 +621,7 @@ __global__ __launch_bounds__(kThreads) void bwd_query_bf16(const u32x4_t* __rest
   for (; t0 < n_end; t0 += 128) {
     const QueryTile<ROPE> cur = next;
     if (t0 + 128 < n_end)
-      load_query_tile<ROPE>(Qh, Oh, irow, t0 + 128, n_end, lane_off, tab_off, cos_t, sin_t, pos0, next);
+      load_query_tile<ROPE>(Qh, Oh, irow, t0 + 128, n_end, lane_off, tab_off, n, g, rp, rtab, al, next);
     const rsrc_t rdq = rows_rsrc(dQh, t0, n_end, orow);
     bf16x8_t bq[2];
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -617,6 +630,8 @@ __global__ __launch_bounds__(kThreads) void bwd_query_bf16(const u32x4_t* __rest
     for (int tb = 0; tb < 2; ++tb) {
       const u32x4_t qr = relu_bf16x8(cur.q[tb]);
       bq[tb] = __builtin_bit_cast(bf16x8_t, qr);
+      f32x4_t ang_c = cur.c[tb], ang_s = cur.sn[tb];
+      if constexpr (ROPE == kRopeAxes) rope_axis_row4(rp, rtab, al, rp.pos0 + t0 + 16 * tb + n, ang_c, ang_s);
       const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
       f32x4_t dacc = mfma16(zrow[0], bq[tb], zero4);
       dacc = mfma16(zrow[1], bq[tb], dacc);
@@ -630,7 +645,7 @@ __global__ __launch_bounds__(kThreads) void bwd_query_bf16(const u32x4_t* __rest
       } else {
 #pragma unroll
         for (int j = 0; j < 8; ++j) y[j] = pq[j];
-        rotate8<false>(y, cur.c[tb], cur.sn[tb]);
+        rotate8<false>(y, ang_c, ang_s);
         bf16x8_t br[3];
         split8(y, br);
         mfma6(scol, br, n0, n1);
@@ -651,7 +666,7 @@ __global__ __launch_bounds__(kThreads) void bwd_query_bf16(const u32x4_t* __rest
       const float dden = -dot * rden * rden;
 #pragma unroll
       for (int j = 0; j < 8; ++j) dr[j] *= rden;
-      if constexpr (ROPE) rotate8<true>(dr, cur.c[tb], cur.sn[tb]);
+      if constexpr (ROPE) rotate8<true>(dr, ang_c, ang_s);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         dr[j] = pq[j] > 0.f ? dr[j] + zf[j] * dden : 0.f;

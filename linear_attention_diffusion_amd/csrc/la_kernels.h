@@ -103,6 +103,120 @@ struct Layout {
 };
 
 // ---------------------------------------------------------------------------
+// RoPE angles
+// ---------------------------------------------------------------------------
+//
+// Pair p of a token at position pos turns by an angle given in one of two
+// forms (the kernels' ROPE template argument):
+//   kRopeTable  cos/sin rows [pos][16] in device memory;
+//   kRopeAxes   SANA-Video's 3D RoPE ("SANA-Video" paper notes, section 3
+//               Stage 2): the latent point of pos = (t * Hl + h) * Wl + w,
+//               pairs 0 .. pt-1 turn with t, the next ph with h, the rest with
+//               w, by angles that depend on that one coordinate; so cos/sin are
+//               per-axis tables [T][pt], [Hl][ph], [Wl][16-pt-ph] back to back
+//               (a few KB; pt and ph even), which each workgroup stages in
+//               LDS.
+// Either way the angle values are the same floats, so the two forms give the
+// same results bit for bit.
+enum { kRopeNone = 0, kRopeTable = 1, kRopeAxes = 2 };
+constexpr int kMaxAxisTab = 1024;  // floats per axis-form table (cos or sin)
+
+struct Rope {
+  const float* cos;
+  const float* sin;
+  int64_t pos0;      // position of token 0
+  int64_t pos_last;  // last position in the call; axis lookups clamp to it
+  int Hl, Wl;        // axis form: latent height and width
+  int pt, ph;        // axis form: pairs turning with t and with h
+  int base_h, base_w;  // axis form: offsets of the h and w tables
+  int n_tab;         // axis form: floats per table
+  double inv_w, inv_hw;  // axis form: 1 / Wl and 1 / (Hl * Wl)
+};
+
+// Axis form: the workgroup copies the tables to LDS as (cos, sin) pairs, entry
+// i at floats 2i, 2i + 1; the caller synchronises before the first lookup.
+template <int ROPE>
+__device__ __forceinline__ void rope_stage(const Rope& r, float* lds, int tid, int nthreads) {
+  if constexpr (ROPE == kRopeAxes) {
+    for (int i = tid; i < r.n_tab; i += nthreads)
+      *reinterpret_cast<float2*>(lds + 2 * i) = float2{r.cos[i], r.sin[i]};
+  }
+}
+
+// Latent coordinates of position pos (clamped to the call's last position),
+// by double-precision reciprocals: floor((n + 1/2) / d) is exact for n < 2^31
+// and d < 2^20, as the fraction stays 1/(2d) away from an integer.  Positions
+// stay below 2^32 (the last is below 2^31, a tile reaches a few past it), so
+// the clamp is 32-bit.
+__device__ __forceinline__ void rope_coords(const Rope& r, int64_t pos, int& t, int& h, int& w) {
+  const unsigned last = (unsigned)r.pos_last;
+  const unsigned n = (unsigned)pos < last ? (unsigned)pos : last;
+  t = (int)__builtin_fma((double)n, r.inv_hw, 0.5 * r.inv_hw);
+  const int rem = (int)n - t * (r.Hl * r.Wl);
+  h = (int)__builtin_fma((double)rem, r.inv_w, 0.5 * r.inv_w);
+  w = rem - h * r.Wl;
+}
+
+// Where pair p's entry sits, as offset + t * wt + h * wh + w * ww: one of the
+// three weights is the pair count of p's axis, the others 0.
+struct AxisPair {
+  int off, wt, wh, ww;
+};
+
+__device__ __forceinline__ AxisPair axis_pair(const Rope& r, int p) {
+  const int pw = 16 - r.pt - r.ph;
+  if (p < r.pt) return AxisPair{p, r.pt, 0, 0};
+  if (p < r.pt + r.ph) return AxisPair{r.base_h + p - r.pt, 0, r.ph, 0};
+  return AxisPair{r.base_w + p - r.pt - r.ph, 0, 0, pw};
+}
+
+__device__ __forceinline__ int axis_entry(const AxisPair& a, int t, int h, int w) {
+  return a.off + t * a.wt + h * a.wh + w * a.ww;
+}
+
+// A lane's pairs 4g .. 4g+3 as two duos (4g, 4g+1) and (4g+2, 4g+3): the axis
+// form has even pair counts per axis, so each duo sits in one axis, at
+// consecutive entries.
+struct AxisLane {
+  AxisPair duo[2];
+};
+
+__device__ __forceinline__ AxisLane axis_lane(const Rope& r, int g) {
+  return AxisLane{{axis_pair(r, 4 * g), axis_pair(r, 4 * g + 2)}};
+}
+
+// cos/sin of pairs 4g .. 4g+3 of position pos from the staged tables: one
+// 16-byte LDS read (cos, sin of both pairs) per duo.
+__device__ __forceinline__ void rope_axis_row4(const Rope& r, const float* lds, const AxisLane& al,
+                                               int64_t pos, f32x4_t& c, f32x4_t& sn) {
+  int t, h, w;
+  rope_coords(r, pos, t, h, w);
+#pragma unroll
+  for (int d = 0; d < 2; ++d) {
+    const f32x4_t e = *reinterpret_cast<const f32x4_t*>(lds + 2 * axis_entry(al.duo[d], t, h, w));
+    c[2 * d] = e[0];
+    sn[2 * d] = e[1];
+    c[2 * d + 1] = e[2];
+    sn[2 * d + 1] = e[3];
+  }
+}
+
+// cos/sin of pair p of position pos, in either form (`lds`: the staged tables).
+template <int ROPE>
+__device__ __forceinline__ void rope_pair(const Rope& r, const float* lds, int64_t pos, int p, float& c, float& sn) {
+  if constexpr (ROPE == kRopeAxes) {
+    int t, h, w;
+    rope_coords(r, pos, t, h, w);
+    const float2 e = *reinterpret_cast<const float2*>(lds + 2 * axis_entry(axis_pair(r, p), t, h, w));
+    c = e.x;
+    sn = e.y;
+  } else {
+    c = r.cos[pos * 16 + p];
+    sn = r.sin[pos * 16 + p];
+  }
+}
+
+// ---------------------------------------------------------------------------
 // bf16 helpers
 // ---------------------------------------------------------------------------
 
@@ -498,14 +612,15 @@ __device__ __forceinline__ void state_tile(const u32x4_t (&kx)[2], const u32x4_t
 
 // DENSE: consecutive tokens are adjacent 64-byte rows (token stride = 32
 // elements), so every tile offset is an instruction immediate.
-template <bool ROPE, bool DENSE, int HEADS>
+template <int ROPE, bool DENSE, int HEADS>
 __global__ __launch_bounds__(kThreads* HEADS) void state_bf16(const u32x4_t* __restrict__ K,
-                                                              const u32x4_t* __restrict__ V, Layout lkv,
-                                                              const float* __restrict__ cos_t,
-                                                              const float* __restrict__ sin_t, int64_t pos0,
+                                                              const u32x4_t* __restrict__ V, Layout lkv, Rope rp,
                                                               StateArgs a, int64_t BH) {
   __shared__ float red[4 * HEADS][kStateElems];
   __shared__ float angles[ROPE ? 4 * HEADS : 1][ROPE ? kAngTile : 1];
+  __shared__ __attribute__((aligned(16))) float rtab[ROPE == kRopeAxes ? 2 * kMaxAxisTab : 1];
+  rope_stage<ROPE>(rp, rtab, threadIdx.x, kThreads * HEADS);
+  if constexpr (ROPE == kRopeAxes) __syncthreads();
 
   int64_t bh, n_begin, n_end;
   int c, s;
@@ -518,6 +633,7 @@ __global__ __launch_bounds__(kThreads* HEADS) void state_bf16(const u32x4_t* __r
   const bool active = bh < BH;
   const int n = lane & 15;
   const int g = lane >> 4;
+  const AxisLane al = axis_lane(rp, g);  // axis form only
 
   // lane's 16-byte piece of a row: features 8g .. 8g+7 of token (tile row) n
   const int64_t row = DENSE ? 64 : lkv.token * 2;  // bytes between tokens
@@ -549,10 +665,11 @@ __global__ __launch_bounds__(kThreads* HEADS) void state_bf16(const u32x4_t* __r
       nk[h] = load16_stream<HEADS>(rk, lane_off + h * 16 * (int)row);
       nv[h] = load16_stream<HEADS>(rv, lane_off + h * 16 * (int)row);
     }
-    if constexpr (ROPE) {
-      load_angle_rows(cos_t, sin_t, pos0, c0, n_end, tab_off, na[0]);
-      load_angle_rows(cos_t, sin_t, pos0, c0 + 32, n_end, tab_off, na[1]);
+    if constexpr (ROPE == kRopeTable) {
+      load_angle_rows(rp.cos, rp.sin, rp.pos0, c0, n_end, tab_off, na[0]);
+      load_angle_rows(rp.cos, rp.sin, rp.pos0, c0 + 32, n_end, tab_off, na[1]);
     }
+    // the axis form's angles come from LDS when the tile is computed
   };
   float* lds = angles[ROPE ? wg : 0];
   if (!active) t0 = n_end;
@@ -560,10 +677,17 @@ __global__ __launch_bounds__(kThreads* HEADS) void state_bf16(const u32x4_t* __r
   for (; t0 < n_end; t0 += 256) {
     const u32x4_t ka[2] = {nk[0], nk[1]}, va[2] = {nv[0], nv[1]};
     const u32x4_t kb[2] = {nk[2], nk[3]}, vb[2] = {nv[2], nv[3]};
-    const TileAnglesRows ra = na[0], rb = na[1];
+    TileAnglesRows ra = na[0], rb = na[1];
     if (t0 + 256 < n_end) load_chunk(t0 + 256);
-    state_tile<ROPE>(ka, va, ra, g, n, lds, sel, selp, acc, accz);
-    if (t0 + 32 < n_end) state_tile<ROPE>(kb, vb, rb, g, n, lds, sel, selp, acc, accz);
+    if constexpr (ROPE == kRopeAxes) {
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        rope_axis_row4(rp, rtab, al, rp.pos0 + t0 + 16 * tb + n, ra.c[tb], ra.s[tb]);
+        rope_axis_row4(rp, rtab, al, rp.pos0 + t0 + 32 + 16 * tb + n, rb.c[tb], rb.s[tb]);
+      }
+    }
+    state_tile<ROPE != 0>(ka, va, ra, g, n, lds, sel, selp, acc, accz);
+    if (t0 + 32 < n_end) state_tile<ROPE != 0>(kb, vb, rb, g, n, lds, sel, selp, acc, accz);
   }
 
   // D lane (n, g): rows 4g + i -> key feature 16fh + 4g + i, column n -> value feature 16fh' + n
@@ -590,15 +714,16 @@ __global__ __launch_bounds__(kThreads* HEADS) void state_bf16(const u32x4_t* __r
 // ---------------------------------------------------------------------------
 // fp32 state pass (VALU): each thread owns S[d][e0..e0+3] (and z[d])
 // ---------------------------------------------------------------------------
-template <bool ROPE>
+template <int ROPE>
 __global__ __launch_bounds__(kThreads) void state_f32(const float* __restrict__ K, const float* __restrict__ V,
-                                                      Layout lkv, const float* __restrict__ cos_t,
-                                                      const float* __restrict__ sin_t, int64_t pos0,
-                                                      StateArgs a) {
+                                                      Layout lkv, Rope rp, StateArgs a) {
   __shared__ float sk[64][kD + 1];   // phi(K), un-rotated
   __shared__ float skr[64][kD + 1];  // phi~(K), rotated (RoPE only)
   __shared__ float sv[64][kD + 1];
   __shared__ float mine[kStateElems];
+  __shared__ __attribute__((aligned(16))) float rtab[ROPE == kRopeAxes ? 2 * kMaxAxisTab : 1];
+  rope_stage<ROPE>(rp, rtab, threadIdx.x, kThreads);
+  if constexpr (ROPE == kRopeAxes) __syncthreads();
 
   int64_t bh, n_begin, n_end;
   int c, s;
@@ -632,10 +757,7 @@ __global__ __launch_bounds__(kThreads) void state_f32(const float* __restrict__ 
       sv[tok][2 * p + 1] = v1;
       if constexpr (ROPE) {
         float c = 1.f, sn = 0.f;
-        if (gt < n_end) {
-          c = cos_t[(pos0 + gt) * 16 + p];
-          sn = sin_t[(pos0 + gt) * 16 + p];
-        }
+        if (gt < n_end) rope_pair<ROPE>(rp, rtab, rp.pos0 + gt, p, c, sn);
         skr[tok][2 * p] = k0 * c - k1 * sn;
         skr[tok][2 * p + 1] = k0 * sn + k1 * c;
       }
@@ -763,46 +885,49 @@ __device__ __forceinline__ u32x4_t apply_tile(u32x4_t q, const ApplyOperands& op
 
 // The four 16-token tiles of a wave's 64-token chunk at t0 (this lane: token
 // t0 + 16u + m, features 8g .. 8g+7), with cos/sin of its pairs under RoPE.
-template <bool ROPE>
+template <int ROPE>
 struct ApplyChunk {
   u32x4_t q[4];
   f32x4_t c[4], sn[4];
 };
 
 // Rows at or past n_end read 0; their outputs are not stored.
-template <bool ROPE, int HEADS>
+template <int ROPE, int HEADS>
 __device__ __forceinline__ void load_apply_chunk(const char* Qh, int64_t row, int64_t t0, int64_t n_end,
-                                                 int lane_off, int tab_off, const float* cos_t,
-                                                 const float* sin_t, int64_t pos0, ApplyChunk<ROPE>& ch) {
+                                                 int lane_off, int tab_off, int m, int g, const Rope& rp,
+                                                 const float* rtab, ApplyChunk<ROPE>& ch) {
   const rsrc_t rq = rows_rsrc(Qh, t0, n_end, row);
 #pragma unroll
   for (int u = 0; u < 4; ++u) ch.q[u] = load16_stream<HEADS>(rq, lane_off + u * 16 * (int)row);
-  if constexpr (ROPE) {
+  if constexpr (ROPE == kRopeTable) {
     // pairs 4g .. 4g+3 of the token at position pos0 + t0 + 16u + m: the same
     // lane offset in a 64-byte table row
-    const rsrc_t rc = make_rsrc(cos_t + (pos0 + t0) * 16, (n_end - t0) * 64);
-    const rsrc_t rs = make_rsrc(sin_t + (pos0 + t0) * 16, (n_end - t0) * 64);
+    const rsrc_t rc = make_rsrc(rp.cos + (rp.pos0 + t0) * 16, (n_end - t0) * 64);
+    const rsrc_t rs = make_rsrc(rp.sin + (rp.pos0 + t0) * 16, (n_end - t0) * 64);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       ch.c[u] = load16(rc, tab_off + u * 1024);
       ch.sn[u] = load16(rs, tab_off + u * 1024);
     }
   }
+  // the axis form's angles come from LDS when the tile is computed
 }
 
-template <bool ROPE, bool DENSE, int HEADS>
+template <int ROPE, bool DENSE, int HEADS>
 __global__ __launch_bounds__(kThreads* HEADS) void apply_bf16(const u32x4_t* __restrict__ Q, u32x4_t* __restrict__ O,
                                                               Layout lq, Layout lo, StateView sv, int64_t N,
                                                               int64_t L, int C, int64_t total, int64_t La, float eps,
-                                                              const float* __restrict__ cos_t,
-                                                              const float* __restrict__ sin_t, int64_t pos0,
-                                                              int64_t BH) {
+                                                              Rope rp, int64_t BH) {
+  __shared__ __attribute__((aligned(16))) float rtab[ROPE == kRopeAxes ? 2 * kMaxAxisTab : 1];
+  rope_stage<ROPE>(rp, rtab, threadIdx.x, kThreads * HEADS);
+  if constexpr (ROPE == kRopeAxes) __syncthreads();
   const int lane = threadIdx.x & 63;
   const int wg = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int half = wg >> 2;
   const int w = wg & 3;
   const int m = lane & 15;
   const int g = lane >> 4;
+  const AxisLane al = axis_lane(rp, g);  // axis form only
   const int64_t qrow = DENSE ? 64 : lq.token * 2, orow = DENSE ? 64 : lo.token * 2;  // bytes between tokens
   const int q_off = m * (int)qrow + g * 16;                // features 8g .. 8g+7 of tile row m
   const int o_off = m * (int)orow + g * 16;
@@ -835,7 +960,7 @@ __global__ __launch_bounds__(kThreads* HEADS) void apply_bf16(const u32x4_t* __r
     // and each chunk's loads before the previous chunk is computed
     int64_t t0 = n_begin + 64 * w;
     ApplyChunk<ROPE> next;
-    if (t0 < n_end) load_apply_chunk<ROPE, HEADS>(Qh, qrow, t0, n_end, q_off, tab_off, cos_t, sin_t, pos0, next);
+    if (t0 < n_end) load_apply_chunk<ROPE, HEADS>(Qh, qrow, t0, n_end, q_off, tab_off, m, g, rp, rtab, next);
     ApplyOperands op;
     const int64_t sc = bh * C + c;
     load_apply_operands(sv.s_base + sc * sv.s_stride, sv.z_base + sc * sv.z_stride, g, m, op);
@@ -843,11 +968,14 @@ __global__ __launch_bounds__(kThreads* HEADS) void apply_bf16(const u32x4_t* __r
     for (; t0 < n_end; t0 += 256) {
       const ApplyChunk<ROPE> cur = next;
       if (t0 + 256 < n_end)
-        load_apply_chunk<ROPE, HEADS>(Qh, qrow, t0 + 256, n_end, q_off, tab_off, cos_t, sin_t, pos0, next);
+        load_apply_chunk<ROPE, HEADS>(Qh, qrow, t0 + 256, n_end, q_off, tab_off, m, g, rp, rtab, next);
       const rsrc_t ro = rows_rsrc(Oh, t0, n_end, orow);
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        store16_nt(ro, o_off + u * 16 * (int)orow, apply_tile<ROPE>(cur.q[u], op, eps, cur.c[u], cur.sn[u]));
+      for (int u = 0; u < 4; ++u) {
+        f32x4_t c = cur.c[u], sn = cur.sn[u];
+        if constexpr (ROPE == kRopeAxes) rope_axis_row4(rp, rtab, al, rp.pos0 + t0 + 16 * u + m, c, sn);
+        store16_nt(ro, o_off + u * 16 * (int)orow, apply_tile<ROPE != 0>(cur.q[u], op, eps, c, sn));
+      }
     }
   }
 }
@@ -856,14 +984,14 @@ __global__ __launch_bounds__(kThreads* HEADS) void apply_bf16(const u32x4_t* __r
 // fp32 apply pass (VALU): thread = (token, 4 output features)
 // ---------------------------------------------------------------------------
 // Workgroup (bh, c, tile) applies tokens [c*L + tile*Lt, ...) of chunk c.
-template <bool ROPE>
+template <int ROPE>
 __global__ __launch_bounds__(kThreads) void apply_f32(const float* __restrict__ Q, float* __restrict__ O,
                                                       Layout lq, Layout lo, StateView sv, int64_t N, int64_t L,
-                                                      int C, int T,
-                                                      int64_t Lt, float eps, const float* __restrict__ cos_t,
-                                                      const float* __restrict__ sin_t, int64_t pos0) {
+                                                      int C, int T, int64_t Lt, float eps, Rope rp) {
   __shared__ float sS[kD][kD];
   __shared__ float sz[kD];
+  __shared__ __attribute__((aligned(16))) float rtab[ROPE == kRopeAxes ? 2 * kMaxAxisTab : 1];
+  rope_stage<ROPE>(rp, rtab, threadIdx.x, kThreads);
   const int64_t bh = blockIdx.x / ((int64_t)C * T);
   const int r = (int)(blockIdx.x % ((int64_t)C * T));
   const int c = r / T;
@@ -890,8 +1018,8 @@ __global__ __launch_bounds__(kThreads) void apply_f32(const float* __restrict__ 
 #pragma unroll
     for (int p = 0; p < 16; ++p) {
       if constexpr (ROPE) {
-        const float c = cos_t[(pos0 + tok) * 16 + p];
-        const float sn = sin_t[(pos0 + tok) * 16 + p];
+        float c, sn;
+        rope_pair<ROPE>(rp, rtab, rp.pos0 + tok, p, c, sn);
         pr[2 * p] = pq[2 * p] * c - pq[2 * p + 1] * sn;
         pr[2 * p + 1] = pq[2 * p] * sn + pq[2 * p + 1] * c;
       } else {

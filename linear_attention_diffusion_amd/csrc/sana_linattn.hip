@@ -25,6 +25,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <type_traits>
 
 #include "la_backward.h"
 #include "la_conv.h"
@@ -128,13 +129,30 @@ int check_sizes(int B, int H, int64_t N, int D, int dtype, int64_t* BH, int64_t*
   return SANA_OK;
 }
 
+// A RoPE argument in the per-axis form names a latent grid.
+bool axis_form(const sana_rope* rope) { return rope->grid[0] != 0 || rope->grid[1] != 0 || rope->grid[2] != 0; }
+
 int check_rope(const sana_rope* rope, int64_t N) {
   if (!rope) return SANA_OK;
   if (!rope->cos || !rope->sin) return SANA_ERR_INVALID;
-  if (!aligned(rope->cos, 16) || !aligned(rope->sin, 16)) return SANA_ERR_INVALID;
   if (rope->pos_offset < 0 || rope->n_pos < 0) return SANA_ERR_INVALID;
   if (rope->pos_offset > rope->n_pos || N > rope->n_pos - rope->pos_offset) return SANA_ERR_INVALID;
-  return SANA_OK;
+  if (!axis_form(rope)) {
+    if (rope->pairs[0] || rope->pairs[1] || rope->pairs[2]) return SANA_ERR_INVALID;
+    return aligned(rope->cos, 16) && aligned(rope->sin, 16) ? SANA_OK : SANA_ERR_INVALID;
+  }
+  // per-axis tables: positions are the grid's points, the pairs split the
+  // head's 16 in even counts, the tables fit the kernels' LDS copy, and the coordinates of a
+  // position come out exact (grid plane below 2^20 points, positions below 2^31)
+  const int64_t T = rope->grid[0], Hl = rope->grid[1], Wl = rope->grid[2];
+  const int64_t pt = rope->pairs[0], ph = rope->pairs[1], pw = rope->pairs[2];
+  if (T <= 0 || Hl <= 0 || Wl <= 0 || pt < 0 || ph < 0 || pw < 0 || pt + ph + pw != la::kD / 2)
+    return SANA_ERR_INVALID;
+  if (pt % 2 || ph % 2) return SANA_ERR_INVALID;  // pairs (2i, 2i+1) share an axis
+  if (Hl * Wl >= ((int64_t)1 << 20) || T * Hl * Wl >= ((int64_t)1 << 31) || rope->n_pos != T * Hl * Wl)
+    return SANA_ERR_INVALID;
+  if (T * pt + Hl * ph + Wl * pw > la::kMaxAxisTab) return SANA_ERR_INVALID;
+  return aligned(rope->cos, 4) && aligned(rope->sin, 4) ? SANA_OK : SANA_ERR_INVALID;
 }
 
 // Grid bounds of the state pass and the fp32 apply pass.
@@ -253,38 +271,71 @@ la::StateView ws_view(const la::StateArgs& a) {
 // heads of the same tokens.
 bool paired_heads(const la::Layout& l) { return l.head == la::kD; }
 
+// The kernels' view of a call's RoPE argument: its form (la::kRopeNone,
+// kRopeTable or kRopeAxes) and the angle source.  N: tokens in the call.
+struct RopeArg {
+  int kind = la::kRopeNone;
+  la::Rope r{};
+};
+
+RopeArg rope_arg(const sana_rope* rope, int64_t N) {
+  RopeArg a;
+  if (!rope) return a;
+  a.r.cos = rope->cos;
+  a.r.sin = rope->sin;
+  a.r.pos0 = rope->pos_offset;
+  a.r.pos_last = rope->pos_offset + (N > 0 ? N - 1 : 0);
+  if (!axis_form(rope)) {
+    a.kind = la::kRopeTable;
+    return a;
+  }
+  a.kind = la::kRopeAxes;
+  const int T = rope->grid[0], Hl = rope->grid[1], Wl = rope->grid[2];
+  a.r.Hl = Hl;
+  a.r.Wl = Wl;
+  a.r.pt = rope->pairs[0];
+  a.r.ph = rope->pairs[1];
+  a.r.base_h = T * rope->pairs[0];
+  a.r.base_w = a.r.base_h + Hl * rope->pairs[1];
+  a.r.n_tab = a.r.base_w + Wl * rope->pairs[2];
+  a.r.inv_w = 1.0 / Wl;
+  a.r.inv_hw = 1.0 / ((double)Hl * Wl);
+  return a;
+}
+
+// Calls f(std::integral_constant<int, kind>) for the RoPE form `kind`, so a
+// launch site names each kernel once for all three forms.
+template <typename F>
+void with_rope(int kind, F&& f) {
+  if (kind == la::kRopeAxes)
+    f(std::integral_constant<int, la::kRopeAxes>{});
+  else if (kind == la::kRopeTable)
+    f(std::integral_constant<int, la::kRopeTable>{});
+  else
+    f(std::integral_constant<int, la::kRopeNone>{});
+}
+
 // State pass, and the finalize when there are several partials per head.
 void launch_state(const void* k, const void* v, const la::Layout& lkv, int dtype, const Geometry& g,
-                  const sana_rope* rope, const la::StateArgs& a, hipStream_t st) {
-  const float* ct = rope ? rope->cos : nullptr;
-  const float* sn = rope ? rope->sin : nullptr;
-  const int64_t pos0 = rope ? rope->pos_offset : 0;
+                  const RopeArg& ra, const la::StateArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)(g.BH * g.C * g.Pc)), block(la::kThreads);
-  if (dtype == SANA_DT_BF16) {
-    const la::u32x4_t* K = static_cast<const la::u32x4_t*>(k);
-    const la::u32x4_t* V = static_cast<const la::u32x4_t*>(v);
-    const bool dense = lkv.token == la::kD;
-    const dim3 pgrid((unsigned)(ceil_div(g.BH, 2) * g.C * g.Pc)), pblock(2 * la::kThreads);
-    if (rope && dense)
-      la::state_bf16<true, true, 1><<<grid, block, 0, st>>>(K, V, lkv, ct, sn, pos0, a, g.BH);
-    else if (rope && paired_heads(lkv))
-      la::state_bf16<true, false, 2><<<pgrid, pblock, 0, st>>>(K, V, lkv, ct, sn, pos0, a, g.BH);
-    else if (rope)
-      la::state_bf16<true, false, 1><<<grid, block, 0, st>>>(K, V, lkv, ct, sn, pos0, a, g.BH);
-    else if (dense)
-      la::state_bf16<false, true, 1><<<grid, block, 0, st>>>(K, V, lkv, ct, sn, pos0, a, g.BH);
-    else if (paired_heads(lkv))
-      la::state_bf16<false, false, 2><<<pgrid, pblock, 0, st>>>(K, V, lkv, ct, sn, pos0, a, g.BH);
-    else
-      la::state_bf16<false, false, 1><<<grid, block, 0, st>>>(K, V, lkv, ct, sn, pos0, a, g.BH);
-  } else {
-    const float* K = static_cast<const float*>(k);
-    const float* V = static_cast<const float*>(v);
-    if (rope)
-      la::state_f32<true><<<grid, block, 0, st>>>(K, V, lkv, ct, sn, pos0, a);
-    else
-      la::state_f32<false><<<grid, block, 0, st>>>(K, V, lkv, ct, sn, pos0, a);
-  }
+  with_rope(ra.kind, [&](auto R) {
+    constexpr int RO = decltype(R)::value;
+    if (dtype == SANA_DT_BF16) {
+      const la::u32x4_t* K = static_cast<const la::u32x4_t*>(k);
+      const la::u32x4_t* V = static_cast<const la::u32x4_t*>(v);
+      const dim3 pgrid((unsigned)(ceil_div(g.BH, 2) * g.C * g.Pc)), pblock(2 * la::kThreads);
+      if (lkv.token == la::kD)
+        la::state_bf16<RO, true, 1><<<grid, block, 0, st>>>(K, V, lkv, ra.r, a, g.BH);
+      else if (paired_heads(lkv))
+        la::state_bf16<RO, false, 2><<<pgrid, pblock, 0, st>>>(K, V, lkv, ra.r, a, g.BH);
+      else
+        la::state_bf16<RO, false, 1><<<grid, block, 0, st>>>(K, V, lkv, ra.r, a, g.BH);
+    } else {
+      la::state_f32<RO><<<grid, block, 0, st>>>(static_cast<const float*>(k), static_cast<const float*>(v), lkv,
+                                                ra.r, a);
+    }
+  });
   if (g.C * g.Pc > 1) {
     const int64_t n_elems = g.BH * la::kStateElems;
     la::state_finalize<<<dim3((unsigned)ceil_div(n_elems, la::kThreads)), dim3(la::kThreads), 0, st>>>(a, n_elems);
@@ -292,47 +343,33 @@ void launch_state(const void* k, const void* v, const la::Layout& lkv, int dtype
 }
 
 void launch_apply(const void* q, void* o, const la::Layout& lq, const la::Layout& lo, int dtype, float eps,
-                  const Geometry& g, const sana_rope* rope,
-                  const la::StateView& sv, hipStream_t st) {
-  const float* ct = rope ? rope->cos : nullptr;
-  const float* sn = rope ? rope->sin : nullptr;
-  const int64_t pos0 = rope ? rope->pos_offset : 0;
-  if (dtype == SANA_DT_BF16) {
-    const la::u32x4_t* Q = static_cast<const la::u32x4_t*>(q);
-    la::u32x4_t* O = static_cast<la::u32x4_t*>(o);
-    const bool dense = lq.token == la::kD && lo.token == la::kD;
-    const bool pair = !dense && (paired_heads(lq) || paired_heads(lo));
-    // ranges of g.La tokens over (head, token), or per head pair
-    const int64_t units = pair ? ceil_div(g.BH, 2) : g.BH;
-    const dim3 grid((unsigned)(pair ? units * ceil_div(g.N, g.La) : ceil_div(units * g.N, g.La))),
-        block(pair ? 2 * la::kThreads : la::kThreads);
-#define LA_APPLY(R, DN, HD)                                                                                     \
-  la::apply_bf16<R, DN, HD><<<grid, block, 0, st>>>(Q, O, lq, lo, sv, g.N, g.L, (int)g.C, units * g.N, g.La, eps, \
-                                                    ct, sn, pos0, g.BH)
-    if (rope && dense)
-      LA_APPLY(true, true, 1);
-    else if (rope && pair)
-      LA_APPLY(true, false, 2);
-    else if (rope)
-      LA_APPLY(true, false, 1);
-    else if (dense)
-      LA_APPLY(false, true, 1);
-    else if (pair)
-      LA_APPLY(false, false, 2);
-    else
-      LA_APPLY(false, false, 1);
-#undef LA_APPLY
-  } else {
-    const dim3 grid((unsigned)(g.BH * g.C * g.T)), block(la::kThreads);
-    const float* Q = static_cast<const float*>(q);
-    float* O = static_cast<float*>(o);
-    if (rope)
-      la::apply_f32<true><<<grid, block, 0, st>>>(Q, O, lq, lo, sv, g.N, g.L, (int)g.C, (int)g.T, g.Lt, eps, ct, sn,
-                                                 pos0);
-    else
-      la::apply_f32<false><<<grid, block, 0, st>>>(Q, O, lq, lo, sv, g.N, g.L, (int)g.C, (int)g.T, g.Lt, eps, ct, sn,
-                                                 pos0);
-  }
+                  const Geometry& g, const RopeArg& ra, const la::StateView& sv, hipStream_t st) {
+  with_rope(ra.kind, [&](auto R) {
+    constexpr int RO = decltype(R)::value;
+    if (dtype == SANA_DT_BF16) {
+      const la::u32x4_t* Q = static_cast<const la::u32x4_t*>(q);
+      la::u32x4_t* O = static_cast<la::u32x4_t*>(o);
+      const bool dense = lq.token == la::kD && lo.token == la::kD;
+      const bool pair = !dense && (paired_heads(lq) || paired_heads(lo));
+      // ranges of g.La tokens over (head, token), or per head pair
+      const int64_t units = pair ? ceil_div(g.BH, 2) : g.BH;
+      const dim3 grid((unsigned)(pair ? units * ceil_div(g.N, g.La) : ceil_div(units * g.N, g.La))),
+          block(pair ? 2 * la::kThreads : la::kThreads);
+      if (dense)
+        la::apply_bf16<RO, true, 1><<<grid, block, 0, st>>>(Q, O, lq, lo, sv, g.N, g.L, (int)g.C, units * g.N, g.La,
+                                                            eps, ra.r, g.BH);
+      else if (pair)
+        la::apply_bf16<RO, false, 2><<<grid, block, 0, st>>>(Q, O, lq, lo, sv, g.N, g.L, (int)g.C, units * g.N, g.La,
+                                                             eps, ra.r, g.BH);
+      else
+        la::apply_bf16<RO, false, 1><<<grid, block, 0, st>>>(Q, O, lq, lo, sv, g.N, g.L, (int)g.C, units * g.N, g.La,
+                                                             eps, ra.r, g.BH);
+    } else {
+      const dim3 grid((unsigned)(g.BH * g.C * g.T)), block(la::kThreads);
+      la::apply_f32<RO><<<grid, block, 0, st>>>(static_cast<const float*>(q), static_cast<float*>(o), lq, lo, sv, g.N,
+                                                g.L, (int)g.C, (int)g.T, g.Lt, eps, ra.r);
+    }
+  });
 }
 
 int launch_status() { return hipGetLastError() == hipSuccess ? SANA_OK : SANA_ERR_HIP; }
@@ -366,51 +403,38 @@ int attend(const void* q, const void* k, const void* v, void* o, const sana_layo
 
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   const la::StateArgs a = state_args(ws, g, kv_in, ksum_in, kv_out, ksum_out);
-  launch_state(k, v, vin.lay, dtype, g, rope, a, st);
-  launch_apply(q, o, vin.lay, vout.lay, dtype, eps, g, rope, ws_view(a), st);
+  const RopeArg ra = rope_arg(rope, N);
+  launch_state(k, v, vin.lay, dtype, g, ra, a, st);
+  launch_apply(q, o, vin.lay, vout.lay, dtype, eps, g, ra, ws_view(a), st);
   return launch_status();
 }
 
 // Key pass of the backward: dK, dV from the state gradient G_c of every chunk.
 void launch_key_pass(const void* k, const void* v, void* dk, void* dv, const la::Layout& lin,
-                     const la::Layout& lout, int dtype, const Geometry& g, const sana_rope* rope,
+                     const la::Layout& lout, int dtype, const Geometry& g, const RopeArg& ra,
                      const la::StateView& view, hipStream_t st) {
-  const float* ct = rope ? rope->cos : nullptr;
-  const float* sn = rope ? rope->sin : nullptr;
-  const int64_t pos0 = rope ? rope->pos_offset : 0;
   const dim3 block(la::kThreads);
-  if (dtype == SANA_DT_BF16) {
-    const dim3 kgrid((unsigned)g.Ga);
-    const auto* K = static_cast<const la::u32x4_t*>(k);
-    const auto* V = static_cast<const la::u32x4_t*>(v);
-    auto* dK = static_cast<la::u32x4_t*>(dk);
-    auto* dV = static_cast<la::u32x4_t*>(dv);
-    const bool dense = lin.token == la::kD && lout.token == la::kD;
-#define LA_KEY(R, DN)                                                                                        \
-  la::bwd_key_bf16<R, DN><<<kgrid, block, 0, st>>>(K, V, dK, dV, lin, lout, view, g.N, g.L, (int)g.C, g.BH * g.N, \
-                                                   g.La, ct, sn, pos0)
-    if (rope && dense)
-      LA_KEY(true, true);
-    else if (rope)
-      LA_KEY(true, false);
-    else if (dense)
-      LA_KEY(false, true);
-    else
-      LA_KEY(false, false);
-#undef LA_KEY
-  } else {
-    const dim3 kgrid((unsigned)(g.BH * g.C * g.T));
-    const auto* K = static_cast<const float*>(k);
-    const auto* V = static_cast<const float*>(v);
-    auto* dK = static_cast<float*>(dk);
-    auto* dV = static_cast<float*>(dv);
-    if (rope)
-      la::bwd_key_vec<true><<<kgrid, block, 0, st>>>(K, V, dK, dV, lin, lout, view, g.N, g.L, (int)g.C, (int)g.T, g.Lt,
-                                                              ct, sn, pos0);
-    else
-      la::bwd_key_vec<false><<<kgrid, block, 0, st>>>(K, V, dK, dV, lin, lout, view, g.N, g.L, (int)g.C, (int)g.T,
-                                                               g.Lt, ct, sn, pos0);
-  }
+  with_rope(ra.kind, [&](auto R) {
+    constexpr int RO = decltype(R)::value;
+    if (dtype == SANA_DT_BF16) {
+      const dim3 kgrid((unsigned)g.Ga);
+      const auto* K = static_cast<const la::u32x4_t*>(k);
+      const auto* V = static_cast<const la::u32x4_t*>(v);
+      auto* dK = static_cast<la::u32x4_t*>(dk);
+      auto* dV = static_cast<la::u32x4_t*>(dv);
+      if (lin.token == la::kD && lout.token == la::kD)
+        la::bwd_key_bf16<RO, true><<<kgrid, block, 0, st>>>(K, V, dK, dV, lin, lout, view, g.N, g.L, (int)g.C,
+                                                            g.BH * g.N, g.La, ra.r);
+      else
+        la::bwd_key_bf16<RO, false><<<kgrid, block, 0, st>>>(K, V, dK, dV, lin, lout, view, g.N, g.L, (int)g.C,
+                                                             g.BH * g.N, g.La, ra.r);
+    } else {
+      const dim3 kgrid((unsigned)(g.BH * g.C * g.T));
+      la::bwd_key_vec<RO><<<kgrid, block, 0, st>>>(static_cast<const float*>(k), static_cast<const float*>(v),
+                                                   static_cast<float*>(dk), static_cast<float*>(dv), lin, lout, view,
+                                                   g.N, g.L, (int)g.C, (int)g.T, g.Lt, ra.r);
+    }
+  });
 }
 
 // Backward: recompute the chunk states (state pass + finalize), then the query
@@ -419,41 +443,31 @@ void launch_key_pass(const void* k, const void* v, void* dk, void* dv, const la:
 // forward's: the query pass reuses the partials, the reverse finalize
 // overwrites the chunk states with G_c once the query pass has read them.
 void launch_backward(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk, void* dv,
-                     const la::Layout& lin, const la::Layout& lout, int dtype, float eps, const Geometry& g, const sana_rope* rope, const la::StateArgs& fwd,
-                     const la::StateArgs& bwd, hipStream_t st) {
-  const float* ct = rope ? rope->cos : nullptr;
-  const float* sn = rope ? rope->sin : nullptr;
-  const int64_t pos0 = rope ? rope->pos_offset : 0;
+                     const la::Layout& lin, const la::Layout& lout, int dtype, float eps, const Geometry& g,
+                     const RopeArg& ra, const la::StateArgs& fwd, const la::StateArgs& bwd, hipStream_t st) {
   const la::StateView view = ws_view(fwd);
   const dim3 block(la::kThreads);
   const dim3 qgrid((unsigned)(g.BH * g.C * g.Pc));
-  if (dtype == SANA_DT_BF16) {
-    const auto* Q = static_cast<const la::u32x4_t*>(q);
-    const auto* dO = static_cast<const la::u32x4_t*>(dout);
-    auto* dQ = static_cast<la::u32x4_t*>(dq);
-    const bool dense = lin.token == la::kD && lout.token == la::kD;
-    if (rope && dense)
-      la::bwd_query_bf16<true, true><<<qgrid, block, 0, st>>>(Q, dO, dQ, lin, lout, view, eps, ct, sn, pos0, bwd);
-    else if (rope)
-      la::bwd_query_bf16<true, false><<<qgrid, block, 0, st>>>(Q, dO, dQ, lin, lout, view, eps, ct, sn, pos0, bwd);
-    else if (dense)
-      la::bwd_query_bf16<false, true><<<qgrid, block, 0, st>>>(Q, dO, dQ, lin, lout, view, eps, ct, sn, pos0, bwd);
-    else
-      la::bwd_query_bf16<false, false><<<qgrid, block, 0, st>>>(Q, dO, dQ, lin, lout, view, eps, ct, sn, pos0, bwd);
-  } else {
-    const auto* Q = static_cast<const float*>(q);
-    const auto* dO = static_cast<const float*>(dout);
-    auto* dQ = static_cast<float*>(dq);
-    if (rope)
-      la::bwd_query_vec<true><<<qgrid, block, 0, st>>>(Q, dO, dQ, lin, lout, view, eps, ct, sn, pos0, bwd);
-    else
-      la::bwd_query_vec<false><<<qgrid, block, 0, st>>>(Q, dO, dQ, lin, lout, view, eps, ct, sn, pos0, bwd);
-  }
+  with_rope(ra.kind, [&](auto R) {
+    constexpr int RO = decltype(R)::value;
+    if (dtype == SANA_DT_BF16) {
+      const auto* Q = static_cast<const la::u32x4_t*>(q);
+      const auto* dO = static_cast<const la::u32x4_t*>(dout);
+      auto* dQ = static_cast<la::u32x4_t*>(dq);
+      if (lin.token == la::kD && lout.token == la::kD)
+        la::bwd_query_bf16<RO, true><<<qgrid, block, 0, st>>>(Q, dO, dQ, lin, lout, view, eps, ra.r, bwd);
+      else
+        la::bwd_query_bf16<RO, false><<<qgrid, block, 0, st>>>(Q, dO, dQ, lin, lout, view, eps, ra.r, bwd);
+    } else {
+      la::bwd_query_vec<RO><<<qgrid, block, 0, st>>>(static_cast<const float*>(q), static_cast<const float*>(dout),
+                                                     static_cast<float*>(dq), lin, lout, view, eps, ra.r, bwd);
+    }
+  });
   if (g.C * g.Pc > 1) {
     const int64_t n_elems = g.BH * la::kStateElems;
     la::state_finalize_reverse<<<dim3((unsigned)ceil_div(n_elems, la::kThreads)), block, 0, st>>>(bwd, n_elems);
   }
-  launch_key_pass(k, v, dk, dv, lin, lout, dtype, g, rope, view, st);
+  launch_key_pass(k, v, dk, dv, lin, lout, dtype, g, ra, view, st);
 }
 
 bool state_pair_ok(const float* s, const float* z) {
@@ -512,8 +526,9 @@ int backward(const void* q, const void* k, const void* v, const void* dout, void
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   const la::StateArgs fwd = state_args(ws, g, kv_in, ksum_in, nullptr, nullptr);
   const la::StateArgs bwd = state_args(ws, g, dkv_out, dksum_out, dkv_in, dksum_in);
-  launch_state(k, v, vin.lay, dtype, g, rope, fwd, st);
-  launch_backward(q, k, v, dout, dq, dk, dv, vin.lay, vout.lay, dtype, eps, g, rope, fwd, bwd, st);
+  const RopeArg ra = rope_arg(rope, N);
+  launch_state(k, v, vin.lay, dtype, g, ra, fwd, st);
+  launch_backward(q, k, v, dout, dq, dk, dv, vin.lay, vout.lay, dtype, eps, g, ra, fwd, bwd, st);
   return launch_status();
 }
 
@@ -627,7 +642,7 @@ int sana_linattn_state_update_backward(const void* k, const void* v, const float
   const Geometry g = make_geometry(bh, N, N, rope != nullptr);
   if (!grids_fit(g)) return SANA_ERR_INVALID;
   const la::Layout flat{(int64_t)H * N * D, N * D, D, H};
-  launch_key_pass(k, v, dk, dv, flat, flat, dtype, g, rope, la::StateView{dkv, dksum, 1024, 32},
+  launch_key_pass(k, v, dk, dv, flat, flat, dtype, g, rope_arg(rope, N), la::StateView{dkv, dksum, 1024, 32},
                   static_cast<hipStream_t>(hip_stream));
   return launch_status();
 }
@@ -653,7 +668,8 @@ int sana_linattn_state_update(const void* k, const void* v, float* kv_state, flo
 
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   const la::Layout flat{(int64_t)H * N * D, N * D, D, H};
-  launch_state(k, v, flat, dtype, g, rope, state_args(ws, g, kv_state, ksum_state, kv_state, ksum_state), st);
+  launch_state(k, v, flat, dtype, g, rope_arg(rope, N), state_args(ws, g, kv_state, ksum_state, kv_state, ksum_state),
+               st);
   return launch_status();
 }
 
@@ -674,7 +690,7 @@ int sana_linattn_apply(const void* q, void* o, const float* kv_state, const floa
   const Geometry g = make_geometry(bh, N, N, rope != nullptr);
   if (!grids_fit(g)) return SANA_ERR_INVALID;
   const la::Layout flat{(int64_t)H * N * D, N * D, D, H};
-  launch_apply(q, o, flat, flat, dtype, eps, g, rope, la::StateView{kv_state, ksum_state, 1024, 32},
+  launch_apply(q, o, flat, flat, dtype, eps, g, rope_arg(rope, N), la::StateView{kv_state, ksum_state, 1024, 32},
                static_cast<hipStream_t>(hip_stream));
   return launch_status();
 }
@@ -733,6 +749,26 @@ int sana_linattn_rope3d_table(int T, int Hl, int Wl, int D, int dt, int dh, int 
             cos_host[row * pairs + p] = (float)std::cos(theta);
             sin_host[row * pairs + p] = (float)std::sin(theta);
           }
+      }
+  return SANA_OK;
+}
+
+int sana_linattn_rope3d_axes(int T, int Hl, int Wl, int D, int dt, int dh, int dw, double base, float* cos_host,
+                             float* sin_host) {
+  if (T < 0 || Hl < 0 || Wl < 0 || D <= 0 || dt < 0 || dh < 0 || dw < 0) return SANA_ERR_INVALID;
+  if ((dt | dh | dw) & 1 || dt + dh + dw != D || !(base > 0.0) || !std::isfinite(base)) return SANA_ERR_INVALID;
+  const int extent[3] = {T, Hl, Wl};
+  const int widths[3] = {dt, dh, dw};
+  if ((int64_t)T * dt + (int64_t)Hl * dh + (int64_t)Wl * dw == 0) return SANA_OK;
+  if (!cos_host || !sin_host) return SANA_ERR_INVALID;
+  int64_t at = 0;
+  for (int a = 0; a < 3; ++a)
+    for (int x = 0; x < extent[a]; ++x)
+      for (int kk = 0; kk < widths[a] / 2; ++kk, ++at) {
+        // the same expression as the full tables' entry for this axis
+        const double theta = (double)x * std::pow(base, -2.0 * kk / widths[a]);
+        cos_host[at] = (float)std::cos(theta);
+        sin_host[at] = (float)std::sin(theta);
       }
   return SANA_OK;
 }

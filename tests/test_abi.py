@@ -171,6 +171,73 @@ def test_rope3d_table_errors():
     assert L.sana_linattn_rope3d_table(0, 2, 2, 32, 8, 12, 12, 1e4, None, None) == la.SANA_OK
 
 
+def _axes_index(T, Hl, Wl, pairs):
+    """Per-axis table offset of pair p at position n, written out plainly."""
+    pt, ph, pw = pairs
+    idx = np.empty((T * Hl * Wl, pt + ph + pw), np.int64)
+    for t in range(T):
+        for h in range(Hl):
+            for w in range(Wl):
+                n = (t * Hl + h) * Wl + w
+                for p in range(pt + ph + pw):
+                    if p < pt:
+                        idx[n, p] = t * pt + p
+                    elif p < pt + ph:
+                        idx[n, p] = T * pt + h * ph + (p - pt)
+                    else:
+                        idx[n, p] = T * pt + Hl * ph + w * pw + (p - pt - ph)
+    return idx
+
+
+@pytest.mark.parametrize("grid,split", [((4, 6, 5), (8, 12, 12)), ((21, 22, 40), (8, 12, 12)),
+                                        ((3, 2, 7), (4, 8, 20))])
+def test_rope3d_axes_equal_the_full_tables(grid, split):
+    """Every entry of the full table is, bit for bit, the per-axis entry of its
+    position's coordinate (the form the kernels stage in LDS)."""
+    cos_a, sin_a = la.rope3d_axes(*grid, split=split)
+    cos_f, sin_f = la.rope3d_table(*grid, split=split)
+    idx = _axes_index(*grid, tuple(x // 2 for x in split))
+    assert cos_a.size == grid[0] * split[0] // 2 + grid[1] * split[1] // 2 + grid[2] * split[2] // 2
+    assert np.array_equal(cos_a[idx], cos_f) and np.array_equal(sin_a[idx], sin_f)
+
+
+def test_rope3d_axes_argument_errors():
+    L = la.lib()
+    buf = np.empty(64, np.float32)
+    p = buf.ctypes.data_as(ctypes.c_void_p)
+    assert L.sana_linattn_rope3d_axes(1, 2, 2, 32, 8, 12, 10, 1e4, p, p) == la.SANA_ERR_INVALID
+    assert L.sana_linattn_rope3d_axes(1, 2, 2, 32, 7, 13, 12, 1e4, p, p) == la.SANA_ERR_INVALID
+    assert L.sana_linattn_rope3d_axes(1, 2, 2, 32, 8, 12, 12, -1.0, p, p) == la.SANA_ERR_INVALID
+    assert L.sana_linattn_rope3d_axes(1, 2, 2, 32, 8, 12, 12, 1e4, p, None) == la.SANA_ERR_INVALID
+    assert L.sana_linattn_rope3d_axes(0, 0, 0, 32, 8, 12, 12, 1e4, None, None) == la.SANA_OK
+
+
+def test_rope_axis_form_argument_errors():
+    """The per-axis RoPE form is checked before any launch: a grid matching
+    n_pos, pairs summing to 16, tables within the LDS copy, exact
+    coordinates, and no pairs in the full form."""
+    def axes(grid=(1, 8, 8), pairs=(4, 6, 6), n_pos=None, pos=0, cos=0x60000000):
+        r = sana_rope(cos, 0x70000000, grid[0] * grid[1] * grid[2] if n_pos is None else n_pos, pos)
+        r.grid[:] = grid
+        r.pairs[:] = pairs
+        return _fwd(rope=ctypes.byref(r))
+    E = la
+    assert axes(pairs=(4, 6, 5)) == E.SANA_ERR_INVALID            # pairs do not sum to D/2
+    assert axes(pairs=(-1, 6, 11)) == E.SANA_ERR_INVALID
+    assert axes(pairs=(3, 6, 7)) == E.SANA_ERR_INVALID             # odd pair counts
+    assert axes(grid=(1, 8, 0)) == E.SANA_ERR_INVALID             # empty axis
+    assert axes(grid=(1, -8, -8)) == E.SANA_ERR_INVALID
+    assert axes(n_pos=65) == E.SANA_ERR_INVALID                   # n_pos is the grid's size
+    assert axes(grid=(1, 8, 7)) == E.SANA_ERR_INVALID             # 56 positions < 64 tokens
+    assert axes(pos=1) == E.SANA_ERR_INVALID                      # 65th position outside the grid
+    assert axes(grid=(1, 4, 200), pairs=(0, 0, 16)) == E.SANA_ERR_INVALID   # 3200 floats > 1024
+    assert axes(grid=(1, 1024, 1024), pairs=(16, 0, 0)) == E.SANA_ERR_INVALID  # Hl*Wl >= 2^20
+    assert axes(cos=0x60000002) == E.SANA_ERR_INVALID             # tables 4-byte aligned
+    r = sana_rope(0x60000000, 0x70000000, 64, 0)
+    r.pairs[:] = (4, 6, 6)                                        # pairs without a grid
+    assert _fwd(rope=ctypes.byref(r)) == E.SANA_ERR_INVALID
+
+
 def test_binding_refuses_host_tensors():
     torch = pytest.importorskip("torch")
     x = torch.zeros(1, 1, 4, 32, dtype=torch.bfloat16)
