@@ -14,7 +14,7 @@ import oracle
 from gpu_util import (device, inputs_on_device, rope_for, run_block_chunks, run_forward, to_dev, to_np,
                       torch_mod)
 from metrics import check, rel_l2
-from workloads import WORKLOADS, generate, reduced
+from workloads import WORKLOADS, f64_from_bf16_bits, generate, reduced
 
 pytestmark = pytest.mark.gpu
 
@@ -399,3 +399,22 @@ def test_geometry_extremes(B, H, N):
     x = generate(w)
     o = run_forward(x)
     check(o, oracle.linattn(x.f64["q"], x.f64["k"], x.f64["v"], w.eps), "bf16", f"extremes B{B}H{H}N{N}")
+
+
+def test_tensors_beyond_2gib():
+    """Each of Q, K, V, O spans 2.24 GB (70 heads x 500000 tokens, bf16), so
+    head 67 straddles byte offset 2^31 and heads 68, 69 lie beyond it.
+    Sampled heads, including those, are checked against the oracle run on that
+    head alone (the oracle cannot take the whole tensor in seconds)."""
+    torch = torch_mod()
+    w = reduced(WORKLOADS["sana16b_4096px"], H=70, N=500_000)
+    assert (w.H - 1) * w.N * w.D * 2 > 2 ** 31
+    print("case tensors beyond 2 GiB: B=1 H=70 N=500000", flush=True)
+    x = generate(w, with_f64=False)
+    q, k, v = inputs_on_device(x)
+    o = la.sana_linattn_forward(q, k, v, eps=w.eps)
+    torch.cuda.synchronize()
+    del q, k, v
+    for h in (0, 35, 67, 69):
+        head = [f64_from_bf16_bits(x.raw[n][:, h:h + 1]) for n in ("q", "k", "v")]
+        check(to_np(o[:, h:h + 1]), oracle.linattn(*head, w.eps), "bf16", f"head {h} of a 2.24 GB tensor")
