@@ -30,6 +30,7 @@
 #include "la_backward.h"
 #include "la_conv.h"
 #include "la_kernels.h"
+#include "la_lines.h"
 
 namespace {
 
@@ -271,6 +272,10 @@ la::StateView ws_view(const la::StateArgs& a) {
 // heads of the same tokens.
 bool paired_heads(const la::Layout& l) { return l.head == la::kD; }
 
+// Pairs (2u, 2u + 1) that never straddle two batches can be read as whole
+// lines by one wave (la_lines.h).
+bool whole_lines(const la::Layout& l) { return paired_heads(l) && l.H % 2 == 0; }
+
 // The kernels' view of a call's RoPE argument: its form (la::kRopeNone,
 // kRopeTable or kRopeAxes) and the angle source.  N: tokens in the call.
 struct RopeArg {
@@ -327,6 +332,8 @@ void launch_state(const void* k, const void* v, const la::Layout& lkv, int dtype
       const dim3 pgrid((unsigned)(ceil_div(g.BH, 2) * g.C * g.Pc)), pblock(2 * la::kThreads);
       if (lkv.token == la::kD)
         la::state_bf16<RO, true, 1><<<grid, block, 0, st>>>(K, V, lkv, ra.r, a, g.BH);
+      else if (whole_lines(lkv))
+        la::state_bf16_lines<RO><<<pgrid, block, 0, st>>>(K, V, lkv, ra.r, a, g.BH / 2);
       else if (paired_heads(lkv))
         la::state_bf16<RO, false, 2><<<pgrid, pblock, 0, st>>>(K, V, lkv, ra.r, a, g.BH);
       else
@@ -350,12 +357,15 @@ void launch_apply(const void* q, void* o, const la::Layout& lq, const la::Layout
       const la::u32x4_t* Q = static_cast<const la::u32x4_t*>(q);
       la::u32x4_t* O = static_cast<la::u32x4_t*>(o);
       const bool dense = lq.token == la::kD && lo.token == la::kD;
+      const bool lines = !dense && whole_lines(lq);
       const bool pair = !dense && (paired_heads(lq) || paired_heads(lo));
       // ranges of g.La tokens over (head, token), or per head pair
       const int64_t units = pair ? ceil_div(g.BH, 2) : g.BH;
       const dim3 grid((unsigned)(pair ? units * ceil_div(g.N, g.La) : ceil_div(units * g.N, g.La))),
-          block(pair ? 2 * la::kThreads : la::kThreads);
-      if (dense)
+          block(pair && !lines ? 2 * la::kThreads : la::kThreads);
+      if (lines)
+        la::apply_bf16_lines<RO><<<grid, block, 0, st>>>(Q, O, lq, lo, sv, g.N, g.L, (int)g.C, g.La, eps, ra.r, units);
+      else if (dense)
         la::apply_bf16<RO, true, 1><<<grid, block, 0, st>>>(Q, O, lq, lo, sv, g.N, g.L, (int)g.C, units * g.N, g.La,
                                                             eps, ra.r, g.BH);
       else if (pair)
