@@ -45,6 +45,12 @@ constexpr int64_t kApplyGroups = kCUs * 3;
 constexpr int64_t kApplyGroupsRope = kCUs * 2;
 constexpr int64_t kMaxSplits = 64;       // partial states per chunk
 constexpr int64_t kMinSplitTokens = 256;
+// With at least this many (head, chunk) items of at most kWholeChunkTokens
+// tokens, one workgroup per chunk beats splitting; with one chunk the state
+// pass then writes the states itself and the finalize launch (~3.5 us) is
+// skipped.
+constexpr int64_t kWholeChunkItems = kCUs / 2;
+constexpr int64_t kWholeChunkTokens = 1024;
 constexpr int64_t kMinApplyTokens = 256;
 constexpr int64_t kMinApplyTokensF32 = 256;
 constexpr int64_t kMaxApplyTokensF32 = 1024;
@@ -71,8 +77,9 @@ Geometry make_geometry(int64_t BH, int64_t N, int64_t L, bool rope) {
   g.L = L < N ? L : N;
   g.C = ceil_div(N, g.L);
   // splits per chunk: about kStateGroups workgroups in all, at least
-  // kMinSplitTokens tokens each
+  // kMinSplitTokens tokens each (none for many short chunks)
   int64_t p = ceil_div(kStateGroups / BH, g.C);
+  if (BH * g.C >= kWholeChunkItems && g.L <= kWholeChunkTokens) p = 1;
   const int64_t p_max = ceil_div(g.L, kMinSplitTokens);
   if (p > p_max) p = p_max;
   if (p > kMaxSplits) p = kMaxSplits;
