@@ -300,6 +300,8 @@ def backward_bench(w, args, dev, stream):
     torch.cuda.synchronize()
     key_ms = k0.elapsed_time(k1) / args.steps
     key_bytes = w.token_heads * 4 * w.D * elem + w.B * w.H * (32 * 32 + 32) * 4
+    train = train_step_timing(w, args, sets, n_sets, chunk, rope_ref, dt, nb, dev, stream)
+
     # fp32 multiply-adds per token-head of the backward: the forward state
     # recompute (S, z: 32*32 + 32), the query pass (num, den, S dnum, dS, dz:
     # 3*32*32 + 2*32) and the key pass (G V, G^T phi~(K): 2*32*32), 2 flop each
@@ -338,11 +340,74 @@ def backward_bench(w, args, dev, stream):
                  "achieved_gbps": alg_bytes / (ms / 1e3) / 1e9,
                  "frac_of_hbm_peak": alg_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS,
                  "flops": flops, "achieved_tflops": flops / (ms / 1e3) / 1e12},
+        "train_step": train,
         "step_ms_percentiles": step_pct,
         "wall_s_timed_region": wall,
         "kernel_source_hash": kernel_source_hash(),
     }
     print(json.dumps(rec), flush=True)
+
+
+def train_step_timing(w, args, sets, n_sets, chunk, rope_ref, dt, nb, dev, stream):
+    """A training step's attention: the forward (block_causal for the chunked
+    workload, else forward), then its backward either recomputing the chunk
+    states (sana_linattn_backward) or reading the ones the forward left in its
+    workspace (sana_linattn_backward_saved).  Each input set has its own
+    workspace and output; each variant is timed over the same steps."""
+    import torch
+
+    import linear_attention_diffusion_amd as la
+
+    L = la.lib()
+    P = ctypes.c_void_p
+    st_ptr = ctypes.c_void_p(stream.cuda_stream)
+    for s in sets:
+        s["o"] = torch.empty_like(s["q"])
+        s["ws"] = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
+
+    def forward(s):
+        ptrs = [P(s[n].data_ptr()) for n in ("q", "k", "v", "o")]
+        ws = P(s["ws"].data_ptr())
+        if w.mode == "block":
+            return L.sana_linattn_block_causal(*ptrs, None, None, None, None, w.B, w.H, w.N, chunk, w.D, dt, w.eps,
+                                               rope_ref, ws, s["ws"].numel(), st_ptr)
+        return L.sana_linattn_forward(*ptrs, w.B, w.H, w.N, w.D, dt, w.eps, rope_ref, ws, s["ws"].numel(), st_ptr)
+
+    def grads(s):
+        return [P(s[n].data_ptr()) for n in ("q", "k", "v", "dout", "dq", "dk", "dv")]
+
+    def recompute(s):
+        return L.sana_linattn_backward(*grads(s), None, None, None, None, None, None, w.B, w.H, w.N, chunk, w.D,
+                                       dt, w.eps, rope_ref, P(s["ws"].data_ptr()), s["ws"].numel(), st_ptr)
+
+    def saved(s):
+        return L.sana_linattn_backward_saved(*grads(s), None, None, None, None, None, None, w.B, w.H, w.N, chunk,
+                                             w.D, dt, w.eps, rope_ref, P(s["ws"].data_ptr()), s["ws"].numel(),
+                                             st_ptr)
+
+    def timed(calls):
+        def one(i):
+            for c in calls:
+                rc = c(sets[i % n_sets])
+                if rc:
+                    raise la.SanaError(rc)
+        for i in range(args.warmup):
+            one(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.steps):
+            one(args.warmup + i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    fwd_ms = timed([forward])
+    rec_ms = timed([forward, recompute])
+    sav_ms = timed([forward, saved])
+    return {"forward_ms": fwd_ms, "forward_plus_backward_ms": rec_ms, "forward_plus_backward_saved_ms": sav_ms,
+            "backward_saved_ms": sav_ms - fwd_ms,
+            "entry_points": "forward/block_causal, then sana_linattn_backward or sana_linattn_backward_saved"}
 
 
 def main():

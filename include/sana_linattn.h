@@ -274,6 +274,26 @@ int sana_linattn_backward_strided(const void* q, const void* k, const void* v, c
                                   int B, int H, int64_t N, int64_t chunk, int D, int dtype, float eps,
                                   const sana_rope* rope, void* ws, size_t ws_bytes, void* hip_stream);
 
+/* sana_linattn_backward_strided without recomputing the chunk states: ws must
+ * be the workspace of the forward call these gradients belong to, unchanged
+ * since (sana_linattn_forward or _strided for chunk = N, or
+ * sana_linattn_block_causal, block_forward or their _strided forms with this
+ * chunk, on tensors of the same B, H, N, dtype and RoPE).  Every such call
+ * leaves its chunk states, carried state included, in the workspace; this call
+ * reads them instead of running the state pass again (the carried state is
+ * therefore not an argument) and overwrites them, so one forward serves one
+ * backward.  The workspace size is the same for both calls.  Results equal
+ * sana_linattn_backward's bit for bit.  Other arguments and errors as for
+ * sana_linattn_backward_strided.  For the callers that keep a forward's
+ * context for its backward, as autograd does. */
+int sana_linattn_backward_saved(const void* q, const void* k, const void* v, const void* dout,
+                                void* dq, void* dk, void* dv,
+                                const sana_layout* in, const sana_layout* out,
+                                const float* dkv_out, const float* dksum_out,
+                                float* dkv_in, float* dksum_in,
+                                int B, int H, int64_t N, int64_t chunk, int D, int dtype, float eps,
+                                const sana_rope* rope, void* ws, size_t ws_bytes, void* hip_stream);
+
 /* Backward of sana_linattn_state_update (the key side of every backward):
  * given the gradient (dkv, dksum) reaching an updated state, the gradients of
  * the keys and values that were added into it.  With

@@ -3,7 +3,7 @@
 Entry points (same names as the C ABI in include/sana_linattn.h):
   sana_linattn_forward, sana_linattn_state_update, sana_linattn_block_forward,
   sana_linattn_block_causal, sana_linattn_apply, sana_linattn_backward,
-  sana_linattn_state_update_backward,
+  sana_linattn_state_update_backward, sana_linattn_backward_saved,
   rope3d_table / rope3d_device (host builder of the 3D RoPE tables),
   rope3d_axes / rope3d_axes_device (the same RoPE as per-axis tables).
 """
@@ -30,6 +30,7 @@ from .binding import (  # noqa: F401
     block_causal_workspace_bytes,
     sana_linattn_apply,
     sana_linattn_backward,
+    sana_linattn_backward_saved,
     sana_linattn_block_causal,
     sana_linattn_block_forward,
     sana_linattn_forward,

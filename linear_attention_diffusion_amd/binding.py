@@ -29,6 +29,7 @@ EXPORTED = (
     "sana_linattn_apply",
     "sana_linattn_backward",
     "sana_linattn_backward_strided",
+    "sana_linattn_backward_saved",
     "sana_linattn_backward_workspace_bytes",
     "sana_linattn_state_update_backward",
     "sana_linattn_temporal_conv3",
@@ -95,6 +96,9 @@ def lib():
     L.sana_linattn_backward_strided.argtypes = [vp, vp, vp, vp, vp, vp, vp, lp, lp, vp, vp, vp, vp, vp, vp, i32, i32,
                                                 i64, i64, i32, i32, f32, rp, vp, sz, vp]
     L.sana_linattn_backward_strided.restype = i32
+    L.sana_linattn_backward_saved.argtypes = [vp, vp, vp, vp, vp, vp, vp, lp, lp, vp, vp, vp, vp, i32, i32, i64, i64,
+                                              i32, i32, f32, rp, vp, sz, vp]
+    L.sana_linattn_backward_saved.restype = i32
     L.sana_linattn_state_update_backward.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, rp, vp]
     L.sana_linattn_state_update_backward.restype = i32
     L.sana_linattn_temporal_conv3.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, vp]
@@ -433,6 +437,38 @@ def sana_linattn_backward(q, k, v, dout, chunk=None, dq=None, dk=None, dv=None, 
                                                    _ptr(ksum_in), _ptr(dkv_out), _ptr(dksum_out), _ptr(dkv_in),
                                                    _ptr(dksum_in), B, H, N, L, D, dt, float(eps), _rope_arg(rope),
                                                    _ptr(workspace), workspace.numel(), _stream(stream, q.device)))
+    return tuple(outs)
+
+
+def sana_linattn_backward_saved(q, k, v, dout, workspace, chunk=None, dq=None, dk=None, dv=None, dkv_out=None,
+                                dksum_out=None, dkv_in=None, dksum_in=None, eps=1e-6, rope=None, stream=None):
+    """sana_linattn_backward reusing the chunk states that the forward call
+    (forward, block_forward or block_causal with the same q, k, v, chunk, rope
+    and carried state) left in `workspace`; the workspace must be unchanged
+    since that call and is consumed (one backward per forward)."""
+    torch = _torch()
+    B, H, N, D = _shape4(q, "q", strided=True)
+    for t, name in ((k, "k"), (v, "v"), (dout, "dout")):
+        if _shape4(t, name, strided=True) != (B, H, N, D) or t.dtype != q.dtype:
+            raise ValueError("q, k, v, dout must have the same shape and dtype")
+    outs = []
+    for t, name in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        if t is None:
+            t = torch.empty((B, H, N, D), dtype=q.dtype, device=q.device)
+        elif _shape4(t, name, strided=True) != (B, H, N, D) or t.dtype != q.dtype:
+            raise ValueError(f"{name} must match q in shape and dtype")
+        outs.append(t)
+    for t, shape in ((dkv_out, (B, H, D, D)), (dksum_out, (B, H, D)), (dkv_in, (B, H, D, D)), (dksum_in, (B, H, D))):
+        if t is not None and (tuple(t.shape) != shape or t.dtype != torch.float32 or not t.is_contiguous()):
+            raise ValueError("states must be contiguous float32 [B, H, D, D] / [B, H, D]")
+    L = max(N if chunk is None else int(chunk), 1)
+    dt = _dtype_code(q)
+    vin, vout = _view(q, k, v, dout), _view(*outs)
+    _check(lib().sana_linattn_backward_saved(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(outs[0]), _ptr(outs[1]),
+                                             _ptr(outs[2]), _lay(vin), _lay(vout), _ptr(dkv_out), _ptr(dksum_out),
+                                             _ptr(dkv_in), _ptr(dksum_in), B, H, N, L, D, dt, float(eps),
+                                             _rope_arg(rope), _ptr(workspace), workspace.numel(),
+                                             _stream(stream, q.device)))
     return tuple(outs)
 
 

@@ -492,10 +492,12 @@ bool state_pair_ok(const float* s, const float* z) {
   return !s || (aligned(s, 4) && aligned(z, 4));
 }
 
+// saved: ws holds the chunk states of the forward call (no recompute).
 int backward(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk, void* dv,
-             const sana_layout* in, const sana_layout* out, const float* kv_in, const float* ksum_in, const float* dkv_out, const float* dksum_out, float* dkv_in,
-             float* dksum_in, int B, int H, int64_t N, int64_t L, int D, int dtype, float eps,
-             const sana_rope* rope, void* ws, size_t ws_bytes, void* hip_stream) {
+             const sana_layout* in, const sana_layout* out, const float* kv_in, const float* ksum_in,
+             const float* dkv_out, const float* dksum_out, float* dkv_in, float* dksum_in, int B, int H, int64_t N,
+             int64_t L, int D, int dtype, float eps, const sana_rope* rope, void* ws, size_t ws_bytes,
+             void* hip_stream, bool saved = false) {
   int64_t bh = 0, elems = 0;
   int rc = check_sizes(B, H, N, D, dtype, &bh, &elems);
   if (rc != SANA_OK) return rc;
@@ -544,7 +546,7 @@ int backward(const void* q, const void* k, const void* v, const void* dout, void
   const la::StateArgs fwd = state_args(ws, g, kv_in, ksum_in, nullptr, nullptr);
   const la::StateArgs bwd = state_args(ws, g, dkv_out, dksum_out, dkv_in, dksum_in);
   const RopeArg ra = rope_arg(rope, N);
-  launch_state(k, v, vin.lay, dtype, g, ra, fwd, st);
+  if (!saved) launch_state(k, v, vin.lay, dtype, g, ra, fwd, st);
   launch_backward(q, k, v, dout, dq, dk, dv, vin.lay, vout.lay, dtype, eps, g, ra, fwd, bwd, st);
   return launch_status();
 }
@@ -637,6 +639,15 @@ int sana_linattn_backward_strided(const void* q, const void* k, const void* v, c
                                   float eps, const sana_rope* rope, void* ws, size_t ws_bytes, void* hip_stream) {
   return backward(q, k, v, dout, dq, dk, dv, in, out, kv_in, ksum_in, dkv_out, dksum_out, dkv_in, dksum_in, B, H, N,
                   chunk, D, dtype, eps, rope, ws, ws_bytes, hip_stream);
+}
+
+int sana_linattn_backward_saved(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk,
+                                void* dv, const sana_layout* in, const sana_layout* out, const float* dkv_out,
+                                const float* dksum_out, float* dkv_in, float* dksum_in, int B, int H, int64_t N,
+                                int64_t chunk, int D, int dtype, float eps, const sana_rope* rope, void* ws,
+                                size_t ws_bytes, void* hip_stream) {
+  return backward(q, k, v, dout, dq, dk, dv, in, out, nullptr, nullptr, dkv_out, dksum_out, dkv_in, dksum_in, B, H, N,
+                  chunk, D, dtype, eps, rope, ws, ws_bytes, hip_stream, true);
 }
 
 int sana_linattn_state_update_backward(const void* k, const void* v, const float* dkv, const float* dksum,

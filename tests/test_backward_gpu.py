@@ -199,3 +199,61 @@ def test_state_update_backward(rope):
     ref = oracle.backward(f["q"], f["k"], f["v"], np.zeros_like(f["q"]), w.eps, angles=ang, dS_out=dS, dz_out=dz)
     check(to_np(dk), ref[1], w.dtype, "state_update_backward dk")
     check(to_np(dv), ref[2], w.dtype, "state_update_backward dv")
+
+
+# --------------------------------------------------------------------------
+# backward from the forward's saved chunk states
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("label,base,changes,chunk,rope,carried,packed", [
+    ("non-causal", "sana16b_4096px", dict(H=4, N=3000), None, False, False, False),
+    ("block-causal, carried state", "video480p_blockcausal", dict(H=3, N=2000, chunk=500), 500, False, True, False),
+    ("single chunk, carried state", "video480p_blockcausal", dict(H=3, N=900, chunk=900), 900, False, True, False),
+    ("per-axis RoPE", "video720p_rope3d", dict(H=2, N=3 * 8 * 20, grid=(3, 8, 20)), 160, True, False, False),
+    ("fp32", "noncausal_f32_b1h1n256", dict(H=3, N=700), 300, False, False, False),
+    ("packed", "sana16b_4096px", dict(H=6, N=1000), None, False, False, True),
+])
+def test_backward_saved_equals_recompute(label, base, changes, chunk, rope, carried, packed):
+    """sana_linattn_backward_saved, given the workspace of the forward call
+    (forward, block_forward or block_causal), skips the state recompute and
+    must give the recomputing backward's gradients bit for bit."""
+    torch = torch_mod()
+    w = reduced(WORKLOADS[base], **changes)
+    print(f"case backward_saved {label}: H={w.H} N={w.N} chunk={chunk} dtype={w.dtype}", flush=True)
+    x = generate(w, names=("q", "k", "v", "dout"))
+    q, k, v, do = (to_dev(x.raw[n], w.dtype) for n in ("q", "k", "v", "dout"))
+    if packed:
+        buf = torch.empty(w.B, w.N, 4, w.H, w.D, dtype=q.dtype, device=device())
+        for i, t in enumerate((q, k, v, do)):
+            buf[:, :, i] = t.permute(0, 2, 1, 3)
+        q, k, v, do = (buf[:, :, i].permute(0, 2, 1, 3) for i in range(4))
+    r = la.rope3d_axes_device(*w.grid, device()) if rope else None
+    kw = {}
+    if carried:
+        S_in, z_in = _state_like(w, 77)
+        kw = dict(kv_in=torch.from_numpy(S_in).to(device()), ksum_in=torch.from_numpy(z_in).to(device()))
+    L = w.N if chunk is None else chunk
+    dt = la.SANA_DT_BF16 if w.dtype == "bf16" else la.SANA_DT_F32
+    ws = torch.empty(max(la.backward_workspace_bytes(w.B, w.H, w.N, L, dtype=dt, has_rope=rope), 256),
+                     dtype=torch.uint8, device=device())
+    g = torch.Generator().manual_seed(3)
+    dkv_out = (torch.randn(w.B, w.H, 32, 32, generator=g) * 1e-3).to(device())
+    dz_out = (torch.randn(w.B, w.H, 32, generator=g) * 1e-4).to(device())
+    if chunk is None:
+        la.sana_linattn_forward(q, k, v, eps=w.eps, rope=r, workspace=ws)
+    elif chunk >= w.N:
+        la.sana_linattn_block_forward(q, k, v, eps=w.eps, rope=r, workspace=ws, **kw)
+    else:
+        la.sana_linattn_block_causal(q, k, v, chunk, eps=w.eps, rope=r, workspace=ws, **kw)
+    outs = []
+    for saved in (True, False):
+        dkv_in = torch.empty(w.B, w.H, 32, 32, device=device())
+        dz_in = torch.empty(w.B, w.H, 32, device=device())
+        common = dict(chunk=chunk, dkv_out=dkv_out, dksum_out=dz_out, dkv_in=dkv_in, dksum_in=dz_in, eps=w.eps, rope=r)
+        if saved:
+            grads = la.sana_linattn_backward_saved(q, k, v, do, ws, **common)
+        else:
+            grads = la.sana_linattn_backward(q, k, v, do, **common, **kw)
+        outs.append(tuple(grads) + (dkv_in, dz_in))
+    for a, b, name in zip(outs[0], outs[1], ("dq", "dk", "dv", "dkv_in", "dksum_in")):
+        assert torch.equal(a, b), f"{label}: {name} differs from the recomputing backward"
