@@ -312,6 +312,17 @@ def test_backward_argument_errors_and_workspace():
     assert bw(q=None, k=None, v=None, do=None, dq=None, dk=None, dv=None, N=0, ws=None) == la.SANA_OK
     assert span < 0x01000000
 
+    # the saved-state backward checks the same arguments (it has no carried state)
+    def bws(dq=dQ, dkv_out=None, dks_out=None, dkv_in=None, dks_in=None, chunk=64, ws=WS, nbytes=n):
+        return L.sana_linattn_backward_saved(A, Bp, C, Dp, dq, dK, dV, None, None, dkv_out, dks_out, dkv_in, dks_in,
+                                             1, 2, 640, chunk, 32, la.SANA_DT_BF16, 1e-6, None, ws, nbytes, None)
+    assert bws(chunk=0) == la.SANA_ERR_INVALID
+    assert bws(dq=A) == la.SANA_ERR_INVALID
+    assert bws(dkv_out=S1) == la.SANA_ERR_INVALID
+    assert bws(dkv_in=dV, dks_in=Z1) == la.SANA_ERR_INVALID
+    assert bws(ws=None) == la.SANA_ERR_WORKSPACE
+    assert bws(nbytes=16) == la.SANA_ERR_WORKSPACE
+
 
 def test_strided_layout_validation():
     """Layout errors come back before anything is launched; a valid packed
