@@ -41,6 +41,22 @@ __device__ __forceinline__ Vec8 load8(const __bf16* p) {
   return r;
 }
 
+// The bf16 kernel keeps its loaded frames as raw 16-byte pieces and widens
+// them to fp32 where they are used: a frame then holds 4 registers, not 8.
+__device__ __forceinline__ u32x4_t load_raw(const __bf16* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+
+__device__ __forceinline__ Vec8 widen(u32x4_t x) {
+  Vec8 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    r.v[2 * j] = bf16lo_to_f32(x[j]);
+    r.v[2 * j + 1] = bf16hi_to_f32(x[j]);
+  }
+  return r;
+}
+
 __device__ __forceinline__ void store8(float* p, const Vec8& x) {
   *reinterpret_cast<f32x4_t*>(p) = f32x4_t{x.v[0], x.v[1], x.v[2], x.v[3]};
   *reinterpret_cast<f32x4_t*>(p + 4) = f32x4_t{x.v[4], x.v[5], x.v[6], x.v[7]};
@@ -89,11 +105,37 @@ __global__ __launch_bounds__(kThreads) void temporal_conv3(const T* __restrict__
 #pragma unroll
   for (int j = 0; j < 8; ++j) bb[j] = bv.v[j];
   const int64_t cache_at = bs * C + c0;
-  const Vec8 zero = {{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}};
-  Vec8 prev = cache_in ? load8(cache_in + cache_at) : zero;
   // blocks of kFrames frames: the block and its right neighbour are requested
   // together, so each thread keeps kFrames + 1 loads in flight
   constexpr int kFrames = 4;
+  if constexpr (sizeof(T) == 2) {
+    const u32x4_t zr = {0u, 0u, 0u, 0u};
+    u32x4_t prev = cache_in ? load_raw(cache_in + cache_at) : zr;
+    for (int f0 = 0; f0 < F; f0 += kFrames) {
+      u32x4_t win[kFrames + 1];
+#pragma unroll
+      for (int u = 0; u <= kFrames; ++u) win[u] = (f0 + u < F) ? load_raw(xc + (f0 + u) * frame) : zr;
+#pragma unroll
+      for (int u = 0; u < kFrames; ++u) {
+        if (f0 + u >= F) break;
+        const Vec8 l = widen(u == 0 ? prev : win[u - 1]), m = widen(win[u]), r = widen(win[u + 1]);
+        Vec8 out;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) out.v[j] = m.v[j] + w0[j] * l.v[j] + w1[j] * m.v[j] + w2[j] * r.v[j] + bb[j];
+        store8(yc + (f0 + u) * frame, out);
+      }
+      const int last = (F - f0 < kFrames ? F - f0 : kFrames) - 1;
+#pragma unroll
+      for (int u = 0; u < kFrames; ++u)
+        if (u == last) prev = win[u];
+    }
+    // the last frame's own bits are the next chunk's cache; this thread read
+    // the old cache entry first, so cache_out may be cache_in
+    if (cache_out) __builtin_nontemporal_store(prev, reinterpret_cast<u32x4_t*>(cache_out + cache_at));
+    return;
+  }
+  const Vec8 zero = {{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}};
+  Vec8 prev = cache_in ? load8(cache_in + cache_at) : zero;
   for (int f0 = 0; f0 < F; f0 += kFrames) {
     Vec8 win[kFrames + 1];
 #pragma unroll
