@@ -16,6 +16,7 @@
 // those of the one-head kernels, so the results are bit-identical.
 #pragma once
 
+#include "la_backward.h"
 #include "la_kernels.h"
 
 namespace la {
@@ -272,6 +273,149 @@ __global__ __launch_bounds__(kThreads) void apply_bf16_lines(const u32x4_t* __re
             store16_nt(ro, o_off + tb * 16 * (int)orow,
                        apply_tile<ROPE != 0>(staged_piece(st, tb, hd, m, g), op[hd], eps, cc[tb], ss[tb]));
         }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Key pass of the backward (dV = G^T phi~(K), dK = [K > 0] (R^T G V + Gz)),
+// split like the apply pass: 32-token steps of both heads per wave, each
+// head's G operands in registers.  Each lane puts its dK and dV pieces where it
+// read the K and V pieces, so paired outputs leave as whole lines too.
+// ---------------------------------------------------------------------------
+template <int ROPE>
+__global__ __launch_bounds__(kThreads) void bwd_key_bf16_lines(const u32x4_t* __restrict__ K,
+                                                               const u32x4_t* __restrict__ V,
+                                                               u32x4_t* __restrict__ dK, u32x4_t* __restrict__ dV,
+                                                               Layout lin, Layout lout, StateView grad, int64_t N,
+                                                               int64_t L, int C, int64_t La, Rope rp,
+                                                               int64_t units) {
+  __shared__ __attribute__((aligned(16))) float smem[4 * 2 * kLineTile];
+  __shared__ __attribute__((aligned(16))) float rtab[ROPE == kRopeAxes ? 2 * kMaxAxisTab : 1];
+  rope_stage<ROPE>(rp, rtab, threadIdx.x, kThreads);
+  if constexpr (ROPE == kRopeAxes) __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int m = lane & 15;
+  const int g = lane >> 4;
+  const AxisLane al = axis_lane(rp, g);  // axis form only
+  const int64_t irow = lin.token * 2, orow = lout.token * 2;  // bytes between tokens
+  const int line_off = (lane >> 3) * (int)irow + (lane & 7) * 16;
+  const int oline_off = (lane >> 3) * (int)orow + (lane & 7) * 16;
+  const int o_off = m * (int)orow + g * 16;
+  const int tab_off = m * 64 + g * 16;
+  float* stk = smem + w * 2 * kLineTile;
+  float* stv = stk + kLineTile;
+
+  const int64_t u = blockIdx.x % units;
+  const int64_t f_begin = u * N + (int64_t)(blockIdx.x / units) * La;
+  const int64_t f_end = (f_begin + La < (u + 1) * N) ? f_begin + La : (u + 1) * N;
+  const int64_t bh0 = 2 * u;
+  const char* Kp = reinterpret_cast<const char*>(K) + lin.base(bh0) * 2;
+  const char* Vp = reinterpret_cast<const char*>(V) + lin.base(bh0) * 2;
+  char* dKh[2] = {reinterpret_cast<char*>(dK) + lout.base(bh0) * 2, reinterpret_cast<char*>(dK) + lout.base(bh0 + 1) * 2};
+  char* dVh[2] = {reinterpret_cast<char*>(dV) + lout.base(bh0) * 2, reinterpret_cast<char*>(dV) + lout.base(bh0 + 1) * 2};
+  const bool out_lines = lout.head == kD;
+
+  for (int64_t f = f_begin; f < f_end;) {
+    const int64_t n_begin = f - u * N;
+    const int c = (int)(n_begin / L);
+    const int64_t c_end = ((int64_t)c + 1) * L < N ? ((int64_t)c + 1) * L : N;
+    const int64_t n_end = (f_end - u * N < c_end) ? f_end - u * N : c_end;
+    f = u * N + n_end;
+
+    int64_t t0 = n_begin + 32 * w;
+    u32x4_t nk[4], nv[4];
+    f32x4_t nc[2], ns[2];  // cos/sin rows of the step (full tables)
+    auto load_step = [&](int64_t t) {
+      load_lines(lines_rsrc(Kp, t, n_end, irow), line_off, irow, nk);
+      load_lines(lines_rsrc(Vp, t, n_end, irow), line_off, irow, nv);
+      if constexpr (ROPE == kRopeTable) {
+        const rsrc_t rc = make_rsrc(rp.cos + (rp.pos0 + t) * 16, (n_end - t) * 64);
+        const rsrc_t rs = make_rsrc(rp.sin + (rp.pos0 + t) * 16, (n_end - t) * 64);
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+          nc[tb] = load16(rc, tab_off + tb * 1024);
+          ns[tb] = load16(rs, tab_off + tb * 1024);
+        }
+      }
+    };
+    if (t0 < n_end) load_step(t0);
+    bf16x8_t gcol[2][2][3], grow[2][2][3];
+    float gz[2][8];
+#pragma unroll
+    for (int hd = 0; hd < 2; ++hd) {
+      const int64_t sc = (bh0 + hd) * C + c;
+      const float* G = grad.s_base + sc * grad.s_stride;
+      const float* Gz = grad.z_base + sc * grad.z_stride;
+      load_column_operands(G, g, m, gcol[hd]);  // dV = G^T phi~(K)
+      load_row_operands(G, g, m, grow[hd]);     // G V
+#pragma unroll
+      for (int j = 0; j < 8; ++j) gz[hd][j] = Gz[8 * g + j];
+    }
+
+    for (; t0 < n_end; t0 += 128) {
+      stage_lines(stk, lane, nk);
+      stage_lines(stv, lane, nv);
+      f32x4_t cc[2] = {nc[0], nc[1]}, ss[2] = {ns[0], ns[1]};
+      if (t0 + 128 < n_end) load_step(t0 + 128);
+      if constexpr (ROPE == kRopeAxes) {
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) rope_axis_row4(rp, rtab, al, rp.pos0 + t0 + 16 * tb + m, cc[tb], ss[tb]);
+      }
+#pragma unroll
+      for (int hd = 0; hd < 2; ++hd) {
+        const rsrc_t rdk = rows_rsrc(dKh[hd], t0, n_end, orow);
+        const rsrc_t rdv = rows_rsrc(dVh[hd], t0, n_end, orow);
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+          const u32x4_t kr = relu_bf16x8(staged_piece(stk, tb, hd, m, g));
+          const u32x4_t vx = staged_piece(stv, tb, hd, m, g);
+          f32x4_t o0, o1;
+          float x[8];
+          if constexpr (ROPE == kRopeNone) {
+            mfma3(gcol[hd], __builtin_bit_cast(bf16x8_t, kr), o0, o1);
+          } else {
+            float y[8];
+            unpack8(kr, y);
+            rotate8<false>(y, cc[tb], ss[tb]);
+            bf16x8_t b[3];
+            split8(y, b);
+            mfma6(gcol[hd], b, o0, o1);
+          }
+          x[0] = o0[0], x[1] = o0[1], x[2] = o0[2], x[3] = o0[3];
+          x[4] = o1[0], x[5] = o1[1], x[6] = o1[2], x[7] = o1[3];
+          const u32x4_t dv_out = pack8(x);
+          mfma3(grow[hd], __builtin_bit_cast(bf16x8_t, vx), o0, o1);
+          x[0] = o0[0], x[1] = o0[1], x[2] = o0[2], x[3] = o0[3];
+          x[4] = o1[0], x[5] = o1[1], x[6] = o1[2], x[7] = o1[3];
+          if constexpr (ROPE != kRopeNone) rotate8<true>(x, cc[tb], ss[tb]);
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            x[2 * p] = (kr[p] & 0xffffu) ? x[2 * p] + gz[hd][2 * p] : 0.f;
+            x[2 * p + 1] = (kr[p] >> 16) ? x[2 * p + 1] + gz[hd][2 * p + 1] : 0.f;
+          }
+          const u32x4_t dk_out = pack8(x);
+          if (out_lines) {
+            put_piece(stk, tb, hd, m, g, dk_out);
+            put_piece(stv, tb, hd, m, g, dv_out);
+          } else {
+            store16_nt(rdk, o_off + tb * 16 * (int)orow, dk_out);
+            store16_nt(rdv, o_off + tb * 16 * (int)orow, dv_out);
+          }
+        }
+      }
+      if (out_lines) {
+        u32x4_t ol[4];
+        const rsrc_t rk = lines_rsrc(dKh[0], t0, n_end, orow);
+        unstage_lines(stk, lane, ol);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) store16_nt(rk, oline_off + j * 8 * (int)orow, ol[j]);
+        const rsrc_t rv = lines_rsrc(dVh[0], t0, n_end, orow);
+        unstage_lines(stv, lane, ol);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) store16_nt(rv, oline_off + j * 8 * (int)orow, ol[j]);
       }
     }
   }

@@ -439,7 +439,10 @@ void launch_key_pass(const void* k, const void* v, void* dk, void* dv, const la:
       const auto* V = static_cast<const la::u32x4_t*>(v);
       auto* dK = static_cast<la::u32x4_t*>(dk);
       auto* dV = static_cast<la::u32x4_t*>(dv);
-      if (lin.token == la::kD && lout.token == la::kD)
+      if (lin.token != la::kD && whole_lines(lin))
+        la::bwd_key_bf16_lines<RO><<<dim3((unsigned)(g.BH / 2 * ceil_div(g.N, g.La))), block, 0, st>>>(
+            K, V, dK, dV, lin, lout, view, g.N, g.L, (int)g.C, g.La, ra.r, g.BH / 2);
+      else if (lin.token == la::kD && lout.token == la::kD)
         la::bwd_key_bf16<RO, true><<<kgrid, block, 0, st>>>(K, V, dK, dV, lin, lout, view, g.N, g.L, (int)g.C,
                                                             g.BH * g.N, g.La, ra.r);
       else
