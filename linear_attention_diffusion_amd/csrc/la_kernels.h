@@ -9,9 +9,10 @@
 // paper notes 2.2: RoPE (phi~) is applied after the ReLU and only in the
 // numerator; 2.3: the carried state is the running sum of S and z.
 //
-// Data layout: Q, K, V, O are [BH][N][32] with the 32 features contiguous
-// (64-byte rows in bf16).  Partial states are [BH][P][33][32] fp32: rows 0..31
-// hold S[d][e], row 32 holds z[d].  States are kv [BH][32][32] + ksum [BH][32].
+// Data layout: Q, K, V, O are [BH][N][32] views (see Layout: token n of head
+// bh at a strided element offset) with the 32 features contiguous (64-byte
+// rows in bf16).  Partial states are [BH][C][P][33][32] fp32: rows 0..31 hold
+// S[d][e], row 32 holds z[d].  States are kv [BH][32][32] + ksum [BH][32].
 //
 // bf16 kernels put both 32-wide contractions on v_mfma_f32_16x16x32_bf16:
 //   A (16x32) lane l holds row (l % 16), k-slice group (l / 16), 8 values;

@@ -15,8 +15,12 @@
 //                   space, one per workgroup, each cut at head and chunk
 //                   boundaries)
 // state_update runs 1-2 only, apply runs 3 only.  The backward runs 1-2 to
-// recompute the chunk states, then its query pass, a reverse finalize and its
-// key pass.  Nothing is allocated, freed or synchronised.
+// recompute the chunk states (backward_saved reads those the forward left in
+// the workspace), then its query pass, a reverse finalize and its key pass.
+// Views whose heads 2u, 2u + 1 share 128-byte lines (bf16, H even) run the
+// passes per head pair, reading whole lines (la_lines.h).  RoPE comes as full
+// cos/sin tables or as per-axis tables; each kernel is instantiated for none,
+// either form.  Nothing is allocated, freed or synchronised.
 
 #include "sana_linattn.h"
 
