@@ -245,6 +245,20 @@ def test_binding_refuses_host_tensors():
         la.sana_linattn_forward(x, x, x)
 
 
+def test_binding_rope_checks():
+    torch = pytest.importorskip("torch")
+    t2 = torch.zeros(8, 16)
+    t1 = torch.zeros(40)
+    with pytest.raises(ValueError):
+        la.Rope(t2, t2)                                   # host tensors
+    with pytest.raises(ValueError):
+        la.Rope(t1, t1, grid=(1, 2, 4))                   # grid without pairs
+    with pytest.raises(ValueError):
+        la.Rope(t2, t2, grid=(1, 2, 4), pairs=(4, 6, 6))  # per-axis tables are 1-D
+    with pytest.raises(TypeError):
+        la.Rope(t2.double(), t2.double())
+
+
 def test_apply_argument_errors():
     L = la.lib()
 
