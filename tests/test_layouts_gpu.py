@@ -59,10 +59,13 @@ def test_forward_packed_inputs(dtype, rope):
     check(to_np(o), oracle.linattn(x.f64["q"], x.f64["k"], x.f64["v"], w.eps, angles=ang), dtype, "packed forward")
 
 
-def test_block_causal_and_block_forward_packed():
+@pytest.mark.parametrize("H", [5, 6])
+def test_block_causal_and_block_forward_packed(H):
+    """H = 5 takes the split-wave path (pairs would straddle batches), H = 6
+    the whole-line kernels; N is ragged against every tile size."""
     torch = torch_mod()
-    w = reduced(WORKLOADS["video480p_blockcausal"], H=5, N=3 * 700 + 111, chunk=700)
-    print("case block-causal packed", flush=True)
+    w = reduced(WORKLOADS["video480p_blockcausal"], H=H, N=3 * 700 + 111, chunk=700)
+    print(f"case block-causal packed H={H}", flush=True)
     x = generate(w)
     (q, k, v), (qv, kv_, vv) = _packed(x)
     kv0 = torch.zeros(w.B, w.H, 32, 32, device=device())
@@ -83,9 +86,10 @@ def test_block_causal_and_block_forward_packed():
     _same(oc, o_ref[:, :, s:e])
 
 
-@pytest.mark.parametrize("rope", [False, True])
-def test_backward_packed(rope):
-    w = reduced(WORKLOADS["video720p_rope3d"], H=4, N=3 * 8 * 20, grid=(3, 8, 20),
+@pytest.mark.parametrize("rope,grid", [(False, (3, 8, 20)), (True, (3, 8, 20)), (False, (3, 7, 21)),
+                                       (True, (3, 7, 21))])
+def test_backward_packed(rope, grid):
+    w = reduced(WORKLOADS["video720p_rope3d"], H=4, N=grid[0] * grid[1] * grid[2], grid=grid,
                 mode="rope" if rope else "noncausal")
     print(f"case backward packed rope={rope}", flush=True)
     x = generate(w, names=("q", "k", "v", "dout"))
