@@ -17,4 +17,6 @@ from .linattn_oracle import (  # noqa: F401
     brute_force,
     backward,
     temporal_conv3,
+    round_bf16,
+    projected_kv_state,
 )

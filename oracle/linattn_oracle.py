@@ -42,6 +42,11 @@ reason in the design notes of this repository):
   * Block-causal visibility: a token sees every token of its own chunk and of
     all earlier chunks, never a later chunk ([Video news] "Design details";
     [Video note] 2.3).
+  * Projection fused with the state (the QKV projection upstream of the
+    attention, [Sana note] "Infra": fusing work into the matmul): the keys and
+    values are the per-head projections of the layer input, K = x W_k and
+    V = x W_v, each rounded to bfloat16 as a bf16 projection stores them, and
+    the state is kv_state of those.  No bias (the pages show none).
   * Backward: the pages say the linear attention's forward and backward passes
     are fused kernels ([Sana note] "Infra") and that the block-causal model is
     trained ([Video note] 3), but print no gradient formulas.  The gradients
@@ -344,3 +349,30 @@ def temporal_conv3(x, w, bias=None, prev_frame=None):
     if bias is not None:
         y = y + np.asarray(bias, dtype=np.float64)
     return y, x[:, F - 1].copy()
+
+
+# --------------------------------------------------------------------------
+# The key/value projection feeding the state
+# --------------------------------------------------------------------------
+
+def round_bf16(x):
+    """Round float64 values to the nearest bfloat16 value (8 significant bits,
+    ties to even), for values in bfloat16's normal range and zero."""
+    m, e = np.frexp(np.asarray(x, dtype=np.float64))
+    return np.ldexp(np.rint(m * 256.0), e - 8)
+
+
+def projected_kv_state(x, w_k, w_v):
+    """State of the keys and values a layer's projection produces.
+
+    x: [B, N, C] layer input; w_k, w_v: [H, C, D] per-head projection weights.
+    K[b, h] = x[b] W_k[h] and V[b, h] = x[b] W_v[h] (float64 products and
+    sums), each rounded to bfloat16 as the projection output is stored, then
+    S = sum_n phi(K_n)^T V_n and z = sum_n phi(K_n) per (batch, head), as in
+    kv_state ([Sana note] item 2); [Sana note] "Infra" for the fusion with the
+    matmul).  Returns S [B, H, D, D], z [B, H, D].
+    """
+    x = np.asarray(x, dtype=np.float64)[:, None]          # [B, 1, N, C]
+    k = round_bf16(np.matmul(x, np.asarray(w_k, dtype=np.float64)[None]))
+    v = round_bf16(np.matmul(x, np.asarray(w_v, dtype=np.float64)[None]))
+    return kv_state(k, v)

@@ -412,3 +412,83 @@ def pin_temporal_conv(impl):
 
 
 ALL_PINS.append(pin_temporal_conv)
+
+
+# --------------------------------------------------------------------------
+# Key/value projection feeding the state
+# --------------------------------------------------------------------------
+
+def _bf16_by_bits(x32):
+    """Round float32 values to bfloat16 through their bit patterns: add
+    0x7fff plus the lowest kept bit, then clear the 16 low bits (round to
+    nearest, ties to even)."""
+    bits = np.asarray(x32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    kept = ((bits + 0x7FFF + ((bits >> 16) & 1)) >> 16) << 16
+    return kept.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def pin_projected_state(impl):
+    """bf16 rounding against the bit-pattern method and hand-made ties; the
+    projected state against a brute-force loop in rationals (rounding written
+    as a search over the two neighbouring bf16 values); identity weights
+    reduce it to kv_state of the input; doubling the input quadruples S."""
+    from fractions import Fraction
+    rng = np.random.default_rng(81)
+    x32 = (rng.standard_normal(4000) * np.float32(3.0)).astype(np.float32)
+    assert np.array_equal(impl.round_bf16(x32.astype(np.float64)), _bf16_by_bits(x32))
+    # ties go to the even neighbour; just above a tie rounds up
+    assert impl.round_bf16(1.0 + 2.0 ** -8) == 1.0
+    assert impl.round_bf16(1.0 + 3 * 2.0 ** -8) == 1.0 + 2.0 ** -6
+    assert impl.round_bf16(1.0 + 2.0 ** -8 + 2.0 ** -20) == 1.0 + 2.0 ** -7
+    assert impl.round_bf16(-(1.0 + 2.0 ** -8 + 2.0 ** -20)) == -(1.0 + 2.0 ** -7)
+
+    def rb_fraction(f):
+        # the nearest value with 8 significant bits, ties to an even last bit
+        if f == 0:
+            return Fraction(0)
+        sign = 1 if f > 0 else -1
+        a = abs(f)
+        e = 0
+        while a >= 2:
+            a /= 2
+            e += 1
+        while a < 1:
+            a *= 2
+            e -= 1
+        lo = Fraction(int(a * 128), 128)
+        hi = lo + Fraction(1, 128)
+        d_lo, d_hi = a - lo, hi - a
+        pick = lo if d_lo < d_hi else hi if d_hi < d_lo else (lo if (lo * 128) % 2 == 0 else hi)
+        return sign * pick * Fraction(2) ** e
+
+    # bf16 inputs with full 8-bit mantissas, so the projections need rounding
+    B, H, N, C, D = 1, 2, 5, 6, 3
+    x = _bf16_by_bits(rng.standard_normal((B, N, C)).astype(np.float32))
+    wk = _bf16_by_bits(rng.standard_normal((H, C, D)).astype(np.float32))
+    wv = _bf16_by_bits(rng.standard_normal((H, C, D)).astype(np.float32))
+    raw = np.matmul(x[:, None], wk[None])
+    assert np.any(raw != _bf16_by_bits(raw.astype(np.float32))), "the case must exercise the rounding"
+    S, z = impl.projected_kv_state(x, wk, wv)
+    assert S.shape == (B, H, D, D) and z.shape == (B, H, D)
+    for h in range(H):
+        K = [[rb_fraction(sum(Fraction(x[0, n, c]) * Fraction(wk[h, c, d]) for c in range(C))) for d in range(D)]
+             for n in range(N)]
+        V = [[rb_fraction(sum(Fraction(x[0, n, c]) * Fraction(wv[h, c, e]) for c in range(C))) for e in range(D)]
+             for n in range(N)]
+        for d in range(D):
+            assert z[0, h, d] == float(sum(max(K[n][d], 0) for n in range(N))), ("z", h, d)
+            for e in range(D):
+                want = sum(max(K[n][d], 0) * V[n][e] for n in range(N))
+                assert S[0, h, d, e] == float(want), ("S", h, d, e)
+    # identity weights: the projection is the input itself (bf16-exact)
+    xi = np.asarray(impl.round_bf16(rng.standard_normal((2, 7, 4))), dtype=np.float64)
+    eye = np.broadcast_to(np.eye(4), (3, 4, 4))
+    S_i, z_i = impl.projected_kv_state(xi, eye, eye)
+    S_k, z_k = impl.kv_state(np.broadcast_to(xi[:, None], (2, 3, 7, 4)), np.broadcast_to(xi[:, None], (2, 3, 7, 4)))
+    assert np.array_equal(S_i, S_k) and np.array_equal(z_i, z_k)
+    # a power-of-two scale commutes with the rounding: S scales by 4, z by 2
+    S2, z2 = impl.projected_kv_state(2.0 * x, wk, wv)
+    assert np.array_equal(S2, 4.0 * S) and np.array_equal(z2, 2.0 * z)
+
+
+ALL_PINS.append(pin_projected_state)
