@@ -216,6 +216,139 @@ def conv_bench(args, dev, stream):
     }), flush=True)
 
 
+def project_bench(args, dev, stream):
+    """Time sana_linattn_project_state, the key/value projection fused with the
+    state update, on the Sana-1.6B 4096 px layer (x [1, 16384, 2240] bf16,
+    W_k and W_v [2240, 2240] bf16, 70 heads), one call per step, cycling input
+    sets (x and both weights) past the Infinity Cache.  Beside it, the same
+    work as two passes on the same stream: a bf16 library GEMM (torch.matmul,
+    hipBLASLt) writing K and V as [N, 2 x 2240], then sana_linattn_state_update
+    reading them.  The fused call and the GEMM are timed in two alternating
+    rounds and the second is reported.  Algorithmic flops: 2 N C (2 H D) for the projection plus
+    2 N H D (D + 1) for the state."""
+    import numpy as np
+    import torch
+
+    import linear_attention_diffusion_amd as la
+    from workloads import PROJECTIONS, generate_projection
+
+    p = PROJECTIONS["sana16b_4096px_kv_proj"]
+    x = generate_projection(p, with_f64=False)
+
+    def td(raw):
+        return torch.from_numpy(raw.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    x0, wk0, wv0 = td(x.raw["x"]), td(x.raw["w_k"]), td(x.raw["w_v"])
+    set_bytes = (x0.numel() + wk0.numel() + wv0.numel()) * 2
+    n_sets = max(2, min(32, math.ceil(1.5 * 2 ** 30 / set_bytes) + 1))
+    sets = [(x0.clone(), wk0.clone(), wv0.clone()) for _ in range(n_sets)]
+    kv = torch.zeros(p.B, p.H, 32, 32, device=dev)
+    z = torch.zeros(p.B, p.H, 32, device=dev)
+    nb = la.project_state_workspace_bytes(p.B, p.H, p.N, p.C)
+    ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
+    L = la.lib()
+    P = ctypes.c_void_p
+    st_ptr = ctypes.c_void_p(stream.cuda_stream)
+    calls = [(P(a.data_ptr()), P(b.data_ptr()), P(c.data_ptr()), P(kv.data_ptr()), P(z.data_ptr()), p.B, p.H, p.N,
+              p.C, 32, la.SANA_DT_BF16, P(ws.data_ptr()), nb, st_ptr) for a, b, c in sets]
+
+    def step(i):
+        rc = L.sana_linattn_project_state(*calls[i % n_sets])
+        if rc:
+            raise la.SanaError(rc)
+
+    def timed(fn, first):
+        for i in range(args.warmup):
+            fn(first + i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.steps):
+            fn(first + args.warmup + i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    # the two-pass path on the same sets
+    wkv = [torch.cat([b, c], 0) for _, b, c in sets]
+    out = torch.empty(p.B * p.N, 2 * p.H * 32, dtype=torch.bfloat16, device=dev)
+    k = torch.empty(p.B, p.H, p.N, 32, dtype=torch.bfloat16, device=dev)
+    v = torch.empty_like(k)
+    ws2 = la.make_workspace(p.B, p.H, p.N, dev)
+
+    def gemm(i):
+        torch.matmul(sets[i % n_sets][0].view(p.B * p.N, p.C), wkv[i % n_sets].t(), out=out)
+
+    def state(i):
+        la.sana_linattn_state_update(k, v, kv, z, workspace=ws2, stream=stream)
+
+    # Both paths are timed twice, alternating, and the second round is
+    # reported: on this part a matrix-core kernel's first few hundred
+    # microseconds of sustained load run slower (clock ramp), which would
+    # otherwise fall on whichever path is timed first.
+    for _ in range(2):
+        ms = timed(step, 0)
+        ms_gemm = timed(gemm, 0)
+    k.copy_(out[:, :p.H * 32].view(p.B, p.N, p.H, 32).permute(0, 2, 1, 3))
+    v.copy_(out[:, p.H * 32:].view(p.B, p.N, p.H, 32).permute(0, 2, 1, 3))
+    ms_state = timed(state, 0)
+    pct = step_percentiles(step, min(args.steps, 20), 0, stream)
+
+    flops = 2.0 * p.B * p.N * p.C * (2 * p.H * 32) + 2.0 * p.B * p.N * p.H * 32 * 33
+    tflops = flops / (ms / 1e3) / 1e12
+    th = p.B * p.N * p.H
+    rec = {
+        "metric": "fused K/V projection + linear-attn state, tokens·heads/s (Sana-1.6B 4096px layer)",
+        "value": th / (ms / 1e3), "unit": "tokens·heads/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "step_ms_percentiles": pct, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) bf16 activations, N(0,1/C) bf16 weights",
+        "config": {"workload": p.name, "pass": "project_state", "B": p.B, "N": p.N, "C": p.C, "H": p.H, "D": p.D,
+                   "input_sets_cycled": n_sets},
+        "roofline": {"bound": "mfma", "kernel": "project_state_bf16", "achieved": tflops, "peak": 2500.0,
+                     "unit": "TFLOP/s", "frac": tflops / 2500.0, "traffic": stored_traffic("project_4096px"),
+                     "algorithmic_flops_per_launch": flops, "avg_launch_ms": ms},
+        "two_pass": {"gemm_ms": ms_gemm, "state_update_ms": ms_state, "total_ms": ms_gemm + ms_state,
+                     "gemm_tflops": 2.0 * p.B * p.N * p.C * (2 * p.H * 32) / (ms_gemm / 1e3) / 1e12,
+                     "fused_speedup": (ms_gemm + ms_state) / ms},
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = project_cpu_baseline(p, args.cpu_budget)
+    print(json.dumps(rec), flush=True)
+
+
+def project_cpu_baseline(p, budget_s):
+    """The float64 oracle's projected_kv_state on the host, over whole heads of
+    the same layer until the budget is spent."""
+    import numpy as np
+
+    import oracle
+    from workloads import generate_projection
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([q.get("num_threads", 1) for q in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    f = generate_projection(p).f64
+    C = p.C
+    wk = f["w_k"].reshape(p.H, 32, C).transpose(0, 2, 1)
+    wv = f["w_v"].reshape(p.H, 32, C).transpose(0, 2, 1)
+    heads, done, runs = 2, 0, 0
+    t0 = time.perf_counter()
+    while True:
+        h0 = (runs * heads) % p.H
+        oracle.projected_kv_state(f["x"], wk[h0:h0 + heads], wv[h0:h0 + heads])
+        done += p.B * heads * p.N
+        runs += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or runs >= 5000:
+            break
+    return {"value": done / el, "unit": "tokens·heads/s", "cores": threads, "kind": "oracle",
+            "sample": f"{runs} run(s) of the float64 oracle over {heads} heads x {p.N} tokens (C={C}) of this "
+                      f"layer, {el:.1f} s on the host"}
+
+
 def backward_bench(w, args, dev, stream):
     """Time sana_linattn_backward: one call per step (dQ, dK, dV from dO; the
     chunk states are recomputed from K, V), the block-causal workload as one
@@ -421,9 +554,11 @@ def main():
     ap.add_argument("--block-mode", choices=["chunks", "sequence"], default="chunks",
                     help="block-causal workload: one block_forward call per chunk (inference, the default) or "
                          "one block_causal call over the whole sequence (all chunks known at once)")
-    ap.add_argument("--pass", dest="which", choices=["forward", "backward", "conv"], default="forward",
+    ap.add_argument("--pass", dest="which", choices=["forward", "backward", "conv", "project"], default="forward",
                     help="forward (the default; the headline metric) or backward: one sana_linattn_backward "
-                         "call per step (dQ, dK, dV; whole sequence in block-causal chunks for that workload)")
+                         "call per step (dQ, dK, dV; whole sequence in block-causal chunks for that workload); "
+                         "conv: the block-inference temporal conv; project: the key/value projection fused "
+                         "with the state update (Sana-1.6B 4096 px layer)")
     ap.add_argument("--layout", choices=["bhnd", "packed"], default="bhnd",
                     help="forward: bhnd = contiguous [B, H, N, D] (the default); packed = Q, K, V read as strided "
                          "views of one [B, N, 3, H, D] projection-style buffer and O written to [B, N, H, D] "
@@ -458,6 +593,9 @@ def main():
         return
     if args.which == "conv":
         conv_bench(args, dev, stream)
+        return
+    if args.which == "project":
+        project_bench(args, dev, stream)
         return
 
     x = generate(w, with_f64=False)

@@ -21,6 +21,8 @@ EXPORTED = (
     "sana_linattn_forward",
     "sana_linattn_forward_strided",
     "sana_linattn_state_update",
+    "sana_linattn_project_state",
+    "sana_linattn_project_state_workspace_bytes",
     "sana_linattn_block_forward",
     "sana_linattn_block_forward_strided",
     "sana_linattn_block_causal",
@@ -69,6 +71,10 @@ def lib():
     L.sana_linattn_forward.restype = i32
     L.sana_linattn_state_update.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32, i32, rp, vp, sz, vp]
     L.sana_linattn_state_update.restype = i32
+    L.sana_linattn_project_state.argtypes = [vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, i32, vp, sz, vp]
+    L.sana_linattn_project_state.restype = i32
+    L.sana_linattn_project_state_workspace_bytes.argtypes = [i32, i32, i64, i32, i32, i32]
+    L.sana_linattn_project_state_workspace_bytes.restype = sz
     L.sana_linattn_block_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, f32,
                                              rp, vp, sz, vp]
     L.sana_linattn_block_forward.restype = i32
@@ -321,6 +327,43 @@ def sana_linattn_state_update(k, v, kv_state, ksum_state, rope=None, workspace=N
     ws, nbytes = _workspace(workspace, B, H, N, D, dt, rope is not None, k.device)
     _check(lib().sana_linattn_state_update(_ptr(k), _ptr(v), _ptr(kv_state), _ptr(ksum_state), B, H, N, D, dt,
                                            _rope_arg(rope), _ptr(ws), nbytes, _stream(stream, k.device)))
+
+
+def project_state_workspace_bytes(B, H, N, C, D=32, dtype=SANA_DT_BF16):
+    return int(lib().sana_linattn_project_state_workspace_bytes(B, H, N, C, D, dtype))
+
+
+def sana_linattn_project_state(x, w_k, w_v, kv_state, ksum_state, workspace=None, stream=None):
+    """kv_state += sum phi(K)^T V, ksum_state += sum phi(K) for K = x W_k^T and
+    V = x W_v^T (per head, rounded to bf16), without writing K or V.
+    x: [B, N, C] bf16; w_k, w_v: [H * D, C] bf16 (a linear layer's weight
+    layout); states [B, H, D, D] and [B, H, D] float32, updated in place."""
+    torch = _torch()
+    if x.dim() != 3 or w_k.dim() != 2 or tuple(w_v.shape) != tuple(w_k.shape):
+        raise ValueError("x must be [B, N, C] and w_k, w_v [H * D, C] of one shape")
+    B, N, C = x.shape
+    if w_k.shape[1] != C:
+        raise ValueError("weights must have C columns")
+    if kv_state.dim() != 4 or tuple(ksum_state.shape) != tuple(kv_state.shape[:3]):
+        raise ValueError("kv_state must be [B, H, D, D] and ksum_state [B, H, D]")
+    H, D = kv_state.shape[1], kv_state.shape[3]
+    if tuple(kv_state.shape) != (B, H, D, D) or w_k.shape[0] != H * D:
+        raise ValueError("states must be [B, H, D, D] with H * D weight rows")
+    for name, t in (("x", x), ("w_k", w_k), ("w_v", w_v)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if x.dtype != torch.bfloat16 or w_k.dtype != torch.bfloat16 or w_v.dtype != torch.bfloat16:
+        raise TypeError("x, w_k, w_v must be bfloat16")
+    for t in (kv_state, ksum_state):
+        if t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("states must be contiguous float32 device tensors")
+    if workspace is None:
+        n = project_state_workspace_bytes(B, H, N, C, D)
+        workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=x.device)
+    _check(lib().sana_linattn_project_state(_ptr(x), _ptr(w_k), _ptr(w_v), _ptr(kv_state), _ptr(ksum_state), B, H,
+                                            N, C, D, SANA_DT_BF16, _ptr(workspace),
+                                            workspace.numel() * workspace.element_size(),
+                                            _stream(stream, x.device)))
 
 
 def sana_linattn_block_forward(q, k, v, o=None, kv_in=None, ksum_in=None, kv_out=None, ksum_out=None,

@@ -35,6 +35,7 @@
 #include "la_conv.h"
 #include "la_kernels.h"
 #include "la_lines.h"
+#include "la_proj.h"
 
 namespace {
 
@@ -564,6 +565,42 @@ size_t workspace(int B, int H, int64_t N, int64_t L, int D, int dtype, int has_r
   return make_geometry(bh, N, L, has_rope != 0).total_bytes;
 }
 
+// Fused K/V projection and state pass: each batch's token blocks of 256 are
+// cut into R ranges of T blocks, one workgroup per (range, head pair), each
+// range of a head leaving one partial state (none when R = 1: the workgroup
+// writes the state itself).  At most kProjMaxRanges partials per head keep the
+// finalize's reads small next to the GEMM.
+constexpr int64_t kProjMaxRanges = 128;
+constexpr int kProjMaxChannels = 65536;  // keeps the kernel's 32-bit byte offsets in range
+
+struct ProjGeometry {
+  int64_t BH = 0, R = 0, T = 0, G = 0;
+  size_t state_off = 0, total_bytes = 0;
+};
+
+// Checks the sizes of sana_linattn_project_state and lays out its workspace.
+int make_proj_geometry(int B, int H, int64_t N, int C, int D, int dtype, ProjGeometry* pg) {
+  if (B < 0 || H < 0 || N < 0 || C <= 0 || D <= 0 || elem_size(dtype) == 0) return SANA_ERR_INVALID;
+  if (D != la::kD || dtype != SANA_DT_BF16) return SANA_ERR_UNSUPPORTED;
+  if (C % la::kProjChannelQuantum || C > kProjMaxChannels) return SANA_ERR_INVALID;
+  const int64_t bh = (int64_t)B * H;
+  if (bh > kMaxGroups || (B > 0 && N > (INT64_MAX / 4) / ((int64_t)B * C))) return SANA_ERR_INVALID;
+  ProjGeometry g;
+  g.BH = bh;
+  if (bh > 0 && N > 0) {
+    const int64_t nblk = ceil_div(N, la::kProjTokens);
+    g.T = ceil_div(nblk, kProjMaxRanges);
+    g.R = ceil_div(nblk, g.T);
+    g.G = (int64_t)B * g.R * ceil_div(H, 2);
+    if (g.G > kMaxGroups) return SANA_ERR_INVALID;
+    const int64_t state = (int64_t)la::kStateElems * (int64_t)sizeof(float);
+    g.state_off = (size_t)round_up(g.R > 1 ? bh * g.R * state : 0, 256);
+    g.total_bytes = g.state_off + (size_t)round_up(bh * state, 256);
+  }
+  *pg = g;
+  return SANA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -806,6 +843,63 @@ int sana_linattn_rope3d_axes(int T, int Hl, int Wl, int D, int dt, int dh, int d
         sin_host[at] = (float)std::sin(theta);
       }
   return SANA_OK;
+}
+
+size_t sana_linattn_project_state_workspace_bytes(int B, int H, int64_t N, int C, int D, int dtype) {
+  ProjGeometry g;
+  return make_proj_geometry(B, H, N, C, D, dtype, &g) == SANA_OK ? g.total_bytes : 0;
+}
+
+int sana_linattn_project_state(const void* x, const void* w_k, const void* w_v, float* kv_state, float* ksum_state,
+                               int B, int H, int64_t N, int C, int D, int dtype, void* ws, size_t ws_bytes,
+                               void* hip_stream) {
+  ProjGeometry g;
+  int rc = make_proj_geometry(B, H, N, C, D, dtype, &g);
+  if (rc != SANA_OK) return rc;
+  if (g.BH == 0 || N == 0) return SANA_OK;
+  if (check_tensor(x) || check_tensor(w_k) || check_tensor(w_v)) return SANA_ERR_INVALID;
+  if (!kv_state || !ksum_state || !aligned(kv_state, 4) || !aligned(ksum_state, 4)) return SANA_ERR_INVALID;
+  const size_t x_bytes = (size_t)B * N * C * 2, w_bytes = (size_t)H * la::kD * C * 2;
+  const size_t kv_bytes = (size_t)g.BH * 1024 * sizeof(float), ks_bytes = (size_t)g.BH * 32 * sizeof(float);
+  const void* ins[3] = {x, w_k, w_v};
+  const size_t in_bytes[3] = {x_bytes, w_bytes, w_bytes};
+  for (int i = 0; i < 3; ++i)
+    if (overlaps(kv_state, kv_bytes, ins[i], in_bytes[i]) || overlaps(ksum_state, ks_bytes, ins[i], in_bytes[i]))
+      return SANA_ERR_INVALID;
+  if (overlaps(kv_state, kv_bytes, ksum_state, ks_bytes)) return SANA_ERR_INVALID;
+  if (!ws || ws_bytes < g.total_bytes) return SANA_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return SANA_ERR_INVALID;
+
+  la::ProjArgs p;
+  p.x = static_cast<const char*>(x);
+  p.wk = static_cast<const char*>(w_k);
+  p.wv = static_cast<const char*>(w_v);
+  p.N = N;
+  p.C = C;
+  p.H = H;
+  p.Hp = (int)ceil_div(H, 2);
+  p.R = g.R;
+  p.T = g.T;
+  p.M = (int64_t)B * g.R;
+  la::StateArgs a;
+  a.partials = static_cast<float*>(ws);
+  a.states = reinterpret_cast<float*>(static_cast<char*>(ws) + g.state_off);
+  a.kv_in = kv_state;
+  a.ksum_in = ksum_state;
+  a.kv_out = kv_state;
+  a.ksum_out = ksum_state;
+  a.N = N;
+  a.L = N;
+  a.Ls = g.T * la::kProjTokens;
+  a.C = 1;
+  a.Pc = (int)g.R;
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  la::project_state_bf16<<<dim3((unsigned)g.G), dim3(la::kThreads), 0, st>>>(p, a);
+  if (g.R > 1) {
+    const int64_t n_elems = g.BH * la::kStateElems;
+    la::state_finalize<<<dim3((unsigned)ceil_div(n_elems, la::kThreads)), dim3(la::kThreads), 0, st>>>(a, n_elems);
+  }
+  return launch_status();
 }
 
 const char* sana_linattn_status_string(int status) {

@@ -1,0 +1,82 @@
+"""Element-wise error bound for the fused key/value projection and state
+update, against the float64 oracle's projected_kv_state.
+
+The bound, derived from the arithmetic.  The kernel sums a projection as
+C / 32 MFMA steps of 32 products each, in fp32: whatever the order inside a
+step, a product passes through at most 31 + C / 32 roundings, so the fp32
+value lies within delta = 2 (C / 32 + 32) 2^-24 sum_c |x_c w_c| of the exact
+one (the factor 2 also covers truncating adders).  Rounding to bf16 is
+monotone, so the kernel's K lies between round(K - delta) and
+round(K + delta), b_K apart: 0 unless K sits next to a rounding boundary, then
+one bf16 step.  The state's fp32 sums pass each product through at most
+31 + N / 32 + (partials) + 2 roundings, bounded by N / 32 + 200.  So, with
+A = |phi(K)|^T |V| over the tokens (the b's added in),
+  |dS| <= b_K^T (|V| + b_V) + |phi(K)|^T b_V + 2 (N / 32 + 200) 2^-24 A,
+  |dz| <= sum b_K + 2 (N / 32 + 200) 2^-24 sum (|phi(K)| + b_K).
+A relative-error bar would not do: one K rounding the other way moves an
+element of S that happens to be near zero by far more than a fixed fraction of
+it.  The aggregate rel-L2 must also stay below 1e-3.  A library GEMM of
+unknown summation order (the unfused path) gets delta = 2 C 2^-24 instead."""
+
+import numpy as np
+
+import oracle
+from metrics import rel_l2
+
+REL_L2 = 1e-3
+U = 2.0 ** -24
+
+
+def oracle_weights(w, H, D=32):
+    """[H*D, C] rows (a linear layer's weight) -> the oracle's [H, C, D]."""
+    C = w.shape[1]
+    return np.ascontiguousarray(w.reshape(H, D, C).transpose(0, 2, 1))
+
+
+def check_projected_state(kv, z, x, heads=None, kv0=None, z0=None, any_order=False):
+    """kv, z (float64, [B, H', 32, 32] and [B, H', 32] for the chosen heads of
+    the ProjectionInputs x) against the oracle within the bound above, with
+    kv0, z0 the states the call started from (None: zero).  any_order: the
+    projection's sums were taken in an unknown order.  Returns (ok, report)."""
+    p = x.workload
+    wk, wv = oracle_weights(x.f64["w_k"], p.H), oracle_weights(x.f64["w_v"], p.H)
+    if heads is not None:
+        wk, wv = wk[heads], wv[heads]
+    S, zr = oracle.projected_kv_state(x.f64["x"], wk, wv)
+    if kv0 is not None:
+        S, zr = S + kv0, zr + z0
+    xa = np.abs(x.f64["x"])[:, None]                           # [B, 1, N, C]
+    C, N = p.C, p.N
+
+    def spread(w):
+        exact = np.matmul(x.f64["x"][:, None], w[None])        # [B, H', N, 32]
+        steps = C if any_order else C / 32 + 32
+        delta = 2.0 * steps * U * np.matmul(xa, np.abs(w)[None])
+        lo, hi = oracle.round_bf16(exact - delta), oracle.round_bf16(exact + delta)
+        return oracle.round_bf16(exact), hi - lo
+
+    K, bK = spread(wk)
+    V, bV = spread(wv)
+    phik = np.maximum(K, 0.0)
+    absV = np.abs(V) + bV
+    kt = np.swapaxes(phik, -1, -2)
+    bkt = np.swapaxes(bK, -1, -2)
+    gam = 2.0 * (N / 32 + 200) * U
+    tol_S = np.matmul(bkt, absV) + np.matmul(kt, bV) + gam * np.matmul(kt + bkt, absV)
+    tol_z = bK.sum(axis=-2) + gam * (phik + bK).sum(axis=-2)
+    n_amb = int(np.count_nonzero(bK)) + int(np.count_nonzero(bV))
+    lines = []
+    for got, want, tol, name in ((kv, S, tol_S, "S"), (z, zr, tol_z, "z")):
+        got = np.asarray(got, dtype=np.float64)
+        err = np.abs(got - want)
+        l2 = rel_l2(got, want)
+        worst = float(np.max(err / np.maximum(tol, 1e-300))) if err.size else 0.0
+        lines.append(f"{name}: rel-L2 {l2:.3e}, max |err| / bound {worst:.3e} "
+                     f"({n_amb} of {K.size + V.size} projected values next to a rounding boundary)")
+        if not np.all(np.isfinite(got)):
+            return False, lines[-1] + ": non-finite output"
+        if l2 > REL_L2:
+            return False, lines[-1] + ": rel-L2 above 1e-3"
+        if not np.all(err <= tol):
+            return False, lines[-1] + ": error above the derived bound"
+    return True, "\n".join(lines)

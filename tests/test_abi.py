@@ -128,6 +128,65 @@ def test_state_update_argument_errors():
     assert su(k=None, v=None, kv=None, ks=None, N=0, ws=None) == la.SANA_OK
 
 
+def test_project_state_argument_errors_and_workspace():
+    L = la.lib()
+    pw = la.project_state_workspace_bytes
+    assert pw(1, 70, 16384, 2240) > 0 and pw(1, 70, 16384, 2240) % 256 == 0
+    # one partial per 256-token range when there are several ranges, plus the state
+    assert pw(1, 70, 16384, 2240) == 70 * 64 * 4224 + 70 * 4224
+    assert pw(1, 3, 256, 64) == ((3 * 4224 + 255) // 256) * 256       # one range: no partials
+    # at most 128 ranges per head, whatever N
+    assert pw(1, 2, 10 ** 7, 32) <= 2 * 129 * 4224 + 512
+    assert pw(1, 2, 0, 64) == 0 and pw(0, 2, 64, 64) == 0
+    assert pw(1, 2, 64, 48) == 0 and pw(1, 2, 64, 0) == 0 and pw(1, 2, 64, 65536 + 32) == 0
+    assert pw(1, 2, 64, 64, D=64) == 0 and pw(1, 2, 64, 64, dtype=la.SANA_DT_F32) == 0
+    n = pw(1, 2, 1000, 64)
+
+    def ps(x=A, wk=Bp, wv=C, kv=Dp, ks=Dp + 8192, B=1, H=2, N=1000, Cin=64, D=32, dt=la.SANA_DT_BF16, ws=WS,
+           nbytes=n):
+        return L.sana_linattn_project_state(x, wk, wv, kv, ks, B, H, N, Cin, D, dt, ws, nbytes, None)
+
+    E = la
+    assert ps(x=None) == E.SANA_ERR_INVALID
+    assert ps(wv=None) == E.SANA_ERR_INVALID
+    assert ps(wk=Bp + 8) == E.SANA_ERR_INVALID             # misaligned weights
+    assert ps(kv=None) == E.SANA_ERR_INVALID
+    assert ps(ks=Dp + 2) == E.SANA_ERR_INVALID             # misaligned state
+    assert ps(ks=Dp + 4096) == E.SANA_ERR_INVALID          # ksum overlaps kv (2 heads x 4 KiB)
+    assert ps(kv=A + 1024) == E.SANA_ERR_INVALID           # state inside x
+    assert ps(ks=Bp + 64) == E.SANA_ERR_INVALID            # ksum inside w_k
+    assert ps(Cin=48) == E.SANA_ERR_INVALID                # not a multiple of 32
+    assert ps(Cin=0) == E.SANA_ERR_INVALID
+    assert ps(Cin=65536 + 32) == E.SANA_ERR_INVALID
+    assert ps(B=-1) == E.SANA_ERR_INVALID
+    assert ps(N=-1) == E.SANA_ERR_INVALID
+    assert ps(dt=9) == E.SANA_ERR_INVALID
+    assert ps(D=64) == E.SANA_ERR_UNSUPPORTED
+    assert ps(dt=la.SANA_DT_F32) == E.SANA_ERR_UNSUPPORTED
+    assert ps(ws=None) == E.SANA_ERR_WORKSPACE
+    assert ps(nbytes=n - 1) == E.SANA_ERR_WORKSPACE
+    assert ps(ws=WS + 64) == E.SANA_ERR_INVALID
+    # no tokens or no heads: the states stay as they are, nothing is touched
+    assert ps(x=None, wk=None, wv=None, kv=None, ks=None, N=0, ws=None) == E.SANA_OK
+    assert ps(x=None, wk=None, wv=None, kv=None, ks=None, B=0, ws=None) == E.SANA_OK
+
+
+def test_binding_project_state_checks():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(1, 64, 64, dtype=torch.bfloat16)
+    w = torch.zeros(64, 64, dtype=torch.bfloat16)
+    kv = torch.zeros(1, 2, 32, 32)
+    z = torch.zeros(1, 2, 32)
+    with pytest.raises(ValueError):
+        la.sana_linattn_project_state(x, w, w, kv, z)          # host tensors
+    with pytest.raises(ValueError):
+        la.sana_linattn_project_state(x[0], w, w, kv, z)       # x must be [B, N, C]
+    with pytest.raises(ValueError):
+        la.sana_linattn_project_state(x, w[:, :32], w[:, :32], kv, z)   # C mismatch
+    with pytest.raises(ValueError):
+        la.sana_linattn_project_state(x, w, w, kv[:, :1], z[:, :1])     # H * D != weight rows
+
+
 def test_block_forward_argument_errors():
     L = la.lib()
     n = la.workspace_bytes(1, 2, 64)

@@ -1,0 +1,102 @@
+"""GPU parity of sana_linattn_project_state: the key/value projection fused with
+the state update, against the float64 oracle's projected_kv_state (K = x W_k^T,
+V = x W_v^T rounded to bf16, then S = sum phi(K)^T V, z = sum phi(K)).
+
+The tolerance is the element-wise bound derived in proj_bound.py."""
+
+import pytest
+
+import linear_attention_diffusion_amd as la
+from gpu_util import device, to_dev, to_np, torch_mod
+from proj_bound import check_projected_state
+from workloads import PROJECTIONS, generate_projection, reduced
+
+pytestmark = pytest.mark.gpu
+
+FULL = PROJECTIONS["sana16b_4096px_kv_proj"]
+
+
+def _check_state(*args, **kw):
+    ok, report = check_projected_state(*args, **kw)
+    print(report, flush=True)
+    assert ok, report
+
+
+def _run(x, kv=None, z=None):
+    torch = torch_mod()
+    p = x.workload
+    dev = device()
+    xs, wk, wv = (to_dev(x.raw[n], "bf16") for n in ("x", "w_k", "w_v"))
+    if kv is None:
+        kv = torch.zeros(p.B, p.H, 32, 32, device=dev)
+        z = torch.zeros(p.B, p.H, 32, device=dev)
+    la.sana_linattn_project_state(xs, wk, wv, kv, z)
+    return kv, z
+
+
+# (B, N, C, H): one 256-token block; ragged tails with an odd head count (the
+# last head pair has one head); several ranges (partials + finalize); more than
+# 128 blocks, so each range spans two blocks
+CASES = [(1, 256, 32, 2), (2, 700, 96, 3), (1, 1000, 64, 4), (1, 5000, 128, 5), (1, 33000, 32, 2)]
+
+
+@pytest.mark.parametrize("B,N,C,H", CASES)
+def test_project_state_matches_oracle(B, N, C, H):
+    print(f"case project_state B={B} N={N} C={C} H={H}", flush=True)
+    x = generate_projection(reduced(FULL, B=B, N=N, C=C, H=H, seed=N + C))
+    kv, z = _run(x)
+    _check_state(to_np(kv), to_np(z), x)
+
+
+def test_project_state_accumulates_in_place():
+    """The call adds to the states it is given, as state_update does."""
+    torch = torch_mod()
+    x = generate_projection(reduced(FULL, B=1, N=1200, C=64, H=3, seed=5))
+    g = torch.Generator().manual_seed(3)
+    kv0 = torch.randn(1, 3, 32, 32, generator=g)
+    z0 = torch.rand(1, 3, 32, generator=g) * 100
+    print("case project_state in place", flush=True)
+    kv, z = _run(x, kv0.to(device()), z0.to(device()))
+    _check_state(to_np(kv), to_np(z), x, kv0=kv0.double().numpy(), z0=z0.double().numpy())
+
+
+def test_project_state_empty_leaves_state():
+    torch = torch_mod()
+    x = generate_projection(reduced(FULL, B=1, N=0, C=64, H=2))
+    kv0 = torch.full((1, 2, 32, 32), 1.5, device=device())
+    z0 = torch.full((1, 2, 32), 2.5, device=device())
+    print("case project_state N=0", flush=True)
+    kv, z = _run(x, kv0.clone(), z0.clone())
+    assert bool((kv == kv0).all()) and bool((z == z0).all())
+
+
+def test_project_state_equals_two_pass_path():
+    """Against the unfused path: a bf16 torch projection writes K and V, then
+    sana_linattn_state_update reads them.  The two roundings of K and V can
+    differ only where the fp32 sums fall on opposite sides of a bf16 boundary:
+    both results must lie within the oracle's bound."""
+    torch = torch_mod()
+    p = reduced(FULL, B=2, N=3000, C=256, H=6, seed=11)
+    x = generate_projection(p)
+    print("case project_state vs two-pass", flush=True)
+    kv, z = _run(x)
+    xs, wk, wv = (to_dev(x.raw[n], "bf16") for n in ("x", "w_k", "w_v"))
+    x2 = xs.reshape(p.B * p.N, p.C)
+    k = (x2 @ wk.t().contiguous()).reshape(p.B, p.N, p.H, 32).permute(0, 2, 1, 3).contiguous()
+    v = (x2 @ wv.t().contiguous()).reshape(p.B, p.N, p.H, 32).permute(0, 2, 1, 3).contiguous()
+    kv2 = torch.zeros_like(kv)
+    z2 = torch.zeros_like(z)
+    la.sana_linattn_state_update(k, v, kv2, z2)
+    _check_state(to_np(kv), to_np(z), x)
+    _check_state(to_np(kv2), to_np(z2), x, any_order=True)
+
+
+def test_full_4096px_layer_sampled_heads():
+    """The Sana-1.6B 4096 px key/value projection (16384 tokens, C = 2240, 70
+    heads) in the launch configuration the benchmark times; the oracle computes
+    five of the heads, including both heads of the first and last pair."""
+    x = generate_projection(FULL)
+    print("case project_state full 4096 px", flush=True)
+    kv, z = _run(x)
+    heads = [0, 1, 37, 68, 69]
+    _check_state(to_np(kv)[:, heads], to_np(z)[:, heads], x, heads)

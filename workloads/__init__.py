@@ -137,6 +137,57 @@ def generate(w: Workload, seed: Optional[int] = None, with_f64: bool = True,
     return Inputs(w, raw, f64)
 
 
+@dataclass(frozen=True)
+class ProjectionWorkload:
+    """Input activations x [B, N, C] and the key and value weights [H*D, C] of
+    one layer (the row layout of a linear layer's weight: row h*D + d is output
+    feature d of head h)."""
+    name: str
+    B: int
+    N: int
+    C: int
+    H: int
+    D: int = 32
+    seed: int = 0
+    note: str = field(default="", compare=False)
+
+
+# Sana-1.6B: width 2240 = 70 heads x 32 ("Sana" research note, "Model
+# architecture", parameters paragraph); 4096 px -> 128 x 128 latent tokens.
+PROJECTIONS = {
+    p.name: p for p in [
+        ProjectionWorkload("sana16b_4096px_kv_proj", B=1, N=16384, C=2240, H=70,
+                           note="Sana-1.6B key/value projection of a 4096 px layer"),
+    ]
+}
+
+
+@dataclass
+class ProjectionInputs:
+    workload: ProjectionWorkload
+    raw: dict      # uint16 bf16 bit patterns: "x" [B, N, C], "w_k", "w_v" [H*D, C]
+    f64: dict      # their exact float64 values
+
+
+def generate_projection(p: ProjectionWorkload, seed: Optional[int] = None, with_f64: bool = True):
+    """Recipe: numpy.random.default_rng(seed) (PCG64); float32 standard_normal
+    drawn in the order x [B, N, C], w_k [H*D, C], w_v [H*D, C]; the weights are
+    multiplied by float32(1 / sqrt(C)) (unit-variance keys and values); all
+    rounded to bf16 by round-to-nearest-even."""
+    rng = np.random.default_rng(p.seed if seed is None else seed)
+    wscale = np.float32(1.0 / np.sqrt(p.C))
+    raw, f64 = {}, {}
+    for name, shape, scale in (("x", (p.B, p.N, p.C), None), ("w_k", (p.H * p.D, p.C), wscale),
+                               ("w_v", (p.H * p.D, p.C), wscale)):
+        a = rng.standard_normal(shape, dtype=np.float32)
+        if scale is not None:
+            a *= scale
+        raw[name] = bf16_bits_from_f32(a)
+        if with_f64:
+            f64[name] = f64_from_bf16_bits(raw[name])
+    return ProjectionInputs(p, raw, f64)
+
+
 def reduced(w: Workload, **changes) -> Workload:
     """A smaller workload with the same distribution and mode (for fast parity cases)."""
     return replace(w, **changes)
