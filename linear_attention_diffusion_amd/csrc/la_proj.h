@@ -12,11 +12,13 @@
 //
 // GEMM: workgroup = 4 waves, tile = 256 tokens x 128 output columns (key and
 // value features of heads h, h + 1), channel steps of 32.  The A tile (256 x
-// 32 of x) and the B tile (128 x 32, rows of W_k and W_v) are staged in LDS,
-// double-buffered, rows padded to 40 bf16; wave w owns tokens 128 (w & 1) ..
-// +127 and head h + (w >> 1): 8 x 4 MFMA blocks of 16 x 16, 32 MFMAs a step.
-// (Measured on the 4096 px layer: a 4-head tile at one workgroup per CU, a
-// 64-channel step, and loads issued two steps ahead were all slower.)
+// 32 of x) and the B tile (128 x 32, rows of W_k and W_v) go from memory
+// straight into LDS (buffer loads with the lds flag: no staging registers, no
+// LDS stores), in three stages, so step k + 2 loads while step k computes;
+// wave w owns tokens 128 (w & 1) .. +127 and head h + (w >> 1): 8 x 4 MFMA
+// blocks of 16 x 16, 32 MFMAs a step.  (Measured on the 4096 px layer: loads
+// staged through registers into padded double-buffered LDS were 7% slower; a
+// 4-head tile at one workgroup per CU 18% slower.)
 //
 // Epilogue: the accumulator block of tokens 16i .. 16i + 15 holds, in lane
 // (n, g), tokens 4g + (0..3) of feature n -- the turned-around layout the
@@ -63,18 +65,41 @@ __device__ __forceinline__ void proj_block(uint32_t blk, uint32_t G, int64_t M, 
   *pi = (int)(in / gsize);
 }
 
+// Loads x and weight rows straight into LDS (buffer_load ... lds): a wave's
+// instruction fills 1 KB of LDS, 16 rows of 64 bytes (one 32-channel step),
+// lane l writing row l / 4, slot l % 4.  Slots are XOR-swizzled: slot s of row
+// r holds 16-byte piece s ^ swz(r) of the row, which makes the MFMA operand
+// reads (16 rows, one piece each) free of bank conflicts with 32 or 64 banks.
+__device__ __forceinline__ int proj_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+__device__ __forceinline__ void lds_dma16(rsrc_t r, char* lds, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+}
+
+// Waits until at most N of this wave's loads are outstanding (vmcnt(N)) and its
+// LDS reads have completed (lgkmcnt(0)), then meets the other waves.  The
+// acquire fence keeps later LDS reads below the barrier; no release fence, which
+// would wait for every load in flight, the next stage's included.
+template <int N>
+__device__ __forceinline__ void proj_stage_barrier() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
 // One workgroup per (token range, head pair): 4 waves, wave w takes tokens
 // 128 (w & 1) .. +127 of each 256-token block and head h + (w >> 1) (64 output
-// columns: 8 x 4 MFMA blocks of 16 x 16).  Two workgroups fit a CU (VGPRs,
-// LDS), which the loads' latency needs.  Staging: thread tid moves 16-byte
-// piece tid % 4 of A rows tid / 4 + 64 j and of B rows tid / 4 + 64 j; B row R
-// is row R % 32 of head h + R / 64's key (bit 5 of R clear) or value weights.
+// columns: 8 x 4 MFMA blocks of 16 x 16).  Three LDS stages of one channel step
+// each (A: 256 token rows, B: 128 weight rows, 64 bytes a row): step k + 2 is
+// loaded while step k computes.  B row R of a stage is row R % 32 of head
+// h + R / 64's key (bit 5 of R clear) or value weights.  Two workgroups fit a
+// CU (VGPRs, 2 x 72 KB of LDS).
 __global__ __launch_bounds__(kThreads, 2) void project_state_bf16(ProjArgs p, StateArgs a) {
-  constexpr int kRow = 40;                    // staged bf16 per row (32 + 8 pad: no bank conflicts)
-  constexpr int kA = kProjTokens * kRow;      // bf16 per A buffer
-  constexpr int kB = 128 * kRow;              // bf16 per B buffer
-  __shared__ __attribute__((aligned(16))) __bf16 sa[2][kA];
-  __shared__ __attribute__((aligned(16))) __bf16 sb[2][kB];
+  constexpr int kStage = (kProjTokens + 128) * 64;  // bytes per stage
+  constexpr int kBOff = kProjTokens * 64;            // B rows after the A rows
+  __shared__ __attribute__((aligned(1024))) char st0[kStage];
+  __shared__ __attribute__((aligned(1024))) char st1[kStage];
+  __shared__ __attribute__((aligned(1024))) char st2[kStage];
 
   int64_t mi;
   int pi;
@@ -91,14 +116,23 @@ __global__ __launch_bounds__(kThreads, 2) void project_state_bf16(ProjArgs p, St
   const int th = w & 1, hh = w >> 1;
   const int row = p.C * 2;  // bytes per token row and per weight row
 
-  const int piece = tid & 3;
-  const int trow = tid >> 2;
-  const int a_off = trow * row + piece * 16;
-  const int b_off = (trow & 31) * row + piece * 16;
+  // loads: lane l fills row l / 4 (of 16), slot l % 4, with the swizzled piece
+  const int dr = lane >> 2;
+  const int dpiece = ((lane & 3) ^ proj_swz(dr)) * 16;
+  int a_voff[4], b_voff[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a_voff[i] = (64 * w + 16 * i + dr) * row + dpiece;
+  // wave w stages rows 32 w .. 32 w + 31 of B: features of head h + (w >> 1),
+  // keys for even w, values for odd w
+#pragma unroll
+  for (int i = 0; i < 2; ++i) b_voff[i] = ((w >> 1) * 32 + 16 * i + dr) * row + dpiece;
   const int heads_here = p.H - h < 2 ? p.H - h : 2;
-  // waves 0, 1 stage key rows, waves 2, 3 value rows
-  const rsrc_t rw = make_rsrc((w >> 1 ? p.wv : p.wk) + (int64_t)h * 32 * row, (int64_t)heads_here * 32 * row);
+  const rsrc_t rw = make_rsrc((w & 1 ? p.wv : p.wk) + (int64_t)h * 32 * row, (int64_t)heads_here * 32 * row);
   const char* xb = p.x + b * p.N * (int64_t)row;
+  // operand reads: lane (n, g) reads piece g of row base + n
+  const int sw = 16 * (g ^ proj_swz(n));
+  const int a_rd = (128 * th + n) * 64 + sw;
+  const int b_rd = kBOff + (64 * hh + n) * 64 + sw;
 
   const unsigned one2 = 0x3f803f80u;
   const bf16x8_t ones = as_bf16x8(one2, one2, one2, one2);
@@ -112,20 +146,11 @@ __global__ __launch_bounds__(kThreads, 2) void project_state_bf16(ProjArgs p, St
     const int64_t tok0 = blk * kProjTokens;
     // rows at or past N read as zero: their keys and values are 0 and add nothing
     const rsrc_t rx = make_rsrc(xb + tok0 * row, (p.N - tok0) * row);
-    u32x4_t ga[4], gb[2];
-    auto fetch = [&](int k) {
+    auto issue = [&](int k, char* stage) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) ga[j] = __builtin_bit_cast(u32x4_t, load16(rx, a_off + j * 64 * row + k * 64));
+      for (int i = 0; i < 4; ++i) lds_dma16(rx, stage + (64 * w + 16 * i) * 64, a_voff[i] + k * 64);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) gb[j] = __builtin_bit_cast(u32x4_t, load16(rw, b_off + j * 32 * row + k * 64));
-    };
-    auto put = [&](int buf) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<u32x4_t*>(&sa[buf][(trow + 64 * j) * kRow + piece * 8]) = ga[j];
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        *reinterpret_cast<u32x4_t*>(&sb[buf][(trow + 64 * j) * kRow + piece * 8]) = gb[j];
+      for (int i = 0; i < 2; ++i) lds_dma16(rw, stage + kBOff + (32 * w + 16 * i) * 64, b_voff[i] + k * 64);
     };
     f32x4_t acc[8][4];
 #pragma unroll
@@ -133,26 +158,56 @@ __global__ __launch_bounds__(kThreads, 2) void project_state_bf16(ProjArgs p, St
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = zero4;
 
-    // the previous block's last step ended with a barrier, so buffer 0 is free
-    fetch(0);
-    put(0);
-    __syncthreads();
-    for (int k = 0; k < nk; ++k) {
-      const int buf = k & 1;
-      if (k + 1 < nk) fetch(k + 1);
+    auto compute = [&](const char* stage) {
       bf16x8_t bf[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bf[j] = *reinterpret_cast<const bf16x8_t*>(&sb[buf][(64 * hh + 16 * j + n) * kRow + 8 * g]);
+      for (int j = 0; j < 4; ++j) bf[j] = *reinterpret_cast<const bf16x8_t*>(stage + b_rd + j * 1024);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const bf16x8_t af =
-            *reinterpret_cast<const bf16x8_t*>(&sa[buf][(128 * th + 16 * i + n) * kRow + 8 * g]);
+        const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(stage + a_rd + i * 1024);
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = mfma16(af, bf[j], acc[i][j]);
       }
-      if (k + 1 < nk) put(buf ^ 1);
-      __syncthreads();
+    };
+    // Step t computes on stage t % 3.  Its barrier waits for the step's own
+    // loads (every wave's) to land and for step t - 1's reads to end
+    // everywhere; then stage (t + 2) % 3 is free for step t + 2's loads.  Each
+    // step issues six loads per wave, so with step t + 1's loads still in
+    // flight the wait is vmcnt(6), and vmcnt(0) at the last step.  In the main
+    // loop the stages are named, not indexed: the compiler then sees that the
+    // operand reads and the loads in flight touch different LDS arrays and adds
+    // no wait of its own (in the last steps it waits for every load).
+    __syncthreads();  // every wave is done with the previous block's stages
+    issue(0, st0);
+    if (nk > 1) issue(1, st1);
+    // steps k .. k + 2 (stages 0, 1, 2), every one with loads to issue
+    auto three = [&](int k) {
+      proj_stage_barrier<6>();
+      issue(k + 2, st2);
+      compute(st0);
+      proj_stage_barrier<6>();
+      issue(k + 3, st0);
+      compute(st1);
+      proj_stage_barrier<6>();
+      issue(k + 4, st1);
+      compute(st2);
+    };
+    // (the compiler adds a wait for every load at the loop head, where it
+    // cannot tell the stages apart across the back edge; unrolling to six
+    // steps an iteration measured no faster)
+    int k = 0;
+    for (; k + 5 <= nk; k += 3) three(k);
+    // the last 1 to 4 steps (k is a multiple of 3: step t is on stage t % 3)
+    for (; k < nk; ++k) {
+      const int sk = k % 3;
+      char* cur = sk == 0 ? st0 : (sk == 1 ? st1 : st2);
+      char* nxt = sk == 0 ? st2 : (sk == 1 ? st0 : st1);
+      if (k + 1 < nk)
+        proj_stage_barrier<6>();
+      else
+        proj_stage_barrier<0>();
+      if (k + 2 < nk) issue(k + 2, nxt);
+      compute(cur);
     }
 
     // acc[i][j], lane (n, g): tokens 128 th + 16 i + 4 g + (0..3) of the
@@ -176,10 +231,11 @@ __global__ __launch_bounds__(kThreads, 2) void project_state_bf16(ProjArgs p, St
     }
   }
 
-  // the waves' sums to LDS (over the A buffers: every read of them ended at
-  // the last step's barrier) as red[2 th + hh], the two token halves of each
-  // head added, and each head's sum written as partial r
-  float(*red)[kStateElems] = reinterpret_cast<float(*)[kStateElems]>(&sa[0][0]);
+  // the waves' sums to LDS (over stage 0: no load is in flight after the last
+  // step) as red[2 th + hh], the two token halves of each head added, and each
+  // head's sum written as partial r
+  __syncthreads();
+  float(*red)[kStateElems] = reinterpret_cast<float(*)[kStateElems]>(st0);
   float* mine = red[2 * th + hh];
 #pragma unroll
   for (int fh = 0; fh < 2; ++fh) {
