@@ -362,17 +362,19 @@ def round_bf16(x):
     return np.ldexp(np.rint(m * 256.0), e - 8)
 
 
-def projected_kv_state(x, w_k, w_v):
+def projected_kv_state(x, w_k, w_v, angles=None, pos_offset=0):
     """State of the keys and values a layer's projection produces.
 
     x: [B, N, C] layer input; w_k, w_v: [H, C, D] per-head projection weights.
     K[b, h] = x[b] W_k[h] and V[b, h] = x[b] W_v[h] (float64 products and
     sums), each rounded to bfloat16 as the projection output is stored, then
-    S = sum_n phi(K_n)^T V_n and z = sum_n phi(K_n) per (batch, head), as in
+    S = sum_n phi~(K_n)^T V_n and z = sum_n phi(K_n) per (batch, head), as in
     kv_state ([Sana note] item 2); [Sana note] "Infra" for the fusion with the
-    matmul).  Returns S [B, H, D, D], z [B, H, D].
+    matmul).  With angles, key n of every batch is rotated at position
+    pos_offset + n after the ReLU, in S only ([Video note] 2.2).  Returns
+    S [B, H, D, D], z [B, H, D].
     """
     x = np.asarray(x, dtype=np.float64)[:, None]          # [B, 1, N, C]
     k = round_bf16(np.matmul(x, np.asarray(w_k, dtype=np.float64)[None]))
     v = round_bf16(np.matmul(x, np.asarray(w_v, dtype=np.float64)[None]))
-    return kv_state(k, v)
+    return kv_state(k, v, angles, pos_offset)

@@ -430,7 +430,8 @@ def _bf16_by_bits(x32):
 def pin_projected_state(impl):
     """bf16 rounding against the bit-pattern method and hand-made ties; the
     projected state against a brute-force loop in rationals (rounding written
-    as a search over the two neighbouring bf16 values); identity weights
+    as a search over the two neighbouring bf16 values), plain and with keys
+    rotated by explicit 2 x 2 rotations at offset positions; identity weights
     reduce it to kv_state of the input; doubling the input quadruples S."""
     from fractions import Fraction
     rng = np.random.default_rng(81)
@@ -489,6 +490,32 @@ def pin_projected_state(impl):
     # a power-of-two scale commutes with the rounding: S scales by 4, z by 2
     S2, z2 = impl.projected_kv_state(2.0 * x, wk, wv)
     assert np.array_equal(S2, 4.0 * S) and np.array_equal(z2, 2.0 * z)
+
+    # rotated keys: the brute force again, each key's pairs (2p, 2p + 1) turned
+    # by an explicit 2 x 2 rotation in rationals from the float64 cos and sin
+    # of its position's angles (positions pos_offset + n); z stays unrotated
+    D2 = 4
+    wk2 = _bf16_by_bits(rng.standard_normal((H, C, D2)).astype(np.float32))
+    wv2 = _bf16_by_bits(rng.standard_normal((H, C, D2)).astype(np.float32))
+    angles = rng.uniform(-3.0, 3.0, (N + 3, D2 // 2))
+    S_r, z_r = impl.projected_kv_state(x, wk2, wv2, angles=angles, pos_offset=2)
+    _, z_plain = impl.projected_kv_state(x, wk2, wv2)
+    assert np.array_equal(z_r, z_plain)
+    for h in range(H):
+        K = [[rb_fraction(sum(Fraction(x[0, n, c]) * Fraction(wk2[h, c, d]) for c in range(C))) for d in range(D2)]
+             for n in range(N)]
+        V = [[rb_fraction(sum(Fraction(x[0, n, c]) * Fraction(wv2[h, c, e]) for c in range(C))) for e in range(D2)]
+             for n in range(N)]
+        for d in range(D2):
+            for e in range(D2):
+                want = Fraction(0)
+                for n in range(N):
+                    p = d // 2
+                    cs, sn = Fraction(np.cos(angles[n + 2, p])), Fraction(np.sin(angles[n + 2, p]))
+                    k0, k1 = max(K[n][2 * p], 0), max(K[n][2 * p + 1], 0)
+                    rot = k0 * cs - k1 * sn if d % 2 == 0 else k0 * sn + k1 * cs
+                    want += rot * V[n][e]
+                assert abs(S_r[0, h, d, e] - float(want)) <= 1e-12 * (1 + abs(float(want))), ("S rotated", h, d, e)
 
 
 ALL_PINS.append(pin_projected_state)

@@ -79,9 +79,11 @@ MUTANTS = {
                           "padded = np.concatenate([prev[:, None], x, x[:, :1]], axis=1)"),
     "proj_rounding_dropped": ("k = round_bf16(np.matmul(x, np.asarray(w_k, dtype=np.float64)[None]))",
                               "k = np.matmul(x, np.asarray(w_k, dtype=np.float64)[None])"),
-    "proj_k_v_swapped": ("return kv_state(k, v)\n", "return kv_state(v, k)\n"),
+    "proj_k_v_swapped": ("return kv_state(k, v, angles, pos_offset)", "return kv_state(v, k, angles, pos_offset)"),
     "proj_round_to_nearest_away": ("return np.ldexp(np.rint(m * 256.0), e - 8)",
                                    "return np.ldexp(np.floor(m * 256.0 + 0.5), e - 8)"),
+    "proj_rotation_dropped": ("return kv_state(k, v, angles, pos_offset)", "return kv_state(k, v)"),
+    "proj_positions_from_zero": ("return kv_state(k, v, angles, pos_offset)", "return kv_state(k, v, angles, 0)"),
     "proj_round_7_bits": ("return np.ldexp(np.rint(m * 256.0), e - 8)", "return np.ldexp(np.rint(m * 128.0), e - 7)"),
     "bwd_carried_state_ignored": ("S = np.zeros(lead + (D, D)) if S_in is None else np.asarray(S_in, dtype=np.float64)\n    z = np.zeros(lead + (D,)) if z_in is None else np.asarray(z_in, dtype=np.float64)\n    states = []",
                                   "S = np.zeros(lead + (D, D))\n    z = np.zeros(lead + (D,)) if z_in is None else np.asarray(z_in, dtype=np.float64)\n    states = []"),
