@@ -224,7 +224,9 @@ def project_bench(args, dev, stream):
     work as two passes on the same stream: a bf16 library GEMM (torch.matmul,
     hipBLASLt) writing K and V as [N, 2 x 2240], then sana_linattn_state_update
     reading them.  The fused call and the GEMM are timed in two alternating
-    rounds and the second is reported.  Algorithmic flops: 2 N C (2 H D) for the projection plus
+    rounds and the second is reported.  With --workload video720p_rope3d: the
+    same width over the SANA-Video 720p layer's 18480 tokens, keys rotated by
+    its 3D RoPE (--rope-form), in both paths.  Algorithmic flops: 2 N C (2 H D) for the projection plus
     2 N H D (D + 1) for the state."""
     import numpy as np
     import torch
@@ -233,6 +235,16 @@ def project_bench(args, dev, stream):
     from workloads import PROJECTIONS, generate_projection
 
     p = PROJECTIONS["sana16b_4096px_kv_proj"]
+    w = WORKLOADS[args.workload]
+    rope = None
+    if w.mode == "rope":
+        # the video layer's keys: the same width, its tokens and 3D RoPE
+        from workloads import reduced
+        p = reduced(p, name=f"{w.name}_kv_proj", N=w.N)
+        rope = make_rope(la, w, dev, args.rope_form)
+    elif w.name != "sana16b_4096px":
+        raise SystemExit("--pass project runs on the sana16b_4096px layer or, with RoPE, video720p_rope3d")
+    rope_ref = None if rope is None else ctypes.byref(rope.struct())
     x = generate_projection(p, with_f64=False)
 
     def td(raw):
@@ -250,7 +262,7 @@ def project_bench(args, dev, stream):
     P = ctypes.c_void_p
     st_ptr = ctypes.c_void_p(stream.cuda_stream)
     calls = [(P(a.data_ptr()), P(b.data_ptr()), P(c.data_ptr()), P(kv.data_ptr()), P(z.data_ptr()), p.B, p.H, p.N,
-              p.C, 32, la.SANA_DT_BF16, P(ws.data_ptr()), nb, st_ptr) for a, b, c in sets]
+              p.C, 32, la.SANA_DT_BF16, rope_ref, P(ws.data_ptr()), nb, st_ptr) for a, b, c in sets]
 
     def step(i):
         rc = L.sana_linattn_project_state(*calls[i % n_sets])
@@ -274,13 +286,13 @@ def project_bench(args, dev, stream):
     out = torch.empty(p.B * p.N, 2 * p.H * 32, dtype=torch.bfloat16, device=dev)
     k = torch.empty(p.B, p.H, p.N, 32, dtype=torch.bfloat16, device=dev)
     v = torch.empty_like(k)
-    ws2 = la.make_workspace(p.B, p.H, p.N, dev)
+    ws2 = la.make_workspace(p.B, p.H, p.N, dev, has_rope=rope is not None)
 
     def gemm(i):
         torch.matmul(sets[i % n_sets][0].view(p.B * p.N, p.C), wkv[i % n_sets].t(), out=out)
 
     def state(i):
-        la.sana_linattn_state_update(k, v, kv, z, workspace=ws2, stream=stream)
+        la.sana_linattn_state_update(k, v, kv, z, rope=rope, workspace=ws2, stream=stream)
 
     # Both paths are timed twice, alternating, and the second round is
     # reported: on this part a matrix-core kernel's first few hundred
@@ -295,18 +307,20 @@ def project_bench(args, dev, stream):
     pct = step_percentiles(step, min(args.steps, 20), 0, stream)
 
     flops = 2.0 * p.B * p.N * p.C * (2 * p.H * 32) + 2.0 * p.B * p.N * p.H * 32 * 33
+    rope_name = None if rope is None else ("3D RoPE, per-axis tables" if rope.grid else "3D RoPE, full tables")
     tflops = flops / (ms / 1e3) / 1e12
     th = p.B * p.N * p.H
     rec = {
-        "metric": "fused K/V projection + linear-attn state, tokens·heads/s (Sana-1.6B 4096px layer)",
+        "metric": "fused K/V projection + linear-attn state, tokens·heads/s (" +
+                  ("Sana-1.6B 4096px layer)" if rope is None else "SANA-Video 720p layer, 3D RoPE)"),
         "value": th / (ms / 1e3), "unit": "tokens·heads/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "step_ms_percentiles": pct, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic: seeded N(0,1) bf16 activations, N(0,1/C) bf16 weights",
         "config": {"workload": p.name, "pass": "project_state", "B": p.B, "N": p.N, "C": p.C, "H": p.H, "D": p.D,
-                   "input_sets_cycled": n_sets},
+                   "rope": rope_name, "input_sets_cycled": n_sets},
         "roofline": {"bound": "mfma", "kernel": "project_state_bf16", "achieved": tflops, "peak": 2500.0,
-                     "unit": "TFLOP/s", "frac": tflops / 2500.0, "traffic": stored_traffic("project_4096px"),
+                     "unit": "TFLOP/s", "frac": tflops / 2500.0, "traffic": stored_traffic("project_4096px") if rope is None else None,
                      "algorithmic_flops_per_launch": flops, "avg_launch_ms": ms},
         "two_pass": {"gemm_ms": ms_gemm, "state_update_ms": ms_state, "total_ms": ms_gemm + ms_state,
                      "gemm_tflops": 2.0 * p.B * p.N * p.C * (2 * p.H * 32) / (ms_gemm / 1e3) / 1e12,
@@ -314,13 +328,16 @@ def project_bench(args, dev, stream):
         "kernel_source_hash": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = project_cpu_baseline(p, args.cpu_budget)
+        import oracle
+        angles = None if rope is None else oracle.rope3d_angles(*w.grid)
+        rec["cpu_baseline"] = project_cpu_baseline(p, args.cpu_budget, angles)
     print(json.dumps(rec), flush=True)
 
 
-def project_cpu_baseline(p, budget_s):
-    """The float64 oracle's projected_kv_state on the host, over whole heads of
-    the same layer until the budget is spent."""
+def project_cpu_baseline(p, budget_s, angles=None):
+    """The float64 oracle's projected_kv_state on the host (keys rotated by
+    `angles` if given), over whole heads of the same layer until the budget is
+    spent."""
     import numpy as np
 
     import oracle
@@ -338,7 +355,7 @@ def project_cpu_baseline(p, budget_s):
     t0 = time.perf_counter()
     while True:
         h0 = (runs * heads) % p.H
-        oracle.projected_kv_state(f["x"], wk[h0:h0 + heads], wv[h0:h0 + heads])
+        oracle.projected_kv_state(f["x"], wk[h0:h0 + heads], wv[h0:h0 + heads], angles)
         done += p.B * heads * p.N
         runs += 1
         el = time.perf_counter() - t0
@@ -558,7 +575,7 @@ def main():
                     help="forward (the default; the headline metric) or backward: one sana_linattn_backward "
                          "call per step (dQ, dK, dV; whole sequence in block-causal chunks for that workload); "
                          "conv: the block-inference temporal conv; project: the key/value projection fused "
-                         "with the state update (Sana-1.6B 4096 px layer)")
+                         "with the state update (Sana-1.6B 4096 px layer, or video720p_rope3d with its RoPE)")
     ap.add_argument("--layout", choices=["bhnd", "packed"], default="bhnd",
                     help="forward: bhnd = contiguous [B, H, N, D] (the default); packed = Q, K, V read as strided "
                          "views of one [B, N, 3, H, D] projection-style buffer and O written to [B, N, H, D] "

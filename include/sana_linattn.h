@@ -164,10 +164,12 @@ int sana_linattn_state_update(const void* k, const void* v, float* kv_state, flo
  * note, "Infra": ReLU(K)^T V fused into the QKV projection, there in an INT8
  * engine).  Per batch b and head h, with K = x[b] W_k[h]^T and V = x[b] W_v[h]^T
  * each rounded to bf16 as a bf16 projection would store them:
- *   kv_state[b][h]   += sum_j phi(K_j)^T V_j
+ *   kv_state[b][h]   += sum_j phi~(K_j)^T V_j
  *   ksum_state[b][h] += sum_j phi(K_j)
  * exactly what sana_linattn_state_update adds for that K and V, which are
- * never written to memory.
+ * never written to memory.  With rope (either form of sana_rope), key j of
+ * every batch is rotated at position pos_offset + j after the ReLU, in the
+ * numerator state only ("SANA-Video" paper notes 2.2); NULL: no rotation.
  * x: input activations [B][N][C] bf16 (channels innermost).  w_k, w_v: weights
  * [H*D][C] bf16, row h*D + d holding output feature d of head h (the layout of
  * a linear layer's weight, or of the key or value rows of a fused QKV weight).
@@ -175,12 +177,12 @@ int sana_linattn_state_update(const void* k, const void* v, float* kv_state, flo
  * ksum_state [B][H][D]: fp32, read and updated in place (zero them first for
  * the state of these N tokens alone).  C must be a positive multiple of 32, at
  * most 65536 (else SANA_ERR_INVALID); only dtype SANA_DT_BF16 and D = 32 have
- * kernels (else SANA_ERR_UNSUPPORTED); no RoPE.  The products accumulate in
+ * kernels (else SANA_ERR_UNSUPPORTED).  The products accumulate in
  * fp32.  ws: at least sana_linattn_project_state_workspace_bytes(...) bytes.
  * B*H*N = 0 leaves the states unchanged. */
 int sana_linattn_project_state(const void* x, const void* w_k, const void* w_v, float* kv_state,
                                float* ksum_state, int B, int H, int64_t N, int C, int D, int dtype,
-                               void* ws, size_t ws_bytes, void* hip_stream);
+                               const sana_rope* rope, void* ws, size_t ws_bytes, void* hip_stream);
 
 /* Workspace bytes for sana_linattn_project_state with these sizes (0 when there
  * is no work or the sizes are invalid).  Pure host function. */

@@ -71,7 +71,7 @@ def lib():
     L.sana_linattn_forward.restype = i32
     L.sana_linattn_state_update.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32, i32, rp, vp, sz, vp]
     L.sana_linattn_state_update.restype = i32
-    L.sana_linattn_project_state.argtypes = [vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, i32, vp, sz, vp]
+    L.sana_linattn_project_state.argtypes = [vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, i32, rp, vp, sz, vp]
     L.sana_linattn_project_state.restype = i32
     L.sana_linattn_project_state_workspace_bytes.argtypes = [i32, i32, i64, i32, i32, i32]
     L.sana_linattn_project_state_workspace_bytes.restype = sz
@@ -333,11 +333,12 @@ def project_state_workspace_bytes(B, H, N, C, D=32, dtype=SANA_DT_BF16):
     return int(lib().sana_linattn_project_state_workspace_bytes(B, H, N, C, D, dtype))
 
 
-def sana_linattn_project_state(x, w_k, w_v, kv_state, ksum_state, workspace=None, stream=None):
-    """kv_state += sum phi(K)^T V, ksum_state += sum phi(K) for K = x W_k^T and
+def sana_linattn_project_state(x, w_k, w_v, kv_state, ksum_state, rope=None, workspace=None, stream=None):
+    """kv_state += sum phi~(K)^T V, ksum_state += sum phi(K) for K = x W_k^T and
     V = x W_v^T (per head, rounded to bf16), without writing K or V.
     x: [B, N, C] bf16; w_k, w_v: [H * D, C] bf16 (a linear layer's weight
-    layout); states [B, H, D, D] and [B, H, D] float32, updated in place."""
+    layout); states [B, H, D, D] and [B, H, D] float32, updated in place.
+    rope: a Rope (either form) rotating key n at position pos_offset + n."""
     torch = _torch()
     if x.dim() != 3 or w_k.dim() != 2 or tuple(w_v.shape) != tuple(w_k.shape):
         raise ValueError("x must be [B, N, C] and w_k, w_v [H * D, C] of one shape")
@@ -361,7 +362,7 @@ def sana_linattn_project_state(x, w_k, w_v, kv_state, ksum_state, workspace=None
         n = project_state_workspace_bytes(B, H, N, C, D)
         workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=x.device)
     _check(lib().sana_linattn_project_state(_ptr(x), _ptr(w_k), _ptr(w_v), _ptr(kv_state), _ptr(ksum_state), B, H,
-                                            N, C, D, SANA_DT_BF16, _ptr(workspace),
+                                            N, C, D, SANA_DT_BF16, _rope_arg(rope), _ptr(workspace),
                                             workspace.numel() * workspace.element_size(),
                                             _stream(stream, x.device)))
 

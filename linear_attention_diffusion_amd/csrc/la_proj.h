@@ -87,6 +87,33 @@ __device__ __forceinline__ void proj_stage_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
+// cos/sin of this lane's two pairs (q[0], q[1]: features n and 16 + n) at
+// position pos0 + tok (tok in the call's range): from the full tables in
+// memory, or from the per-axis tables staged in LDS (rtab; ap: where each
+// pair's entries sit), the coordinates computed once for both.
+template <int ROPE>
+__device__ __forceinline__ void proj_angles(const Rope& r, const float* rtab, const AxisPair (&ap)[2], int64_t tok,
+                                            float (&c)[2], float (&sn)[2]) {
+  const int64_t pos = r.pos0 + tok;
+  if constexpr (ROPE == kRopeAxes) {
+    int t, h, w;
+    rope_coords(r, pos, t, h, w);
+#pragma unroll
+    for (int fh = 0; fh < 2; ++fh) {
+      const float2 e = *reinterpret_cast<const float2*>(rtab + 2 * axis_entry(ap[fh], t, h, w));
+      c[fh] = e.x;
+      sn[fh] = e.y;
+    }
+  } else {
+#pragma unroll
+    for (int fh = 0; fh < 2; ++fh) {
+      const int q = (16 * fh + (int)(threadIdx.x & 15)) >> 1;
+      c[fh] = r.cos[pos * 16 + q];
+      sn[fh] = r.sin[pos * 16 + q];
+    }
+  }
+}
+
 // One workgroup per (token range, head pair): 4 waves, wave w takes tokens
 // 128 (w & 1) .. +127 of each 256-token block and head h + (w >> 1) (64 output
 // columns: 8 x 4 MFMA blocks of 16 x 16).  Three LDS stages of one channel step
@@ -94,12 +121,14 @@ __device__ __forceinline__ void proj_stage_barrier() {
 // loaded while step k computes.  B row R of a stage is row R % 32 of head
 // h + R / 64's key (bit 5 of R clear) or value weights.  Two workgroups fit a
 // CU (VGPRs, 2 x 72 KB of LDS).
-__global__ __launch_bounds__(kThreads, 2) void project_state_bf16(ProjArgs p, StateArgs a) {
+template <int ROPE>
+__global__ __launch_bounds__(kThreads, 2) void project_state_bf16(ProjArgs p, Rope rp, StateArgs a) {
   constexpr int kStage = (kProjTokens + 128) * 64;  // bytes per stage
   constexpr int kBOff = kProjTokens * 64;            // B rows after the A rows
   __shared__ __attribute__((aligned(1024))) char st0[kStage];
   __shared__ __attribute__((aligned(1024))) char st1[kStage];
   __shared__ __attribute__((aligned(1024))) char st2[kStage];
+  __shared__ __attribute__((aligned(16))) float rtab[ROPE == kRopeAxes ? 2 * kMaxAxisTab : 1];
 
   int64_t mi;
   int pi;
@@ -133,6 +162,12 @@ __global__ __launch_bounds__(kThreads, 2) void project_state_bf16(ProjArgs p, St
   const int sw = 16 * (g ^ proj_swz(n));
   const int a_rd = (128 * th + n) * 64 + sw;
   const int b_rd = kBOff + (64 * hh + n) * 64 + sw;
+  // RoPE: the pair partner's sign, and where the per-axis entries of this
+  // lane's pairs (features n and 16 + n) sit; the axis tables go to LDS (the
+  // first block's barrier orders the copy before any lookup)
+  const float sgn = (n & 1) ? 1.f : -1.f;
+  const AxisPair ap[2] = {axis_pair(rp, n >> 1), axis_pair(rp, (16 + n) >> 1)};
+  rope_stage<ROPE>(rp, rtab, tid, kThreads);
 
   const unsigned one2 = 0x3f803f80u;
   const bf16x8_t ones = as_bf16x8(one2, one2, one2, one2);
@@ -223,10 +258,56 @@ __global__ __launch_bounds__(kThreads, 2) void project_state_bf16(ProjArgs p, St
         vb[fh] = pack_turned(acc[2 * t][2 + fh], acc[2 * t + 1][2 + fh]);
       }
 #pragma unroll
-      for (int fh = 0; fh < 2; ++fh) {
-        Z[fh] = mfma16(ka[fh], ones, Z[fh]);
-        S[fh][0] = mfma16(ka[fh], vb[0], S[fh][0]);
-        S[fh][1] = mfma16(ka[fh], vb[1], S[fh][1]);
+      for (int fh = 0; fh < 2; ++fh) Z[fh] = mfma16(ka[fh], ones, Z[fh]);
+      if constexpr (ROPE == kRopeNone) {
+#pragma unroll
+        for (int fh = 0; fh < 2; ++fh) {
+          S[fh][0] = mfma16(ka[fh], vb[0], S[fh][0]);
+          S[fh][1] = mfma16(ka[fh], vb[1], S[fh][1]);
+        }
+      } else {
+        // Slot s of ka[fh] holds phi(K) of feature f = 16 fh + n for token
+        // tok0 + 128 th + 16 (2t + s / 4) + 4 g + s % 4; the pair partner
+        // f ^ 1 sits in lane n ^ 1, same slot.  Rotated: x c - x' s for even
+        // f, x' s + x c for odd f, in fp32, then split into three bf16 parts
+        // contracted against V one by one.  A token's angles are looked up
+        // once for both feature halves.
+        u32x4_t kw[2], pw[2];
+#pragma unroll
+        for (int fh = 0; fh < 2; ++fh) {
+          kw[fh] = __builtin_bit_cast(u32x4_t, ka[fh]);
+#pragma unroll
+          for (int d = 0; d < 4; ++d) pw[fh][d] = (unsigned)__builtin_amdgcn_mov_dpp((int)kw[fh][d], 0xB1, 0xF, 0xF, false);
+        }
+        unsigned part[2][3][4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          float y[2][2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int slot = 2 * d + e;
+            const int64_t tok = tok0 + 128 * th + 16 * (2 * t + (slot >> 2)) + 4 * g + (slot & 3);
+            float c[2], sn[2];
+            proj_angles<ROPE>(rp, rtab, ap, tok < p.N ? tok : p.N - 1, c, sn);
+#pragma unroll
+            for (int fh = 0; fh < 2; ++fh) {
+              const float x = e ? bf16hi_to_f32(kw[fh][d]) : bf16lo_to_f32(kw[fh][d]);
+              const float xp = sgn * (e ? bf16hi_to_f32(pw[fh][d]) : bf16lo_to_f32(pw[fh][d]));
+              y[fh][e] = x * c[fh] + xp * sn[fh];
+            }
+          }
+#pragma unroll
+          for (int fh = 0; fh < 2; ++fh) split3_bf16x2(y[fh][0], y[fh][1], part[fh][0][d], part[fh][1][d], part[fh][2][d]);
+        }
+#pragma unroll
+        for (int fh = 0; fh < 2; ++fh) {
+#pragma unroll
+          for (int k = 0; k < 3; ++k) {
+            const bf16x8_t ar = as_bf16x8(part[fh][k][0], part[fh][k][1], part[fh][k][2], part[fh][k][3]);
+            S[fh][0] = mfma16(ar, vb[0], S[fh][0]);
+            S[fh][1] = mfma16(ar, vb[1], S[fh][1]);
+          }
+        }
       }
     }
   }

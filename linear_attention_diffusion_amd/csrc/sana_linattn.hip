@@ -851,8 +851,8 @@ size_t sana_linattn_project_state_workspace_bytes(int B, int H, int64_t N, int C
 }
 
 int sana_linattn_project_state(const void* x, const void* w_k, const void* w_v, float* kv_state, float* ksum_state,
-                               int B, int H, int64_t N, int C, int D, int dtype, void* ws, size_t ws_bytes,
-                               void* hip_stream) {
+                               int B, int H, int64_t N, int C, int D, int dtype, const sana_rope* rope, void* ws,
+                               size_t ws_bytes, void* hip_stream) {
   ProjGeometry g;
   int rc = make_proj_geometry(B, H, N, C, D, dtype, &g);
   if (rc != SANA_OK) return rc;
@@ -867,6 +867,7 @@ int sana_linattn_project_state(const void* x, const void* w_k, const void* w_v, 
     if (overlaps(kv_state, kv_bytes, ins[i], in_bytes[i]) || overlaps(ksum_state, ks_bytes, ins[i], in_bytes[i]))
       return SANA_ERR_INVALID;
   if (overlaps(kv_state, kv_bytes, ksum_state, ks_bytes)) return SANA_ERR_INVALID;
+  if ((rc = check_rope(rope, N)) != SANA_OK) return rc;
   if (!ws || ws_bytes < g.total_bytes) return SANA_ERR_WORKSPACE;
   if (!aligned(ws, 256)) return SANA_ERR_INVALID;
 
@@ -894,7 +895,11 @@ int sana_linattn_project_state(const void* x, const void* w_k, const void* w_v, 
   a.C = 1;
   a.Pc = (int)g.R;
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
-  la::project_state_bf16<<<dim3((unsigned)g.G), dim3(la::kThreads), 0, st>>>(p, a);
+  const RopeArg ra = rope_arg(rope, N);
+  with_rope(ra.kind, [&](auto R) {
+    constexpr int RO = decltype(R)::value;
+    la::project_state_bf16<RO><<<dim3((unsigned)g.G), dim3(la::kThreads), 0, st>>>(p, ra.r, a);
+  });
   if (g.R > 1) {
     const int64_t n_elems = g.BH * la::kStateElems;
     la::state_finalize<<<dim3((unsigned)ceil_div(n_elems, la::kThreads)), dim3(la::kThreads), 0, st>>>(a, n_elems);

@@ -13,6 +13,13 @@ one bf16 step.  The state's fp32 sums pass each product through at most
 A = |phi(K)|^T |V| over the tokens (the b's added in),
   |dS| <= b_K^T (|V| + b_V) + |phi(K)|^T b_V + 2 (N / 32 + 200) 2^-24 A,
   |dz| <= sum b_K + 2 (N / 32 + 200) 2^-24 sum (|phi(K)| + b_K).
+With RoPE, S contracts the rotated keys y = R phi(K): y_d = x_d c -+ x_d' s
+(d' = d ^ 1), taken in fp32 from float32 cos/sin and split into three bf16
+parts.  Against the oracle's float64 rotation, |dy_d| <= b_d + b_d' +
+6 2^-24 (|x_d| + |x_d'| + b_d + b_d') (|c|, |s| <= 1: two products and a sum,
+the float32 rounding of cos and sin, the split's remainder), and the bound
+above holds with y and dy in place of phi(K) and b_K in S, and 3 N / 32 in
+place of N / 32 (three parts added per 32 tokens); z stays unrotated.
 A relative-error bar would not do: one K rounding the other way moves an
 element of S that happens to be near zero by far more than a fixed fraction of
 it.  The aggregate rel-L2 must also stay below 1e-3.  A library GEMM of
@@ -33,16 +40,17 @@ def oracle_weights(w, H, D=32):
     return np.ascontiguousarray(w.reshape(H, D, C).transpose(0, 2, 1))
 
 
-def check_projected_state(kv, z, x, heads=None, kv0=None, z0=None, any_order=False):
+def check_projected_state(kv, z, x, heads=None, kv0=None, z0=None, any_order=False, angles=None, pos_offset=0):
     """kv, z (float64, [B, H', 32, 32] and [B, H', 32] for the chosen heads of
     the ProjectionInputs x) against the oracle within the bound above, with
     kv0, z0 the states the call started from (None: zero).  any_order: the
-    projection's sums were taken in an unknown order.  Returns (ok, report)."""
+    projection's sums were taken in an unknown order.  angles, pos_offset: the
+    keys' RoPE, as for the oracle.  Returns (ok, report)."""
     p = x.workload
     wk, wv = oracle_weights(x.f64["w_k"], p.H), oracle_weights(x.f64["w_v"], p.H)
     if heads is not None:
         wk, wv = wk[heads], wv[heads]
-    S, zr = oracle.projected_kv_state(x.f64["x"], wk, wv)
+    S, zr = oracle.projected_kv_state(x.f64["x"], wk, wv, angles, pos_offset)
     if kv0 is not None:
         S, zr = S + kv0, zr + z0
     xa = np.abs(x.f64["x"])[:, None]                           # [B, 1, N, C]
@@ -59,10 +67,17 @@ def check_projected_state(kv, z, x, heads=None, kv0=None, z0=None, any_order=Fal
     V, bV = spread(wv)
     phik = np.maximum(K, 0.0)
     absV = np.abs(V) + bV
-    kt = np.swapaxes(phik, -1, -2)
-    bkt = np.swapaxes(bK, -1, -2)
-    gam = 2.0 * (N / 32 + 200) * U
-    tol_S = np.matmul(bkt, absV) + np.matmul(kt, bV) + gam * np.matmul(kt + bkt, absV)
+    if angles is None:
+        Y, bY = phik, bK
+    else:
+        Y = np.abs(oracle.rotate_pairs(phik, angles[pos_offset:pos_offset + N]))
+        sw = np.arange(phik.shape[-1]) ^ 1                      # pair partner of each feature
+        bY = bK + bK[..., sw] + 6.0 * U * (phik + phik[..., sw] + bK + bK[..., sw])
+    yt = np.swapaxes(np.abs(Y), -1, -2)
+    byt = np.swapaxes(bY, -1, -2)
+    # with RoPE each 32-token group adds three parts to the accumulator
+    gam = 2.0 * ((1 if angles is None else 3) * N / 32 + 200) * U
+    tol_S = np.matmul(byt, absV) + np.matmul(yt, bV) + gam * np.matmul(yt + byt, absV)
     tol_z = bK.sum(axis=-2) + gam * (phik + bK).sum(axis=-2)
     n_amb = int(np.count_nonzero(bK)) + int(np.count_nonzero(bV))
     lines = []

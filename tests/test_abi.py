@@ -142,9 +142,9 @@ def test_project_state_argument_errors_and_workspace():
     assert pw(1, 2, 64, 64, D=64) == 0 and pw(1, 2, 64, 64, dtype=la.SANA_DT_F32) == 0
     n = pw(1, 2, 1000, 64)
 
-    def ps(x=A, wk=Bp, wv=C, kv=Dp, ks=Dp + 8192, B=1, H=2, N=1000, Cin=64, D=32, dt=la.SANA_DT_BF16, ws=WS,
-           nbytes=n):
-        return L.sana_linattn_project_state(x, wk, wv, kv, ks, B, H, N, Cin, D, dt, ws, nbytes, None)
+    def ps(x=A, wk=Bp, wv=C, kv=Dp, ks=Dp + 8192, B=1, H=2, N=1000, Cin=64, D=32, dt=la.SANA_DT_BF16, rope=None,
+           ws=WS, nbytes=n):
+        return L.sana_linattn_project_state(x, wk, wv, kv, ks, B, H, N, Cin, D, dt, rope, ws, nbytes, None)
 
     E = la
     assert ps(x=None) == E.SANA_ERR_INVALID
@@ -166,6 +166,11 @@ def test_project_state_argument_errors_and_workspace():
     assert ps(ws=None) == E.SANA_ERR_WORKSPACE
     assert ps(nbytes=n - 1) == E.SANA_ERR_WORKSPACE
     assert ps(ws=WS + 64) == E.SANA_ERR_INVALID
+    # RoPE tables must cover the N positions read
+    r = sana_rope(0x60000000, 0x70000000, 999, 0)
+    assert ps(rope=ctypes.byref(r)) == E.SANA_ERR_INVALID
+    r = sana_rope(0x60000000, 0x70000000, 1000, 1)
+    assert ps(rope=ctypes.byref(r)) == E.SANA_ERR_INVALID
     # no tokens or no heads: the states stay as they are, nothing is touched
     assert ps(x=None, wk=None, wv=None, kv=None, ks=None, N=0, ws=None) == E.SANA_OK
     assert ps(x=None, wk=None, wv=None, kv=None, ks=None, B=0, ws=None) == E.SANA_OK

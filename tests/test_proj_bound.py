@@ -75,3 +75,55 @@ def test_planted_mistakes_fail(case, mistake):
         S, z = _state(trunc(_proj(x, wk, False)), trunc(_proj(x, wv, False)))
     ok, report = check_projected_state(S, z, x)
     assert not ok, f"{mistake} passed the bound: {report}"
+
+
+@pytest.fixture(scope="module")
+def rope_case():
+    grid = (2, 5, 7)
+    x = generate_projection(reduced(PROJECTIONS["sana16b_4096px_kv_proj"], B=2, N=60, C=64, H=2, seed=22))
+    wk, wv = oracle_weights(x.f64["w_k"], 2), oracle_weights(x.f64["w_v"], 2)
+    return x, wk, wv, oracle.rope3d_angles(*grid)
+
+
+def _rotated_state(x, wk, wv, angles, off, rotate):
+    k, v = _proj(x, wk), _proj(x, wv)
+    phik = np.maximum(k, 0.0)
+    S = np.matmul(np.swapaxes(rotate(phik, angles[off:off + x.workload.N]), -1, -2), v)
+    return S, phik.sum(axis=-2)
+
+
+def test_rope_oracle_and_float32_rotation_pass(rope_case):
+    x, wk, wv, angles = rope_case
+    S, z = oracle.projected_kv_state(x.f64["x"], wk, wv, angles, 10)
+    ok, report = check_projected_state(S, z, x, angles=angles, pos_offset=10)
+    assert ok, report
+
+    def rot32(y, a):
+        # float32 cos/sin and float32 products, as the kernel computes them
+        c, s = np.cos(a).astype(np.float32), np.sin(a).astype(np.float32)
+        y = y.astype(np.float32)
+        out = np.empty_like(y)
+        out[..., 0::2] = y[..., 0::2] * c - y[..., 1::2] * s
+        out[..., 1::2] = y[..., 0::2] * s + y[..., 1::2] * c
+        return out.astype(np.float64)
+
+    S32, z32 = _rotated_state(x, wk, wv, angles, 10, rot32)
+    ok, report = check_projected_state(S32, z32, x, angles=angles, pos_offset=10)
+    assert ok, report
+
+
+@pytest.mark.parametrize("mistake", ["unrotated", "sign", "offset", "rotated_z"])
+def test_rope_planted_mistakes_fail(rope_case, mistake):
+    x, wk, wv, angles = rope_case
+    if mistake == "unrotated":
+        S, z = oracle.projected_kv_state(x.f64["x"], wk, wv)
+    elif mistake == "sign":
+        S, z = oracle.projected_kv_state(x.f64["x"], wk, wv, -angles, 10)
+    elif mistake == "offset":
+        S, z = oracle.projected_kv_state(x.f64["x"], wk, wv, angles, 0)
+    else:
+        S, _ = oracle.projected_kv_state(x.f64["x"], wk, wv, angles, 10)
+        phik = np.maximum(_proj(x, wk), 0.0)
+        z = oracle.rotate_pairs(phik, angles[10:10 + x.workload.N]).sum(axis=-2)
+    ok, report = check_projected_state(S, z, x, angles=angles, pos_offset=10)
+    assert not ok, f"{mistake} passed the bound: {report}"

@@ -7,6 +7,7 @@ The tolerance is the element-wise bound derived in proj_bound.py."""
 import pytest
 
 import linear_attention_diffusion_amd as la
+import oracle
 from gpu_util import device, to_dev, to_np, torch_mod
 from proj_bound import check_projected_state
 from workloads import PROJECTIONS, generate_projection, reduced
@@ -22,7 +23,7 @@ def _check_state(*args, **kw):
     assert ok, report
 
 
-def _run(x, kv=None, z=None):
+def _run(x, kv=None, z=None, rope=None):
     torch = torch_mod()
     p = x.workload
     dev = device()
@@ -30,7 +31,7 @@ def _run(x, kv=None, z=None):
     if kv is None:
         kv = torch.zeros(p.B, p.H, 32, 32, device=dev)
         z = torch.zeros(p.B, p.H, 32, device=dev)
-    la.sana_linattn_project_state(xs, wk, wv, kv, z)
+    la.sana_linattn_project_state(xs, wk, wv, kv, z, rope=rope)
     return kv, z
 
 
@@ -100,3 +101,36 @@ def test_full_4096px_layer_sampled_heads():
     kv, z = _run(x)
     heads = [0, 1, 37, 68, 69]
     _check_state(to_np(kv)[:, heads], to_np(z)[:, heads], x, heads)
+
+
+def _same(a, b, what):
+    torch = torch_mod()
+    assert bool((a.view(torch.int32) == b.view(torch.int32)).all()), f"{what}: the two RoPE forms differ"
+
+
+@pytest.mark.parametrize("B,N,C,H,grid,offset", [(2, 480, 64, 3, (3, 8, 20), 0), (1, 300, 96, 2, (4, 10, 12), 150),
+                                                 (1, 1000, 32, 5, (5, 10, 20), 0)])
+def test_project_state_rope(B, N, C, H, grid, offset):
+    """Keys rotated by the 3D RoPE at positions offset .. offset + N - 1, with
+    the full tables and with the per-axis tables (bit-identical to each
+    other), against the oracle."""
+    print(f"case project_state rope B={B} N={N} C={C} H={H} grid={grid} offset={offset}", flush=True)
+    x = generate_projection(reduced(FULL, B=B, N=N, C=C, H=H, seed=N + 7))
+    table = la.rope3d_device(*grid, device()).at(offset)
+    axes = la.rope3d_axes_device(*grid, device()).at(offset)
+    kv_t, z_t = _run(x, rope=table)
+    kv_a, z_a = _run(x, rope=axes)
+    _same(kv_a, kv_t, "S")
+    _same(z_a, z_t, "z")
+    _check_state(to_np(kv_a), to_np(z_a), x, angles=oracle.rope3d_angles(*grid), pos_offset=offset)
+
+
+def test_full_720p_layer_rope_sampled_heads():
+    """The SANA-Video 720p layer's keys (21 x 22 x 40 = 18480 tokens, C = 2240,
+    70 heads) with the per-axis 3D RoPE; the oracle computes four heads."""
+    grid = (21, 22, 40)
+    x = generate_projection(reduced(FULL, N=grid[0] * grid[1] * grid[2], seed=3))
+    print("case project_state full 720p rope", flush=True)
+    kv, z = _run(x, rope=la.rope3d_axes_device(*grid, device()))
+    heads = [0, 1, 36, 69]
+    _check_state(to_np(kv)[:, heads], to_np(z)[:, heads], x, heads, angles=oracle.rope3d_angles(*grid))
