@@ -162,7 +162,8 @@ __global__ __launch_bounds__(kThreads) void bwd_query_vec(const float* __restric
 #pragma unroll
       for (int u = 0; u < 4; ++u) num[u] += qd * sS[d][f0 + u];
     }
-    const float rden = 1.f / den;
+    // rows past the split's end carry zeros: they must add nothing, eps = 0 included
+    const float rden = live ? 1.f / den : 0.f;
     float dot = 0.f;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -636,7 +637,8 @@ __global__ __launch_bounds__(kThreads) void bwd_query_bf16(const u32x4_t* __rest
       f32x4_t dacc = mfma16(zrow[0], bq[tb], zero4);
       dacc = mfma16(zrow[1], bq[tb], dacc);
       dacc = mfma16(zrow[2], bq[tb], dacc);
-      const float rden = 1.f / (dacc[0] + eps);
+      // rows past the split's end carry zeros: they must add nothing, eps = 0 included
+      const float rden = t0 + 16 * tb + n < n_end ? 1.f / (dacc[0] + eps) : 0.f;
       float pq[8], y[8];
       unpack8(qr, pq);
       f32x4_t n0, n1;

@@ -421,4 +421,266 @@ __global__ __launch_bounds__(kThreads) void bwd_key_bf16_lines(const u32x4_t* __
   }
 }
 
+// Query pass of the backward for head-paired views.  A workgroup of eight
+// waves takes heads 2u and 2u + 1 of one split: waves 2p and 2p + 1 (pair p)
+// take heads 2u and 2u + 1 of the same 32-token tiles, 4k + p for k = 0, 1,
+// ...  Per tile, the pair's first wave loads the 32 whole lines of Q (both
+// heads) and the second those of dO into the pair's LDS tiles; after a
+// barrier each wave computes its own head exactly as bwd_query_bf16 does, and
+// dQ goes back through a line tile when the output pairs heads too.  Pair p
+// sees the tiles of the one-head kernel's wave p, in the same order, so the
+// partial dS and dz sum in the same order and the results are bit-identical to
+// it.  Every wave runs the same number of tiles (those past the split's end
+// load zeros and store nothing), as the loop holds workgroup barriers.
+template <int ROPE>
+__global__ __launch_bounds__(2 * kThreads) void bwd_query_bf16_lines(const u32x4_t* __restrict__ Q,
+                                                                 const u32x4_t* __restrict__ dO,
+                                                                 u32x4_t* __restrict__ dQ, Layout lin, Layout lout,
+                                                                 StateView fwd, float eps, Rope rp, StateArgs a,
+                                                                 int64_t units) {
+  // line tiles: per pair Q, dO and dQ; then, after the loop, the reduction
+  constexpr int kLines = 4 * 3 * kLineTile;
+  constexpr int kRed = 2 * 4 * kStateElems;
+  __shared__ __attribute__((aligned(16))) float smem[kLines > kRed ? kLines : kRed];
+  __shared__ float tiles[8][ROPE ? 2 : 1][kTileFloats];
+  __shared__ __attribute__((aligned(16))) float rtab[ROPE == kRopeAxes ? 2 * kMaxAxisTab : 1];
+  rope_stage<ROPE>(rp, rtab, threadIdx.x, 2 * kThreads);
+  if constexpr (ROPE == kRopeAxes) __syncthreads();
+
+  int64_t u, n_begin, n_end;
+  int c, s;
+  state_item(a, u, c, s, n_begin, n_end, units);
+  const int64_t bh0 = 2 * u;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int pr = w >> 1, hd = w & 1;
+  const int64_t bh = bh0 + hd;
+  const int n = lane & 15;
+  const int g = lane >> 4;
+  const AxisLane al = axis_lane(rp, g);  // axis form only
+  const int64_t irow = lin.token * 2, orow = lout.token * 2;  // bytes between tokens
+  const int line_off = (lane >> 3) * (int)irow + (lane & 7) * 16;
+  const int oline_off = (lane >> 3) * (int)orow + (lane & 7) * 16;
+  const int out_off = n * (int)orow + g * 16;
+  const int tab_off = n * 64 + g * 16;
+  const bool out_lines = lout.head == kD;
+  // the pair's first wave streams Q, the second dO
+  const char* src = reinterpret_cast<const char*>(hd ? dO : Q) + lin.base(bh0) * 2;
+  char* dQp = reinterpret_cast<char*>(dQ) + lout.base(bh0) * 2;
+  char* dQh = reinterpret_cast<char*>(dQ) + lout.base(bh) * 2;
+  float* st_q = smem + pr * 3 * kLineTile;
+  float* st_o = st_q + kLineTile;
+  float* st_dq = st_o + kLineTile;
+  float* dn_tile = tiles[w][0];
+  float* pq_tile = tiles[w][ROPE ? 1 : 0];
+
+  const int64_t sc = bh * a.C + c;
+  const float* S = fwd.s_base + sc * fwd.s_stride;
+  const float* Z = fwd.z_base + sc * fwd.z_stride;
+  bf16x8_t scol[2][3], srow[2][3], zrow[3];
+  load_column_operands(S, g, n, scol);  // num = S^T phi~(Q)
+  load_row_operands(S, g, n, srow);     // S dO
+  load_vector_operands(Z, g, zrow);     // den
+  float zf[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) zf[j] = Z[8 * g + j];
+  const bf16x8_t sel[2] = {select_operand(g, n, 0), select_operand(g, n, 1)};
+
+  f32x4_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) acc[i][0] = acc[i][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float dzacc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) dzacc[e] = 0.f;
+
+  // tile index i of the split -> tokens n_begin + 32 i; pair pr takes i = 4k + pr
+  const int64_t n_tiles = (n_end - n_begin + 31) / 32;
+  const int64_t iters = (n_tiles + 3) / 4;
+  auto tile_t0 = [&](int64_t it) { return n_begin + 32 * (4 * it + pr); };
+  u32x4_t nl[4];
+  TileAnglesRows na;
+  auto load_tile = [&](int64_t t0) {
+    load_lines(lines_rsrc(src, t0, n_end, irow), line_off, irow, nl);
+    if constexpr (ROPE == kRopeTable) load_angle_rows(rp.cos, rp.sin, rp.pos0, t0, n_end, tab_off, na);
+  };
+  if (iters > 0) load_tile(tile_t0(0));
+
+  for (int64_t it = 0; it < iters; ++it) {
+    const int64_t t0 = tile_t0(it);
+    stage_lines(hd ? st_o : st_q, lane, nl);
+    TileAnglesRows ang = na;
+    __syncthreads();  // both halves of the pair's tile are staged
+    if (it + 1 < iters) load_tile(tile_t0(it + 1));
+    u32x4_t qx[2], ox[2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      qx[tb] = staged_piece(st_q, tb, hd, n, g);
+      ox[tb] = staged_piece(st_o, tb, hd, n, g);
+    }
+    const rsrc_t rdq = rows_rsrc(dQh, t0, n_end, orow);
+    bf16x8_t bq[2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      const u32x4_t qr = relu_bf16x8(qx[tb]);
+      bq[tb] = __builtin_bit_cast(bf16x8_t, qr);
+      f32x4_t ang_c = ang.c[tb], ang_s = ang.s[tb];
+      if constexpr (ROPE == kRopeAxes) rope_axis_row4(rp, rtab, al, rp.pos0 + t0 + 16 * tb + n, ang_c, ang_s);
+      const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+      f32x4_t dacc = mfma16(zrow[0], bq[tb], zero4);
+      dacc = mfma16(zrow[1], bq[tb], dacc);
+      dacc = mfma16(zrow[2], bq[tb], dacc);
+      // rows past the split's end carry zeros: they must add nothing, eps = 0 included
+      const float rden = t0 + 16 * tb + n < n_end ? 1.f / (dacc[0] + eps) : 0.f;
+      float pq[8], y[8];
+      unpack8(qr, pq);
+      f32x4_t n0, n1;
+      if constexpr (!ROPE) {
+        mfma3(scol, bq[tb], n0, n1);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) y[j] = pq[j];
+        rotate8<false>(y, ang_c, ang_s);
+        bf16x8_t br[3];
+        split8(y, br);
+        mfma6(scol, br, n0, n1);
+      }
+      f32x4_t s0, s1;
+      mfma3(srow, __builtin_bit_cast(bf16x8_t, ox[tb]), s0, s1);
+      float gd[8], num[8], dr[8];
+      unpack8(ox[tb], gd);
+      num[0] = n0[0], num[1] = n0[1], num[2] = n0[2], num[3] = n0[3];
+      num[4] = n1[0], num[5] = n1[1], num[6] = n1[2], num[7] = n1[3];
+      dr[0] = s0[0], dr[1] = s0[1], dr[2] = s0[2], dr[3] = s0[3];
+      dr[4] = s1[0], dr[5] = s1[1], dr[6] = s1[2], dr[7] = s1[3];
+      float dot = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dot += gd[j] * num[j];
+      dot += __shfl_xor(dot, 16);
+      dot += __shfl_xor(dot, 32);
+      const float dden = -dot * rden * rden;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dr[j] *= rden;
+      if constexpr (ROPE) rotate8<true>(dr, ang_c, ang_s);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        dr[j] = pq[j] > 0.f ? dr[j] + zf[j] * dden : 0.f;
+        dzacc[j] += pq[j] * dden;
+      }
+      if (out_lines)
+        put_piece(st_dq, tb, hd, n, g, pack8(dr));
+      else
+        store16_nt(rdq, out_off + tb * 16 * (int)orow, pack8(dr));
+      // dnum (and phi~(Q)) of token row 16tb + n, features 8g .. 8g+7
+      float* rowp = dn_tile + (16 * tb + n) * kTileRow + 8 * g;
+      *reinterpret_cast<f32x4_t*>(rowp) = f32x4_t{gd[0] * rden, gd[1] * rden, gd[2] * rden, gd[3] * rden};
+      *reinterpret_cast<f32x4_t*>(rowp + 4) = f32x4_t{gd[4] * rden, gd[5] * rden, gd[6] * rden, gd[7] * rden};
+      if constexpr (ROPE) {
+        float* rowq = pq_tile + (16 * tb + n) * kTileRow + 8 * g;
+        *reinterpret_cast<f32x4_t*>(rowq) = f32x4_t{y[0], y[1], y[2], y[3]};
+        *reinterpret_cast<f32x4_t*>(rowq + 4) = f32x4_t{y[4], y[5], y[6], y[7]};
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // turned-around operands: lane (n, g), k-slots (tb, i) = tokens 16tb + 4g + i
+    bf16x8_t bd[2][3];  // dnum, B operand for value half fh' (columns n)
+#pragma unroll
+    for (int fh = 0; fh < 2; ++fh) {
+      unsigned part[3][4];
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        const float* col = dn_tile + (16 * tb + 4 * g) * kTileRow + 16 * fh + n;
+        split3_bf16x2(col[0], col[kTileRow], part[0][2 * tb], part[1][2 * tb], part[2][2 * tb]);
+        split3_bf16x2(col[2 * kTileRow], col[3 * kTileRow], part[0][2 * tb + 1], part[1][2 * tb + 1],
+                      part[2][2 * tb + 1]);
+      }
+#pragma unroll
+      for (int k = 0; k < 3; ++k) bd[fh][k] = as_bf16x8(part[k][0], part[k][1], part[k][2], part[k][3]);
+    }
+    if constexpr (!ROPE) {
+#pragma unroll
+      for (int fh = 0; fh < 2; ++fh) {
+        const bf16x8_t aq = pack_turned(turn(bq[0], sel[fh]), turn(bq[1], sel[fh]));
+#pragma unroll
+        for (int fv = 0; fv < 2; ++fv) {
+          acc[fh][fv] = mfma16(aq, bd[fv][0], acc[fh][fv]);
+          acc[fh][fv] = mfma16(aq, bd[fv][1], acc[fh][fv]);
+          acc[fh][fv] = mfma16(aq, bd[fv][2], acc[fh][fv]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int fh = 0; fh < 2; ++fh) {
+        unsigned part[3][4];
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+          const float* col = pq_tile + (16 * tb + 4 * g) * kTileRow + 16 * fh + n;
+          split3_bf16x2(col[0], col[kTileRow], part[0][2 * tb], part[1][2 * tb], part[2][2 * tb]);
+          split3_bf16x2(col[2 * kTileRow], col[3 * kTileRow], part[0][2 * tb + 1], part[1][2 * tb + 1],
+                        part[2][2 * tb + 1]);
+        }
+        bf16x8_t aq[3];
+#pragma unroll
+        for (int k = 0; k < 3; ++k) aq[k] = as_bf16x8(part[k][0], part[k][1], part[k][2], part[k][3]);
+#pragma unroll
+        for (int fv = 0; fv < 2; ++fv) {
+          f32x4_t x = acc[fh][fv];
+          x = mfma16(aq[0], bd[fv][0], x);
+          x = mfma16(aq[0], bd[fv][1], x);
+          x = mfma16(aq[1], bd[fv][0], x);
+          x = mfma16(aq[0], bd[fv][2], x);
+          x = mfma16(aq[2], bd[fv][0], x);
+          x = mfma16(aq[1], bd[fv][1], x);
+          acc[fh][fv] = x;
+        }
+      }
+    }
+    __syncthreads();  // the dQ tile is complete; every read of the Q and dO tiles is done
+    if (out_lines) {
+      u32x4_t x[4];
+      unstage_lines(st_dq, lane, x);
+      const rsrc_t r = lines_rsrc(dQp, t0, n_end, orow);
+#pragma unroll
+      for (int j = 2 * hd; j < 2 * hd + 2; ++j) store16_nt(r, oline_off + j * 8 * (int)orow, x[j]);
+    }
+  }
+
+  // dz: sum the 16 lanes of each group (token rows), feature 8g + j
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float x = dzacc[e];
+    x += __shfl_xor(x, 1);
+    x += __shfl_xor(x, 2);
+    x += __shfl_xor(x, 4);
+    x += __shfl_xor(x, 8);
+    dzacc[e] = x;
+  }
+  // partials of head hd: red[hd][pr] (the one-head kernel's wave pr)
+  __syncthreads();  // the reduction area overlaps the line tiles
+  float(*red)[4][kStateElems] = reinterpret_cast<float(*)[4][kStateElems]>(smem);
+  float* rw = red[hd][pr];
+#pragma unroll
+  for (int fh = 0; fh < 2; ++fh) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d = 16 * fh + 4 * g + i;
+      rw[d * 32 + n] = acc[fh][0][i];
+      rw[d * 32 + 16 + n] = acc[fh][1][i];
+    }
+  }
+  if (n == 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) rw[1024 + 8 * g + e] = dzacc[e];
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < 2 * kStateElems; idx += 2 * kThreads) {
+    float(*r)[kStateElems] = red[idx / kStateElems];
+    const int e = idx % kStateElems;
+    r[0][e] = (r[0][e] + r[1][e]) + (r[2][e] + r[3][e]);
+  }
+  __syncthreads();
+  // waves 0-3 write head 2u's partial, waves 4-7 head 2u + 1's
+  write_partial(red[threadIdx.x >> 8][0], bh0 + (threadIdx.x >> 8), c, s, a, threadIdx.x & 255);
+}
+
 }  // namespace la

@@ -479,8 +479,12 @@ void launch_backward(const void* q, const void* k, const void* v, const void* do
       const auto* Q = static_cast<const la::u32x4_t*>(q);
       const auto* dO = static_cast<const la::u32x4_t*>(dout);
       auto* dQ = static_cast<la::u32x4_t*>(dq);
+      const dim3 pgrid((unsigned)(ceil_div(g.BH, 2) * g.C * g.Pc));
       if (lin.token == la::kD && lout.token == la::kD)
         la::bwd_query_bf16<RO, true><<<qgrid, block, 0, st>>>(Q, dO, dQ, lin, lout, view, eps, ra.r, bwd);
+      else if (whole_lines(lin))
+        la::bwd_query_bf16_lines<RO><<<pgrid, dim3(2 * la::kThreads), 0, st>>>(Q, dO, dQ, lin, lout, view, eps, ra.r,
+                                                                               bwd, g.BH / 2);
       else
         la::bwd_query_bf16<RO, false><<<qgrid, block, 0, st>>>(Q, dO, dQ, lin, lout, view, eps, ra.r, bwd);
     } else {

@@ -87,6 +87,17 @@ def test_backward_small(case):
     _run(w, chunk, rope=grid is not None, carried=carried, out_grad=out_grad, label="small")
 
 
+@pytest.mark.parametrize("dtype,chunk", [("bf16", None), ("bf16", 300), ("f32", None), ("f32", 300)])
+def test_backward_eps_zero_ragged(dtype, chunk):
+    """eps = 0 with token ranges that end inside a 32-token tile: the rows
+    padded past a range's end hold zeros, and their 1 / (den + eps) must not
+    reach dS or dz (every real row has den > 0 here)."""
+    w = Workload(name="bwd_eps0", B=1, H=3, N=1000, dtype=dtype, scale=0.5 if dtype == "bf16" else 1.0, eps=0.0)
+    dq, dk, dv, dkv, dz = _run(w, chunk, label="eps0")
+    for t in (dq, dk, dv, dkv, dz):
+        assert bool(torch_mod().isfinite(t).all())
+
+
 @pytest.mark.parametrize("name", ["sana16b_4096px", "video720p_rope3d", "video480p_blockcausal"])
 def test_backward_full_size(name):
     w = WORKLOADS[name]

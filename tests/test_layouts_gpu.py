@@ -86,15 +86,19 @@ def test_block_causal_and_block_forward_packed(H):
     _same(oc, o_ref[:, :, s:e])
 
 
-@pytest.mark.parametrize("rope,grid", [(False, (3, 8, 20)), (True, (3, 8, 20)), (False, (3, 7, 21)),
-                                       (True, (3, 7, 21))])
-def test_backward_packed(rope, grid):
+@pytest.mark.parametrize("rope,grid,eps", [(False, (3, 8, 20), 1e-6), (True, (3, 8, 20), 1e-6),
+                                           (False, (3, 7, 21), 1e-6), (True, (3, 7, 21), 1e-6),
+                                           (False, (3, 7, 21), 0.0), ("axes", (2, 9, 25), 1e-6)])
+def test_backward_packed(rope, grid, eps):
+    """The backward read from a packed [B, N, 4, H, D] buffer (q, k, v, dO) and
+    written to [B, N, H, D]: with H even the query and key passes take head
+    pairs from whole lines; bit-identical to the contiguous call."""
     w = reduced(WORKLOADS["video720p_rope3d"], H=4, N=grid[0] * grid[1] * grid[2], grid=grid,
-                mode="rope" if rope else "noncausal")
-    print(f"case backward packed rope={rope}", flush=True)
+                mode="rope" if rope else "noncausal", eps=eps)
+    print(f"case backward packed rope={rope} grid={grid} eps={eps}", flush=True)
     x = generate(w, names=("q", "k", "v", "dout"))
     (q, k, v, do), (qv, kv_, vv, dov) = _packed(x, ("q", "k", "v", "dout"))
-    r = rope_for(w) if rope else None
+    r = (la.rope3d_axes_device(*grid, device()) if rope == "axes" else rope_for(w)) if rope else None
     ref_dev = la.sana_linattn_backward(q, k, v, do, chunk=160, eps=w.eps, rope=r)
     outs = [_bnhd(w, q.dtype) for _ in range(3)]
     la.sana_linattn_backward(qv, kv_, vv, dov, chunk=160, dq=outs[0], dk=outs[1], dv=outs[2], eps=w.eps, rope=r)
