@@ -387,11 +387,25 @@ def backward_bench(w, args, dev, stream):
     base = {n: to_dev(x.raw[n]) for n in ("q", "k", "v", "dout")}
     set_bytes = 7 * base["q"].numel() * base["q"].element_size()
     n_sets = max(2, min(16, math.ceil(1.5 * 2 ** 30 / set_bytes) + 1))
+    packed = args.layout == "packed"
+    if packed and w.mode == "block":
+        raise SystemExit("--layout packed covers the non-causal and RoPE workloads")
     sets = []
     for i in range(n_sets):
-        s = {n: (t if i == 0 else t.clone()) for n, t in base.items()}
-        for n in ("dq", "dk", "dv"):
-            s[n] = torch.empty_like(base["q"])
+        if packed:
+            # q, k, v, dO as [B, H, N, D] views of one [B, N, 4, H, D] buffer;
+            # dQ, dK, dV as views of [B, N, H, D] buffers
+            buf = torch.empty(w.B, w.N, 4, w.H, w.D, dtype=base["q"].dtype, device=dev)
+            s = {}
+            for j, n in enumerate(("q", "k", "v", "dout")):
+                buf[:, :, j] = base[n].permute(0, 2, 1, 3)
+                s[n] = buf[:, :, j].permute(0, 2, 1, 3)
+            for n in ("dq", "dk", "dv"):
+                s[n] = torch.empty(w.B, w.N, w.H, w.D, dtype=base["q"].dtype, device=dev).permute(0, 2, 1, 3)
+        else:
+            s = {n: (t if i == 0 else t.clone()) for n, t in base.items()}
+            for n in ("dq", "dk", "dv"):
+                s[n] = torch.empty_like(base["q"])
         sets.append(s)
     chunk = w.chunk if w.mode == "block" else w.N
     rope = make_rope(la, w, dev, args.rope_form)
@@ -402,13 +416,23 @@ def backward_bench(w, args, dev, stream):
     P = ctypes.c_void_p
     rope_ref = None if rope is None else ctypes.byref(rope.struct())
     st_ptr = ctypes.c_void_p(stream.cuda_stream)
-    calls = [(P(s["q"].data_ptr()), P(s["k"].data_ptr()), P(s["v"].data_ptr()), P(s["dout"].data_ptr()),
-              P(s["dq"].data_ptr()), P(s["dk"].data_ptr()), P(s["dv"].data_ptr()), None, None, None, None, None,
-              None, w.B, w.H, w.N, chunk, w.D, dt, w.eps, rope_ref, P(ws.data_ptr()), ws.numel(), st_ptr)
-             for s in sets]
+    if packed:
+        lin = la.sana_layout(*sets[0]["q"].stride()[:3])
+        lout = la.sana_layout(*sets[0]["dq"].stride()[:3])
+        calls = [(P(s["q"].data_ptr()), P(s["k"].data_ptr()), P(s["v"].data_ptr()), P(s["dout"].data_ptr()),
+                  P(s["dq"].data_ptr()), P(s["dk"].data_ptr()), P(s["dv"].data_ptr()), ctypes.byref(lin),
+                  ctypes.byref(lout), None, None, None, None, None, None, w.B, w.H, w.N, chunk, w.D, dt, w.eps,
+                  rope_ref, P(ws.data_ptr()), ws.numel(), st_ptr) for s in sets]
+        entry = L.sana_linattn_backward_strided
+    else:
+        calls = [(P(s["q"].data_ptr()), P(s["k"].data_ptr()), P(s["v"].data_ptr()), P(s["dout"].data_ptr()),
+                  P(s["dq"].data_ptr()), P(s["dk"].data_ptr()), P(s["dv"].data_ptr()), None, None, None, None, None,
+                  None, w.B, w.H, w.N, chunk, w.D, dt, w.eps, rope_ref, P(ws.data_ptr()), ws.numel(), st_ptr)
+                 for s in sets]
+        entry = L.sana_linattn_backward
 
     def step(i):
-        rc = L.sana_linattn_backward(*calls[i % n_sets])
+        rc = entry(*calls[i % n_sets])
         if rc:
             raise la.SanaError(rc)
 
@@ -434,23 +458,26 @@ def backward_bench(w, args, dev, stream):
     g = torch.Generator(device="cpu").manual_seed(5)
     dkv = torch.randn(w.B, w.H, 32, 32, generator=g).to(dev)
     dksum = torch.randn(w.B, w.H, 32, generator=g).to(dev)
+    # (contiguous K, V, dK, dV: the key pass on its own takes no layout views)
+    key_sets = sets if not packed else [{"k": base["k"], "v": base["v"], "dk": torch.empty_like(base["k"]),
+                                         "dv": torch.empty_like(base["v"])}]
     key_calls = [(P(s["k"].data_ptr()), P(s["v"].data_ptr()), P(dkv.data_ptr()), P(dksum.data_ptr()),
                   P(s["dk"].data_ptr()), P(s["dv"].data_ptr()), w.B, w.H, w.N, w.D, dt, rope_ref, st_ptr)
-                 for s in sets]
+                 for s in key_sets]
     for i in range(args.warmup):
-        L.sana_linattn_state_update_backward(*key_calls[i % n_sets])
+        L.sana_linattn_state_update_backward(*key_calls[i % len(key_calls)])
     torch.cuda.synchronize()
     k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     k0.record(stream)
     for i in range(args.steps):
-        rc = L.sana_linattn_state_update_backward(*key_calls[i % n_sets])
+        rc = L.sana_linattn_state_update_backward(*key_calls[i % len(key_calls)])
         if rc:
             raise la.SanaError(rc)
     k1.record(stream)
     torch.cuda.synchronize()
     key_ms = k0.elapsed_time(k1) / args.steps
     key_bytes = w.token_heads * 4 * w.D * elem + w.B * w.H * (32 * 32 + 32) * 4
-    train = train_step_timing(w, args, sets, n_sets, chunk, rope_ref, dt, nb, dev, stream)
+    train = None if packed else train_step_timing(w, args, sets, n_sets, chunk, rope_ref, dt, nb, dev, stream)
 
     # fp32 multiply-adds per token-head of the backward: the forward state
     # recompute (S, z: 32*32 + 32), the query pass (num, den, S dnum, dS, dz:
@@ -471,7 +498,7 @@ def backward_bench(w, args, dev, stream):
         "data": "synthetic: seeded i.i.d. N(0,1)x0.5 bf16 tensors at the workload's latent shape (dO drawn after Q, K, V)",
         "config": {"workload": w.name, "pass": "backward", "B": w.B, "H": w.H, "N": w.N, "D": w.D,
                    "mode": w.mode, "chunk": chunk, "grid": w.grid, "input_sets_cycled": n_sets,
-                   "rope_form": args.rope_form if w.mode == "rope" else None},
+                   "layout": args.layout, "rope_form": args.rope_form if w.mode == "rope" else None},
         "roofline": {
             "bound": "hbm",
             "kernel": "bwd_key_bf16" if w.dtype == "bf16" else "bwd_key_vec",
@@ -484,7 +511,8 @@ def backward_bench(w, args, dev, stream):
             "avg_launch_ms": key_ms,
             "tokens_per_launch": w.token_heads,
         },
-        "call": {"entry_point": "sana_linattn_backward",
+        "call": {"entry_point": ("sana_linattn_backward_strided (packed [B,N,4,H,D] in, [B,N,H,D] out)" if packed
+                                 else "sana_linattn_backward"),
                  "kernels": "state pass + finalize + query pass + reverse finalize + key pass",
                  "avg_ms": ms, "algorithmic_bytes": alg_bytes,
                  "achieved_gbps": alg_bytes / (ms / 1e3) / 1e9,
@@ -577,9 +605,9 @@ def main():
                          "conv: the block-inference temporal conv; project: the key/value projection fused "
                          "with the state update (Sana-1.6B 4096 px layer, or video720p_rope3d with its RoPE)")
     ap.add_argument("--layout", choices=["bhnd", "packed"], default="bhnd",
-                    help="forward: bhnd = contiguous [B, H, N, D] (the default); packed = Q, K, V read as strided "
-                         "views of one [B, N, 3, H, D] projection-style buffer and O written to [B, N, H, D] "
-                         "(sana_linattn_forward_strided; non-causal and RoPE workloads)")
+                    help="bhnd = contiguous [B, H, N, D] (the default); packed = Q, K, V (and dO for the backward) "
+                         "read as strided views of one [B, N, 3 (4), H, D] projection-style buffer and O (dQ, dK, "
+                         "dV) written to [B, N, H, D] (the *_strided entry points; non-causal and RoPE workloads)")
     ap.add_argument("--rope-form", choices=["table", "axes"], default="axes",
                     help="RoPE workload: axes = the 3D RoPE's per-axis tables, staged in LDS by each workgroup (the "
                          "default); table = full [pos][16] cos/sin tables, streamed per head")
