@@ -23,7 +23,9 @@
 // Epilogue: the accumulator block of tokens 16i .. 16i + 15 holds, in lane
 // (n, g), tokens 4g + (0..3) of feature n -- the turned-around layout the
 // state pass builds with selection MFMAs -- so two row blocks pack straight
-// into the bf16 operands of S = phi(K)^T V and z = sum phi(K).
+// into the bf16 operands of S = phi(K)^T V and z = sum phi(K).  With RoPE,
+// phi(K) is rotated in fp32 first (the pair partner comes from the
+// neighbouring lane) and contracted as three bf16 parts; z stays unrotated.
 //
 // Blocks of the (token range, head pair) grid are dealt to the XCDs in
 // contiguous runs, and inside a run walk 4 token ranges per head pair: the
@@ -120,7 +122,7 @@ __device__ __forceinline__ void proj_angles(const Rope& r, const float* rtab, co
 // each (A: 256 token rows, B: 128 weight rows, 64 bytes a row): step k + 2 is
 // loaded while step k computes.  B row R of a stage is row R % 32 of head
 // h + R / 64's key (bit 5 of R clear) or value weights.  Two workgroups fit a
-// CU (VGPRs, 2 x 72 KB of LDS).
+// CU (VGPRs; 72 KB of LDS each, 80 KB with the per-axis RoPE tables).
 template <int ROPE>
 __global__ __launch_bounds__(kThreads, 2) void project_state_bf16(ProjArgs p, Rope rp, StateArgs a) {
   constexpr int kStage = (kProjTokens + 128) * 64;  // bytes per stage

@@ -18,5 +18,6 @@ from .linattn_oracle import (  # noqa: F401
     backward,
     temporal_conv3,
     round_bf16,
+    projected_apply,
     projected_kv_state,
 )

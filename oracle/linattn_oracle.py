@@ -378,3 +378,19 @@ def projected_kv_state(x, w_k, w_v, angles=None, pos_offset=0):
     k = round_bf16(np.matmul(x, np.asarray(w_k, dtype=np.float64)[None]))
     v = round_bf16(np.matmul(x, np.asarray(w_v, dtype=np.float64)[None]))
     return kv_state(k, v, angles, pos_offset)
+
+
+def projected_apply(x, w_q, S, z, eps, angles=None, pos_offset=0):
+    """Outputs of the queries a layer's projection produces, against a given
+    state.
+
+    x: [B, N, C] layer input; w_q: [H, C, D] per-head query weights; S
+    [B, H, D, D], z [B, H, D]: the state (for example projected_kv_state's).
+    Q[b, h] = x[b] W_q[h] (float64), rounded to bfloat16 as the projection
+    output is stored, then O = phi~(Q).S / (phi(Q).z + eps) as in apply_state
+    ([Video note] 2.1, 2.2; [Sana note] "Infra" for the fusion with the
+    matmul).  Returns O [B, H, N, D].
+    """
+    x = np.asarray(x, dtype=np.float64)[:, None]          # [B, 1, N, C]
+    q = round_bf16(np.matmul(x, np.asarray(w_q, dtype=np.float64)[None]))
+    return apply_state(q, np.asarray(S, dtype=np.float64), np.asarray(z, dtype=np.float64), eps, angles, pos_offset)

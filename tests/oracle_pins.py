@@ -519,3 +519,78 @@ def pin_projected_state(impl):
 
 
 ALL_PINS.append(pin_projected_state)
+
+
+def pin_projected_apply(impl):
+    """The projected queries' outputs against a brute force in rationals: the
+    query projection rounded by search, its ReLU, the numerator with explicit
+    2 x 2 rotations at offset positions and the unrotated denominator, each
+    output one rational division; identity weights reduce it to apply_state of
+    the input; a positive power-of-two scale of the input leaves O unchanged at
+    eps = 0."""
+    from fractions import Fraction
+    rng = np.random.default_rng(91)
+
+    def rb_fraction(f):
+        if f == 0:
+            return Fraction(0)
+        sign = 1 if f > 0 else -1
+        a, e = abs(f), 0
+        while a >= 2:
+            a /= 2
+            e += 1
+        while a < 1:
+            a *= 2
+            e -= 1
+        lo = Fraction(int(a * 128), 128)
+        hi = lo + Fraction(1, 128)
+        d_lo, d_hi = a - lo, hi - a
+        pick = lo if d_lo < d_hi else hi if d_hi < d_lo else (lo if (lo * 128) % 2 == 0 else hi)
+        return sign * pick * Fraction(2) ** e
+
+    B, H, N, C, D = 1, 2, 4, 5, 4
+    x = _bf16_by_bits(rng.standard_normal((B, N, C)).astype(np.float32))
+    wq = _bf16_by_bits(rng.standard_normal((H, C, D)).astype(np.float32))
+    S = rng.standard_normal((B, H, D, D))
+    z = rng.uniform(0.5, 2.0, (B, H, D))
+    angles = rng.uniform(-3.0, 3.0, (N + 2, D // 2))
+    eps = 1e-3
+    raw = np.matmul(x[:, None], wq[None])
+    assert np.any(raw != _bf16_by_bits(raw.astype(np.float32))), "the case must exercise the rounding"
+    for ang, off in ((None, 0), (angles, 2)):
+        O = impl.projected_apply(x, wq, S, z, eps, angles=ang, pos_offset=off)
+        assert O.shape == (B, H, N, D)
+        for h in range(H):
+            for n in range(N):
+                Q = [max(rb_fraction(sum(Fraction(x[0, n, c]) * Fraction(wq[h, c, d]) for c in range(C))), 0)
+                     for d in range(D)]
+                den = sum(Q[d] * Fraction(z[0, h, d]) for d in range(D)) + Fraction(eps)
+                if ang is None:
+                    R = Q
+                else:
+                    R = []
+                    for d in range(D):
+                        p = d // 2
+                        cs, sn = Fraction(np.cos(ang[n + off, p])), Fraction(np.sin(ang[n + off, p]))
+                        q0, q1 = Q[2 * p], Q[2 * p + 1]
+                        R.append(q0 * cs - q1 * sn if d % 2 == 0 else q0 * sn + q1 * cs)
+                for e in range(D):
+                    want = float(sum(R[d] * Fraction(S[0, h, d, e]) for d in range(D)) / den)
+                    assert abs(O[0, h, n, e] - want) <= 1e-12 * (1 + abs(want)), ("O", ang is None, h, n, e)
+    # identity weights: the projection is the input itself (bf16-exact)
+    xi = np.asarray(impl.round_bf16(rng.standard_normal((1, 6, 4))), dtype=np.float64)
+    eye = np.broadcast_to(np.eye(4), (2, 4, 4))
+    Si = rng.standard_normal((1, 2, 4, 4))
+    zi = rng.uniform(0.5, 2.0, (1, 2, 4))
+    got = impl.projected_apply(xi, eye, Si, zi, 1e-6)
+    want = impl.apply_state(np.broadcast_to(xi[:, None], (1, 2, 6, 4)), Si, zi, 1e-6)
+    assert np.array_equal(got, want)
+    # numerator and denominator are both linear in phi(Q): a power-of-two scale
+    # cancels exactly at eps = 0 (rows with phi(Q) = 0 are 0/0 in both)
+    O1 = impl.projected_apply(x, wq, S, z, 0.0)
+    O4 = impl.projected_apply(4.0 * x, wq, S, z, 0.0)
+    assert np.count_nonzero(np.isfinite(O1)) > O1.size // 2
+    assert np.array_equal(O1, O4, equal_nan=True)
+
+
+ALL_PINS.append(pin_projected_apply)

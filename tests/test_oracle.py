@@ -84,6 +84,10 @@ MUTANTS = {
                                    "return np.ldexp(np.floor(m * 256.0 + 0.5), e - 8)"),
     "proj_rotation_dropped": ("return kv_state(k, v, angles, pos_offset)", "return kv_state(k, v)"),
     "proj_positions_from_zero": ("return kv_state(k, v, angles, pos_offset)", "return kv_state(k, v, angles, 0)"),
+    "papply_rounding_dropped": ("q = round_bf16(np.matmul(x, np.asarray(w_q, dtype=np.float64)[None]))",
+                                "q = np.matmul(x, np.asarray(w_q, dtype=np.float64)[None])"),
+    "papply_rotation_dropped": ("np.asarray(z, dtype=np.float64), eps, angles, pos_offset)",
+                                "np.asarray(z, dtype=np.float64), eps)"),
     "proj_round_7_bits": ("return np.ldexp(np.rint(m * 256.0), e - 8)", "return np.ldexp(np.rint(m * 128.0), e - 7)"),
     "bwd_carried_state_ignored": ("S = np.zeros(lead + (D, D)) if S_in is None else np.asarray(S_in, dtype=np.float64)\n    z = np.zeros(lead + (D,)) if z_in is None else np.asarray(z_in, dtype=np.float64)\n    states = []",
                                   "S = np.zeros(lead + (D, D))\n    z = np.zeros(lead + (D,)) if z_in is None else np.asarray(z_in, dtype=np.float64)\n    states = []"),
