@@ -188,6 +188,24 @@ int sana_linattn_project_state(const void* x, const void* w_k, const void* w_v, 
  * is no work or the sizes are invalid).  Pure host function. */
 size_t sana_linattn_project_state_workspace_bytes(int B, int H, int64_t N, int C, int D, int dtype);
 
+/* The query projection and the apply step in one pass (the other half of the
+ * projection fusion the "Sana" research note lists under "Infra").  Per batch
+ * b and head h, with Q = x[b] W_q[h]^T rounded to bf16 as a bf16 projection
+ * would store it (never written to memory):
+ *   O_i = phi~(Q_i) . S / (phi(Q_i) . z + eps),  S = kv_state[b][h], z = ksum_state[b][h]
+ * exactly what sana_linattn_apply computes for that Q ("SANA-Video" paper
+ * notes 2.1, 2.2: RoPE, if any, in the numerator only, query i at position
+ * pos_offset + i).  x: [B][N][C] bf16; w_q: [H*D][C] bf16 (row h*D + d = query
+ * feature d of head h), both 16-byte aligned; o: bf16 outputs [B][H][N][D]
+ * through the view `out` (NULL: contiguous; e.g. [B][N][H][D]), overlapping
+ * no input; kv_state [B][H][D][D], ksum_state [B][H][D]: fp32, read only (for
+ * example from sana_linattn_project_state).  C a positive multiple of 32, at
+ * most 65536; only bf16 and D = 32 have kernels.  No workspace.  B*H*N = 0 is
+ * a no-op. */
+int sana_linattn_project_apply(const void* x, const void* w_q, void* o, const sana_layout* out,
+                               const float* kv_state, const float* ksum_state, int B, int H, int64_t N, int C,
+                               int D, int dtype, float eps, const sana_rope* rope, void* hip_stream);
+
 /* sana_linattn_forward with Q, K, V read through the view `in` and O written
  * through `out` (NULL: contiguous), e.g. straight from a [B][N][3][H][D] QKV
  * projection output, with no relayout copy.  Everything else as for

@@ -23,6 +23,7 @@ EXPORTED = (
     "sana_linattn_state_update",
     "sana_linattn_project_state",
     "sana_linattn_project_state_workspace_bytes",
+    "sana_linattn_project_apply",
     "sana_linattn_block_forward",
     "sana_linattn_block_forward_strided",
     "sana_linattn_block_causal",
@@ -75,6 +76,9 @@ def lib():
     L.sana_linattn_project_state.restype = i32
     L.sana_linattn_project_state_workspace_bytes.argtypes = [i32, i32, i64, i32, i32, i32]
     L.sana_linattn_project_state_workspace_bytes.restype = sz
+    L.sana_linattn_project_apply.argtypes = [vp, vp, vp, ctypes.POINTER(sana_layout), vp, vp, i32, i32, i64, i32,
+                                             i32, i32, f32, rp, vp]
+    L.sana_linattn_project_apply.restype = i32
     L.sana_linattn_block_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, f32,
                                              rp, vp, sz, vp]
     L.sana_linattn_block_forward.restype = i32
@@ -365,6 +369,37 @@ def sana_linattn_project_state(x, w_k, w_v, kv_state, ksum_state, rope=None, wor
                                             N, C, D, SANA_DT_BF16, _rope_arg(rope), _ptr(workspace),
                                             workspace.numel() * workspace.element_size(),
                                             _stream(stream, x.device)))
+
+
+def sana_linattn_project_apply(x, w_q, kv_state, ksum_state, o=None, eps=1e-6, rope=None, stream=None):
+    """O = phi~(Q).S / (phi(Q).z + eps) for Q = x W_q^T (per head, rounded to
+    bf16), without writing Q.  x: [B, N, C] bf16; w_q: [H * D, C] bf16;
+    states [B, H, D, D], [B, H, D] float32.  o: a [B, H, N, D] bf16 view
+    (allocated contiguous if not given), e.g. of a [B, N, H, D] buffer."""
+    torch = _torch()
+    if x.dim() != 3 or w_q.dim() != 2:
+        raise ValueError("x must be [B, N, C] and w_q [H * D, C]")
+    B, N, C = x.shape
+    if kv_state.dim() != 4 or tuple(ksum_state.shape) != tuple(kv_state.shape[:3]):
+        raise ValueError("kv_state must be [B, H, D, D] and ksum_state [B, H, D]")
+    H, D = kv_state.shape[1], kv_state.shape[3]
+    if tuple(kv_state.shape) != (B, H, D, D) or tuple(w_q.shape) != (H * D, C):
+        raise ValueError("states must be [B, H, D, D] with w_q [H * D, C]")
+    for name, t in (("x", x), ("w_q", w_q)):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be a contiguous bfloat16 device tensor")
+    for t in (kv_state, ksum_state):
+        if t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("states must be contiguous float32 device tensors")
+    if o is None:
+        o = torch.empty((B, H, N, D), dtype=torch.bfloat16, device=x.device)
+    elif _shape4(o, "o", strided=True) != (B, H, N, D) or o.dtype != torch.bfloat16:
+        raise ValueError("o must be a [B, H, N, D] bfloat16 view")
+    vout = _view(o)
+    _check(lib().sana_linattn_project_apply(_ptr(x), _ptr(w_q), _ptr(o), _lay(vout), _ptr(kv_state),
+                                            _ptr(ksum_state), B, H, N, C, D, SANA_DT_BF16, float(eps),
+                                            _rope_arg(rope), _stream(stream, x.device)))
+    return o
 
 
 def sana_linattn_block_forward(q, k, v, o=None, kv_in=None, ksum_in=None, kv_out=None, ksum_out=None,

@@ -116,20 +116,87 @@ __device__ __forceinline__ void proj_angles(const Rope& r, const float* rtab, co
   }
 }
 
+// The GEMM of one 256-token block: acc[i][j] (lane (n, g): tokens
+// 128 (w & 1) + 16 i + 4 g + (0..3), column 16 j + n of this wave's 64) over
+// all nk 32-channel steps.  Three LDS stages of one step each (A: 256 token
+// rows at 0, B: 128 weight rows at kProjBOff, 64 bytes a row); wave w's loads fill
+// A rows 64 w .. 64 w + 63 (a_voff: row offsets in x, rsrc rx) and B rows
+// 32 w .. 32 w + 31 (b_voff, rsrc rw); step k + 2 is loaded while step k
+// computes.  Step t computes on stage t % 3.  Its barrier waits for the step's
+// own loads (every wave's) to land and for step t - 1's reads to end
+// everywhere; then stage (t + 2) % 3 is free for step t + 2's loads.  Each
+// step issues six loads per wave, so with step t + 1's loads still in flight
+// the wait is vmcnt(6), and vmcnt(0) at the last step.  In the main loop the
+// stages are named, not indexed: the compiler then sees that the operand reads
+// and the loads in flight touch different LDS arrays and adds no wait of its
+// own (at the loop head, where it cannot tell the stages apart across the back
+// edge, and in the last steps it waits for every load; unrolling to six steps
+// an iteration measured no faster).  The caller has synchronised the
+// workgroup since the stages were last read.
+constexpr int kProjStage = (kProjTokens + 128) * 64;  // bytes per stage
+constexpr int kProjBOff = kProjTokens * 64;            // B rows after the A rows
+
+__device__ __forceinline__ void proj_gemm(rsrc_t rx, rsrc_t rw, const int (&a_voff)[4], const int (&b_voff)[2],
+                                          int a_rd, int b_rd, int nk, int w, char* st0, char* st1, char* st2,
+                                          f32x4_t (&acc)[8][4]) {
+  auto issue = [&](int k, char* stage) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lds_dma16(rx, stage + (64 * w + 16 * i) * 64, a_voff[i] + k * 64);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) lds_dma16(rw, stage + kProjBOff + (32 * w + 16 * i) * 64, b_voff[i] + k * 64);
+  };
+  auto compute = [&](const char* stage) {
+    bf16x8_t bf[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bf[j] = *reinterpret_cast<const bf16x8_t*>(stage + b_rd + j * 1024);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(stage + a_rd + i * 1024);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma16(af, bf[j], acc[i][j]);
+    }
+  };
+  issue(0, st0);
+  if (nk > 1) issue(1, st1);
+  // steps k .. k + 2 (stages 0, 1, 2), every one with loads to issue
+  auto three = [&](int k) {
+    proj_stage_barrier<6>();
+    issue(k + 2, st2);
+    compute(st0);
+    proj_stage_barrier<6>();
+    issue(k + 3, st0);
+    compute(st1);
+    proj_stage_barrier<6>();
+    issue(k + 4, st1);
+    compute(st2);
+  };
+  int k = 0;
+  for (; k + 5 <= nk; k += 3) three(k);
+  // the last 1 to 4 steps (k is a multiple of 3: step t is on stage t % 3)
+  for (; k < nk; ++k) {
+    const int sk = k % 3;
+    char* cur = sk == 0 ? st0 : (sk == 1 ? st1 : st2);
+    char* nxt = sk == 0 ? st2 : (sk == 1 ? st0 : st1);
+    if (k + 1 < nk)
+      proj_stage_barrier<6>();
+    else
+      proj_stage_barrier<0>();
+    if (k + 2 < nk) issue(k + 2, nxt);
+    compute(cur);
+  }
+}
+
 // One workgroup per (token range, head pair): 4 waves, wave w takes tokens
 // 128 (w & 1) .. +127 of each 256-token block and head h + (w >> 1) (64 output
-// columns: 8 x 4 MFMA blocks of 16 x 16).  Three LDS stages of one channel step
-// each (A: 256 token rows, B: 128 weight rows, 64 bytes a row): step k + 2 is
-// loaded while step k computes.  B row R of a stage is row R % 32 of head
-// h + R / 64's key (bit 5 of R clear) or value weights.  Two workgroups fit a
-// CU (VGPRs; 72 KB of LDS each, 80 KB with the per-axis RoPE tables).
+// columns: 8 x 4 MFMA blocks of 16 x 16) through proj_gemm.  B row R of a
+// stage is row R % 32 of head h + R / 64's key (bit 5 of R clear) or value
+// weights.  Two workgroups fit a CU (VGPRs; 72 KB of LDS each, 80 KB with the
+// per-axis RoPE tables).
 template <int ROPE>
 __global__ __launch_bounds__(kThreads, 2) void project_state_bf16(ProjArgs p, Rope rp, StateArgs a) {
-  constexpr int kStage = (kProjTokens + 128) * 64;  // bytes per stage
-  constexpr int kBOff = kProjTokens * 64;            // B rows after the A rows
-  __shared__ __attribute__((aligned(1024))) char st0[kStage];
-  __shared__ __attribute__((aligned(1024))) char st1[kStage];
-  __shared__ __attribute__((aligned(1024))) char st2[kStage];
+  __shared__ __attribute__((aligned(1024))) char st0[kProjStage];
+  __shared__ __attribute__((aligned(1024))) char st1[kProjStage];
+  __shared__ __attribute__((aligned(1024))) char st2[kProjStage];
   __shared__ __attribute__((aligned(16))) float rtab[ROPE == kRopeAxes ? 2 * kMaxAxisTab : 1];
 
   int64_t mi;
@@ -163,7 +230,7 @@ __global__ __launch_bounds__(kThreads, 2) void project_state_bf16(ProjArgs p, Ro
   // operand reads: lane (n, g) reads piece g of row base + n
   const int sw = 16 * (g ^ proj_swz(n));
   const int a_rd = (128 * th + n) * 64 + sw;
-  const int b_rd = kBOff + (64 * hh + n) * 64 + sw;
+  const int b_rd = kProjBOff + (64 * hh + n) * 64 + sw;
   // RoPE: the pair partner's sign, and where the per-axis entries of this
   // lane's pairs (features n and 16 + n) sit; the axis tables go to LDS (the
   // first block's barrier orders the copy before any lookup)
@@ -183,69 +250,13 @@ __global__ __launch_bounds__(kThreads, 2) void project_state_bf16(ProjArgs p, Ro
     const int64_t tok0 = blk * kProjTokens;
     // rows at or past N read as zero: their keys and values are 0 and add nothing
     const rsrc_t rx = make_rsrc(xb + tok0 * row, (p.N - tok0) * row);
-    auto issue = [&](int k, char* stage) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) lds_dma16(rx, stage + (64 * w + 16 * i) * 64, a_voff[i] + k * 64);
-#pragma unroll
-      for (int i = 0; i < 2; ++i) lds_dma16(rw, stage + kBOff + (32 * w + 16 * i) * 64, b_voff[i] + k * 64);
-    };
     f32x4_t acc[8][4];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = zero4;
-
-    auto compute = [&](const char* stage) {
-      bf16x8_t bf[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) bf[j] = *reinterpret_cast<const bf16x8_t*>(stage + b_rd + j * 1024);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(stage + a_rd + i * 1024);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16(af, bf[j], acc[i][j]);
-      }
-    };
-    // Step t computes on stage t % 3.  Its barrier waits for the step's own
-    // loads (every wave's) to land and for step t - 1's reads to end
-    // everywhere; then stage (t + 2) % 3 is free for step t + 2's loads.  Each
-    // step issues six loads per wave, so with step t + 1's loads still in
-    // flight the wait is vmcnt(6), and vmcnt(0) at the last step.  In the main
-    // loop the stages are named, not indexed: the compiler then sees that the
-    // operand reads and the loads in flight touch different LDS arrays and adds
-    // no wait of its own (in the last steps it waits for every load).
     __syncthreads();  // every wave is done with the previous block's stages
-    issue(0, st0);
-    if (nk > 1) issue(1, st1);
-    // steps k .. k + 2 (stages 0, 1, 2), every one with loads to issue
-    auto three = [&](int k) {
-      proj_stage_barrier<6>();
-      issue(k + 2, st2);
-      compute(st0);
-      proj_stage_barrier<6>();
-      issue(k + 3, st0);
-      compute(st1);
-      proj_stage_barrier<6>();
-      issue(k + 4, st1);
-      compute(st2);
-    };
-    // (the compiler adds a wait for every load at the loop head, where it
-    // cannot tell the stages apart across the back edge; unrolling to six
-    // steps an iteration measured no faster)
-    int k = 0;
-    for (; k + 5 <= nk; k += 3) three(k);
-    // the last 1 to 4 steps (k is a multiple of 3: step t is on stage t % 3)
-    for (; k < nk; ++k) {
-      const int sk = k % 3;
-      char* cur = sk == 0 ? st0 : (sk == 1 ? st1 : st2);
-      char* nxt = sk == 0 ? st2 : (sk == 1 ? st0 : st1);
-      if (k + 1 < nk)
-        proj_stage_barrier<6>();
-      else
-        proj_stage_barrier<0>();
-      if (k + 2 < nk) issue(k + 2, nxt);
-      compute(cur);
-    }
+    proj_gemm(rx, rw, a_voff, b_voff, a_rd, b_rd, nk, w, st0, st1, st2, acc);
 
     // acc[i][j], lane (n, g): tokens 128 th + 16 i + 4 g + (0..3) of the
     // block, column 16 j + n of head h + hh (j = 0, 1: key features; 2, 3:
@@ -335,6 +346,180 @@ __global__ __launch_bounds__(kThreads, 2) void project_state_bf16(ProjArgs p, Ro
   __syncthreads();
   write_partial(red[0], bh, 0, r, a);
   if (heads_here == 2) write_partial(red[1], bh + 1, 0, r, a);
+}
+
+// ---------------------------------------------------------------------------
+// Query projection fused with the apply pass
+// ---------------------------------------------------------------------------
+//
+// Q = x W_q^T through the same GEMM (four heads of 32 query features per
+// workgroup: wave w takes tokens 128 (w & 1) .. +127 and heads h + 2 (w >> 1)
+// and h + 2 (w >> 1) + 1), rounded to bf16 as a bf16 projection would store
+// it, and applied to the heads' states in the epilogue, so Q never reaches
+// memory: O = phi~(Q).S / (phi(Q).z + eps).  The apply pass takes phi(Q) as an
+// MFMA B operand with a token in each column; the GEMM leaves it turned
+// around (a feature in each lane), so a selection MFMA turns each pair of
+// 16-token blocks back, exactly (bf16 values times 1.0), with a lane's k-slots
+// s holding features 4g + s (s < 4) and 16 + 4g + s - 4 (s >= 4); the S and z
+// operands are loaded in that order, and apply_tile does the rest.
+
+struct ProjApplyArgs {
+  const char* x;     // [B][N][C] bf16
+  const char* wq;    // [H * 32][C] bf16: row h * 32 + d = query feature d of head h
+  char* o;           // outputs, bf16, through lo
+  Layout lo;
+  const float* kv;   // states [B * H][32][32] fp32
+  const float* ks;   // [B * H][32] fp32
+  int64_t N;
+  int C;
+  int H;
+  int Hq;            // head quads, ceil(H / 4)
+  int64_t R;         // 256-token blocks per batch
+  int64_t M;         // B * R
+  float eps;
+};
+
+// B operand that picks, from a turned-around pair of 16-token blocks (k-slot
+// s of lane g: token 4g + s % 4 of block s / 4), block bb's tokens in natural
+// order: slot s of lane (n, g) is 1.0 where s / 4 == bb and 4g + s % 4 == n.
+__device__ __forceinline__ bf16x8_t untangle_select(int g, int n, int bb) {
+  unsigned d[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int s0 = 2 * q, s1 = 2 * q + 1;
+    const bool h0 = (s0 >> 2) == bb && 4 * g + (s0 & 3) == n;
+    const bool h1 = (s1 >> 2) == bb && 4 * g + (s1 & 3) == n;
+    d[q] = (h0 ? 0x3f80u : 0u) | (h1 ? 0x3f800000u : 0u);
+  }
+  return as_bf16x8(d[0], d[1], d[2], d[3]);
+}
+
+// apply_tile's S^T and z operands (see load_apply_operands) for B operands
+// whose k-slot s holds feature 4g + s (s < 4) or 16 + 4g + s - 4 (s >= 4).
+__device__ __forceinline__ void proj_apply_operands(const float* S, const float* z, int g, int m,
+                                                    ApplyOperands& op) {
+  auto feat = [&](int s) { return s < 4 ? 4 * g + s : 12 + 4 * g + s; };
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    const int e = 8 * (m >> 2) + 4 * hf + (m & 3);
+    unsigned part[3][4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      split3_bf16x2(S[feat(2 * q) * 32 + e], S[feat(2 * q + 1) * 32 + e], part[0][q], part[1][q], part[2][q]);
+#pragma unroll
+    for (int k = 0; k < 3; ++k) op.s[hf][k] = as_bf16x8(part[k][0], part[k][1], part[k][2], part[k][3]);
+  }
+  unsigned part[3][4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    split3_bf16x2(z[feat(2 * q)], z[feat(2 * q + 1)], part[0][q], part[1][q], part[2][q]);
+#pragma unroll
+  for (int k = 0; k < 3; ++k) op.z[k] = as_bf16x8(part[k][0], part[k][1], part[k][2], part[k][3]);
+}
+
+// One workgroup per (256-token block, head quad).
+template <int ROPE>
+__global__ __launch_bounds__(kThreads, 2) void project_apply_bf16(ProjApplyArgs p, Rope rp) {
+  __shared__ __attribute__((aligned(1024))) char st0[kProjStage];
+  __shared__ __attribute__((aligned(1024))) char st1[kProjStage];
+  __shared__ __attribute__((aligned(1024))) char st2[kProjStage];
+  __shared__ __attribute__((aligned(16))) float rtab[ROPE == kRopeAxes ? 2 * kMaxAxisTab : 1];
+
+  int64_t mi;
+  int pi;
+  proj_block(blockIdx.x, gridDim.x, p.M, p.Hq, &mi, &pi);
+  const int64_t b = mi / p.R;
+  const int64_t tok0 = (mi % p.R) * kProjTokens;
+  const int h = 4 * pi;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15;
+  const int g = lane >> 4;
+  const int th = w & 1, hh = w >> 1;
+  const int row = p.C * 2;
+
+  const int dr = lane >> 2;
+  const int dpiece = ((lane & 3) ^ proj_swz(dr)) * 16;
+  int a_voff[4], b_voff[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a_voff[i] = (64 * w + 16 * i + dr) * row + dpiece;
+  // wave w stages B rows 32 w .. 32 w + 31: the query weights of head h + w
+#pragma unroll
+  for (int i = 0; i < 2; ++i) b_voff[i] = (32 * w + 16 * i + dr) * row + dpiece;
+  const int heads_here = p.H - h < 4 ? p.H - h : 4;
+  const rsrc_t rw = make_rsrc(p.wq + (int64_t)h * 32 * row, (int64_t)heads_here * 32 * row);
+  // rows at or past N read as zero; their outputs are not stored
+  const rsrc_t rx = make_rsrc(p.x + (b * p.N + tok0) * (int64_t)row, (p.N - tok0) * row);
+  const int sw = 16 * (g ^ proj_swz(n));
+  const int a_rd = (128 * th + n) * 64 + sw;
+  const int b_rd = kProjBOff + (64 * hh + n) * 64 + sw;
+  // RoPE: this lane's pairs are 2g, 2g + 1, 8 + 2g, 9 + 2g (its k-slot pairs)
+  const AxisPair ap[4] = {axis_pair(rp, 2 * g), axis_pair(rp, 2 * g + 1), axis_pair(rp, 8 + 2 * g),
+                          axis_pair(rp, 9 + 2 * g)};
+  rope_stage<ROPE>(rp, rtab, tid, kThreads);
+
+  const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+  f32x4_t acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = zero4;
+  __syncthreads();  // the RoPE tables are staged
+  proj_gemm(rx, rw, a_voff, b_voff, a_rd, b_rd, p.C / 32, w, st0, st1, st2, acc);
+
+  // acc[i][2u + fh], lane (n, g): tokens 128 th + 16 i + 4 g + (0..3),
+  // feature 16 fh + n of head h + 2 hh + u
+  const bf16x8_t sel[2] = {untangle_select(g, n, 0), untangle_select(g, n, 1)};
+  const int64_t tw0 = tok0 + 128 * th;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int hu = h + 2 * hh + u;
+    if (hu >= p.H) break;
+    const int64_t bh = b * p.H + hu;
+    ApplyOperands op;
+    proj_apply_operands(p.kv + bh * 1024, p.ks + bh * 32, g, n, op);
+    const int64_t orow = p.lo.token * 2;
+    const rsrc_t ro = rows_rsrc(p.o + p.lo.base(bh) * 2, tw0, p.N, orow);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      bf16x8_t A[2];
+#pragma unroll
+      for (int fh = 0; fh < 2; ++fh)
+        A[fh] = __builtin_bit_cast(bf16x8_t, relu_bf16x8(__builtin_bit_cast(
+                                                 u32x4_t, pack_turned(acc[2 * t][2 * u + fh], acc[2 * t + 1][2 * u + fh]))));
+#pragma unroll
+      for (int bb = 0; bb < 2; ++bb) {
+        const f32x4_t d0 = mfma16(A[0], sel[bb], zero4), d1 = mfma16(A[1], sel[bb], zero4);
+        const u32x4_t q = {pack_bf16x2(d0[0], d0[1]), pack_bf16x2(d0[2], d0[3]), pack_bf16x2(d1[0], d1[1]),
+                           pack_bf16x2(d1[2], d1[3])};
+        const int tr = 16 * (2 * t + bb) + n;  // this lane's token row in the wave's 128
+        f32x4_t c = zero4, sn = zero4;
+        if constexpr (ROPE != kRopeNone) {
+          const int64_t tok = tw0 + tr < p.N ? tw0 + tr : p.N - 1;
+          const int64_t pos = rp.pos0 + tok;
+          if constexpr (ROPE == kRopeAxes) {
+            int ct, chh, cw;
+            rope_coords(rp, pos, ct, chh, cw);
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+              const float2 e = *reinterpret_cast<const float2*>(rtab + 2 * axis_entry(ap[q4], ct, chh, cw));
+              c[q4] = e.x;
+              sn[q4] = e.y;
+            }
+          } else {
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+              const int pq = (q4 < 2 ? 2 * g : 6 + 2 * g) + q4;
+              c[q4] = rp.cos[pos * 16 + pq];
+              sn[q4] = rp.sin[pos * 16 + pq];
+            }
+          }
+        }
+        store16_nt(ro, tr * (int)orow + 16 * g, apply_tile<ROPE != kRopeNone>(q, op, p.eps, c, sn));
+      }
+    }
+  }
 }
 
 }  // namespace la

@@ -911,6 +911,52 @@ int sana_linattn_project_state(const void* x, const void* w_k, const void* w_v, 
   return launch_status();
 }
 
+int sana_linattn_project_apply(const void* x, const void* w_q, void* o, const sana_layout* out,
+                               const float* kv_state, const float* ksum_state, int B, int H, int64_t N, int C, int D,
+                               int dtype, float eps, const sana_rope* rope, void* hip_stream) {
+  ProjGeometry pg;
+  int rc = make_proj_geometry(B, H, N, C, D, dtype, &pg);
+  if (rc != SANA_OK) return rc;
+  if (!std::isfinite(eps) || eps < 0.f) return SANA_ERR_INVALID;
+  if (pg.BH == 0 || N == 0) return SANA_OK;
+  if (check_tensor(x) || check_tensor(w_q) || check_tensor(o)) return SANA_ERR_INVALID;
+  if (!kv_state || !ksum_state || !aligned(kv_state, 4) || !aligned(ksum_state, 4)) return SANA_ERR_INVALID;
+  View vout;
+  if ((rc = make_view(out, B, H, N, D, 2, true, &vout)) != SANA_OK) return rc;
+  const size_t x_bytes = (size_t)B * N * C * 2, w_bytes = (size_t)H * la::kD * C * 2;
+  const size_t kv_bytes = (size_t)pg.BH * 1024 * sizeof(float), ks_bytes = (size_t)pg.BH * 32 * sizeof(float);
+  const void* ins[4] = {x, w_q, kv_state, ksum_state};
+  const size_t in_bytes[4] = {x_bytes, w_bytes, kv_bytes, ks_bytes};
+  for (int i = 0; i < 4; ++i)
+    if (overlaps(o, vout.span, ins[i], in_bytes[i])) return SANA_ERR_INVALID;
+  if ((rc = check_rope(rope, N)) != SANA_OK) return rc;
+  const int64_t nblk = ceil_div(N, la::kProjTokens);
+  const int64_t groups = (int64_t)B * nblk * ceil_div(H, 4);
+  if (groups > kMaxGroups) return SANA_ERR_INVALID;
+
+  la::ProjApplyArgs p;
+  p.x = static_cast<const char*>(x);
+  p.wq = static_cast<const char*>(w_q);
+  p.o = static_cast<char*>(o);
+  p.lo = vout.lay;
+  p.kv = kv_state;
+  p.ks = ksum_state;
+  p.N = N;
+  p.C = C;
+  p.H = H;
+  p.Hq = (int)ceil_div(H, 4);
+  p.R = nblk;
+  p.M = (int64_t)B * nblk;
+  p.eps = eps;
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  const RopeArg ra = rope_arg(rope, N);
+  with_rope(ra.kind, [&](auto R) {
+    constexpr int RO = decltype(R)::value;
+    la::project_apply_bf16<RO><<<dim3((unsigned)groups), dim3(la::kThreads), 0, st>>>(p, ra.r);
+  });
+  return launch_status();
+}
+
 const char* sana_linattn_status_string(int status) {
   switch (status) {
     case SANA_OK: return "SANA_OK";

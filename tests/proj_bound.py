@@ -28,7 +28,7 @@ unknown summation order (the unfused path) gets delta = 2 C 2^-24 instead."""
 import numpy as np
 
 import oracle
-from metrics import rel_l2
+from metrics import BF16_MAX_REL, BF16_REL_L2, FLOOR, rel_l2
 
 REL_L2 = 1e-3
 U = 2.0 ** -24
@@ -38,6 +38,19 @@ def oracle_weights(w, H, D=32):
     """[H*D, C] rows (a linear layer's weight) -> the oracle's [H, C, D]."""
     C = w.shape[1]
     return np.ascontiguousarray(w.reshape(H, D, C).transpose(0, 2, 1))
+
+
+def _spread(x, w, any_order=False):
+    """bf16(x w) for x [B, N, C] and w [H', C, 32], and the width b of its
+    rounding interval: the fp32 sum lies within delta of the exact value, so
+    the kernel's bf16 value lies between round(exact - delta) and
+    round(exact + delta)."""
+    C = x.shape[-1]
+    exact = np.matmul(x[:, None], w[None])                     # [B, H', N, 32]
+    steps = C if any_order else C / 32 + 32
+    delta = 2.0 * steps * U * np.matmul(np.abs(x)[:, None], np.abs(w)[None])
+    lo, hi = oracle.round_bf16(exact - delta), oracle.round_bf16(exact + delta)
+    return oracle.round_bf16(exact), hi - lo, lo, hi
 
 
 def check_projected_state(kv, z, x, heads=None, kv0=None, z0=None, any_order=False, angles=None, pos_offset=0):
@@ -53,15 +66,11 @@ def check_projected_state(kv, z, x, heads=None, kv0=None, z0=None, any_order=Fal
     S, zr = oracle.projected_kv_state(x.f64["x"], wk, wv, angles, pos_offset)
     if kv0 is not None:
         S, zr = S + kv0, zr + z0
-    xa = np.abs(x.f64["x"])[:, None]                           # [B, 1, N, C]
-    C, N = p.C, p.N
+    N = p.N
 
     def spread(w):
-        exact = np.matmul(x.f64["x"][:, None], w[None])        # [B, H', N, 32]
-        steps = C if any_order else C / 32 + 32
-        delta = 2.0 * steps * U * np.matmul(xa, np.abs(w)[None])
-        lo, hi = oracle.round_bf16(exact - delta), oracle.round_bf16(exact + delta)
-        return oracle.round_bf16(exact), hi - lo
+        q, b, _lo, _hi = _spread(x.f64["x"], w, any_order)
+        return q, b
 
     K, bK = spread(wk)
     V, bV = spread(wv)
@@ -95,3 +104,50 @@ def check_projected_state(kv, z, x, heads=None, kv0=None, z0=None, any_order=Fal
         if not np.all(err <= tol):
             return False, lines[-1] + ": error above the derived bound"
     return True, "\n".join(lines)
+
+
+def check_projected_apply(o, x, S, z, eps, heads=None, angles=None, pos_offset=0, any_order=False):
+    """o (float64 [B, H', N, 32], the chosen heads of the ProjectionInputs x,
+    with w_q) against the oracle's projected_apply with states S, z.
+
+    The output is o_e = sum_d y_d S_de / (sum_d p_d z_d + eps), p = phi(Q), y
+    = p or its RoPE rotation R p.  Where a feature of Q is next to a bf16
+    rounding boundary (the interval of _spread), the kernel may hold the other
+    neighbour: p_f moves by at most b_f = relu(hi_f) - relu(lo_f) (one bf16
+    step, or less across zero), and o_e by b_f |d o_e / d p_f| <= b_f (|S_fe|
+    (+ |S_f'e|, f' = f ^ 1, under the rotation) + |o_e| z_f) / den, to first
+    order; the factor 1.5 covers the second-order term (b_f / p_f <= 2^-7).
+    Elsewhere the bf16 bar holds: |err_e| <= 2e-2 max(|o_e|, 1e-3 rms(o)),
+    plus the ambiguity term; the rel-L2 over the whole output stays <= 4e-3.
+    any_order: Q's sums were taken in an unknown order.  Returns (ok, report)."""
+    p = x.workload
+    wq = oracle_weights(x.f64["w_q"], p.H)
+    S = np.asarray(S, dtype=np.float64)
+    z = np.asarray(z, dtype=np.float64)
+    if heads is not None:
+        wq, S, z = wq[heads], S[:, heads], z[:, heads]
+    want = oracle.projected_apply(x.f64["x"], wq, S, z, eps, angles, pos_offset)
+    Q, _b, lo, hi = _spread(x.f64["x"], wq, any_order)
+    bp = np.maximum(hi, 0.0) - np.maximum(lo, 0.0)               # [B, H', N, 32]
+    den = np.matmul(np.maximum(Q, 0.0), z[..., :, None]) + eps  # [B, H', N, 1]
+    Sa = np.abs(S)
+    if angles is not None:
+        Sa = Sa + Sa[..., np.arange(Sa.shape[-2]) ^ 1, :]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        amb = 1.5 * (np.matmul(bp, Sa) + np.abs(want) * np.matmul(bp, z[..., :, None])) / den
+    amb = np.where(np.isfinite(amb), amb, np.inf)
+    o = np.asarray(o, dtype=np.float64)
+    rms = float(np.sqrt(np.mean(want * want))) if want.size else 0.0
+    tol = BF16_MAX_REL * np.maximum(np.abs(want), FLOOR * rms) + amb
+    err = np.abs(o - want)
+    l2 = rel_l2(o, want)
+    worst = float(np.max(err / np.maximum(tol, 1e-300))) if err.size else 0.0
+    report = (f"rel-L2 {l2:.3e}, max |err| / bound {worst:.3e} ({int(np.count_nonzero(bp))} of {bp.size} "
+              f"query features next to a rounding boundary)")
+    if not np.all(np.isfinite(o)):
+        return False, report + ": non-finite output"
+    if l2 > BF16_REL_L2:
+        return False, report + ": rel-L2 above 4e-3"
+    if not np.all(err <= tol):
+        return False, report + ": error above the bound"
+    return True, report

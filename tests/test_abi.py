@@ -192,6 +192,54 @@ def test_binding_project_state_checks():
         la.sana_linattn_project_state(x, w, w, kv[:, :1], z[:, :1])     # H * D != weight rows
 
 
+def test_project_apply_argument_errors():
+    L = la.lib()
+    E = la
+    def pa(x=A, wq=Bp, o=WS, lay=None, kv=Dp, ks=Dp + 8192, B=1, H=2, N=1000, Cin=64, D=32,
+           dt=la.SANA_DT_BF16, eps=1e-6, rope=None):
+        return L.sana_linattn_project_apply(x, wq, o, lay, kv, ks, B, H, N, Cin, D, dt, eps, rope, None)
+
+    assert pa(x=None) == E.SANA_ERR_INVALID
+    assert pa(wq=None) == E.SANA_ERR_INVALID
+    assert pa(o=None) == E.SANA_ERR_INVALID
+    assert pa(kv=None) == E.SANA_ERR_INVALID
+    assert pa(ks=Dp + 2) == E.SANA_ERR_INVALID             # misaligned state
+    assert pa(wq=Bp + 8) == E.SANA_ERR_INVALID             # misaligned weights
+    assert pa(o=A + 4096) == E.SANA_ERR_INVALID            # output inside x
+    assert pa(o=Bp + 64) == E.SANA_ERR_INVALID             # output inside w_q
+    assert pa(o=Dp - 64) == E.SANA_ERR_INVALID             # output runs into kv
+    assert pa(Cin=48) == E.SANA_ERR_INVALID                # not a multiple of 32
+    assert pa(Cin=0) == E.SANA_ERR_INVALID
+    assert pa(B=-1) == E.SANA_ERR_INVALID
+    assert pa(N=-1) == E.SANA_ERR_INVALID
+    assert pa(eps=-1.0) == E.SANA_ERR_INVALID
+    assert pa(eps=float("nan")) == E.SANA_ERR_INVALID
+    assert pa(D=64) == E.SANA_ERR_UNSUPPORTED
+    assert pa(dt=la.SANA_DT_F32) == E.SANA_ERR_UNSUPPORTED
+    assert pa(lay=ctypes.byref(la.sana_layout(1000 * 2 * 32, 32, 16))) == E.SANA_ERR_INVALID   # token stride < D
+    r = sana_rope(0x60000000, 0x70000000, 999, 0)          # tables shorter than N
+    assert pa(rope=ctypes.byref(r)) == E.SANA_ERR_INVALID
+    # no tokens or no heads: nothing is touched
+    assert pa(x=None, wq=None, o=None, kv=None, ks=None, N=0) == E.SANA_OK
+    assert pa(x=None, wq=None, o=None, kv=None, ks=None, B=0) == E.SANA_OK
+
+
+def test_binding_project_apply_checks():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(1, 64, 64, dtype=torch.bfloat16)
+    w = torch.zeros(64, 64, dtype=torch.bfloat16)
+    kv = torch.zeros(1, 2, 32, 32)
+    z = torch.zeros(1, 2, 32)
+    with pytest.raises(ValueError):
+        la.sana_linattn_project_apply(x, w, kv, z)                      # host tensors
+    with pytest.raises(ValueError):
+        la.sana_linattn_project_apply(x[0], w, kv, z)                   # x must be [B, N, C]
+    with pytest.raises(ValueError):
+        la.sana_linattn_project_apply(x, w, kv[:, :1], z[:, :1])        # H * D != weight rows
+    with pytest.raises(ValueError):
+        la.sana_linattn_project_apply(x, w, kv, z[:, :, :16])           # ksum shape
+
+
 def test_block_forward_argument_errors():
     L = la.lib()
     n = la.workspace_bytes(1, 2, 64)

@@ -4,12 +4,14 @@ V = x W_v^T rounded to bf16, then S = sum phi(K)^T V, z = sum phi(K)).
 
 The tolerance is the element-wise bound derived in proj_bound.py."""
 
+import numpy as np
 import pytest
 
 import linear_attention_diffusion_amd as la
 import oracle
 from gpu_util import device, to_dev, to_np, torch_mod
-from proj_bound import check_projected_state
+from metrics import BF16_REL_L2, rel_l2
+from proj_bound import check_projected_apply, check_projected_state, oracle_weights
 from workloads import PROJECTIONS, generate_projection, reduced
 
 pytestmark = pytest.mark.gpu
@@ -134,3 +136,101 @@ def test_full_720p_layer_rope_sampled_heads():
     kv, z = _run(x, rope=la.rope3d_axes_device(*grid, device()))
     heads = [0, 1, 36, 69]
     _check_state(to_np(kv)[:, heads], to_np(z)[:, heads], x, heads, angles=oracle.rope3d_angles(*grid))
+
+
+# ---------------------------------------------------------------------------
+# query projection fused with the apply step
+# ---------------------------------------------------------------------------
+
+def _state_for(p, seed):
+    """A realistic state for the apply: the oracle's state of another draw of
+    K and V (unit variance, N tokens), rounded to fp32 (the values both sides
+    use)."""
+    rng = np.random.default_rng(seed)
+    k = oracle.round_bf16(rng.standard_normal((p.B, p.H, p.N or 1, 32)))
+    v = oracle.round_bf16(rng.standard_normal((p.B, p.H, p.N or 1, 32)))
+    S, z = oracle.kv_state(k, v)
+    return S.astype(np.float32), z.astype(np.float32)
+
+
+def _run_apply(x, S, z, eps=1e-6, rope=None, o=None):
+    torch = torch_mod()
+    xs, wq = to_dev(x.raw["x"], "bf16"), to_dev(x.raw["w_q"], "bf16")
+    return la.sana_linattn_project_apply(xs, wq, torch.from_numpy(S).to(device()), torch.from_numpy(z).to(device()),
+                                         o=o, eps=eps, rope=rope)
+
+
+def _check_apply(*args, **kw):
+    ok, report = check_projected_apply(*args, **kw)
+    print(report, flush=True)
+    assert ok, report
+
+
+@pytest.mark.parametrize("B,N,C,H", [(1, 256, 32, 4), (2, 700, 96, 3), (1, 1000, 64, 6), (1, 5000, 128, 5)])
+def test_project_apply_matches_oracle(B, N, C, H):
+    print(f"case project_apply B={B} N={N} C={C} H={H}", flush=True)
+    x = generate_projection(reduced(FULL, B=B, N=N, C=C, H=H, seed=N + C + 1), names=("x", "w_q"))
+    S, z = _state_for(x.workload, 7)
+    o = _run_apply(x, S, z)
+    _check_apply(to_np(o), x, S, z, 1e-6)
+
+
+@pytest.mark.parametrize("grid,offset", [((3, 8, 20), 0), ((4, 10, 12), 150)])
+def test_project_apply_rope_and_strided_output(grid, offset):
+    """Queries rotated by the 3D RoPE (both table forms, bit-identical), and
+    outputs written straight into a [B, N, H, D] buffer."""
+    torch = torch_mod()
+    N = 480 - offset if offset else 480
+    x = generate_projection(reduced(FULL, B=2, N=N, C=64, H=6, seed=17), names=("x", "w_q"))
+    S, z = _state_for(x.workload, 8)
+    table = la.rope3d_device(*grid, device()).at(offset)
+    axes = la.rope3d_axes_device(*grid, device()).at(offset)
+    print(f"case project_apply rope grid={grid} offset={offset}", flush=True)
+    o_t = _run_apply(x, S, z, rope=table)
+    o_bnhd = torch.empty(2, N, 6, 32, dtype=torch.bfloat16, device=device()).permute(0, 2, 1, 3)
+    o_a = _run_apply(x, S, z, rope=axes, o=o_bnhd)
+    assert bool((o_a.contiguous().view(torch.int16) == o_t.view(torch.int16)).all()), "forms or layouts differ"
+    _check_apply(to_np(o_a), x, S, z, 1e-6, angles=oracle.rope3d_angles(*grid), pos_offset=offset)
+
+
+def test_project_apply_full_4096px_sampled_heads():
+    """The Sana-1.6B 4096 px layer's queries (16384 tokens, C = 2240, 70 heads)
+    in the launch configuration the benchmark times; the oracle computes five
+    heads, including the last, partial head quad."""
+    x = generate_projection(FULL, names=("x", "w_q"))
+    S, z = _state_for(reduced(FULL, N=4096), 9)
+    print("case project_apply full 4096 px", flush=True)
+    o = _run_apply(x, S, z)
+    heads = [0, 3, 35, 68, 69]
+    _check_apply(to_np(o)[:, heads], x, S, z, 1e-6, heads=heads)
+
+
+def test_projected_layer_end_to_end():
+    """project_state then project_apply: the whole attention of a layer from
+    its input x.  The state is checked within its bound, the output within the
+    apply's bound given that state, and both the fused and the unfused path
+    (torch GEMMs + forward) against the oracle's attention of the
+    bf16-rounded projections by rel-L2."""
+    torch = torch_mod()
+    p = reduced(FULL, B=2, N=1500, C=128, H=4, seed=23)
+    x = generate_projection(p, names=("x", "w_k", "w_v", "w_q"))
+    print("case projected layer end to end", flush=True)
+    xs, wk, wv, wq = (to_dev(x.raw[n], "bf16") for n in ("x", "w_k", "w_v", "w_q"))
+    kv = torch.zeros(p.B, p.H, 32, 32, device=device())
+    z = torch.zeros(p.B, p.H, 32, device=device())
+    la.sana_linattn_project_state(xs, wk, wv, kv, z)
+    o = la.sana_linattn_project_apply(xs, wq, kv, z)
+    _check_state(to_np(kv), to_np(z), x)
+    _check_apply(to_np(o), x, to_np(kv), to_np(z), 1e-6)
+    f = x.f64
+    proj = [oracle.round_bf16(np.matmul(f["x"][:, None], oracle_weights(f[n], p.H)[None]))
+            for n in ("w_q", "w_k", "w_v")]
+    want = oracle.linattn(*proj, 1e-6)
+    x2 = xs.reshape(p.B * p.N, p.C)
+    q, k, v = ((x2 @ w.t().contiguous()).reshape(p.B, p.N, p.H, 32).permute(0, 2, 1, 3).contiguous()
+               for w in (wq, wk, wv))
+    unfused = la.sana_linattn_forward(q, k, v)
+    for name, got in (("fused", o), ("unfused", unfused)):
+        l2 = rel_l2(to_np(got), want)
+        print(f"{name} layer: rel-L2 {l2:.3e} against the oracle", flush=True)
+        assert l2 <= BF16_REL_L2, name

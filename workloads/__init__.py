@@ -139,8 +139,8 @@ def generate(w: Workload, seed: Optional[int] = None, with_f64: bool = True,
 
 @dataclass(frozen=True)
 class ProjectionWorkload:
-    """Input activations x [B, N, C] and the key and value weights [H*D, C] of
-    one layer (the row layout of a linear layer's weight: row h*D + d is output
+    """Input activations x [B, N, C] and the key, value and query weights
+    [H*D, C] of one layer (the row layout of a linear layer's weight: row h*D + d is output
     feature d of head h)."""
     name: str
     B: int
@@ -165,23 +165,28 @@ PROJECTIONS = {
 @dataclass
 class ProjectionInputs:
     workload: ProjectionWorkload
-    raw: dict      # uint16 bf16 bit patterns: "x" [B, N, C], "w_k", "w_v" [H*D, C]
+    raw: dict      # uint16 bf16 bit patterns: "x" [B, N, C], "w_k", "w_v", "w_q" [H*D, C]
     f64: dict      # their exact float64 values
 
 
-def generate_projection(p: ProjectionWorkload, seed: Optional[int] = None, with_f64: bool = True):
+def generate_projection(p: ProjectionWorkload, seed: Optional[int] = None, with_f64: bool = True,
+                        names=("x", "w_k", "w_v")):
     """Recipe: numpy.random.default_rng(seed) (PCG64); float32 standard_normal
-    drawn in the order x [B, N, C], w_k [H*D, C], w_v [H*D, C]; the weights are
-    multiplied by float32(1 / sqrt(C)) (unit-variance keys and values); all
+    drawn in the order x [B, N, C], w_k [H*D, C], w_v [H*D, C], w_q [H*D, C]
+    (drawn up to the last of `names`, kept for those in `names`); the weights
+    are multiplied by float32(1 / sqrt(C)) (unit-variance projections); all
     rounded to bf16 by round-to-nearest-even."""
+    order = ("x", "w_k", "w_v", "w_q")
     rng = np.random.default_rng(p.seed if seed is None else seed)
     wscale = np.float32(1.0 / np.sqrt(p.C))
     raw, f64 = {}, {}
-    for name, shape, scale in (("x", (p.B, p.N, p.C), None), ("w_k", (p.H * p.D, p.C), wscale),
-                               ("w_v", (p.H * p.D, p.C), wscale)):
+    for name in order[:1 + max(order.index(n) for n in names)]:
+        shape = (p.B, p.N, p.C) if name == "x" else (p.H * p.D, p.C)
         a = rng.standard_normal(shape, dtype=np.float32)
-        if scale is not None:
-            a *= scale
+        if name not in names:
+            continue
+        if name != "x":
+            a *= wscale
         raw[name] = bf16_bits_from_f32(a)
         if with_f64:
             f64[name] = f64_from_bf16_bits(raw[name])
