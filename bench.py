@@ -334,6 +334,109 @@ def project_bench(args, dev, stream):
     print(json.dumps(rec), flush=True)
 
 
+def project_apply_bench(args, dev, stream):
+    """Time sana_linattn_project_apply, the query projection fused with the
+    apply step, on the Sana-1.6B 4096 px layer (x [1, 16384, 2240] bf16, W_q
+    [2240, 2240] bf16, 70 heads, a given fp32 state), one call per step,
+    cycling input sets (x and W_q) past the Infinity Cache; with --workload
+    video720p_rope3d the 720p layer's 18480 tokens with its 3D RoPE.  Beside
+    it, the unfused path on the same stream: a bf16 library GEMM (torch.matmul,
+    hipBLASLt) writing Q as [N, 2240], then sana_linattn_apply reading Q
+    [B, H, N, D] (the regrouping copy between the two is not counted).  Timed
+    in two alternating rounds, the second reported.  Algorithmic flops:
+    2 N C H D for the projection plus 2 N H D (D + 1) for the apply."""
+    import numpy as np
+    import torch
+
+    import linear_attention_diffusion_amd as la
+    from workloads import PROJECTIONS, generate_projection, reduced
+
+    p = reduced(PROJECTIONS["sana16b_4096px_kv_proj"], name="sana16b_4096px_q_proj")
+    w = WORKLOADS[args.workload]
+    rope = None
+    if w.mode == "rope":
+        p = reduced(p, name=f"{w.name}_q_proj", N=w.N)
+        rope = make_rope(la, w, dev, args.rope_form)
+    elif w.name != "sana16b_4096px":
+        raise SystemExit("--pass project_apply runs on the sana16b_4096px layer or, with RoPE, video720p_rope3d")
+    rope_ref = None if rope is None else ctypes.byref(rope.struct())
+    x = generate_projection(p, with_f64=False, names=("x", "w_q"))
+
+    def td(raw):
+        return torch.from_numpy(raw.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    x0, wq0 = td(x.raw["x"]), td(x.raw["w_q"])
+    set_bytes = (x0.numel() + wq0.numel()) * 2 + p.B * p.N * p.H * 32 * 2
+    n_sets = max(2, min(32, math.ceil(1.5 * 2 ** 30 / set_bytes) + 1))
+    sets = [(x0.clone(), wq0.clone(), torch.empty(p.B, p.H, p.N, 32, dtype=torch.bfloat16, device=dev))
+            for _ in range(n_sets)]
+    g = torch.Generator(device="cpu").manual_seed(1)
+    kv = (torch.randn(p.B, p.H, 32, 32, generator=g) * 50).to(dev)
+    z = (torch.rand(p.B, p.H, 32, generator=g) * 4000 + 10).to(dev)
+    L = la.lib()
+    P = ctypes.c_void_p
+    st_ptr = ctypes.c_void_p(stream.cuda_stream)
+    calls = [(P(a.data_ptr()), P(b.data_ptr()), P(o.data_ptr()), None, P(kv.data_ptr()), P(z.data_ptr()), p.B, p.H,
+              p.N, p.C, 32, la.SANA_DT_BF16, 1e-6, rope_ref, st_ptr) for a, b, o in sets]
+
+    def step(i):
+        rc = L.sana_linattn_project_apply(*calls[i % n_sets])
+        if rc:
+            raise la.SanaError(rc)
+
+    def timed(fn, first):
+        for i in range(args.warmup):
+            fn(first + i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.steps):
+            fn(first + args.warmup + i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    out = torch.empty(p.B * p.N, p.H * 32, dtype=torch.bfloat16, device=dev)
+    q = torch.empty(p.B, p.H, p.N, 32, dtype=torch.bfloat16, device=dev)
+
+    def gemm(i):
+        torch.matmul(sets[i % n_sets][0].view(p.B * p.N, p.C), sets[i % n_sets][1].t(), out=out)
+
+    def apply(i):
+        la.sana_linattn_apply(q, kv, z, o=sets[i % n_sets][2], rope=rope, stream=stream)
+
+    # alternating rounds, the second reported (matrix-core clock ramp)
+    for _ in range(2):
+        ms = timed(step, 0)
+        ms_gemm = timed(gemm, 0)
+    q.copy_(out.view(p.B, p.N, p.H, 32).permute(0, 2, 1, 3))
+    ms_apply = timed(apply, 0)
+    pct = step_percentiles(step, min(args.steps, 20), 0, stream)
+
+    flops = 2.0 * p.B * p.N * p.C * (p.H * 32) + 2.0 * p.B * p.N * p.H * 32 * 33
+    rope_name = None if rope is None else ("3D RoPE, per-axis tables" if rope.grid else "3D RoPE, full tables")
+    tflops = flops / (ms / 1e3) / 1e12
+    th = p.B * p.N * p.H
+    rec = {
+        "metric": "fused Q projection + linear-attn apply, tokens·heads/s (" +
+                  ("Sana-1.6B 4096px layer)" if rope is None else "SANA-Video 720p layer, 3D RoPE)"),
+        "value": th / (ms / 1e3), "unit": "tokens·heads/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "step_ms_percentiles": pct, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) bf16 activations, N(0,1/C) bf16 weights, random fp32 state",
+        "config": {"workload": p.name, "pass": "project_apply", "B": p.B, "N": p.N, "C": p.C, "H": p.H, "D": p.D,
+                   "rope": rope_name, "input_sets_cycled": n_sets},
+        "roofline": {"bound": "mfma", "kernel": "project_apply_bf16", "achieved": tflops, "peak": 2500.0,
+                     "unit": "TFLOP/s", "frac": tflops / 2500.0, "traffic": None,
+                     "algorithmic_flops_per_launch": flops, "avg_launch_ms": ms},
+        "two_pass": {"gemm_ms": ms_gemm, "apply_ms": ms_apply, "total_ms": ms_gemm + ms_apply,
+                     "gemm_tflops": 2.0 * p.B * p.N * p.C * (p.H * 32) / (ms_gemm / 1e3) / 1e12,
+                     "fused_speedup": (ms_gemm + ms_apply) / ms},
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def project_cpu_baseline(p, budget_s, angles=None):
     """The float64 oracle's projected_kv_state on the host (keys rotated by
     `angles` if given), over whole heads of the same layer until the budget is
@@ -599,11 +702,12 @@ def main():
     ap.add_argument("--block-mode", choices=["chunks", "sequence"], default="chunks",
                     help="block-causal workload: one block_forward call per chunk (inference, the default) or "
                          "one block_causal call over the whole sequence (all chunks known at once)")
-    ap.add_argument("--pass", dest="which", choices=["forward", "backward", "conv", "project"], default="forward",
+    ap.add_argument("--pass", dest="which", choices=["forward", "backward", "conv", "project", "project_apply"], default="forward",
                     help="forward (the default; the headline metric) or backward: one sana_linattn_backward "
                          "call per step (dQ, dK, dV; whole sequence in block-causal chunks for that workload); "
                          "conv: the block-inference temporal conv; project: the key/value projection fused "
-                         "with the state update (Sana-1.6B 4096 px layer, or video720p_rope3d with its RoPE)")
+                         "with the state update (Sana-1.6B 4096 px layer, or video720p_rope3d with its RoPE); "
+                         "project_apply: the query projection fused with the apply step (same layers)")
     ap.add_argument("--layout", choices=["bhnd", "packed"], default="bhnd",
                     help="bhnd = contiguous [B, H, N, D] (the default); packed = Q, K, V (and dO for the backward) "
                          "read as strided views of one [B, N, 3 (4), H, D] projection-style buffer and O (dQ, dK, "
@@ -641,6 +745,9 @@ def main():
         return
     if args.which == "project":
         project_bench(args, dev, stream)
+        return
+    if args.which == "project_apply":
+        project_apply_bench(args, dev, stream)
         return
 
     x = generate(w, with_f64=False)
