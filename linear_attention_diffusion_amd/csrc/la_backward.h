@@ -54,8 +54,8 @@ __device__ __forceinline__ f32x4_t rotate4(f32x4_t x, const Rope& rp, const floa
     float c, s;
     rope_pair<ROPE>(rp, rtab, pos, f0 / 2 + u, c, s);
     if (INVERSE) s = -s;
-    y[2 * u] = x[2 * u] * c - x[2 * u + 1] * s;
-    y[2 * u + 1] = x[2 * u] * s + x[2 * u + 1] * c;
+    y[2 * u] = rot_lo(x[2 * u], x[2 * u + 1], c, s);
+    y[2 * u + 1] = rot_hi(x[2 * u], x[2 * u + 1], c, s);
   }
   return y;
 }
@@ -381,8 +381,8 @@ __device__ __forceinline__ void rotate8(float (&x)[8], f32x4_t c, f32x4_t sn) {
   for (int p = 0; p < 4; ++p) {
     const float s = INVERSE ? -sn[p] : sn[p];
     const float x0 = x[2 * p], x1 = x[2 * p + 1];
-    x[2 * p] = x0 * c[p] - x1 * s;
-    x[2 * p + 1] = x0 * s + x1 * c[p];
+    x[2 * p] = rot_lo(x0, x1, c[p], s);
+    x[2 * p + 1] = rot_hi(x0, x1, c[p], s);
   }
 }
 

@@ -241,6 +241,13 @@ __device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
 // each residual is exact in fp32 (x - bf16(x) has at most 16 significant
 // bits).  Called for a pair (a, b), each part comes back as one dword of two
 // packed bf16.
+// One RoPE pair rotation, (a, b) -> (a c - b s, a s + b c), with its fused
+// multiply-adds written out: left to the compiler, the contraction may fuse
+// either product of a c - b s depending on the surrounding code, and two
+// kernels (or two table forms) inlining the same source could round apart.
+__device__ __forceinline__ float rot_lo(float a, float b, float c, float s) { return __builtin_fmaf(a, c, -(b * s)); }
+__device__ __forceinline__ float rot_hi(float a, float b, float c, float s) { return __builtin_fmaf(a, s, b * c); }
+
 __device__ __forceinline__ void split3_bf16x2(float a, float b, unsigned& hi, unsigned& mid, unsigned& lo) {
   hi = pack_bf16x2(a, b);
   const float ra = a - bf16lo_to_f32(hi), rb = b - bf16hi_to_f32(hi);
@@ -759,8 +766,8 @@ __global__ __launch_bounds__(kThreads) void state_f32(const float* __restrict__ 
       if constexpr (ROPE) {
         float c = 1.f, sn = 0.f;
         if (gt < n_end) rope_pair<ROPE>(rp, rtab, rp.pos0 + gt, p, c, sn);
-        skr[tok][2 * p] = k0 * c - k1 * sn;
-        skr[tok][2 * p + 1] = k0 * sn + k1 * c;
+        skr[tok][2 * p] = rot_lo(k0, k1, c, sn);
+        skr[tok][2 * p + 1] = rot_hi(k0, k1, c, sn);
       }
     }
     __syncthreads();
@@ -856,7 +863,7 @@ __device__ __forceinline__ u32x4_t apply_tile(u32x4_t q, const ApplyOperands& op
     for (int p = 0; p < 4; ++p) {
       const float x0 = bf16lo_to_f32(q[p]);
       const float x1 = bf16hi_to_f32(q[p]);
-      split3_bf16x2(x0 * c[p] - x1 * sn[p], x0 * sn[p] + x1 * c[p], rq[0][p], rq[1][p], rq[2][p]);
+      split3_bf16x2(rot_lo(x0, x1, c[p], sn[p]), rot_hi(x0, x1, c[p], sn[p]), rq[0][p], rq[1][p], rq[2][p]);
     }
     bf16x8_t b_r[3];
 #pragma unroll
@@ -1021,8 +1028,8 @@ __global__ __launch_bounds__(kThreads) void apply_f32(const float* __restrict__ 
       if constexpr (ROPE) {
         float c, sn;
         rope_pair<ROPE>(rp, rtab, rp.pos0 + tok, p, c, sn);
-        pr[2 * p] = pq[2 * p] * c - pq[2 * p + 1] * sn;
-        pr[2 * p + 1] = pq[2 * p] * sn + pq[2 * p + 1] * c;
+        pr[2 * p] = rot_lo(pq[2 * p], pq[2 * p + 1], c, sn);
+        pr[2 * p + 1] = rot_hi(pq[2 * p], pq[2 * p + 1], c, sn);
       } else {
         pr[2 * p] = pq[2 * p];
         pr[2 * p + 1] = pq[2 * p + 1];

@@ -306,7 +306,7 @@ __global__ __launch_bounds__(kThreads, 2) void project_state_bf16(ProjArgs p, Ro
             for (int fh = 0; fh < 2; ++fh) {
               const float x = e ? bf16hi_to_f32(kw[fh][d]) : bf16lo_to_f32(kw[fh][d]);
               const float xp = sgn * (e ? bf16hi_to_f32(pw[fh][d]) : bf16lo_to_f32(pw[fh][d]));
-              y[fh][e] = x * c[fh] + xp * sn[fh];
+              y[fh][e] = __builtin_fmaf(x, c[fh], xp * sn[fh]);  // the fusion fixed, as in rot_lo
             }
           }
 #pragma unroll

@@ -175,6 +175,19 @@ def test_project_apply_matches_oracle(B, N, C, H):
     _check_apply(to_np(o), x, S, z, 1e-6)
 
 
+@pytest.mark.parametrize("N", [25500, 25444])
+def test_project_apply_many_blocks_ragged(N):
+    """600 workgroups (3 batch rows x 100 blocks x 2 head quads, H = 6): more
+    than one round of resident workgroups, and every batch row ends in a ragged
+    block (156 tokens, or 100, which leaves the block's second 128 tokens
+    empty)."""
+    print(f"case project_apply many blocks N={N}", flush=True)
+    x = generate_projection(reduced(FULL, B=3, N=N, C=64, H=6, seed=N), names=("x", "w_q"))
+    S, z = _state_for(reduced(x.workload, N=2000), 10)
+    o = _run_apply(x, S, z)
+    _check_apply(to_np(o), x, S, z, 1e-6)
+
+
 @pytest.mark.parametrize("grid,offset", [((3, 8, 20), 0), ((4, 10, 12), 150)])
 def test_project_apply_rope_and_strided_output(grid, offset):
     """Queries rotated by the 3D RoPE (both table forms, bit-identical), and
