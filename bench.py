@@ -427,20 +427,25 @@ def project_apply_bench(args, dev, stream):
         "config": {"workload": p.name, "pass": "project_apply", "B": p.B, "N": p.N, "C": p.C, "H": p.H, "D": p.D,
                    "rope": rope_name, "input_sets_cycled": n_sets},
         "roofline": {"bound": "mfma", "kernel": "project_apply_bf16", "achieved": tflops, "peak": 2500.0,
-                     "unit": "TFLOP/s", "frac": tflops / 2500.0, "traffic": None,
+                     "unit": "TFLOP/s", "frac": tflops / 2500.0,
+                     "traffic": stored_traffic("project_apply_4096px") if rope is None else None,
                      "algorithmic_flops_per_launch": flops, "avg_launch_ms": ms},
         "two_pass": {"gemm_ms": ms_gemm, "apply_ms": ms_apply, "total_ms": ms_gemm + ms_apply,
                      "gemm_tflops": 2.0 * p.B * p.N * p.C * (p.H * 32) / (ms_gemm / 1e3) / 1e12,
                      "fused_speedup": (ms_gemm + ms_apply) / ms},
         "kernel_source_hash": kernel_source_hash(),
     }
+    if not args.no_cpu_baseline:
+        import oracle
+        angles = None if rope is None else oracle.rope3d_angles(*w.grid)
+        rec["cpu_baseline"] = project_cpu_baseline(p, args.cpu_budget, angles, query=True)
     print(json.dumps(rec), flush=True)
 
 
-def project_cpu_baseline(p, budget_s, angles=None):
+def project_cpu_baseline(p, budget_s, angles=None, query=False):
     """The float64 oracle's projected_kv_state on the host (keys rotated by
-    `angles` if given), over whole heads of the same layer until the budget is
-    spent."""
+    `angles` if given), or with `query` its projected_apply against a fixed
+    state, over whole heads of the same layer until the budget is spent."""
     import numpy as np
 
     import oracle
@@ -450,15 +455,24 @@ def project_cpu_baseline(p, budget_s, angles=None):
         threads = max([q.get("num_threads", 1) for q in threadpool_info()] or [1])
     except Exception:
         threads = len(os.sched_getaffinity(0))
-    f = generate_projection(p).f64
+    f = generate_projection(p, names=("x", "w_q") if query else ("x", "w_k", "w_v")).f64
     C = p.C
-    wk = f["w_k"].reshape(p.H, 32, C).transpose(0, 2, 1)
-    wv = f["w_v"].reshape(p.H, 32, C).transpose(0, 2, 1)
     heads, done, runs = 2, 0, 0
+    if query:
+        wq = f["w_q"].reshape(p.H, 32, C).transpose(0, 2, 1)
+        rng = np.random.default_rng(1)
+        S = rng.standard_normal((p.B, heads, 32, 32)) * 50
+        z = rng.random((p.B, heads, 32)) * 4000 + 10
+    else:
+        wk = f["w_k"].reshape(p.H, 32, C).transpose(0, 2, 1)
+        wv = f["w_v"].reshape(p.H, 32, C).transpose(0, 2, 1)
     t0 = time.perf_counter()
     while True:
         h0 = (runs * heads) % p.H
-        oracle.projected_kv_state(f["x"], wk[h0:h0 + heads], wv[h0:h0 + heads], angles)
+        if query:
+            oracle.projected_apply(f["x"], wq[h0:h0 + heads], S, z, 1e-6, angles)
+        else:
+            oracle.projected_kv_state(f["x"], wk[h0:h0 + heads], wv[h0:h0 + heads], angles)
         done += p.B * heads * p.N
         runs += 1
         el = time.perf_counter() - t0

@@ -1,4 +1,5 @@
-// Key/value projection fused with the state pass (gfx950 / CDNA4).
+// Projections fused with the attention (gfx950 / CDNA4): keys and values with
+// the state pass, queries with the apply pass.
 //
 // Ahead of the attention, a layer projects its input x [B][N][C] into keys and
 // values, K = x W_k^T and V = x W_v^T (per head, 32 features each).  Unfused,
@@ -31,6 +32,10 @@
 // contiguous runs, and inside a run walk 4 token ranges per head pair: the
 // workgroups resident on one XCD then share each x slice among several head
 // pairs and each weight slice among 4 token ranges in its L2.
+//
+// The query side (project_apply_bf16, at the end) runs the same GEMM over four
+// heads' query weights and hands each 16-token tile of Q to the apply pass's
+// arithmetic in registers.
 #pragma once
 
 #include "la_kernels.h"
