@@ -199,9 +199,12 @@ size_t sana_linattn_project_state_workspace_bytes(int B, int H, int64_t N, int C
  * feature d of head h), both 16-byte aligned; o: bf16 outputs [B][H][N][D]
  * through the view `out` (NULL: contiguous; e.g. [B][N][H][D]), overlapping
  * no input; kv_state [B][H][D][D], ksum_state [B][H][D]: fp32, read only (for
- * example from sana_linattn_project_state).  C a positive multiple of 32, at
- * most 65536; only bf16 and D = 32 have kernels.  No workspace.  B*H*N = 0 is
- * a no-op. */
+ * example from sana_linattn_project_state).  eps >= 0 and finite.
+ * SANA_ERR_INVALID: negative sizes, C not a positive multiple of 32 or above
+ * 65536, a NULL or misaligned pointer, o overlapping an input, a bad view, bad
+ * eps, or RoPE tables shorter than pos_offset + N.  SANA_ERR_UNSUPPORTED: a
+ * dtype other than bf16 or D other than 32.  No workspace.  B*H*N = 0 is a
+ * no-op that touches nothing. */
 int sana_linattn_project_apply(const void* x, const void* w_q, void* o, const sana_layout* out,
                                const float* kv_state, const float* ksum_state, int B, int H, int64_t N, int C,
                                int D, int dtype, float eps, const sana_rope* rope, void* hip_stream);
