@@ -39,8 +39,8 @@ def _run(x, kv=None, z=None, rope=None):
 
 # (B, N, C, H): one 256-token block; ragged tails with an odd head count (the
 # last head pair has one head); several ranges (partials + finalize); more than
-# 128 blocks, so each range spans two blocks
-CASES = [(1, 256, 32, 2), (2, 700, 96, 3), (1, 1000, 64, 4), (1, 5000, 128, 5), (1, 33000, 32, 2)]
+# 128 blocks, so each range spans two blocks; a single head
+CASES = [(1, 256, 32, 2), (2, 700, 96, 3), (1, 1000, 64, 4), (1, 5000, 128, 5), (1, 33000, 32, 2), (1, 300, 64, 1)]
 
 
 @pytest.mark.parametrize("B,N,C,H", CASES)
@@ -166,13 +166,23 @@ def _check_apply(*args, **kw):
     assert ok, report
 
 
-@pytest.mark.parametrize("B,N,C,H", [(1, 256, 32, 4), (2, 700, 96, 3), (1, 1000, 64, 6), (1, 5000, 128, 5)])
+@pytest.mark.parametrize("B,N,C,H", [(1, 256, 32, 4), (2, 700, 96, 3), (1, 1000, 64, 6), (1, 5000, 128, 5),
+                                     (1, 300, 64, 1)])
 def test_project_apply_matches_oracle(B, N, C, H):
     print(f"case project_apply B={B} N={N} C={C} H={H}", flush=True)
     x = generate_projection(reduced(FULL, B=B, N=N, C=C, H=H, seed=N + C + 1), names=("x", "w_q"))
     S, z = _state_for(x.workload, 7)
     o = _run_apply(x, S, z)
     _check_apply(to_np(o), x, S, z, 1e-6)
+
+
+def test_project_apply_empty_touches_nothing():
+    torch = torch_mod()
+    x = generate_projection(reduced(FULL, B=1, N=0, C=64, H=2), names=("x", "w_q"))
+    S, z = _state_for(reduced(x.workload, N=100), 11)
+    o = torch.full((1, 2, 0, 32), 1.0, dtype=torch.bfloat16, device=device())
+    print("case project_apply N=0", flush=True)
+    assert _run_apply(x, S, z, o=o) is o
 
 
 @pytest.mark.parametrize("N", [25500, 25444])
