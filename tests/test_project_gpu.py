@@ -176,6 +176,16 @@ def test_project_apply_matches_oracle(B, N, C, H):
     _check_apply(to_np(o), x, S, z, 1e-6)
 
 
+def test_project_apply_eps_zero_ragged():
+    """eps = 0 with a ragged last block: the rows past N, whose queries read as
+    zero (0 / 0), must not reach the output."""
+    x = generate_projection(reduced(FULL, B=2, N=700, C=64, H=3, seed=31), names=("x", "w_q"))
+    S, z = _state_for(x.workload, 12)
+    print("case project_apply eps=0", flush=True)
+    o = _run_apply(x, S, z, eps=0.0)
+    _check_apply(to_np(o), x, S, z, 0.0)
+
+
 def test_project_apply_empty_touches_nothing():
     torch = torch_mod()
     x = generate_projection(reduced(FULL, B=1, N=0, C=64, H=2), names=("x", "w_q"))
