@@ -51,6 +51,15 @@ def test_project_state_matches_oracle(B, N, C, H):
     _check_state(to_np(kv), to_np(z), x)
 
 
+def test_project_state_max_channels():
+    """C = 65536, the largest channel count the call accepts (2048 channel
+    steps; x rows of 128 KB)."""
+    print("case project_state C=65536", flush=True)
+    x = generate_projection(reduced(FULL, B=1, N=300, C=65536, H=3, seed=41))
+    kv, z = _run(x)
+    _check_state(to_np(kv), to_np(z), x)
+
+
 def test_project_state_accumulates_in_place():
     """The call adds to the states it is given, as state_update does."""
     torch = torch_mod()
@@ -184,6 +193,13 @@ def test_project_apply_eps_zero_ragged():
     print("case project_apply eps=0", flush=True)
     o = _run_apply(x, S, z, eps=0.0)
     _check_apply(to_np(o), x, S, z, 0.0)
+
+
+def test_project_apply_max_channels():
+    print("case project_apply C=65536", flush=True)
+    x = generate_projection(reduced(FULL, B=1, N=300, C=65536, H=3, seed=42), names=("x", "w_q"))
+    S, z = _state_for(x.workload, 13)
+    _check_apply(to_np(_run_apply(x, S, z)), x, S, z, 1e-6)
 
 
 def test_project_apply_empty_touches_nothing():
