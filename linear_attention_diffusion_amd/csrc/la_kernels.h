@@ -334,9 +334,13 @@ __device__ __forceinline__ void store16_nt(rsrc_t r, int off, u32x4_t x) {
 // ---------------------------------------------------------------------------
 
 // Element idx (33 x 32 layout) of the carried state, 0 when there is none.
+__device__ __forceinline__ float carried_state(const float* kv_in, const float* ksum_in, int64_t bh, int idx) {
+  if (idx < 1024) return kv_in ? kv_in[bh * 1024 + idx] : 0.f;
+  return ksum_in ? ksum_in[bh * 32 + (idx - 1024)] : 0.f;
+}
+
 __device__ __forceinline__ float carried(const StateArgs& a, int64_t bh, int idx) {
-  if (idx < 1024) return a.kv_in ? a.kv_in[bh * 1024 + idx] : 0.f;
-  return a.ksum_in ? a.ksum_in[bh * 32 + (idx - 1024)] : 0.f;
+  return carried_state(a.kv_in, a.ksum_in, bh, idx);
 }
 
 // Stores element idx of the last chunk's state as the committed state.
@@ -618,6 +622,87 @@ __device__ __forceinline__ void state_tile(const u32x4_t (&kx)[2], const u32x4_t
   }
 }
 
+// One wave's share of a token range of one head: the 64-token chunks at t0,
+// t0 + 256, ... below n_end (a workgroup's four waves start 64 tokens apart),
+// accumulated into acc (S blocks, key half fh x value half fh') and accz (z).
+// The next chunk's loads are issued before the current chunk is computed.
+// `row`: bytes between tokens; `lds`: the wave's angle tile (RoPE only);
+// `rtab`: the staged per-axis tables (axis form only).
+template <int ROPE, int HEADS>
+__device__ __forceinline__ void state_accumulate(const char* Kh, const char* Vh, int64_t row, int64_t t0,
+                                                 int64_t n_end, const Rope& rp, const float* rtab, float* lds, int g,
+                                                 int n, f32x4_t (&acc)[2][2], f32x4_t (&accz)[2]) {
+  const AxisLane al = axis_lane(rp, g);  // axis form only
+  // lane's 16-byte piece of a row: features 8g .. 8g+7 of token (tile row) n
+  const int lane_off = n * (int)row + g * 16;
+  const int tab_off = n * 64 + g * 16;  // the same piece of a cos/sin table row
+
+  const bf16x8_t sel[2] = {select_operand(g, n, 0), select_operand(g, n, 1)};
+  const bf16x8_t selp[2] = {partner_operand(g, n, 0), partner_operand(g, n, 1)};
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    accz[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    acc[i][0] = accz[i];
+    acc[i][1] = accz[i];
+  }
+
+  // each wave takes 64-token chunks (two 32-token tiles of two 16-row halves)
+  u32x4_t nk[4], nv[4];
+  TileAnglesRows na[2];  // cos/sin rows of the two tiles (RoPE only)
+  auto load_chunk = [&](int64_t c0) {
+    const rsrc_t rk = rows_rsrc(Kh, c0, n_end, row);
+    const rsrc_t rv = rows_rsrc(Vh, c0, n_end, row);
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      nk[h] = load16_stream<HEADS>(rk, lane_off + h * 16 * (int)row);
+      nv[h] = load16_stream<HEADS>(rv, lane_off + h * 16 * (int)row);
+    }
+    if constexpr (ROPE == kRopeTable) {
+      load_angle_rows(rp.cos, rp.sin, rp.pos0, c0, n_end, tab_off, na[0]);
+      load_angle_rows(rp.cos, rp.sin, rp.pos0, c0 + 32, n_end, tab_off, na[1]);
+    }
+    // the axis form's angles come from LDS when the tile is computed
+  };
+  if (t0 < n_end) load_chunk(t0);
+  for (; t0 < n_end; t0 += 256) {
+    const u32x4_t ka[2] = {nk[0], nk[1]}, va[2] = {nv[0], nv[1]};
+    const u32x4_t kb[2] = {nk[2], nk[3]}, vb[2] = {nv[2], nv[3]};
+    TileAnglesRows ra = na[0], rb = na[1];
+    if (t0 + 256 < n_end) load_chunk(t0 + 256);
+    if constexpr (ROPE == kRopeAxes) {
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        rope_axis_row4(rp, rtab, al, rp.pos0 + t0 + 16 * tb + n, ra.c[tb], ra.s[tb]);
+        rope_axis_row4(rp, rtab, al, rp.pos0 + t0 + 32 + 16 * tb + n, rb.c[tb], rb.s[tb]);
+      }
+    }
+    state_tile<ROPE != 0>(ka, va, ra, g, n, lds, sel, selp, acc, accz);
+    if (t0 + 32 < n_end) state_tile<ROPE != 0>(kb, vb, rb, g, n, lds, sel, selp, acc, accz);
+  }
+}
+
+// A wave's accumulators into its 33 x 32 LDS tile.  D lane (n, g): rows
+// 4g + i -> key feature 16fh + 4g + i, column n -> value feature 16fh' + n.
+__device__ __forceinline__ void state_to_lds(const f32x4_t (&acc)[2][2], const f32x4_t (&accz)[2], float* rw, int g,
+                                             int n) {
+#pragma unroll
+  for (int fh = 0; fh < 2; ++fh) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d = 16 * fh + 4 * g + i;
+      rw[d * 32 + n] = acc[fh][0][i];
+      rw[d * 32 + 16 + n] = acc[fh][1][i];
+      if (n == 0) rw[1024 + d] = accz[fh][i];
+    }
+  }
+}
+
+// The four waves' tiles of r[0..3] summed into r[0], in a fixed order.
+__device__ __forceinline__ void sum_wave_tiles(float (*r)[kStateElems], int tid) {
+  for (int idx = tid; idx < kStateElems; idx += kThreads)
+    r[0][idx] = (r[0][idx] + r[1][idx]) + (r[2][idx] + r[3][idx]);
+}
+
 // DENSE: consecutive tokens are adjacent 64-byte rows (token stride = 32
 // elements), so every tile offset is an instruction immediate.
 template <int ROPE, bool DENSE, int HEADS>
@@ -641,82 +726,19 @@ __global__ __launch_bounds__(kThreads* HEADS) void state_bf16(const u32x4_t* __r
   const bool active = bh < BH;
   const int n = lane & 15;
   const int g = lane >> 4;
-  const AxisLane al = axis_lane(rp, g);  // axis form only
 
-  // lane's 16-byte piece of a row: features 8g .. 8g+7 of token (tile row) n
   const int64_t row = DENSE ? 64 : lkv.token * 2;  // bytes between tokens
   const char* Kh = reinterpret_cast<const char*>(K) + lkv.base(bh) * 2;
   const char* Vh = reinterpret_cast<const char*>(V) + lkv.base(bh) * 2;
-  const int lane_off = n * (int)row + g * 16;
-  const int tab_off = n * 64 + g * 16;  // the same piece of a cos/sin table row
-
-  const bf16x8_t sel[2] = {select_operand(g, n, 0), select_operand(g, n, 1)};
-  const bf16x8_t selp[2] = {partner_operand(g, n, 0), partner_operand(g, n, 1)};
   f32x4_t acc[2][2], accz[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    accz[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    acc[i][0] = accz[i];
-    acc[i][1] = accz[i];
-  }
-
-  // each wave takes 64-token chunks (two 32-token tiles of two 16-row halves);
-  // the next chunk's loads are issued before the current chunk is computed
-  int64_t t0 = n_begin + 64 * w;
-  u32x4_t nk[4], nv[4];
-  TileAnglesRows na[2];  // cos/sin rows of the two tiles (RoPE only)
-  auto load_chunk = [&](int64_t c0) {
-    const rsrc_t rk = rows_rsrc(Kh, c0, n_end, row);
-    const rsrc_t rv = rows_rsrc(Vh, c0, n_end, row);
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      nk[h] = load16_stream<HEADS>(rk, lane_off + h * 16 * (int)row);
-      nv[h] = load16_stream<HEADS>(rv, lane_off + h * 16 * (int)row);
-    }
-    if constexpr (ROPE == kRopeTable) {
-      load_angle_rows(rp.cos, rp.sin, rp.pos0, c0, n_end, tab_off, na[0]);
-      load_angle_rows(rp.cos, rp.sin, rp.pos0, c0 + 32, n_end, tab_off, na[1]);
-    }
-    // the axis form's angles come from LDS when the tile is computed
-  };
-  float* lds = angles[ROPE ? wg : 0];
-  if (!active) t0 = n_end;
-  if (t0 < n_end) load_chunk(t0);
-  for (; t0 < n_end; t0 += 256) {
-    const u32x4_t ka[2] = {nk[0], nk[1]}, va[2] = {nv[0], nv[1]};
-    const u32x4_t kb[2] = {nk[2], nk[3]}, vb[2] = {nv[2], nv[3]};
-    TileAnglesRows ra = na[0], rb = na[1];
-    if (t0 + 256 < n_end) load_chunk(t0 + 256);
-    if constexpr (ROPE == kRopeAxes) {
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        rope_axis_row4(rp, rtab, al, rp.pos0 + t0 + 16 * tb + n, ra.c[tb], ra.s[tb]);
-        rope_axis_row4(rp, rtab, al, rp.pos0 + t0 + 32 + 16 * tb + n, rb.c[tb], rb.s[tb]);
-      }
-    }
-    state_tile<ROPE != 0>(ka, va, ra, g, n, lds, sel, selp, acc, accz);
-    if (t0 + 32 < n_end) state_tile<ROPE != 0>(kb, vb, rb, g, n, lds, sel, selp, acc, accz);
-  }
-
-  // D lane (n, g): rows 4g + i -> key feature 16fh + 4g + i, column n -> value feature 16fh' + n
-  float* rw = red[wg];
-#pragma unroll
-  for (int fh = 0; fh < 2; ++fh) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int d = 16 * fh + 4 * g + i;
-      rw[d * 32 + n] = acc[fh][0][i];
-      rw[d * 32 + 16 + n] = acc[fh][1][i];
-      if (n == 0) rw[1024 + d] = accz[fh][i];
-    }
-  }
+  state_accumulate<ROPE, HEADS>(Kh, Vh, row, active ? n_begin + 64 * w : n_end, n_end, rp, rtab,
+                                angles[ROPE ? wg : 0], g, n, acc, accz);
+  state_to_lds(acc, accz, red[wg], g, n);
   __syncthreads();
-  float* const r = red[4 * half];
   const int tid = threadIdx.x & (kThreads - 1);
-  for (int idx = tid; idx < kStateElems; idx += kThreads)
-    r[idx] = (r[idx] + r[kStateElems + idx]) + (r[2 * kStateElems + idx] + r[3 * kStateElems + idx]);
+  sum_wave_tiles(red + 4 * half, tid);
   __syncthreads();
-  if (active) write_partial(r, bh, c, s, a, tid);
+  if (active) write_partial(red[4 * half], bh, c, s, a, tid);
 }
 
 // ---------------------------------------------------------------------------
@@ -921,6 +943,28 @@ __device__ __forceinline__ void load_apply_chunk(const char* Qh, int64_t row, in
   // the axis form's angles come from LDS when the tile is computed
 }
 
+// A wave's 64-token chunks t0, t0 + 256, ... below n_end of one head, the
+// first of which `next` already holds (loaded before the state operands were
+// fetched): each chunk's loads go out before the previous chunk is computed.
+template <int ROPE, int HEADS>
+__device__ __forceinline__ void apply_stream(const char* Qh, char* Oh, int64_t qrow, int64_t orow, int64_t t0,
+                                             int64_t n_end, int q_off, int o_off, int tab_off, int m, int g,
+                                             const Rope& rp, const float* rtab, const AxisLane& al,
+                                             const ApplyOperands& op, float eps, ApplyChunk<ROPE>& next) {
+  for (; t0 < n_end; t0 += 256) {
+    const ApplyChunk<ROPE> cur = next;
+    if (t0 + 256 < n_end)
+      load_apply_chunk<ROPE, HEADS>(Qh, qrow, t0 + 256, n_end, q_off, tab_off, m, g, rp, rtab, next);
+    const rsrc_t ro = rows_rsrc(Oh, t0, n_end, orow);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      f32x4_t c = cur.c[u], sn = cur.sn[u];
+      if constexpr (ROPE == kRopeAxes) rope_axis_row4(rp, rtab, al, rp.pos0 + t0 + 16 * u + m, c, sn);
+      store16_nt(ro, o_off + u * 16 * (int)orow, apply_tile<ROPE != 0>(cur.q[u], op, eps, c, sn));
+    }
+  }
+}
+
 template <int ROPE, bool DENSE, int HEADS>
 __global__ __launch_bounds__(kThreads* HEADS) void apply_bf16(const u32x4_t* __restrict__ Q, u32x4_t* __restrict__ O,
                                                               Layout lq, Layout lo, StateView sv, int64_t N,
@@ -973,18 +1017,8 @@ __global__ __launch_bounds__(kThreads* HEADS) void apply_bf16(const u32x4_t* __r
     const int64_t sc = bh * C + c;
     load_apply_operands(sv.s_base + sc * sv.s_stride, sv.z_base + sc * sv.z_stride, g, m, op);
 
-    for (; t0 < n_end; t0 += 256) {
-      const ApplyChunk<ROPE> cur = next;
-      if (t0 + 256 < n_end)
-        load_apply_chunk<ROPE, HEADS>(Qh, qrow, t0 + 256, n_end, q_off, tab_off, m, g, rp, rtab, next);
-      const rsrc_t ro = rows_rsrc(Oh, t0, n_end, orow);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        f32x4_t c = cur.c[u], sn = cur.sn[u];
-        if constexpr (ROPE == kRopeAxes) rope_axis_row4(rp, rtab, al, rp.pos0 + t0 + 16 * u + m, c, sn);
-        store16_nt(ro, o_off + u * 16 * (int)orow, apply_tile<ROPE != 0>(cur.q[u], op, eps, c, sn));
-      }
-    }
+    apply_stream<ROPE, HEADS>(Qh, Oh, qrow, orow, t0, n_end, q_off, o_off, tab_off, m, g, rp, rtab, al, op, eps,
+                              next);
   }
 }
 
