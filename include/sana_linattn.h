@@ -235,6 +235,32 @@ int sana_linattn_block_forward(const void* q, const void* k, const void* v, void
                                int B, int H, int64_t N, int D, int dtype, float eps,
                                const sana_rope* rope, void* ws, size_t ws_bytes, void* hip_stream);
 
+/* Bytes of the static scratch array behind sana_linattn_block_forward_noalloc
+ * (one copy per GPU, held until the process ends). */
+#define SANA_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+
+/* sana_linattn_block_forward for callers that cannot allocate: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The same computation and kernels as sana_linattn_block_forward (bit for bit
+ * the same outputs and commits), with no workspace argument: its scratch
+ * (split partials and the chunk state) lives in a file-scope device array of
+ * SANA_NOALLOC_SCRATCH_BYTES, whose address on the current device is looked
+ * up once, on the first call on that device (so make that first call outside
+ * graph capture).  The call allocates and frees nothing, copies, clears and
+ * synchronises nothing.  A call that needs more scratch than the array holds
+ * (sana_linattn_workspace_bytes(B, H, N, ...) > SANA_NOALLOC_SCRATCH_BYTES,
+ * i.e. more than about 1900 heads B*H) returns SANA_ERR_WORKSPACE before
+ * anything is launched.  Every call on one GPU shares that GPU's array and no
+ * call needs its earlier contents; calls that overlap on one GPU (two streams
+ * at once) race on it and must not be made.  hip_stream must belong to the
+ * current device.  A failed address lookup returns SANA_ERR_HIP.  Other
+ * arguments, layouts and errors: as sana_linattn_block_forward. */
+int sana_linattn_block_forward_noalloc(const void* q, const void* k, const void* v, void* o,
+                                       const float* kv_in, const float* ksum_in,
+                                       float* kv_out, float* ksum_out,
+                                       int B, int H, int64_t N, int D, int dtype, float eps,
+                                       const sana_rope* rope, void* hip_stream);
+
 /* sana_linattn_block_forward through layout views (see sana_linattn_forward_strided). */
 int sana_linattn_block_forward_strided(const void* q, const void* k, const void* v, void* o,
                                        const sana_layout* in, const sana_layout* out,

@@ -15,6 +15,7 @@ from .build import LIB_PATH
 
 SANA_OK, SANA_ERR_INVALID, SANA_ERR_UNSUPPORTED, SANA_ERR_WORKSPACE, SANA_ERR_HIP = 0, -1, -2, -3, -4
 SANA_DT_F32, SANA_DT_BF16 = 0, 1
+NOALLOC_SCRATCH_BYTES = 8 << 20  # SANA_NOALLOC_SCRATCH_BYTES in include/sana_linattn.h
 
 EXPORTED = (
     "sana_linattn_workspace_bytes",
@@ -25,6 +26,7 @@ EXPORTED = (
     "sana_linattn_project_state_workspace_bytes",
     "sana_linattn_project_apply",
     "sana_linattn_block_forward",
+    "sana_linattn_block_forward_noalloc",
     "sana_linattn_block_forward_strided",
     "sana_linattn_block_causal",
     "sana_linattn_block_causal_strided",
@@ -82,6 +84,9 @@ def lib():
     L.sana_linattn_block_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, f32,
                                              rp, vp, sz, vp]
     L.sana_linattn_block_forward.restype = i32
+    L.sana_linattn_block_forward_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, f32,
+                                                     rp, vp]
+    L.sana_linattn_block_forward_noalloc.restype = i32
     L.sana_linattn_block_causal.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i64, i64, i32, i32, f32,
                                             rp, vp, sz, vp]
     L.sana_linattn_block_causal.restype = i32
@@ -429,6 +434,28 @@ def sana_linattn_block_forward(q, k, v, o=None, kv_in=None, ksum_in=None, kv_out
                                                         _ptr(kv_in), _ptr(ksum_in), _ptr(kv_out), _ptr(ksum_out),
                                                         B, H, N, D, dt, float(eps), _rope_arg(rope), _ptr(ws),
                                                         nbytes, _stream(stream, q.device)))
+    return o
+
+
+def sana_linattn_block_forward_noalloc(q, k, v, o=None, kv_in=None, ksum_in=None, kv_out=None, ksum_out=None,
+                                       eps=1e-6, rope=None, stream=None):
+    """sana_linattn_block_forward without a workspace: the library's static
+    per-GPU scratch array stands in for it (contiguous [B, H, N, D] tensors).
+    Calls that overlap on one GPU race on that array."""
+    torch = _torch()
+    B, H, N, D = _shape4(q, "q")
+    if _shape4(k, "k") != (B, H, N, D) or _shape4(v, "v") != (B, H, N, D):
+        raise ValueError("q, k, v must have the same shape")
+    if o is None:
+        o = torch.empty((B, H, N, D), dtype=q.dtype, device=q.device)
+    elif _shape4(o, "o") != (B, H, N, D) or o.dtype != q.dtype:
+        raise ValueError("o must match q in shape and dtype")
+    for t, shape in ((kv_in, (B, H, D, D)), (ksum_in, (B, H, D)), (kv_out, (B, H, D, D)), (ksum_out, (B, H, D))):
+        if t is not None and (tuple(t.shape) != shape or t.dtype != torch.float32 or not t.is_contiguous()):
+            raise ValueError("states must be contiguous float32 [B, H, D, D] / [B, H, D]")
+    _check(lib().sana_linattn_block_forward_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(kv_in), _ptr(ksum_in),
+                                                    _ptr(kv_out), _ptr(ksum_out), B, H, N, D, _dtype_code(q),
+                                                    float(eps), _rope_arg(rope), _stream(stream, q.device)))
     return o
 
 

@@ -29,6 +29,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <type_traits>
 
 #include "la_backward.h"
@@ -36,6 +37,11 @@
 #include "la_kernels.h"
 #include "la_lines.h"
 #include "la_proj.h"
+
+// Scratch of sana_linattn_block_forward_noalloc: one copy per GPU.  In host
+// code this name is a stand-in, not a device address; host code uses only the
+// address that scratch_address() looks up.
+static __device__ __align__(256) unsigned char scratch[SANA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -605,6 +611,25 @@ int make_proj_geometry(int B, int H, int64_t N, int C, int D, int dtype, ProjGeo
   return SANA_OK;
 }
 
+// The device address of the current GPU's scratch array: looked up once per
+// device (with that device current) and kept.
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mutex;
+void* g_scratch[kMaxDevices] = {};
+
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SANA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SANA_ERR_HIP;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return SANA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -638,6 +663,19 @@ int sana_linattn_block_forward(const void* q, const void* k, const void* v, void
                                void* hip_stream) {
   return attend(q, k, v, o, nullptr, nullptr, kv_in, ksum_in, kv_out, ksum_out, B, H, N, N > 0 ? N : 1, D, dtype,
                 eps, rope, ws, ws_bytes, hip_stream);
+}
+
+int sana_linattn_block_forward_noalloc(const void* q, const void* k, const void* v, void* o, const float* kv_in,
+                                       const float* ksum_in, float* kv_out, float* ksum_out, int B, int H, int64_t N,
+                                       int D, int dtype, float eps, const sana_rope* rope, void* hip_stream) {
+  // too large for the array: rejected before any device call
+  if (workspace(B, H, N, N > 0 ? N : 1, D, dtype, rope != nullptr) > SANA_NOALLOC_SCRATCH_BYTES)
+    return SANA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const int rc = scratch_address(&ws);
+  if (rc != SANA_OK) return rc;
+  return attend(q, k, v, o, nullptr, nullptr, kv_in, ksum_in, kv_out, ksum_out, B, H, N, N > 0 ? N : 1, D, dtype,
+                eps, rope, ws, SANA_NOALLOC_SCRATCH_BYTES, hip_stream);
 }
 
 int sana_linattn_block_forward_strided(const void* q, const void* k, const void* v, void* o, const sana_layout* in,

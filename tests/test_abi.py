@@ -76,6 +76,22 @@ def _fwd(q=A, k=Bp, v=C, o=Dp, B=1, H=2, N=64, D=32, dt=la.SANA_DT_BF16, eps=1e-
     return la.lib().sana_linattn_forward(q, k, v, o, B, H, N, D, dt, eps, rope, ws, nbytes, None)
 
 
+def test_noalloc_rejects_calls_beyond_its_scratch():
+    """More heads than the static scratch array holds: SANA_ERR_WORKSPACE before
+    any device call (the pointers are fake)."""
+    L = la.lib()
+    limit = la.binding.NOALLOC_SCRATCH_BYTES
+    for B, H, N in [(1, 4000, 64), (2, 1000, 5000), (1, 2000, 16384)]:
+        assert la.workspace_bytes(B, H, N) > limit
+        rc = L.sana_linattn_block_forward_noalloc(A, Bp, C, Dp, None, None, None, None, B, H, N, 32,
+                                                  la.SANA_DT_BF16, 1e-6, None, None)
+        assert rc == la.SANA_ERR_WORKSPACE, (B, H, N, rc)
+    # the workloads this build measures fit
+    for B, H, N in [(1, 70, 4680), (1, 70, 16384), (1, 70, 18480), (4, 36, 1024)]:
+        for rope in (False, True):
+            assert la.workspace_bytes(B, H, N, has_rope=rope) <= limit
+
+
 def test_forward_argument_errors():
     E = la
     assert _fwd(q=None) == E.SANA_ERR_INVALID
