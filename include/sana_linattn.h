@@ -47,15 +47,19 @@
  *              without waiting for it.
  *   Workspace  `ws` is device scratch of at least
  *              sana_linattn_workspace_bytes(...) bytes, 256-byte aligned, with
- *              no initial contents required.  Calls that overlap in time must
- *              use different workspaces.
+ *              no initial contents required.  The part of it a call writes
+ *              (its workspace_bytes) may overlap none of the call's tensors,
+ *              states or RoPE tables (SANA_ERR_INVALID).  Calls that overlap
+ *              in time must use different workspaces.
  *   Errors     Arguments are checked before anything is enqueued; on error
  *              nothing is launched and a negative sana_status is returned:
  *                SANA_ERR_INVALID      NULL pointer where work exists, B, H or
  *                                      N negative, chunk <= 0, D <= 0, unknown dtype,
  *                                      non-finite or negative eps, misaligned
- *                                      pointer, O overlapping Q/K/V, RoPE rows
- *                                      out of the table, size overflow
+ *                                      pointer, O overlapping Q/K/V, a
+ *                                      workspace overlapping a buffer of the
+ *                                      call, RoPE rows out of the table, size
+ *                                      overflow
  *                SANA_ERR_UNSUPPORTED  D != 32
  *                SANA_ERR_WORKSPACE    ws NULL or ws_bytes too small
  *                SANA_ERR_HIP          a launch reported a HIP error

@@ -29,6 +29,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <initializer_list>
 #include <mutex>
 #include <type_traits>
 
@@ -185,6 +186,34 @@ int check_workspace(const Geometry& g, const void* ws, size_t ws_bytes) {
 }
 
 int check_tensor(const void* p) { return (p && aligned(p, 16)) ? SANA_OK : SANA_ERR_INVALID; }
+
+// An address span [p, p + bytes) a call reads or writes.
+struct Span {
+  const void* p;
+  size_t bytes;
+};
+
+// Bytes of the RoPE tables a call reads (none without RoPE).
+size_t rope_table_bytes(const sana_rope* rope) {
+  if (!rope) return 0;
+  if (rope->grid[0] || rope->grid[1] || rope->grid[2])
+    return (size_t)((int64_t)rope->grid[0] * rope->pairs[0] + (int64_t)rope->grid[1] * rope->pairs[1] +
+                    (int64_t)rope->grid[2] * rope->pairs[2]) * sizeof(float);
+  return (size_t)rope->n_pos * (la::kD / 2) * sizeof(float);
+}
+
+// The part of the workspace a call writes may overlap none of the tensors,
+// states or tables it touches.
+int check_workspace_overlaps(const void* ws, size_t used, std::initializer_list<Span> spans,
+                             const sana_rope* rope) {
+  for (const Span& t : spans)
+    if (overlaps(ws, used, t.p, t.bytes)) return SANA_ERR_INVALID;
+  if (rope) {
+    const size_t tab = rope_table_bytes(rope);
+    if (overlaps(ws, used, rope->cos, tab) || overlaps(ws, used, rope->sin, tab)) return SANA_ERR_INVALID;
+  }
+  return SANA_OK;
+}
 
 // A tensor's element layout and the bytes from its first element to one past
 // its last.
@@ -428,6 +457,15 @@ int attend(const void* q, const void* k, const void* v, void* o, const sana_layo
   if ((rc = check_rope(rope, N)) != SANA_OK) return rc;
   const Geometry g = make_geometry(bh, N, L, rope != nullptr);
   if ((rc = check_workspace(g, ws, ws_bytes)) != SANA_OK) return rc;
+  {
+    const size_t kv_bytes = (size_t)bh * 1024 * sizeof(float), ks_bytes = (size_t)bh * 32 * sizeof(float);
+    if ((rc = check_workspace_overlaps(ws, g.total_bytes,
+                                       {{q, vin.span}, {k, vin.span}, {v, vin.span}, {o, vout.span},
+                                        {kv_in, kv_bytes}, {ksum_in, ks_bytes}, {kv_out, kv_bytes},
+                                        {ksum_out, ks_bytes}},
+                                       rope)) != SANA_OK)
+      return rc;
+  }
 
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   const la::StateArgs a = state_args(ws, g, kv_in, ksum_in, kv_out, ksum_out);
@@ -559,6 +597,13 @@ int backward(const void* q, const void* k, const void* v, const void* dout, void
   if ((rc = check_rope(rope, N)) != SANA_OK) return rc;
   const Geometry g = make_geometry(bh, N, L, rope != nullptr);
   if ((rc = check_workspace(g, ws, ws_bytes)) != SANA_OK) return rc;
+  if ((rc = check_workspace_overlaps(ws, g.total_bytes,
+                                     {{q, ibytes}, {k, ibytes}, {v, ibytes}, {dout, ibytes}, {dq, obytes},
+                                      {dk, obytes}, {dv, obytes}, {kv_in, kv_bytes}, {ksum_in, ks_bytes},
+                                      {dkv_out, kv_bytes}, {dksum_out, ks_bytes}, {dkv_in, kv_bytes},
+                                      {dksum_in, ks_bytes}},
+                                     rope)) != SANA_OK)
+    return rc;
 
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   const la::StateArgs fwd = state_args(ws, g, kv_in, ksum_in, nullptr, nullptr);
@@ -779,6 +824,10 @@ int sana_linattn_state_update(const void* k, const void* v, float* kv_state, flo
   if ((rc = check_rope(rope, N)) != SANA_OK) return rc;
   const Geometry g = make_geometry(bh, N, N, rope != nullptr);
   if ((rc = check_workspace(g, ws, ws_bytes)) != SANA_OK) return rc;
+  if ((rc = check_workspace_overlaps(ws, g.total_bytes,
+                                     {{k, bytes}, {v, bytes}, {kv_state, kv_bytes}, {ksum_state, ks_bytes}},
+                                     rope)) != SANA_OK)
+    return rc;
 
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   const la::Layout flat{(int64_t)H * N * D, N * D, D, H};
@@ -912,6 +961,11 @@ int sana_linattn_project_state(const void* x, const void* w_k, const void* w_v, 
   if ((rc = check_rope(rope, N)) != SANA_OK) return rc;
   if (!ws || ws_bytes < g.total_bytes) return SANA_ERR_WORKSPACE;
   if (!aligned(ws, 256)) return SANA_ERR_INVALID;
+  if ((rc = check_workspace_overlaps(ws, g.total_bytes,
+                                     {{x, x_bytes}, {w_k, w_bytes}, {w_v, w_bytes}, {kv_state, kv_bytes},
+                                      {ksum_state, ks_bytes}},
+                                     rope)) != SANA_OK)
+    return rc;
 
   la::ProjArgs p;
   p.x = static_cast<const char*>(x);

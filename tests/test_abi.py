@@ -466,6 +466,38 @@ def test_backward_argument_errors_and_workspace():
     assert bws(nbytes=16) == la.SANA_ERR_WORKSPACE
 
 
+def test_workspace_may_not_overlap_the_call_buffers():
+    """The part of the workspace a call writes may overlap none of its tensors,
+    states or RoPE tables: SANA_ERR_INVALID before anything is launched."""
+    L = la.lib()
+    E = la.SANA_ERR_INVALID
+    assert _fwd(ws=A) == E                      # over q
+    assert _fwd(ws=A + 4096) == E               # inside q (2 heads x 64 tokens x 64 B = 8 KiB)
+    assert _fwd(ws=Dp) == E                     # over o
+    assert _fwd(ws=Bp + 256) == E               # inside k
+    tables = sana_rope(WS + 1024, 0x70000000, 64, 0)   # cos table inside the workspace
+    assert _fwd(rope=ctypes.byref(tables), nbytes=la.workspace_bytes(1, 2, 64, has_rope=True)) == E
+    tables = sana_rope(0x60000000, WS, 64, 0)          # sin table at the workspace
+    assert _fwd(rope=ctypes.byref(tables), nbytes=la.workspace_bytes(1, 2, 64, has_rope=True)) == E
+    # a workspace right after q's last byte is fine as far as overlaps go (the
+    # call then fails later only because the pointers are fake: not tested)
+    n = la.workspace_bytes(1, 2, 64)
+    S, Z = 0x68000000, 0x68100000
+    assert L.sana_linattn_block_forward(A, Bp, C, Dp, S, Z, S, Z, 1, 2, 64, 32, la.SANA_DT_BF16, 1e-6, None, S, n,
+                                        None) == E              # over the state it commits
+    assert L.sana_linattn_block_forward(A, Bp, C, Dp, None, None, S, Z, 1, 2, 64, 32, la.SANA_DT_BF16, 1e-6, None,
+                                        Z - 256, n, None) == E  # runs into the key sum
+    assert L.sana_linattn_state_update(A, Bp, C, Dp, 1, 2, 64, 32, la.SANA_DT_BF16, None, C, n, None) == E
+    assert L.sana_linattn_state_update(A, Bp, C, Dp, 1, 2, 64, 32, la.SANA_DT_BF16, None, Bp, n, None) == E
+    nb = la.backward_workspace_bytes(1, 2, 640, 64)
+    dQ = 0x60000000
+    assert L.sana_linattn_backward(A, Bp, C, Dp, dQ, dQ + 0x01000000, dQ + 0x02000000, None, None, None, None, None,
+                                   None, 1, 2, 640, 64, 32, la.SANA_DT_BF16, 1e-6, None, dQ, nb, None) == E
+    npj = la.project_state_workspace_bytes(1, 2, 1000, 64)
+    assert L.sana_linattn_project_state(A, Bp, C, Dp, Dp + 8192, 1, 2, 1000, 64, 32, la.SANA_DT_BF16, None, A + 512,
+                                        npj, None) == E    # inside x
+
+
 def test_strided_layout_validation():
     """Layout errors come back before anything is launched; a valid packed
     layout passes the checks and is stopped by the undersized workspace."""
