@@ -18,7 +18,9 @@ Prints ONE JSON line.  `roofline` describes the dominant kernel, the apply
 pass (apply_bf16): after the main timed region it is launched on its own,
 through sana_linattn_apply on the state the forward computes, in the same
 launch configuration, and timed with HIP events on the launch stream.
-`cpu_baseline` times the float64 oracle on the host cores.
+`cpu_baseline` times the float64 oracle on the host cores, in a child process
+whose BLAS/OpenMP thread counts are set, before NumPy loads, to the cores this
+process may run on.
 """
 
 import argparse
@@ -27,6 +29,8 @@ import hashlib
 import json
 import math
 import os
+import statistics
+import subprocess
 import sys
 import time
 
@@ -84,38 +88,97 @@ def make_rope(la, w, dev, form):
     return la.rope3d_axes_device(*w.grid, dev) if form == "axes" else la.rope3d_device(*w.grid, dev)
 
 
-def cpu_baseline(w, x, budget_s):
-    """Time the float64 oracle on the host on the same workload's inputs."""
+def cpu_model():
+    """The host CPU's model string, from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(spec, budget_s):
+    """Time the float64 oracle on the host: a child process (this script with
+    --cpu-worker) runs it with OMP/OpenBLAS/MKL thread counts set, before NumPy
+    is imported, to the cores this process may use.  Input generation is not
+    timed; the result is the median run, over at least 3 runs and about
+    `budget_s` seconds (one run if a run takes more than 10 s)."""
+    cores = len(os.sched_getaffinity(0))
+    env = dict(os.environ, OMP_NUM_THREADS=str(cores), OPENBLAS_NUM_THREADS=str(cores), MKL_NUM_THREADS=str(cores))
+    res = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-worker",
+                          json.dumps(dict(spec, budget_s=budget_s))],
+                         env=env, capture_output=True, text=True, timeout=30 * budget_s + 600)
+    if res.returncode != 0:
+        raise RuntimeError(f"cpu baseline worker failed ({res.returncode}):\n{res.stderr[-2000:]}")
+    out = json.loads(res.stdout.strip().splitlines()[-1])
+    out.update(cores=out.pop("threads"), cpu=cpu_model(), affinity_cores=cores)
+    return out
+
+
+def cpu_worker(spec):
+    """Child process of cpu_baseline: times the oracle on one workload and prints
+    one JSON line."""
     import numpy as np
 
     import oracle
+    from workloads import PROJECTIONS, generate_projection, reduced
     try:
         from threadpoolctl import threadpool_info
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # threadpoolctl missing: report the affinity
-        threads = len(os.sched_getaffinity(0))
-    f = x.f64
-    angles = oracle.rope3d_angles(*w.grid) if w.mode == "rope" else None
-    # bounded sample: whole heads of the workload, as many as fit the budget
-    heads = w.H
-    t0 = time.perf_counter()
-    done = 0
-    runs = 0
-    while True:
-        h0 = (runs * heads) % w.H
-        sl = slice(h0, h0 + heads)
-        if w.mode == "block":
-            oracle.block_causal(f["q"][:, sl], f["k"][:, sl], f["v"][:, sl], w.chunk, w.eps)
+    except Exception:  # threadpoolctl missing: the thread count the environment asks for
+        threads = int(os.environ.get("OPENBLAS_NUM_THREADS", "1"))
+    if spec["kind"] == "attention":
+        w = WORKLOADS[spec["workload"]]
+        f = generate(w).f64
+        angles = oracle.rope3d_angles(*w.grid) if w.mode == "rope" else None
+
+        def run():
+            if w.mode == "block":
+                oracle.block_causal(f["q"], f["k"], f["v"], w.chunk, w.eps)
+            else:
+                oracle.linattn(f["q"], f["k"], f["v"], w.eps, angles=angles)
+        units = w.token_heads
+        what = f"the whole workload ({w.B * w.H} heads x {w.N} tokens)"
+    else:
+        p = reduced(PROJECTIONS["sana16b_4096px_kv_proj"], name=spec["name"], N=spec["N"])
+        angles = oracle.rope3d_angles(*spec["grid"]) if spec["grid"] else None
+        query = spec["query"]
+        f = generate_projection(p, names=("x", "w_q") if query else ("x", "w_k", "w_v")).f64
+        heads = 2
+        counter = {"run": 0}
+        if query:
+            wq = f["w_q"].reshape(p.H, 32, p.C).transpose(0, 2, 1)
+            rng = np.random.default_rng(1)
+            S = rng.standard_normal((p.B, heads, 32, 32)) * 50
+            z = rng.random((p.B, heads, 32)) * 4000 + 10
         else:
-            oracle.linattn(f["q"][:, sl], f["k"][:, sl], f["v"][:, sl], w.eps, angles=angles)
-        done += w.B * heads * w.N
-        runs += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or runs >= 50:
+            wk = f["w_k"].reshape(p.H, 32, p.C).transpose(0, 2, 1)
+            wv = f["w_v"].reshape(p.H, 32, p.C).transpose(0, 2, 1)
+
+        def run():
+            h0 = (counter["run"] * heads) % p.H
+            counter["run"] += 1
+            if query:
+                oracle.projected_apply(f["x"], wq[h0:h0 + heads], S, z, 1e-6, angles)
+            else:
+                oracle.projected_kv_state(f["x"], wk[h0:h0 + heads], wv[h0:h0 + heads], angles)
+        units = p.B * heads * p.N
+        what = f"{heads} heads x {p.N} tokens (C={p.C}) of this layer per run"
+    times = []
+    while len(times) < 3 or (sum(times) < spec["budget_s"] and len(times) < 2000):
+        t0 = time.perf_counter()
+        run()
+        times.append(time.perf_counter() - t0)
+        if len(times) == 1 and times[0] > 10.0:
             break
-    return {"value": done / el, "unit": UNIT, "cores": threads, "kind": "oracle",
-            "sample": f"{runs} run(s) of the float64 oracle over all {w.H} heads x {w.N} tokens "
-                      f"(B={w.B}) of this workload, {el:.1f} s on the host"}
+    med = statistics.median(times)
+    print(json.dumps({"value": units / med, "unit": UNIT, "threads": threads, "kind": "oracle",
+                      "runs": len(times), "median_run_s": med,
+                      "sample": f"float64 oracle over {what}; median of {len(times)} runs "
+                                f"({sum(times):.1f} s of CPU work), input generation not timed"}), flush=True)
 
 
 def step_percentiles(step, steps, first, stream):
@@ -328,9 +391,8 @@ def project_bench(args, dev, stream):
         "kernel_source_hash": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:
-        import oracle
-        angles = None if rope is None else oracle.rope3d_angles(*w.grid)
-        rec["cpu_baseline"] = project_cpu_baseline(p, args.cpu_budget, angles)
+        rec["cpu_baseline"] = cpu_baseline({"kind": "project", "query": False, "name": p.name, "N": p.N,
+                                            "grid": list(w.grid) if rope is not None else None}, args.cpu_budget)
     print(json.dumps(rec), flush=True)
 
 
@@ -436,51 +498,9 @@ def project_apply_bench(args, dev, stream):
         "kernel_source_hash": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:
-        import oracle
-        angles = None if rope is None else oracle.rope3d_angles(*w.grid)
-        rec["cpu_baseline"] = project_cpu_baseline(p, args.cpu_budget, angles, query=True)
+        rec["cpu_baseline"] = cpu_baseline({"kind": "project", "query": True, "name": p.name, "N": p.N,
+                                            "grid": list(w.grid) if rope is not None else None}, args.cpu_budget)
     print(json.dumps(rec), flush=True)
-
-
-def project_cpu_baseline(p, budget_s, angles=None, query=False):
-    """The float64 oracle's projected_kv_state on the host (keys rotated by
-    `angles` if given), or with `query` its projected_apply against a fixed
-    state, over whole heads of the same layer until the budget is spent."""
-    import numpy as np
-
-    import oracle
-    from workloads import generate_projection
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([q.get("num_threads", 1) for q in threadpool_info()] or [1])
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
-    f = generate_projection(p, names=("x", "w_q") if query else ("x", "w_k", "w_v")).f64
-    C = p.C
-    heads, done, runs = 2, 0, 0
-    if query:
-        wq = f["w_q"].reshape(p.H, 32, C).transpose(0, 2, 1)
-        rng = np.random.default_rng(1)
-        S = rng.standard_normal((p.B, heads, 32, 32)) * 50
-        z = rng.random((p.B, heads, 32)) * 4000 + 10
-    else:
-        wk = f["w_k"].reshape(p.H, 32, C).transpose(0, 2, 1)
-        wv = f["w_v"].reshape(p.H, 32, C).transpose(0, 2, 1)
-    t0 = time.perf_counter()
-    while True:
-        h0 = (runs * heads) % p.H
-        if query:
-            oracle.projected_apply(f["x"], wq[h0:h0 + heads], S, z, 1e-6, angles)
-        else:
-            oracle.projected_kv_state(f["x"], wk[h0:h0 + heads], wv[h0:h0 + heads], angles)
-        done += p.B * heads * p.N
-        runs += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or runs >= 5000:
-            break
-    return {"value": done / el, "unit": "tokens·heads/s", "cores": threads, "kind": "oracle",
-            "sample": f"{runs} run(s) of the float64 oracle over {heads} heads x {p.N} tokens (C={C}) of this "
-                      f"layer, {el:.1f} s on the host"}
 
 
 def backward_bench(w, args, dev, stream):
@@ -729,9 +749,13 @@ def main():
     ap.add_argument("--rope-form", choices=["table", "axes"], default="axes",
                     help="RoPE workload: axes = the 3D RoPE's per-axis tables, staged in LDS by each workgroup (the "
                          "default); table = full [pos][16] cos/sin tables, streamed per head")
+    ap.add_argument("--cpu-worker", default=None, help=argparse.SUPPRESS)
     ap.add_argument("--copy-probe", action="store_true",
                     help="time a plain 1 GiB device-to-device copy instead (HBM reference and counter scale)")
     args = ap.parse_args()
+    if args.cpu_worker is not None:
+        cpu_worker(json.loads(args.cpu_worker))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
@@ -975,8 +999,7 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        xf = generate(w)
-        rec["cpu_baseline"] = cpu_baseline(w, xf, args.cpu_budget)
+        rec["cpu_baseline"] = cpu_baseline({"kind": "attention", "workload": w.name}, args.cpu_budget)
     print(json.dumps(rec), flush=True)
 
 
