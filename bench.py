@@ -203,23 +203,57 @@ def step_percentiles(step, steps, first, stream):
 
 
 def copy_probe(steps, warmup, nbytes=2 ** 30):
-    """A plain copy kernel of known size: reads and writes `nbytes` per launch."""
+    """HBM ceilings of this part, each on buffers far larger than the 256 MB
+    MALL: a plain 1 GiB device copy (torch copy_: reads and writes `nbytes`;
+    also the kernel whose FETCH_SIZE / WRITE_SIZE counters scale the traffic
+    figures), a pure 1 GiB write (torch fill_), a 1 GiB read reduced to one
+    number (torch sum), and this library's read-only state pass over a large
+    K, V (70 heads x 65536 tokens, 587 MB, sana_linattn_state_update)."""
     import torch
+
+    import linear_attention_diffusion_amd as la
     dev = torch.device("cuda:0")
     src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
     dst = torch.empty_like(src)
-    for _ in range(warmup):
-        dst.copy_(src)
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(steps):
-        dst.copy_(src)
-    b.record()
-    torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / steps
+
+    def timed(fn, n=steps):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(n):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    ms_copy = timed(lambda: dst.copy_(src))
+    ms_fill = timed(lambda: dst.fill_(2.0))
+    ms_sum = timed(lambda: src.sum())
+    H, N = 70, 65536
+    g = torch.Generator(device="cpu").manual_seed(1)
+    kv = [tuple((torch.randn(1, H, N, 32, generator=g) * 0.5).to(torch.bfloat16).to(dev) for _ in range(2))
+          for _ in range(2)]
+    S = torch.zeros(1, H, 32, 32, device=dev)
+    z = torch.zeros(1, H, 32, device=dev)
+    ws = la.make_workspace(1, H, N, dev)
+    it = [0]
+
+    def state():
+        k, v = kv[it[0] % 2]
+        it[0] += 1
+        la.sana_linattn_state_update(k, v, S, z, workspace=ws)
+    ms_state = timed(state)
+    kv_bytes = 2 * H * N * 32 * 2
+
+    def gbps(b, ms):
+        return b / (ms / 1e3) / 1e9
     print(json.dumps({"copy_probe_bytes_read": nbytes, "copy_probe_bytes_written": nbytes,
-                      "ms_per_copy": ms, "gbps_read_plus_write": 2 * nbytes / (ms / 1e3) / 1e9}), flush=True)
+                      "ms_per_copy": ms_copy, "gbps_read_plus_write": gbps(2 * nbytes, ms_copy),
+                      "fill_gbps_write": gbps(nbytes, ms_fill), "sum_gbps_read": gbps(nbytes, ms_sum),
+                      "state_pass_gbps_read": gbps(kv_bytes, ms_state), "state_pass_bytes": kv_bytes,
+                      "state_pass_ms": ms_state}), flush=True)
 
 
 def conv_bench(args, dev, stream):
@@ -275,6 +309,71 @@ def conv_bench(args, dev, stream):
         "roofline": {"bound": "hbm", "kernel": "temporal_conv3", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": stored_traffic("conv_480p_chunk"),
                      "algorithmic_bytes_per_launch": alg, "avg_launch_ms": ms},
+        "kernel_source_hash": kernel_source_hash(),
+    }), flush=True)
+
+
+def block_infer_bench(args, dev, stream):
+    """Time one chunk of block linear diffusion inference ("SANA-Video" paper
+    notes, section 4): T denoising passes that read the cache, then the commit
+    pass, through one synthetic layer (QKV projection + attention through the
+    cache, output projection + residual, temporal conv through its cache) at
+    the 480p chunk: 3 latent frames of 30 x 52 tokens, 70 heads of 32, the
+    Sana-1.6B width C = 2240, bf16.  T = 4 (the pages give no step count).
+    Timed with the fused projection kernels (project_state + project_apply)
+    and, beside it, the unfused path (one torch GEMM for Q, K, V, then
+    block_forward), alternating, the second round reported.  Chunk inputs are
+    cycled; the layer's weights stay the same, as in inference."""
+    import torch
+
+    from linear_attention_diffusion_amd import block_infer
+
+    B, H, C, F, S, T = 1, 70, 2240, 3, 30 * 52, 4
+    N = F * S
+    layers = {fused: [block_infer.SyntheticLayer(C, H, dev, seed=1, fused=fused)] for fused in (True, False)}
+    g = torch.Generator(device="cpu").manual_seed(5)
+    n_sets = 8
+    noise = [(torch.randn(B, N, C, generator=g)).to(torch.bfloat16).to(dev) for _ in range(n_sets)]
+    step_noise = [[(torch.randn(B, N, C, generator=g)).to(torch.bfloat16).to(dev) for _ in range(T - 1)]
+                  for _ in range(n_sets)]
+    timesteps = [(j + 1) / T for j in range(T)]
+
+    def chunk(fused, i, caches):
+        x = noise[i % n_sets]
+        for j in range(T, 0, -1):
+            y0 = block_infer.run_model(layers[fused], caches, x, F, commit=False)
+            if j == 1:
+                block_infer.run_model(layers[fused], caches, y0, F, commit=True)
+            else:
+                t = timesteps[j - 2]
+                x = (1.0 - t) * y0 + t * step_noise[i % n_sets][T - j]
+
+    def timed(fused):
+        caches = [block_infer.BlockCache(B, H, S, C, torch.bfloat16, dev)]
+        for i in range(args.warmup):
+            chunk(fused, i, caches)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.steps):
+            chunk(fused, args.warmup + i, caches)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    ms = {}
+    for _ in range(2):
+        for fused in (True, False):
+            ms[fused] = timed(fused)
+    print(json.dumps({
+        "metric": "block-inference chunk (T denoising passes + commit, 1 synthetic layer) latent tokens/s",
+        "value": N / (ms[True] / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms[True], "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) bf16 chunk noise, N(0,1/C) bf16 weights, random conv filters",
+        "config": {"workload": "480p chunk, one layer", "pass": "block_infer", "B": B, "H": H, "C": C, "frames": F,
+                   "spatial": S, "T": T, "input_sets_cycled": n_sets},
+        "per_chunk_ms": {"fused_projections": ms[True], "unfused_gemm_then_block_forward": ms[False]},
+        "fused_speedup": ms[False] / ms[True],
         "kernel_source_hash": kernel_source_hash(),
     }), flush=True)
 
@@ -736,12 +835,15 @@ def main():
     ap.add_argument("--block-mode", choices=["chunks", "sequence"], default="chunks",
                     help="block-causal workload: one block_forward call per chunk (inference, the default) or "
                          "one block_causal call over the whole sequence (all chunks known at once)")
-    ap.add_argument("--pass", dest="which", choices=["forward", "backward", "conv", "project", "project_apply"], default="forward",
+    ap.add_argument("--pass", dest="which", choices=["forward", "backward", "conv", "project", "project_apply",
+                                                     "block_infer"], default="forward",
                     help="forward (the default; the headline metric) or backward: one sana_linattn_backward "
                          "call per step (dQ, dK, dV; whole sequence in block-causal chunks for that workload); "
                          "conv: the block-inference temporal conv; project: the key/value projection fused "
                          "with the state update (Sana-1.6B 4096 px layer, or video720p_rope3d with its RoPE); "
-                         "project_apply: the query projection fused with the apply step (same layers)")
+                         "project_apply: the query projection fused with the apply step (same layers); "
+                         "block_infer: one chunk of block inference (denoising passes + commit) through a "
+                         "synthetic layer, fused projections against the unfused path")
     ap.add_argument("--layout", choices=["bhnd", "packed"], default="bhnd",
                     help="bhnd = contiguous [B, H, N, D] (the default); packed = Q, K, V (and dO for the backward) "
                          "read as strided views of one [B, N, 3 (4), H, D] projection-style buffer and O (dQ, dK, "
@@ -786,6 +888,9 @@ def main():
         return
     if args.which == "project_apply":
         project_apply_bench(args, dev, stream)
+        return
+    if args.which == "block_infer":
+        block_infer_bench(args, dev, stream)
         return
 
     x = generate(w, with_f64=False)

@@ -11,10 +11,16 @@ earlier chunk through O(D^2) state and one frame, never through earlier tokens.
 
 The layers here are synthetic (seeded random weights): no trained model is
 available, and the point is the control flow and the cache.  Each layer is
-    QKV projection  ->  block-causal linear attention through the cache
-    (read from the packed projection output with no relayout)
+    QKV projection + block-causal linear attention through the cache
     ->  output projection + residual  ->  temporal conv through the conv cache
-and ignores the timestep.  Readings where the pages leave a step open: the
+and ignores the timestep.  The attention runs in the fused projection kernels
+("Sana" research note, Infra: ReLU(K)^T V fused with the QKV projection):
+sana_linattn_project_state adds the chunk's phi~(K)^T V and phi(K) to a copy of
+the carried state (to the cache itself on the commit pass) without writing K or
+V, and sana_linattn_project_apply computes O from the queries' projection
+against that state without writing Q -- the same as block_forward on the
+projected Q, K, V.  With fused=False the layer instead projects with one torch
+GEMM and runs block_forward on strided views of its packed output.  Readings where the pages leave a step open: the
 noise schedule is the flow-matching interpolation x_t = (1 - t) x0 + t eps
 (SANA's flow objective), and the model output is taken as the prediction of
 the clean chunk.  Every attention and convolution step runs in this library's
@@ -37,20 +43,55 @@ class BlockCache:
         self.ksum = torch.zeros(B, H, 32, device=device)
         self.conv = torch.zeros(B, spatial, C, dtype=dtype, device=device)
         self.committed = False
+        # a denoising pass's state: the carried state plus the chunk, not committed
+        self.step_kv = torch.empty_like(self.kv)
+        self.step_ksum = torch.empty_like(self.ksum)
 
 
 class SyntheticLayer:
-    """A DiT-style layer with seeded random weights (see the module note)."""
+    """A DiT-style layer with seeded random weights (see the module note).
 
-    def __init__(self, C, H, device, seed, dtype=None):
+    The QKV weight is a linear layer's [3 H 32, C] matrix: rows h*32 + d of
+    w_q, w_k, w_v (its three row blocks) give feature d of head h."""
+
+    def __init__(self, C, H, device, seed, dtype=None, fused=True):
         torch = _b._torch()
         dtype = dtype or torch.bfloat16
         g = torch.Generator().manual_seed(seed)
-        self.C, self.H = C, H
-        self.wqkv = (torch.randn(C, 3 * H * 32, generator=g) / math.sqrt(C)).to(dtype).to(device)
+        self.C, self.H, self.fused = C, H, fused
+        w = (torch.randn(3 * H * 32, C, generator=g) / math.sqrt(C)).to(dtype).to(device)
+        self.wq, self.wk, self.wv = (w[i * H * 32:(i + 1) * H * 32] for i in range(3))
+        self.wqkv_t = w.t().contiguous()          # [C, 3 H 32] for the unfused projection
         self.wo = (torch.randn(H * 32, C, generator=g) / math.sqrt(H * 32)).to(dtype).to(device)
         self.conv_w = (torch.randn(C, 3, generator=g) * 0.25).to(device)
         self.conv_b = (torch.randn(C, generator=g) * 0.05).to(device)
+        # when a list: every attention call appends (x, carried kv, carried ksum,
+        # the state the fused apply read (kv, ksum) or None, o, commit, pos0),
+        # copies taken around the call (for inspection)
+        self.record = None
+
+    def attend(self, x, cache, commit, eps, rope, pos0, o):
+        """O of the chunk's tokens into o [B, N, H, 32]: the carried state plus the
+        chunk's own keys and values, committed to the cache when `commit`.
+        Returns the state the fused apply read (None on the unfused path)."""
+        r = None if rope is None else rope.at(pos0)
+        if self.fused:
+            if commit:
+                kv, ks = cache.kv, cache.ksum
+            else:
+                kv, ks = cache.step_kv, cache.step_ksum
+                kv.copy_(cache.kv)
+                ks.copy_(cache.ksum)
+            _b.sana_linattn_project_state(x, self.wk, self.wv, kv, ks, rope=r)
+            _b.sana_linattn_project_apply(x, self.wq, kv, ks, o=o.permute(0, 2, 1, 3), eps=eps, rope=r)
+            return kv, ks
+        B, N, C = x.shape
+        qkv = (x.reshape(B * N, C) @ self.wqkv_t).view(B, N, 3, self.H, 32)
+        q, k, v = (qkv[:, :, i].permute(0, 2, 1, 3) for i in range(3))
+        _b.sana_linattn_block_forward(q, k, v, o=o.permute(0, 2, 1, 3), kv_in=cache.kv, ksum_in=cache.ksum,
+                                      kv_out=cache.kv if commit else None, ksum_out=cache.ksum if commit else None,
+                                      eps=eps, rope=r)
+        return None
 
     def __call__(self, x, cache, frames, commit, eps=1e-6, rope=None, pos0=0):
         """x: [B, frames * spatial, C] -> same shape.  commit: update the cache."""
@@ -58,12 +99,12 @@ class SyntheticLayer:
         B, N, C = x.shape
         H = self.H
         spatial = N // frames
-        qkv = (x.reshape(B * N, C) @ self.wqkv).view(B, N, 3, H, 32)
-        q, k, v = (qkv[:, :, i].permute(0, 2, 1, 3) for i in range(3))
         o = torch.empty(B, N, H, 32, dtype=x.dtype, device=x.device)
-        _b.sana_linattn_block_forward(q, k, v, o=o.permute(0, 2, 1, 3), kv_in=cache.kv, ksum_in=cache.ksum,
-                                      kv_out=cache.kv if commit else None, ksum_out=cache.ksum if commit else None,
-                                      eps=eps, rope=None if rope is None else rope.at(pos0))
+        carried = None if self.record is None else (cache.kv.clone(), cache.ksum.clone())
+        used = self.attend(x, cache, commit, eps, rope, pos0, o)
+        if self.record is not None:
+            used = None if used is None else (used[0].clone(), used[1].clone())
+            self.record.append((x.clone(), carried[0], carried[1], used, o.clone(), commit, pos0))
         h = x + (o.view(B * N, H * 32) @ self.wo).view(B, N, C)
         y = _b.sana_linattn_temporal_conv3(h.view(B, frames, spatial, C), self.conv_w, self.conv_b,
                                            cache_in=cache.conv if cache.committed else None,

@@ -12,7 +12,9 @@ one bf16 step.  The state's fp32 sums pass each product through at most
 31 + N / 32 + (partials) + 2 roundings, bounded by N / 32 + 200.  So, with
 A = |phi(K)|^T |V| over the tokens (the b's added in),
   |dS| <= b_K^T (|V| + b_V) + |phi(K)|^T b_V + 2 (N / 32 + 200) 2^-24 A,
-  |dz| <= sum b_K + 2 (N / 32 + 200) 2^-24 sum (|phi(K)| + b_K).
+  |dz| <= sum b_K + 2 (N / 32 + 200) 2^-24 sum (|phi(K)| + b_K),
+plus, when the call starts from a carried state S0 (z0), the same factor times
+|S0| (|z0|): it is the first term of those sums.
 With RoPE, S contracts the rotated keys y = R phi(K): y_d = x_d c -+ x_d' s
 (d' = d ^ 1), taken in fp32 from float32 cos/sin and split into three bf16
 parts.  Against the oracle's float64 rotation, |dy_d| <= b_d + b_d' +
@@ -88,6 +90,11 @@ def check_projected_state(kv, z, x, heads=None, kv0=None, z0=None, any_order=Fal
     gam = 2.0 * ((1 if angles is None else 3) * N / 32 + 200) * U
     tol_S = np.matmul(byt, absV) + np.matmul(yt, bV) + gam * np.matmul(yt + byt, absV)
     tol_z = bK.sum(axis=-2) + gam * (phik + bK).sum(axis=-2)
+    if kv0 is not None:
+        # the carried state enters the same fp32 sums: each rounding is relative
+        # to the running total, which includes it
+        tol_S = tol_S + gam * np.abs(kv0)
+        tol_z = tol_z + gam * np.abs(z0)
     n_amb = int(np.count_nonzero(bK)) + int(np.count_nonzero(bV))
     lines = []
     for got, want, tol, name in ((kv, S, tol_S, "S"), (z, zr, tol_z, "z")):

@@ -2,6 +2,8 @@
 and of the block inference loop (against a float64 replica that rounds to
 bf16 where the device path stores bf16)."""
 
+from types import SimpleNamespace
+
 import numpy as np
 import pytest
 
@@ -11,7 +13,8 @@ from block_infer_ref import RefCache, RefLayer, bf
 from block_infer_ref import block_linear_diffusion as ref_loop
 from gpu_util import device, to_dev, to_np, torch_mod
 from linear_attention_diffusion_amd import block_infer
-from metrics import check, rel_l2
+from metrics import BF16_MAX_REL, BF16_REL_L2, check, rel_l2
+from proj_bound import check_projected_apply, check_projected_state
 from workloads import bf16_bits_from_f32
 
 pytestmark = pytest.mark.gpu
@@ -45,12 +48,12 @@ def test_temporal_conv_against_oracle(dtype, B, F, S, C, with_cache):
     assert np.array_equal(to_np(cache), last)          # in-place commit of the last frame
 
 
-def _setup(B=1, C=64, H=2, frames=2, grid_hw=(3, 4), M=3, T=3, layers=2, seed=3):
-    torch = torch_mod()
+def _setup(B=1, C=64, H=2, frames=2, grid_hw=(3, 4), M=3, T=3, layers=2, seed=3, fused=True):
     spatial = grid_hw[0] * grid_hw[1]
     N = frames * spatial
-    dev_layers = [block_infer.SyntheticLayer(C, H, device(), seed + i) for i in range(layers)]
-    ref_layers = [RefLayer(to_np(l.wqkv), to_np(l.wo), to_np(l.conv_w), to_np(l.conv_b), H) for l in dev_layers]
+    dev_layers = [block_infer.SyntheticLayer(C, H, device(), seed + i, fused=fused) for i in range(layers)]
+    ref_layers = [RefLayer(to_np(l.wq), to_np(l.wk), to_np(l.wv), to_np(l.wo), to_np(l.conv_w), to_np(l.conv_b), H)
+                  for l in dev_layers]
     rng = np.random.default_rng(seed)
     noise = bf(rng.standard_normal((M, B, N, C)).astype(np.float32))
     step_noise = bf(rng.standard_normal((M, T - 1, B, N, C)).astype(np.float32))
@@ -60,31 +63,109 @@ def _setup(B=1, C=64, H=2, frames=2, grid_hw=(3, 4), M=3, T=3, layers=2, seed=3)
                 grid=(M * frames, grid_hw[0], grid_hw[1]))
 
 
-@pytest.mark.parametrize("rope", [False, True])
-def test_block_inference_loop(rope):
+def _check_sum(got, want, mag, what):
+    """A cache part that is a sum of many terms (a carried state: a sum over
+    every committed token; the conv cache: a residual plus a projection)
+    against the replica: rel-L2 at the bf16 bar, and each element within 2e-2
+    of the sum of its terms' magnitudes, the scale of its rounding error (an
+    element that cancels to near zero keeps the absolute error of its terms,
+    which the bf16 rounding of the projections sets)."""
+    l2 = rel_l2(got, want)
+    worst = float(np.max(np.abs(got - want) / np.maximum(mag, 1e-30)))
+    print(f"{what}: rel-L2 {l2:.3e}, max error / term magnitude {worst:.3e}", flush=True)
+    assert np.all(np.isfinite(got)) and l2 <= BF16_REL_L2 and worst <= BF16_MAX_REL, what
+
+
+def _run_and_compare(s, rope, what, loop_bar=BF16_REL_L2):
+    """The device loop against the float64 replica.  Every attention call the
+    loop makes is checked per element on that call's own inputs (the device's
+    x and the carried state it read), which keeps rounding drift from earlier
+    calls out of the check.  Through the fused projections, the state the call
+    forms and the outputs it applies are each held to the element-wise bounds
+    derived for those kernels (tests/proj_bound.py: the bf16 bar plus the one
+    bf16 step a projected value next to a rounding boundary may take, fp32
+    against float64); the unfused path's outputs are held to the bf16 bar
+    against the oracle on bf16(x W^T).
+    The whole loop's output is held to the bf16 rel-L2 bar against the replica
+    run end to end, and every cache part as in _check_sum.  `loop_bar`, when
+    given, replaces those end-to-end checks by rel-L2 <= loop_bar (for the
+    unfused path, whose K and V come from torch's GEMM)."""
     torch = torch_mod()
-    s = _setup()
-    print(f"case block inference rope={rope}", flush=True)
     caches = [block_infer.BlockCache(s["B"], s["H"], s["spatial"], s["C"], torch.bfloat16, device())
               for _ in s["dev_layers"]]
+    for layer in s["dev_layers"]:
+        layer.record = []
     r = la.rope3d_device(*s["grid"], device()) if rope else None
     out = block_infer.block_linear_diffusion(s["dev_layers"], caches, _bf16_dev(s["noise"]),
                                              _bf16_dev(s["step_noise"]), s["timesteps"], s["frames"], rope=r)
-    ref_caches = [RefCache(s["B"], s["H"], s["spatial"], s["C"]) for _ in s["ref_layers"]]
     ang = oracle.rope3d_angles(*s["grid"]) if rope else None
+    B, N, H = s["B"], s["N"], s["H"]
+    for li, (layer, ref) in enumerate(zip(s["dev_layers"], s["ref_layers"])):
+        for ci, (x, kv_in, ks_in, used, o, commit, pos0) in enumerate(layer.record):
+            tag = f"{what}: layer {li} call {ci}"
+            o = to_np(o).transpose(0, 2, 1, 3)
+            if used is not None:
+                xs = SimpleNamespace(workload=SimpleNamespace(H=H, N=N),
+                                     f64={"x": to_np(x), "w_q": ref.wq, "w_k": ref.wk, "w_v": ref.wv})
+                ok, rep = check_projected_state(to_np(used[0]), to_np(used[1]), xs, kv0=to_np(kv_in),
+                                                z0=to_np(ks_in), angles=ang, pos_offset=pos0)
+                print(f"{tag} state: {rep}", flush=True)
+                assert ok, f"{tag} state: {rep}"
+                ok, rep = check_projected_apply(o, xs, to_np(used[0]), to_np(used[1]), 1e-6, angles=ang,
+                                                pos_offset=pos0)
+                print(f"{tag} attention: {rep}", flush=True)
+                assert ok, f"{tag} attention: {rep}"
+                continue
+            xf = to_np(x).reshape(B * N, s["C"])
+            q, k, v = (np.ascontiguousarray(bf(xf @ w.T).reshape(B, N, H, 32).transpose(0, 2, 1, 3))
+                       for w in (ref.wq, ref.wk, ref.wv))
+            want, _, _ = oracle.block_forward(q, k, v, to_np(kv_in), to_np(ks_in), 1e-6, ang, pos0)
+            check(o, want, "bf16", f"{tag} attention")
+        layer.record = None
+    ref_caches = [RefCache(s["B"], s["H"], s["spatial"], s["C"]) for _ in s["ref_layers"]]
     want = ref_loop(s["ref_layers"], ref_caches, s["noise"], s["step_noise"], s["timesteps"], s["frames"], 1e-6, ang)
-    err = rel_l2(to_np(out), want)
-    print(f"block inference rope={rope}: output rel-L2 {err:.3e}", flush=True)
-    assert err <= 1e-2
-    for c, rc in zip(caches, ref_caches):
-        assert rel_l2(to_np(c.kv), rc.S) <= 1e-2 and rel_l2(to_np(c.ksum), rc.z) <= 1e-2
-        assert rel_l2(to_np(c.conv), rc.conv) <= 1e-2
+    l2 = rel_l2(to_np(out), want)
+    print(f"{what}: loop output rel-L2 {l2:.3e}", flush=True)
+    assert l2 <= loop_bar
+    if loop_bar != BF16_REL_L2:
+        for c, rc in zip(caches, ref_caches):
+            for got, ref in ((c.kv, rc.S), (c.ksum, rc.z), (c.conv, rc.conv)):
+                assert rel_l2(to_np(got), ref) <= loop_bar
+        return
+    for i, (c, rc) in enumerate(zip(caches, ref_caches)):
+        _check_sum(to_np(c.kv), rc.S, rc.S_mag, f"{what}: layer {i} state S")
+        _check_sum(to_np(c.ksum), rc.z, rc.z, f"{what}: layer {i} key sum")
+        _check_sum(to_np(c.conv), rc.conv, rc.conv_mag, f"{what}: layer {i} conv cache")
+
+
+@pytest.mark.parametrize("rope", [False, True])
+@pytest.mark.parametrize("fused", [True, False])
+def test_block_inference_loop(rope, fused):
+    """fused=False (the benchmark's comparison path) projects Q, K, V with
+    torch's bf16 GEMM, whose results stray further from the bf16 rounding of
+    the exact products than an fp32-accumulated product does (on this stack
+    the carried state then differs by ~2.5e-3 rel-L2 after a few commits): its
+    attention calls are held to the same per-call bar, the end-to-end loop to
+    rel-L2 <= 1e-2."""
+    print(f"case block inference rope={rope} fused={fused}", flush=True)
+    _run_and_compare(_setup(fused=fused), rope, f"toy loop rope={rope} fused={fused}",
+                     BF16_REL_L2 if fused else 1e-2)
+
+
+def test_block_inference_loop_at_the_480p_chunk():
+    """The loop at a SANA-Video 480p chunk: 3 latent frames of 30 x 52 tokens,
+    70 heads, the Sana-1.6B width C = 2240, one layer, two chunks of two
+    denoising steps and a commit each, through the fused projections."""
+    print("case block inference 480p chunk", flush=True)
+    s = _setup(B=1, C=2240, H=70, frames=3, grid_hw=(30, 52), M=2, T=2, layers=1, seed=11)
+    _run_and_compare(s, False, "480p chunk loop")
 
 
 def test_denoising_steps_leave_the_cache_untouched():
     """Read-only calls (every denoising step) leave all three cache parts
-    bit-identical; the commit pass changes them; the committed attention state
-    equals state_update over the clean pass's keys and values."""
+    bit-identical; the commit pass changes them, and its attention state is
+    exactly the fused key/value projection of the clean pass added to the
+    carried state."""
     torch = torch_mod()
     s = _setup(M=1, T=2)
     caches = [block_infer.BlockCache(s["B"], s["H"], s["spatial"], s["C"], torch.bfloat16, device())
@@ -95,13 +176,8 @@ def test_denoising_steps_leave_the_cache_untouched():
     block_infer.run_model(s["dev_layers"], caches, x, s["frames"], commit=False)
     for c, (kv, z, conv) in zip(caches, snap):
         assert torch.equal(c.kv, kv) and torch.equal(c.ksum, z) and torch.equal(c.conv, conv)
-    # the commit adds exactly the layer's clean-pass keys and values
     layer, cache = s["dev_layers"][0], caches[0]
-    B, N, C, H = s["B"], s["N"], s["C"], s["H"]
-    qkv = (x.reshape(B * N, C) @ layer.wqkv).view(B, N, 3, H, 32)
-    k, v = (qkv[:, :, i].permute(0, 2, 1, 3).contiguous() for i in (1, 2))
     kv_want, z_want = snap[0][0].clone(), snap[0][1].clone()
-    la.sana_linattn_state_update(k, v, kv_want, z_want)
+    la.sana_linattn_project_state(x, layer.wk, layer.wv, kv_want, z_want)
     block_infer.run_model(s["dev_layers"][:1], caches[:1], x, s["frames"], commit=True)
-    assert rel_l2(to_np(cache.kv), to_np(kv_want)) <= 1e-6
-    assert rel_l2(to_np(cache.ksum), to_np(z_want)) <= 1e-6
+    assert torch.equal(cache.kv, kv_want) and torch.equal(cache.ksum, z_want)
