@@ -134,14 +134,30 @@ struct Rope {
   double inv_w, inv_hw;  // axis form: 1 / Wl and 1 / (Hl * Wl)
 };
 
-// Axis form: the workgroup copies the tables to LDS as (cos, sin) pairs, entry
-// i at floats 2i, 2i + 1; the caller synchronises before the first lookup.
+// Axis form: the workgroup copies the tables to LDS in duos.  Entries 2d and
+// 2d + 1 (with even pair counts per axis, two pairs of one axis at one
+// coordinate) go to floats 4d .. 4d+3 as cos 2d, cos 2d+1, sin 2d, sin 2d+1,
+// so one 16-byte read gives a duo's cosines and sines each in a register pair.
+// The caller synchronises before the first lookup.
 template <int ROPE>
 __device__ __forceinline__ void rope_stage(const Rope& r, float* lds, int tid, int nthreads) {
   if constexpr (ROPE == kRopeAxes) {
-    for (int i = tid; i < r.n_tab; i += nthreads)
-      *reinterpret_cast<float2*>(lds + 2 * i) = float2{r.cos[i], r.sin[i]};
+    for (int d = tid; d < r.n_tab / 2; d += nthreads)
+      *reinterpret_cast<f32x4_t*>(lds + 4 * d) =
+          f32x4_t{r.cos[2 * d], r.cos[2 * d + 1], r.sin[2 * d], r.sin[2 * d + 1]};
   }
+}
+
+// cos/sin of staged entry e
+__device__ __forceinline__ void axis_cs(const float* lds, int e, float& c, float& sn) {
+  const float* d = lds + 4 * (e >> 1) + (e & 1);
+  c = d[0];
+  sn = d[2];
+}
+
+// cos e, cos e+1, sin e, sin e+1 of the duo that starts at staged entry e (even)
+__device__ __forceinline__ f32x4_t axis_duo(const float* lds, int e) {
+  return *reinterpret_cast<const f32x4_t*>(lds + 2 * e);
 }
 
 // Latent coordinates of position pos (clamped to the call's last position),
@@ -155,7 +171,7 @@ __device__ __forceinline__ void rope_coords(const Rope& r, int64_t pos, int& t, 
   t = (int)__builtin_fma((double)n, r.inv_hw, 0.5 * r.inv_hw);
   const int rem = (int)n - t * (r.Hl * r.Wl);
   h = (int)__builtin_fma((double)rem, r.inv_w, 0.5 * r.inv_w);
-  w = rem - h * r.Wl;
+  w = rem - (int)__umul24(h, r.Wl);  // h Wl <= rem < Hl Wl < 2^20
 }
 
 // Where pair p's entry sits, as offset + t * wt + h * wh + w * ww: one of the
@@ -171,8 +187,11 @@ __device__ __forceinline__ AxisPair axis_pair(const Rope& r, int p) {
   return AxisPair{r.base_w + p - r.pt - r.ph, 0, 0, pw};
 }
 
+// 24-bit products (full rate): the one non-zero weight's coordinate times it
+// stays below the table size (at most kMaxAxisTab), and a zero weight gives 0
+// whatever the coordinate's high bits.
 __device__ __forceinline__ int axis_entry(const AxisPair& a, int t, int h, int w) {
-  return a.off + t * a.wt + h * a.wh + w * a.ww;
+  return (int)(__umul24(t, a.wt) + __umul24(h, a.wh) + __umul24(w, a.ww)) + a.off;
 }
 
 // A lane's pairs 4g .. 4g+3 as two duos (4g, 4g+1) and (4g+2, 4g+3): the axis
@@ -194,10 +213,10 @@ __device__ __forceinline__ void rope_axis_row4(const Rope& r, const float* lds, 
   rope_coords(r, pos, t, h, w);
 #pragma unroll
   for (int d = 0; d < 2; ++d) {
-    const f32x4_t e = *reinterpret_cast<const f32x4_t*>(lds + 2 * axis_entry(al.duo[d], t, h, w));
+    const f32x4_t e = axis_duo(lds, axis_entry(al.duo[d], t, h, w));
     c[2 * d] = e[0];
-    sn[2 * d] = e[1];
-    c[2 * d + 1] = e[2];
+    c[2 * d + 1] = e[1];
+    sn[2 * d] = e[2];
     sn[2 * d + 1] = e[3];
   }
 }
@@ -208,9 +227,7 @@ __device__ __forceinline__ void rope_pair(const Rope& r, const float* lds, int64
   if constexpr (ROPE == kRopeAxes) {
     int t, h, w;
     rope_coords(r, pos, t, h, w);
-    const float2 e = *reinterpret_cast<const float2*>(lds + 2 * axis_entry(axis_pair(r, p), t, h, w));
-    c = e.x;
-    sn = e.y;
+    axis_cs(lds, axis_entry(axis_pair(r, p), t, h, w), c, sn);
   } else {
     c = r.cos[pos * 16 + p];
     sn = r.sin[pos * 16 + p];
@@ -237,10 +254,6 @@ __device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(unsigned, v);
 }
 
-// x = hi + mid + lo with hi = bf16(x), mid = bf16(x - hi), lo = bf16(x - hi - mid);
-// each residual is exact in fp32 (x - bf16(x) has at most 16 significant
-// bits).  Called for a pair (a, b), each part comes back as one dword of two
-// packed bf16.
 // One RoPE pair rotation, (a, b) -> (a c - b s, a s + b c), with its fused
 // multiply-adds written out: left to the compiler, the contraction may fuse
 // either product of a c - b s depending on the surrounding code, and two
@@ -248,11 +261,39 @@ __device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
 __device__ __forceinline__ float rot_lo(float a, float b, float c, float s) { return __builtin_fmaf(a, c, -(b * s)); }
 __device__ __forceinline__ float rot_hi(float a, float b, float c, float s) { return __builtin_fmaf(a, s, b * c); }
 
+// A constant the compiler cannot see through, held in an SGPR.  The packed
+// bf16 operand below must reach the instruction as these exact bits: folded
+// into an inline constant, (-1.0, 0) is encoded as the fp32 inline -1.0, which
+// the hardware reads as (0, -1.0).
+__device__ __forceinline__ unsigned sgpr_constant(unsigned x) {
+  asm("" : "+s"(x));
+  return x;
+}
+
+// x minus the bf16 in the low (high) half of `packed`, as one bf16 dot product
+// (v_dot2c_f32_bf16) against (-1, 0) (against (0, -1)): both products are
+// exact and, for the bf16 rounding of x, so is the difference (x - bf16(x)
+// has at most 16 significant bits), so the instruction's one rounding changes
+// nothing.  It replaces an unpack and a subtraction.  The other half enters
+// as a product with 0, which is NaN only if that half is infinite.
+__device__ __forceinline__ float minus_lo_bf16(unsigned packed, float x) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, packed),
+                                         __builtin_bit_cast(bf16x2_t, sgpr_constant(0x0000bf80u)), x, false);
+}
+__device__ __forceinline__ float minus_hi_bf16(unsigned packed, float x) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, packed),
+                                         __builtin_bit_cast(bf16x2_t, sgpr_constant(0xbf800000u)), x, false);
+}
+
+// x = hi + mid + lo with hi = bf16(x), mid = bf16(x - hi), lo = bf16(x - hi - mid);
+// each residual is exact in fp32 (x - bf16(x) has at most 16 significant
+// bits).  Called for a pair (a, b), each part comes back as one dword of two
+// packed bf16.
 __device__ __forceinline__ void split3_bf16x2(float a, float b, unsigned& hi, unsigned& mid, unsigned& lo) {
   hi = pack_bf16x2(a, b);
-  const float ra = a - bf16lo_to_f32(hi), rb = b - bf16hi_to_f32(hi);
+  const float ra = minus_lo_bf16(hi, a), rb = minus_hi_bf16(hi, b);
   mid = pack_bf16x2(ra, rb);
-  lo = pack_bf16x2(ra - bf16lo_to_f32(mid), rb - bf16hi_to_f32(mid));
+  lo = pack_bf16x2(minus_lo_bf16(mid, ra), minus_hi_bf16(mid, rb));
 }
 
 __device__ __forceinline__ unsigned lo_halves(unsigned a, unsigned b) { return (a & 0xffffu) | (b << 16); }

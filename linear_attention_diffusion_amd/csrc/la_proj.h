@@ -107,9 +107,7 @@ __device__ __forceinline__ void proj_angles(const Rope& r, const float* rtab, co
     rope_coords(r, pos, t, h, w);
 #pragma unroll
     for (int fh = 0; fh < 2; ++fh) {
-      const float2 e = *reinterpret_cast<const float2*>(rtab + 2 * axis_entry(ap[fh], t, h, w));
-      c[fh] = e.x;
-      sn[fh] = e.y;
+      axis_cs(rtab, axis_entry(ap[fh], t, h, w), c[fh], sn[fh]);
     }
   } else {
 #pragma unroll
@@ -459,9 +457,9 @@ __global__ __launch_bounds__(kThreads, 2) void project_apply_bf16(ProjApplyArgs 
   const int sw = 16 * (g ^ proj_swz(n));
   const int a_rd = (128 * th + n) * 64 + sw;
   const int b_rd = kProjBOff + (64 * hh + n) * 64 + sw;
-  // RoPE: this lane's pairs are 2g, 2g + 1, 8 + 2g, 9 + 2g (its k-slot pairs)
-  const AxisPair ap[4] = {axis_pair(rp, 2 * g), axis_pair(rp, 2 * g + 1), axis_pair(rp, 8 + 2 * g),
-                          axis_pair(rp, 9 + 2 * g)};
+  // RoPE: this lane's pairs are 2g, 2g + 1, 8 + 2g, 9 + 2g (its k-slot pairs),
+  // two duos of the staged tables (pair counts per axis are even)
+  const AxisPair ap[2] = {axis_pair(rp, 2 * g), axis_pair(rp, 8 + 2 * g)};
   rope_stage<ROPE>(rp, rtab, tid, kThreads);
 
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
@@ -507,10 +505,12 @@ __global__ __launch_bounds__(kThreads, 2) void project_apply_bf16(ProjApplyArgs 
             int ct, chh, cw;
             rope_coords(rp, pos, ct, chh, cw);
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-              const float2 e = *reinterpret_cast<const float2*>(rtab + 2 * axis_entry(ap[q4], ct, chh, cw));
-              c[q4] = e.x;
-              sn[q4] = e.y;
+            for (int d = 0; d < 2; ++d) {
+              const f32x4_t e = axis_duo(rtab, axis_entry(ap[d], ct, chh, cw));
+              c[2 * d] = e[0];
+              c[2 * d + 1] = e[1];
+              sn[2 * d] = e[2];
+              sn[2 * d + 1] = e[3];
             }
           } else {
 #pragma unroll
