@@ -47,14 +47,15 @@ static __device__ __align__(256) unsigned char scratch[SANA_NOALLOC_SCRATCH_BYTE
 namespace {
 
 // MI355X: 256 compute units.  Both passes size their grids to one resident
-// round of workgroups, at the count that measured fastest on the Sana-1.6B
-// 4096 px layer: state 2 per CU (8 waves, each with a 64-token chunk of K and V
-// in flight; the RoPE variant's register use allows no more), apply 3 per CU
-// (2 with RoPE, for the same reason).
+// round of workgroups, at the count that measured fastest: state 2 per CU (8
+// waves, each with a 64-token chunk of K and V in flight; the RoPE variant's
+// register use allows no more), apply 3 per CU on the Sana-1.6B 4096 px layer
+// (4 were slower there), and 4 per CU with RoPE on the 720p layer, where each
+// wave computes longer per chunk and more waves keep more loads in flight.
 constexpr int64_t kCUs = 256;
 constexpr int64_t kStateGroups = kCUs * 2;
 constexpr int64_t kApplyGroups = kCUs * 3;
-constexpr int64_t kApplyGroupsRope = kCUs * 2;
+constexpr int64_t kApplyGroupsRope = kCUs * 4;
 constexpr int64_t kMaxSplits = 64;       // partial states per chunk
 constexpr int64_t kMinSplitTokens = 256;
 // With at least this many (head, chunk) items of at most kWholeChunkTokens
