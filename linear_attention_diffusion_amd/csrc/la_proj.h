@@ -4,23 +4,26 @@
 // Ahead of the attention, a layer projects its input x [B][N][C] into keys and
 // values, K = x W_k^T and V = x W_v^T (per head, 32 features each).  Unfused,
 // the projection GEMM writes K and V to HBM in bf16 and the state pass reads
-// them back.  Here one kernel computes a head pair's K and V tiles with MFMA
+// them back.  Here one kernel computes four heads' K and V tiles with MFMA
 // and contracts them into the heads' states on the spot, so K and V never
 // reach memory (the fusion of ReLU(K)^T V into the QKV projection that the
 // "Sana" research note lists under "Infra", there in an INT8 engine; here in
 // bf16).  The tiles are rounded to bf16, as a bf16 projection would store
 // them, and then contracted as in the state pass.
 //
-// GEMM: workgroup = 4 waves, tile = 256 tokens x 128 output columns (key and
-// value features of heads h, h + 1), channel steps of 32.  The A tile (256 x
-// 32 of x) and the B tile (128 x 32, rows of W_k and W_v) go from memory
+// GEMM: workgroup = 8 waves, tile = 256 tokens x 256 output columns (key and
+// value features of heads h .. h + 3), channel steps of 32.  The A tile (256 x
+// 32 of x) and the B tile (256 x 32, rows of W_k and W_v) go from memory
 // straight into LDS (buffer loads with the lds flag: no staging registers, no
 // LDS stores), in three stages, so step k + 2 loads while step k computes;
 // wave w owns tokens 128 (w & 1) .. +127 and head h + (w >> 1): 8 x 4 MFMA
-// blocks of 16 x 16, 32 MFMAs a step.  (Measured on the 4096 px layer: loads
-// staged through registers into padded double-buffered LDS were 7% slower; a
-// 4-head tile at one workgroup per CU 18% slower.)
-//
+// blocks of 16 x 16, 32 MFMAs a step.  One workgroup fills a CU (96 KB of LDS;
+// 2 waves per SIMD).  Measured against the earlier 4-wave, 256 x 128 tile at
+// two workgroups per CU: the x tile now feeds four heads instead of two, and
+// each step's LDS traffic per flop falls by an eighth.  (Also measured on the
+// 4096 px layer: loads staged through registers into padded double-buffered
+// LDS were 7% slower.)
+
 // Epilogue: the accumulator block of tokens 16i .. 16i + 15 holds, in lane
 // (n, g), tokens 4g + (0..3) of feature n -- the turned-around layout the
 // state pass builds with selection MFMAs -- so two row blocks pack straight
@@ -28,12 +31,12 @@
 // phi(K) is rotated in fp32 first (the pair partner comes from the
 // neighbouring lane) and contracted as three bf16 parts; z stays unrotated.
 //
-// Blocks of the (token range, head pair) grid are dealt to the XCDs in
-// contiguous runs, and inside a run walk 4 token ranges per head pair: the
+// Blocks of the (token range, head group) grid are dealt to the XCDs in
+// contiguous runs, and inside a run walk 4 token ranges per head group: the
 // workgroups resident on one XCD then share each x slice among several head
-// pairs and each weight slice among 4 token ranges in its L2.
+// groups and each weight slice among 4 token ranges in its L2.
 //
-// The query side (project_apply_bf16, at the end) runs the same GEMM over four
+// The query side (project_apply_bf16, at the end) runs the same GEMM over eight
 // heads' query weights and hands each 16-token tile of Q to the apply pass's
 // arithmetic in registers.
 #pragma once
@@ -43,9 +46,12 @@
 namespace la {
 
 constexpr int kProjTokens = 256;   // tokens per workgroup block
-constexpr int kProjGroupM = 4;     // token ranges walked together per head pair (measured best of 1..35)
+constexpr int kProjGroupM = 4;     // token ranges walked together per head group (measured best of 1..35)
 constexpr int kProjChannelQuantum = 32;  // C must be a multiple of this
 constexpr int kXcds = 8;
+constexpr int kProjWaves = 8;                // waves per workgroup
+constexpr int kProjThreads = 64 * kProjWaves;
+constexpr int kProjCols = 32 * kProjWaves;   // B rows (output columns) per stage
 
 struct ProjArgs {
   const char* x;    // [B][N][C] bf16
@@ -54,7 +60,7 @@ struct ProjArgs {
   int64_t N;        // tokens per batch
   int C;            // input channels (a multiple of 32)
   int H;
-  int Hp;           // head pairs, ceil(H / 2)
+  int Hp;           // head groups of four, ceil(H / 4)
   int64_t R;        // token ranges per batch
   int64_t T;        // blocks of kProjTokens per range
   int64_t M;        // B * R
@@ -122,29 +128,29 @@ __device__ __forceinline__ void proj_angles(const Rope& r, const float* rtab, co
 // The GEMM of one 256-token block: acc[i][j] (lane (n, g): tokens
 // 128 (w & 1) + 16 i + 4 g + (0..3), column 16 j + n of this wave's 64) over
 // all nk 32-channel steps.  Three LDS stages of one step each (A: 256 token
-// rows at 0, B: 128 weight rows at kProjBOff, 64 bytes a row); wave w's loads fill
-// A rows 64 w .. 64 w + 63 (a_voff: row offsets in x, rsrc rx) and B rows
+// rows at 0, B: 256 weight rows at kProjBOff, 64 bytes a row); wave w's loads
+// fill A rows 32 w .. 32 w + 31 (a_voff: row offsets in x, rsrc rx) and B rows
 // 32 w .. 32 w + 31 (b_voff, rsrc rw); step k + 2 is loaded while step k
 // computes.  Step t computes on stage t % 3.  Its barrier waits for the step's
 // own loads (every wave's) to land and for step t - 1's reads to end
 // everywhere; then stage (t + 2) % 3 is free for step t + 2's loads.  Each
-// step issues six loads per wave, so with step t + 1's loads still in flight
-// the wait is vmcnt(6), and vmcnt(0) at the last step.  In the main loop the
+// step issues four loads per wave, so with step t + 1's loads still in flight
+// the wait is vmcnt(4), and vmcnt(0) at the last step.  In the main loop the
 // stages are named, not indexed: the compiler then sees that the operand reads
 // and the loads in flight touch different LDS arrays and adds no wait of its
-// own (at the loop head, where it cannot tell the stages apart across the back
-// edge, and in the last steps it waits for every load; unrolling to six steps
-// an iteration measured no faster).  The caller has synchronised the
-// workgroup since the stages were last read.
-constexpr int kProjStage = (kProjTokens + 128) * 64;  // bytes per stage
+// own, except at the loop head, where it cannot tell the stages apart across
+// the back edge and waits for every load.  Six steps per iteration halve
+// those waits (measured 3-4% faster than three; 24 steps were no faster).  The
+// caller has synchronised the workgroup since the stages were last read.
+constexpr int kProjStage = (kProjTokens + kProjCols) * 64;  // bytes per stage
 constexpr int kProjBOff = kProjTokens * 64;            // B rows after the A rows
 
-__device__ __forceinline__ void proj_gemm(rsrc_t rx, rsrc_t rw, const int (&a_voff)[4], const int (&b_voff)[2],
+__device__ __forceinline__ void proj_gemm(rsrc_t rx, rsrc_t rw, const int (&a_voff)[2], const int (&b_voff)[2],
                                           int a_rd, int b_rd, int nk, int w, char* st0, char* st1, char* st2,
                                           f32x4_t (&acc)[8][4]) {
   auto issue = [&](int k, char* stage) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lds_dma16(rx, stage + (64 * w + 16 * i) * 64, a_voff[i] + k * 64);
+    for (int i = 0; i < 2; ++i) lds_dma16(rx, stage + (32 * w + 16 * i) * 64, a_voff[i] + k * 64);
 #pragma unroll
     for (int i = 0; i < 2; ++i) lds_dma16(rw, stage + kProjBOff + (32 * w + 16 * i) * 64, b_voff[i] + k * 64);
   };
@@ -163,17 +169,21 @@ __device__ __forceinline__ void proj_gemm(rsrc_t rx, rsrc_t rw, const int (&a_vo
   if (nk > 1) issue(1, st1);
   // steps k .. k + 2 (stages 0, 1, 2), every one with loads to issue
   auto three = [&](int k) {
-    proj_stage_barrier<6>();
+    proj_stage_barrier<4>();
     issue(k + 2, st2);
     compute(st0);
-    proj_stage_barrier<6>();
+    proj_stage_barrier<4>();
     issue(k + 3, st0);
     compute(st1);
-    proj_stage_barrier<6>();
+    proj_stage_barrier<4>();
     issue(k + 4, st1);
     compute(st2);
   };
   int k = 0;
+  for (; k + 8 <= nk; k += 6) {
+    three(k);
+    three(k + 3);
+  }
   for (; k + 5 <= nk; k += 3) three(k);
   // the last 1 to 4 steps (k is a multiple of 3: step t is on stage t % 3)
   for (; k < nk; ++k) {
@@ -181,7 +191,7 @@ __device__ __forceinline__ void proj_gemm(rsrc_t rx, rsrc_t rw, const int (&a_vo
     char* cur = sk == 0 ? st0 : (sk == 1 ? st1 : st2);
     char* nxt = sk == 0 ? st2 : (sk == 1 ? st0 : st1);
     if (k + 1 < nk)
-      proj_stage_barrier<6>();
+      proj_stage_barrier<4>();
     else
       proj_stage_barrier<0>();
     if (k + 2 < nk) issue(k + 2, nxt);
@@ -189,14 +199,14 @@ __device__ __forceinline__ void proj_gemm(rsrc_t rx, rsrc_t rw, const int (&a_vo
   }
 }
 
-// One workgroup per (token range, head pair): 4 waves, wave w takes tokens
+// One workgroup per (token range, head group): 8 waves, wave w takes tokens
 // 128 (w & 1) .. +127 of each 256-token block and head h + (w >> 1) (64 output
 // columns: 8 x 4 MFMA blocks of 16 x 16) through proj_gemm.  B row R of a
 // stage is row R % 32 of head h + R / 64's key (bit 5 of R clear) or value
-// weights.  Two workgroups fit a CU (VGPRs; 72 KB of LDS each, 80 KB with the
-// per-axis RoPE tables).
+// weights.  One workgroup fills a CU (96 KB of LDS, 104 KB with the per-axis
+// RoPE tables).
 template <int ROPE>
-__global__ __launch_bounds__(kThreads, 2) void project_state_bf16(ProjArgs p, Rope rp, StateArgs a) {
+__global__ __launch_bounds__(kProjThreads, 1) void project_state_bf16(ProjArgs p, Rope rp, StateArgs a) {
   __shared__ __attribute__((aligned(1024))) char st0[kProjStage];
   __shared__ __attribute__((aligned(1024))) char st1[kProjStage];
   __shared__ __attribute__((aligned(1024))) char st2[kProjStage];
@@ -207,7 +217,7 @@ __global__ __launch_bounds__(kThreads, 2) void project_state_bf16(ProjArgs p, Ro
   proj_block(blockIdx.x, gridDim.x, p.M, p.Hp, &mi, &pi);
   const int64_t b = mi / p.R;
   const int r = (int)(mi % p.R);
-  const int h = 2 * pi;
+  const int h = 4 * pi;
   const int64_t bh = b * p.H + h;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -220,14 +230,14 @@ __global__ __launch_bounds__(kThreads, 2) void project_state_bf16(ProjArgs p, Ro
   // loads: lane l fills row l / 4 (of 16), slot l % 4, with the swizzled piece
   const int dr = lane >> 2;
   const int dpiece = ((lane & 3) ^ proj_swz(dr)) * 16;
-  int a_voff[4], b_voff[2];
+  int a_voff[2], b_voff[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) a_voff[i] = (64 * w + 16 * i + dr) * row + dpiece;
+  for (int i = 0; i < 2; ++i) a_voff[i] = (32 * w + 16 * i + dr) * row + dpiece;
   // wave w stages rows 32 w .. 32 w + 31 of B: features of head h + (w >> 1),
   // keys for even w, values for odd w
 #pragma unroll
   for (int i = 0; i < 2; ++i) b_voff[i] = ((w >> 1) * 32 + 16 * i + dr) * row + dpiece;
-  const int heads_here = p.H - h < 2 ? p.H - h : 2;
+  const int heads_here = p.H - h < 4 ? p.H - h : 4;
   const rsrc_t rw = make_rsrc((w & 1 ? p.wv : p.wk) + (int64_t)h * 32 * row, (int64_t)heads_here * 32 * row);
   const char* xb = p.x + b * p.N * (int64_t)row;
   // operand reads: lane (n, g) reads piece g of row base + n
@@ -239,7 +249,7 @@ __global__ __launch_bounds__(kThreads, 2) void project_state_bf16(ProjArgs p, Ro
   // first block's barrier orders the copy before any lookup)
   const float sgn = (n & 1) ? 1.f : -1.f;
   const AxisPair ap[2] = {axis_pair(rp, n >> 1), axis_pair(rp, (16 + n) >> 1)};
-  rope_stage<ROPE>(rp, rtab, tid, kThreads);
+  rope_stage<ROPE>(rp, rtab, tid, kProjThreads);
 
   const unsigned one2 = 0x3f803f80u;
   const bf16x8_t ones = as_bf16x8(one2, one2, one2, one2);
@@ -328,12 +338,13 @@ __global__ __launch_bounds__(kThreads, 2) void project_state_bf16(ProjArgs p, Ro
     }
   }
 
-  // the waves' sums to LDS (over stage 0: no load is in flight after the last
-  // step) as red[2 th + hh], the two token halves of each head added, and each
-  // head's sum written as partial r
+  // the waves' sums to LDS (over stages 0 and 1: no load is in flight after
+  // the last step), token half th of head hh as red_th[hh]; the halves are
+  // added and each head's sum is written as partial r
   __syncthreads();
-  float(*red)[kStateElems] = reinterpret_cast<float(*)[kStateElems]>(st0);
-  float* mine = red[2 * th + hh];
+  float(*red0)[kStateElems] = reinterpret_cast<float(*)[kStateElems]>(st0);
+  float(*red1)[kStateElems] = reinterpret_cast<float(*)[kStateElems]>(st1);
+  float* mine = (th ? red1 : red0)[hh];
 #pragma unroll
   for (int fh = 0; fh < 2; ++fh) {
 #pragma unroll
@@ -345,17 +356,20 @@ __global__ __launch_bounds__(kThreads, 2) void project_state_bf16(ProjArgs p, Ro
     }
   }
   __syncthreads();
-  for (int idx = tid; idx < 2 * kStateElems; idx += kThreads) red[0][idx] += red[2][idx];
+  for (int idx = tid; idx < 4 * kStateElems; idx += kProjThreads) red0[0][idx] += red1[0][idx];
   __syncthreads();
-  write_partial(red[0], bh, 0, r, a);
-  if (heads_here == 2) write_partial(red[1], bh + 1, 0, r, a);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int hq = 2 * j + (tid >> 8);
+    if (hq < heads_here) write_partial(red0[hq], bh + hq, 0, r, a, tid & 255);
+  }
 }
 
 // ---------------------------------------------------------------------------
 // Query projection fused with the apply pass
 // ---------------------------------------------------------------------------
 //
-// Q = x W_q^T through the same GEMM (four heads of 32 query features per
+// Q = x W_q^T through the same GEMM (eight heads of 32 query features per
 // workgroup: wave w takes tokens 128 (w & 1) .. +127 and heads h + 2 (w >> 1)
 // and h + 2 (w >> 1) + 1), rounded to bf16 as a bf16 projection would store
 // it, and applied to the heads' states in the epilogue, so Q never reaches
@@ -376,7 +390,7 @@ struct ProjApplyArgs {
   int64_t N;
   int C;
   int H;
-  int Hq;            // head quads, ceil(H / 4)
+  int Hq;            // head groups of eight, ceil(H / 8)
   int64_t R;         // 256-token blocks per batch
   int64_t M;         // B * R
   float eps;
@@ -420,9 +434,9 @@ __device__ __forceinline__ void proj_apply_operands(const float* S, const float*
   for (int k = 0; k < 3; ++k) op.z[k] = as_bf16x8(part[k][0], part[k][1], part[k][2], part[k][3]);
 }
 
-// One workgroup per (256-token block, head quad).
+// One workgroup per (256-token block, group of eight heads).
 template <int ROPE>
-__global__ __launch_bounds__(kThreads, 2) void project_apply_bf16(ProjApplyArgs p, Rope rp) {
+__global__ __launch_bounds__(kProjThreads, 1) void project_apply_bf16(ProjApplyArgs p, Rope rp) {
   __shared__ __attribute__((aligned(1024))) char st0[kProjStage];
   __shared__ __attribute__((aligned(1024))) char st1[kProjStage];
   __shared__ __attribute__((aligned(1024))) char st2[kProjStage];
@@ -433,7 +447,7 @@ __global__ __launch_bounds__(kThreads, 2) void project_apply_bf16(ProjApplyArgs 
   proj_block(blockIdx.x, gridDim.x, p.M, p.Hq, &mi, &pi);
   const int64_t b = mi / p.R;
   const int64_t tok0 = (mi % p.R) * kProjTokens;
-  const int h = 4 * pi;
+  const int h = 8 * pi;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -444,13 +458,13 @@ __global__ __launch_bounds__(kThreads, 2) void project_apply_bf16(ProjApplyArgs 
 
   const int dr = lane >> 2;
   const int dpiece = ((lane & 3) ^ proj_swz(dr)) * 16;
-  int a_voff[4], b_voff[2];
+  int a_voff[2], b_voff[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) a_voff[i] = (64 * w + 16 * i + dr) * row + dpiece;
+  for (int i = 0; i < 2; ++i) a_voff[i] = (32 * w + 16 * i + dr) * row + dpiece;
   // wave w stages B rows 32 w .. 32 w + 31: the query weights of head h + w
 #pragma unroll
   for (int i = 0; i < 2; ++i) b_voff[i] = (32 * w + 16 * i + dr) * row + dpiece;
-  const int heads_here = p.H - h < 4 ? p.H - h : 4;
+  const int heads_here = p.H - h < 8 ? p.H - h : 8;
   const rsrc_t rw = make_rsrc(p.wq + (int64_t)h * 32 * row, (int64_t)heads_here * 32 * row);
   // rows at or past N read as zero; their outputs are not stored
   const rsrc_t rx = make_rsrc(p.x + (b * p.N + tok0) * (int64_t)row, (p.N - tok0) * row);
@@ -460,7 +474,7 @@ __global__ __launch_bounds__(kThreads, 2) void project_apply_bf16(ProjApplyArgs 
   // RoPE: this lane's pairs are 2g, 2g + 1, 8 + 2g, 9 + 2g (its k-slot pairs),
   // two duos of the staged tables (pair counts per axis are even)
   const AxisPair ap[2] = {axis_pair(rp, 2 * g), axis_pair(rp, 8 + 2 * g)};
-  rope_stage<ROPE>(rp, rtab, tid, kThreads);
+  rope_stage<ROPE>(rp, rtab, tid, kProjThreads);
 
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
   f32x4_t acc[8][4];

@@ -622,7 +622,7 @@ size_t workspace(int B, int H, int64_t N, int64_t L, int D, int dtype, int has_r
 }
 
 // Fused K/V projection and state pass: each batch's token blocks of 256 are
-// cut into R ranges of T blocks, one workgroup per (range, head pair), each
+// cut into R ranges of T blocks, one workgroup per (range, four heads), each
 // range of a head leaving one partial state (none when R = 1: the workgroup
 // writes the state itself).  At most kProjMaxRanges partials per head keep the
 // finalize's reads small next to the GEMM.
@@ -647,7 +647,7 @@ int make_proj_geometry(int B, int H, int64_t N, int C, int D, int dtype, ProjGeo
     const int64_t nblk = ceil_div(N, la::kProjTokens);
     g.T = ceil_div(nblk, kProjMaxRanges);
     g.R = ceil_div(nblk, g.T);
-    g.G = (int64_t)B * g.R * ceil_div(H, 2);
+    g.G = (int64_t)B * g.R * ceil_div(H, 4);
     if (g.G > kMaxGroups) return SANA_ERR_INVALID;
     const int64_t state = (int64_t)la::kStateElems * (int64_t)sizeof(float);
     g.state_off = (size_t)round_up(g.R > 1 ? bh * g.R * state : 0, 256);
@@ -975,7 +975,7 @@ int sana_linattn_project_state(const void* x, const void* w_k, const void* w_v, 
   p.N = N;
   p.C = C;
   p.H = H;
-  p.Hp = (int)ceil_div(H, 2);
+  p.Hp = (int)ceil_div(H, 4);
   p.R = g.R;
   p.T = g.T;
   p.M = (int64_t)B * g.R;
@@ -995,7 +995,7 @@ int sana_linattn_project_state(const void* x, const void* w_k, const void* w_v, 
   const RopeArg ra = rope_arg(rope, N);
   with_rope(ra.kind, [&](auto R) {
     constexpr int RO = decltype(R)::value;
-    la::project_state_bf16<RO><<<dim3((unsigned)g.G), dim3(la::kThreads), 0, st>>>(p, ra.r, a);
+    la::project_state_bf16<RO><<<dim3((unsigned)g.G), dim3(la::kProjThreads), 0, st>>>(p, ra.r, a);
   });
   if (g.R > 1) {
     const int64_t n_elems = g.BH * la::kStateElems;
@@ -1024,7 +1024,7 @@ int sana_linattn_project_apply(const void* x, const void* w_q, void* o, const sa
     if (overlaps(o, vout.span, ins[i], in_bytes[i])) return SANA_ERR_INVALID;
   if ((rc = check_rope(rope, N)) != SANA_OK) return rc;
   const int64_t nblk = ceil_div(N, la::kProjTokens);
-  const int64_t groups = (int64_t)B * nblk * ceil_div(H, 4);
+  const int64_t groups = (int64_t)B * nblk * ceil_div(H, 8);
   if (groups > kMaxGroups) return SANA_ERR_INVALID;
 
   la::ProjApplyArgs p;
@@ -1037,7 +1037,7 @@ int sana_linattn_project_apply(const void* x, const void* w_q, void* o, const sa
   p.N = N;
   p.C = C;
   p.H = H;
-  p.Hq = (int)ceil_div(H, 4);
+  p.Hq = (int)ceil_div(H, 8);
   p.R = nblk;
   p.M = (int64_t)B * nblk;
   p.eps = eps;
@@ -1045,7 +1045,7 @@ int sana_linattn_project_apply(const void* x, const void* w_q, void* o, const sa
   const RopeArg ra = rope_arg(rope, N);
   with_rope(ra.kind, [&](auto R) {
     constexpr int RO = decltype(R)::value;
-    la::project_apply_bf16<RO><<<dim3((unsigned)groups), dim3(la::kThreads), 0, st>>>(p, ra.r);
+    la::project_apply_bf16<RO><<<dim3((unsigned)groups), dim3(la::kProjThreads), 0, st>>>(p, ra.r);
   });
   return launch_status();
 }
