@@ -38,9 +38,11 @@ def _run(x, kv=None, z=None, rope=None):
 
 
 # (B, N, C, H): one 256-token block; ragged tails with an odd head count (the
-# last head pair has one head); several ranges (partials + finalize); more than
-# 128 blocks, so each range spans two blocks; a single head
-CASES = [(1, 256, 32, 2), (2, 700, 96, 3), (1, 1000, 64, 4), (1, 5000, 128, 5), (1, 33000, 32, 2), (1, 300, 64, 1)]
+# last group of four heads is partial); several ranges (partials + finalize);
+# more than 128 blocks, so each range spans two blocks; a single head; three
+# head groups of four, the last with one head, over two batches
+CASES = [(1, 256, 32, 2), (2, 700, 96, 3), (1, 1000, 64, 4), (1, 5000, 128, 5), (1, 33000, 32, 2), (1, 300, 64, 1),
+         (2, 600, 64, 9)]
 
 
 @pytest.mark.parametrize("B,N,C,H", CASES)
@@ -176,7 +178,7 @@ def _check_apply(*args, **kw):
 
 
 @pytest.mark.parametrize("B,N,C,H", [(1, 256, 32, 4), (2, 700, 96, 3), (1, 1000, 64, 6), (1, 5000, 128, 5),
-                                     (1, 300, 64, 1)])
+                                     (1, 300, 64, 1), (2, 600, 64, 11), (1, 520, 32, 16)])
 def test_project_apply_matches_oracle(B, N, C, H):
     print(f"case project_apply B={B} N={N} C={C} H={H}", flush=True)
     x = generate_projection(reduced(FULL, B=B, N=N, C=C, H=H, seed=N + C + 1), names=("x", "w_q"))
@@ -213,10 +215,10 @@ def test_project_apply_empty_touches_nothing():
 
 @pytest.mark.parametrize("N", [25500, 25444])
 def test_project_apply_many_blocks_ragged(N):
-    """600 workgroups (3 batch rows x 100 blocks x 2 head quads, H = 6): more
-    than one round of resident workgroups, and every batch row ends in a ragged
-    block (156 tokens, or 100, which leaves the block's second 128 tokens
-    empty)."""
+    """300 workgroups (3 batch rows x 100 blocks x 1 group of eight heads,
+    H = 6): more than one round of resident workgroups (one per CU), and every
+    batch row ends in a ragged block (156 tokens, or 100, which leaves the
+    block's second 128 tokens empty)."""
     print(f"case project_apply many blocks N={N}", flush=True)
     x = generate_projection(reduced(FULL, B=3, N=N, C=64, H=6, seed=N), names=("x", "w_q"))
     S, z = _state_for(reduced(x.workload, N=2000), 10)
@@ -245,7 +247,7 @@ def test_project_apply_rope_and_strided_output(grid, offset):
 def test_project_apply_full_4096px_sampled_heads():
     """The Sana-1.6B 4096 px layer's queries (16384 tokens, C = 2240, 70 heads)
     in the launch configuration the benchmark times; the oracle computes five
-    heads, including the last, partial head quad."""
+    heads, including the last, partial group of eight (six heads)."""
     x = generate_projection(FULL, names=("x", "w_q"))
     S, z = _state_for(reduced(FULL, N=4096), 9)
     print("case project_apply full 4096 px", flush=True)
