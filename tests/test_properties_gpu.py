@@ -1,9 +1,11 @@
-"""Property test (Hypothesis) of the HIP path against the float64 oracle over
+"""Property tests (Hypothesis) of the HIP path against the float64 oracle over
 random shapes: batch, heads, ragged token counts (1 .. 2600, so one to several
 split partials and a ragged last tile), the three forms (non-causal, 3D RoPE in
 either table form, block-causal at a random chunk length) and both I/O dtypes,
 each held to the tolerance of its dtype (rel-L2 <= 1e-5 for fp32; rel-L2 <=
-4e-3 and floored max rel <= 2e-2 for bf16)."""
+4e-3 and floored max rel <= 2e-2 for bf16); and single block_forward calls from
+a carried state, read-only or committing, with RoPE at random position
+offsets."""
 
 import pytest
 from hypothesis import HealthCheck, given, settings
@@ -58,3 +60,67 @@ def test_hip_path_matches_the_oracle(case):
         o = la.sana_linattn_forward(q, k, v, eps=w.eps)
         ref = oracle.linattn(f["q"], f["k"], f["v"], w.eps)
     check(to_np(o), ref, w.dtype, tag)
+
+
+@st.composite
+def block_cases(draw):
+    """One block_forward call: a carried state, read-only or committed in place,
+    with or without 3D RoPE at a random position offset into its grid."""
+    dtype = draw(st.sampled_from(["bf16", "bf16", "f32"]))
+    B = draw(st.integers(1, 2))
+    H = draw(st.integers(1, 4))
+    grid, offset = None, 0
+    if draw(st.booleans()):
+        grid = (draw(st.integers(1, 4)), draw(st.integers(1, 10)), draw(st.integers(1, 30)))
+        n_pos = grid[0] * grid[1] * grid[2]
+        N = draw(st.integers(1, n_pos))
+        offset = draw(st.integers(0, n_pos - N))
+    else:
+        N = draw(st.integers(1, 2600))
+    commit = draw(st.booleans())
+    form = draw(st.sampled_from(["table", "axes"]))
+    seed = draw(st.integers(0, 2**31 - 1))
+    base = WORKLOADS["noncausal_f32_b1h1n256"] if dtype == "f32" else WORKLOADS["sana16b_4096px"]
+    return reduced(base, B=B, H=H, N=N, seed=seed), grid, offset, commit, form
+
+
+@settings(max_examples=30, deadline=None, derandomize=True, suppress_health_check=[HealthCheck.too_slow])
+@given(case=block_cases())
+def test_block_forward_matches_the_oracle(case):
+    """sana_linattn_block_forward against oracle.block_forward from the same
+    carried state (S0 ~ N(0, 1), z0 = 50 |N(0, 1)|, both stored in fp32): the
+    outputs at the dtype's tolerance, and the state either left untouched
+    (read only) or committed in place to the oracle's new state (rel-L2 <= 1e-5
+    for S, 1e-6 for z)."""
+    import numpy as np
+    import torch
+
+    from metrics import rel_l2
+
+    w, grid, offset, commit, form = case
+    x = generate(w)
+    q, k, v = inputs_on_device(x)
+    rng = np.random.default_rng(w.seed + 1)
+    S0 = rng.standard_normal((w.B, w.H, 32, 32)).astype(np.float32)
+    z0 = (np.abs(rng.standard_normal((w.B, w.H, 32))) * 50).astype(np.float32)
+    kv = torch.from_numpy(S0).to(device())
+    z = torch.from_numpy(z0).to(device())
+    rope, angles = None, None
+    if grid is not None:
+        rope = (la.rope3d_axes_device if form == "axes" else la.rope3d_device)(*grid, device()).at(offset)
+        angles = oracle.rope3d_angles(*grid)
+    tag = (f"B={w.B} H={w.H} N={w.N} {w.dtype} grid={grid} offset={offset} commit={commit} form={form} "
+           f"seed={w.seed}")
+    print("case block_forward", tag, flush=True)
+    if commit:
+        o = la.sana_linattn_block_forward(q, k, v, kv_in=kv, ksum_in=z, kv_out=kv, ksum_out=z, eps=w.eps, rope=rope)
+    else:
+        o = la.sana_linattn_block_forward(q, k, v, kv_in=kv, ksum_in=z, eps=w.eps, rope=rope)
+    f = x.f64
+    ref, S_ref, z_ref = oracle.block_forward(f["q"], f["k"], f["v"], S0.astype(np.float64), z0.astype(np.float64),
+                                             w.eps, angles, offset)
+    check(to_np(o), ref, w.dtype, tag)
+    if commit:
+        assert rel_l2(to_np(kv), S_ref) <= 1e-5 and rel_l2(to_np(z), z_ref) <= 1e-6, tag
+    else:
+        assert np.array_equal(to_np(kv), S0) and np.array_equal(to_np(z), z0), tag
