@@ -545,6 +545,21 @@ __device__ __forceinline__ u32x4_t relu_bf16x8(u32x4_t x) {
   return x;
 }
 
+// pack_turned's words, passed through an empty asm: where a ReLU of the packed
+// bf16 follows, the compiler would otherwise split each two-float conversion
+// into two one-float conversions and a v_perm (three instructions for one).
+__device__ __forceinline__ u32x4_t pack_turned_words(f32x4_t t0, f32x4_t t1) {
+  unsigned w0 = pack_bf16x2(t0[0], t0[1]), w1 = pack_bf16x2(t0[2], t0[3]);
+  unsigned w2 = pack_bf16x2(t1[0], t1[1]), w3 = pack_bf16x2(t1[2], t1[3]);
+  asm("" : "+v"(w0), "+v"(w1), "+v"(w2), "+v"(w3));
+  return u32x4_t{w0, w1, w2, w3};
+}
+
+// phi of a freshly computed tile: pack_turned, then the ReLU of the packed bf16
+__device__ __forceinline__ u32x4_t pack_turned_relu(f32x4_t t0, f32x4_t t1) {
+  return relu_bf16x8(pack_turned_words(t0, t1));
+}
+
 // cos and sin that lane (n, g) needs for a 32-token tile at t0: element
 // [fh][tb][i] belongs to pair 8fh + n / 2 of token t0 + 16tb + 4g + i.  They
 // are loaded like K (16-byte row pieces: lane (n, g) gets pairs 4g .. 4g+3 of

@@ -64,18 +64,67 @@ struct ProjArgs {
   int64_t R;        // token ranges per batch
   int64_t T;        // blocks of kProjTokens per range
   int64_t M;        // B * R
+  uint32_t G;       // tiles: M * Hp
 };
 
-// Block (range mi, pair pi) of the grid for workgroup `blk` of `G`.
-__device__ __forceinline__ void proj_block(uint32_t blk, uint32_t G, int64_t M, int P, int64_t* mi, int* pi) {
+// Tiles and the tail.  The grid holds G tiles (token range or block, head
+// group).  The hardware deals workgroup blk to XCD blk % 8, and each XCD runs
+// its workgroups in order, one per CU on its 32 CUs; XCD x takes a contiguous
+// run of `count` tiles.  Equal tiles then run in rounds of 32, the last holding
+// count % 32.  When that tail is at most 16 tiles, each of them runs as two
+// half tiles (half of the group's heads each), all at once: the last round
+// takes about half a tile's time instead of a whole one.  Either way every
+// (token, head) belongs to exactly one workgroup.
+constexpr uint32_t kXcdCUs = 32;  // compute units per XCD
+
+__host__ __device__ inline uint32_t proj_split(uint32_t count) {
+  const uint32_t tail = count % kXcdCUs;
+  return 2 * tail <= kXcdCUs ? tail : 0;
+}
+
+// Workgroups to launch for G tiles: every XCD gets as many slots as the
+// busiest one needs (runs of G / 8 or G / 8 + 1 tiles, plus their split
+// tails); the spare slots exit at once.
+__host__ __device__ inline uint32_t proj_grid(uint32_t G) {
+  const uint32_t q = G / kXcds;
+  uint32_t most = q + proj_split(q);
+  if (G % kXcds) {
+    const uint32_t m1 = q + 1 + proj_split(q + 1);
+    most = m1 > most ? m1 : most;
+  }
+  return most * kXcds;
+}
+
+struct ProjTile {
+  int64_t mi;  // token range (or block) row of the grid
+  int pi;      // head group
+  int half;    // -1: all of the group's heads; 0, 1: its first or second half
+};
+
+// The tile of workgroup blk; false for a spare slot.  Inside an XCD's run the
+// tiles walk kProjGroupM token ranges per head group, so the workgroups
+// resident on one XCD share each x slice among head groups and each weight
+// slice among token ranges in its L2.
+__device__ __forceinline__ bool proj_tile(uint32_t blk, uint32_t G, int64_t M, int P, ProjTile* t) {
   const uint32_t q = G / kXcds, rem = G % kXcds, xcd = blk % kXcds, slot = blk / kXcds;
-  const uint32_t L = (xcd < rem ? xcd * (q + 1) : rem * (q + 1) + (xcd - rem) * q) + slot;
+  const uint32_t count = q + (xcd < rem ? 1u : 0u), start = xcd * q + (xcd < rem ? xcd : rem);
+  const uint32_t split = proj_split(count), whole = count - split;
+  if (slot >= count + split) return false;
+  uint32_t L;
+  if (slot < whole) {
+    L = start + slot;
+    t->half = -1;
+  } else {
+    L = start + whole + (slot - whole) / 2;
+    t->half = (int)((slot - whole) & 1);
+  }
   const int64_t per_group = (int64_t)kProjGroupM * P;
-  const int64_t first = (int64_t)(L / per_group) * kProjGroupM;
+  const int64_t first = ((int64_t)L / per_group) * kProjGroupM;
   const int64_t gsize = M - first < kProjGroupM ? M - first : kProjGroupM;
   const int64_t in = (int64_t)L % per_group;
-  *mi = first + in % gsize;
-  *pi = (int)(in / gsize);
+  t->mi = first + in % gsize;
+  t->pi = (int)(in / gsize);
+  return true;
 }
 
 // Loads x and weight rows straight into LDS (buffer_load ... lds): a wave's
@@ -100,66 +149,44 @@ __device__ __forceinline__ void proj_stage_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
-// cos/sin of this lane's two pairs (q[0], q[1]: features n and 16 + n) at
-// position pos0 + tok (tok in the call's range): from the full tables in
-// memory, or from the per-axis tables staged in LDS (rtab; ap: where each
-// pair's entries sit), the coordinates computed once for both.
-template <int ROPE>
-__device__ __forceinline__ void proj_angles(const Rope& r, const float* rtab, const AxisPair (&ap)[2], int64_t tok,
-                                            float (&c)[2], float (&sn)[2]) {
-  const int64_t pos = r.pos0 + tok;
-  if constexpr (ROPE == kRopeAxes) {
-    int t, h, w;
-    rope_coords(r, pos, t, h, w);
-#pragma unroll
-    for (int fh = 0; fh < 2; ++fh) {
-      axis_cs(rtab, axis_entry(ap[fh], t, h, w), c[fh], sn[fh]);
-    }
-  } else {
-#pragma unroll
-    for (int fh = 0; fh < 2; ++fh) {
-      const int q = (16 * fh + (int)(threadIdx.x & 15)) >> 1;
-      c[fh] = r.cos[pos * 16 + q];
-      sn[fh] = r.sin[pos * 16 + q];
-    }
-  }
-}
-
 // The GEMM of one 256-token block: acc[i][j] (lane (n, g): tokens
-// 128 (w & 1) + 16 i + 4 g + (0..3), column 16 j + n of this wave's 64) over
-// all nk 32-channel steps.  Three LDS stages of one step each (A: 256 token
-// rows at 0, B: 256 weight rows at kProjBOff, 64 bytes a row); wave w's loads
-// fill A rows 32 w .. 32 w + 31 (a_voff: row offsets in x, rsrc rx) and B rows
-// 32 w .. 32 w + 31 (b_voff, rsrc rw); step k + 2 is loaded while step k
-// computes.  Step t computes on stage t % 3.  Its barrier waits for the step's
-// own loads (every wave's) to land and for step t - 1's reads to end
-// everywhere; then stage (t + 2) % 3 is free for step t + 2's loads.  Each
-// step issues four loads per wave, so with step t + 1's loads still in flight
-// the wait is vmcnt(4), and vmcnt(0) at the last step.  In the main loop the
-// stages are named, not indexed: the compiler then sees that the operand reads
-// and the loads in flight touch different LDS arrays and adds no wait of its
-// own, except at the loop head, where it cannot tell the stages apart across
-// the back edge and waits for every load.  Six steps per iteration halve
-// those waits (measured 3-4% faster than three; 24 steps were no faster).  The
-// caller has synchronised the workgroup since the stages were last read.
+// a_row + 16 i + 4 g + (0..3), column 16 j + n of this wave's 64; RB row
+// blocks) over all nk 32-channel steps.  Three LDS stages of one step each (A:
+// 256 token rows at 0, B: up to 256 weight rows at kProjBOff, 64 bytes a row);
+// wave w's loads fill A rows 32 w .. 32 w + 31 (a_voff: row offsets in x,
+// rsrc rx) and B rows 16 NB w .. 16 NB w + 16 NB - 1 (b_voff, rsrc rw); step
+// k + 2 is loaded while step k computes.  Step t computes on stage t % 3.  Its
+// barrier waits for the step's own loads (every wave's) to land and for step
+// t - 1's reads to end everywhere; then stage (t + 2) % 3 is free for step
+// t + 2's loads.  Each step issues 2 + NB loads per wave, so with step t + 1's
+// loads still in flight the wait is vmcnt(2 + NB), and vmcnt(0) at the last
+// step.  In the main loop the stages are named, not indexed: the compiler then
+// sees that the operand reads and the loads in flight touch different LDS
+// arrays and adds no wait of its own, except at the loop head, where it cannot
+// tell the stages apart across the back edge and waits for every load.  Six
+// steps per iteration halve those waits (measured 3-4% faster than three; 24
+// steps were no faster).  The caller has synchronised the workgroup since the
+// stages were last read.
 constexpr int kProjStage = (kProjTokens + kProjCols) * 64;  // bytes per stage
 constexpr int kProjBOff = kProjTokens * 64;            // B rows after the A rows
 
-__device__ __forceinline__ void proj_gemm(rsrc_t rx, rsrc_t rw, const int (&a_voff)[2], const int (&b_voff)[2],
+template <int RB, int NB>
+__device__ __forceinline__ void proj_gemm(rsrc_t rx, rsrc_t rw, const int (&a_voff)[2], const int (&b_voff)[NB],
                                           int a_rd, int b_rd, int nk, int w, char* st0, char* st1, char* st2,
-                                          f32x4_t (&acc)[8][4]) {
+                                          f32x4_t (&acc)[RB][4]) {
+  constexpr int kLoads = 2 + NB;  // loads per wave and step
   auto issue = [&](int k, char* stage) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) lds_dma16(rx, stage + (32 * w + 16 * i) * 64, a_voff[i] + k * 64);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) lds_dma16(rw, stage + kProjBOff + (32 * w + 16 * i) * 64, b_voff[i] + k * 64);
+    for (int i = 0; i < NB; ++i) lds_dma16(rw, stage + kProjBOff + (16 * NB * w + 16 * i) * 64, b_voff[i] + k * 64);
   };
   auto compute = [&](const char* stage) {
     bf16x8_t bf[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) bf[j] = *reinterpret_cast<const bf16x8_t*>(stage + b_rd + j * 1024);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < RB; ++i) {
       const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(stage + a_rd + i * 1024);
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = mfma16(af, bf[j], acc[i][j]);
@@ -169,13 +196,13 @@ __device__ __forceinline__ void proj_gemm(rsrc_t rx, rsrc_t rw, const int (&a_vo
   if (nk > 1) issue(1, st1);
   // steps k .. k + 2 (stages 0, 1, 2), every one with loads to issue
   auto three = [&](int k) {
-    proj_stage_barrier<4>();
+    proj_stage_barrier<kLoads>();
     issue(k + 2, st2);
     compute(st0);
-    proj_stage_barrier<4>();
+    proj_stage_barrier<kLoads>();
     issue(k + 3, st0);
     compute(st1);
-    proj_stage_barrier<4>();
+    proj_stage_barrier<kLoads>();
     issue(k + 4, st1);
     compute(st2);
   };
@@ -191,7 +218,7 @@ __device__ __forceinline__ void proj_gemm(rsrc_t rx, rsrc_t rw, const int (&a_vo
     char* cur = sk == 0 ? st0 : (sk == 1 ? st1 : st2);
     char* nxt = sk == 0 ? st2 : (sk == 1 ? st0 : st1);
     if (k + 1 < nk)
-      proj_stage_barrier<4>();
+      proj_stage_barrier<kLoads>();
     else
       proj_stage_barrier<0>();
     if (k + 2 < nk) issue(k + 2, nxt);
@@ -199,57 +226,145 @@ __device__ __forceinline__ void proj_gemm(rsrc_t rx, rsrc_t rw, const int (&a_vo
   }
 }
 
-// One workgroup per (token range, head group): 8 waves, wave w takes tokens
-// 128 (w & 1) .. +127 of each 256-token block and head h + (w >> 1) (64 output
-// columns: 8 x 4 MFMA blocks of 16 x 16) through proj_gemm.  B row R of a
-// stage is row R % 32 of head h + R / 64's key (bit 5 of R clear) or value
-// weights.  One workgroup fills a CU (96 KB of LDS, 104 KB with the per-axis
-// RoPE tables).
+// RoPE in the epilogues: once the GEMM of a block is done, its workgroup writes
+// the cos/sin of every (token, pair) of the block into an LDS stage that no load
+// or operand read touches any more (below), and the epilogue reads them from
+// there.  Thread (token j = tid % 256, half = tid / 256) fills pairs
+// 8 half .. 8 half + 7 of token j: its coordinates once, then four duos.
+//
+// Duo i of the half row: {cos, cos, sin, sin} of pairs 8 half + 2i and
+// 8 half + 2i + 1 at position pos0 + tok (tok clamped into the call's tokens by
+// the caller), from the per-axis tables staged in LDS (rtab) or the full
+// tables in memory.
 template <int ROPE>
-__global__ __launch_bounds__(kProjThreads, 1) void project_state_bf16(ProjArgs p, Rope rp, StateArgs a) {
-  __shared__ __attribute__((aligned(1024))) char st0[kProjStage];
-  __shared__ __attribute__((aligned(1024))) char st1[kProjStage];
-  __shared__ __attribute__((aligned(1024))) char st2[kProjStage];
-  __shared__ __attribute__((aligned(16))) float rtab[ROPE == kRopeAxes ? 2 * kMaxAxisTab : 1];
+__device__ __forceinline__ void proj_rope_half_row(const Rope& r, const float* rtab, int64_t tok, int half,
+                                                   f32x4_t (&duo)[4]) {
+  const int64_t pos = r.pos0 + tok;
+  if constexpr (ROPE == kRopeAxes) {
+    int t, h, w;
+    rope_coords(r, pos, t, h, w);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) duo[i] = axis_duo(rtab, axis_entry(axis_pair(r, 8 * half + 2 * i), t, h, w));
+  } else {
+    const float* c = r.cos + pos * 16 + 8 * half;
+    const float* s = r.sin + pos * 16 + 8 * half;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) duo[i] = f32x4_t{c[2 * i], c[2 * i + 1], s[2 * i], s[2 * i + 1]};
+  }
+}
 
-  int64_t mi;
-  int pi;
-  proj_block(blockIdx.x, gridDim.x, p.M, p.Hp, &mi, &pi);
+// The stage that the block's GEMM of nk steps leaves free: step k reads stage
+// k % 3 and step k's loads were issued at step k - 2, so stage nk % 3 was last
+// read at step nk - 3 and takes no load after it; every wave's reads of it ended
+// before the barrier of step nk - 2.  A wave that has passed the last step's
+// barrier may write it.
+__device__ __forceinline__ char* proj_free_stage(int nk, char* st0, char* st1, char* st2) {
+  const int s = nk % 3;
+  return s == 0 ? st0 : (s == 1 ? st1 : st2);
+}
+
+// Hides a thread index from the compiler, so that the table writers' addresses
+// are computed where they are used, after the GEMM.  Left visible, they are
+// loop invariants that the compiler computes once ahead of the block loop and
+// keeps live through the GEMM: at the register limit that costs the GEMM its
+// operand prefetch (measured: 256 VGPRs and an MFMA stalled on each LDS read,
+// about 5% slower tiles, against 233 VGPRs with the reads issued ahead).
+__device__ __forceinline__ void opaque_index(int& i) { asm volatile("" : "+v"(i)); }
+
+// Key/value epilogue table, pair-major: entry (pair q, token quad u) is 32
+// bytes, cos of tokens 4u .. 4u+3 then their sin, at q * 2048 + (u ^ (q & 7)) *
+// 32.  An epilogue read takes one pair's quad per lane; the XOR puts the eight
+// pairs that a quarter-wave reads in distinct banks.  32 KB: one stage.
+__device__ __forceinline__ int kv_tab_entry(int q, int u) { return q * 2048 + ((u ^ (q & 7)) << 5); }
+
+template <int ROPE>
+__device__ __forceinline__ void kv_rope_table(const Rope& r, const float* rtab, int64_t tok0, int64_t N, int tid,
+                                              char* tab) {
+  opaque_index(tid);
+  const int j = tid & (kProjTokens - 1), half = tid / kProjTokens;
+  const int64_t tok = tok0 + j < N ? tok0 + j : N - 1;
+  f32x4_t duo[4];
+  proj_rope_half_row<ROPE>(r, rtab, tok, half, duo);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      float* p = reinterpret_cast<float*>(tab + kv_tab_entry(8 * half + 2 * i + e, j >> 2)) + (j & 3);
+      p[0] = duo[i][e];
+      p[4] = duo[i][2 + e];
+    }
+}
+
+// Query epilogue table, token-major: token j's row is 128 bytes, duo d (pairs
+// 2d, 2d + 1 as {cos, cos, sin, sin}) in 16-byte slot d ^ (j & 7) ^ ((j >> 3) &
+// 1).  A read takes one duo of sixteen consecutive tokens (a lane each); the
+// slot pattern keeps every eight of them (and every sixteen, with 64 banks)
+// in distinct banks.  32 KB: one stage.
+__device__ __forceinline__ int q_tab_entry(int j, int d) { return j * 128 + ((d ^ (j & 7) ^ ((j >> 3) & 1)) << 4); }
+
+template <int ROPE>
+__device__ __forceinline__ void q_rope_table(const Rope& r, const float* rtab, int64_t tok0, int64_t N, int tid,
+                                             char* tab) {
+  opaque_index(tid);
+  const int j = tid & (kProjTokens - 1), half = tid / kProjTokens;
+  const int64_t tok = tok0 + j < N ? tok0 + j : N - 1;
+  f32x4_t duo[4];
+  proj_rope_half_row<ROPE>(r, rtab, tok, half, duo);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) *reinterpret_cast<f32x4_t*>(tab + q_tab_entry(j, 4 * half + i)) = duo[i];
+}
+
+// One tile: a token range of 256-token blocks and HG heads from head h (four,
+// or two for a half tile), 8 waves.  Wave w takes head h + w / WPH and tokens
+// TPW (w % WPH) .. + TPW - 1 of each block (WPH = 8 / HG waves per head, TPW =
+// 256 / WPH tokens: 128, or 64 in a half tile), 64 output columns (the head's
+// key and value features: RB x 4 MFMA blocks of 16 x 16) through proj_gemm.  B
+// row R of a stage is row R % 32 of head h + R / 64's key (bit 5 of R clear)
+// or value weights.  One workgroup fills a CU (96 KB of LDS, 104 KB with the
+// per-axis RoPE tables).
+template <int ROPE, int HG>
+__device__ __forceinline__ void project_state_tile(const ProjArgs& p, const Rope& rp, const StateArgs& a, int64_t mi,
+                                                   int h, char* st0, char* st1, char* st2, const float* rtab) {
+  constexpr int WPH = 8 / HG;               // waves per head
+  constexpr int TPW = kProjTokens / WPH;    // tokens per wave and block
+  constexpr int RB = TPW / 16;              // its 16-token row blocks
+  constexpr int NB = HG / 2;                // B loads (16 rows) per wave and step
   const int64_t b = mi / p.R;
   const int r = (int)(mi % p.R);
-  const int h = 4 * pi;
   const int64_t bh = b * p.H + h;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15;
   const int g = lane >> 4;
-  const int th = w & 1, hh = w >> 1;
+  const int tw = w % WPH, hh = w / WPH;
   const int row = p.C * 2;  // bytes per token row and per weight row
 
   // loads: lane l fills row l / 4 (of 16), slot l % 4, with the swizzled piece
   const int dr = lane >> 2;
   const int dpiece = ((lane & 3) ^ proj_swz(dr)) * 16;
-  int a_voff[2], b_voff[2];
+  int a_voff[2], b_voff[NB];
 #pragma unroll
   for (int i = 0; i < 2; ++i) a_voff[i] = (32 * w + 16 * i + dr) * row + dpiece;
-  // wave w stages rows 32 w .. 32 w + 31 of B: features of head h + (w >> 1),
-  // keys for even w, values for odd w
+  // wave w stages B rows rb0 .. rb0 + 16 NB - 1, all of one head and one matrix
+  const int rb0 = 16 * NB * w;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) b_voff[i] = ((w >> 1) * 32 + 16 * i + dr) * row + dpiece;
-  const int heads_here = p.H - h < 4 ? p.H - h : 4;
-  const rsrc_t rw = make_rsrc((w & 1 ? p.wv : p.wk) + (int64_t)h * 32 * row, (int64_t)heads_here * 32 * row);
+  for (int i = 0; i < NB; ++i) b_voff[i] = ((rb0 >> 6) * 32 + ((rb0 + 16 * i) & 31) + dr) * row + dpiece;
+  const int heads_here = p.H - h < HG ? p.H - h : HG;
+  const rsrc_t rw =
+      make_rsrc(((rb0 >> 5) & 1 ? p.wv : p.wk) + (int64_t)h * 32 * row, (int64_t)heads_here * 32 * row);
   const char* xb = p.x + b * p.N * (int64_t)row;
   // operand reads: lane (n, g) reads piece g of row base + n
   const int sw = 16 * (g ^ proj_swz(n));
-  const int a_rd = (128 * th + n) * 64 + sw;
+  const int a_rd = (TPW * tw + n) * 64 + sw;
   const int b_rd = kProjBOff + (64 * hh + n) * 64 + sw;
-  // RoPE: the pair partner's sign, and where the per-axis entries of this
-  // lane's pairs (features n and 16 + n) sit; the axis tables go to LDS (the
-  // first block's barrier orders the copy before any lookup)
-  const float sgn = (n & 1) ? 1.f : -1.f;
-  const AxisPair ap[2] = {axis_pair(rp, n >> 1), axis_pair(rp, (16 + n) >> 1)};
-  rope_stage<ROPE>(rp, rtab, tid, kProjThreads);
+  // RoPE: the pair partner's sign bits (flipped for even features), and where
+  // this lane's angle quads sit in the block's table: pair 8 fh + (n >> 1),
+  // token quad TPW / 4 tw + 8 t + 4 hs + g at tb[hs] + 16384 fh + 256 t
+  const unsigned sgn_bits = (n & 1) ? 0u : 0x80008000u;
+  int tb[2];
+#pragma unroll
+  for (int hs = 0; hs < 2; ++hs) tb[hs] = kv_tab_entry(n >> 1, TPW / 4 * tw + 4 * hs + g);
 
   const unsigned one2 = 0x3f803f80u;
   const bf16x8_t ones = as_bf16x8(one2, one2, one2, one2);
@@ -263,24 +378,28 @@ __global__ __launch_bounds__(kProjThreads, 1) void project_state_bf16(ProjArgs p
     const int64_t tok0 = blk * kProjTokens;
     // rows at or past N read as zero: their keys and values are 0 and add nothing
     const rsrc_t rx = make_rsrc(xb + tok0 * row, (p.N - tok0) * row);
-    f32x4_t acc[8][4];
+    f32x4_t acc[RB][4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < RB; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = zero4;
     __syncthreads();  // every wave is done with the previous block's stages
-    proj_gemm(rx, rw, a_voff, b_voff, a_rd, b_rd, nk, w, st0, st1, st2, acc);
+    proj_gemm<RB, NB>(rx, rw, a_voff, b_voff, a_rd, b_rd, nk, w, st0, st1, st2, acc);
+    [[maybe_unused]] char* const tab = proj_free_stage(nk, st0, st1, st2);
+    if constexpr (ROPE != kRopeNone) {
+      kv_rope_table<ROPE>(rp, rtab, tok0, p.N, tid, tab);
+      __syncthreads();  // the table is whole before any lane reads it
+    }
 
-    // acc[i][j], lane (n, g): tokens 128 th + 16 i + 4 g + (0..3) of the
+    // acc[i][j], lane (n, g): tokens TPW tw + 16 i + 4 g + (0..3) of the
     // block, column 16 j + n of head h + hh (j = 0, 1: key features; 2, 3:
     // value features).  Row blocks 2t, 2t + 1 make one 32-token contraction.
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < RB / 2; ++t) {
       bf16x8_t ka[2], vb[2];
 #pragma unroll
       for (int fh = 0; fh < 2; ++fh) {
-        ka[fh] = __builtin_bit_cast(
-            bf16x8_t, relu_bf16x8(__builtin_bit_cast(u32x4_t, pack_turned(acc[2 * t][fh], acc[2 * t + 1][fh]))));
+        ka[fh] = __builtin_bit_cast(bf16x8_t, pack_turned_relu(acc[2 * t][fh], acc[2 * t + 1][fh]));
         vb[fh] = pack_turned(acc[2 * t][2 + fh], acc[2 * t + 1][2 + fh]);
       }
 #pragma unroll
@@ -293,18 +412,30 @@ __global__ __launch_bounds__(kProjThreads, 1) void project_state_bf16(ProjArgs p
         }
       } else {
         // Slot s of ka[fh] holds phi(K) of feature f = 16 fh + n for token
-        // tok0 + 128 th + 16 (2t + s / 4) + 4 g + s % 4; the pair partner
+        // tok0 + TPW tw + 16 (2t + s / 4) + 4 g + s % 4; the pair partner
         // f ^ 1 sits in lane n ^ 1, same slot.  Rotated: x c - x' s for even
         // f, x' s + x c for odd f, in fp32, then split into three bf16 parts
-        // contracted against V one by one.  A token's angles are looked up
-        // once for both feature halves.
+        // contracted against V one by one.  The partner comes over by DPP
+        // with its sign already applied (an exact flip of the bf16 sign
+        // bits); the angles of slots 4 hs .. 4 hs + 3 are one 16-byte quad of
+        // cosines and one of sines.
         u32x4_t kw[2], pw[2];
 #pragma unroll
         for (int fh = 0; fh < 2; ++fh) {
           kw[fh] = __builtin_bit_cast(u32x4_t, ka[fh]);
 #pragma unroll
-          for (int d = 0; d < 4; ++d) pw[fh][d] = (unsigned)__builtin_amdgcn_mov_dpp((int)kw[fh][d], 0xB1, 0xF, 0xF, false);
+          for (int d = 0; d < 4; ++d)
+            pw[fh][d] = (unsigned)__builtin_amdgcn_mov_dpp((int)kw[fh][d], 0xB1, 0xF, 0xF, false) ^ sgn_bits;
         }
+        f32x4_t cq[2][2], sq[2][2];
+#pragma unroll
+        for (int fh = 0; fh < 2; ++fh)
+#pragma unroll
+          for (int hs = 0; hs < 2; ++hs) {
+            const char* e = tab + tb[hs] + 16384 * fh + 256 * t;
+            cq[fh][hs] = *reinterpret_cast<const f32x4_t*>(e);
+            sq[fh][hs] = *reinterpret_cast<const f32x4_t*>(e + 16);
+          }
         unsigned part[2][3][4];
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
@@ -312,14 +443,12 @@ __global__ __launch_bounds__(kProjThreads, 1) void project_state_bf16(ProjArgs p
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
             const int slot = 2 * d + e;
-            const int64_t tok = tok0 + 128 * th + 16 * (2 * t + (slot >> 2)) + 4 * g + (slot & 3);
-            float c[2], sn[2];
-            proj_angles<ROPE>(rp, rtab, ap, tok < p.N ? tok : p.N - 1, c, sn);
 #pragma unroll
             for (int fh = 0; fh < 2; ++fh) {
               const float x = e ? bf16hi_to_f32(kw[fh][d]) : bf16lo_to_f32(kw[fh][d]);
-              const float xp = sgn * (e ? bf16hi_to_f32(pw[fh][d]) : bf16lo_to_f32(pw[fh][d]));
-              y[fh][e] = __builtin_fmaf(x, c[fh], xp * sn[fh]);  // the fusion fixed, as in rot_lo
+              const float xp = e ? bf16hi_to_f32(pw[fh][d]) : bf16lo_to_f32(pw[fh][d]);
+              const float c = cq[fh][slot >> 2][slot & 3], sn = sq[fh][slot >> 2][slot & 3];
+              y[fh][e] = __builtin_fmaf(x, c, xp * sn);  // the fusion fixed, as in rot_lo
             }
           }
 #pragma unroll
@@ -338,13 +467,15 @@ __global__ __launch_bounds__(kProjThreads, 1) void project_state_bf16(ProjArgs p
     }
   }
 
-  // the waves' sums to LDS (over stages 0 and 1: no load is in flight after
-  // the last step), token half th of head hh as red_th[hh]; the halves are
-  // added and each head's sum is written as partial r
+  // The waves' sums to LDS, over stages 0 and 1 (no load is in flight after
+  // the last step): wave (tw, hh) writes slot tw HG + hh, slots 0 .. 3 in
+  // stage 0 and 4 .. 7 in stage 1, one state (kStateElems floats) each.  Then
+  // head hq's sum, its token parts added in order, is written as partial r.
   __syncthreads();
-  float(*red0)[kStateElems] = reinterpret_cast<float(*)[kStateElems]>(st0);
-  float(*red1)[kStateElems] = reinterpret_cast<float(*)[kStateElems]>(st1);
-  float* mine = (th ? red1 : red0)[hh];
+  float* red0 = reinterpret_cast<float*>(st0);
+  float* red1 = reinterpret_cast<float*>(st1);
+  const int slot = tw * HG + hh;
+  float* mine = (slot < 4 ? red0 : red1) + (slot & 3) * kStateElems;
 #pragma unroll
   for (int fh = 0; fh < 2; ++fh) {
 #pragma unroll
@@ -356,13 +487,45 @@ __global__ __launch_bounds__(kProjThreads, 1) void project_state_bf16(ProjArgs p
     }
   }
   __syncthreads();
-  for (int idx = tid; idx < 4 * kStateElems; idx += kProjThreads) red0[0][idx] += red1[0][idx];
+  // element idx of head hq (idx < HG kStateElems) sits at idx + tw HG
+  // kStateElems of the two stages taken as one run of 8 states
+  for (int idx = tid; idx < HG * kStateElems; idx += kProjThreads) {
+    float sum = red0[idx];
+#pragma unroll
+    for (int k = 1; k < WPH; ++k) {
+      const int q = idx + k * HG * kStateElems;
+      sum += q < 4 * kStateElems ? red0[q] : red1[q - 4 * kStateElems];
+    }
+    red0[idx] = sum;
+  }
   __syncthreads();
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < HG / 2; ++j) {
     const int hq = 2 * j + (tid >> 8);
-    if (hq < heads_here) write_partial(red0[hq], bh + hq, 0, r, a, tid & 255);
+    if (hq < heads_here) write_partial(red0 + hq * kStateElems, bh + hq, 0, r, a, tid & 255);
   }
+}
+
+// Workgroup blk's tile (see proj_tile): a whole head group of four, or one
+// half of it (two heads) in an XCD's last round.
+template <int ROPE>
+__global__ __launch_bounds__(kProjThreads, 1) void project_state_bf16(ProjArgs p, Rope rp, StateArgs a) {
+  __shared__ __attribute__((aligned(1024))) char st0[kProjStage];
+  __shared__ __attribute__((aligned(1024))) char st1[kProjStage];
+  __shared__ __attribute__((aligned(1024))) char st2[kProjStage];
+  __shared__ __attribute__((aligned(16))) float rtab[ROPE == kRopeAxes ? 2 * kMaxAxisTab : 1];
+
+  ProjTile t;
+  if (!proj_tile(blockIdx.x, p.G, p.M, p.Hp, &t)) return;
+  const int h = 4 * t.pi + (t.half > 0 ? 2 : 0);
+  if (h >= p.H) return;  // the second half of a group with two heads or fewer
+  // the axis tables go to LDS; the first block's barrier orders the copy
+  // before any lookup
+  rope_stage<ROPE>(rp, rtab, threadIdx.x, kProjThreads);
+  if (t.half < 0)
+    project_state_tile<ROPE, 4>(p, rp, a, t.mi, h, st0, st1, st2, rtab);
+  else
+    project_state_tile<ROPE, 2>(p, rp, a, t.mi, h, st0, st1, st2, rtab);
 }
 
 // ---------------------------------------------------------------------------
@@ -393,6 +556,7 @@ struct ProjApplyArgs {
   int Hq;            // head groups of eight, ceil(H / 8)
   int64_t R;         // 256-token blocks per batch
   int64_t M;         // B * R
+  uint32_t G;        // tiles: M * Hq
   float eps;
 };
 
@@ -434,61 +598,68 @@ __device__ __forceinline__ void proj_apply_operands(const float* S, const float*
   for (int k = 0; k < 3; ++k) op.z[k] = as_bf16x8(part[k][0], part[k][1], part[k][2], part[k][3]);
 }
 
-// One workgroup per (256-token block, group of eight heads).
-template <int ROPE>
-__global__ __launch_bounds__(kProjThreads, 1) void project_apply_bf16(ProjApplyArgs p, Rope rp) {
-  __shared__ __attribute__((aligned(1024))) char st0[kProjStage];
-  __shared__ __attribute__((aligned(1024))) char st1[kProjStage];
-  __shared__ __attribute__((aligned(1024))) char st2[kProjStage];
-  __shared__ __attribute__((aligned(16))) float rtab[ROPE == kRopeAxes ? 2 * kMaxAxisTab : 1];
-
-  int64_t mi;
-  int pi;
-  proj_block(blockIdx.x, gridDim.x, p.M, p.Hq, &mi, &pi);
+// One tile: a 256-token block and HG heads from head h (eight, or four for a
+// half tile), 8 waves.  Wave w takes heads h + 2 hh, h + 2 hh + 1 (hh = w /
+// WPG) and tokens TPW tw .. + TPW - 1 of the block (tw = w % WPG; WPG = 16 / HG
+// waves per head pair, TPW = 256 / WPG tokens: 128, or 64 in a half tile).
+template <int ROPE, int HG>
+__device__ __forceinline__ void project_apply_tile(const ProjApplyArgs& p, const Rope& rp, int64_t mi, int h,
+                                                   char* st0, char* st1, char* st2, const float* rtab) {
+  constexpr int WPG = 16 / HG;             // waves per head pair
+  constexpr int TPW = kProjTokens / WPG;   // tokens per wave
+  constexpr int RB = TPW / 16;             // its 16-token row blocks
+  constexpr int NB = HG / 4;               // B loads (16 rows) per wave and step
   const int64_t b = mi / p.R;
   const int64_t tok0 = (mi % p.R) * kProjTokens;
-  const int h = 8 * pi;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15;
   const int g = lane >> 4;
-  const int th = w & 1, hh = w >> 1;
+  const int tw = w % WPG, hh = w / WPG;
   const int row = p.C * 2;
 
   const int dr = lane >> 2;
   const int dpiece = ((lane & 3) ^ proj_swz(dr)) * 16;
-  int a_voff[2], b_voff[2];
+  int a_voff[2], b_voff[NB];
 #pragma unroll
   for (int i = 0; i < 2; ++i) a_voff[i] = (32 * w + 16 * i + dr) * row + dpiece;
-  // wave w stages B rows 32 w .. 32 w + 31: the query weights of head h + w
+  // wave w stages B rows 16 NB w .. + 16 NB - 1 (the query weights are 32 rows
+  // a head, head-major)
 #pragma unroll
-  for (int i = 0; i < 2; ++i) b_voff[i] = (32 * w + 16 * i + dr) * row + dpiece;
-  const int heads_here = p.H - h < 8 ? p.H - h : 8;
+  for (int i = 0; i < NB; ++i) b_voff[i] = (16 * NB * w + 16 * i + dr) * row + dpiece;
+  const int heads_here = p.H - h < HG ? p.H - h : HG;
   const rsrc_t rw = make_rsrc(p.wq + (int64_t)h * 32 * row, (int64_t)heads_here * 32 * row);
   // rows at or past N read as zero; their outputs are not stored
   const rsrc_t rx = make_rsrc(p.x + (b * p.N + tok0) * (int64_t)row, (p.N - tok0) * row);
   const int sw = 16 * (g ^ proj_swz(n));
-  const int a_rd = (128 * th + n) * 64 + sw;
+  const int a_rd = (TPW * tw + n) * 64 + sw;
   const int b_rd = kProjBOff + (64 * hh + n) * 64 + sw;
   // RoPE: this lane's pairs are 2g, 2g + 1, 8 + 2g, 9 + 2g (its k-slot pairs),
-  // two duos of the staged tables (pair counts per axis are even)
-  const AxisPair ap[2] = {axis_pair(rp, 2 * g), axis_pair(rp, 8 + 2 * g)};
-  rope_stage<ROPE>(rp, rtab, tid, kProjThreads);
+  // duos g and 4 + g of its token's row in the block's table (tokens
+  // TPW tw + 16 m + n, m = 2t + bb: at tb[d] + 2048 m)
+  int tb[2];
+#pragma unroll
+  for (int d = 0; d < 2; ++d) tb[d] = q_tab_entry(TPW * tw + n, 4 * d + g);
 
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
-  f32x4_t acc[8][4];
+  f32x4_t acc[RB][4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < RB; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = zero4;
   __syncthreads();  // the RoPE tables are staged
-  proj_gemm(rx, rw, a_voff, b_voff, a_rd, b_rd, p.C / 32, w, st0, st1, st2, acc);
+  proj_gemm<RB, NB>(rx, rw, a_voff, b_voff, a_rd, b_rd, p.C / 32, w, st0, st1, st2, acc);
+  [[maybe_unused]] char* const tab = proj_free_stage(p.C / 32, st0, st1, st2);
+  if constexpr (ROPE != kRopeNone) {
+    q_rope_table<ROPE>(rp, rtab, tok0, p.N, tid, tab);
+    __syncthreads();  // the table is whole before any lane reads it
+  }
 
-  // acc[i][2u + fh], lane (n, g): tokens 128 th + 16 i + 4 g + (0..3),
+  // acc[i][2u + fh], lane (n, g): tokens TPW tw + 16 i + 4 g + (0..3),
   // feature 16 fh + n of head h + 2 hh + u
   const bf16x8_t sel[2] = {untangle_select(g, n, 0), untangle_select(g, n, 1)};
-  const int64_t tw0 = tok0 + 128 * th;
+  const int64_t tw0 = tok0 + TPW * tw;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int hu = h + 2 * hh + u;
@@ -499,46 +670,51 @@ __global__ __launch_bounds__(kProjThreads, 1) void project_apply_bf16(ProjApplyA
     const int64_t orow = p.lo.token * 2;
     const rsrc_t ro = rows_rsrc(p.o + p.lo.base(bh) * 2, tw0, p.N, orow);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < RB / 2; ++t) {
       bf16x8_t A[2];
 #pragma unroll
       for (int fh = 0; fh < 2; ++fh)
-        A[fh] = __builtin_bit_cast(bf16x8_t, relu_bf16x8(__builtin_bit_cast(
-                                                 u32x4_t, pack_turned(acc[2 * t][2 * u + fh], acc[2 * t + 1][2 * u + fh]))));
+        A[fh] = __builtin_bit_cast(bf16x8_t, pack_turned_relu(acc[2 * t][2 * u + fh], acc[2 * t + 1][2 * u + fh]));
 #pragma unroll
       for (int bb = 0; bb < 2; ++bb) {
         const f32x4_t d0 = mfma16(A[0], sel[bb], zero4), d1 = mfma16(A[1], sel[bb], zero4);
-        const u32x4_t q = {pack_bf16x2(d0[0], d0[1]), pack_bf16x2(d0[2], d0[3]), pack_bf16x2(d1[0], d1[1]),
-                           pack_bf16x2(d1[2], d1[3])};
-        const int tr = 16 * (2 * t + bb) + n;  // this lane's token row in the wave's 128
+        const u32x4_t q = pack_turned_words(d0, d1);
+        const int tr = 16 * (2 * t + bb) + n;  // this lane's token row in the wave's TPW
         f32x4_t c = zero4, sn = zero4;
         if constexpr (ROPE != kRopeNone) {
-          const int64_t tok = tw0 + tr < p.N ? tw0 + tr : p.N - 1;
-          const int64_t pos = rp.pos0 + tok;
-          if constexpr (ROPE == kRopeAxes) {
-            int ct, chh, cw;
-            rope_coords(rp, pos, ct, chh, cw);
 #pragma unroll
-            for (int d = 0; d < 2; ++d) {
-              const f32x4_t e = axis_duo(rtab, axis_entry(ap[d], ct, chh, cw));
-              c[2 * d] = e[0];
-              c[2 * d + 1] = e[1];
-              sn[2 * d] = e[2];
-              sn[2 * d + 1] = e[3];
-            }
-          } else {
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-              const int pq = (q4 < 2 ? 2 * g : 6 + 2 * g) + q4;
-              c[q4] = rp.cos[pos * 16 + pq];
-              sn[q4] = rp.sin[pos * 16 + pq];
-            }
+          for (int d = 0; d < 2; ++d) {
+            const f32x4_t e = *reinterpret_cast<const f32x4_t*>(tab + tb[d] + 2048 * (2 * t + bb));
+            c[2 * d] = e[0];
+            c[2 * d + 1] = e[1];
+            sn[2 * d] = e[2];
+            sn[2 * d + 1] = e[3];
           }
         }
         store16_nt(ro, tr * (int)orow + 16 * g, apply_tile<ROPE != kRopeNone>(q, op, p.eps, c, sn));
       }
     }
   }
+}
+
+// Workgroup blk's tile (see proj_tile): a 256-token block and a group of eight
+// heads, or one half of the group (four heads) in an XCD's last round.
+template <int ROPE>
+__global__ __launch_bounds__(kProjThreads, 1) void project_apply_bf16(ProjApplyArgs p, Rope rp) {
+  __shared__ __attribute__((aligned(1024))) char st0[kProjStage];
+  __shared__ __attribute__((aligned(1024))) char st1[kProjStage];
+  __shared__ __attribute__((aligned(1024))) char st2[kProjStage];
+  __shared__ __attribute__((aligned(16))) float rtab[ROPE == kRopeAxes ? 2 * kMaxAxisTab : 1];
+
+  ProjTile t;
+  if (!proj_tile(blockIdx.x, p.G, p.M, p.Hq, &t)) return;
+  const int h = 8 * t.pi + (t.half > 0 ? 4 : 0);
+  if (h >= p.H) return;  // the second half of a group with four heads or fewer
+  rope_stage<ROPE>(rp, rtab, threadIdx.x, kProjThreads);
+  if (t.half < 0)
+    project_apply_tile<ROPE, 8>(p, rp, t.mi, h, st0, st1, st2, rtab);
+  else
+    project_apply_tile<ROPE, 4>(p, rp, t.mi, h, st0, st1, st2, rtab);
 }
 
 }  // namespace la

@@ -979,6 +979,7 @@ int sana_linattn_project_state(const void* x, const void* w_k, const void* w_v, 
   p.R = g.R;
   p.T = g.T;
   p.M = (int64_t)B * g.R;
+  p.G = (uint32_t)g.G;
   la::StateArgs a;
   a.partials = static_cast<float*>(ws);
   a.states = reinterpret_cast<float*>(static_cast<char*>(ws) + g.state_off);
@@ -995,7 +996,7 @@ int sana_linattn_project_state(const void* x, const void* w_k, const void* w_v, 
   const RopeArg ra = rope_arg(rope, N);
   with_rope(ra.kind, [&](auto R) {
     constexpr int RO = decltype(R)::value;
-    la::project_state_bf16<RO><<<dim3((unsigned)g.G), dim3(la::kProjThreads), 0, st>>>(p, ra.r, a);
+    la::project_state_bf16<RO><<<dim3(la::proj_grid(p.G)), dim3(la::kProjThreads), 0, st>>>(p, ra.r, a);
   });
   if (g.R > 1) {
     const int64_t n_elems = g.BH * la::kStateElems;
@@ -1040,12 +1041,13 @@ int sana_linattn_project_apply(const void* x, const void* w_q, void* o, const sa
   p.Hq = (int)ceil_div(H, 8);
   p.R = nblk;
   p.M = (int64_t)B * nblk;
+  p.G = (uint32_t)groups;
   p.eps = eps;
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   const RopeArg ra = rope_arg(rope, N);
   with_rope(ra.kind, [&](auto R) {
     constexpr int RO = decltype(R)::value;
-    la::project_apply_bf16<RO><<<dim3((unsigned)groups), dim3(la::kProjThreads), 0, st>>>(p, ra.r);
+    la::project_apply_bf16<RO><<<dim3(la::proj_grid(p.G)), dim3(la::kProjThreads), 0, st>>>(p, ra.r);
   });
   return launch_status();
 }

@@ -40,9 +40,15 @@ def _run(x, kv=None, z=None, rope=None):
 # (B, N, C, H): one 256-token block; ragged tails with an odd head count (the
 # last group of four heads is partial); several ranges (partials + finalize);
 # more than 128 blocks, so each range spans two blocks; a single head; three
-# head groups of four, the last with one head, over two batches
+# head groups of four, the last with one head, over two batches.  The grid deals
+# each XCD a run of tiles and runs the last round's tiles (when at most 16) as
+# half tiles of two heads: the cases up to here have runs of 16 tiles or fewer
+# (half tiles only).  272 tiles (runs of 34: 32 whole tiles, then 2 tiles as 4
+# halves) and 264 (runs of 33, a ragged block, three heads in the last group)
+# mix both kinds in each run; 132 tiles of two-block ranges give runs of 17
+# (whole tiles: a tail of 17 stays whole) and 16 (halves).
 CASES = [(1, 256, 32, 2), (2, 700, 96, 3), (1, 1000, 64, 4), (1, 5000, 128, 5), (1, 33000, 32, 2), (1, 300, 64, 1),
-         (2, 600, 64, 9)]
+         (2, 600, 64, 9), (2, 17408, 32, 6), (2, 16740, 32, 7), (1, 33700, 32, 7)]
 
 
 @pytest.mark.parametrize("B,N,C,H", CASES)
@@ -177,8 +183,12 @@ def _check_apply(*args, **kw):
     assert ok, report
 
 
+# the last two cases mix whole tiles (eight heads) and half tiles (four heads):
+# 272 tiles (runs of 34 per XCD) and 264 (runs of 33, a ragged last block, six
+# heads in the second group)
 @pytest.mark.parametrize("B,N,C,H", [(1, 256, 32, 4), (2, 700, 96, 3), (1, 1000, 64, 6), (1, 5000, 128, 5),
-                                     (1, 300, 64, 1), (2, 600, 64, 11), (1, 520, 32, 16)])
+                                     (1, 300, 64, 1), (2, 600, 64, 11), (1, 520, 32, 16), (2, 17408, 32, 12),
+                                     (1, 33700, 32, 14)])
 def test_project_apply_matches_oracle(B, N, C, H):
     print(f"case project_apply B={B} N={N} C={C} H={H}", flush=True)
     x = generate_projection(reduced(FULL, B=B, N=N, C=C, H=H, seed=N + C + 1), names=("x", "w_q"))
@@ -226,22 +236,40 @@ def test_project_apply_many_blocks_ragged(N):
     _check_apply(to_np(o), x, S, z, 1e-6)
 
 
-@pytest.mark.parametrize("grid,offset", [((3, 8, 20), 0), ((4, 10, 12), 150)])
-def test_project_apply_rope_and_strided_output(grid, offset):
+# (grid, offset, N, C, H): C = 64, 96 and 32 give 2, 3 and 1 channel steps,
+# so the angle table of the epilogue sits in each of the three LDS stages; the
+# third case has two groups of eight heads (the second partial) and a ragged
+# last block
+@pytest.mark.parametrize("grid,offset,N,C,H", [((3, 8, 20), 0, 480, 64, 6), ((4, 10, 12), 150, 330, 64, 6),
+                                               ((5, 10, 20), 0, 1000, 96, 9), ((4, 10, 12), 0, 480, 32, 3)])
+def test_project_apply_rope_and_strided_output(grid, offset, N, C, H):
     """Queries rotated by the 3D RoPE (both table forms, bit-identical), and
     outputs written straight into a [B, N, H, D] buffer."""
     torch = torch_mod()
-    N = 480 - offset if offset else 480
-    x = generate_projection(reduced(FULL, B=2, N=N, C=64, H=6, seed=17), names=("x", "w_q"))
+    x = generate_projection(reduced(FULL, B=2, N=N, C=C, H=H, seed=17 + C), names=("x", "w_q"))
     S, z = _state_for(x.workload, 8)
     table = la.rope3d_device(*grid, device()).at(offset)
     axes = la.rope3d_axes_device(*grid, device()).at(offset)
-    print(f"case project_apply rope grid={grid} offset={offset}", flush=True)
+    print(f"case project_apply rope grid={grid} offset={offset} N={N} C={C} H={H}", flush=True)
     o_t = _run_apply(x, S, z, rope=table)
-    o_bnhd = torch.empty(2, N, 6, 32, dtype=torch.bfloat16, device=device()).permute(0, 2, 1, 3)
+    o_bnhd = torch.empty(2, N, H, 32, dtype=torch.bfloat16, device=device()).permute(0, 2, 1, 3)
     o_a = _run_apply(x, S, z, rope=axes, o=o_bnhd)
     assert bool((o_a.contiguous().view(torch.int16) == o_t.view(torch.int16)).all()), "forms or layouts differ"
     _check_apply(to_np(o_a), x, S, z, 1e-6, angles=oracle.rope3d_angles(*grid), pos_offset=offset)
+
+
+def test_project_apply_full_720p_rope_sampled_heads():
+    """The SANA-Video 720p layer's queries (21 x 22 x 40 = 18480 tokens,
+    C = 2240, 70 heads) with the per-axis 3D RoPE, in the launch configuration
+    the benchmark times; the oracle computes four heads, including the last,
+    partial group of eight."""
+    grid = (21, 22, 40)
+    x = generate_projection(reduced(FULL, N=grid[0] * grid[1] * grid[2], seed=5), names=("x", "w_q"))
+    S, z = _state_for(reduced(FULL, N=4096), 14)
+    print("case project_apply full 720p rope", flush=True)
+    o = _run_apply(x, S, z, rope=la.rope3d_axes_device(*grid, device()))
+    heads = [0, 9, 42, 69]
+    _check_apply(to_np(o)[:, heads], x, S, z, 1e-6, heads=heads, angles=oracle.rope3d_angles(*grid))
 
 
 def test_project_apply_full_4096px_sampled_heads():
