@@ -71,25 +71,31 @@ struct ProjArgs {
 // group).  The hardware deals workgroup blk to XCD blk % 8, and each XCD runs
 // its workgroups in order, one per CU on its 32 CUs; XCD x takes a contiguous
 // run of `count` tiles.  Equal tiles then run in rounds of 32, the last holding
-// count % 32.  When that tail is at most 16 tiles, each of them runs as two
-// half tiles (half of the group's heads each), all at once: the last round
-// takes about half a tile's time instead of a whole one.  Either way every
-// (token, head) belongs to exactly one workgroup.
+// tail = count % 32.  That round runs with most CUs idle, so its tiles are cut
+// into s parts each (s = 4 when the parts still fit on the 32 CUs at once,
+// else 2, else none): the round then takes a part's time instead of a whole
+// tile's.  Either way every (token, head) belongs to exactly one workgroup.
 constexpr uint32_t kXcdCUs = 32;  // compute units per XCD
 
-__host__ __device__ inline uint32_t proj_split(uint32_t count) {
+// parts per tail tile for a run of `count` tiles
+__host__ __device__ inline uint32_t proj_parts(uint32_t count) {
   const uint32_t tail = count % kXcdCUs;
-  return 2 * tail <= kXcdCUs ? tail : 0;
+  return tail == 0 ? 1u : (4 * tail <= kXcdCUs ? 4u : (2 * tail <= kXcdCUs ? 2u : 1u));
+}
+
+// slots (workgroups) a run of `count` tiles takes
+__host__ __device__ inline uint32_t proj_slots(uint32_t count) {
+  return count + (proj_parts(count) - 1) * (count % kXcdCUs);
 }
 
 // Workgroups to launch for G tiles: every XCD gets as many slots as the
-// busiest one needs (runs of G / 8 or G / 8 + 1 tiles, plus their split
-// tails); the spare slots exit at once.
+// busiest one needs (runs of G / 8 or G / 8 + 1 tiles); the spare slots exit
+// at once.
 __host__ __device__ inline uint32_t proj_grid(uint32_t G) {
   const uint32_t q = G / kXcds;
-  uint32_t most = q + proj_split(q);
+  uint32_t most = proj_slots(q);
   if (G % kXcds) {
-    const uint32_t m1 = q + 1 + proj_split(q + 1);
+    const uint32_t m1 = proj_slots(q + 1);
     most = m1 > most ? m1 : most;
   }
   return most * kXcds;
@@ -98,7 +104,8 @@ __host__ __device__ inline uint32_t proj_grid(uint32_t G) {
 struct ProjTile {
   int64_t mi;  // token range (or block) row of the grid
   int pi;      // head group
-  int half;    // -1: all of the group's heads; 0, 1: its first or second half
+  int parts;   // 1: the whole tile; 2, 4: one of that many parts
+  int part;    // which one
 };
 
 // The tile of workgroup blk; false for a spare slot.  Inside an XCD's run the
@@ -108,15 +115,17 @@ struct ProjTile {
 __device__ __forceinline__ bool proj_tile(uint32_t blk, uint32_t G, int64_t M, int P, ProjTile* t) {
   const uint32_t q = G / kXcds, rem = G % kXcds, xcd = blk % kXcds, slot = blk / kXcds;
   const uint32_t count = q + (xcd < rem ? 1u : 0u), start = xcd * q + (xcd < rem ? xcd : rem);
-  const uint32_t split = proj_split(count), whole = count - split;
-  if (slot >= count + split) return false;
+  const uint32_t parts = proj_parts(count), whole = parts > 1 ? count - count % kXcdCUs : count;
+  if (slot >= proj_slots(count)) return false;
   uint32_t L;
   if (slot < whole) {
     L = start + slot;
-    t->half = -1;
+    t->parts = 1;
+    t->part = 0;
   } else {
-    L = start + whole + (slot - whole) / 2;
-    t->half = (int)((slot - whole) & 1);
+    L = start + whole + (slot - whole) / parts;
+    t->parts = (int)parts;
+    t->part = (int)((slot - whole) % parts);
   }
   const int64_t per_group = (int64_t)kProjGroupM * P;
   const int64_t first = ((int64_t)L / per_group) * kProjGroupM;
@@ -130,9 +139,14 @@ __device__ __forceinline__ bool proj_tile(uint32_t blk, uint32_t G, int64_t M, i
 // Loads x and weight rows straight into LDS (buffer_load ... lds): a wave's
 // instruction fills 1 KB of LDS, 16 rows of 64 bytes (one 32-channel step),
 // lane l writing row l / 4, slot l % 4.  Slots are XOR-swizzled: slot s of row
-// r holds 16-byte piece s ^ swz(r) of the row, which makes the MFMA operand
-// reads (16 rows, one piece each) free of bank conflicts with 32 or 64 banks.
-__device__ __forceinline__ int proj_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+// r holds 16-byte piece s ^ swz(r) of the row.  An MFMA operand read takes
+// piece g of 16 consecutive rows in each quarter-wave; with swz(r) =
+// ((r >> 2) ^ (r >> 1)) & 3 such a read runs at the LDS's full rate, 1 KB in
+// about 4.6 cycles per CU, at every row offset the kernels use.  That was
+// measured with 16-byte reads of each layout from 8 waves per CU: the layouts
+// that simple bank models call conflict-free (no swizzle, or (r >> 1) ^ (r >>
+// 3), or r >> 2, or r & 3) all take 8 cycles per 1 KB, half the rate.
+__device__ __forceinline__ int proj_swz(int r) { return ((r >> 2) ^ (r >> 1)) & 3; }
 
 __device__ __forceinline__ void lds_dma16(rsrc_t r, char* lds, int voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
@@ -149,17 +163,20 @@ __device__ __forceinline__ void proj_stage_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
-// The GEMM of one 256-token block: acc[i][j] (lane (n, g): tokens
+// The GEMM of one block of 256 (or 128) tokens: acc[i][j] (lane (n, g): tokens
 // a_row + 16 i + 4 g + (0..3), column 16 j + n of this wave's 64; RB row
 // blocks) over all nk 32-channel steps.  Three LDS stages of one step each (A:
-// 256 token rows at 0, B: up to 256 weight rows at kProjBOff, 64 bytes a row);
-// wave w's loads fill A rows 32 w .. 32 w + 31 (a_voff: row offsets in x,
-// rsrc rx) and B rows 16 NB w .. 16 NB w + 16 NB - 1 (b_voff, rsrc rw); step
-// k + 2 is loaded while step k computes.  Step t computes on stage t % 3.  Its
-// barrier waits for the step's own loads (every wave's) to land and for step
-// t - 1's reads to end everywhere; then stage (t + 2) % 3 is free for step
-// t + 2's loads.  Each step issues 2 + NB loads per wave, so with step t + 1's
-// loads still in flight the wait is vmcnt(2 + NB), and vmcnt(0) at the last
+// up to 256 token rows at 0, B: up to 256 weight rows at kProjBOff, 64 bytes a
+// row).  Wave w's loads fill A rows 16 NA w .. + 16 NA - 1 (a_voff: row offsets
+// in x, rsrc rx) and, for the first BW waves, B rows 16 NB w .. + 16 NB - 1
+// (b_voff, rsrc rw); step k + 2 is loaded while step k computes.  Step t
+// computes on stage t % 3.  Its barrier waits for the step's own loads (every
+// wave's) to land and for step t - 1's reads to end everywhere; then stage
+// (t + 2) % 3 is free for step t + 2's loads.  A wave issues NA + NB loads a
+// step (NA when it stages no B rows), so with step t + 1's loads still in
+// flight the wait is vmcnt(NA + NB) (vmcnt(NA) when only some waves stage B:
+// the loads land in order, so the B-staging waves then also wait for one load
+// of step t + 1, which has had a whole step to land), and vmcnt(0) at the last
 // step.  In the main loop the stages are named, not indexed: the compiler then
 // sees that the operand reads and the loads in flight touch different LDS
 // arrays and adds no wait of its own, except at the loop head, where it cannot
@@ -170,16 +187,19 @@ __device__ __forceinline__ void proj_stage_barrier() {
 constexpr int kProjStage = (kProjTokens + kProjCols) * 64;  // bytes per stage
 constexpr int kProjBOff = kProjTokens * 64;            // B rows after the A rows
 
-template <int RB, int NB>
-__device__ __forceinline__ void proj_gemm(rsrc_t rx, rsrc_t rw, const int (&a_voff)[2], const int (&b_voff)[NB],
+template <int RB, int NA, int NB, int BW>
+__device__ __forceinline__ void proj_gemm(rsrc_t rx, rsrc_t rw, const int (&a_voff)[NA], const int (&b_voff)[NB],
                                           int a_rd, int b_rd, int nk, int w, char* st0, char* st1, char* st2,
                                           f32x4_t (&acc)[RB][4]) {
-  constexpr int kLoads = 2 + NB;  // loads per wave and step
+  constexpr int kLoads = BW == kProjWaves ? NA + NB : NA;  // the wait count (see above)
   auto issue = [&](int k, char* stage) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) lds_dma16(rx, stage + (32 * w + 16 * i) * 64, a_voff[i] + k * 64);
+    for (int i = 0; i < NA; ++i) lds_dma16(rx, stage + (16 * NA * w + 16 * i) * 64, a_voff[i] + k * 64);
+    if (BW == kProjWaves || w < BW) {
 #pragma unroll
-    for (int i = 0; i < NB; ++i) lds_dma16(rw, stage + kProjBOff + (16 * NB * w + 16 * i) * 64, b_voff[i] + k * 64);
+      for (int i = 0; i < NB; ++i)
+        lds_dma16(rw, stage + kProjBOff + (16 * NB * w + 16 * i) * 64, b_voff[i] + k * 64);
+    }
   };
   auto compute = [&](const char* stage) {
     bf16x8_t bf[4];
@@ -314,21 +334,23 @@ __device__ __forceinline__ void q_rope_table(const Rope& r, const float* rtab, i
   for (int i = 0; i < 4; ++i) *reinterpret_cast<f32x4_t*>(tab + q_tab_entry(j, 4 * half + i)) = duo[i];
 }
 
-// One tile: a token range of 256-token blocks and HG heads from head h (four,
-// or two for a half tile), 8 waves.  Wave w takes head h + w / WPH and tokens
-// TPW (w % WPH) .. + TPW - 1 of each block (WPH = 8 / HG waves per head, TPW =
-// 256 / WPH tokens: 128, or 64 in a half tile), 64 output columns (the head's
-// key and value features: RB x 4 MFMA blocks of 16 x 16) through proj_gemm.  B
-// row R of a stage is row R % 32 of head h + R / 64's key (bit 5 of R clear)
-// or value weights.  One workgroup fills a CU (96 KB of LDS, 104 KB with the
-// per-axis RoPE tables).
+// One tile: a token range of 256-token blocks and HG heads from head h (four;
+// two for a half tile, one for a quarter), 8 waves.  Wave w takes head h + w /
+// WPH and tokens TPW (w % WPH) .. + TPW - 1 of each block (WPH = 8 / HG waves
+// per head, TPW = 256 / WPH tokens: 128, 64 or 32), 64 output columns (the
+// head's key and value features: RB x 4 MFMA blocks of 16 x 16) through
+// proj_gemm.  B row R of a stage is row R % 32 of head h + R / 64's key (bit 5
+// of R clear) or value weights: 64 HG rows, 16 NB rows a wave (one head's 64
+// rows fill only four waves' loads).  One workgroup fills a CU (96 KB of LDS,
+// 104 KB with the per-axis RoPE tables).
 template <int ROPE, int HG>
 __device__ __forceinline__ void project_state_tile(const ProjArgs& p, const Rope& rp, const StateArgs& a, int64_t mi,
                                                    int h, char* st0, char* st1, char* st2, const float* rtab) {
   constexpr int WPH = 8 / HG;               // waves per head
   constexpr int TPW = kProjTokens / WPH;    // tokens per wave and block
   constexpr int RB = TPW / 16;              // its 16-token row blocks
-  constexpr int NB = HG / 2;                // B loads (16 rows) per wave and step
+  constexpr int NB = HG > 1 ? HG / 2 : 1;   // B loads (16 rows) per wave and step
+  constexpr int BW = HG > 1 ? kProjWaves : 4;  // waves that stage B rows
   const int64_t b = mi / p.R;
   const int r = (int)(mi % p.R);
   const int64_t bh = b * p.H + h;
@@ -384,7 +406,7 @@ __device__ __forceinline__ void project_state_tile(const ProjArgs& p, const Rope
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = zero4;
     __syncthreads();  // every wave is done with the previous block's stages
-    proj_gemm<RB, NB>(rx, rw, a_voff, b_voff, a_rd, b_rd, nk, w, st0, st1, st2, acc);
+    proj_gemm<RB, 2, NB, BW>(rx, rw, a_voff, b_voff, a_rd, b_rd, nk, w, st0, st1, st2, acc);
     [[maybe_unused]] char* const tab = proj_free_stage(nk, st0, st1, st2);
     if constexpr (ROPE != kRopeNone) {
       kv_rope_table<ROPE>(rp, rtab, tok0, p.N, tid, tab);
@@ -500,14 +522,14 @@ __device__ __forceinline__ void project_state_tile(const ProjArgs& p, const Rope
   }
   __syncthreads();
 #pragma unroll
-  for (int j = 0; j < HG / 2; ++j) {
+  for (int j = 0; j < (HG + 1) / 2; ++j) {
     const int hq = 2 * j + (tid >> 8);
     if (hq < heads_here) write_partial(red0 + hq * kStateElems, bh + hq, 0, r, a, tid & 255);
   }
 }
 
-// Workgroup blk's tile (see proj_tile): a whole head group of four, or one
-// half of it (two heads) in an XCD's last round.
+// Workgroup blk's tile (see proj_tile): a whole head group of four, or in an
+// XCD's last round one of its halves (two heads) or quarters (one head).
 template <int ROPE>
 __global__ __launch_bounds__(kProjThreads, 1) void project_state_bf16(ProjArgs p, Rope rp, StateArgs a) {
   __shared__ __attribute__((aligned(1024))) char st0[kProjStage];
@@ -517,15 +539,17 @@ __global__ __launch_bounds__(kProjThreads, 1) void project_state_bf16(ProjArgs p
 
   ProjTile t;
   if (!proj_tile(blockIdx.x, p.G, p.M, p.Hp, &t)) return;
-  const int h = 4 * t.pi + (t.half > 0 ? 2 : 0);
-  if (h >= p.H) return;  // the second half of a group with two heads or fewer
+  const int h = 4 * t.pi + t.part * (4 / t.parts);
+  if (h >= p.H) return;  // a part past the group's last head
   // the axis tables go to LDS; the first block's barrier orders the copy
   // before any lookup
   rope_stage<ROPE>(rp, rtab, threadIdx.x, kProjThreads);
-  if (t.half < 0)
+  if (t.parts == 1)
     project_state_tile<ROPE, 4>(p, rp, a, t.mi, h, st0, st1, st2, rtab);
-  else
+  else if (t.parts == 2)
     project_state_tile<ROPE, 2>(p, rp, a, t.mi, h, st0, st1, st2, rtab);
+  else
+    project_state_tile<ROPE, 1>(p, rp, a, t.mi, h, st0, st1, st2, rtab);
 }
 
 // ---------------------------------------------------------------------------
@@ -598,19 +622,23 @@ __device__ __forceinline__ void proj_apply_operands(const float* S, const float*
   for (int k = 0; k < 3; ++k) op.z[k] = as_bf16x8(part[k][0], part[k][1], part[k][2], part[k][3]);
 }
 
-// One tile: a 256-token block and HG heads from head h (eight, or four for a
-// half tile), 8 waves.  Wave w takes heads h + 2 hh, h + 2 hh + 1 (hh = w /
-// WPG) and tokens TPW tw .. + TPW - 1 of the block (tw = w % WPG; WPG = 16 / HG
-// waves per head pair, TPW = 256 / WPG tokens: 128, or 64 in a half tile).
-template <int ROPE, int HG>
-__device__ __forceinline__ void project_apply_tile(const ProjApplyArgs& p, const Rope& rp, int64_t mi, int h,
-                                                   char* st0, char* st1, char* st2, const float* rtab) {
+// One tile: TT tokens from tok_off of a 256-token block and HG heads from head
+// h (all 256 tokens and eight heads; four heads for a half tile; 128 tokens
+// and four heads for a quarter), 8 waves.  Wave w takes heads h + 2 hh,
+// h + 2 hh + 1 (hh = w / WPG) and tokens TPW tw .. + TPW - 1 of the tile
+// (tw = w % WPG; WPG = 16 / HG waves per head pair, TPW = TT / WPG tokens:
+// 128, 64 or 32).
+template <int ROPE, int HG, int TT>
+__device__ __forceinline__ void project_apply_tile(const ProjApplyArgs& p, const Rope& rp, int64_t mi, int tok_off,
+                                                   int h, char* st0, char* st1, char* st2, const float* rtab) {
   constexpr int WPG = 16 / HG;             // waves per head pair
-  constexpr int TPW = kProjTokens / WPG;   // tokens per wave
+  constexpr int TPW = TT / WPG;            // tokens per wave
   constexpr int RB = TPW / 16;             // its 16-token row blocks
+  constexpr int NA = TT / 128;             // A loads (16 rows) per wave and step
   constexpr int NB = HG / 4;               // B loads (16 rows) per wave and step
   const int64_t b = mi / p.R;
-  const int64_t tok0 = (mi % p.R) * kProjTokens;
+  const int64_t tok0 = (mi % p.R) * kProjTokens + tok_off;
+  if (tok0 >= p.N) return;  // a quarter past the end of a ragged last block
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -621,9 +649,9 @@ __device__ __forceinline__ void project_apply_tile(const ProjApplyArgs& p, const
 
   const int dr = lane >> 2;
   const int dpiece = ((lane & 3) ^ proj_swz(dr)) * 16;
-  int a_voff[2], b_voff[NB];
+  int a_voff[NA], b_voff[NB];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) a_voff[i] = (32 * w + 16 * i + dr) * row + dpiece;
+  for (int i = 0; i < NA; ++i) a_voff[i] = (16 * NA * w + 16 * i + dr) * row + dpiece;
   // wave w stages B rows 16 NB w .. + 16 NB - 1 (the query weights are 32 rows
   // a head, head-major)
 #pragma unroll
@@ -649,7 +677,7 @@ __device__ __forceinline__ void project_apply_tile(const ProjApplyArgs& p, const
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = zero4;
   __syncthreads();  // the RoPE tables are staged
-  proj_gemm<RB, NB>(rx, rw, a_voff, b_voff, a_rd, b_rd, p.C / 32, w, st0, st1, st2, acc);
+  proj_gemm<RB, NA, NB, kProjWaves>(rx, rw, a_voff, b_voff, a_rd, b_rd, p.C / 32, w, st0, st1, st2, acc);
   [[maybe_unused]] char* const tab = proj_free_stage(p.C / 32, st0, st1, st2);
   if constexpr (ROPE != kRopeNone) {
     q_rope_table<ROPE>(rp, rtab, tok0, p.N, tid, tab);
@@ -698,7 +726,9 @@ __device__ __forceinline__ void project_apply_tile(const ProjApplyArgs& p, const
 }
 
 // Workgroup blk's tile (see proj_tile): a 256-token block and a group of eight
-// heads, or one half of the group (four heads) in an XCD's last round.
+// heads, or in an XCD's last round one half of the group (four heads) or one
+// quarter (four heads, 128 tokens: part 2 hq + th, heads 4 hq.., tokens
+// 128 th..).
 template <int ROPE>
 __global__ __launch_bounds__(kProjThreads, 1) void project_apply_bf16(ProjApplyArgs p, Rope rp) {
   __shared__ __attribute__((aligned(1024))) char st0[kProjStage];
@@ -708,13 +738,16 @@ __global__ __launch_bounds__(kProjThreads, 1) void project_apply_bf16(ProjApplyA
 
   ProjTile t;
   if (!proj_tile(blockIdx.x, p.G, p.M, p.Hq, &t)) return;
-  const int h = 8 * t.pi + (t.half > 0 ? 4 : 0);
-  if (h >= p.H) return;  // the second half of a group with four heads or fewer
+  const int hq = t.parts == 4 ? t.part >> 1 : t.part;  // which four heads (parts 2 and 4)
+  const int h = 8 * t.pi + (t.parts == 1 ? 0 : 4 * hq);
+  if (h >= p.H) return;  // a part past the group's last head
   rope_stage<ROPE>(rp, rtab, threadIdx.x, kProjThreads);
-  if (t.half < 0)
-    project_apply_tile<ROPE, 8>(p, rp, t.mi, h, st0, st1, st2, rtab);
+  if (t.parts == 1)
+    project_apply_tile<ROPE, 8, 256>(p, rp, t.mi, 0, h, st0, st1, st2, rtab);
+  else if (t.parts == 2)
+    project_apply_tile<ROPE, 4, 256>(p, rp, t.mi, 0, h, st0, st1, st2, rtab);
   else
-    project_apply_tile<ROPE, 4>(p, rp, t.mi, h, st0, st1, st2, rtab);
+    project_apply_tile<ROPE, 4, 128>(p, rp, t.mi, 128 * (t.part & 1), h, st0, st1, st2, rtab);
 }
 
 }  // namespace la

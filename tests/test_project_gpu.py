@@ -40,13 +40,14 @@ def _run(x, kv=None, z=None, rope=None):
 # (B, N, C, H): one 256-token block; ragged tails with an odd head count (the
 # last group of four heads is partial); several ranges (partials + finalize);
 # more than 128 blocks, so each range spans two blocks; a single head; three
-# head groups of four, the last with one head, over two batches.  The grid deals
-# each XCD a run of tiles and runs the last round's tiles (when at most 16) as
-# half tiles of two heads: the cases up to here have runs of 16 tiles or fewer
-# (half tiles only).  272 tiles (runs of 34: 32 whole tiles, then 2 tiles as 4
-# halves) and 264 (runs of 33, a ragged block, three heads in the last group)
-# mix both kinds in each run; 132 tiles of two-block ranges give runs of 17
-# (whole tiles: a tail of 17 stays whole) and 16 (halves).
+# head groups of four, the last with one head, over two batches.  The grid
+# deals each XCD a run of tiles and cuts the tiles of the run's last round
+# (count % 32 of them) into parts when that helps: four one-head quarters when
+# at most 8, two two-head halves when at most 16.  Runs here: up to 9 tiles
+# (quarters only), except 65 tiles (runs of 8 and 9: quarters and halves);
+# 272 and 264 tiles (runs of 34 and 33: whole tiles, then quarters; the second
+# with a ragged block and three heads in the last group); 132 tiles of
+# two-block ranges (runs of 17, whole tiles only, and 16, halves only).
 CASES = [(1, 256, 32, 2), (2, 700, 96, 3), (1, 1000, 64, 4), (1, 5000, 128, 5), (1, 33000, 32, 2), (1, 300, 64, 1),
          (2, 600, 64, 9), (2, 17408, 32, 6), (2, 16740, 32, 7), (1, 33700, 32, 7)]
 
@@ -127,8 +128,10 @@ def _same(a, b, what):
     assert bool((a.view(torch.int32) == b.view(torch.int32)).all()), f"{what}: the two RoPE forms differ"
 
 
+# the first three run as quarter tiles (one head each); the last, 96 tiles in
+# runs of 12, as half tiles
 @pytest.mark.parametrize("B,N,C,H,grid,offset", [(2, 480, 64, 3, (3, 8, 20), 0), (1, 300, 96, 2, (4, 10, 12), 150),
-                                                 (1, 1000, 32, 5, (5, 10, 20), 0)])
+                                                 (1, 1000, 32, 5, (5, 10, 20), 0), (1, 12288, 32, 6, (12, 32, 32), 0)])
 def test_project_state_rope(B, N, C, H, grid, offset):
     """Keys rotated by the 3D RoPE at positions offset .. offset + N - 1, with
     the full tables and with the per-axis tables (bit-identical to each
@@ -183,12 +186,14 @@ def _check_apply(*args, **kw):
     assert ok, report
 
 
-# the last two cases mix whole tiles (eight heads) and half tiles (four heads):
-# 272 tiles (runs of 34 per XCD) and 264 (runs of 33, a ragged last block, six
-# heads in the second group)
+# Tile kinds (see CASES above; here a whole tile is eight heads, a half four
+# heads, a quarter four heads and 128 tokens): the first seven run as
+# quarters; 272 tiles (runs of 34 per XCD) and 264 (runs of 33, a ragged last
+# block, six heads in the second group) as whole tiles, then quarters; 96
+# tiles (runs of 12, a ragged last block) as halves.
 @pytest.mark.parametrize("B,N,C,H", [(1, 256, 32, 4), (2, 700, 96, 3), (1, 1000, 64, 6), (1, 5000, 128, 5),
                                      (1, 300, 64, 1), (2, 600, 64, 11), (1, 520, 32, 16), (2, 17408, 32, 12),
-                                     (1, 33700, 32, 14)])
+                                     (1, 33700, 32, 14), (1, 12132, 32, 12)])
 def test_project_apply_matches_oracle(B, N, C, H):
     print(f"case project_apply B={B} N={N} C={C} H={H}", flush=True)
     x = generate_projection(reduced(FULL, B=B, N=N, C=C, H=H, seed=N + C + 1), names=("x", "w_q"))
@@ -225,10 +230,12 @@ def test_project_apply_empty_touches_nothing():
 
 @pytest.mark.parametrize("N", [25500, 25444])
 def test_project_apply_many_blocks_ragged(N):
-    """300 workgroups (3 batch rows x 100 blocks x 1 group of eight heads,
-    H = 6): more than one round of resident workgroups (one per CU), and every
-    batch row ends in a ragged block (156 tokens, or 100, which leaves the
-    block's second 128 tokens empty)."""
+    """300 tiles (3 batch rows x 100 blocks x 1 group of eight heads, H = 6):
+    more than one round of resident workgroups (one per CU), and every batch
+    row ends in a ragged block (156 tokens, or 100, which leaves the block's
+    second 128 tokens empty).  The last XCD's run ends with blocks 295 .. 299
+    cut into quarter tiles of 128 tokens, so with N = 25444 one quarter of the
+    last block holds no token at all."""
     print(f"case project_apply many blocks N={N}", flush=True)
     x = generate_projection(reduced(FULL, B=3, N=N, C=64, H=6, seed=N), names=("x", "w_q"))
     S, z = _state_for(reduced(x.workload, N=2000), 10)
@@ -239,9 +246,11 @@ def test_project_apply_many_blocks_ragged(N):
 # (grid, offset, N, C, H): C = 64, 96 and 32 give 2, 3 and 1 channel steps,
 # so the angle table of the epilogue sits in each of the three LDS stages; the
 # third case has two groups of eight heads (the second partial) and a ragged
-# last block
+# last block.  These run as quarter tiles; the last case (96 tiles in runs of
+# 12) as half tiles.
 @pytest.mark.parametrize("grid,offset,N,C,H", [((3, 8, 20), 0, 480, 64, 6), ((4, 10, 12), 150, 330, 64, 6),
-                                               ((5, 10, 20), 0, 1000, 96, 9), ((4, 10, 12), 0, 480, 32, 3)])
+                                               ((5, 10, 20), 0, 1000, 96, 9), ((4, 10, 12), 0, 480, 32, 3),
+                                               ((12, 32, 32), 0, 12288, 32, 6)])
 def test_project_apply_rope_and_strided_output(grid, offset, N, C, H):
     """Queries rotated by the 3D RoPE (both table forms, bit-identical), and
     outputs written straight into a [B, N, H, D] buffer."""
