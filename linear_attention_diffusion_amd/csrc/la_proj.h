@@ -30,11 +30,15 @@
 // into the bf16 operands of S = phi(K)^T V and z = sum phi(K).  With RoPE,
 // phi(K) is rotated in fp32 first (the pair partner comes from the
 // neighbouring lane) and contracted as three bf16 parts; z stays unrotated.
+// The angles come from a table of the block's 256 tokens x 16 pairs that the
+// workgroup writes, once per block, into the LDS stage the GEMM left free.
 //
-// Blocks of the (token range, head group) grid are dealt to the XCDs in
+// Tiles of the (token range, head group) grid are dealt to the XCDs in
 // contiguous runs, and inside a run walk 4 token ranges per head group: the
 // workgroups resident on one XCD then share each x slice among several head
-// groups and each weight slice among 4 token ranges in its L2.
+// groups and each weight slice among 4 token ranges in its L2.  The tiles of
+// each XCD's last round, when few, run as halves or quarters (fewer heads, or
+// fewer tokens on the query side), so that round fills more of the XCD.
 //
 // The query side (project_apply_bf16, at the end) runs the same GEMM over eight
 // heads' query weights and hands each 16-token tile of Q to the apply pass's
