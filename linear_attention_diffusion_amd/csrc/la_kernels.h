@@ -1079,6 +1079,66 @@ __global__ __launch_bounds__(kThreads* HEADS) void apply_bf16(const u32x4_t* __r
 }
 
 // ---------------------------------------------------------------------------
+// Whole-head forward (bf16, dense layouts): state pass and apply in one launch
+// ---------------------------------------------------------------------------
+// When each head is one chunk taken by one workgroup (short sequences over
+// many heads), the workgroup that sums a head's state can apply it as well:
+// no partial, no finalize, no second launch.  Both halves are the passes' own
+// code -- the same four waves and chunk order, the same wave-tile sum, the
+// same apply tiles -- so the results are those of the two-launch path bit for
+// bit.  Each wave's first query chunk is loaded before the state work starts.
+// The full-table RoPE form is not taken here: its prefetched angle rows would
+// sit in registers through the state pass.
+template <int ROPE>
+__global__ __launch_bounds__(kThreads) void forward_whole_bf16(const u32x4_t* __restrict__ K,
+                                                               const u32x4_t* __restrict__ V,
+                                                               const u32x4_t* __restrict__ Q, u32x4_t* __restrict__ O,
+                                                               Layout lin, Layout lo, Rope rp, StateArgs a, int64_t N,
+                                                               float eps) {
+  static_assert(ROPE != kRopeTable, "the full-table form takes the two-launch path");
+  __shared__ float red[4][kStateElems];
+  __shared__ float angles[ROPE ? 4 : 1][ROPE ? kAngTile : 1];
+  __shared__ __attribute__((aligned(16))) float rtab[ROPE == kRopeAxes ? 2 * kMaxAxisTab : 1];
+  rope_stage<ROPE>(rp, rtab, threadIdx.x, kThreads);
+  if constexpr (ROPE == kRopeAxes) __syncthreads();
+  const int64_t bh = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15;
+  const int g = lane >> 4;
+  const char* Kh = reinterpret_cast<const char*>(K) + lin.base(bh) * 2;
+  const char* Vh = reinterpret_cast<const char*>(V) + lin.base(bh) * 2;
+  const char* Qh = reinterpret_cast<const char*>(Q) + lin.base(bh) * 2;
+  char* Oh = reinterpret_cast<char*>(O) + lo.base(bh) * 2;
+  const int lane_off = n * 64 + g * 16;  // features 8g .. 8g+7 of tile row n (64-byte rows)
+  const int64_t t0 = 64 * w;
+
+  ApplyChunk<ROPE> next;
+  if (t0 < N) load_apply_chunk<ROPE, 1>(Qh, 64, t0, N, lane_off, lane_off, n, g, rp, rtab, next);
+
+  f32x4_t acc[2][2], accz[2];
+  state_accumulate<ROPE, 1>(Kh, Vh, 64, t0, N, rp, rtab, angles[ROPE ? w : 0], g, n, acc, accz);
+  state_to_lds(acc, accz, red[w], g, n);
+  __syncthreads();
+  sum_wave_tiles(red, tid);
+  __syncthreads();
+  // the head's state: the carried one plus this sequence's, committed when
+  // asked, and kept in red[1] for the apply
+  for (int idx = tid; idx < kStateElems; idx += kThreads) {
+    const float x = carried(a, bh, idx) + red[0][idx];
+    red[1][idx] = x;
+    if (a.kv_out) commit(a, bh, idx, x);
+  }
+  __syncthreads();
+
+  ApplyOperands op;
+  load_apply_operands(red[1], red[1] + 1024, g, n, op);
+  const AxisLane al = axis_lane(rp, g);  // axis form only
+  apply_stream<ROPE, 1>(Qh, Oh, 64, 64, t0, N, lane_off, lane_off, lane_off, n, g, rp, rtab, al, op, eps, next);
+}
+
+// ---------------------------------------------------------------------------
 // fp32 apply pass (VALU): thread = (token, 4 output features)
 // ---------------------------------------------------------------------------
 // Workgroup (bh, c, tile) applies tokens [c*L + tile*Lt, ...) of chunk c.

@@ -471,6 +471,20 @@ int attend(const void* q, const void* k, const void* v, void* o, const sana_layo
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   const la::StateArgs a = state_args(ws, g, kv_in, ksum_in, kv_out, ksum_out);
   const RopeArg ra = rope_arg(rope, N);
+  // one chunk of one split per head, dense bf16 layouts: a head's state and
+  // its apply in one workgroup, one launch (the full-table RoPE form keeps
+  // the two passes)
+  if (dtype == SANA_DT_BF16 && g.C == 1 && g.Pc == 1 && vin.lay.token == la::kD && vout.lay.token == la::kD &&
+      ra.kind != la::kRopeTable) {
+    with_rope(ra.kind, [&](auto R) {
+      constexpr int RO = decltype(R)::value;
+      if constexpr (RO != la::kRopeTable)
+        la::forward_whole_bf16<RO><<<dim3((unsigned)g.BH), dim3(la::kThreads), 0, st>>>(
+            static_cast<const la::u32x4_t*>(k), static_cast<const la::u32x4_t*>(v),
+            static_cast<const la::u32x4_t*>(q), static_cast<la::u32x4_t*>(o), vin.lay, vout.lay, ra.r, a, N, eps);
+    });
+    return launch_status();
+  }
   launch_state(k, v, vin.lay, dtype, g, ra, a, st);
   launch_apply(q, o, vin.lay, vout.lay, dtype, eps, g, ra, ws_view(a), st);
   return launch_status();
