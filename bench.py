@@ -17,7 +17,11 @@ Inputs are resident in HBM before timing starts.  Several input/output sets
 Prints ONE JSON line.  `roofline` describes the dominant kernel, the apply
 pass (apply_bf16): after the main timed region it is launched on its own,
 through sana_linattn_apply on the state the forward computes, in the same
-launch configuration, and timed with HIP events on the launch stream.
+launch configuration, and timed with HIP events on the launch stream.  When
+the library runs each call as one kernel (every head one chunk of one split:
+sana_linattn_forward_launches returns 1), the dominant kernel is that one,
+forward_whole_bf16, and `roofline` takes the call's own bytes and time; the
+apply-alone figures are then in `apply_alone`.
 `cpu_baseline` times the float64 oracle on the host cores, in a child process
 whose BLAS/OpenMP thread counts are set, before NumPy loads, to the cores this
 process may run on.
@@ -65,18 +69,20 @@ def algorithmic_bytes(w):
     return b
 
 
-def stored_traffic(name):
+def stored_traffic(name, kernel=None):
     """HBM bytes per launch of the dominant kernel (of the forward, or of the
     backward for names "backward_<workload>"), from committed rocprofv3
     counter runs (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter
     reads for a copy kernel of known size), if they were taken on the current
-    kernel sources; else None."""
+    kernel sources (and, when `kernel` is given, for that kernel); else None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
     if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    if kernel is not None and rec.get("kernel") != kernel:
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -1022,6 +1028,19 @@ def main():
     launches = w.n_chunks if (w.mode == "block" and args.block_mode == "chunks") else 1
     call_ms = ms_per_step / launches
 
+    # kernels per call, from the library's own geometry: one launch (state and
+    # apply of a head in one workgroup) when every head is one chunk of one
+    # split; else the state pass and the apply, and the finalize when a head
+    # has several partials
+    rope_form = 0 if rope is None else (2 if rope.grid else 1)
+    if w.mode == "block" and args.block_mode == "chunks":
+        n_kernels = la.forward_launches(w.B, w.H, w.chunk, None, w.D, dt, rope_form, not packed)
+    else:
+        n_kernels = la.forward_launches(w.B, w.H, w.N, w.chunk if w.mode == "block" else None, w.D, dt, rope_form,
+                                        not packed)
+    kernels = {1: "state pass and apply in one launch (forward_whole_bf16)", 2: "state pass + apply pass",
+               3: "state pass + finalize + apply pass"}.get(n_kernels, "none")
+
     # roofline of the dominant kernel: the apply pass, launched alone on the
     # state of its head (one chunk's worth of tokens in block mode)
     n_apply = w.chunk if w.mode == "block" else w.N
@@ -1054,7 +1073,15 @@ def main():
     apply_ms = a_start.elapsed_time(a_end) / args.steps
     apply_bytes = w.B * w.H * n_apply * 2 * w.D * (2 if w.dtype == "bf16" else 4) + w.B * w.H * (32 * 32 + 32) * 4
     achieved = apply_bytes / (apply_ms / 1e3) / 1e9
-    traffic = stored_traffic(w.name)
+    roof_kernel = "apply_bf16" if w.dtype == "bf16" else "apply_f32"
+    roof_bytes, roof_ms, roof_tokens = apply_bytes, apply_ms, w.B * w.H * n_apply
+    if n_kernels == 1:
+        # the call is one kernel: its own bytes and time (the apply-alone
+        # figures stay in the record as `apply_alone`)
+        roof_kernel, roof_bytes, roof_ms = "forward_whole_bf16", alg_bytes / launches, call_ms
+        roof_tokens = w.token_heads // launches
+        achieved = roof_bytes / (roof_ms / 1e3) / 1e9
+    traffic = stored_traffic(w.name, roof_kernel)
 
     rec = {
         "metric": METRIC,
@@ -1075,22 +1102,25 @@ def main():
                    "layout": args.layout, "rope_form": args.rope_form if w.mode == "rope" else None},
         "roofline": {
             "bound": "hbm",
-            "kernel": "apply_bf16" if w.dtype == "bf16" else "apply_f32",
+            "kernel": roof_kernel,
             "achieved": achieved,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
             "traffic": traffic,
-            "algorithmic_bytes_per_launch": apply_bytes,
-            "avg_launch_ms": apply_ms,
-            "tokens_per_launch": w.B * w.H * n_apply,
+            "algorithmic_bytes_per_launch": roof_bytes,
+            "avg_launch_ms": roof_ms,
+            "tokens_per_launch": roof_tokens,
         },
+        "apply_alone": {"kernel": "apply_bf16" if w.dtype == "bf16" else "apply_f32", "avg_launch_ms": apply_ms,
+                        "algorithmic_bytes_per_launch": apply_bytes,
+                        "achieved_gbps": apply_bytes / (apply_ms / 1e3) / 1e9},
         "call": {
             "entry_point": ("sana_linattn_forward_strided (packed [B,N,3,H,D] in, [B,N,H,D] out)" if packed else
                             "sana_linattn_forward" if w.mode != "block" else
                             "sana_linattn_block_causal (whole sequence)" if args.block_mode == "sequence" else
                             "sana_linattn_block_forward (per chunk)"),
-            "kernels": "state pass + finalize + apply pass",
+            "kernels": kernels,
             "avg_ms": call_ms,
             "algorithmic_bytes": alg_bytes / launches,
             "achieved_gbps": (alg_bytes / launches) / (call_ms / 1e3) / 1e9,

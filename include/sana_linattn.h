@@ -143,6 +143,20 @@ typedef struct {
  * Returns 0 as well for invalid sizes; the entry points then reject them. */
 size_t sana_linattn_workspace_bytes(int B, int H, int64_t N, int D, int dtype, int has_rope);
 
+/* Kernel launches that one call of sana_linattn_forward (chunk = N),
+ * sana_linattn_block_forward (chunk = N) or sana_linattn_block_causal (chunk)
+ * makes for these sizes, for tools that report per-kernel figures.  1 when
+ * every head is one chunk taken by one workgroup (see the geometry in the
+ * implementation: at least 128 heads of at most 1024 tokens, or heads of at
+ * most 256) with bf16 data in dense layouts and no full-table RoPE: the state
+ * pass and the apply then run in one launch.  Otherwise 2 (state pass, apply)
+ * or 3 (with the finalize, when a head has several partials).  rope_form: 0
+ * none, 1 full tables, 2 per-axis tables; dense: 1 when Q, K, V and O are
+ * contiguous [B, H, N, D].  Pure host function, no HIP call; returns 0 when
+ * the call would launch nothing (B*H*N == 0) or for invalid arguments. */
+int sana_linattn_forward_launches(int B, int H, int64_t N, int64_t chunk, int D, int dtype, int rope_form,
+                                  int dense);
+
 /* Non-causal forward ("Sana" research note, Model architecture item 2;
  * "SANA-Video" paper notes 2.1, 2.2):
  *   O_i = phi~(Q_i) . S / (phi(Q_i) . z + eps) with S, z summed over all N

@@ -19,6 +19,7 @@ NOALLOC_SCRATCH_BYTES = 8 << 20  # SANA_NOALLOC_SCRATCH_BYTES in include/sana_li
 
 EXPORTED = (
     "sana_linattn_workspace_bytes",
+    "sana_linattn_forward_launches",
     "sana_linattn_forward",
     "sana_linattn_forward_strided",
     "sana_linattn_state_update",
@@ -70,6 +71,8 @@ def lib():
     rp = ctypes.POINTER(sana_rope)
     L.sana_linattn_workspace_bytes.argtypes = [i32, i32, i64, i32, i32, i32]
     L.sana_linattn_workspace_bytes.restype = sz
+    L.sana_linattn_forward_launches.argtypes = [i32, i32, i64, i64, i32, i32, i32, i32]
+    L.sana_linattn_forward_launches.restype = i32
     L.sana_linattn_forward.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32, i32, f32, rp, vp, sz, vp]
     L.sana_linattn_forward.restype = i32
     L.sana_linattn_state_update.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32, i32, rp, vp, sz, vp]
@@ -280,6 +283,13 @@ def rope3d_axes_device(T, Hl, Wl, device, D=32, split=(8, 12, 12), base=10000.0)
 
 def workspace_bytes(B, H, N, D=32, dtype=SANA_DT_BF16, has_rope=False):
     return int(lib().sana_linattn_workspace_bytes(B, H, N, D, dtype, int(bool(has_rope))))
+
+
+def forward_launches(B, H, N, chunk=None, D=32, dtype=SANA_DT_BF16, rope_form=0, dense=True):
+    """Kernel launches of one forward / block_forward (chunk None: one chunk)
+    or block_causal call; rope_form 0 none, 1 full tables, 2 per-axis."""
+    c = N if chunk is None else chunk
+    return int(lib().sana_linattn_forward_launches(B, H, N, c if c > 0 else 1, D, dtype, rope_form, int(bool(dense))))
 
 
 def make_workspace(B, H, N, device, D=32, dtype=SANA_DT_BF16, has_rope=False):

@@ -432,6 +432,12 @@ void launch_apply(const void* q, void* o, const la::Layout& lq, const la::Layout
 
 int launch_status() { return hipGetLastError() == hipSuccess ? SANA_OK : SANA_ERR_HIP; }
 
+// One launch per call (forward_whole_bf16): each head one chunk of one split,
+// dense bf16 layouts, no full-table RoPE.
+bool whole_head(int dtype, const Geometry& g, bool dense, int rope_kind) {
+  return dtype == SANA_DT_BF16 && g.C == 1 && g.Pc == 1 && dense && rope_kind != la::kRopeTable;
+}
+
 // Shared body of forward, block_forward and block_causal: chunks of L tokens
 // (L >= N for one chunk), carried state in, optional commit out.
 int attend(const void* q, const void* k, const void* v, void* o, const sana_layout* in, const sana_layout* out,
@@ -474,8 +480,7 @@ int attend(const void* q, const void* k, const void* v, void* o, const sana_layo
   // one chunk of one split per head, dense bf16 layouts: a head's state and
   // its apply in one workgroup, one launch (the full-table RoPE form keeps
   // the two passes)
-  if (dtype == SANA_DT_BF16 && g.C == 1 && g.Pc == 1 && vin.lay.token == la::kD && vout.lay.token == la::kD &&
-      ra.kind != la::kRopeTable) {
+  if (whole_head(dtype, g, vin.lay.token == la::kD && vout.lay.token == la::kD, ra.kind)) {
     with_rope(ra.kind, [&](auto R) {
       constexpr int RO = decltype(R)::value;
       if constexpr (RO != la::kRopeTable)
@@ -701,6 +706,18 @@ size_t sana_linattn_workspace_bytes(int B, int H, int64_t N, int D, int dtype, i
 size_t sana_linattn_block_causal_workspace_bytes(int B, int H, int64_t N, int64_t chunk, int D, int dtype,
                                                  int has_rope) {
   return workspace(B, H, N, chunk, D, dtype, has_rope);
+}
+
+int sana_linattn_forward_launches(int B, int H, int64_t N, int64_t chunk, int D, int dtype, int rope_form,
+                                  int dense) {
+  int64_t bh = 0, elems = 0;
+  if (chunk <= 0 || rope_form < 0 || rope_form > 2 || check_sizes(B, H, N, D, dtype, &bh, &elems) != SANA_OK)
+    return 0;
+  if (elems == 0) return 0;
+  const int kind = rope_form == 2 ? la::kRopeAxes : (rope_form == 1 ? la::kRopeTable : la::kRopeNone);
+  const Geometry g = make_geometry(bh, N, chunk, rope_form != 0);
+  if (whole_head(dtype, g, dense != 0, kind)) return 1;
+  return g.C * g.Pc > 1 ? 3 : 2;
 }
 
 int sana_linattn_forward(const void* q, const void* k, const void* v, void* o, int B, int H, int64_t N, int D,

@@ -40,6 +40,11 @@ int main() {
   EXPECT(sana_linattn_workspace_bytes(1, 2, 10, 64, BF, 0), 0);
   EXPECT(sana_linattn_workspace_bytes(1, 2, -1, 32, BF, 0), 0);
   EXPECT(sana_linattn_workspace_bytes(1, 2, 10, 32, 9, 0), 0);
+  EXPECT(sana_linattn_forward_launches(0, 2, 10, 10, 32, BF, 0, 1), 0);
+  EXPECT(sana_linattn_forward_launches(1, 2, 10, 0, 32, BF, 0, 1), 0);
+  EXPECT(sana_linattn_forward_launches(1, 2, 10, 10, 32, BF, 5, 1), 0);
+  EXPECT(sana_linattn_forward_launches(1, 2, -3, 10, 32, BF, 0, 1), 0);
+  EXPECT(sana_linattn_forward_launches(4, 36, 1024, 1024, 32, BF, 0, 1), 1);
   for (int B = 1; B <= 3; ++B)
     for (int H = 1; H <= 80; H += 13)
       for (int64_t N : {1LL, 63LL, 1024LL, 4680LL, 16384LL, 1000003LL}) {
@@ -51,6 +56,11 @@ int main() {
         for (int64_t chunk : {1LL, 7LL, 4680LL})
           if (sana_linattn_block_causal_workspace_bytes(B, H, N, chunk, 32, BF, 1) == 0) ++failures;
         (void)sana_linattn_project_state_workspace_bytes(B, H, N, 2240, 32, BF);
+        for (int form = 0; form <= 2; ++form) {
+          const int n = sana_linattn_forward_launches(B, H, N, N, 32, BF, form, 1);
+          if (n < 1 || n > 3) ++failures;
+          if (sana_linattn_forward_launches(B, H, N, 1000, 32, BF, form, 0) < 2) ++failures;
+        }
       }
   EXPECT(sana_linattn_block_causal_workspace_bytes(1, 2, 100, 0, 32, BF, 0), 0);
   EXPECT(sana_linattn_backward_workspace_bytes(1, 2, 100, -3, 32, BF, 0), 0);

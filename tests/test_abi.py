@@ -523,3 +523,27 @@ def test_strided_layout_validation():
     assert fwd(packed, la.sana_layout(N * H * D, 0, H * D)) == la.SANA_ERR_INVALID      # heads of o alias
     assert fwd(packed, la.sana_layout(N * H * D, D, D)) == la.SANA_ERR_INVALID          # tokens of o overlap heads
     assert fwd(packed, bnhd, o=QKV + 64) == la.SANA_ERR_INVALID                         # o inside the inputs' span
+
+
+def test_forward_launches_follows_the_geometry():
+    """The launch-count query: one launch when every head is one chunk of one
+    split (the Sana-0.6B 1024 px layer: 144 heads of 1024 tokens; any head of
+    at most 256 tokens) with dense bf16 and no full-table RoPE; otherwise the
+    state pass and the apply, plus the finalize when a head has several
+    partials."""
+    bf16, f32 = la.SANA_DT_BF16, la.SANA_DT_F32
+    assert la.forward_launches(4, 36, 1024) == 1
+    assert la.forward_launches(4, 36, 1024, rope_form=2) == 1
+    assert la.forward_launches(4, 36, 1024, rope_form=1) == 2
+    assert la.forward_launches(4, 36, 1024, dense=False) == 2
+    assert la.forward_launches(4, 36, 1024, dtype=f32) == 2
+    assert la.forward_launches(1, 3, 200) == 1
+    assert la.forward_launches(1, 70, 16384) == 3
+    assert la.forward_launches(1, 70, 4680) == 3
+    assert la.forward_launches(1, 70, 46800, chunk=4680) == 3
+    assert la.forward_launches(1, 70, 512, chunk=256) == 3
+    assert la.forward_launches(1, 2, 0) == 0
+    assert la.forward_launches(1, 2, 100, D=64) == 0
+    assert la.forward_launches(1, 2, 100, rope_form=3) == 0
+    assert bf16 != f32
+
