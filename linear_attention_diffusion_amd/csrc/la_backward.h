@@ -66,9 +66,11 @@ __device__ __forceinline__ f32x4_t rotate4(f32x4_t x, const Rope& rp, const floa
 //
 // One thread per state element of every head.  It starts from the gradient
 // reaching the committed state (kv_in/ksum_in of `a`, or 0), walks the head's
-// C x Pc partials from the last to the first, 16 loads in flight at a time,
-// stores the running sum at the start of every chunk (G_c) and commits the
-// total (G_0, the gradient of the carried state) to kv_out/ksum_out.
+// C x Pc partials from the last to the first, BATCH loads in flight at a time
+// (issued unconditionally, as in state_finalize), stores the running sum at
+// the start of every chunk (G_c) and commits the total (G_0, the gradient of
+// the carried state) to kv_out/ksum_out.
+template <int BATCH>
 __global__ __launch_bounds__(kThreads) void state_finalize_reverse(StateArgs a, int64_t n_elems) {
   const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (i >= n_elems) return;
@@ -78,15 +80,25 @@ __global__ __launch_bounds__(kThreads) void state_finalize_reverse(StateArgs a, 
   const float* src = a.partials + bh * total * kStateElems + idx;
   float* dst = a.states + bh * a.C * kStateElems + idx;
   float acc = carried(a, bh, idx);
-  for (int q0 = total - 1; q0 >= 0; q0 -= 16) {
-    float v[16];
+  int c = a.C - 1, s = a.Pc - 1;  // chunk and split of the next partial
+  for (int q1 = total; q1 > 0; q1 -= BATCH) {
+    // slot u holds partial q1 - 1 - u (the first partial again once past it)
+    const int nb = q1 < BATCH ? q1 : BATCH;
+    float v[BATCH];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) v[u] = (q0 - u >= 0) ? src[(int64_t)(q0 - u) * kStateElems] : 0.f;
+    for (int u = 0; u < BATCH; ++u) v[u] = src[(int64_t)max(q1 - 1 - u, 0) * kStateElems];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int q = q0 - u;
-      acc += v[u];
-      if (q >= 0 && q % a.Pc == 0) dst[(int64_t)(q / a.Pc) * kStateElems] = acc;
+    for (int u = 0; u < BATCH; ++u) {
+      if (u < nb) {
+        acc += v[u];
+        if (s == 0) {
+          dst[(int64_t)c * kStateElems] = acc;
+          s = a.Pc - 1;
+          --c;
+        } else {
+          --s;
+        }
+      }
     }
   }
   if (a.kv_out) commit(a, bh, idx, acc);

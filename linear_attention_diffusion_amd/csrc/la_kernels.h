@@ -411,11 +411,19 @@ __device__ __forceinline__ void write_partial(const float* mine, int64_t bh, int
 }
 
 // One thread per state element of every head.  It walks the head's C x Pc
-// partials in order, 16 loads in flight at a time (loads past the end read 0,
-// which leaves the ordered sum unchanged), adding each to the carried state,
-// and stores the running sum at the end of every chunk; the last one is also
-// committed.  kv_out may alias kv_in: each element is read and written by the
-// same thread.
+// partials in order, BATCH loads in flight at a time, adding each to the
+// carried state, and stores the running sum at the end of every chunk; the
+// last one is also committed.  kv_out may alias kv_in: each element is read
+// and written by the same thread.
+//
+// The loads of a batch go out unconditionally, those past the head's last
+// partial reading that partial again (unused): a predicated load per partial
+// leaves the compiler unable to keep them in flight together.  The host takes
+// BATCH = 16 for up to 16 partials per head and 64 above: the fused
+// projections leave one partial per 256-token range, 64-73 per head on the
+// large layers, and a wave then has 64 x 256 B in flight instead of walking
+// them in four or five round trips.
+template <int BATCH>
 __global__ __launch_bounds__(kThreads) void state_finalize(StateArgs a, int64_t n_elems) {
   const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (i >= n_elems) return;
@@ -425,15 +433,22 @@ __global__ __launch_bounds__(kThreads) void state_finalize(StateArgs a, int64_t 
   const float* src = a.partials + bh * total * kStateElems + idx;
   float* dst = a.states + bh * a.C * kStateElems + idx;
   float acc = carried(a, bh, idx);
-  for (int q0 = 0; q0 < total; q0 += 16) {
-    float v[16];
+  int c = 0, s = 0;  // chunk and split of the next partial
+  for (int q0 = 0; q0 < total; q0 += BATCH) {
+    float v[BATCH];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) v[u] = (q0 + u < total) ? src[(int64_t)(q0 + u) * kStateElems] : 0.f;
+    for (int u = 0; u < BATCH; ++u) v[u] = src[(int64_t)min(q0 + u, total - 1) * kStateElems];
+    const int nb = total - q0;
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int q = q0 + u;
-      acc += v[u];
-      if (q < total && (q + 1) % a.Pc == 0) dst[(int64_t)(q / a.Pc) * kStateElems] = acc;
+    for (int u = 0; u < BATCH; ++u) {
+      if (u < nb) {
+        acc += v[u];
+        if (++s == a.Pc) {
+          dst[(int64_t)c * kStateElems] = acc;
+          s = 0;
+          ++c;
+        }
+      }
     }
   }
   if (a.kv_out) commit(a, bh, idx, acc);

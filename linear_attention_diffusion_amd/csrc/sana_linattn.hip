@@ -368,6 +368,27 @@ void with_rope(int kind, F&& f) {
     f(std::integral_constant<int, la::kRopeNone>{});
 }
 
+// The ordered sum of every head's C x Pc partials into its chunk states
+// (reverse: the suffix sums of the backward pass), one thread per state
+// element, with 16 partials in flight per thread, or 64 when a head has more
+// than 16.
+void launch_finalize(const la::StateArgs& a, int64_t BH, hipStream_t st, bool reverse = false) {
+  const int64_t n_elems = BH * la::kStateElems;
+  const dim3 grid((unsigned)ceil_div(n_elems, la::kThreads)), block(la::kThreads);
+  const bool deep = a.C * a.Pc > 16;
+  if (reverse) {
+    if (deep)
+      la::state_finalize_reverse<64><<<grid, block, 0, st>>>(a, n_elems);
+    else
+      la::state_finalize_reverse<16><<<grid, block, 0, st>>>(a, n_elems);
+  } else {
+    if (deep)
+      la::state_finalize<64><<<grid, block, 0, st>>>(a, n_elems);
+    else
+      la::state_finalize<16><<<grid, block, 0, st>>>(a, n_elems);
+  }
+}
+
 // State pass, and the finalize when there are several partials per head.
 void launch_state(const void* k, const void* v, const la::Layout& lkv, int dtype, const Geometry& g,
                   const RopeArg& ra, const la::StateArgs& a, hipStream_t st) {
@@ -391,10 +412,7 @@ void launch_state(const void* k, const void* v, const la::Layout& lkv, int dtype
                                                 ra.r, a);
     }
   });
-  if (g.C * g.Pc > 1) {
-    const int64_t n_elems = g.BH * la::kStateElems;
-    la::state_finalize<<<dim3((unsigned)ceil_div(n_elems, la::kThreads)), dim3(la::kThreads), 0, st>>>(a, n_elems);
-  }
+  if (g.C * g.Pc > 1) launch_finalize(a, g.BH, st);
 }
 
 void launch_apply(const void* q, void* o, const la::Layout& lq, const la::Layout& lo, int dtype, float eps,
@@ -556,10 +574,7 @@ void launch_backward(const void* q, const void* k, const void* v, const void* do
                                                      static_cast<float*>(dq), lin, lout, view, eps, ra.r, bwd);
     }
   });
-  if (g.C * g.Pc > 1) {
-    const int64_t n_elems = g.BH * la::kStateElems;
-    la::state_finalize_reverse<<<dim3((unsigned)ceil_div(n_elems, la::kThreads)), block, 0, st>>>(bwd, n_elems);
-  }
+  if (g.C * g.Pc > 1) launch_finalize(bwd, g.BH, st, true);
   launch_key_pass(k, v, dk, dv, lin, lout, dtype, g, ra, view, st);
 }
 
@@ -1029,10 +1044,7 @@ int sana_linattn_project_state(const void* x, const void* w_k, const void* w_v, 
     constexpr int RO = decltype(R)::value;
     la::project_state_bf16<RO><<<dim3(la::proj_grid(p.G)), dim3(la::kProjThreads), 0, st>>>(p, ra.r, a);
   });
-  if (g.R > 1) {
-    const int64_t n_elems = g.BH * la::kStateElems;
-    la::state_finalize<<<dim3((unsigned)ceil_div(n_elems, la::kThreads)), dim3(la::kThreads), 0, st>>>(a, n_elems);
-  }
+  if (g.R > 1) launch_finalize(a, g.BH, st);
   return launch_status();
 }
 

@@ -76,6 +76,9 @@ SMALL = [
     ("bf16", 1, 4, 5000, 4680, None, True, True),
     ("bf16", 1, 3, 2000, 333, (5, 20, 20), True, True),
     ("bf16", 1, 2, 4097, None, (17, 1, 241), False, False),
+    # 14 chunks x 6 splits: 84 partials per head, so both finalize directions
+    # walk two batches with chunk ends inside each
+    ("bf16", 1, 2, 20000, 1500, None, True, True),
 ]
 
 
