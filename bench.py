@@ -488,7 +488,7 @@ def project_bench(args, dev, stream):
         "config": {"workload": p.name, "pass": "project_state", "B": p.B, "N": p.N, "C": p.C, "H": p.H, "D": p.D,
                    "rope": rope_name, "input_sets_cycled": n_sets},
         "roofline": {"bound": "mfma", "kernel": "project_state_bf16", "achieved": tflops, "peak": 2500.0,
-                     "unit": "TFLOP/s", "frac": tflops / 2500.0, "traffic": stored_traffic("project_4096px") if rope is None else None,
+                     "unit": "TFLOP/s", "frac": tflops / 2500.0, "traffic": stored_traffic("project_4096px" if rope is None else "project_720p_rope3d"),
                      "algorithmic_flops_per_launch": flops, "avg_launch_ms": ms},
         "two_pass": {"gemm_ms": ms_gemm, "state_update_ms": ms_state, "total_ms": ms_gemm + ms_state,
                      "gemm_tflops": 2.0 * p.B * p.N * p.C * (2 * p.H * 32) / (ms_gemm / 1e3) / 1e12,
@@ -595,7 +595,7 @@ def project_apply_bench(args, dev, stream):
                    "rope": rope_name, "input_sets_cycled": n_sets},
         "roofline": {"bound": "mfma", "kernel": "project_apply_bf16", "achieved": tflops, "peak": 2500.0,
                      "unit": "TFLOP/s", "frac": tflops / 2500.0,
-                     "traffic": stored_traffic("project_apply_4096px") if rope is None else None,
+                     "traffic": stored_traffic("project_apply_4096px" if rope is None else "project_apply_720p_rope3d"),
                      "algorithmic_flops_per_launch": flops, "avg_launch_ms": ms},
         "two_pass": {"gemm_ms": ms_gemm, "apply_ms": ms_apply, "total_ms": ms_gemm + ms_apply,
                      "gemm_tflops": 2.0 * p.B * p.N * p.C * (p.H * 32) / (ms_gemm / 1e3) / 1e12,

@@ -462,6 +462,13 @@ int sana_linattn_rope3d_axes(int T, int Hl, int Wl, int D, int dt, int dh, int d
 /* Static string naming a status code. */
 const char* sana_linattn_status_string(int status);
 
+/* Static string: the first 16 hex digits of the SHA-256 over the kernel
+ * sources the library was compiled from (every csrc *.h and *.hip file, its
+ * name, a zero byte, then its bytes, in name order), as the build passes it in;
+ * "unknown" for a build that did not.  A caller holding the sources can compare
+ * it with their hash and refuse a library built from other sources. */
+const char* sana_linattn_source_hash(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -11,6 +11,7 @@ import os
 
 import numpy as np
 
+from . import build as _build
 from .build import LIB_PATH
 
 SANA_OK, SANA_ERR_INVALID, SANA_ERR_UNSUPPORTED, SANA_ERR_WORKSPACE, SANA_ERR_HIP = 0, -1, -2, -3, -4
@@ -42,6 +43,7 @@ EXPORTED = (
     "sana_linattn_rope3d_table",
     "sana_linattn_rope3d_axes",
     "sana_linattn_status_string",
+    "sana_linattn_source_hash",
 )
 
 
@@ -127,6 +129,16 @@ def lib():
     L.sana_linattn_rope3d_axes.restype = i32
     L.sana_linattn_status_string.argtypes = [i32]
     L.sana_linattn_status_string.restype = ctypes.c_char_p
+    L.sana_linattn_source_hash.argtypes = []
+    L.sana_linattn_source_hash.restype = ctypes.c_char_p
+    # refuse a library older than the kernel sources next to it
+    csrc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(LIB_PATH))), "csrc")
+    if os.path.isdir(csrc):
+        built, want = L.sana_linattn_source_hash().decode(), _build.source_hash(csrc)
+        if built != want:
+            raise ImportError(f"{LIB_PATH} was compiled from other kernel sources ({built}) than those in {csrc} "
+                              f"({want}): run __graft_entry__.build() (or python -m "
+                              "linear_attention_diffusion_amd.build) first")
     _LIB = L
     return L
 

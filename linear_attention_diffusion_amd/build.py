@@ -4,6 +4,7 @@ hipcc cross-compiles without a GPU.  The library lands in
 linear_attention_diffusion_amd/_lib/ next to this file.
 """
 
+import hashlib
 import os
 import shutil
 import subprocess
@@ -32,6 +33,18 @@ FLAGS = [
 ]
 
 
+def source_hash(csrc=CSRC):
+    """sha256[:16] over the kernel sources in `csrc` (every *.h and *.hip, by
+    name then content, in name order); compiled into the library, whose
+    sana_linattn_source_hash() returns it."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".h", ".hip")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
 def hipcc():
     exe = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(exe):
@@ -43,7 +56,7 @@ def build(verbose=False):
     """Compile every HIP source into LIB_PATH (always recompiles)."""
     os.makedirs(LIB_DIR, exist_ok=True)
     tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), *FLAGS, "-I", INCLUDE, "-I", CSRC,
+    cmd = [hipcc(), *FLAGS, f'-DSANA_SOURCE_HASH="{source_hash()}"', "-I", INCLUDE, "-I", CSRC,
            *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
     if verbose:
         print(" ".join(cmd), file=sys.stderr)

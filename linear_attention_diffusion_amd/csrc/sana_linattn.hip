@@ -39,6 +39,11 @@
 #include "la_lines.h"
 #include "la_proj.h"
 
+// sha256[:16] of the kernel sources, passed in by the build
+#ifndef SANA_SOURCE_HASH
+#define SANA_SOURCE_HASH "unknown"
+#endif
+
 // Scratch of sana_linattn_block_forward_noalloc: one copy per GPU.  In host
 // code this name is a stand-in, not a device address; host code uses only the
 // address that scratch_address() looks up.
@@ -1094,6 +1099,8 @@ int sana_linattn_project_apply(const void* x, const void* w_q, void* o, const sa
   });
   return launch_status();
 }
+
+const char* sana_linattn_source_hash(void) { return SANA_SOURCE_HASH; }
 
 const char* sana_linattn_status_string(int status) {
   switch (status) {

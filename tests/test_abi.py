@@ -547,3 +547,10 @@ def test_forward_launches_follows_the_geometry():
     assert la.forward_launches(1, 2, 100, rope_form=3) == 0
     assert bf16 != f32
 
+
+
+def test_library_was_built_from_these_sources():
+    """The library reports the hash of the kernel sources it was compiled
+    from; the loader refuses one built from other sources."""
+    from linear_attention_diffusion_amd import build
+    assert la.binding.lib().sana_linattn_source_hash().decode() == build.source_hash()
