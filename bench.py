@@ -214,7 +214,11 @@ def copy_probe(steps, warmup, nbytes=2 ** 30):
     also the kernel whose FETCH_SIZE / WRITE_SIZE counters scale the traffic
     figures), a pure 1 GiB write (torch fill_), a 1 GiB read reduced to one
     number (torch sum), and this library's read-only state pass over a large
-    K, V (70 heads x 65536 tokens, 587 MB, sana_linattn_state_update)."""
+    K, V (70 heads x 65536 tokens, 587 MB, sana_linattn_state_update).  Also
+    the floor of a dependent launch: 500 back-to-back fills of a 1 KB buffer
+    (one workgroup) and of a 2 MB buffer (torch's fill kernel, 512 workgroups of
+    256), each waiting for the one before, as the passes of one call do,
+    replayed from a HIP graph so that the host's per-call cost does not enter."""
     import torch
 
     import linear_attention_diffusion_amd as la
@@ -237,6 +241,21 @@ def copy_probe(steps, warmup, nbytes=2 ** 30):
     ms_copy = timed(lambda: dst.copy_(src))
     ms_fill = timed(lambda: dst.fill_(2.0))
     ms_sum = timed(lambda: src.sum())
+    def graph_launch_us(t, n=500):
+        # n dependent fills captured once and replayed, so that the host's
+        # per-call cost does not enter; fill_ with a non-zero value is a kernel
+        stream = torch.cuda.Stream()
+        with torch.cuda.stream(stream):
+            t.fill_(3.0)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=stream):
+                for _ in range(n):
+                    t.fill_(3.0)
+        return timed(graph.replay, n=4) * 1e3 / n
+
+    launch_us_1 = graph_launch_us(torch.empty(256, dtype=torch.float32, device=dev))
+    launch_us_512 = graph_launch_us(torch.empty(512 * 1024, dtype=torch.float32, device=dev))
     H, N = 70, 65536
     g = torch.Generator(device="cpu").manual_seed(1)
     kv = [tuple((torch.randn(1, H, N, 32, generator=g) * 0.5).to(torch.bfloat16).to(dev) for _ in range(2))
@@ -259,7 +278,8 @@ def copy_probe(steps, warmup, nbytes=2 ** 30):
                       "ms_per_copy": ms_copy, "gbps_read_plus_write": gbps(2 * nbytes, ms_copy),
                       "fill_gbps_write": gbps(nbytes, ms_fill), "sum_gbps_read": gbps(nbytes, ms_sum),
                       "state_pass_gbps_read": gbps(kv_bytes, ms_state), "state_pass_bytes": kv_bytes,
-                      "state_pass_ms": ms_state}), flush=True)
+                      "state_pass_ms": ms_state, "dependent_launch_us_1kb_fill": launch_us_1,
+                      "dependent_launch_us_2mb_fill": launch_us_512}), flush=True)
 
 
 def conv_bench(args, dev, stream):
