@@ -1060,6 +1060,15 @@ def main():
                                         not packed)
     kernels = {1: "state pass and apply in one launch (forward_whole_bf16)", 2: "state pass + apply pass",
                3: "state pass + finalize + apply pass"}.get(n_kernels, "none")
+    # two launches where a head has several partials: the apply sums them
+    # itself (apply_fold_bf16); the same geometry read through a strided view
+    # would take three
+    n_call = w.chunk if (w.mode == "block" and args.block_mode == "chunks") else w.N
+    folded = n_kernels == 2 and la.forward_launches(
+        w.B, w.H, n_call, w.chunk if (w.mode == "block" and args.block_mode != "chunks") else None, w.D, dt,
+        rope_form, False) == 3
+    if folded:
+        kernels = "state pass + apply that sums the partials (apply_fold_bf16)"
 
     # roofline of the dominant kernel: the apply pass, launched alone on the
     # state of its head (one chunk's worth of tokens in block mode)
@@ -1095,10 +1104,12 @@ def main():
     achieved = apply_bytes / (apply_ms / 1e3) / 1e9
     roof_kernel = "apply_bf16" if w.dtype == "bf16" else "apply_f32"
     roof_bytes, roof_ms, roof_tokens = apply_bytes, apply_ms, w.B * w.H * n_apply
-    if n_kernels == 1:
-        # the call is one kernel: its own bytes and time (the apply-alone
+    if n_kernels == 1 or folded:
+        # the call is one kernel, or the state pass and the apply that does the
+        # finalize's work: the call's own bytes and time (the apply-alone
         # figures stay in the record as `apply_alone`)
-        roof_kernel, roof_bytes, roof_ms = "forward_whole_bf16", alg_bytes / launches, call_ms
+        roof_kernel = "forward_whole_bf16" if n_kernels == 1 else "state_bf16+apply_fold_bf16"
+        roof_bytes, roof_ms = alg_bytes / launches, call_ms
         roof_tokens = w.token_heads // launches
         achieved = roof_bytes / (roof_ms / 1e3) / 1e9
     traffic = stored_traffic(w.name, roof_kernel)

@@ -476,6 +476,27 @@ __device__ __forceinline__ void state_item(const StateArgs& a, int64_t& bh, int&
   n_end = (n_begin + a.Ls < c_end) ? n_begin + a.Ls : c_end;
 }
 
+// The same items dealt XCD by XCD: workgroup b runs on XCD b % 8 (MI355X), and
+// heads x, x + 8, x + 16, ... take the slots b / 8 of XCD x, all of a head's
+// items on one XCD.  Slots past the last head are left without a head
+// (bh >= BH).  For the apply that sums the partials itself (apply_fold_bf16),
+// whose workgroups of a head sit on the same XCD.
+constexpr int kXcdCount = 8;
+
+__device__ __forceinline__ void state_item_xcd(const StateArgs& a, int64_t& bh, int& c, int& s, int64_t& n_begin,
+                                               int64_t& n_end) {
+  const int per_head = a.C * a.Pc;
+  const int slot = blockIdx.x / kXcdCount;
+  bh = blockIdx.x % kXcdCount + (int64_t)kXcdCount * (slot / per_head);
+  const int r = slot % per_head;
+  c = r / a.Pc;
+  s = r % a.Pc;
+  const int64_t c_begin = (int64_t)c * a.L;
+  const int64_t c_end = (c_begin + a.L < a.N) ? c_begin + a.L : a.N;
+  n_begin = c_begin + (int64_t)s * a.Ls;
+  n_end = (n_begin + a.Ls < c_end) ? n_begin + a.Ls : c_end;
+}
+
 // ---------------------------------------------------------------------------
 // bf16 state pass: split-N partial S and z with MFMA
 // ---------------------------------------------------------------------------
@@ -776,7 +797,8 @@ __device__ __forceinline__ void sum_wave_tiles(float (*r)[kStateElems], int tid)
 
 // DENSE: consecutive tokens are adjacent 64-byte rows (token stride = 32
 // elements), so every tile offset is an instruction immediate.
-template <int ROPE, bool DENSE, int HEADS>
+// XCD: items dealt by state_item_xcd (one head per workgroup only).
+template <int ROPE, bool DENSE, int HEADS, bool XCD = false>
 __global__ __launch_bounds__(kThreads* HEADS) void state_bf16(const u32x4_t* __restrict__ K,
                                                               const u32x4_t* __restrict__ V, Layout lkv, Rope rp,
                                                               StateArgs a, int64_t BH) {
@@ -788,7 +810,12 @@ __global__ __launch_bounds__(kThreads* HEADS) void state_bf16(const u32x4_t* __r
 
   int64_t bh, n_begin, n_end;
   int c, s;
-  state_item(a, bh, c, s, n_begin, n_end, HEADS == 2 ? (BH + 1) / 2 : 0);
+  if constexpr (XCD) {
+    static_assert(HEADS == 1, "XCD-dealt items take one head per workgroup");
+    state_item_xcd(a, bh, c, s, n_begin, n_end);
+  } else {
+    state_item(a, bh, c, s, n_begin, n_end, HEADS == 2 ? (BH + 1) / 2 : 0);
+  }
   const int lane = threadIdx.x & 63;
   const int wg = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int half = wg >> 2;  // which of the workgroup's heads
@@ -1014,18 +1041,20 @@ __device__ __forceinline__ void load_apply_chunk(const char* Qh, int64_t row, in
   // the axis form's angles come from LDS when the tile is computed
 }
 
-// A wave's 64-token chunks t0, t0 + 256, ... below n_end of one head, the
-// first of which `next` already holds (loaded before the state operands were
-// fetched): each chunk's loads go out before the previous chunk is computed.
+// A wave's 64-token chunks t0, t0 + step, ... below n_end of one head (step:
+// 64 tokens per wave of the workgroup), the first of which `next` already
+// holds (loaded before the state operands were fetched): each chunk's loads go
+// out before the previous chunk is computed.
 template <int ROPE, int HEADS>
 __device__ __forceinline__ void apply_stream(const char* Qh, char* Oh, int64_t qrow, int64_t orow, int64_t t0,
                                              int64_t n_end, int q_off, int o_off, int tab_off, int m, int g,
                                              const Rope& rp, const float* rtab, const AxisLane& al,
-                                             const ApplyOperands& op, float eps, ApplyChunk<ROPE>& next) {
-  for (; t0 < n_end; t0 += 256) {
+                                             const ApplyOperands& op, float eps, ApplyChunk<ROPE>& next,
+                                             int step = 256) {
+  for (; t0 < n_end; t0 += step) {
     const ApplyChunk<ROPE> cur = next;
-    if (t0 + 256 < n_end)
-      load_apply_chunk<ROPE, HEADS>(Qh, qrow, t0 + 256, n_end, q_off, tab_off, m, g, rp, rtab, next);
+    if (t0 + step < n_end)
+      load_apply_chunk<ROPE, HEADS>(Qh, qrow, t0 + step, n_end, q_off, tab_off, m, g, rp, rtab, next);
     const rsrc_t ro = rows_rsrc(Oh, t0, n_end, orow);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -1151,6 +1180,101 @@ __global__ __launch_bounds__(kThreads) void forward_whole_bf16(const u32x4_t* __
   load_apply_operands(red[1], red[1] + 1024, g, n, op);
   const AxisLane al = axis_lane(rp, g);  // axis form only
   apply_stream<ROPE, 1>(Qh, Oh, 64, 64, t0, N, lane_off, lane_off, lane_off, n, g, rp, rtab, al, op, eps, next);
+}
+
+// ---------------------------------------------------------------------------
+// Apply with the finalize folded in (bf16, dense, no RoPE, one chunk)
+// ---------------------------------------------------------------------------
+// Two launches per call instead of three: the state pass (items dealt XCD by
+// XCD) leaves each head's Pc partials, and each of the head's P apply
+// workgroups of WAVES waves, on the same XCD, sums them itself onto the carried
+// state, in split order as the finalize does, before applying the state to
+// its 1/P of the queries.  The state, the saved chunk state (part 0) and the
+// commit (part P - 1) are the finalize's bit for bit, and the apply tiles are
+// apply_bf16's, so the results are the three-launch path's.
+//
+// Commit.  When kv_out may alias kv_in, parts 0 .. P-2 publish per call that
+// they have read the carried state (flags[bh * P + p] = epoch, a number the
+// host takes fresh for every call), and part P - 1 waits for those words
+// before it stores.  Its siblings have lower block numbers on the same XCD,
+// so they were dispatched before it and every wait ends; the spin is bounded
+// as well.
+constexpr int kFoldMaxSplits = 16;
+constexpr int kFoldSpinLimit = 1 << 22;
+
+struct FoldArgs {
+  int64_t Na;        // queries per part (a multiple of 64)
+  unsigned* flags;   // [BH][P] arrival words (commit over a carried state), else null
+  unsigned epoch;    // this call's number
+  int P;             // workgroups per head
+};
+
+template <int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void apply_fold_bf16(const u32x4_t* __restrict__ Q, u32x4_t* __restrict__ O,
+                                                              Layout lq, Layout lo, StateArgs a, FoldArgs f, int64_t BH,
+                                                              float eps) {
+  constexpr int kFoldThreads = 64 * WAVES;
+  __shared__ float st[kStateElems];
+  const int slot = blockIdx.x / kXcdCount;
+  const int64_t bh = blockIdx.x % kXcdCount + (int64_t)kXcdCount * (slot / f.P);
+  const int p = slot % f.P;
+  if (bh >= BH) return;
+  const int64_t N = a.N;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int m = lane & 15;
+  const int g = lane >> 4;
+  const char* Qh = reinterpret_cast<const char*>(Q) + lq.base(bh) * 2;
+  char* Oh = reinterpret_cast<char*>(O) + lo.base(bh) * 2;
+  const int lane_off = m * 64 + g * 16;
+
+  // this part's queries: each wave's first chunk goes out first
+  const int64_t q_begin = (int64_t)p * f.Na;
+  const int64_t q_end = (q_begin + f.Na < N) ? q_begin + f.Na : N;
+  const int64_t t0 = q_begin + 64 * wave;
+  const Rope rp{};
+  ApplyChunk<kRopeNone> next;
+  if (t0 < q_end) load_apply_chunk<kRopeNone, 1>(Qh, 64, t0, q_end, lane_off, lane_off, m, g, rp, nullptr, next);
+
+  // the head's state: the carried one plus the partials in split order; the
+  // loads go out together (those past the last partial re-read it, unused)
+  const float* src = a.partials + bh * a.Pc * kStateElems;
+  for (int idx = tid; idx < kStateElems; idx += kFoldThreads) {
+    float v[kFoldMaxSplits];
+#pragma unroll
+    for (int u = 0; u < kFoldMaxSplits; ++u) v[u] = src[(int64_t)min(u, a.Pc - 1) * kStateElems + idx];
+    float acc = carried(a, bh, idx);
+#pragma unroll
+    for (int u = 0; u < kFoldMaxSplits; ++u)
+      if (u < a.Pc) acc += v[u];
+    st[idx] = acc;
+    if (p == 0) a.states[bh * kStateElems + idx] = acc;
+  }
+  __syncthreads();
+  // every lane has used its carried values: say so to the committing part
+  if (f.flags && p != f.P - 1 && tid == 0)
+    __hip_atomic_store(f.flags + bh * f.P + p, f.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  ApplyOperands op;
+  load_apply_operands(st, st + 1024, g, m, op);
+  const AxisLane al = axis_lane(rp, g);
+  apply_stream<kRopeNone, 1>(Qh, Oh, 64, 64, t0, q_end, lane_off, lane_off, lane_off, m, g, rp, nullptr, al, op, eps,
+                             next, 64 * WAVES);
+
+  if (a.kv_out && p == f.P - 1) {
+    if (f.flags && tid == 0) {
+      for (int u = 0; u < f.P - 1; ++u) {
+        for (int spin = 0; spin < kFoldSpinLimit; ++spin) {
+          if (__hip_atomic_load(f.flags + bh * f.P + u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == f.epoch)
+            break;
+          __builtin_amdgcn_s_sleep(2);
+        }
+      }
+    }
+    __syncthreads();
+    for (int idx = tid; idx < kStateElems; idx += kFoldThreads) commit(a, bh, idx, st[idx]);
+  }
 }
 
 // ---------------------------------------------------------------------------

@@ -29,6 +29,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <atomic>
 #include <initializer_list>
 #include <mutex>
 #include <type_traits>
@@ -74,6 +75,13 @@ constexpr int64_t kMinApplyTokensF32 = 256;
 constexpr int64_t kMaxApplyTokensF32 = 1024;
 // a launch may hold at most 2^32 - 1 work-items: 2^24 - 1 workgroups of 256
 constexpr int64_t kMaxGroups = ((int64_t)1 << 24) - 1;
+// Apply with the finalize folded in: at most this many CUs' worth of
+// workgroups per head (each workgroup reads the head's partials), and heads of
+// at most this many tokens.
+constexpr int64_t kFoldMaxParts = 4;
+constexpr int64_t kFoldMaxTokens = 1 << 20;
+// heads longer than this take 8-wave folded-apply workgroups, shorter 16-wave
+constexpr int64_t kFoldWideTokens = 8192;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
@@ -124,7 +132,8 @@ Geometry make_geometry(int64_t BH, int64_t N, int64_t L, bool rope) {
   g.T = ceil_div(g.L, lt);
 
   const int64_t state = (int64_t)la::kStateElems * (int64_t)sizeof(float);
-  const int64_t partials = g.C * g.Pc > 1 ? BH * g.C * g.Pc * state : 0;
+  // (+ one word per head and part: the arrival flags of apply_fold_bf16)
+  const int64_t partials = g.C * g.Pc > 1 ? BH * g.C * g.Pc * state + BH * kFoldMaxParts * 16 * 4 : 0;
   g.partial_off = 0;
   g.state_off = (size_t)round_up(partials, 256);
   g.total_bytes = g.state_off + (size_t)round_up(BH * g.C * state, 256);
@@ -461,6 +470,57 @@ bool whole_head(int dtype, const Geometry& g, bool dense, int rope_kind) {
   return dtype == SANA_DT_BF16 && g.C == 1 && g.Pc == 1 && dense && rope_kind != la::kRopeTable;
 }
 
+// Waves per workgroup of the folded apply.  Each workgroup reads its head's
+// partials once, so chunk-sized heads take one 16-wave workgroup per CU (fewer
+// copies of the partials against few bytes per head), longer heads two 8-wave
+// workgroups per CU (every CU busy; measured 3% faster on 16384 tokens, 1.6%
+// slower on 4680).
+int fold_waves(const Geometry& g) { return g.N > kFoldWideTokens ? 8 : 16; }
+
+// Workgroups per head of the apply with the finalize folded in
+// (apply_fold_bf16), or 0 where the three-launch path is taken.  It needs one
+// chunk in 2 .. kFoldMaxSplits splits, dense bf16 layouts and no RoPE; a
+// head's P workgroups share one XCD's 32 CUs with the XCD's other heads, and
+// together they keep at least half the CUs busy.
+int64_t fold_parts(int dtype, const Geometry& g, bool dense, int rope_kind) {
+  if (dtype != SANA_DT_BF16 || g.C != 1 || g.Pc < 2 || g.Pc > la::kFoldMaxSplits || !dense ||
+      rope_kind != la::kRopeNone || g.N > kFoldMaxTokens)
+    return 0;
+  // 16 waves resident per CU
+  const int64_t per_cu = 16 / fold_waves(g);
+  int64_t P = (kCUs / la::kXcdCount) * per_cu / ceil_div(g.BH, la::kXcdCount);
+  if (P > kFoldMaxParts * per_cu) P = kFoldMaxParts * per_cu;
+  if (P < 2 || g.BH * P < kCUs * per_cu / 2) return 0;
+  return P;
+}
+
+// A fresh number per folded call: its commit over a carried state waits for
+// flags holding this call's number (see apply_fold_bf16).
+std::atomic<unsigned> g_fold_epoch{0x5a5a0001u};
+
+// State pass (items dealt XCD by XCD), then the apply that sums the partials.
+void launch_fold(const void* q, const void* k, const void* v, void* o, const la::Layout& lin, const la::Layout& lo,
+                 const Geometry& g, int64_t P, const la::StateArgs& a, float eps, hipStream_t st) {
+  const la::Rope none{};
+  const int64_t heads_per_xcd = ceil_div(g.BH, la::kXcdCount);
+  la::state_bf16<la::kRopeNone, true, 1, true>
+      <<<dim3((unsigned)(la::kXcdCount * heads_per_xcd * g.Pc)), dim3(la::kThreads), 0, st>>>(
+          static_cast<const la::u32x4_t*>(k), static_cast<const la::u32x4_t*>(v), lin, none, a, g.BH);
+  la::FoldArgs f;
+  f.P = (int)P;
+  f.Na = round_up(ceil_div(g.N, P), 64);
+  // the flags live in the partials' scratch past the partials themselves
+  f.flags = (a.kv_out && a.kv_in) ? reinterpret_cast<unsigned*>(a.partials + g.BH * g.Pc * la::kStateElems) : nullptr;
+  f.epoch = g_fold_epoch.fetch_add(2u, std::memory_order_relaxed);
+  const dim3 grid((unsigned)(la::kXcdCount * heads_per_xcd * P));
+  const auto* Q = static_cast<const la::u32x4_t*>(q);
+  auto* O = static_cast<la::u32x4_t*>(o);
+  if (fold_waves(g) == 8)
+    la::apply_fold_bf16<8><<<grid, dim3(64 * 8), 0, st>>>(Q, O, lin, lo, a, f, g.BH, eps);
+  else
+    la::apply_fold_bf16<16><<<grid, dim3(64 * 16), 0, st>>>(Q, O, lin, lo, a, f, g.BH, eps);
+}
+
 // Shared body of forward, block_forward and block_causal: chunks of L tokens
 // (L >= N for one chunk), carried state in, optional commit out.
 int attend(const void* q, const void* k, const void* v, void* o, const sana_layout* in, const sana_layout* out,
@@ -503,7 +563,14 @@ int attend(const void* q, const void* k, const void* v, void* o, const sana_layo
   // one chunk of one split per head, dense bf16 layouts: a head's state and
   // its apply in one workgroup, one launch (the full-table RoPE form keeps
   // the two passes)
-  if (whole_head(dtype, g, vin.lay.token == la::kD && vout.lay.token == la::kD, ra.kind)) {
+  const bool dense = vin.lay.token == la::kD && vout.lay.token == la::kD;
+  // one chunk split a few ways over a few dozen heads: the apply sums the
+  // partials itself, two launches
+  if (const int64_t P = fold_parts(dtype, g, dense, ra.kind)) {
+    launch_fold(q, k, v, o, vin.lay, vout.lay, g, P, a, eps, st);
+    return launch_status();
+  }
+  if (whole_head(dtype, g, dense, ra.kind)) {
     with_rope(ra.kind, [&](auto R) {
       constexpr int RO = decltype(R)::value;
       if constexpr (RO != la::kRopeTable)
@@ -737,6 +804,7 @@ int sana_linattn_forward_launches(int B, int H, int64_t N, int64_t chunk, int D,
   const int kind = rope_form == 2 ? la::kRopeAxes : (rope_form == 1 ? la::kRopeTable : la::kRopeNone);
   const Geometry g = make_geometry(bh, N, chunk, rope_form != 0);
   if (whole_head(dtype, g, dense != 0, kind)) return 1;
+  if (fold_parts(dtype, g, dense != 0, kind)) return 2;
   return g.C * g.Pc > 1 ? 3 : 2;
 }
 

@@ -528,9 +528,11 @@ def test_strided_layout_validation():
 def test_forward_launches_follows_the_geometry():
     """The launch-count query: one launch when every head is one chunk of one
     split (the Sana-0.6B 1024 px layer: 144 heads of 1024 tokens; any head of
-    at most 256 tokens) with dense bf16 and no full-table RoPE; otherwise the
-    state pass and the apply, plus the finalize when a head has several
-    partials."""
+    at most 256 tokens) with dense bf16 and no full-table RoPE; two (the state
+    pass and an apply that sums the partials itself) for one chunk in 2-16
+    splits over 32-128 heads with dense bf16 and no RoPE (the 4096 px layer,
+    the 480p video chunk); otherwise the state pass and the apply, plus the
+    finalize when a head has several partials."""
     bf16, f32 = la.SANA_DT_BF16, la.SANA_DT_F32
     assert la.forward_launches(4, 36, 1024) == 1
     assert la.forward_launches(4, 36, 1024, rope_form=2) == 1
@@ -538,8 +540,14 @@ def test_forward_launches_follows_the_geometry():
     assert la.forward_launches(4, 36, 1024, dense=False) == 2
     assert la.forward_launches(4, 36, 1024, dtype=f32) == 2
     assert la.forward_launches(1, 3, 200) == 1
-    assert la.forward_launches(1, 70, 16384) == 3
-    assert la.forward_launches(1, 70, 4680) == 3
+    assert la.forward_launches(1, 70, 16384) == 2
+    assert la.forward_launches(1, 70, 4680) == 2
+    assert la.forward_launches(1, 70, 4680, rope_form=2) == 3
+    assert la.forward_launches(1, 70, 4680, dense=False) == 3
+    assert la.forward_launches(1, 70, 4680, dtype=f32) == 3
+    assert la.forward_launches(1, 31, 4680) == 3        # too few heads to fill half the CUs
+    assert la.forward_launches(1, 32, 4680) == 2
+    assert la.forward_launches(1, 130, 4680) == 3       # one workgroup per head would fit an XCD
     assert la.forward_launches(1, 70, 46800, chunk=4680) == 3
     assert la.forward_launches(1, 70, 512, chunk=256) == 3
     assert la.forward_launches(1, 2, 0) == 0
