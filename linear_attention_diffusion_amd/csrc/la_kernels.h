@@ -1183,7 +1183,7 @@ __global__ __launch_bounds__(kThreads) void forward_whole_bf16(const u32x4_t* __
 }
 
 // ---------------------------------------------------------------------------
-// Apply with the finalize folded in (bf16, dense, no RoPE, one chunk)
+// Apply with the finalize folded in (bf16, dense, one chunk; no RoPE or per-axis)
 // ---------------------------------------------------------------------------
 // Two launches per call instead of three: the state pass (items dealt XCD by
 // XCD) leaves each head's Pc partials, and each of the head's P apply
@@ -1209,16 +1209,23 @@ struct FoldArgs {
   int P;             // workgroups per head
 };
 
-template <int WAVES>
-__global__ __launch_bounds__(64 * WAVES) void apply_fold_bf16(const u32x4_t* __restrict__ Q, u32x4_t* __restrict__ O,
+// ROPE: none or the per-axis form (its tables staged in LDS, as apply_bf16
+// stages them).
+// 16 waves per CU: at most 128 VGPRs (the second bound is waves per SIMD).
+template <int WAVES, int ROPE>
+__global__ __launch_bounds__(64 * WAVES, 4) void apply_fold_bf16(const u32x4_t* __restrict__ Q, u32x4_t* __restrict__ O,
                                                               Layout lq, Layout lo, StateArgs a, FoldArgs f, int64_t BH,
-                                                              float eps) {
+                                                              float eps, Rope rp) {
+  static_assert(ROPE != kRopeTable, "the full-table form takes the three-launch path");
   constexpr int kFoldThreads = 64 * WAVES;
   __shared__ float st[kStateElems];
+  __shared__ __attribute__((aligned(16))) float rtab[ROPE == kRopeAxes ? 2 * kMaxAxisTab : 1];
   const int slot = blockIdx.x / kXcdCount;
   const int64_t bh = blockIdx.x % kXcdCount + (int64_t)kXcdCount * (slot / f.P);
   const int p = slot % f.P;
   if (bh >= BH) return;
+  rope_stage<ROPE>(rp, rtab, threadIdx.x, kFoldThreads);
+  if constexpr (ROPE == kRopeAxes) __syncthreads();
   const int64_t N = a.N;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1233,9 +1240,8 @@ __global__ __launch_bounds__(64 * WAVES) void apply_fold_bf16(const u32x4_t* __r
   const int64_t q_begin = (int64_t)p * f.Na;
   const int64_t q_end = (q_begin + f.Na < N) ? q_begin + f.Na : N;
   const int64_t t0 = q_begin + 64 * wave;
-  const Rope rp{};
-  ApplyChunk<kRopeNone> next;
-  if (t0 < q_end) load_apply_chunk<kRopeNone, 1>(Qh, 64, t0, q_end, lane_off, lane_off, m, g, rp, nullptr, next);
+  ApplyChunk<ROPE> next;
+  if (t0 < q_end) load_apply_chunk<ROPE, 1>(Qh, 64, t0, q_end, lane_off, lane_off, m, g, rp, rtab, next);
 
   // the head's state: the carried one plus the partials in split order; the
   // loads go out together (those past the last partial re-read it, unused)
@@ -1259,8 +1265,8 @@ __global__ __launch_bounds__(64 * WAVES) void apply_fold_bf16(const u32x4_t* __r
   ApplyOperands op;
   load_apply_operands(st, st + 1024, g, m, op);
   const AxisLane al = axis_lane(rp, g);
-  apply_stream<kRopeNone, 1>(Qh, Oh, 64, 64, t0, q_end, lane_off, lane_off, lane_off, m, g, rp, nullptr, al, op, eps,
-                             next, 64 * WAVES);
+  apply_stream<ROPE, 1>(Qh, Oh, 64, 64, t0, q_end, lane_off, lane_off, lane_off, m, g, rp, rtab, al, op, eps, next,
+                        64 * WAVES);
 
   if (a.kv_out && p == f.P - 1) {
     if (f.flags && tid == 0) {

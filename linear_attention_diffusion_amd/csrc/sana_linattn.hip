@@ -479,12 +479,12 @@ int fold_waves(const Geometry& g) { return g.N > kFoldWideTokens ? 8 : 16; }
 
 // Workgroups per head of the apply with the finalize folded in
 // (apply_fold_bf16), or 0 where the three-launch path is taken.  It needs one
-// chunk in 2 .. kFoldMaxSplits splits, dense bf16 layouts and no RoPE; a
+// chunk in 2 .. kFoldMaxSplits splits, dense bf16 layouts and no full-table RoPE; a
 // head's P workgroups share one XCD's 32 CUs with the XCD's other heads, and
 // together they keep at least half the CUs busy.
 int64_t fold_parts(int dtype, const Geometry& g, bool dense, int rope_kind) {
   if (dtype != SANA_DT_BF16 || g.C != 1 || g.Pc < 2 || g.Pc > la::kFoldMaxSplits || !dense ||
-      rope_kind != la::kRopeNone || g.N > kFoldMaxTokens)
+      rope_kind == la::kRopeTable || g.N > kFoldMaxTokens)
     return 0;
   // 16 waves resident per CU
   const int64_t per_cu = 16 / fold_waves(g);
@@ -499,13 +499,12 @@ int64_t fold_parts(int dtype, const Geometry& g, bool dense, int rope_kind) {
 std::atomic<unsigned> g_fold_epoch{0x5a5a0001u};
 
 // State pass (items dealt XCD by XCD), then the apply that sums the partials.
+template <int RO>
 void launch_fold(const void* q, const void* k, const void* v, void* o, const la::Layout& lin, const la::Layout& lo,
-                 const Geometry& g, int64_t P, const la::StateArgs& a, float eps, hipStream_t st) {
-  const la::Rope none{};
+                 const Geometry& g, int64_t P, const RopeArg& ra, const la::StateArgs& a, float eps, hipStream_t st) {
   const int64_t heads_per_xcd = ceil_div(g.BH, la::kXcdCount);
-  la::state_bf16<la::kRopeNone, true, 1, true>
-      <<<dim3((unsigned)(la::kXcdCount * heads_per_xcd * g.Pc)), dim3(la::kThreads), 0, st>>>(
-          static_cast<const la::u32x4_t*>(k), static_cast<const la::u32x4_t*>(v), lin, none, a, g.BH);
+  la::state_bf16<RO, true, 1, true><<<dim3((unsigned)(la::kXcdCount * heads_per_xcd * g.Pc)), dim3(la::kThreads), 0, st>>>(
+      static_cast<const la::u32x4_t*>(k), static_cast<const la::u32x4_t*>(v), lin, ra.r, a, g.BH);
   la::FoldArgs f;
   f.P = (int)P;
   f.Na = round_up(ceil_div(g.N, P), 64);
@@ -516,9 +515,9 @@ void launch_fold(const void* q, const void* k, const void* v, void* o, const la:
   const auto* Q = static_cast<const la::u32x4_t*>(q);
   auto* O = static_cast<la::u32x4_t*>(o);
   if (fold_waves(g) == 8)
-    la::apply_fold_bf16<8><<<grid, dim3(64 * 8), 0, st>>>(Q, O, lin, lo, a, f, g.BH, eps);
+    la::apply_fold_bf16<8, RO><<<grid, dim3(64 * 8), 0, st>>>(Q, O, lin, lo, a, f, g.BH, eps, ra.r);
   else
-    la::apply_fold_bf16<16><<<grid, dim3(64 * 16), 0, st>>>(Q, O, lin, lo, a, f, g.BH, eps);
+    la::apply_fold_bf16<16, RO><<<grid, dim3(64 * 16), 0, st>>>(Q, O, lin, lo, a, f, g.BH, eps, ra.r);
 }
 
 // Shared body of forward, block_forward and block_causal: chunks of L tokens
@@ -567,7 +566,10 @@ int attend(const void* q, const void* k, const void* v, void* o, const sana_layo
   // one chunk split a few ways over a few dozen heads: the apply sums the
   // partials itself, two launches
   if (const int64_t P = fold_parts(dtype, g, dense, ra.kind)) {
-    launch_fold(q, k, v, o, vin.lay, vout.lay, g, P, a, eps, st);
+    if (ra.kind == la::kRopeAxes)
+      launch_fold<la::kRopeAxes>(q, k, v, o, vin.lay, vout.lay, g, P, ra, a, eps, st);
+    else
+      launch_fold<la::kRopeNone>(q, k, v, o, vin.lay, vout.lay, g, P, ra, a, eps, st);
     return launch_status();
   }
   if (whole_head(dtype, g, dense, ra.kind)) {

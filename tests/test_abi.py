@@ -530,8 +530,8 @@ def test_forward_launches_follows_the_geometry():
     split (the Sana-0.6B 1024 px layer: 144 heads of 1024 tokens; any head of
     at most 256 tokens) with dense bf16 and no full-table RoPE; two (the state
     pass and an apply that sums the partials itself) for one chunk in 2-16
-    splits over 32-128 heads with dense bf16 and no RoPE (the 4096 px layer,
-    the 480p video chunk); otherwise the state pass and the apply, plus the
+    splits over 32-128 heads with dense bf16 and no full-table RoPE (the 4096
+    px layer, the 480p video chunk, the 720p layer); otherwise the state pass and the apply, plus the
     finalize when a head has several partials."""
     bf16, f32 = la.SANA_DT_BF16, la.SANA_DT_F32
     assert la.forward_launches(4, 36, 1024) == 1
@@ -542,7 +542,8 @@ def test_forward_launches_follows_the_geometry():
     assert la.forward_launches(1, 3, 200) == 1
     assert la.forward_launches(1, 70, 16384) == 2
     assert la.forward_launches(1, 70, 4680) == 2
-    assert la.forward_launches(1, 70, 4680, rope_form=2) == 3
+    assert la.forward_launches(1, 70, 4680, rope_form=2) == 2
+    assert la.forward_launches(1, 70, 4680, rope_form=1) == 3       # full-table RoPE keeps three
     assert la.forward_launches(1, 70, 4680, dense=False) == 3
     assert la.forward_launches(1, 70, 4680, dtype=f32) == 3
     assert la.forward_launches(1, 31, 4680) == 3        # too few heads to fill half the CUs

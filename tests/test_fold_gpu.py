@@ -161,3 +161,42 @@ def test_fold_forward_4096px_full_size():
     o2 = la.sana_linattn_forward(_padded(q), _padded(k), _padded(v), eps=w.eps)
     _same(o, o2, "O")
     check(to_np(o), oracle.linattn(x.f64["q"], x.f64["k"], x.f64["v"], w.eps), "bf16", "folded 4096 px forward")
+
+
+@pytest.mark.parametrize("B,H,N,grid,offset,commit", [(1, 70, 2 * 40 * 50, (2, 40, 50), 0, False),
+                                                      (1, 40, 3 * 30 * 52, (5, 30, 52), 1560, True)])
+def test_fold_per_axis_rope_equals_three_launch_path(B, H, N, grid, offset, commit):
+    """SANA-Video's per-axis 3D RoPE ("SANA-Video" paper notes 2.2; section 3
+    Stage 2) through the two-launch path: a forward over two latent frames,
+    and a committing chunk call at a frame offset from a carried state, each
+    bit for bit as the padded-view three-launch path and within the oracle
+    bars."""
+    torch = torch_mod()
+    assert la.forward_launches(B, H, N, rope_form=2) == 2
+    w = reduced(WORKLOADS["video720p_rope3d"], B=B, H=H, N=N, grid=grid, mode="rope")
+    print(f"case folded per-axis RoPE B={B} H={H} N={N} offset={offset} commit={commit}", flush=True)
+    x = generate(w)
+    q, k, v = (to_dev(x.raw[n], "bf16") for n in ("q", "k", "v"))
+    r = la.rope3d_axes_device(*grid, device()).at(offset)
+    kv0, z0 = _carried(B, H, 11)
+    res = []
+    for view in (lambda t: t, _padded):
+        if commit:
+            kv, z = kv0.to(device()), z0.to(device())
+            o = la.sana_linattn_block_forward(view(q), view(k), view(v), kv_in=kv, ksum_in=z, kv_out=kv, ksum_out=z,
+                                              eps=w.eps, rope=r)
+            res.append((o, kv, z))
+        else:
+            res.append((la.sana_linattn_forward(view(q), view(k), view(v), eps=w.eps, rope=r), None, None))
+    _same(res[0][0], res[1][0], "O")
+    ang = oracle.rope3d_angles(*grid)
+    if commit:
+        _same(res[0][1], res[1][1], "committed S")
+        _same(res[0][2], res[1][2], "committed z")
+        ref_o, ref_s, ref_z = oracle.block_forward(x.f64["q"], x.f64["k"], x.f64["v"], kv0.double().numpy(),
+                                                   z0.double().numpy(), w.eps, ang, offset)
+        check(to_np(res[0][0]), ref_o, "bf16", "folded RoPE block_forward")
+        check(to_np(res[0][1]), ref_s, "f32", "folded RoPE committed S")
+    else:
+        check(to_np(res[0][0]), oracle.linattn(x.f64["q"], x.f64["k"], x.f64["v"], w.eps, angles=ang), "bf16",
+              "folded RoPE forward")
